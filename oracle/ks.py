@@ -1,0 +1,39 @@
+"""fp64 oracle of the Kronecker-sparse (KS) matmul (test infrastructure only).
+
+Source: "Fast Inference with Kronecker-Sparse Matrices" (arXiv 2405.15013), abstract:
+a KS matrix is one whose support is a Kronecker product of identity and all-ones
+blocks.  The pattern used here is I_a (x) 1_{b x c} (x) I_d, an (a*b*d) x (a*c*d)
+matrix K with a*b*c*d nonzeros, applied to rows as Y = X K.
+
+The page gives no value layout.  Reading adopted: row-major Kronecker indices,
+row (alpha, beta, delta) -> (alpha*b + beta)*d + delta and column
+(alpha, gamma, delta) -> (alpha*c + gamma)*d + delta, with the nonzero values
+stored as vals[alpha][delta][beta][gamma] (a x d x b x c).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .kron import as64, kron_block
+
+
+def support(a: int, b: int, c: int, d: int) -> np.ndarray:
+    """0/1 support I_a (x) 1_{b x c} (x) I_d, built with the block-by-block Kronecker product."""
+    return kron_block(kron_block(np.eye(a), np.ones((b, c))), np.eye(d))
+
+
+def dense(vals, a: int, b: int, c: int, d: int) -> np.ndarray:
+    """Scatter vals[alpha][delta][beta][gamma] into the dense (a*b*d) x (a*c*d) matrix."""
+    V = as64(vals).reshape(a, d, b, c)
+    K = np.zeros((a * b * d, a * c * d))
+    for al in range(a):
+        for de in range(d):
+            rows = (al * b + np.arange(b)) * d + de
+            cols = (al * c + np.arange(c)) * d + de
+            K[np.ix_(rows, cols)] = V[al, de]
+    return K
+
+
+def matmul(x, vals, a: int, b: int, c: int, d: int) -> np.ndarray:
+    """Y = X K with K the dense KS matrix."""
+    return as64(x) @ dense(vals, a, b, c, d)
