@@ -1,0 +1,167 @@
+/*
+ * libkron -- Kronecker-factored linear layers and Kronecker-sparse matmuls on AMD
+ * Instinct MI355X (gfx950).  Plain C ABI: device pointers, sizes, a HIP stream.
+ *
+ * Notation (Kronecker layer tutorial, intro and "Build W, then multiply"):
+ *   S      p x q                sparsity mask (l1-penalised); NULL means S == 1
+ *   A      r x p x q            A_i, i = 0..r-1
+ *   B      r x m x n            B_i
+ *   C_i    = S o A_i            (elementwise product)
+ *   W      = sum_i kron(C_i, B_i), (p*m) x (q*n), oriented in x out
+ *   y      = x W + bias         x is N x (p*m), y is N x (q*n), bias has q*n entries
+ * The library never forms W.  Each row x_n is read as a p x m row-major matrix X_n
+ * and the row of y is vec_row(sum_i C_i^T X_n B_i) + bias (tutorial, "The vec trick"
+ * and "The vec trick without the loop"): the X_n B_i products stay on chip.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor arguments are DEVICE pointers to dense row-major fp32 (or bf16 where
+ *     stated) arrays, base address aligned to 16 bytes.  The caller owns all memory,
+ *     including any workspace; no entry point allocates or frees device memory.
+ *   - Calls are asynchronous on `stream` (0 = the null stream).  No host sync.
+ *   - Arguments are validated on the host before any HIP call.  On error nothing is
+ *     launched, nothing is written, and a kron_status_t other than KRON_OK is
+ *     returned; kron_last_error() then holds a detail string for the calling thread.
+ *     A failed kernel launch returns KRON_E_HIP.  Nothing aborts, prints or throws.
+ *   - Gradient outputs are overwritten, not accumulated.
+ *   - Results are deterministic: the same inputs on the same device give bitwise
+ *     identical outputs (fixed-order reductions, no floating-point atomics).
+ *   - Calls are thread-safe; the only global state is the per-thread error string.
+ */
+#ifndef LIBKRON_KRON_H
+#define LIBKRON_KRON_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KRON_ABI_VERSION 1
+
+typedef enum {
+  KRON_OK = 0,
+  KRON_E_NULL = 1,        /* a required pointer is NULL (or an optional pair is inconsistent) */
+  KRON_E_SHAPE = 2,       /* a size is out of range or sizes disagree                       */
+  KRON_E_ALIGN = 3,       /* a pointer is not 16-byte aligned                                */
+  KRON_E_ALIAS = 4,       /* an output overlaps an input or another output                   */
+  KRON_E_DTYPE = 5,       /* unknown dtype                                                   */
+  KRON_E_WORKSPACE = 6,   /* workspace missing or smaller than required                      */
+  KRON_E_UNSUPPORTED = 7, /* valid, but beyond what this build supports (see limits below)   */
+  KRON_E_HIP = 8,         /* a HIP call failed; kron_last_error() has hipGetErrorString      */
+  KRON_E_ARG = 9          /* another invalid argument (step < 1, negative count, bad flag)   */
+} kron_status_t;
+
+typedef enum { KRON_F32 = 0, KRON_BF16 = 1 } kron_dtype_t;
+
+/* kron_shape_t.flags */
+#define KRON_RELU_OUT     1u  /* fwd: y = max(x W + bias, 0)                              */
+#define KRON_DX_RELU_MASK 2u  /* bwd: dX = (dY W^T) o [x > 0]  (x is the output of a ReLU) */
+
+typedef struct {
+  int64_t N;                 /* rows, >= 0                              */
+  int32_t p, q, m, n, r;     /* in = p*m, out = q*n; each >= 1          */
+  uint32_t flags;            /* KRON_RELU_OUT | KRON_DX_RELU_MASK       */
+} kron_shape_t;
+
+/* Limits of this build: 1 <= p,q,m,n <= 4096, 1 <= r <= 64, p*m and q*n <= 65536,
+ * N <= 2^31 - 1; r*p*q and r*m*n <= 2^24.  Shapes whose per-row working set does not
+ * fit in one workgroup's LDS return KRON_E_UNSUPPORTED. */
+
+int32_t kron_abi_version(void);
+const char* kron_status_str(int32_t status);
+/* Detail string of the last failed call on this thread ("" if none).  Valid until the
+ * next call on the same thread. */
+const char* kron_last_error(void);
+
+/* Host-only shape validation (no HIP call); returns KRON_OK or the error. */
+int32_t kron_linear_check(const kron_shape_t* shape);
+
+/* Bytes of workspace kron_linear_bwd needs for this shape (0 on an invalid shape).
+ * Depends only on the shape. */
+size_t kron_linear_bwd_workspace_bytes(const kron_shape_t* shape);
+
+/*
+ * Forward: y = x W + bias (tutorial, "The vec trick without the loop": the rank is
+ * fused into one pass, the X_n B_i products never leave the chip).  Terms with
+ * S[j,k] == 0 contribute nothing (zero blocks of W, tutorial intro).
+ *   x    [N, p*m]   S [p, q] or NULL   A [r, p, q]   B [r, m, n]
+ *   bias [q*n] or NULL                  y [N, q*n]  (must not overlap any input)
+ */
+int32_t kron_linear_fwd(const kron_shape_t* shape, const float* x, const float* S,
+                        const float* A, const float* B, const float* bias, float* y,
+                        hipStream_t stream);
+
+/*
+ * Backward of y = x W + bias for the upstream gradient dy [N, q*n]:
+ *   dx    = dy W^T                      [N, p*m]   (NULL: not computed)
+ *   dS    = sum_i A_i o dC_i            [p, q]     (must be NULL iff S is NULL)
+ *   dA_i  = S o dC_i                    [r, p, q]  (dC_i when S is NULL)
+ *   dB_i  = sum_n X_n^T G_{n,i}         [r, m, n]  with G_{n,i} = C_i dY_n
+ *   dbias = sum_n dy_n                  [q*n]      (NULL: not computed)
+ * where dC_i = sum_n (X_n B_i) dY_n^T.  X_n B_i is recomputed on chip rather than
+ * stored by the forward.  With KRON_DX_RELU_MASK, dx is multiplied by [x > 0].
+ * N == 0 is valid: the parameter gradients are set to zero.
+ * workspace: device buffer of at least kron_linear_bwd_workspace_bytes(shape) bytes,
+ * 256-byte aligned; its contents on entry are ignored.  Outputs must not overlap each
+ * other, the inputs or the workspace.
+ */
+int32_t kron_linear_bwd(const kron_shape_t* shape, const float* x, const float* S,
+                        const float* A, const float* B, const float* dy,
+                        float* dx, float* dS, float* dA, float* dB, float* dbias,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Kronecker-sparse matmul ("Fast Inference with Kronecker-Sparse Matrices", abstract):
+ * Y = X K with K of support I_a (x) 1_{b x c} (x) I_d, (a*b*d) x (a*c*d):
+ *   Y[n, (al*c + ga)*d + de] = sum_be X[n, (al*b + be)*d + de] * vals[al][de][be][ga]
+ *   x    [N, a*b*d]  fp32 or bf16 (in_dtype)
+ *   vals [a, d, b, c] same dtype as x
+ *   y    [N, a*c*d]  fp32, accumulated in fp32
+ * Limits: a*b*d and a*c*d <= 65536.
+ */
+int32_t ks_matmul(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype,
+                  const void* x, const void* vals, float* y, hipStream_t stream);
+
+/*
+ * Fused multi-tensor Adam with an l1 penalty (tutorial, "Setup": Adam update of the
+ * training step; intro: l1 penalty on S).  For tensor t and element e:
+ *   g  = grads[t][e] + l1[t] * sign(params[t][e])       (sign(0) = 0)
+ *   m  = beta1*m + (1-beta1)*g,   v = beta2*v + (1-beta2)*g*g
+ *   params -= lr * (m / (1 - beta1^step)) / (sqrt(v / (1 - beta2^step)) + eps)
+ * params, grads, m, v, numel and l1 are HOST arrays of length ntensors; the first four
+ * hold device pointers.  l1 may be NULL (no penalty).  step >= 1.  Tensors with
+ * numel 0 are skipped.  Up to 4096 tensors per call.  The hyper-parameters are taken in
+ * double: 1 - beta and the bias corrections are formed on the host in double and
+ * rounded once to fp32 (1 - 0.999f in fp32 would be off by 1.3e-5 relative).
+ */
+int32_t kron_adam_l1_step(int32_t ntensors, float* const* params, const float* const* grads,
+                          float* const* m, float* const* v, const int64_t* numel,
+                          const float* l1, int64_t step, double lr, double beta1, double beta2,
+                          double eps, hipStream_t stream);
+
+/*
+ * Dense classification head with mean softmax cross-entropy, forward and backward in
+ * one call (tutorial, "Setup": the 10-class output layer stays dense; the loss is the
+ * cross-entropy):
+ *   z = h Wh + bh,  loss = mean_n (logsumexp(z_n) - z_n[label_n])
+ *   dz = (softmax(z) - onehot(label)) / N
+ *   dWh = h^T dz [K, C],  dbh = sum_n dz [C],  dh = dz Wh^T [N, K]
+ * With KRON_DX_RELU_MASK in flags, dh is multiplied by [h > 0].
+ *   h [N, K]  Wh [K, C]  bh [C]  labels [N] int64 in [0, C)
+ *   loss: one device float.  dh may be NULL.
+ * Labels outside [0, C) make the loss NaN (no out-of-bounds access).
+ * Limits: 1 <= C <= 64, 1 <= K <= 8192.  workspace as for kron_linear_bwd.
+ */
+size_t kron_head_ce_workspace_bytes(int64_t N, int32_t K, int32_t C);
+int32_t kron_head_ce(int64_t N, int32_t K, int32_t C, const float* h, const float* Wh,
+                     const float* bh, const int64_t* labels, float* loss, float* dh,
+                     float* dWh, float* dbh, uint32_t flags, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBKRON_KRON_H */

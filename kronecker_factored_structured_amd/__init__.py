@@ -1,0 +1,15 @@
+"""Kronecker-factored structured layers on AMD MI355X (gfx950).
+
+The compute lives in libkron.so (HIP kernels behind a C ABI, include/kron.h); this
+package is its Python binding.  Build the library with
+`python -m kronecker_factored_structured_amd.build`.
+"""
+from . import _lib
+from .api import (kron_adam_l1_step, kron_head_ce, kron_linear_bwd, kron_linear_bwd_workspace_bytes,
+                  kron_linear_fwd, ks_matmul, layer_shape)
+from .layers import KronLinear, KronMLPStep, KSLinear
+
+__all__ = [
+    "kron_linear_fwd", "kron_linear_bwd", "kron_linear_bwd_workspace_bytes", "ks_matmul",
+    "kron_adam_l1_step", "kron_head_ce", "layer_shape", "KronLinear", "KSLinear", "KronMLPStep", "_lib",
+]

@@ -1,0 +1,337 @@
+// C ABI of libkron: argument validation (host only, before any HIP call), launch
+// planning and dispatch to the kernels.  See include/kron.h for the contract.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kron_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(kron_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+int32_t ok() {
+  g_last_error.clear();
+  return KRON_OK;
+}
+
+int32_t hip_fail(hipError_t e, const char* where) {
+  return fail(KRON_E_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Range {
+  const void* p;
+  size_t bytes;
+  const char* name;
+};
+
+bool overlap(const Range& a, const Range& b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + a.bytes;
+  const uintptr_t b0 = (uintptr_t)b.p, b1 = b0 + b.bytes;
+  return a0 < b1 && b0 < a1;
+}
+
+// Every output must be disjoint from every input and from every other output.
+int32_t check_alias(const Range* outs, int nout, const Range* ins, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlap(outs[i], ins[j]))
+        return fail(KRON_E_ALIAS, "output %s overlaps input %s", outs[i].name, ins[j].name);
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(KRON_E_ALIAS, "output %s overlaps output %s", outs[i].name, outs[j].name);
+  }
+  return KRON_OK;
+}
+
+int32_t check_align(const Range* rs, int n) {
+  for (int i = 0; i < n; ++i)
+    if (rs[i].p && !aligned16(rs[i].p))
+      return fail(KRON_E_ALIGN, "%s is not 16-byte aligned (%p)", rs[i].name, rs[i].p);
+  return KRON_OK;
+}
+
+constexpr int32_t kMaxDim = 4096;
+constexpr int32_t kMaxRank = 64;
+constexpr int64_t kMaxFeatures = 65536;
+constexpr int64_t kMaxParams = int64_t(1) << 24;
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+
+int32_t check_shape(const kron_shape_t* s) {
+  if (!s) return fail(KRON_E_NULL, "shape is NULL");
+  if (s->N < 0 || s->N > kMaxRows) return fail(KRON_E_SHAPE, "N = %lld out of range", (long long)s->N);
+  const int32_t d[5] = {s->p, s->q, s->m, s->n, s->r};
+  const char* nm[5] = {"p", "q", "m", "n", "r"};
+  for (int i = 0; i < 5; ++i)
+    if (d[i] < 1) return fail(KRON_E_SHAPE, "%s = %d must be >= 1", nm[i], d[i]);
+  for (int i = 0; i < 4; ++i)
+    if (d[i] > kMaxDim) return fail(KRON_E_UNSUPPORTED, "%s = %d exceeds %d", nm[i], d[i], kMaxDim);
+  if (s->r > kMaxRank) return fail(KRON_E_UNSUPPORTED, "r = %d exceeds %d", s->r, kMaxRank);
+  const int64_t in = (int64_t)s->p * s->m, out = (int64_t)s->q * s->n;
+  if (in > kMaxFeatures || out > kMaxFeatures)
+    return fail(KRON_E_UNSUPPORTED, "in = %lld or out = %lld exceeds %lld", (long long)in, (long long)out,
+                (long long)kMaxFeatures);
+  if ((int64_t)s->r * s->p * s->q > kMaxParams || (int64_t)s->r * s->m * s->n > kMaxParams)
+    return fail(KRON_E_UNSUPPORTED, "factor tensors exceed %lld elements", (long long)kMaxParams);
+  if (s->flags & ~(KRON_RELU_OUT | KRON_DX_RELU_MASK))
+    return fail(KRON_E_ARG, "unknown flag bits 0x%x", s->flags);
+  return KRON_OK;
+}
+
+struct BwdPlan {
+  int T;
+  int G;
+  size_t ws_bytes;
+};
+
+BwdPlan bwd_plan(const kron_shape_t* s, bool want_dx) {
+  BwdPlan pl{0, 0, 0};
+  pl.T = kron::generic_bwd_rows_per_tile(s->p, s->q, s->m, s->n, want_dx);
+  if (pl.T == 0) return pl;
+  pl.G = kron::generic_bwd_groups(s->N, pl.T);
+  const int64_t PW = kron::partial_width(s->p, s->q, s->m, s->n, s->r);
+  pl.ws_bytes = (size_t)pl.G * (size_t)PW * sizeof(float);
+  return pl;
+}
+
+// Workspace bytes for a shape: the larger of the plans with and without dx, so the
+// caller need not know which one a call will take.
+size_t bwd_workspace(const kron_shape_t* s) {
+  const BwdPlan a = bwd_plan(s, true), b = bwd_plan(s, false);
+  size_t w = a.ws_bytes > b.ws_bytes ? a.ws_bytes : b.ws_bytes;
+  return w == 0 ? 256 : (w + 255) & ~size_t(255);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kron_abi_version(void) { return KRON_ABI_VERSION; }
+
+const char* kron_status_str(int32_t st) {
+  switch (st) {
+    case KRON_OK: return "ok";
+    case KRON_E_NULL: return "null pointer";
+    case KRON_E_SHAPE: return "invalid shape";
+    case KRON_E_ALIGN: return "misaligned pointer";
+    case KRON_E_ALIAS: return "overlapping buffers";
+    case KRON_E_DTYPE: return "unknown dtype";
+    case KRON_E_WORKSPACE: return "workspace missing or too small";
+    case KRON_E_UNSUPPORTED: return "unsupported by this build";
+    case KRON_E_HIP: return "HIP error";
+    case KRON_E_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+const char* kron_last_error(void) { return g_last_error.c_str(); }
+
+int32_t kron_linear_check(const kron_shape_t* s) {
+  const int32_t st = check_shape(s);
+  if (st != KRON_OK) return st;
+  if (kron::generic_fwd_rows_per_tile(s->p, s->q, s->m, s->n) == 0 ||
+      kron::generic_bwd_rows_per_tile(s->p, s->q, s->m, s->n, true) == 0)
+    return fail(KRON_E_UNSUPPORTED, "per-row working set of p=%d q=%d m=%d n=%d exceeds LDS", s->p, s->q,
+                s->m, s->n);
+  return ok();
+}
+
+size_t kron_linear_bwd_workspace_bytes(const kron_shape_t* s) {
+  if (kron_linear_check(s) != KRON_OK) return 0;
+  return bwd_workspace(s);
+}
+
+int32_t kron_linear_fwd(const kron_shape_t* s, const float* x, const float* S, const float* A,
+                        const float* B, const float* bias, float* y, hipStream_t stream) {
+  int32_t st = kron_linear_check(s);
+  if (st != KRON_OK) return st;
+  if (s->flags & KRON_DX_RELU_MASK) return fail(KRON_E_ARG, "KRON_DX_RELU_MASK is a backward flag");
+  if (!A || !B) return fail(KRON_E_NULL, "A and B are required");
+  if (s->N > 0 && (!x || !y)) return fail(KRON_E_NULL, "x and y are required when N > 0");
+  const size_t in = (size_t)s->p * s->m, out = (size_t)s->q * s->n;
+  const Range ins[5] = {{x, (size_t)s->N * in * 4, "x"},
+                        {S, (size_t)s->p * s->q * 4, "S"},
+                        {A, (size_t)s->r * s->p * s->q * 4, "A"},
+                        {B, (size_t)s->r * s->m * s->n * 4, "B"},
+                        {bias, out * 4, "bias"}};
+  const Range outs[1] = {{y, (size_t)s->N * out * 4, "y"}};
+  if ((st = check_align(ins, 5)) != KRON_OK || (st = check_align(outs, 1)) != KRON_OK) return st;
+  if ((st = check_alias(outs, 1, ins, 5)) != KRON_OK) return st;
+  if (s->N == 0) return ok();
+  kron::LayerArgs a{};
+  a.N = s->N; a.p = s->p; a.q = s->q; a.m = s->m; a.n = s->n; a.r = s->r; a.flags = s->flags;
+  a.x = x; a.S = S; a.A = A; a.B = B; a.bias = bias; a.y = y;
+  hipError_t e = kron::launch_fwd_generic(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "kron_linear_fwd launch");
+  return ok();
+}
+
+int32_t kron_linear_bwd(const kron_shape_t* s, const float* x, const float* S, const float* A,
+                        const float* B, const float* dy, float* dx, float* dS, float* dA, float* dB,
+                        float* dbias, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int32_t st = kron_linear_check(s);
+  if (st != KRON_OK) return st;
+  if (s->flags & KRON_RELU_OUT) return fail(KRON_E_ARG, "KRON_RELU_OUT is a forward flag");
+  if (!A || !B || !dA || !dB) return fail(KRON_E_NULL, "A, B, dA and dB are required");
+  if ((S == nullptr) != (dS == nullptr)) return fail(KRON_E_NULL, "dS must be given exactly when S is");
+  if (s->N > 0 && (!x || !dy)) return fail(KRON_E_NULL, "x and dy are required when N > 0");
+  if ((s->flags & KRON_DX_RELU_MASK) && !dx) return fail(KRON_E_ARG, "KRON_DX_RELU_MASK needs dx");
+  const size_t need = bwd_workspace(s);
+  if (!workspace || workspace_bytes < need)
+    return fail(KRON_E_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if (((uintptr_t)workspace & 255u) != 0) return fail(KRON_E_ALIGN, "workspace is not 256-byte aligned");
+  const size_t in = (size_t)s->p * s->m, out = (size_t)s->q * s->n;
+  const size_t pq = (size_t)s->p * s->q, mn = (size_t)s->m * s->n;
+  const Range ins[6] = {{x, (size_t)s->N * in * 4, "x"},     {S, pq * 4, "S"},
+                        {A, s->r * pq * 4, "A"},             {B, s->r * mn * 4, "B"},
+                        {dy, (size_t)s->N * out * 4, "dy"},  {workspace, need, "workspace"}};
+  const Range outs[5] = {{dx, (size_t)s->N * in * 4, "dx"}, {dS, pq * 4, "dS"}, {dA, s->r * pq * 4, "dA"},
+                         {dB, s->r * mn * 4, "dB"},         {dbias, out * 4, "dbias"}};
+  if ((st = check_align(ins, 6)) != KRON_OK || (st = check_align(outs, 5)) != KRON_OK) return st;
+  if ((st = check_alias(outs, 5, ins, 6)) != KRON_OK) return st;
+
+  kron::LayerArgs a{};
+  a.N = s->N; a.p = s->p; a.q = s->q; a.m = s->m; a.n = s->n; a.r = s->r; a.flags = s->flags;
+  a.x = x; a.S = S; a.A = A; a.B = B; a.dy = dy;
+  a.dx = s->N > 0 ? dx : nullptr;
+  a.dS = dS; a.dA = dA; a.dB = dB; a.dbias = dbias;
+  a.part = (float*)workspace;
+  const BwdPlan pl = bwd_plan(s, a.dx != nullptr);
+  hipError_t e = kron::launch_bwd_generic(a, pl.G, stream);
+  if (e != hipSuccess) return hip_fail(e, "kron_linear_bwd launch");
+  kron::RedPlan rp{};
+  rp.nseg = 3;
+  rp.seg[0] = kron::RedSeg{dB, s->r * s->m * s->n, 1.f};
+  rp.seg[1] = kron::RedSeg{dA, s->r * s->p * s->q, 1.f};
+  rp.seg[2] = kron::RedSeg{dbias, s->q * s->n, 1.f};
+  const int32_t PW = (int32_t)kron::partial_width(s->p, s->q, s->m, s->n, s->r);
+  e = kron::launch_column_reduce(a.part, pl.G, PW, rp, stream);
+  if (e != hipSuccess) return hip_fail(e, "kron_linear_bwd reduce launch");
+  if (S) {
+    e = kron::launch_bwd_epilogue(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "kron_linear_bwd epilogue launch");
+  }
+  return ok();
+}
+
+int32_t ks_matmul(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype, const void* x,
+                  const void* vals, float* y, hipStream_t stream) {
+  if (N < 0 || N > kMaxRows) return fail(KRON_E_SHAPE, "N = %lld out of range", (long long)N);
+  if (a < 1 || b < 1 || c < 1 || d < 1) return fail(KRON_E_SHAPE, "a, b, c, d must be >= 1");
+  const int64_t in = (int64_t)a * b * d, out = (int64_t)a * c * d;
+  if (in > kMaxFeatures || out > kMaxFeatures)
+    return fail(KRON_E_UNSUPPORTED, "a*b*d = %lld or a*c*d = %lld exceeds %lld", (long long)in,
+                (long long)out, (long long)kMaxFeatures);
+  if (in_dtype != KRON_F32 && in_dtype != KRON_BF16) return fail(KRON_E_DTYPE, "dtype %d", in_dtype);
+  if (!kron::ks_supported(a, b, c, d)) return fail(KRON_E_UNSUPPORTED, "b*d = %lld too large", (long long)b * d);
+  if (!vals) return fail(KRON_E_NULL, "vals is required");
+  if (N > 0 && (!x || !y)) return fail(KRON_E_NULL, "x and y are required when N > 0");
+  const size_t es = in_dtype == KRON_F32 ? 4 : 2;
+  const Range ins[2] = {{x, (size_t)N * in * es, "x"}, {vals, (size_t)a * b * c * d * es, "vals"}};
+  const Range outs[1] = {{y, (size_t)N * out * 4, "y"}};
+  int32_t st;
+  if ((st = check_align(ins, 2)) != KRON_OK || (st = check_align(outs, 1)) != KRON_OK) return st;
+  if ((st = check_alias(outs, 1, ins, 2)) != KRON_OK) return st;
+  if (N == 0) return ok();
+  kron::KSArgs k{N, a, b, c, d, in_dtype, x, vals, y};
+  hipError_t e = kron::launch_ks(k, stream);
+  if (e != hipSuccess) return hip_fail(e, "ks_matmul launch");
+  return ok();
+}
+
+int32_t kron_adam_l1_step(int32_t ntensors, float* const* params, const float* const* grads, float* const* m,
+                          float* const* v, const int64_t* numel, const float* l1, int64_t step, double lr,
+                          double beta1, double beta2, double eps, hipStream_t stream) {
+  if (ntensors < 0 || ntensors > 4096) return fail(KRON_E_ARG, "ntensors = %d out of range", ntensors);
+  if (ntensors == 0) return ok();
+  if (!params || !grads || !m || !v || !numel) return fail(KRON_E_NULL, "pointer arrays are required");
+  if (step < 1) return fail(KRON_E_ARG, "step = %lld must be >= 1", (long long)step);
+  if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0) || !(eps >= 0.0) || !std::isfinite(lr))
+    return fail(KRON_E_ARG, "hyper-parameters out of range");
+  for (int32_t t = 0; t < ntensors; ++t) {
+    if (numel[t] < 0) return fail(KRON_E_ARG, "numel[%d] < 0", t);
+    if (numel[t] == 0) continue;
+    if (!params[t] || !grads[t] || !m[t] || !v[t]) return fail(KRON_E_NULL, "tensor %d has a NULL pointer", t);
+    const Range rs[4] = {{params[t], 0, "param"}, {grads[t], 0, "grad"}, {m[t], 0, "m"}, {v[t], 0, "v"}};
+    int32_t st = check_align(rs, 4);
+    if (st != KRON_OK) return st;
+    const size_t by = (size_t)numel[t] * 4;
+    const Range outs[3] = {{params[t], by, "param"}, {m[t], by, "m"}, {v[t], by, "v"}};
+    const Range ins[1] = {{grads[t], by, "grad"}};
+    if ((st = check_alias(outs, 3, ins, 1)) != KRON_OK) return st;
+  }
+  const double bc1 = 1.0 - std::pow(beta1, (double)step);
+  const double bc2 = 1.0 - std::pow(beta2, (double)step);
+  kron::AdamHyper hp{(float)lr, (float)beta1, (float)(1.0 - beta1), (float)beta2, (float)(1.0 - beta2),
+                     (float)eps, (float)(1.0 / bc1), (float)(1.0 / bc2)};
+  for (int32_t t0 = 0; t0 < ntensors; t0 += kron::kAdamMaxPerLaunch) {
+    kron::AdamBatch batch{};
+    int64_t maxn = 0;
+    for (int32_t t = t0; t < ntensors && t < t0 + kron::kAdamMaxPerLaunch; ++t) {
+      if (numel[t] == 0) continue;
+      kron::AdamTensor& T = batch.t[batch.count++];
+      T.p = params[t]; T.g = grads[t]; T.m = m[t]; T.v = v[t]; T.numel = numel[t];
+      T.l1 = l1 ? l1[t] : 0.f;
+      if (numel[t] > maxn) maxn = numel[t];
+    }
+    hipError_t e = kron::launch_adam(batch, maxn, hp, stream);
+    if (e != hipSuccess) return hip_fail(e, "kron_adam_l1_step launch");
+  }
+  return ok();
+}
+
+size_t kron_head_ce_workspace_bytes(int64_t N, int32_t K, int32_t C) {
+  if (N < 0 || K < 1 || C < 1) return 0;
+  const int G = kron::head_groups(N);
+  const size_t floats = (size_t)N * C + (size_t)N + (size_t)G * ((size_t)K * C + C + 1);
+  return ((floats * 4 + 255) & ~size_t(255)) + 256;
+}
+
+int32_t kron_head_ce(int64_t N, int32_t K, int32_t C, const float* h, const float* Wh, const float* bh,
+                     const int64_t* labels, float* loss, float* dh, float* dWh, float* dbh, uint32_t flags,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (N < 0 || N > kMaxRows) return fail(KRON_E_SHAPE, "N = %lld out of range", (long long)N);
+  if (K < 1 || C < 1) return fail(KRON_E_SHAPE, "K and C must be >= 1");
+  if (C > 64 || K > 8192 || (int64_t)K * C > 16384)
+    return fail(KRON_E_UNSUPPORTED, "K = %d, C = %d beyond the limits (C <= 64, K <= 8192, K*C <= 16384)", K, C);
+  if (flags & ~KRON_DX_RELU_MASK) return fail(KRON_E_ARG, "unknown flag bits 0x%x", flags);
+  if (!Wh || !bh || !loss || !dWh || !dbh) return fail(KRON_E_NULL, "Wh, bh, loss, dWh and dbh are required");
+  if (N > 0 && (!h || !labels)) return fail(KRON_E_NULL, "h and labels are required when N > 0");
+  const size_t need = kron_head_ce_workspace_bytes(N, K, C);
+  if (!workspace || workspace_bytes < need)
+    return fail(KRON_E_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if (((uintptr_t)workspace & 255u) != 0) return fail(KRON_E_ALIGN, "workspace is not 256-byte aligned");
+  const Range ins[5] = {{h, (size_t)N * K * 4, "h"},      {Wh, (size_t)K * C * 4, "Wh"}, {bh, (size_t)C * 4, "bh"},
+                        {labels, (size_t)N * 8, "labels"}, {workspace, need, "workspace"}};
+  const Range outs[4] = {{loss, 4, "loss"}, {dh, (size_t)N * K * 4, "dh"}, {dWh, (size_t)K * C * 4, "dWh"},
+                         {dbh, (size_t)C * 4, "dbh"}};
+  int32_t st;
+  if ((st = check_align(ins, 5)) != KRON_OK || (st = check_align(outs, 4)) != KRON_OK) return st;
+  if ((st = check_alias(outs, 4, ins, 5)) != KRON_OK) return st;
+  kron::HeadArgs a{};
+  a.N = N; a.K = K; a.C = C; a.flags = flags; a.h = h; a.W = Wh; a.b = bh; a.labels = labels;
+  a.loss = loss; a.dh = dh; a.dW = dWh; a.db = dbh;
+  a.dz = (float*)workspace;
+  const size_t dz_floats = ((size_t)N * C + (size_t)N + 63) & ~size_t(63);
+  a.part = a.dz + dz_floats;
+  hipError_t e = kron::launch_head(a, kron::head_groups(N), stream);
+  if (e != hipSuccess) return hip_fail(e, "kron_head_ce launch");
+  return ok();
+}
+
+}  // extern "C"

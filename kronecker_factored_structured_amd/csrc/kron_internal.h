@@ -1,0 +1,130 @@
+// Internal declarations of libkron: launchers implemented in the .hip files and
+// called by the C-ABI layer (kron_api.cpp).  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+#include "kron.h"
+
+namespace kron {
+
+// ---------------------------------------------------------------------------------
+// Column reduction of per-workgroup partial sums: part is G x PW fp32 (row g holds
+// workgroup g's partial sums); column c is summed over g in a fixed order in fp64 and
+// written, scaled, to the segment that covers c.
+// ---------------------------------------------------------------------------------
+struct RedSeg {
+  float* dst;     // NULL: skip this segment
+  int32_t count;  // columns in this segment
+  float scale;
+};
+constexpr int kMaxRedSeg = 4;
+struct RedPlan {
+  RedSeg seg[kMaxRedSeg];
+  int32_t nseg;
+};
+hipError_t launch_column_reduce(const float* part, int32_t G, int32_t PW, const RedPlan& plan,
+                                hipStream_t stream);
+
+// ---------------------------------------------------------------------------------
+// Kronecker layer.
+// ---------------------------------------------------------------------------------
+struct LayerArgs {
+  int64_t N;
+  int32_t p, q, m, n, r;
+  uint32_t flags;
+  const float* x;
+  const float* S;
+  const float* A;
+  const float* B;
+  const float* bias;
+  const float* dy;
+  float* y;
+  float* dx;
+  float* dS;
+  float* dA;
+  float* dB;
+  float* dbias;
+  float* part;   // workspace: G x PW partial sums
+};
+
+// Partial-sum width of one workgroup: r*m*n (dB) + r*p*q (dC) + q*n (dbias).
+inline int64_t partial_width(int64_t p, int64_t q, int64_t m, int64_t n, int64_t r) {
+  return r * m * n + r * p * q + q * n;
+}
+
+// Generic path: any shape whose per-tile working set fits in LDS.
+int generic_fwd_rows_per_tile(int p, int q, int m, int n);        // 0: unsupported
+int generic_bwd_rows_per_tile(int p, int q, int m, int n, bool want_dx);
+int generic_bwd_groups(int64_t N, int T);
+hipError_t launch_fwd_generic(const LayerArgs& a, hipStream_t s);
+hipError_t launch_bwd_generic(const LayerArgs& a, int G, hipStream_t s);
+
+// Epilogue after the column reduction left dC_i in dA: dS = sum_i A_i o dC_i and
+// dA_i = S o dC_i (only launched when S is given).
+hipError_t launch_bwd_epilogue(const LayerArgs& a, hipStream_t s);
+
+
+// ---------------------------------------------------------------------------------
+// Kronecker-sparse matmul.
+// ---------------------------------------------------------------------------------
+struct KSArgs {
+  int64_t N;
+  int32_t a, b, c, d;
+  int32_t dtype;   // KRON_F32 / KRON_BF16
+  const void* x;
+  const void* vals;
+  float* y;
+};
+bool ks_supported(int a, int b, int c, int d);
+hipError_t launch_ks(const KSArgs& k, hipStream_t s);
+
+// ---------------------------------------------------------------------------------
+// Adam + l1.
+// ---------------------------------------------------------------------------------
+struct AdamTensor {
+  float* p;
+  const float* g;
+  float* m;
+  float* v;
+  int64_t numel;
+  float l1;
+  float pad_;
+};
+constexpr int kAdamMaxPerLaunch = 64;
+struct AdamBatch {
+  AdamTensor t[kAdamMaxPerLaunch];
+  int32_t count;
+  int32_t pad_;
+};
+// Hyper-parameters rounded once to fp32 from host doubles.
+struct AdamHyper {
+  float lr, beta1, one_minus_beta1, beta2, one_minus_beta2, eps, inv_bc1, inv_bc2;
+};
+hipError_t launch_adam(const AdamBatch& b, int64_t max_numel, const AdamHyper& h, hipStream_t s);
+
+// ---------------------------------------------------------------------------------
+// Dense head + softmax cross-entropy.
+// ---------------------------------------------------------------------------------
+struct HeadArgs {
+  int64_t N;
+  int32_t K, C;
+  uint32_t flags;
+  const float* h;
+  const float* W;
+  const float* b;
+  const int64_t* labels;
+  float* loss;
+  float* dh;
+  float* dW;
+  float* db;
+  float* dz;     // workspace: N x C
+  float* part;   // workspace: G x (K*C + C + 1)
+};
+int head_groups(int64_t N);
+int64_t head_rows_per_group(int64_t N);
+hipError_t launch_head(const HeadArgs& a, int G, hipStream_t s);
+
+}  // namespace kron

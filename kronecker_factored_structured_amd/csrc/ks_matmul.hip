@@ -1,0 +1,83 @@
+// Kronecker-sparse matmul Y = X K, K with support I_a (x) 1_{b x c} (x) I_d
+// ("Fast Inference with Kronecker-Sparse Matrices", abstract: supports that are
+// Kronecker products of identity and all-ones blocks).
+//
+// Index map (row-major Kronecker indices): input column (al*b + be)*d + de, output
+// column (al*c + ga)*d + de, value vals[al][de][be][ga].  For a fixed alpha the input
+// columns form one contiguous slab of b*d floats per row and the output columns one
+// contiguous slab of c*d floats, so the kernel is output-stationary without any
+// permutation pass: a workgroup stages T rows of one alpha-slab in LDS, de-interleaves
+// delta on chip by indexing, and writes its c*d outputs per row straight to y.
+#include "kron_internal.h"
+
+namespace kron {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr size_t kKsLds = 64 * 1024;
+
+__device__ __forceinline__ float load_in(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_in(const uint16_t* p, int64_t i) {
+  return __uint_as_float(((uint32_t)p[i]) << 16);
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void ks_generic_kernel(int64_t N, int a, int b, int c, int d,
+                                                              int T, const TIn* __restrict__ x,
+                                                              const TIn* __restrict__ vals,
+                                                              float* __restrict__ y) {
+  extern __shared__ float Xs[];   // T x (b*d)
+  const int al = blockIdx.y;
+  const int bd = b * d, cd = c * d;
+  const int64_t in = (int64_t)a * bd, outw = (int64_t)a * cd;
+  const int64_t row0 = (int64_t)blockIdx.x * T;
+  const int rows = (int)((N - row0) < T ? (N - row0) : T);
+  for (int e = threadIdx.x; e < rows * bd; e += kThreads) {
+    const int t = e / bd, k = e - t * bd;
+    Xs[e] = load_in(x, (row0 + t) * in + (int64_t)al * bd + k);
+  }
+  __syncthreads();
+  const TIn* V = vals + (int64_t)al * d * b * c;
+  for (int o = threadIdx.x; o < rows * cd; o += kThreads) {
+    const int t = o / cd, rem = o - t * cd, ga = rem / d, de = rem - ga * d;
+    const TIn* v = V + (int64_t)de * b * c + ga;
+    const float* xr = Xs + t * bd + de;
+    float acc = 0.f;
+    for (int be = 0; be < b; ++be) acc = fmaf(xr[be * d], load_in(v, (int64_t)be * c), acc);
+    y[(row0 + t) * outw + (int64_t)al * cd + rem] = acc;
+  }
+}
+
+int ks_rows_per_tile(int b, int d) {
+  const int64_t bd = (int64_t)b * d;
+  for (int T = 64; T >= 1; T /= 2)
+    if ((int64_t)T * bd * (int64_t)sizeof(float) <= (int64_t)kKsLds) return T;
+  return 0;
+}
+
+}  // namespace
+
+bool ks_supported(int a, int b, int c, int d) {
+  (void)a;
+  (void)c;
+  return ks_rows_per_tile(b, d) > 0;
+}
+
+hipError_t launch_ks(const KSArgs& k, hipStream_t s) {
+  const int T = ks_rows_per_tile(k.b, k.d);
+  if (T == 0) return hipErrorInvalidValue;
+  const int64_t gx = (k.N + T - 1) / T;
+  if (gx == 0) return hipSuccess;
+  const size_t lds = (size_t)T * k.b * k.d * sizeof(float);
+  dim3 grid((unsigned)gx, (unsigned)k.a);
+  if (k.dtype == KRON_F32) {
+    hipLaunchKernelGGL(ks_generic_kernel<float>, grid, dim3(kThreads), lds, s, k.N, k.a, k.b, k.c, k.d,
+                       T, (const float*)k.x, (const float*)k.vals, k.y);
+  } else {
+    hipLaunchKernelGGL(ks_generic_kernel<uint16_t>, grid, dim3(kThreads), lds, s, k.N, k.a, k.b, k.c,
+                       k.d, T, (const uint16_t*)k.x, (const uint16_t*)k.vals, k.y);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kron

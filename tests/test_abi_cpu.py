@@ -1,0 +1,175 @@
+"""The C-ABI library loads, exports every symbol include/kron.h declares, and rejects
+bad arguments on the host before any HIP call (CPU only: no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kronecker_factored_structured_amd import _lib
+from kronecker_factored_structured_amd._lib import KronShape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kron.h")
+
+# Fake, never-dereferenced device addresses: validation fails before any HIP call.
+BASE = 0x7f0000000000
+
+
+def P(off=0):
+    return ctypes.c_void_p(BASE + off)
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_python_exports():
+    assert set(header_functions()) == set(_lib.EXPORTS)
+
+
+def test_library_loads_and_exports_every_symbol():
+    L = _lib.lib()
+    for name in header_functions():
+        assert hasattr(L, name), name
+    assert L.kron_abi_version() == 1
+    assert _lib.status_str(0) == "ok"
+    assert _lib.status_str(_lib.KRON_E_WORKSPACE) == "workspace missing or too small"
+
+
+def check(shape):
+    return _lib.lib().kron_linear_check(ctypes.byref(shape))
+
+
+def test_shape_validation():
+    assert check(KronShape(20000, 32, 32, 32, 32, 4, 0)) == 0
+    assert check(KronShape(0, 1, 1, 1, 1, 1, 0)) == 0
+    assert check(KronShape(-1, 32, 32, 32, 32, 4, 0)) == _lib.KRON_E_SHAPE
+    assert check(KronShape(10, 0, 32, 32, 32, 4, 0)) == _lib.KRON_E_SHAPE
+    assert check(KronShape(10, 32, 32, 32, 32, 0, 0)) == _lib.KRON_E_SHAPE
+    assert check(KronShape(10, 32, 32, 32, 32, 65, 0)) == _lib.KRON_E_UNSUPPORTED
+    assert check(KronShape(10, 4096, 32, 32, 32, 1, 0)) == _lib.KRON_E_UNSUPPORTED  # in > 65536
+    assert check(KronShape(10, 32, 32, 32, 32, 4, 8)) == _lib.KRON_E_ARG           # unknown flag
+    assert "flag" in _lib.last_error()
+    assert _lib.lib().kron_linear_check(None) == _lib.KRON_E_NULL
+
+
+def test_workspace_size_depends_on_shape_only():
+    L = _lib.lib()
+    s = KronShape(20000, 32, 32, 32, 32, 4, 0)
+    w = L.kron_linear_bwd_workspace_bytes(ctypes.byref(s))
+    assert w > 0 and w % 256 == 0
+    assert L.kron_linear_bwd_workspace_bytes(ctypes.byref(s)) == w
+    assert L.kron_linear_bwd_workspace_bytes(ctypes.byref(KronShape(-1, 1, 1, 1, 1, 1, 0))) == 0
+
+
+def fwd(shape, x, S, A, B, bias, y):
+    return _lib.lib().kron_linear_fwd(ctypes.byref(shape), x, S, A, B, bias, y, None)
+
+
+def test_fwd_argument_errors():
+    s = KronShape(4, 2, 2, 2, 2, 1, 0)
+    MB = 1 << 20
+    assert fwd(s, P(0), None, None, P(2 * MB), None, P(3 * MB)) == _lib.KRON_E_NULL
+    assert fwd(s, None, None, P(MB), P(2 * MB), None, P(3 * MB)) == _lib.KRON_E_NULL
+    assert fwd(s, P(4), None, P(MB), P(2 * MB), None, P(3 * MB)) == _lib.KRON_E_ALIGN
+    assert fwd(s, P(0), None, P(MB), P(2 * MB), None, P(16)) == _lib.KRON_E_ALIAS   # y overlaps x
+    assert "overlaps" in _lib.last_error()
+    s2 = KronShape(4, 2, 2, 2, 2, 1, _lib.KRON_DX_RELU_MASK)
+    assert fwd(s2, P(0), None, P(MB), P(2 * MB), None, P(3 * MB)) == _lib.KRON_E_ARG
+    # N == 0 is a valid no-op and launches nothing
+    s0 = KronShape(0, 2, 2, 2, 2, 1, 0)
+    assert fwd(s0, None, None, P(MB), P(2 * MB), None, None) == 0
+
+
+def bwd(shape, x, S, A, B, dy, dx, dS, dA, dB, dbias, ws, wsb):
+    return _lib.lib().kron_linear_bwd(ctypes.byref(shape), x, S, A, B, dy, dx, dS, dA, dB, dbias, ws,
+                                      ctypes.c_size_t(wsb), None)
+
+
+def test_bwd_argument_errors():
+    MB = 1 << 20
+    s = KronShape(4, 2, 2, 2, 2, 1, 0)
+    need = _lib.lib().kron_linear_bwd_workspace_bytes(ctypes.byref(s))
+    args = dict(x=P(0), S=P(MB), A=P(2 * MB), B=P(3 * MB), dy=P(4 * MB), dx=P(5 * MB), dS=P(6 * MB),
+                dA=P(7 * MB), dB=P(8 * MB), dbias=P(9 * MB), ws=P(10 * MB), wsb=need)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return bwd(s, **a)
+
+    assert call(dS=None) == _lib.KRON_E_NULL                  # S given but no dS
+    assert call(S=None) == _lib.KRON_E_NULL                   # dS given but no S
+    assert call(dA=None) == _lib.KRON_E_NULL
+    assert call(ws=None) == _lib.KRON_E_WORKSPACE
+    assert call(wsb=need - 1) == _lib.KRON_E_WORKSPACE
+    assert call(ws=P(10 * MB + 16)) == _lib.KRON_E_ALIGN      # workspace must be 256-B aligned
+    assert call(dx=P(4 * MB)) == _lib.KRON_E_ALIAS            # dx overlaps dy
+    assert call(dB=P(7 * MB)) == _lib.KRON_E_ALIAS            # two outputs overlap
+    assert call(dA=P(10 * MB)) == _lib.KRON_E_ALIAS           # output overlaps workspace
+    sr = KronShape(4, 2, 2, 2, 2, 1, _lib.KRON_RELU_OUT)
+    a = dict(args)
+    assert bwd(sr, **a) == _lib.KRON_E_ARG
+    sm = KronShape(4, 2, 2, 2, 2, 1, _lib.KRON_DX_RELU_MASK)
+    a["dx"] = None
+    assert bwd(sm, **a) == _lib.KRON_E_ARG
+
+
+def test_ks_argument_errors():
+    L = _lib.lib()
+    MB = 1 << 20
+    assert L.ks_matmul(-1, 2, 48, 192, 4, 0, P(0), P(MB), P(2 * MB), None) == _lib.KRON_E_SHAPE
+    assert L.ks_matmul(8, 0, 48, 192, 4, 0, P(0), P(MB), P(2 * MB), None) == _lib.KRON_E_SHAPE
+    assert L.ks_matmul(8, 2, 48, 192, 4, 7, P(0), P(MB), P(2 * MB), None) == _lib.KRON_E_DTYPE
+    assert L.ks_matmul(8, 2, 48, 192, 4, 0, P(0), None, P(2 * MB), None) == _lib.KRON_E_NULL
+    assert L.ks_matmul(8, 2, 48, 192, 4, 0, P(2), P(MB), P(2 * MB), None) == _lib.KRON_E_ALIGN
+    assert L.ks_matmul(8, 2, 48, 192, 4, 0, P(0), P(MB), P(64), None) == _lib.KRON_E_ALIAS
+    assert L.ks_matmul(8, 2, 48, 65536, 4, 0, P(0), P(MB), P(2 * MB), None) == _lib.KRON_E_UNSUPPORTED
+    assert L.ks_matmul(0, 2, 48, 192, 4, 1, None, P(MB), None, None) == 0
+
+
+def test_adam_argument_errors():
+    L = _lib.lib()
+    arr = ctypes.c_void_p * 1
+    p, g, m, v = arr(BASE), arr(BASE + (1 << 20)), arr(BASE + (2 << 20)), arr(BASE + (3 << 20))
+    n = (ctypes.c_int64 * 1)(10)
+    assert L.kron_adam_l1_step(0, None, None, None, None, None, None, 1, 1e-3, 0.9, 0.999, 1e-8, None) == 0
+    assert L.kron_adam_l1_step(1, p, g, m, v, n, None, 0, 1e-3, 0.9, 0.999, 1e-8, None) == _lib.KRON_E_ARG
+    assert L.kron_adam_l1_step(1, p, g, m, v, n, None, 1, 1e-3, 1.0, 0.999, 1e-8, None) == _lib.KRON_E_ARG
+    assert L.kron_adam_l1_step(1, None, g, m, v, n, None, 1, 1e-3, 0.9, 0.999, 1e-8, None) == _lib.KRON_E_NULL
+    m2 = arr(BASE + 8)
+    assert L.kron_adam_l1_step(1, p, g, m2, v, n, None, 1, 1e-3, 0.9, 0.999, 1e-8, None) == _lib.KRON_E_ALIGN
+    m3 = arr(BASE + 16)      # m overlaps the parameter
+    assert L.kron_adam_l1_step(1, p, g, m3, v, n, None, 1, 1e-3, 0.9, 0.999, 1e-8, None) == _lib.KRON_E_ALIAS
+
+
+def test_head_argument_errors():
+    L = _lib.lib()
+    MB = 1 << 20
+    need = L.kron_head_ce_workspace_bytes(100, 1024, 10)
+    assert need > 0
+    args = [100, 1024, 10, P(0), P(MB), P(2 * MB), P(3 * MB), P(4 * MB), P(5 * MB), P(6 * MB), P(7 * MB), 0,
+            P(8 * MB), ctypes.c_size_t(need), None]
+    bad = list(args); bad[2] = 65
+    assert L.kron_head_ce(*bad) == _lib.KRON_E_UNSUPPORTED
+    bad = list(args); bad[13] = ctypes.c_size_t(need - 1)
+    assert L.kron_head_ce(*bad) == _lib.KRON_E_WORKSPACE
+    bad = list(args); bad[11] = 1
+    assert L.kron_head_ce(*bad) == _lib.KRON_E_ARG
+    bad = list(args); bad[7] = None
+    assert L.kron_head_ce(*bad) == _lib.KRON_E_NULL
+    bad = list(args); bad[8] = P(0)   # dh overlaps h
+    assert L.kron_head_ce(*bad) == _lib.KRON_E_ALIAS
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    import kronecker_factored_structured_amd as K
+    x = torch.zeros(4, 4)
+    A = torch.zeros(1, 2, 2)
+    B = torch.zeros(1, 2, 2)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        K.kron_linear_fwd(x, None, A, B)

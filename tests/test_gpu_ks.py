@@ -1,0 +1,97 @@
+"""GPU parity of ks_matmul (through the C ABI) against the fp64 oracle: fp32 and bf16
+inputs (fp32 accumulation and output), support pattern bit-exact."""
+import numpy as np
+import pytest
+
+from _harness import TOL_BF16, TOL_F32, dev, host, rel_err
+from oracle import ks as OKS
+from workloads import ks_inputs, vit_ks
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def K():
+    import kronecker_factored_structured_amd as mod
+    return mod
+
+
+def run(inp):
+    print(f"[ks] N={inp.x.shape[0]} abcd=({inp.a},{inp.b},{inp.c},{inp.d}) dtype={inp.dtype}", flush=True)
+    if inp.dtype == "bf16":
+        x = dev(inp.x_bits.view(np.int16)).view(torch.bfloat16)
+        v = dev(inp.vals_bits.view(np.int16)).view(torch.bfloat16)
+    else:
+        x, v = dev(inp.x), dev(inp.vals)
+    y = K().ks_matmul(x, v, inp.a, inp.b, inp.c, inp.d)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_vit_shape_full_size(dtype):
+    """(a,b,c,d) = (2,48,192,4), 25,216 rows."""
+    inp = vit_ks(dtype)
+    y = run(inp)
+    want = OKS.matmul(inp.x, inp.vals, inp.a, inp.b, inp.c, inp.d)
+    e = rel_err(host(y), want)
+    print(f"   rel error {e:.2e}", flush=True)
+    assert e <= (TOL_F32 if dtype == "f32" else TOL_BF16)
+    # both sides see the same bf16-rounded values, so fp32 accumulation is the only error
+    assert e <= TOL_F32
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("abcd", [(2, 48, 192, 4), (1, 5, 7, 1), (3, 4, 2, 5), (4, 1, 1, 3), (1, 64, 64, 1),
+                                  (2, 3, 130, 2)])
+def test_support_bit_exact(dtype, abcd):
+    """Identity input: Y = K exactly, values on the support and +0.0 off it."""
+    a, b, c, d = abcd
+    inp = ks_inputs(41, a * b * d, a, b, c, d, dtype)
+    eye = np.eye(a * b * d, dtype=np.float32)
+    if dtype == "bf16":
+        from workloads import bf16_bits
+        inp.x_bits = bf16_bits(eye)
+    inp.x = eye
+    y = run(inp)
+    want = OKS.dense(inp.vals, a, b, c, d).astype(np.float32)
+    got = y.cpu().numpy()
+    assert np.array_equal(got.view(np.int32), want.view(np.int32))
+    assert np.array_equal(got != 0, OKS.support(a, b, c, d) != 0)
+
+
+@pytest.mark.parametrize("N", [0, 1, 63, 1001])
+def test_ragged_rows(N):
+    inp = ks_inputs(42, N, 2, 48, 192, 4, "f32")
+    y = run(inp)
+    if N:
+        assert rel_err(host(y), OKS.matmul(inp.x, inp.vals, 2, 48, 192, 4)) <= TOL_F32
+    else:
+        assert y.shape == (0, 1536)
+
+
+def test_kron_layer_equals_chain_of_ks_on_gpu():
+    """The Kronecker layer factors as two KS matmuls: (I_p (x) B_all) then the C_i factor."""
+    from workloads import kron_inputs
+    p, q, m, n, r = 8, 6, 4, 5, 3
+    inp = kron_inputs(43, 300, p, q, m, n, r, s_mode="uniform_zeroed")
+    C = inp.S[None] * inp.A
+    V1 = np.zeros((p, 1, m, r * n), np.float32)
+    for j in range(p):
+        for i in range(r):
+            V1[j, 0, :, i * n:(i + 1) * n] = inp.B[i]
+    V2 = np.zeros((1, n, r * p, q), np.float32)
+    for b in range(n):
+        for j in range(p):
+            for i in range(r):
+                V2[0, b, j * r + i, :] = C[i, j, :]
+    z = K().ks_matmul(dev(inp.x), dev(V1), p, m, r * n, 1)
+    y2 = K().ks_matmul(z, dev(V2), 1, r * p, q, n)
+    y1 = K().kron_linear_fwd(dev(inp.x), dev(inp.S), dev(inp.A), dev(inp.B), None)
+    assert rel_err(host(y2), host(y1)) <= TOL_F32
