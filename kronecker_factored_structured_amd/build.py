@@ -24,6 +24,7 @@ ARCH = "gfx950"
 SOURCES = [
     "kron_api.cpp",
     "kron_generic.hip",
+    "kron_mfma.hip",
     "ks_matmul.hip",
     "adam_l1.hip",
     "head_ce.hip",
@@ -32,7 +33,7 @@ SOURCES = [
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wno-unused-function", "-Wno-cuda-compat",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

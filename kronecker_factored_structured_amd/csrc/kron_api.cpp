@@ -93,17 +93,23 @@ int32_t check_shape(const kron_shape_t* s) {
   return KRON_OK;
 }
 
+// Which backward kernel runs for a shape, with how many workgroups (= partial rows).
 struct BwdPlan {
-  int T;
+  bool mfma;
   int G;
   size_t ws_bytes;
 };
 
 BwdPlan bwd_plan(const kron_shape_t* s, bool want_dx) {
-  BwdPlan pl{0, 0, 0};
-  pl.T = kron::generic_bwd_rows_per_tile(s->p, s->q, s->m, s->n, want_dx);
-  if (pl.T == 0) return pl;
-  pl.G = kron::generic_bwd_groups(s->N, pl.T);
+  BwdPlan pl{false, 0, 0};
+  if (kron::mfma_bwd_supported(s->p, s->q, s->m, s->n, s->r)) {
+    pl.mfma = true;
+    pl.G = kron::mfma_bwd_groups(s->N);
+  } else {
+    const int T = kron::generic_bwd_rows_per_tile(s->p, s->q, s->m, s->n, want_dx);
+    if (T == 0) return pl;
+    pl.G = kron::generic_bwd_groups(s->N, T);
+  }
   const int64_t PW = kron::partial_width(s->p, s->q, s->m, s->n, s->r);
   pl.ws_bytes = (size_t)pl.G * (size_t)PW * sizeof(float);
   return pl;
@@ -176,7 +182,8 @@ int32_t kron_linear_fwd(const kron_shape_t* s, const float* x, const float* S, c
   kron::LayerArgs a{};
   a.N = s->N; a.p = s->p; a.q = s->q; a.m = s->m; a.n = s->n; a.r = s->r; a.flags = s->flags;
   a.x = x; a.S = S; a.A = A; a.B = B; a.bias = bias; a.y = y;
-  hipError_t e = kron::launch_fwd_generic(a, stream);
+  hipError_t e = kron::mfma_fwd_supported(a.p, a.q, a.m, a.n, a.r) ? kron::launch_fwd_mfma(a, stream)
+                                                                    : kron::launch_fwd_generic(a, stream);
   if (e != hipSuccess) return hip_fail(e, "kron_linear_fwd launch");
   return ok();
 }
@@ -212,7 +219,7 @@ int32_t kron_linear_bwd(const kron_shape_t* s, const float* x, const float* S, c
   a.dS = dS; a.dA = dA; a.dB = dB; a.dbias = dbias;
   a.part = (float*)workspace;
   const BwdPlan pl = bwd_plan(s, a.dx != nullptr);
-  hipError_t e = kron::launch_bwd_generic(a, pl.G, stream);
+  hipError_t e = pl.mfma ? kron::launch_bwd_mfma(a, pl.G, stream) : kron::launch_bwd_generic(a, pl.G, stream);
   if (e != hipSuccess) return hip_fail(e, "kron_linear_bwd launch");
   kron::RedPlan rp{};
   rp.nseg = 3;

@@ -62,6 +62,13 @@ int generic_bwd_groups(int64_t N, int T);
 hipError_t launch_fwd_generic(const LayerArgs& a, hipStream_t s);
 hipError_t launch_bwd_generic(const LayerArgs& a, int G, hipStream_t s);
 
+// Matrix-core path for the shapes in its table (see kron_mfma.hip).
+bool mfma_fwd_supported(int p, int q, int m, int n, int r);
+bool mfma_bwd_supported(int p, int q, int m, int n, int r);
+int mfma_bwd_groups(int64_t N);
+hipError_t launch_fwd_mfma(const LayerArgs& a, hipStream_t s);
+hipError_t launch_bwd_mfma(const LayerArgs& a, int G, hipStream_t s);
+
 // Epilogue after the column reduction left dC_i in dA: dS = sum_i A_i o dC_i and
 // dA_i = S o dC_i (only launched when S is given).
 hipError_t launch_bwd_epilogue(const LayerArgs& a, hipStream_t s);
