@@ -222,17 +222,14 @@ int32_t kron_linear_bwd(const kron_shape_t* s, const float* x, const float* S, c
   hipError_t e = pl.mfma ? kron::launch_bwd_mfma(a, pl.G, stream) : kron::launch_bwd_generic(a, pl.G, stream);
   if (e != hipSuccess) return hip_fail(e, "kron_linear_bwd launch");
   kron::RedPlan rp{};
-  rp.nseg = 3;
+  rp.nseg = 4;
   rp.seg[0] = kron::RedSeg{dB, s->r * s->m * s->n, 1.f};
   rp.seg[1] = kron::RedSeg{dA, s->r * s->p * s->q, 1.f};
-  rp.seg[2] = kron::RedSeg{dbias, s->q * s->n, 1.f};
+  rp.seg[2] = kron::RedSeg{dS, s->p * s->q, 1.f};
+  rp.seg[3] = kron::RedSeg{dbias, s->q * s->n, 1.f};
   const int32_t PW = (int32_t)kron::partial_width(s->p, s->q, s->m, s->n, s->r);
   e = kron::launch_column_reduce(a.part, pl.G, PW, rp, stream);
   if (e != hipSuccess) return hip_fail(e, "kron_linear_bwd reduce launch");
-  if (S) {
-    e = kron::launch_bwd_epilogue(a, stream);
-    if (e != hipSuccess) return hip_fail(e, "kron_linear_bwd epilogue launch");
-  }
   return ok();
 }
 

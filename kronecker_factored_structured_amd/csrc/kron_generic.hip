@@ -1,5 +1,5 @@
-// Generic (any-shape) kernels of the Kronecker-factored layer, the fixed-order column
-// reduction shared by every backward, and the dS/dA epilogue.
+// Generic (any-shape) kernels of the Kronecker-factored layer and the fixed-order
+// column reduction shared by every backward.
 //
 // Math (Kronecker layer tutorial, "The vec trick" and "The vec trick without the
 // loop"): with X_n the p x m row-major view of row x_n and C_i = S o A_i,
@@ -99,10 +99,11 @@ __global__ __launch_bounds__(kThreads) void bwd_generic_kernel(
   float* Ss = Cs + pq;           // p x q
   float* dXs = Ss + pq;          // T x in (only with dx)
   const int tid = threadIdx.x;
-  const int PW = r * mn + r * pq + out;
+  const int PW = (int)partial_width(p, q, m, n, r);
   float* pdB = part + (int64_t)blockIdx.x * PW;
-  float* pdC = pdB + r * mn;
-  float* pdb = pdC + r * pq;
+  float* pdC = pdB + r * mn;     // dC_i during the loop, dA_i at the end
+  float* pdS = pdC + r * pq;
+  float* pdb = pdS + pq;
   for (int e = tid; e < PW; e += kThreads) pdB[e] = 0.f;
   if (S)
     for (int e = tid; e < pq; e += kThreads) Ss[e] = S[e];
@@ -181,50 +182,78 @@ __global__ __launch_bounds__(kThreads) void bwd_generic_kernel(
       }
     }
   }
+  // this workgroup's dC_i -> its shares of dA_i = S o dC_i and dS = sum_i A_i o dC_i
+  __syncthreads();
+  for (int e = tid; e < pq; e += kThreads) {
+    const float sv = S ? S[e] : 1.f;
+    float ds = 0.f;
+    for (int i = 0; i < r; ++i) {
+      const float dc = pdC[i * pq + e];
+      ds = fmaf(A[(int64_t)i * pq + e], dc, ds);
+      pdC[i * pq + e] = sv * dc;
+    }
+    pdS[e] = S ? ds : 0.f;
+  }
 }
 
-// part is G x PW; block (64, 8): threadIdx.x picks a column, threadIdx.y a stride-8
-// subset of the G rows; fp64 sums are combined in a fixed tree.
-__global__ __launch_bounds__(512) void column_reduce_kernel(const float* __restrict__ part, int G,
-                                                            int PW, RedPlan plan) {
-  __shared__ double red[8][64];
-  const int col = blockIdx.x * 64 + threadIdx.x;
-  double s = 0.0;
-  if (col < PW)
-    for (int g = threadIdx.y; g < G; g += 8) s += (double)part[(int64_t)g * PW + col];
-  red[threadIdx.y][threadIdx.x] = s;
-  __syncthreads();
-  if (threadIdx.y < 4) red[threadIdx.y][threadIdx.x] += red[threadIdx.y + 4][threadIdx.x];
-  __syncthreads();
-  if (threadIdx.y < 2) red[threadIdx.y][threadIdx.x] += red[threadIdx.y + 2][threadIdx.x];
-  __syncthreads();
-  if (threadIdx.y == 0 && col < PW) {
-    const double tot = red[0][threadIdx.x] + red[1][threadIdx.x];
-    int c = col;
-    for (int k = 0; k < plan.nseg; ++k) {
-      if (c < plan.seg[k].count) {
-        if (plan.seg[k].dst) plan.seg[k].dst[c] = (float)(tot * (double)plan.seg[k].scale);
-        break;
+// part is G x PW.  Block (16, 16): threadIdx.x picks VEC consecutive columns (read as one
+// vector), threadIdx.y the rows g = threadIdx.y (mod 16) with four loads in flight per
+// step.  The fp64 per-thread sums are combined in a fixed tree, so the result does not
+// depend on timing.
+template <int VEC>
+__global__ __launch_bounds__(256) void column_reduce_kernel(const float* __restrict__ part, int G, int PW,
+                                                            RedPlan plan) {
+  typedef float fv __attribute__((ext_vector_type(VEC)));
+  __shared__ double red[16][16 * VEC];
+  const int col0 = (blockIdx.x * 16 + threadIdx.x) * VEC;
+  const int ty = threadIdx.y;
+  double s[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) s[v] = 0.0;
+  if (col0 < PW) {
+    const float* p = part + col0;
+    auto ld = [&](int g) { return *reinterpret_cast<const fv*>(p + (int64_t)g * PW); };
+    int g = ty;
+    for (; g + 48 < G; g += 64) {
+      const fv a0 = ld(g), a1 = ld(g + 16), a2 = ld(g + 32), a3 = ld(g + 48);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        s[v] += (double)a0[v];
+        s[v] += (double)a1[v];
+        s[v] += (double)a2[v];
+        s[v] += (double)a3[v];
       }
-      c -= plan.seg[k].count;
+    }
+    for (; g < G; g += 16) {
+      const fv a = ld(g);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) s[v] += (double)a[v];
     }
   }
-}
-
-__global__ __launch_bounds__(256) void bwd_epilogue_kernel(int pq, int r, const float* __restrict__ S,
-                                                           const float* __restrict__ A,
-                                                           float* __restrict__ dA,
-                                                           float* __restrict__ dS) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= pq) return;
-  const float s = S[e];
-  float acc = 0.f;
-  for (int i = 0; i < r; ++i) {
-    const float dc = dA[(int64_t)i * pq + e];
-    acc = fmaf(A[(int64_t)i * pq + e], dc, acc);
-    dA[(int64_t)i * pq + e] = s * dc;
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) red[ty][threadIdx.x * VEC + v] = s[v];
+  __syncthreads();
+  for (int h = 8; h >= 1; h /= 2) {
+    if (ty < h)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) red[ty][threadIdx.x * VEC + v] += red[ty + h][threadIdx.x * VEC + v];
+    __syncthreads();
   }
-  dS[e] = acc;
+  if (ty == 0) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      int c = col0 + v;
+      if (c >= PW) break;
+      const double tot = red[0][threadIdx.x * VEC + v];
+      for (int k = 0; k < plan.nseg; ++k) {
+        if (c < plan.seg[k].count) {
+          if (plan.seg[k].dst) plan.seg[k].dst[c] = (float)(tot * (double)plan.seg[k].scale);
+          break;
+        }
+        c -= plan.seg[k].count;
+      }
+    }
+  }
 }
 
 size_t fwd_lds_floats(int T, int p, int q, int m, int n) {
@@ -279,15 +308,13 @@ hipError_t launch_bwd_generic(const LayerArgs& a, int G, hipStream_t s) {
 hipError_t launch_column_reduce(const float* part, int32_t G, int32_t PW, const RedPlan& plan,
                                 hipStream_t stream) {
   if (PW == 0) return hipSuccess;
-  hipLaunchKernelGGL(column_reduce_kernel, dim3((PW + 63) / 64), dim3(64, 8), 0, stream, part, G, PW,
-                     plan);
-  return hipGetLastError();
-}
-
-hipError_t launch_bwd_epilogue(const LayerArgs& a, hipStream_t s) {
-  const int pq = a.p * a.q;
-  hipLaunchKernelGGL(bwd_epilogue_kernel, dim3((pq + 255) / 256), dim3(256), 0, s, pq, a.r, a.S, a.A,
-                     a.dA, a.dS);
+  // vector loads need every row of the partial block 16-byte aligned
+  if (PW % 4 == 0 && ((uintptr_t)part & 15) == 0)
+    hipLaunchKernelGGL(column_reduce_kernel<4>, dim3((PW + 63) / 64), dim3(16, 16), 0, stream, part, G, PW,
+                       plan);
+  else
+    hipLaunchKernelGGL(column_reduce_kernel<1>, dim3((PW + 15) / 16), dim3(16, 16), 0, stream, part, G, PW,
+                       plan);
   return hipGetLastError();
 }
 

@@ -50,9 +50,14 @@ struct LayerArgs {
   float* part;   // workspace: G x PW partial sums
 };
 
-// Partial-sum width of one workgroup: r*m*n (dB) + r*p*q (dC) + q*n (dbias).
-inline int64_t partial_width(int64_t p, int64_t q, int64_t m, int64_t n, int64_t r) {
-  return r * m * n + r * p * q + q * n;
+// Partial sums of one backward workgroup, in this order:
+//   dB (r*m*n) | dA (r*p*q) | dS (p*q) | dbias (q*n)
+// A workgroup accumulates dC_i over its rows and turns it into its share of
+// dA_i = S o dC_i and dS = sum_i A_i o dC_i before writing (both are linear in dC), so
+// one fixed-order column reduction yields every parameter gradient.  The dS slot is
+// present (and zero) when S is absent, so the width depends on the shape only.
+__host__ __device__ inline int64_t partial_width(int64_t p, int64_t q, int64_t m, int64_t n, int64_t r) {
+  return r * m * n + r * p * q + p * q + q * n;
 }
 
 // Generic path: any shape whose per-tile working set fits in LDS.
@@ -69,9 +74,6 @@ int mfma_bwd_groups(int64_t N);
 hipError_t launch_fwd_mfma(const LayerArgs& a, hipStream_t s);
 hipError_t launch_bwd_mfma(const LayerArgs& a, int G, hipStream_t s);
 
-// Epilogue after the column reduction left dC_i in dA: dS = sum_i A_i o dC_i and
-// dA_i = S o dC_i (only launched when S is given).
-hipError_t launch_bwd_epilogue(const LayerArgs& a, hipStream_t s);
 
 
 // ---------------------------------------------------------------------------------

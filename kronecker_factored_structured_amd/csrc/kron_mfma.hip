@@ -18,22 +18,27 @@
 //            (contraction over b); dB_i contracts G_i over j, so G_i^T takes one trip
 //            through a per-wavefront LDS tile to swap its indices.
 // Contraction orders inside a K step are free as long as both operands agree; the
-// kernels use a(s,g) = g*SA + s for the a index (so a lane's X values are contiguous in
-// memory) and 4*s + g for the j and k indices read from LDS or memory.
+// kernels pick them so that each lane's values are contiguous where they are read.
 //
 // One wavefront processes one row at a time and all r ranks of it; workgroups are
-// persistent and stride over rows.  The factor operands (B_i and C_i in the exact lane
-// layouts the products need) are built once per workgroup in LDS.  Dimensions that are
-// not multiples of 16 (4 for contraction steps) are padded with zeros inside the tiles.
-// The backward keeps dC_i and dB_i accumulators in registers over all of a wavefront's
-// rows, combines the four wavefronts of a workgroup in LDS in a fixed order and writes one
-// partial sum per workgroup; the shared fixed-order column reduction finishes the sums.
+// persistent and stride over rows.  Each workgroup first stages B and S o A in LDS with
+// coalesced vector loads and then lays out operand tables: for every product, the exact
+// values each lane needs, chunk-interleaved ([chunk][lane][4 floats]) so that one
+// ds_read_b128 per chunk is contiguous across the wavefront (no bank conflicts).
+// Dimensions that are not multiples of 16 (4 for contraction steps) are padded with zeros
+// inside the tiles.  The backward keeps dC_i and dB_i accumulators in registers over all
+// of a wavefront's rows, combines the four wavefronts of a workgroup in LDS in a fixed
+// order, turns dC into its shares of dA and dS, and writes one partial row per workgroup;
+// the shared fixed-order column reduction finishes the sums.
+#include <atomic>
+
 #include "kron_internal.h"
 
 namespace kron {
 namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;   // four wavefronts
 constexpr int kWaves = kThreads / 64;
@@ -44,8 +49,9 @@ __device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// L contiguous floats with the widest aligned vector loads.
 template <int L>
-__device__ __forceinline__ void lds_load(float (&dst)[L], const float* src) {
+__device__ __forceinline__ void vload(float (&dst)[L], const float* src) {
   if constexpr (L % 4 == 0) {
 #pragma unroll
     for (int t = 0; t < L / 4; ++t) {
@@ -55,12 +61,51 @@ __device__ __forceinline__ void lds_load(float (&dst)[L], const float* src) {
   } else if constexpr (L % 2 == 0) {
 #pragma unroll
     for (int t = 0; t < L / 2; ++t) {
-      const float2 v = reinterpret_cast<const float2*>(src)[t];
-      dst[2 * t] = v.x; dst[2 * t + 1] = v.y;
+      const f2 v = reinterpret_cast<const f2*>(src)[t];
+      dst[2 * t] = v[0]; dst[2 * t + 1] = v[1];
     }
   } else {
 #pragma unroll
     for (int t = 0; t < L; ++t) dst[t] = src[t];
+  }
+}
+
+// Operand tables: a lane's L values are stored as L/W chunks of W floats,
+// [chunk][lane][W], so that a chunk read is contiguous across the wavefront.
+template <int L>
+constexpr int chunk_width() { return L % 4 == 0 ? 4 : (L % 2 == 0 ? 2 : 1); }
+
+template <int L>
+__device__ __forceinline__ void table_read(float (&dst)[L], const float* blk, int lane) {
+  constexpr int W = chunk_width<L>();
+#pragma unroll
+  for (int t = 0; t < L / W; ++t) {
+    if constexpr (W == 4) {
+      const f4 v = reinterpret_cast<const f4*>(blk)[t * 64 + lane];
+      dst[4 * t] = v[0]; dst[4 * t + 1] = v[1]; dst[4 * t + 2] = v[2]; dst[4 * t + 3] = v[3];
+    } else if constexpr (W == 2) {
+      const f2 v = reinterpret_cast<const f2*>(blk)[t * 64 + lane];
+      dst[2 * t] = v[0]; dst[2 * t + 1] = v[1];
+    } else {
+      dst[t] = blk[t * 64 + lane];
+    }
+  }
+}
+
+// Lay out table[i][tile][chunk][lane][w] (i < R, tile < T, L values per lane) from
+// val(i, tile, g, c, s) with s = chunk * W + w.
+template <int R, int T, int L, class F>
+__device__ __forceinline__ void build_table(float* tab, F val) {
+  constexpr int W = chunk_width<L>();
+  constexpr int total = R * T * 64 * L;
+  for (int e = threadIdx.x; e < total; e += kThreads) {
+    int r = e;
+    const int w = r % W; r /= W;
+    const int l = r % 64; r /= 64;
+    const int ch = r % (L / W); r /= (L / W);
+    const int tile = r % T;
+    const int i = r / T;
+    tab[e] = val(i, tile, l >> 4, l & 15, ch * W + w);
   }
 }
 
@@ -73,46 +118,97 @@ struct Dims {
   static constexpr int TB = (N + 15) / 16;  // over b (n)
   static constexpr int SA = (M + 3) / 4;    // K steps over a:  a = g*SA + s
   static constexpr int SK = (Q + 3) / 4;    // K steps over k:  k = 4*s + g
-  static constexpr int SJ = TJ * 4;         // K steps over j:  j = 4*s + g (padded p)
+  static constexpr int SJ = TJ * 4;         // K steps over j:  j = g*SJ + s (padded p)
   static constexpr int IN = P * M, OUT = Q * N;
-  // LDS operand tables (floats)
-  static constexpr int BOP = R * TB * 64 * SA;       // B_i[g*SA+s][16tb+c]
-  static constexpr int COPF = R * TK * 64 * SJ;      // C_i[16tj+4g+v][16tk+c]
-  static constexpr int COPG = R * TJ * 64 * SK;      // C_i[16tj+c][4s+g]
-  static constexpr int BOPX = R * TA * 64 * TB * 4;  // B_i[16ta+c][16tb+4g+v]
-  // per-wavefront G tile, row stride chosen so the four lane groups of a read hit
-  // different LDS bank halves
-  static constexpr int LDG = 16 * TB + ((TB % 2 == 0) ? 16 : 0);
-  static constexpr int GS = 16 * TJ * LDG;
-  static constexpr int PW = R * M * N + R * P * Q + Q * N;
-  static constexpr size_t FWD_LDS = (size_t)(BOP + COPF) * 4;
-  static constexpr size_t BWD_LDS_MAIN = (size_t)(BOP + COPG + BOPX + kWaves * GS) * 4;
-  static constexpr size_t BWD_LDS = BWD_LDS_MAIN > (size_t)PW * 4 ? BWD_LDS_MAIN : (size_t)PW * 4;
+  // operand tables (floats): per rank and tile, 64 lanes x L values
+  static constexpr int BOP = R * TB * 64 * SA;       // B_i[g*SA+s][16tb+c]       L = SA
+  static constexpr int COPF = R * TK * 64 * SJ;      // C_i[16tj+4g+v][16tk+c]    L = SJ (s = 4tj+v)
+  static constexpr int COPG = R * TJ * 64 * SK;      // C_i[16tj+c][4s+g]         L = SK
+  static constexpr int BOPX = R * TA * 64 * TB * 4;  // B_i[16ta+c][16tb+4g+v]    L = 4TB (s = 4tb+v)
+  // raw staging of B (R*M*N) and C = S o A (R*P*Q)
+  static constexpr int RAWB = R * M * N;
+  static constexpr int RAWC = (R * P * Q + 3) / 4 * 4;
+  static constexpr int RAW = RAWB + RAWC;
+  // per-wavefront G^T -> G tile: gs[b][j], row stride LDGT = 16*TJ + 4 (conflict-free
+  // b32 writes of a D tile and b128 reads of a lane's j run)
+  static constexpr int LDGT = 16 * TJ + 4;
+  static constexpr int GS = 16 * TB * LDGT;
+  static constexpr int PW = R * M * N + R * P * Q + P * Q + Q * N;   // see partial_width()
+  static constexpr int PWW = R * M * N + R * P * Q + Q * N;           // one wavefront's sums
+  // the forward stages the raw factors next to its tables when they fit, else builds the
+  // tables straight from global memory
+  static constexpr bool FWD_RAW = (size_t)(BOP + COPF + RAW) * 4 <= kMaxLds;
+  static constexpr int FWD_FLOATS = BOP + COPF + (FWD_RAW ? RAW : 0);
+  static constexpr int BWD_TABLES = BOP + COPG + BOPX;
+  static constexpr int BWD_SCRATCH = (kWaves * GS > RAW) ? kWaves * GS : RAW;
+  static constexpr int BWD_MAIN = BWD_TABLES + BWD_SCRATCH;
+  static constexpr size_t FWD_LDS = (size_t)FWD_FLOATS * 4;
+  static constexpr size_t BWD_LDS = (size_t)(BWD_MAIN > kWaves * PWW ? BWD_MAIN : kWaves * PWW) * 4;
   // registers held across a backward row (accumulators and per-row operands), in floats
-  static constexpr int BWD_REGS = R * TJ * TK * 4 + R * TA * TB * 4 + TK * TB * 4 + TJ * SA + TA * SJ +
-                                  TK * TB * 4 + TB * SK + TA * TJ * 4 + TB * TJ * 8;
+  static constexpr int ROW_REGS = TJ * SA + TA * SJ + TK * TB * 4 + TB * SK;
+  static constexpr int BWD_REGS =
+      R * TJ * TK * 4 + R * TA * TB * 4 + TK * TB * 4 + ROW_REGS + TA * TJ * 4 + TB * TJ * 8;
   static_assert(M % 4 == 0 && N % 4 == 0, "rows are moved as 4-float vectors");
   static constexpr bool FWD_OK = FWD_LDS <= kMaxLds;
-  static constexpr bool BWD_OK = BWD_LDS <= kMaxLds && BWD_REGS <= 400;
+  // thresholds measured against the compiler's allocation (no scratch below them)
+  static constexpr bool BWD_OK = BWD_LDS <= kMaxLds && BWD_REGS <= 360;
+  static constexpr bool BWD_PREFETCH = BWD_REGS + ROW_REGS <= 420;   // double-buffer the row operands
 };
 
-__device__ __forceinline__ float cval(const float* S, const float* A, int i, int j, int k, int P, int Q) {
-  const float a = A[(i * P + j) * Q + k];
-  return S ? S[j * Q + k] * a : a;
+// Stage B (as is) and C = S o A in LDS with coalesced 16-byte loads.
+template <class D>
+__device__ __forceinline__ void stage_raw(float* rB, float* rC, const float* __restrict__ B,
+                                          const float* __restrict__ S, const float* __restrict__ A) {
+  constexpr int PQ = D::P * D::Q;
+#pragma unroll 4
+  for (int e = threadIdx.x; e < D::RAWB / 4; e += kThreads)
+    reinterpret_cast<f4*>(rB)[e] = reinterpret_cast<const f4*>(B)[e];
+  if constexpr (PQ % 4 == 0) {
+#pragma unroll 4
+    for (int e = threadIdx.x; e < D::R * PQ / 4; e += kThreads) {
+      f4 a = reinterpret_cast<const f4*>(A)[e];
+      if (S) a *= reinterpret_cast<const f4*>(S)[e % (PQ / 4)];
+      reinterpret_cast<f4*>(rC)[e] = a;
+    }
+  } else {
+    for (int e = threadIdx.x; e < D::R * PQ; e += kThreads) rC[e] = S ? S[e % PQ] * A[e] : A[e];
+  }
 }
 
-// Fill the B-operand table of the forward's first product (also the A operand of the
-// backward's Z^T product): bop[i][tb][lane][s] = B_i[a = g*SA+s][b = 16tb+c].
 template <class D>
-__device__ void fill_bop(float* bop, const float* B) {
-  for (int e = threadIdx.x; e < D::BOP; e += kThreads) {
-    int t = e;
-    const int s = t % D::SA; t /= D::SA;
-    const int l = t % 64; t /= 64;
-    const int tb = t % D::TB; const int i = t / D::TB;
-    const int g = l >> 4, c = l & 15;
-    const int a = g * D::SA + s, b = 16 * tb + c;
-    bop[e] = (a < D::M && b < D::N) ? B[(i * D::M + a) * D::N + b] : 0.f;
+__device__ __forceinline__ float rawB(const float* rB, int i, int a, int b) {
+  return (a < D::M && b < D::N) ? rB[(i * D::M + a) * D::N + b] : 0.f;
+}
+template <class D>
+__device__ __forceinline__ float rawC(const float* rC, int i, int j, int k) {
+  return (j < D::P && k < D::Q) ? rC[(i * D::P + j) * D::Q + k] : 0.f;
+}
+
+// Wait, before the row loop, for the first row's prefetched operands.  The loop body
+// issues the next row's loads before the current row's stores, so on the loop's back
+// edge only stores are outstanding when the operands are consumed; without this wait the
+// loop head would merge that state with the preheader's (loads outstanding) and wait for
+// every store of the previous row.
+template <class T, int A, int B>
+__device__ __forceinline__ void settle(const T (&v)[A][B]) {
+#pragma unroll
+  for (int i = 0; i < A; ++i)
+#pragma unroll
+    for (int j = 0; j < B; ++j) asm volatile("" ::"v"(v[i][j]));
+}
+
+// X[j = 16tj+c][a = g*SA+s] of one row: SA contiguous floats per lane and tile.
+template <class D>
+__device__ __forceinline__ void load_xa(float (&xa)[D::TJ][D::SA], const float* xr, int g, int c) {
+#pragma unroll
+  for (int tj = 0; tj < D::TJ; ++tj) {
+    const int j = 16 * tj + c;
+    if (j < D::P) {
+      vload<D::SA>(xa[tj], xr + j * D::M + g * D::SA);
+    } else {
+#pragma unroll
+      for (int s = 0; s < D::SA; ++s) xa[tj][s] = 0.f;
+    }
   }
 }
 
@@ -125,18 +221,30 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
                                                             const float* __restrict__ bias,
                                                             float* __restrict__ y) {
   extern __shared__ float lds[];
-  float* bop = lds;
-  float* cop = bop + D::BOP;
-  fill_bop<D>(bop, B);
-  // cop[i][tk][lane][tj*4+v] = C_i[j = 16tj+4g+v][k = 16tk+c]
-  for (int e = threadIdx.x; e < D::COPF; e += kThreads) {
-    int t = e;
-    const int sv = t % D::SJ; t /= D::SJ;
-    const int l = t % 64; t /= 64;
-    const int tk = t % D::TK; const int i = t / D::TK;
-    const int g = l >> 4, c = l & 15;
-    const int j = 16 * (sv / 4) + 4 * g + (sv % 4), k = 16 * tk + c;
-    cop[e] = (j < D::P && k < D::Q) ? cval(Sm, A, i, j, k, D::P, D::Q) : 0.f;
+  float* bop = lds;              // B_i[g*SA+s][16tb+c]
+  float* cop = bop + D::BOP;     // C_i[16tj+4g+v][16tk+c]
+  if constexpr (D::FWD_RAW) {
+    float* rB = cop + D::COPF;
+    float* rC = rB + D::RAWB;
+    stage_raw<D>(rB, rC, B, Sm, A);
+    __syncthreads();
+    build_table<D::R, D::TB, D::SA>(bop, [&](int i, int tb, int g, int c, int s) {
+      return rawB<D>(rB, i, g * D::SA + s, 16 * tb + c);
+    });
+    build_table<D::R, D::TK, D::SJ>(cop, [&](int i, int tk, int g, int c, int sv) {
+      return rawC<D>(rC, i, 16 * (sv / 4) + 4 * g + (sv % 4), 16 * tk + c);
+    });
+  } else {
+    build_table<D::R, D::TB, D::SA>(bop, [&](int i, int tb, int g, int c, int s) {
+      const int a = g * D::SA + s, b = 16 * tb + c;
+      return (a < D::M && b < D::N) ? B[(i * D::M + a) * D::N + b] : 0.f;
+    });
+    build_table<D::R, D::TK, D::SJ>(cop, [&](int i, int tk, int g, int c, int sv) {
+      const int j = 16 * (sv / 4) + 4 * g + (sv % 4), k = 16 * tk + c;
+      if (j >= D::P || k >= D::Q) return 0.f;
+      const float a = A[(i * D::P + j) * D::Q + k];
+      return Sm ? Sm[j * D::Q + k] * a : a;
+    });
   }
   __syncthreads();
 
@@ -154,28 +262,15 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
   const bool relu = flags & KRON_RELU_OUT;
 
   for (int64_t row = (int64_t)blockIdx.x * kWaves + wave; row < N; row += (int64_t)gridDim.x * kWaves) {
-    const float* xr = x + row * D::IN;
     float xa[D::TJ][D::SA];   // X[j = 16tj+c][a = g*SA+s]
-#pragma unroll
-    for (int tj = 0; tj < D::TJ; ++tj) {
-      const int j = 16 * tj + c;
-      if (j < D::P && g * D::SA < D::M) {
-        lds_load<D::SA>(xa[tj], xr + j * D::M + g * D::SA);   // global load, same vector widths
-#pragma unroll
-        for (int s = 0; s < D::SA; ++s)
-          if (g * D::SA + s >= D::M) xa[tj][s] = 0.f;
-      } else {
-#pragma unroll
-        for (int s = 0; s < D::SA; ++s) xa[tj][s] = 0.f;
-      }
-    }
+    load_xa<D>(xa, x + row * D::IN, g, c);
     f4 acc[D::TB][D::TK];
 #pragma unroll
     for (int tb = 0; tb < D::TB; ++tb)
 #pragma unroll
       for (int tk = 0; tk < D::TK; ++tk) acc[tb][tk] = f4{0.f, 0.f, 0.f, 0.f};
 
-    // (ranks beyond four are not unrolled: the operand loads hoisted across an unrolled
+    // (ranks beyond four are not unrolled: the operand reads hoisted across an unrolled
     // rank loop would not fit the register file)
 #pragma unroll(D::R <= 4 ? D::R : 2)
     for (int i = 0; i < D::R; ++i) {
@@ -183,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
 #pragma unroll
       for (int tb = 0; tb < D::TB; ++tb) {
         float bo[D::SA];
-        lds_load<D::SA>(bo, bop + ((i * D::TB + tb) * 64 + lane) * D::SA);
+        table_read<D::SA>(bo, bop + (i * D::TB + tb) * 64 * D::SA, lane);
 #pragma unroll
         for (int tj = 0; tj < D::TJ; ++tj) {
           f4 t = f4{0.f, 0.f, 0.f, 0.f};
@@ -195,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
 #pragma unroll
       for (int tk = 0; tk < D::TK; ++tk) {
         float co[D::SJ];
-        lds_load<D::SJ>(co, cop + ((i * D::TK + tk) * 64 + lane) * D::SJ);
+        table_read<D::SJ>(co, cop + (i * D::TK + tk) * 64 * D::SJ, lane);
 #pragma unroll
         for (int tb = 0; tb < D::TB; ++tb)
 #pragma unroll
@@ -223,6 +318,42 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
   }
 }
 
+// The backward's per-row operands.
+template <class D>
+struct BwdRow {
+  float xa[D::TJ][D::SA];    // X[j = 16tj+c][a = g*SA+s]       B operand of Z^T
+  float xaj[D::TA][D::SJ];   // X[j = g*SJ+s][a = 16ta+c]       A operand of dB
+  f4 dyk[D::TK][D::TB];      // dY[k = 16tk+c][b = 16tb+4g+v]   B operand of dC
+  float dyb[D::TB][D::SK];   // dY[k = 4s+g][b = 16tb+c]        A operand of G^T
+};
+
+template <class D>
+__device__ __forceinline__ void load_bwd_row(BwdRow<D>& o, const float* xr, const float* dyr, int g, int c) {
+  load_xa<D>(o.xa, xr, g, c);
+#pragma unroll
+  for (int ta = 0; ta < D::TA; ++ta)
+#pragma unroll
+    for (int s = 0; s < D::SJ; ++s) {
+      const int j = g * D::SJ + s, a = 16 * ta + c;
+      o.xaj[ta][s] = (j < D::P && a < D::M) ? xr[j * D::M + a] : 0.f;
+    }
+#pragma unroll
+  for (int tk = 0; tk < D::TK; ++tk)
+#pragma unroll
+    for (int tb = 0; tb < D::TB; ++tb) {
+      const int k = 16 * tk + c, b0 = 16 * tb + 4 * g;
+      o.dyk[tk][tb] = (k < D::Q && b0 < D::N) ? *reinterpret_cast<const f4*>(dyr + k * D::N + b0)
+                                             : f4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+  for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+    for (int s = 0; s < D::SK; ++s) {
+      const int k = 4 * s + g, b = 16 * tb + c;
+      o.dyb[tb][s] = (k < D::Q && b < D::N) ? dyr[k * D::N + b] : 0.f;
+    }
+}
+
 template <class D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, const float* __restrict__ Sm,
@@ -232,31 +363,25 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
   float* bop = lds;                 // B_i[g*SA+s][16tb+c]        (A operand of Z^T)
   float* copg = bop + D::BOP;       // C_i[16tj+c][4s+g]          (B operand of G^T)
   float* bopx = copg + D::COPG;     // B_i[16ta+c][16tb+4g+v]     (A operand of dX^T)
-  float* gsall = bopx + D::BOPX;    // per-wavefront G tiles
-  fill_bop<D>(bop, B);
-  for (int e = threadIdx.x; e < D::COPG; e += kThreads) {
-    int t = e;
-    const int s = t % D::SK; t /= D::SK;
-    const int l = t % 64; t /= 64;
-    const int tj = t % D::TJ; const int i = t / D::TJ;
-    const int g = l >> 4, c = l & 15;
-    const int j = 16 * tj + c, k = 4 * s + g;
-    copg[e] = (j < D::P && k < D::Q) ? cval(Sm, A, i, j, k, D::P, D::Q) : 0.f;
-  }
-  for (int e = threadIdx.x; e < D::BOPX; e += kThreads) {
-    int t = e;
-    const int sv = t % (D::TB * 4); t /= D::TB * 4;
-    const int l = t % 64; t /= 64;
-    const int ta = t % D::TA; const int i = t / D::TA;
-    const int g = l >> 4, c = l & 15;
-    const int a = 16 * ta + c, b = 16 * (sv / 4) + 4 * g + (sv % 4);
-    bopx[e] = (a < D::M && b < D::N) ? B[(i * D::M + a) * D::N + b] : 0.f;
-  }
+  float* scratch = bopx + D::BOPX;  // raw factors while the tables are built, then G tiles
+  float* rB = scratch;
+  float* rC = rB + D::RAWB;
+  stage_raw<D>(rB, rC, B, Sm, A);
+  __syncthreads();
+  build_table<D::R, D::TB, D::SA>(bop, [&](int i, int tb, int g, int c, int s) {
+    return rawB<D>(rB, i, g * D::SA + s, 16 * tb + c);
+  });
+  build_table<D::R, D::TJ, D::SK>(copg, [&](int i, int tj, int g, int c, int s) {
+    return rawC<D>(rC, i, 16 * tj + c, 4 * s + g);
+  });
+  build_table<D::R, D::TA, D::TB * 4>(bopx, [&](int i, int ta, int g, int c, int sv) {
+    return rawB<D>(rB, i, 16 * ta + c, 16 * (sv / 4) + 4 * g + (sv % 4));
+  });
   __syncthreads();
 
   const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   const int wave = threadIdx.x >> 6;
-  float* gs = gsall + wave * D::GS;
+  float* gs = scratch + wave * D::GS;   // G[j][b] stored as gs[b * LDGT + j]
   const bool want_dx = dx != nullptr;
   const bool mask = flags & KRON_DX_RELU_MASK;
 
@@ -279,49 +404,33 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
 #pragma unroll
     for (int tb = 0; tb < D::TB; ++tb) db[tk][tb] = f4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t row = (int64_t)blockIdx.x * kWaves + wave; row < N; row += (int64_t)gridDim.x * kWaves) {
+  const int64_t stride = (int64_t)gridDim.x * kWaves;
+  int64_t row = (int64_t)blockIdx.x * kWaves + wave;
+  BwdRow<D> nx;   // the next row's operands, loaded while the current row computes
+  if constexpr (D::BWD_PREFETCH) {
+    if (row < N) load_bwd_row<D>(nx, x + row * D::IN, dy + row * D::OUT, g, c);
+    settle(nx.xa);
+    settle(nx.xaj);
+    settle(nx.dyk);
+    settle(nx.dyb);
+  }
+  for (; row < N; row += stride) {
     const float* xr = x + row * D::IN;
-    const float* dyr = dy + row * D::OUT;
-    float xa[D::TJ][D::SA];    // X[j = 16tj+c][a = g*SA+s]       B operand of Z^T
-    float xaj[D::TA][D::SJ];   // X[j = 4s+g][a = 16ta+c]         A operand of dB
-    f4 dyk[D::TK][D::TB];      // dY[k = 16tk+c][b = 16tb+4g+v]   B operand of dC
-    float dyb[D::TB][D::SK];   // dY[k = 4s+g][b = 16tb+c]        A operand of G^T
-#pragma unroll
-    for (int tj = 0; tj < D::TJ; ++tj) {
-      const int j = 16 * tj + c;
-      if (j < D::P && g * D::SA < D::M) {
-        lds_load<D::SA>(xa[tj], xr + j * D::M + g * D::SA);
-#pragma unroll
-        for (int s = 0; s < D::SA; ++s)
-          if (g * D::SA + s >= D::M) xa[tj][s] = 0.f;
-      } else {
-#pragma unroll
-        for (int s = 0; s < D::SA; ++s) xa[tj][s] = 0.f;
-      }
+    BwdRow<D> cur;
+    if constexpr (D::BWD_PREFETCH) {
+      cur = nx;
+      if (row + stride < N) load_bwd_row<D>(nx, x + (row + stride) * D::IN, dy + (row + stride) * D::OUT, g, c);
+    } else {
+      load_bwd_row<D>(cur, xr, dy + row * D::OUT, g, c);
     }
-#pragma unroll
-    for (int ta = 0; ta < D::TA; ++ta)
-#pragma unroll
-      for (int s = 0; s < D::SJ; ++s) {
-        const int j = 4 * s + g, a = 16 * ta + c;
-        xaj[ta][s] = (j < D::P && a < D::M) ? xr[j * D::M + a] : 0.f;
-      }
+    const auto& xa = cur.xa;
+    const auto& xaj = cur.xaj;
+    const auto& dyk = cur.dyk;
+    const auto& dyb = cur.dyb;
 #pragma unroll
     for (int tk = 0; tk < D::TK; ++tk)
 #pragma unroll
-      for (int tb = 0; tb < D::TB; ++tb) {
-        const int k = 16 * tk + c, b0 = 16 * tb + 4 * g;
-        dyk[tk][tb] = (k < D::Q && b0 < D::N) ? *reinterpret_cast<const f4*>(dyr + k * D::N + b0)
-                                             : f4{0.f, 0.f, 0.f, 0.f};
-        db[tk][tb] += dyk[tk][tb];
-      }
-#pragma unroll
-    for (int tb = 0; tb < D::TB; ++tb)
-#pragma unroll
-      for (int s = 0; s < D::SK; ++s) {
-        const int k = 4 * s + g, b = 16 * tb + c;
-        dyb[tb][s] = (k < D::Q && b < D::N) ? dyr[k * D::N + b] : 0.f;
-      }
+      for (int tb = 0; tb < D::TB; ++tb) db[tk][tb] += dyk[tk][tb];
 
     f4 dxt[D::TA][D::TJ];       // dX^T[a = 16ta+4g+v][j = 16tj+c]
 #pragma unroll
@@ -336,7 +445,7 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
 #pragma unroll
       for (int tb = 0; tb < D::TB; ++tb) {
         float bo[D::SA];
-        lds_load<D::SA>(bo, bop + ((i * D::TB + tb) * 64 + lane) * D::SA);
+        table_read<D::SA>(bo, bop + (i * D::TB + tb) * 64 * D::SA, lane);
 #pragma unroll
         for (int tj = 0; tj < D::TJ; ++tj) {
           f4 t = f4{0.f, 0.f, 0.f, 0.f};
@@ -359,7 +468,7 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
 #pragma unroll
       for (int tj = 0; tj < D::TJ; ++tj) {
         float co[D::SK];
-        lds_load<D::SK>(co, copg + ((i * D::TJ + tj) * 64 + lane) * D::SK);
+        table_read<D::SK>(co, copg + (i * D::TJ + tj) * 64 * D::SK, lane);
 #pragma unroll
         for (int tb = 0; tb < D::TB; ++tb) {
           f4 t = f4{0.f, 0.f, 0.f, 0.f};
@@ -368,12 +477,20 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
           gt[tb][tj] = t;
         }
       }
+      // G^T -> LDS (gs[b][j]) first, so that the dX^T products below cover the round trip
+#pragma unroll
+      for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+        for (int tj = 0; tj < D::TJ; ++tj)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) gs[(16 * tb + 4 * g + v) * D::LDGT + 16 * tj + c] = gt[tb][tj][v];
+      __builtin_amdgcn_wave_barrier();
       // dX^T[a][j] += sum_b B_i[a][b] G^T[b][j]
       if (want_dx) {
 #pragma unroll
         for (int ta = 0; ta < D::TA; ++ta) {
           float bx[D::TB * 4];
-          lds_load<D::TB * 4>(bx, bopx + ((i * D::TA + ta) * 64 + lane) * (D::TB * 4));
+          table_read<D::TB * 4>(bx, bopx + (i * D::TA + ta) * 64 * D::TB * 4, lane);
 #pragma unroll
           for (int tj = 0; tj < D::TJ; ++tj)
 #pragma unroll
@@ -382,21 +499,16 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
               for (int v = 0; v < 4; ++v) dxt[ta][tj] = mfma(bx[tb * 4 + v], gt[tb][tj][v], dxt[ta][tj]);
         }
       }
-      // G^T -> LDS as G[j][b]; dB_i[a][b] += sum_j X[j][a] G[j][b]
+      // dB_i[a][b] += sum_j X[j][a] G[j][b] with j = g*SJ + s
 #pragma unroll
-      for (int tb = 0; tb < D::TB; ++tb)
+      for (int tb = 0; tb < D::TB; ++tb) {
+        float gv[D::SJ];
+        vload<D::SJ>(gv, gs + (16 * tb + c) * D::LDGT + g * D::SJ);
 #pragma unroll
-        for (int tj = 0; tj < D::TJ; ++tj)
-          *reinterpret_cast<f4*>(gs + (16 * tj + c) * D::LDG + 16 * tb + 4 * g) = gt[tb][tj];
-      __builtin_amdgcn_wave_barrier();
+        for (int s = 0; s < D::SJ; ++s)
 #pragma unroll
-      for (int tb = 0; tb < D::TB; ++tb)
-#pragma unroll
-        for (int s = 0; s < D::SJ; ++s) {
-          const float gv = gs[(4 * s + g) * D::LDG + 16 * tb + c];
-#pragma unroll
-          for (int ta = 0; ta < D::TA; ++ta) dB[i][ta][tb] = mfma(xaj[ta][s], gv, dB[i][ta][tb]);
-        }
+          for (int ta = 0; ta < D::TA; ++ta) dB[i][ta][tb] = mfma(xaj[ta][s], gv[s], dB[i][ta][tb]);
+      }
       __builtin_amdgcn_wave_barrier();
     }
     if (want_dx) {
@@ -419,56 +531,64 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
     }
   }
 
-  // Combine the wavefronts' partial sums in LDS in wave order, then write this
-  // workgroup's partial row: [dB (R*M*N) | dC (R*P*Q) | dbias (Q*N)].
+  // Every wavefront stores its partial sums in its own LDS block at once, then the
+  // workgroup adds the blocks in wave order and writes its partial row
+  //   [dB (R*M*N) | dA (R*P*Q) | dS (P*Q) | dbias (Q*N)]
+  // turning dC into its shares of dA_i = S o dC_i and dS = sum_i A_i o dC_i on the way.
   __syncthreads();
-  float* red = lds;
-  for (int w = 0; w < kWaves; ++w) {
-    if (wave == w) {
+  constexpr int MN = D::M * D::N, PQ = D::P * D::Q, QN = D::Q * D::N;
+  float* red = lds + wave * D::PWW;   // [dB | dC | dbias] of this wavefront
 #pragma unroll
-      for (int i = 0; i < D::R; ++i) {
+  for (int i = 0; i < D::R; ++i) {
 #pragma unroll
-        for (int ta = 0; ta < D::TA; ++ta)
+    for (int ta = 0; ta < D::TA; ++ta)
 #pragma unroll
-          for (int tb = 0; tb < D::TB; ++tb)
+      for (int tb = 0; tb < D::TB; ++tb)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int a = 16 * ta + 4 * g + v, b = 16 * tb + c;
-              if (a < D::M && b < D::N) {
-                float* p = red + (i * D::M + a) * D::N + b;
-                *p = (w == 0) ? dB[i][ta][tb][v] : *p + dB[i][ta][tb][v];
-              }
-            }
+        for (int v = 0; v < 4; ++v) {
+          const int a = 16 * ta + 4 * g + v, b = 16 * tb + c;
+          if (a < D::M && b < D::N) red[i * MN + a * D::N + b] = dB[i][ta][tb][v];
+        }
 #pragma unroll
-        for (int tj = 0; tj < D::TJ; ++tj)
-#pragma unroll
-          for (int tk = 0; tk < D::TK; ++tk)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int j = 16 * tj + 4 * g + v, k = 16 * tk + c;
-              if (j < D::P && k < D::Q) {
-                float* p = red + D::R * D::M * D::N + (i * D::P + j) * D::Q + k;
-                *p = (w == 0) ? dC[i][tj][tk][v] : *p + dC[i][tj][tk][v];
-              }
-            }
-      }
+    for (int tj = 0; tj < D::TJ; ++tj)
 #pragma unroll
       for (int tk = 0; tk < D::TK; ++tk)
 #pragma unroll
-        for (int tb = 0; tb < D::TB; ++tb)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int k = 16 * tk + c, b = 16 * tb + 4 * g + v;
-            if (k < D::Q && b < D::N) {
-              float* p = red + D::R * (D::M * D::N + D::P * D::Q) + k * D::N + b;
-              *p = (w == 0) ? db[tk][tb][v] : *p + db[tk][tb][v];
-            }
-          }
-    }
-    __syncthreads();
+        for (int v = 0; v < 4; ++v) {
+          const int j = 16 * tj + 4 * g + v, k = 16 * tk + c;
+          if (j < D::P && k < D::Q) red[D::R * MN + i * PQ + j * D::Q + k] = dC[i][tj][tk][v];
+        }
   }
+#pragma unroll
+  for (int tk = 0; tk < D::TK; ++tk)
+#pragma unroll
+    for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int k = 16 * tk + c, b = 16 * tb + 4 * g + v;
+        if (k < D::Q && b < D::N) red[D::R * (MN + PQ) + k * D::N + b] = db[tk][tb][v];
+      }
+  __syncthreads();
   float* out = part + (int64_t)blockIdx.x * D::PW;
-  for (int e = threadIdx.x; e < D::PW; e += kThreads) out[e] = red[e];
+  auto wsum = [&](int e) {
+    float t = lds[e];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) t += lds[w * D::PWW + e];
+    return t;
+  };
+  for (int e = threadIdx.x; e < D::R * MN; e += kThreads) out[e] = wsum(e);
+  for (int e = threadIdx.x; e < PQ; e += kThreads) {
+    const float sv = Sm ? Sm[e] : 1.f;
+    float ds = 0.f;
+#pragma unroll
+    for (int i = 0; i < D::R; ++i) {
+      const float dcv = wsum(D::R * MN + i * PQ + e);
+      ds = fmaf(A[i * PQ + e], dcv, ds);
+      out[D::R * MN + i * PQ + e] = sv * dcv;
+    }
+    out[D::R * (MN + PQ) + e] = Sm ? ds : 0.f;
+  }
+  for (int e = threadIdx.x; e < QN; e += kThreads) out[D::R * (MN + PQ) + PQ + e] = wsum(D::R * (MN + PQ) + e);
 }
 
 // ---------------------------------------------------------------------------------
@@ -477,26 +597,53 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
 struct Entry {
   int p, q, m, n, r;
   bool fwd_ok, bwd_ok;
-  size_t fwd_lds, bwd_lds;
   void (*fwd)(const LayerArgs&, int, hipStream_t);
   void (*bwd)(const LayerArgs&, int, hipStream_t);
 };
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// The forward is persistent: as many workgroups as fit on the device at once (and no
+// more than one row per wavefront), each wavefront striding over rows.
 template <class D>
-void run_fwd(const LayerArgs& a, int grid, hipStream_t s) {
+void run_fwd(const LayerArgs& a, int max_grid, hipStream_t s) {
   if constexpr (D::FWD_OK) {
-    (void)hipFuncSetAttribute((const void*)fwd_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        (int)D::FWD_LDS);
-    hipLaunchKernelGGL(fwd_mfma_kernel<D>, dim3(grid), dim3(kThreads), D::FWD_LDS, s, a.N, a.flags, a.x, a.S,
-                       a.A, a.B, a.bias, a.y);
+    static const int per_cu = [] {
+      (void)hipFuncSetAttribute((const void*)fwd_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)D::FWD_LDS);
+      int nb = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fwd_mfma_kernel<D>, kThreads, D::FWD_LDS) !=
+              hipSuccess || nb < 1)
+        nb = 1;
+      return nb;
+    }();
+    int64_t grid = (int64_t)per_cu * device_cus();
+    if (grid > max_grid) grid = max_grid;
+    hipLaunchKernelGGL(fwd_mfma_kernel<D>, dim3((unsigned)grid), dim3(kThreads), D::FWD_LDS, s, a.N, a.flags,
+                       a.x, a.S, a.A, a.B, a.bias, a.y);
   }
 }
 
 template <class D>
 void run_bwd(const LayerArgs& a, int grid, hipStream_t s) {
   if constexpr (D::BWD_OK) {
-    (void)hipFuncSetAttribute((const void*)bwd_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        (int)D::BWD_LDS);
+    static const bool attr = [] {
+      (void)hipFuncSetAttribute((const void*)bwd_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)D::BWD_LDS);
+      return true;
+    }();
+    (void)attr;
     hipLaunchKernelGGL(bwd_mfma_kernel<D>, dim3(grid), dim3(kThreads), D::BWD_LDS, s, a.N, a.flags, a.x, a.S,
                        a.A, a.B, a.dy, a.dx, a.part);
   }
@@ -504,8 +651,7 @@ void run_bwd(const LayerArgs& a, int grid, hipStream_t s) {
 
 #define KRON_ENTRY(P, Q, M, N, R)                                                                      \
   Entry{P, Q, M, N, R, Dims<P, Q, M, N, R>::FWD_OK, Dims<P, Q, M, N, R>::BWD_OK,                        \
-        Dims<P, Q, M, N, R>::FWD_LDS, Dims<P, Q, M, N, R>::BWD_LDS, &run_fwd<Dims<P, Q, M, N, R>>,       \
-        &run_bwd<Dims<P, Q, M, N, R>>}
+        &run_fwd<Dims<P, Q, M, N, R>>, &run_bwd<Dims<P, Q, M, N, R>>}
 
 // The shapes of the workloads: the 64x64 tiny layer (m = 8), the 1024x1024 layers with
 // m = 32 and m = 64, and the GPT-2 FFN pair 768 <-> 3072.
@@ -544,10 +690,8 @@ hipError_t launch_fwd_mfma(const LayerArgs& a, hipStream_t s) {
   const Entry* e = find(a.p, a.q, a.m, a.n, a.r);
   if (!e || !e->fwd_ok) return hipErrorInvalidValue;
   if (a.N == 0) return hipSuccess;
-  // enough workgroups to fill every CU several times; each wavefront strides over rows
   int64_t grid = (a.N + kWaves - 1) / kWaves;
-  const int64_t cap = 256 * 4;
-  if (grid > cap) grid = cap;
+  if (grid > (1 << 20)) grid = 1 << 20;
   e->fwd(a, (int)grid, s);
   return hipGetLastError();
 }
