@@ -104,7 +104,7 @@ BwdPlan bwd_plan(const kron_shape_t* s, bool want_dx) {
   BwdPlan pl{false, 0, 0};
   if (kron::mfma_bwd_supported(s->p, s->q, s->m, s->n, s->r)) {
     pl.mfma = true;
-    pl.G = kron::mfma_bwd_groups(s->N);
+    pl.G = kron::mfma_bwd_groups(s->N, s->p, s->q, s->m, s->n, s->r);
   } else {
     const int T = kron::generic_bwd_rows_per_tile(s->p, s->q, s->m, s->n, want_dx);
     if (T == 0) return pl;

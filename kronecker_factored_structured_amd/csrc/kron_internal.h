@@ -70,7 +70,7 @@ hipError_t launch_bwd_generic(const LayerArgs& a, int G, hipStream_t s);
 // Matrix-core path for the shapes in its table (see kron_mfma.hip).
 bool mfma_fwd_supported(int p, int q, int m, int n, int r);
 bool mfma_bwd_supported(int p, int q, int m, int n, int r);
-int mfma_bwd_groups(int64_t N);
+int mfma_bwd_groups(int64_t N, int p, int q, int m, int n, int r);
 hipError_t launch_fwd_mfma(const LayerArgs& a, hipStream_t s);
 hipError_t launch_bwd_mfma(const LayerArgs& a, int G, hipStream_t s);
 

@@ -42,7 +42,7 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;   // four wavefronts
 constexpr int kWaves = kThreads / 64;
-constexpr int kBwdGroups = 256; // workgroups of the backward (fixed: the workspace depends on it)
+constexpr int kBwdGroups = 256; // workgroups of the backward per 256 CUs (fixed: the workspace depends on it)
 constexpr size_t kMaxLds = 160 * 1024;
 
 __device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
@@ -163,6 +163,27 @@ __device__ __forceinline__ void stage_raw(float* rB, float* rC, const float* __r
 #pragma unroll 4
   for (int e = threadIdx.x; e < D::RAWB / 4; e += kThreads)
     reinterpret_cast<f4*>(rB)[e] = reinterpret_cast<const f4*>(B)[e];
+  if constexpr (PQ % 4 == 0) {
+#pragma unroll 4
+    for (int e = threadIdx.x; e < D::R * PQ / 4; e += kThreads) {
+      f4 a = reinterpret_cast<const f4*>(A)[e];
+      if (S) a *= reinterpret_cast<const f4*>(S)[e % (PQ / 4)];
+      reinterpret_cast<f4*>(rC)[e] = a;
+    }
+  } else {
+    for (int e = threadIdx.x; e < D::R * PQ; e += kThreads) rC[e] = S ? S[e % PQ] * A[e] : A[e];
+  }
+}
+
+template <class D>
+__device__ __forceinline__ void stage_raw_b(float* rB, const float* __restrict__ B) {
+#pragma unroll 4
+  for (int e = threadIdx.x; e < D::RAWB / 4; e += kThreads)
+    reinterpret_cast<f4*>(rB)[e] = reinterpret_cast<const f4*>(B)[e];
+}
+template <class D>
+__device__ __forceinline__ void stage_raw_c(float* rC, const float* __restrict__ S, const float* __restrict__ A) {
+  constexpr int PQ = D::P * D::Q;
   if constexpr (PQ % 4 == 0) {
 #pragma unroll 4
     for (int e = threadIdx.x; e < D::R * PQ / 4; e += kThreads) {
@@ -366,6 +387,12 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
   float* scratch = bopx + D::BOPX;  // raw factors while the tables are built, then G tiles
   float* rB = scratch;
   float* rC = rB + D::RAWB;
+  BwdRow<D> nx;   // the next row's operands, loaded while the current row computes; the
+                  // first row's loads are issued before the tables are built
+  if constexpr (D::BWD_PREFETCH) {
+    const int64_t row0 = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (row0 < N) load_bwd_row<D>(nx, x + row0 * D::IN, dy + row0 * D::OUT, (threadIdx.x & 63) >> 4, threadIdx.x & 15);
+  }
   stage_raw<D>(rB, rC, B, Sm, A);
   __syncthreads();
   build_table<D::R, D::TB, D::SA>(bop, [&](int i, int tb, int g, int c, int s) {
@@ -406,9 +433,7 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
 
   const int64_t stride = (int64_t)gridDim.x * kWaves;
   int64_t row = (int64_t)blockIdx.x * kWaves + wave;
-  BwdRow<D> nx;   // the next row's operands, loaded while the current row computes
   if constexpr (D::BWD_PREFETCH) {
-    if (row < N) load_bwd_row<D>(nx, x + row * D::IN, dy + row * D::OUT, g, c);
     settle(nx.xa);
     settle(nx.xaj);
     settle(nx.dyk);
@@ -438,22 +463,38 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
 #pragma unroll
       for (int tj = 0; tj < D::TJ; ++tj) dxt[ta][tj] = f4{0.f, 0.f, 0.f, 0.f};
 
+    // Operand tables are read one product (or one rank) ahead of their use, so that the
+    // LDS latency hides behind the matrix products in flight.
+    float bo_next[D::TB][D::SA];
+#pragma unroll
+    for (int tb = 0; tb < D::TB; ++tb) table_read<D::SA>(bo_next[tb], bop + tb * 64 * D::SA, lane);
 #pragma unroll
     for (int i = 0; i < D::R; ++i) {
+      float bo[D::TB][D::SA];
+#pragma unroll
+      for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+        for (int s = 0; s < D::SA; ++s) bo[tb][s] = bo_next[tb][s];
+      float co[D::TJ][D::SK];
+#pragma unroll
+      for (int tj = 0; tj < D::TJ; ++tj) table_read<D::SK>(co[tj], copg + (i * D::TJ + tj) * 64 * D::SK, lane);
+      float bx[D::TA][D::TB * 4];
+      if (want_dx) {
+#pragma unroll
+        for (int ta = 0; ta < D::TA; ++ta)
+          table_read<D::TB * 4>(bx[ta], bopx + (i * D::TA + ta) * 64 * D::TB * 4, lane);
+      }
       // Z^T[b][j] = sum_a B_i[a][b] X[j][a]
       f4 zt[D::TB][D::TJ];
 #pragma unroll
-      for (int tb = 0; tb < D::TB; ++tb) {
-        float bo[D::SA];
-        table_read<D::SA>(bo, bop + (i * D::TB + tb) * 64 * D::SA, lane);
+      for (int tb = 0; tb < D::TB; ++tb)
 #pragma unroll
         for (int tj = 0; tj < D::TJ; ++tj) {
           f4 t = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < D::SA; ++s) t = mfma(bo[s], xa[tj][s], t);
+          for (int s = 0; s < D::SA; ++s) t = mfma(bo[tb][s], xa[tj][s], t);
           zt[tb][tj] = t;
         }
-      }
       // dC_i[j][k] += sum_b Z^T[b][j] dY[k][b]
 #pragma unroll
       for (int tj = 0; tj < D::TJ; ++tj)
@@ -466,17 +507,14 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
       // G^T[b][j] = sum_k dY[k][b] C_i[j][k]
       f4 gt[D::TB][D::TJ];
 #pragma unroll
-      for (int tj = 0; tj < D::TJ; ++tj) {
-        float co[D::SK];
-        table_read<D::SK>(co, copg + (i * D::TJ + tj) * 64 * D::SK, lane);
+      for (int tj = 0; tj < D::TJ; ++tj)
 #pragma unroll
         for (int tb = 0; tb < D::TB; ++tb) {
           f4 t = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < D::SK; ++s) t = mfma(dyb[tb][s], co[s], t);
+          for (int s = 0; s < D::SK; ++s) t = mfma(dyb[tb][s], co[tj][s], t);
           gt[tb][tj] = t;
         }
-      }
       // G^T -> LDS (gs[b][j]) first, so that the dX^T products below cover the round trip
 #pragma unroll
       for (int tb = 0; tb < D::TB; ++tb)
@@ -488,16 +526,18 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
       // dX^T[a][j] += sum_b B_i[a][b] G^T[b][j]
       if (want_dx) {
 #pragma unroll
-        for (int ta = 0; ta < D::TA; ++ta) {
-          float bx[D::TB * 4];
-          table_read<D::TB * 4>(bx, bopx + (i * D::TA + ta) * 64 * D::TB * 4, lane);
+        for (int ta = 0; ta < D::TA; ++ta)
 #pragma unroll
           for (int tj = 0; tj < D::TJ; ++tj)
 #pragma unroll
             for (int tb = 0; tb < D::TB; ++tb)
 #pragma unroll
-              for (int v = 0; v < 4; ++v) dxt[ta][tj] = mfma(bx[tb * 4 + v], gt[tb][tj][v], dxt[ta][tj]);
-        }
+              for (int v = 0; v < 4; ++v) dxt[ta][tj] = mfma(bx[ta][tb * 4 + v], gt[tb][tj][v], dxt[ta][tj]);
+      }
+      if (i + 1 < D::R) {
+#pragma unroll
+        for (int tb = 0; tb < D::TB; ++tb)
+          table_read<D::SA>(bo_next[tb], bop + ((i + 1) * D::TB + tb) * 64 * D::SA, lane);
       }
       // dB_i[a][b] += sum_j X[j][a] G[j][b] with j = g*SJ + s
 #pragma unroll
@@ -592,11 +632,344 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
 }
 
 // ---------------------------------------------------------------------------------
+// Rank-parallel backward.  A workgroup of four wavefronts owns RPI = 4 / R rows at a
+// time; wavefront w computes rank w % R of row slot w / R.  The rows' X and dY are staged
+// once per step in LDS with padded strides, every wavefront reads its operands from there
+// and keeps only its own rank's dC_i and dB_i in registers, so two workgroups (two
+// wavefronts per SIMD) fit on a compute unit.  dX^T partials of the R ranks of a row
+// meet in LDS and are added in rank order.  K-step orders: a = g*SA + s for X B_i,
+// j, k = 16*(s/4) + 4*g + s%4 for the j and k contractions (the D-tile row order), so
+// that every LDS read and write of the step is free of bank conflicts.
+// ---------------------------------------------------------------------------------
+template <class D>
+struct RP {
+  static constexpr int R = D::R;
+  static constexpr int RPI = 4 / R;                 // rows per step
+  static constexpr int LX = 16 * D::TA + 4;         // X row stride (a padded to 16*TA)
+  static constexpr int XR = 16 * D::TJ;             // X rows (j padded)
+  static constexpr int LY = 16 * D::TB + 4;         // dY row stride
+  static constexpr int YR = 16 * D::TK;             // dY rows (k padded)
+  static constexpr int SLOT = XR * LX + YR * LY;    // one row's X and dY
+  static constexpr int ROWBUF = RPI * SLOT;
+  static constexpr int SKP = 4 * D::TK;             // k steps (padded)
+  static constexpr int COPG = R * D::TJ * 64 * SKP; // C_i[16tj+c][kappa(s,g)]
+  static constexpr int TABLES = D::BOP + COPG + D::BOPX;
+  static constexpr int LDGT = 16 * D::TJ + 4;       // G tile gs[b][j]
+  static constexpr int GS = 16 * D::TB * LDGT;
+  static constexpr int LDXP = 16 * D::TA + 4;       // dX partial dxp[j][a]
+  static constexpr int DXP = 16 * D::TJ * LDXP;
+  static constexpr int WREG = GS > DXP ? GS : DXP;  // per wavefront: G tile, then dX partial
+  static constexpr int RAWMAX = D::RAWB > D::RAWC ? D::RAWB : D::RAWC;
+  static constexpr int WORK = (ROWBUF + 4 * WREG) > RAWMAX ? (ROWBUF + 4 * WREG) : RAWMAX;
+  static constexpr int MAIN = TABLES + WORK;
+  static constexpr int COMBINE = RPI * D::PWW;
+  static constexpr size_t LDS = (size_t)(MAIN > COMBINE ? MAIN : COMBINE) * 4;
+  static constexpr int NF4 = ROWBUF / SLOT * (D::IN + D::OUT) / 4;   // float4s staged per step
+  static constexpr int NPF = (NF4 + kThreads - 1) / kThreads;
+  static constexpr bool OK = (R == 1 || R == 2 || R == 4) && LDS * 2 <= kMaxLds && D::IN % 4 == 0 &&
+                             D::OUT % 4 == 0;
+};
+
+__device__ __forceinline__ int kidx(int s, int g) { return 16 * (s >> 2) + 4 * g + (s & 3); }
+
+template <class D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_rp_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, const float* __restrict__ Sm,
+                   const float* __restrict__ A, const float* __restrict__ B, const float* __restrict__ dy,
+                   float* __restrict__ dx, float* __restrict__ part) {
+  using Q = RP<D>;
+  extern __shared__ float lds[];
+  float* bop = lds;                      // B_i[g*SA+s][16tb+c]
+  float* copg = bop + D::BOP;            // C_i[16tj+c][kappa(s,g)]
+  float* bopx = copg + Q::COPG;          // B_i[16ta+c][16tb+4g+v]
+  float* work = bopx + D::BOPX;
+  float* rowbuf = work;                  // RPI slots of [X (XR x LX) | dY (YR x LY)]
+  float* wreg = work + Q::ROWBUF;        // per wavefront: G tile / dX partial
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int wave = tid >> 6;
+  const int slot = wave / Q::R, rank = wave % Q::R;
+  const int64_t ngrp = (N + Q::RPI - 1) / Q::RPI;
+
+  // prefetch of the first step's rows (registers), issued before the tables are built
+  f4 pf[Q::NPF];
+  auto fetch = [&](int64_t grp) {
+#pragma unroll
+    for (int t = 0; t < Q::NPF; ++t) {
+      const int f = tid + t * kThreads;
+      f4 v = f4{0.f, 0.f, 0.f, 0.f};
+      if (f < Q::NF4) {
+        const int s = f / ((D::IN + D::OUT) / 4), o = 4 * (f % ((D::IN + D::OUT) / 4));
+        const int64_t row = grp * Q::RPI + s;
+        if (grp < ngrp && row < N)
+          v = o < D::IN ? *reinterpret_cast<const f4*>(x + row * D::IN + o)
+                        : *reinterpret_cast<const f4*>(dy + row * D::OUT + (o - D::IN));
+      }
+      pf[t] = v;
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int t = 0; t < Q::NPF; ++t) {
+      const int f = tid + t * kThreads;
+      if (f < Q::NF4) {
+        const int s = f / ((D::IN + D::OUT) / 4), o = 4 * (f % ((D::IN + D::OUT) / 4));
+        float* sb = rowbuf + s * Q::SLOT;
+        float* dst = o < D::IN ? sb + (o / D::M) * Q::LX + o % D::M
+                               : sb + Q::XR * Q::LX + ((o - D::IN) / D::N) * Q::LY + (o - D::IN) % D::N;
+        *reinterpret_cast<f4*>(dst) = pf[t];
+      }
+    }
+  };
+  fetch(blockIdx.x);
+
+  // operand tables, B first and then C through the same staging area
+  stage_raw_b<D>(work, B);
+  __syncthreads();
+  build_table<D::R, D::TB, D::SA>(bop, [&](int i, int tb, int gg, int cc, int s) {
+    return rawB<D>(work, i, gg * D::SA + s, 16 * tb + cc);
+  });
+  build_table<D::R, D::TA, D::TB * 4>(bopx, [&](int i, int ta, int gg, int cc, int sv) {
+    return rawB<D>(work, i, 16 * ta + cc, 16 * (sv / 4) + 4 * gg + (sv % 4));
+  });
+  __syncthreads();
+  stage_raw_c<D>(work, Sm, A);
+  __syncthreads();
+  build_table<D::R, D::TJ, Q::SKP>(copg, [&](int i, int tj, int gg, int cc, int s) {
+    return rawC<D>(work, i, 16 * tj + cc, kidx(s, gg));
+  });
+  __syncthreads();
+  for (int e = tid; e < Q::ROWBUF; e += kThreads) rowbuf[e] = 0.f;   // padding stays zero
+  __syncthreads();
+
+  const float* bop_i = bop + rank * D::TB * 64 * D::SA;
+  const float* copg_i = copg + rank * D::TJ * 64 * Q::SKP;
+  const float* bopx_i = bopx + rank * D::TA * 64 * D::TB * 4;
+  float* gs = wreg + wave * Q::WREG;      // G[j][b] as gs[b * LDGT + j]; later dX^T partial [j][a]
+  const float* Xs = rowbuf + slot * Q::SLOT;
+  const float* Ys = Xs + Q::XR * Q::LX;
+  const bool want_dx = dx != nullptr;
+  const bool mask = flags & KRON_DX_RELU_MASK;
+
+  f4 dC[D::TJ][D::TK];    // dC_rank[j = 16tj+4g+v][k = 16tk+c]
+  f4 dB[D::TA][D::TB];    // dB_rank[a = 16ta+4g+v][b = 16tb+c]
+  f4 db[D::TK][D::TB];    // dbias[k = 16tk+c][b = 16tb+4g+v] (rank 0 only)
+#pragma unroll
+  for (int tj = 0; tj < D::TJ; ++tj)
+#pragma unroll
+    for (int tk = 0; tk < D::TK; ++tk) dC[tj][tk] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ta = 0; ta < D::TA; ++ta)
+#pragma unroll
+    for (int tb = 0; tb < D::TB; ++tb) dB[ta][tb] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int tk = 0; tk < D::TK; ++tk)
+#pragma unroll
+    for (int tb = 0; tb < D::TB; ++tb) db[tk][tb] = f4{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t grp = blockIdx.x; grp < ngrp; grp += gridDim.x) {
+    stash();
+    __syncthreads();
+    fetch(grp + gridDim.x);
+    // Z^T[b][j] = sum_a B_i[a][b] X[j][a]
+    f4 zt[D::TB][D::TJ];
+    {
+      float xa[D::TJ][D::SA];
+#pragma unroll
+      for (int tj = 0; tj < D::TJ; ++tj) vload<D::SA>(xa[tj], Xs + (16 * tj + c) * Q::LX + g * D::SA);
+#pragma unroll
+      for (int tb = 0; tb < D::TB; ++tb) {
+        float bo[D::SA];
+        table_read<D::SA>(bo, bop_i + tb * 64 * D::SA, lane);
+#pragma unroll
+        for (int tj = 0; tj < D::TJ; ++tj) {
+          f4 t = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < D::SA; ++s) t = mfma(bo[s], xa[tj][s], t);
+          zt[tb][tj] = t;
+        }
+      }
+    }
+    // dC[j][k] += sum_b Z^T[b][j] dY[k][b]
+    {
+      f4 dyk[D::TK][D::TB];
+#pragma unroll
+      for (int tk = 0; tk < D::TK; ++tk)
+#pragma unroll
+        for (int tb = 0; tb < D::TB; ++tb)
+          dyk[tk][tb] = *reinterpret_cast<const f4*>(Ys + (16 * tk + c) * Q::LY + 16 * tb + 4 * g);
+      if (rank == 0) {
+#pragma unroll
+        for (int tk = 0; tk < D::TK; ++tk)
+#pragma unroll
+          for (int tb = 0; tb < D::TB; ++tb) db[tk][tb] += dyk[tk][tb];
+      }
+#pragma unroll
+      for (int tj = 0; tj < D::TJ; ++tj)
+#pragma unroll
+        for (int tk = 0; tk < D::TK; ++tk)
+#pragma unroll
+          for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) dC[tj][tk] = mfma(zt[tb][tj][v], dyk[tk][tb][v], dC[tj][tk]);
+    }
+    // G^T[b][j] = sum_k dY[k][b] C_i[j][k], k = kappa(s, g)
+    f4 gt[D::TB][D::TJ];
+    {
+      float dyb[D::TB][Q::SKP];
+#pragma unroll
+      for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+        for (int s = 0; s < Q::SKP; ++s) dyb[tb][s] = Ys[kidx(s, g) * Q::LY + 16 * tb + c];
+#pragma unroll
+      for (int tj = 0; tj < D::TJ; ++tj) {
+        float co[Q::SKP];
+        table_read<Q::SKP>(co, copg_i + tj * 64 * Q::SKP, lane);
+#pragma unroll
+        for (int tb = 0; tb < D::TB; ++tb) {
+          f4 t = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < Q::SKP; ++s) t = mfma(dyb[tb][s], co[s], t);
+          gt[tb][tj] = t;
+        }
+      }
+    }
+    // G^T -> LDS as gs[b][j]
+#pragma unroll
+    for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+      for (int tj = 0; tj < D::TJ; ++tj)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) gs[(16 * tb + 4 * g + v) * Q::LDGT + 16 * tj + c] = gt[tb][tj][v];
+    __builtin_amdgcn_wave_barrier();
+    // dX^T[a][j] = sum_b B_i[a][b] G^T[b][j]   (this rank's share)
+    f4 dxt[D::TA][D::TJ];
+#pragma unroll
+    for (int ta = 0; ta < D::TA; ++ta) {
+      float bx[D::TB * 4];
+      table_read<D::TB * 4>(bx, bopx_i + ta * 64 * D::TB * 4, lane);
+#pragma unroll
+      for (int tj = 0; tj < D::TJ; ++tj) {
+        f4 t = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) t = mfma(bx[tb * 4 + v], gt[tb][tj][v], t);
+        dxt[ta][tj] = t;
+      }
+    }
+    // dB[a][b] += sum_j X[j][a] G[j][b], j = kappa(s, g)
+#pragma unroll
+    for (int ta = 0; ta < D::TA; ++ta) {
+      float xaj[D::SJ];
+#pragma unroll
+      for (int s = 0; s < D::SJ; ++s) xaj[s] = Xs[kidx(s, g) * Q::LX + 16 * ta + c];
+#pragma unroll
+      for (int tb = 0; tb < D::TB; ++tb) {
+        float gv[D::SJ];
+#pragma unroll
+        for (int tj = 0; tj < D::TJ; ++tj) {
+          const f4 q4 = *reinterpret_cast<const f4*>(gs + (16 * tb + c) * Q::LDGT + 16 * tj + 4 * g);
+          gv[4 * tj] = q4[0]; gv[4 * tj + 1] = q4[1]; gv[4 * tj + 2] = q4[2]; gv[4 * tj + 3] = q4[3];
+        }
+#pragma unroll
+        for (int s = 0; s < D::SJ; ++s) dB[ta][tb] = mfma(xaj[s], gv[s], dB[ta][tb]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // this rank's dX^T partial -> LDS as dxp[j][a]
+#pragma unroll
+    for (int ta = 0; ta < D::TA; ++ta)
+#pragma unroll
+      for (int tj = 0; tj < D::TJ; ++tj)
+        *reinterpret_cast<f4*>(gs + (16 * tj + c) * Q::LDXP + 16 * ta + 4 * g) = dxt[ta][tj];
+    __syncthreads();
+    // dX of the step's rows: add the R rank partials of each row in rank order
+    if (want_dx) {
+      constexpr int PER_ROW = D::IN / 4;
+      for (int f = tid; f < Q::RPI * PER_ROW; f += kThreads) {
+        const int s = f / PER_ROW, o = 4 * (f % PER_ROW);
+        const int64_t row = grp * Q::RPI + s;
+        if (row >= N) continue;
+        const int j = o / D::M, a = o % D::M;
+        f4 acc = *reinterpret_cast<const f4*>(wreg + (s * Q::R) * Q::WREG + j * Q::LDXP + a);
+#pragma unroll
+        for (int i = 1; i < Q::R; ++i)
+          acc += *reinterpret_cast<const f4*>(wreg + (s * Q::R + i) * Q::WREG + j * Q::LDXP + a);
+        if (mask) {
+          const f4 xv = *reinterpret_cast<const f4*>(x + row * D::IN + o);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[v] = xv[v] > 0.f ? acc[v] : 0.f;
+        }
+        *reinterpret_cast<f4*>(dx + row * D::IN + o) = acc;
+      }
+    }
+  }
+
+  // Partial row of this workgroup: [dB (R*M*N) | dA (R*P*Q) | dS (P*Q) | dbias (Q*N)].
+  __syncthreads();
+  constexpr int MN = D::M * D::N, PQ = D::P * D::Q, QN = D::Q * D::N;
+  float* red = lds + slot * D::PWW;   // [dB | dC | dbias] of this row slot
+#pragma unroll
+  for (int ta = 0; ta < D::TA; ++ta)
+#pragma unroll
+    for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int a = 16 * ta + 4 * g + v, b = 16 * tb + c;
+        if (a < D::M && b < D::N) red[rank * MN + a * D::N + b] = dB[ta][tb][v];
+      }
+#pragma unroll
+  for (int tj = 0; tj < D::TJ; ++tj)
+#pragma unroll
+    for (int tk = 0; tk < D::TK; ++tk)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = 16 * tj + 4 * g + v, k = 16 * tk + c;
+        if (j < D::P && k < D::Q) red[D::R * MN + rank * PQ + j * D::Q + k] = dC[tj][tk][v];
+      }
+  if (rank == 0) {
+#pragma unroll
+    for (int tk = 0; tk < D::TK; ++tk)
+#pragma unroll
+      for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int k = 16 * tk + c, b = 16 * tb + 4 * g + v;
+          if (k < D::Q && b < D::N) red[D::R * (MN + PQ) + k * D::N + b] = db[tk][tb][v];
+        }
+  }
+  __syncthreads();
+  float* out = part + (int64_t)blockIdx.x * D::PW;
+  auto ssum = [&](int e) {
+    float t = lds[e];
+#pragma unroll
+    for (int s = 1; s < Q::RPI; ++s) t += lds[s * D::PWW + e];
+    return t;
+  };
+  for (int e = tid; e < D::R * MN; e += kThreads) out[e] = ssum(e);
+  for (int e = tid; e < PQ; e += kThreads) {
+    const float sv = Sm ? Sm[e] : 1.f;
+    float ds = 0.f;
+#pragma unroll
+    for (int i = 0; i < D::R; ++i) {
+      const float dcv = ssum(D::R * MN + i * PQ + e);
+      ds = fmaf(A[i * PQ + e], dcv, ds);
+      out[D::R * MN + i * PQ + e] = sv * dcv;
+    }
+    out[D::R * (MN + PQ) + e] = Sm ? ds : 0.f;
+  }
+  for (int e = tid; e < QN; e += kThreads) out[D::R * (MN + PQ) + PQ + e] = ssum(D::R * (MN + PQ) + e);
+}
+
+// ---------------------------------------------------------------------------------
 // Shape table.
 // ---------------------------------------------------------------------------------
 struct Entry {
   int p, q, m, n, r;
-  bool fwd_ok, bwd_ok;
+  bool fwd_ok, bwd_ok, bwd_rp;
+  int rows_per_step;   // of the rank-parallel backward
   void (*fwd)(const LayerArgs&, int, hipStream_t);
   void (*bwd)(const LayerArgs&, int, hipStream_t);
 };
@@ -637,7 +1010,16 @@ void run_fwd(const LayerArgs& a, int max_grid, hipStream_t s) {
 
 template <class D>
 void run_bwd(const LayerArgs& a, int grid, hipStream_t s) {
-  if constexpr (D::BWD_OK) {
+  if constexpr (RP<D>::OK) {
+    static const bool attr = [] {
+      (void)hipFuncSetAttribute((const void*)bwd_rp_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)RP<D>::LDS);
+      return true;
+    }();
+    (void)attr;
+    hipLaunchKernelGGL(bwd_rp_kernel<D>, dim3(grid), dim3(kThreads), RP<D>::LDS, s, a.N, a.flags, a.x, a.S,
+                       a.A, a.B, a.dy, a.dx, a.part);
+  } else if constexpr (D::BWD_OK) {
     static const bool attr = [] {
       (void)hipFuncSetAttribute((const void*)bwd_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)D::BWD_LDS);
@@ -650,8 +1032,9 @@ void run_bwd(const LayerArgs& a, int grid, hipStream_t s) {
 }
 
 #define KRON_ENTRY(P, Q, M, N, R)                                                                      \
-  Entry{P, Q, M, N, R, Dims<P, Q, M, N, R>::FWD_OK, Dims<P, Q, M, N, R>::BWD_OK,                        \
-        &run_fwd<Dims<P, Q, M, N, R>>, &run_bwd<Dims<P, Q, M, N, R>>}
+  Entry{P, Q, M, N, R, Dims<P, Q, M, N, R>::FWD_OK,                                                    \
+        Dims<P, Q, M, N, R>::BWD_OK || RP<Dims<P, Q, M, N, R>>::OK, RP<Dims<P, Q, M, N, R>>::OK,         \
+        RP<Dims<P, Q, M, N, R>>::RPI, &run_fwd<Dims<P, Q, M, N, R>>, &run_bwd<Dims<P, Q, M, N, R>>}
 
 // The shapes of the workloads: the 64x64 tiny layer (m = 8), the 1024x1024 layers with
 // m = 32 and m = 64, and the GPT-2 FFN pair 768 <-> 3072.
@@ -681,7 +1064,13 @@ bool mfma_bwd_supported(int p, int q, int m, int n, int r) {
   return e && e->bwd_ok;
 }
 
-int mfma_bwd_groups(int64_t N) {
+int mfma_bwd_groups(int64_t N, int p, int q, int m, int n, int r) {
+  const Entry* e = find(p, q, m, n, r);
+  if (e && e->bwd_rp) {
+    // two workgroups per compute unit, each stepping over rows_per_step rows at a time
+    const int64_t g = (N + e->rows_per_step - 1) / e->rows_per_step;
+    return (int)(g < 2 * kBwdGroups ? g : 2 * kBwdGroups);
+  }
   const int64_t g = (N + kWaves - 1) / kWaves;
   return (int)(g < kBwdGroups ? g : kBwdGroups);
 }
