@@ -1,19 +1,25 @@
-"""Benchmark of the Kronecker-factored layer's forward + backward on one MI355X.
+"""Benchmark of the Kronecker-factored layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--cpu-seconds 10]
+    python bench.py --workload {headline,tiny,mlp_step,gpt2_ffn,ks}
+    python bench.py --calibrate-copy      (plain device copy of known size, for HBM counters)
 
-One step is one kron_linear_fwd + one kron_linear_bwd call (x, S, A, B, dy resident in
-HBM; outputs and workspace preallocated) on the 1024 x 1024 layer with m = n = 32
-(p = q = 32), r = 4, half of S zeroed, 20,000 rows.  Prints one JSON line.
+Default workload (one JSON line): one step is one kron_linear_fwd + one kron_linear_bwd
+call (x, S, A, B, dy resident in HBM; outputs and workspace preallocated) on the
+1024 x 1024 layer with m = n = 32 (p = q = 32), r = 4, half of S zeroed, 20,000 rows.
 
 Algorithmic work per row (counted once, whatever the kernels execute):
   forward  2*r*n*(p*m + nnz)                 flops, 4*(in + out) bytes
   backward 2*r*n*(nnz + 2*p*m + p*q)         flops, 4*(2*in + out) bytes
-with nnz the number of nonzero entries of S.
+with nnz the number of nonzero entries of S (S-zero terms are not counted as work).
+The roofline entry describes the backward call, the dominant launch: its main kernel
+and the fixed-order reduction of the per-workgroup partial sums, timed together with
+HIP events on the stream the kernels run on.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -24,13 +30,36 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_FP32_TFLOPS = 157.3     # MI355X dense fp32 (matrix cores), published
+PEAK_FP32_TFLOPS = 157.3     # MI355X dense fp32 matrix, published
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 METRIC = "kron_linear fwd+bwd rows/s and % of HBM/fp32 roofline, 1024² m=32 r=4"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_kron_linear_bwd_headline.json")
+KERNEL_SOURCES = ("kron_mfma.hip", "kron_generic.hip", "kron_api.cpp", "kron_internal.h")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "kronecker_factored_structured_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per backward call from the committed counter summary, or None when the
+    kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("bytes_per_call")
 
 
 def work_per_row(p, q, m, n, r, nnz):
@@ -41,17 +70,35 @@ def work_per_row(p, q, m, n, r, nnz):
     return ff, fb, bf, bb
 
 
+def timed(fn, steps, warmup):
+    """Mean ms per call of fn (events on the current stream) and the host wall clock."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, (time.perf_counter() - w0) * 1e3 / steps
+
+
+def cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(inp, seconds: float):
     """The oracle (as it stands) on the same workload, repeated for about `seconds`."""
     from oracle import kron as OK
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
     N = inp.x.shape[0]
-    rows, t0 = 0, time.perf_counter()
-    calls = 0
+    rows, calls, t0 = 0, 0, time.perf_counter()
     while True:
         OK.forward(inp.x, inp.S, inp.A, inp.B, inp.bias)
         OK.backward(inp.x, inp.S, inp.A, inp.B, inp.dy, want_dx=True)
@@ -60,91 +107,73 @@ def cpu_baseline(inp, seconds: float):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
-    return {"value": rows / dt, "unit": "rows/s", "cores": int(cores), "kind": "oracle",
+    return {"value": rows / dt, "unit": "rows/s", "cores": int(cpu_threads()), "kind": "oracle",
             "sample": f"{calls} x (fwd+bwd over all {N} rows of the same workload), fp64 numpy/OpenBLAS, "
                       f"{dt:.1f} s"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (the Kronecker layer's hot path runs on one GPU's share "
-              f"of rows); --gpus {args.gpus} is not supported", file=sys.stderr)
-        sys.exit(2)
+class Layer:
+    """Device tensors and preallocated outputs of one Kronecker layer workload."""
 
+    def __init__(self, inp, dev):
+        import torch
+        import kronecker_factored_structured_amd as K
+        self.K = K
+        t = lambda a: None if a is None else torch.from_numpy(a).to(dev).contiguous()
+        self.x, self.S, self.A, self.B, self.bias, self.dy = (t(a) for a in (inp.x, inp.S, inp.A, inp.B,
+                                                                           inp.bias, inp.dy))
+        sh = inp.shape
+        self.y = torch.empty(sh.N, sh.q * sh.n, device=dev)
+        self.outs = dict(dx=torch.empty_like(self.x), dS=None if self.S is None else torch.empty_like(self.S),
+                         dA=torch.empty_like(self.A), dB=torch.empty_like(self.B),
+                         dbias=None if self.bias is None else torch.empty_like(self.bias))
+        shape = K.layer_shape(sh.N, self.S, self.A, self.B)
+        self.ws = torch.empty(K.kron_linear_bwd_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+
+    def fwd(self):
+        self.K.kron_linear_fwd(self.x, self.S, self.A, self.B, self.bias, out=self.y)
+
+    def bwd(self):
+        self.K.kron_linear_bwd(self.x, self.S, self.A, self.B, self.dy, workspace=self.ws, outs=self.outs)
+
+
+def split_times(layer, steps):
+    """Mean seconds of the forward and of the backward call, from events around each call."""
     import torch
-    import kronecker_factored_structured_amd as K
-    from workloads import headline_layer
-
-    if not torch.cuda.is_available():
-        raise SystemExit("no GPU visible")
-    dev = torch.device("cuda:0")
-    inp = headline_layer()
-    sh = inp.shape
-    N, p, q, m, n, r = sh.N, sh.p, sh.q, sh.m, sh.n, sh.r
-    nnz = int(np.count_nonzero(inp.S))
-    t = lambda a: torch.from_numpy(a).to(dev).contiguous()
-    x, S, A, B, bias, dy = t(inp.x), t(inp.S), t(inp.A), t(inp.B), t(inp.bias), t(inp.dy)
-    y = torch.empty(N, q * n, device=dev)
-    outs = dict(dx=torch.empty_like(x), dS=torch.empty_like(S), dA=torch.empty_like(A),
-                dB=torch.empty_like(B), dbias=torch.empty_like(bias))
-    shape = K.layer_shape(N, S, A, B)
-    ws = torch.empty(K.kron_linear_bwd_workspace_bytes(shape), dtype=torch.uint8, device=dev)
-
-    def fwd():
-        K.kron_linear_fwd(x, S, A, B, bias, out=y)
-
-    def bwd():
-        K.kron_linear_bwd(x, S, A, B, dy, workspace=ws, outs=outs)
-
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
-        fwd()
-        bwd()
-    torch.cuda.synchronize()
-
-    # Whole-step timing.
-    log(f"[bench] timing {args.steps} steps")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
-        fwd()
-        bwd()
-    e1.record()
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - w0) * 1e3 / args.steps
-    ms_step = e0.elapsed_time(e1) / args.steps
-
-    # Per-call timing with events on the stream the kernels run on.
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     for a, b, c in ev:
         a.record()
-        fwd()
+        layer.fwd()
         b.record()
-        bwd()
+        layer.bwd()
         c.record()
     torch.cuda.synchronize()
     t_fwd = float(np.mean([a.elapsed_time(b) for a, b, _ in ev])) * 1e-3
     t_bwd = float(np.mean([b.elapsed_time(c) for _, b, c in ev])) * 1e-3
+    return t_fwd, t_bwd
 
+
+def run_headline(args, dev):
+    from workloads import headline_layer
+    inp = headline_layer()
+    sh = inp.shape
+    N, p, q, m, n, r = sh.N, sh.p, sh.q, sh.m, sh.n, sh.r
+    nnz = int(np.count_nonzero(inp.S))
+    L = Layer(inp, dev)
+    log(f"[bench] headline: warmup {args.warmup}, timing {args.steps} steps")
+    ms_step, wall_ms = timed(lambda: (L.fwd(), L.bwd()), args.steps, args.warmup)
+    t_fwd, t_bwd = split_times(L, args.steps)
     ff, fb, bf, bb = work_per_row(p, q, m, n, r, nnz)
     t_roof = max(N * (ff + fb) / (PEAK_FP32_TFLOPS * 1e12), N * (bf + bb) / (PEAK_HBM_GBS * 1e9))
-    # Dominant launch: the backward call (its main kernel plus the fixed-order reduction).
     achieved = N * fb / t_bwd / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": None,
-                "kernel": "kron_linear_bwd", "t_us": round(t_bwd * 1e6, 2),
-                "flop_per_row": fb, "rows": N}
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
+                "traffic": measured_traffic(),
+                "kernel": "kron_linear_bwd (main kernel + fixed-order partial-sum reduction)",
+                "t_us": round(t_bwd * 1e6, 2), "flop_per_row": fb, "rows": N,
+                "algorithmic_bytes": N * bb}
     value = N / (ms_step * 1e-3)
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "rows/s", "n_gpus": 1,
@@ -160,11 +189,152 @@ def main():
                           "effective_tflops": round(N * (ff + fb) / (ms_step * 1e-3) / 1e12, 3)},
         "t_fwd_us": round(t_fwd * 1e6, 2), "t_bwd_us": round(t_bwd * 1e6, 2),
         "wall_ms_per_step": round(wall_ms, 5),
+        "kernel_source_sha": kernel_source_sha(),
     }
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (oracle) for ~{args.cpu_seconds} s")
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
+
+
+def layer_record(name, inp, L, args, extra=None):
+    sh = inp.shape
+    N, p, q, m, n, r = sh.N, sh.p, sh.q, sh.m, sh.n, sh.r
+    nnz = p * q if inp.S is None else int(np.count_nonzero(inp.S))
+    ms, _ = timed(lambda: (L.fwd(), L.bwd()), args.steps, args.warmup)
+    t_fwd, t_bwd = split_times(L, args.steps)
+    ff, fb, bf, bb = work_per_row(p, q, m, n, r, nnz)
+    if inp.S is None:   # dense factors: the cheaper association of each product counts
+        ff = 2 * r * min(p * n * (m + q), q * m * (p + n))
+        fb = 2 * ff
+    t_roof = max(N * (ff + fb) / (PEAK_FP32_TFLOPS * 1e12), N * (bf + bb) / (PEAK_HBM_GBS * 1e9))
+    rec = {"workload": name, "rows_per_s": round(N / (ms * 1e-3), 1), "us_per_fwd_bwd": round(ms * 1e3, 2),
+           "t_fwd_us": round(t_fwd * 1e6, 2), "t_bwd_us": round(t_bwd * 1e6, 2),
+           "effective_tflops": round(N * (ff + fb) / (ms * 1e-3) / 1e12, 3),
+           "t_roof_us": round(t_roof * 1e6, 2), "roofline_frac": round(t_roof / (ms * 1e-3), 4),
+           "bound": "fp32" if N * (ff + fb) / (PEAK_FP32_TFLOPS * 1e12) >= N * (bf + bb) / (PEAK_HBM_GBS * 1e9)
+           else "hbm",
+           "shape": {"N": N, "p": p, "q": q, "m": m, "n": n, "r": r}}
+    if extra:
+        rec.update(extra)
+    print(json.dumps(rec), flush=True)
+
+
+def run_tiny(args, dev):
+    from workloads import tiny_layer
+    inp = tiny_layer()
+    layer_record("tiny: 64 rows, 64x64, m=8, r=2", inp, Layer(inp, dev), args)
+
+
+def run_gpt2(args, dev):
+    from workloads import gpt2_ffn_layers
+    for r in (1, 2, 4, 8):
+        up, down = gpt2_ffn_layers(r)
+        layer_record(f"gpt2 ffn 768->3072 (A 32x64, B 24x48), r={r}, 8192 rows", up, Layer(up, dev), args)
+        layer_record(f"gpt2 ffn 3072->768 (A 64x32, B 48x24), r={r}, 8192 rows", down, Layer(down, dev), args)
+
+
+def run_mlp_step(args, dev):
+    import torch
+    import kronecker_factored_structured_amd as K
+    from workloads import mlp_step_inputs
+    inp = mlp_step_inputs()
+    step = K.KronMLPStep(inp.layers, inp.head_w, inp.head_b, inp.lam, inp.lr, dev)
+    x = torch.from_numpy(inp.x).to(dev)
+    lab = torch.from_numpy(inp.labels).to(dev)
+    ms, wall = timed(lambda: step.step(x, lab), args.steps, args.warmup)
+    N = x.shape[0]
+    # kron layers: layer 1 without dX, layer 2 with dX; head: 3 products of N x 1024 x 10
+    p, m, r = 16, 64, 2
+    ff = 2 * r * m * (p * m + p * p)
+    fb2 = 2 * ff
+    fb1 = fb2 - 2 * r * m * p * m
+    head = 3 * 2 * 1024 * 10
+    flops = N * (2 * ff + fb1 + fb2 + head)
+    print(json.dumps({"workload": "mlp_step: MLP 1024-1024-1024-10, Kronecker hidden layers m=64 r=2, "
+                                  "CE + 1e-4*sum|S|, fused Adam, 20000 rows",
+                      "ms_per_step": round(ms, 4), "wall_ms_per_step": round(wall, 4),
+                      "rows_per_s": round(N / (ms * 1e-3), 1),
+                      "effective_tflops": round(flops / (ms * 1e-3) / 1e12, 3),
+                      "t_roof_us": round(flops / (PEAK_FP32_TFLOPS * 1e12) * 1e6, 2)}), flush=True)
+
+
+def run_ks(args, dev):
+    import torch
+    import kronecker_factored_structured_amd as K
+    from workloads import vit_ks
+    for dtype in ("f32", "bf16"):
+        sets = []
+        for s in range(3):   # rotate buffer sets so the working set exceeds the last-level cache
+            inp = vit_ks(dtype, seed=5 + 10 * s)
+            if dtype == "bf16":
+                x = torch.from_numpy(inp.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+                v = torch.from_numpy(inp.vals_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+            else:
+                x = torch.from_numpy(inp.x).to(dev)
+                v = torch.from_numpy(inp.vals).to(dev)
+            y = torch.empty(x.shape[0], inp.a * inp.c * inp.d, device=dev)
+            sets.append((x, v, y))
+        a, b, c, d = inp.a, inp.b, inp.c, inp.d
+        it = [0]
+
+        def call():
+            x, v, y = sets[it[0] % len(sets)]
+            it[0] += 1
+            K.ks_matmul(x, v, a, b, c, d, out=y)
+
+        ms, _ = timed(call, args.steps, args.warmup)
+        N = sets[0][0].shape[0]
+        s_in = 4 if dtype == "f32" else 2
+        flops = N * 2 * a * b * c * d
+        byts = N * (s_in * a * b * d + 4 * a * c * d) + s_in * a * b * c * d
+        t_roof = max(flops / (PEAK_FP32_TFLOPS * 1e12), byts / (PEAK_HBM_GBS * 1e9))
+        print(json.dumps({"workload": f"ks_matmul (a,b,c,d)=(2,48,192,4), 25216 rows, {dtype} inputs",
+                          "us_per_call": round(ms * 1e3, 2), "rows_per_s": round(N / (ms * 1e-3), 1),
+                          "achieved_gbs": round(byts / (ms * 1e-3) / 1e9, 1),
+                          "effective_tflops": round(flops / (ms * 1e-3) / 1e12, 3),
+                          "t_roof_us": round(t_roof * 1e6, 2), "roofline_frac": round(t_roof / (ms * 1e-3), 4),
+                          "bound": "hbm"}), flush=True)
+
+
+def run_copy(args, dev):
+    """Plain device-to-device copy of a known size (reference for the HBM counters)."""
+    import torch
+    nbytes = 1 << 30
+    a = torch.empty(nbytes // 4, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    for _ in range(args.steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": nbytes,
+                      "bytes_written_per_copy": nbytes, "copies": args.steps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="headline",
+                    choices=("headline", "tiny", "mlp_step", "gpt2_ffn", "ks"))
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the Kronecker layer's hot path runs on one GPU's share "
+              f"of rows); --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        return run_copy(args, dev)
+    {"headline": run_headline, "tiny": run_tiny, "mlp_step": run_mlp_step, "gpt2_ffn": run_gpt2,
+     "ks": run_ks}[args.workload](args, dev)
 
 
 if __name__ == "__main__":
