@@ -26,6 +26,7 @@ SOURCES = [
     "kron_generic.hip",
     "kron_mfma.hip",
     "ks_matmul.hip",
+    "ks_mfma.hip",
     "adam_l1.hip",
     "head_ce.hip",
 ]

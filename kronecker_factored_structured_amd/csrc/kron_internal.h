@@ -89,6 +89,9 @@ struct KSArgs {
 };
 bool ks_supported(int a, int b, int c, int d);
 hipError_t launch_ks(const KSArgs& k, hipStream_t s);
+// Matrix-core path for the (b, c, d) in its table (see ks_mfma.hip).
+bool ks_mfma_supported(int a, int b, int c, int d);
+hipError_t launch_ks_mfma(const KSArgs& k, hipStream_t s);
 
 // ---------------------------------------------------------------------------------
 // Adam + l1.

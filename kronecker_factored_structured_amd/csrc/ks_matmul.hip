@@ -64,6 +64,7 @@ bool ks_supported(int a, int b, int c, int d) {
 }
 
 hipError_t launch_ks(const KSArgs& k, hipStream_t s) {
+  if (ks_mfma_supported(k.a, k.b, k.c, k.d)) return launch_ks_mfma(k, s);
   const int T = ks_rows_per_tile(k.b, k.d);
   if (T == 0) return hipErrorInvalidValue;
   const int64_t gx = (k.N + T - 1) / T;

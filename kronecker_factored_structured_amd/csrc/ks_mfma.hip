@@ -1,0 +1,251 @@
+// Matrix-core kernel of the Kronecker-sparse matmul Y = X K, K of support
+// I_a (x) 1_{b x c} (x) I_d ("Fast Inference with Kronecker-Sparse Matrices", abstract).
+//
+// For one (alpha, delta) the product is an ordinary GEMM over the rows,
+//   Y[n, (al*c + ga)*d + de] = sum_be X[n, (al*b + be)*d + de] * V[al][de][be][ga],
+// and the d GEMMs of one alpha read and write interleaved columns.  The kernel is output
+// stationary: a task is 16 rows x (a group of 16-wide gamma tiles) x all d deltas of one
+// alpha, so a lane holds the d values of delta for one (row, beta) -- one vector load of
+// X -- and writes the d values of delta for one (row, gamma) -- one vector store of Y.
+// No permutation pass exists: the interleave is absorbed by which accumulator a product
+// goes to.  Products are 16x16x4 fp32 MFMAs; bf16 inputs are widened to fp32 on load
+// (a bf16 x bf16 product is exact in fp32, so only the accumulation order differs from a
+// bf16 matrix instruction).
+//
+// Workgroups (8 wavefronts) are specialised by alpha and keep V[alpha] in LDS as
+// chunk-interleaved operand tables: table[de][gamma tile][chunk][lane][4] holds
+// V[al][de][be = g*SB + s][ga = 16*tile + c] for K step s, so that one ds_read_b128 per
+// chunk is contiguous across the wavefront.  Tasks are dealt round-robin to the
+// workgroup's wavefronts; the GQ gamma groups of a row tile go to neighbouring
+// wavefronts, which share its X through the L1 cache.
+#include "kron_internal.h"
+
+namespace kron {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 512;   // eight wavefronts
+constexpr int kWaves = kThreads / 64;
+constexpr size_t kMaxLds = 160 * 1024;
+
+__device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int B_, int C_, int D_>
+struct KS {
+  static constexpr int Bv = B_, Cv = C_, Dv = D_;
+  static constexpr int SB = B_ / 4;          // K steps per lane group: be = g*SB + s
+  static constexpr int TG = C_ / 16;         // gamma tiles
+  static constexpr int GQ = TG % 3 == 0 && TG > 3 ? TG / 3 : (TG % 2 == 0 && TG > 2 ? TG / 2 : 1);
+  static constexpr int TPQ = TG / GQ;        // gamma tiles per task
+  static constexpr int TABLE = D_ * TG * 64 * SB;   // = d*b*c floats
+  static constexpr size_t LDS = (size_t)TABLE * 4;
+  static constexpr bool OK = B_ % 4 == 0 && C_ % 16 == 0 && (D_ == 1 || D_ == 2 || D_ == 4) && LDS <= kMaxLds &&
+                             SB % 4 == 0;
+};
+
+template <int L>
+__device__ __forceinline__ void table_read4(float (&dst)[L], const float* blk, int lane) {
+#pragma unroll
+  for (int t = 0; t < L / 4; ++t) {
+    const f4 v = reinterpret_cast<const f4*>(blk)[t * 64 + lane];
+    dst[4 * t] = v[0]; dst[4 * t + 1] = v[1]; dst[4 * t + 2] = v[2]; dst[4 * t + 3] = v[3];
+  }
+}
+
+template <int DV>
+__device__ __forceinline__ void load_d(float (&dst)[DV], const float* p) {
+  if constexpr (DV == 4) {
+    const f4 v = *reinterpret_cast<const f4*>(p);
+    dst[0] = v[0]; dst[1] = v[1]; dst[2] = v[2]; dst[3] = v[3];
+  } else if constexpr (DV == 2) {
+    const f2 v = *reinterpret_cast<const f2*>(p);
+    dst[0] = v[0]; dst[1] = v[1];
+  } else {
+    dst[0] = p[0];
+  }
+}
+template <int DV>
+__device__ __forceinline__ void load_d(float (&dst)[DV], const uint16_t* p) {
+  if constexpr (DV == 4) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    dst[0] = __uint_as_float(v.x << 16); dst[1] = __uint_as_float(v.x & 0xffff0000u);
+    dst[2] = __uint_as_float(v.y << 16); dst[3] = __uint_as_float(v.y & 0xffff0000u);
+  } else if constexpr (DV == 2) {
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(p);
+    dst[0] = __uint_as_float(v << 16); dst[1] = __uint_as_float(v & 0xffff0000u);
+  } else {
+    dst[0] = __uint_as_float(((uint32_t)p[0]) << 16);
+  }
+}
+__device__ __forceinline__ float widen(float v) { return v; }
+__device__ __forceinline__ float widen(uint16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+template <class K, class TIn>
+__global__ __launch_bounds__(kThreads) void ks_mfma_kernel(int64_t N, int a_count, const TIn* __restrict__ x,
+                                                           const TIn* __restrict__ vals,
+                                                           float* __restrict__ y) {
+  constexpr int b = K::Bv, c_ = K::Cv, d = K::Dv, SB = K::SB;
+  extern __shared__ float tab[];
+  const int groups_per_alpha = gridDim.x / a_count;
+  const int al = blockIdx.x / groups_per_alpha;
+  const int gidx = blockIdx.x % groups_per_alpha;
+  // V[al] -> table[de][tile][chunk][lane][4]: each thread gathers the four K steps of one
+  // (lane, chunk) and writes them with one 16-byte LDS store (consecutive threads write
+  // consecutive 16 bytes); the sixteen lanes of a group read sixteen consecutive gammas
+  const TIn* V = vals + (int64_t)al * d * b * c_;
+#pragma unroll 4
+  for (int e4 = threadIdx.x; e4 < K::TABLE / 4; e4 += kThreads) {
+    int r = e4;
+    const int l = r % 64; r /= 64;
+    const int ch = r % (SB / 4); r /= (SB / 4);
+    const int tile = r % K::TG;
+    const int de = r / K::TG;
+    const int be0 = (l >> 4) * SB + ch * 4, ga = 16 * tile + (l & 15);
+    const TIn* src = V + ((int64_t)de * b + be0) * c_ + ga;
+    reinterpret_cast<f4*>(tab)[e4] = f4{widen(src[0]), widen(src[c_]), widen(src[2 * c_]), widen(src[3 * c_])};
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  const int wave = threadIdx.x >> 6;
+  const int64_t in_w = (int64_t)a_count * b * d, out_w = (int64_t)a_count * c_ * d;
+  const int64_t tiles = (N + 15) / 16;
+  const int64_t ntasks = tiles * K::GQ;
+  const int64_t stride = (int64_t)groups_per_alpha * kWaves;
+  // A operand of a task: X[row][(al*b + be)*d + de] for be = g*SB + s, all de; the next
+  // task's is loaded while the current one computes
+  auto load_x = [&](float (&xa)[SB][d], int64_t task) {
+    const int64_t row = task / K::GQ * 16 + c;
+    if (task < ntasks && row < N) {
+      const TIn* xr = x + row * in_w + ((int64_t)al * b + g * SB) * d;
+#pragma unroll
+      for (int s = 0; s < SB; ++s) load_d<d>(xa[s], xr + s * d);
+    } else {
+#pragma unroll
+      for (int s = 0; s < SB; ++s)
+#pragma unroll
+        for (int de = 0; de < d; ++de) xa[s][de] = 0.f;
+    }
+  };
+  int64_t task = (int64_t)gidx * kWaves + wave;
+  float xn[SB][d];
+  load_x(xn, task);
+  // wait here for the first task's loads, so that the loop head only ever has the
+  // previous task's stores outstanding (a merged wait there would drain them)
+#pragma unroll
+  for (int s = 0; s < SB; ++s)
+#pragma unroll
+    for (int de = 0; de < d; ++de) asm volatile("" ::"v"(xn[s][de]));
+  for (; task < ntasks; task += stride) {
+    const int64_t rt = task / K::GQ;
+    const int q = (int)(task % K::GQ);
+    float xa[SB][d];
+#pragma unroll
+    for (int s = 0; s < SB; ++s)
+#pragma unroll
+      for (int de = 0; de < d; ++de) xa[s][de] = xn[s][de];
+    load_x(xn, task + stride);
+    f4 acc[K::TPQ][d];
+#pragma unroll
+    for (int t = 0; t < K::TPQ; ++t)
+#pragma unroll
+      for (int de = 0; de < d; ++de) acc[t][de] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ch = 0; ch < SB / 4; ++ch) {
+      float bv[K::TPQ][d][4];
+#pragma unroll
+      for (int t = 0; t < K::TPQ; ++t)
+#pragma unroll
+        for (int de = 0; de < d; ++de) {
+          const int tile = q * K::TPQ + t;
+          const f4 v = reinterpret_cast<const f4*>(tab + ((de * K::TG + tile) * (SB / 4) + ch) * 64 * 4)[lane];
+          bv[t][de][0] = v[0]; bv[t][de][1] = v[1]; bv[t][de][2] = v[2]; bv[t][de][3] = v[3];
+        }
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4)
+#pragma unroll
+        for (int t = 0; t < K::TPQ; ++t)
+#pragma unroll
+          for (int de = 0; de < d; ++de) acc[t][de] = mfma(xa[ch * 4 + w4][de], bv[t][de][w4], acc[t][de]);
+    }
+    // acc[t][de] register v = Y[row = 16rt + 4g + v][ga = 16*(q*TPQ + t) + c] for delta de
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t orow = rt * 16 + 4 * g + v;
+      if (orow >= N) continue;
+      float* yr = y + orow * out_w + (int64_t)al * c_ * d;
+#pragma unroll
+      for (int t = 0; t < K::TPQ; ++t) {
+        const int ga = 16 * (q * K::TPQ + t) + c;
+        if constexpr (d == 4) {
+          *reinterpret_cast<f4*>(yr + ga * 4) = f4{acc[t][0][v], acc[t][1][v], acc[t][2][v], acc[t][3][v]};
+        } else if constexpr (d == 2) {
+          *reinterpret_cast<f2*>(yr + ga * 2) = f2{acc[t][0][v], acc[t][1][v]};
+        } else {
+          yr[ga] = acc[t][0][v];
+        }
+      }
+    }
+  }
+}
+
+struct KsEntry {
+  int b, c, d;
+  bool ok;
+  size_t lds;
+  const void* kf32;
+  const void* kbf16;
+};
+
+#define KS_ENTRY(B, C, D)                                                                                 \
+  KsEntry{B, C, D, KS<B, C, D>::OK, KS<B, C, D>::LDS, (const void*)&ks_mfma_kernel<KS<B, C, D>, float>,   \
+          (const void*)&ks_mfma_kernel<KS<B, C, D>, uint16_t>}
+
+// The ViT-S/16 MLP pattern (b, c, d) = (48, 192, 4), plus
+// the Kronecker-layer factors written as KS matrices with d = 1.
+const KsEntry kKsTable[] = {
+    KS_ENTRY(48, 192, 4), KS_ENTRY(32, 128, 1), KS_ENTRY(128, 32, 1), KS_ENTRY(64, 64, 1),
+};
+
+const KsEntry* ks_find(int b, int c, int d) {
+  for (const KsEntry& e : kKsTable)
+    if (e.b == b && e.c == c && e.d == d && e.ok) return &e;
+  return nullptr;
+}
+
+int device_cus_ks() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) return 256;
+  return v;
+}
+
+}  // namespace
+
+bool ks_mfma_supported(int a, int b, int c, int d) {
+  (void)a;
+  return ks_find(b, c, d) != nullptr;
+}
+
+hipError_t launch_ks_mfma(const KSArgs& k, hipStream_t s) {
+  const KsEntry* e = ks_find(k.b, k.c, k.d);
+  if (!e) return hipErrorInvalidValue;
+  if (k.N == 0) return hipSuccess;
+  const void* fn = k.dtype == KRON_F32 ? e->kf32 : e->kbf16;
+  (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)e->lds);
+  // one workgroup per compute unit, split evenly between the alphas
+  int per_alpha = device_cus_ks() / k.a;
+  if (per_alpha < 1) per_alpha = 1;
+  const int64_t tasks = (k.N + 15) / 16 * 4;
+  const int64_t need = (tasks + kWaves - 1) / kWaves;
+  if (per_alpha > need) per_alpha = (int)need;
+  const int grid = per_alpha * k.a;
+  void* args[] = {(void*)&k.N, (void*)&k.a, (void*)&k.x, (void*)&k.vals, (void*)&k.y};
+  return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, e->lds, s);
+}
+
+}  // namespace kron
