@@ -196,17 +196,19 @@ __global__ __launch_bounds__(kThreads) void bwd_generic_kernel(
   }
 }
 
-// part is G x PW.  Block (16, 16): threadIdx.x picks VEC consecutive columns (read as one
-// vector), threadIdx.y the rows g = threadIdx.y (mod 16) with four loads in flight per
-// step.  The fp64 per-thread sums are combined in a fixed tree, so the result does not
-// depend on timing.
-template <int VEC>
-__global__ __launch_bounds__(256) void column_reduce_kernel(const float* __restrict__ part, int G, int PW,
-                                                            RedPlan plan) {
+// part is G x PW.  A workgroup of CX * RY threads reduces CX * VEC consecutive columns
+// (one 128-byte line of each partial row): thread (tx, ty) reads VEC columns as one
+// vector from rows g = ty (mod RY), eight loads in flight, and sums them in fp64 in row
+// order; the RY per-thread sums are then combined in a fixed tree, so the result does
+// not depend on timing.
+template <int VEC, int CX, int RY>
+__global__ __launch_bounds__(CX * RY) void column_reduce_kernel(const float* __restrict__ part, int G, int PW,
+                                                                RedPlan plan) {
   typedef float fv __attribute__((ext_vector_type(VEC)));
-  __shared__ double red[16][16 * VEC];
-  const int col0 = (blockIdx.x * 16 + threadIdx.x) * VEC;
-  const int ty = threadIdx.y;
+  constexpr int U = 8;
+  __shared__ double red[RY][CX * VEC];
+  const int tx = threadIdx.x % CX, ty = threadIdx.x / CX;
+  const int col0 = (blockIdx.x * CX + tx) * VEC;
   double s[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) s[v] = 0.0;
@@ -214,29 +216,29 @@ __global__ __launch_bounds__(256) void column_reduce_kernel(const float* __restr
     const float* p = part + col0;
     auto ld = [&](int g) { return *reinterpret_cast<const fv*>(p + (int64_t)g * PW); };
     int g = ty;
-    for (; g + 48 < G; g += 64) {
-      const fv a0 = ld(g), a1 = ld(g + 16), a2 = ld(g + 32), a3 = ld(g + 48);
+    for (; g + (U - 1) * RY < G; g += U * RY) {
+      fv a[U];
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        s[v] += (double)a0[v];
-        s[v] += (double)a1[v];
-        s[v] += (double)a2[v];
-        s[v] += (double)a3[v];
-      }
+      for (int u = 0; u < U; ++u) a[u] = ld(g + u * RY);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) s[v] += (double)a[u][v];
     }
-    for (; g < G; g += 16) {
+    for (; g < G; g += RY) {
       const fv a = ld(g);
 #pragma unroll
       for (int v = 0; v < VEC; ++v) s[v] += (double)a[v];
     }
   }
 #pragma unroll
-  for (int v = 0; v < VEC; ++v) red[ty][threadIdx.x * VEC + v] = s[v];
+  for (int v = 0; v < VEC; ++v) red[ty][tx * VEC + v] = s[v];
   __syncthreads();
-  for (int h = 8; h >= 1; h /= 2) {
+#pragma unroll
+  for (int h = RY / 2; h >= 1; h /= 2) {
     if (ty < h)
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) red[ty][threadIdx.x * VEC + v] += red[ty + h][threadIdx.x * VEC + v];
+      for (int v = 0; v < VEC; ++v) red[ty][tx * VEC + v] += red[ty + h][tx * VEC + v];
     __syncthreads();
   }
   if (ty == 0) {
@@ -244,7 +246,7 @@ __global__ __launch_bounds__(256) void column_reduce_kernel(const float* __restr
     for (int v = 0; v < VEC; ++v) {
       int c = col0 + v;
       if (c >= PW) break;
-      const double tot = red[0][threadIdx.x * VEC + v];
+      const double tot = red[0][tx * VEC + v];
       for (int k = 0; k < plan.nseg; ++k) {
         if (c < plan.seg[k].count) {
           if (plan.seg[k].dst) plan.seg[k].dst[c] = (float)(tot * (double)plan.seg[k].scale);
@@ -310,11 +312,11 @@ hipError_t launch_column_reduce(const float* part, int32_t G, int32_t PW, const 
   if (PW == 0) return hipSuccess;
   // vector loads need every row of the partial block 16-byte aligned
   if (PW % 4 == 0 && ((uintptr_t)part & 15) == 0)
-    hipLaunchKernelGGL(column_reduce_kernel<4>, dim3((PW + 63) / 64), dim3(16, 16), 0, stream, part, G, PW,
-                       plan);
+    hipLaunchKernelGGL((column_reduce_kernel<4, 8, 64>), dim3((PW + 31) / 32), dim3(512), 0, stream, part, G,
+                       PW, plan);
   else
-    hipLaunchKernelGGL(column_reduce_kernel<1>, dim3((PW + 15) / 16), dim3(16, 16), 0, stream, part, G, PW,
-                       plan);
+    hipLaunchKernelGGL((column_reduce_kernel<1, 32, 16>), dim3((PW + 31) / 32), dim3(512), 0, stream, part, G,
+                       PW, plan);
   return hipGetLastError();
 }
 

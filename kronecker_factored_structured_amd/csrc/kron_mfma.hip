@@ -244,6 +244,13 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
   extern __shared__ float lds[];
   float* bop = lds;              // B_i[g*SA+s][16tb+c]
   float* cop = bop + D::BOP;     // C_i[16tj+4g+v][16tk+c]
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  const int wave = threadIdx.x >> 6;
+  const int64_t stride = (int64_t)gridDim.x * kWaves;
+  int64_t row = (int64_t)blockIdx.x * kWaves + wave;
+  // the first row's X is loaded while the tables are built
+  float xa[D::TJ][D::SA];   // X[j = 16tj+c][a = g*SA+s]
+  if (row < N) load_xa<D>(xa, x + row * D::IN, g, c);
   if constexpr (D::FWD_RAW) {
     float* rB = cop + D::COPF;
     float* rC = rB + D::RAWB;
@@ -269,8 +276,6 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
   }
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-  const int wave = threadIdx.x >> 6;
   f4 bb[D::TB][D::TK];
 #pragma unroll
   for (int tb = 0; tb < D::TB; ++tb)
@@ -282,9 +287,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
     }
   const bool relu = flags & KRON_RELU_OUT;
 
-  for (int64_t row = (int64_t)blockIdx.x * kWaves + wave; row < N; row += (int64_t)gridDim.x * kWaves) {
-    float xa[D::TJ][D::SA];   // X[j = 16tj+c][a = g*SA+s]
-    load_xa<D>(xa, x + row * D::IN, g, c);
+  for (; row < N; row += stride) {
     f4 acc[D::TB][D::TK];
 #pragma unroll
     for (int tb = 0; tb < D::TB; ++tb)
@@ -336,6 +339,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
           *reinterpret_cast<f4*>(yr + k * D::N + b0) = o;
         }
       }
+    if (row + stride < N) load_xa<D>(xa, x + (row + stride) * D::IN, g, c);
   }
 }
 
