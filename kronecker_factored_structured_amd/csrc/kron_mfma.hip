@@ -31,6 +31,7 @@
 // order, turns dC into its shares of dA and dS, and writes one partial row per workgroup;
 // the shared fixed-order column reduction finishes the sums.
 #include <atomic>
+#include <type_traits>
 
 #include "kron_internal.h"
 
@@ -287,7 +288,16 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
     }
   const bool relu = flags & KRON_RELU_OUT;
 
+  // The next row's X is loaded at the top of each row (the last row reloads itself), and
+  // a scheduling barrier keeps the compiler from sinking those loads towards their use.
+  float xn[D::TJ][D::SA];
+  settle(xa);
   for (; row < N; row += stride) {
+    {
+      const int64_t nr = row + stride < N ? row + stride : row;
+      load_xa<D>(xn, x + nr * D::IN, g, c);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     f4 acc[D::TB][D::TK];
 #pragma unroll
     for (int tb = 0; tb < D::TB; ++tb)
@@ -339,7 +349,10 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
           *reinterpret_cast<f4*>(yr + k * D::N + b0) = o;
         }
       }
-    if (row + stride < N) load_xa<D>(xa, x + (row + stride) * D::IN, g, c);
+#pragma unroll
+    for (int tj = 0; tj < D::TJ; ++tj)
+#pragma unroll
+      for (int s = 0; s < D::SA; ++s) xa[tj][s] = xn[tj][s];
   }
 }
 
@@ -676,7 +689,10 @@ struct RP {
 
 __device__ __forceinline__ int kidx(int s, int g) { return 16 * (s >> 2) + 4 * g + (s & 3); }
 
-template <class D>
+// DXM: 0 = no dX, 1 = dX, 2 = dX masked by [x > 0].  With the mode fixed at compile time
+// and the one partial row group peeled off the loop, every step issues the same stores,
+// so the wait for the next step's prefetched rows does not also wait for them.
+template <class D, int DXM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_rp_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, const float* __restrict__ Sm,
                    const float* __restrict__ A, const float* __restrict__ B, const float* __restrict__ dy,
@@ -753,8 +769,7 @@ void bwd_rp_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, const
   float* gs = wreg + wave * Q::WREG;      // G[j][b] as gs[b * LDGT + j]; later dX^T partial [j][a]
   const float* Xs = rowbuf + slot * Q::SLOT;
   const float* Ys = Xs + Q::XR * Q::LX;
-  const bool want_dx = dx != nullptr;
-  const bool mask = flags & KRON_DX_RELU_MASK;
+  (void)flags;
 
   f4 dC[D::TJ][D::TK];    // dC_rank[j = 16tj+4g+v][k = 16tk+c]
   f4 dB[D::TA][D::TB];    // dB_rank[a = 16ta+4g+v][b = 16tb+c]
@@ -772,7 +787,8 @@ void bwd_rp_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, const
 #pragma unroll
     for (int tb = 0; tb < D::TB; ++tb) db[tk][tb] = f4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t grp = blockIdx.x; grp < ngrp; grp += gridDim.x) {
+  auto step = [&](int64_t grp, auto tail_c) {
+    constexpr bool kTail = decltype(tail_c)::value;
     stash();
     __syncthreads();
     fetch(grp + gridDim.x);
@@ -889,27 +905,37 @@ void bwd_rp_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, const
       for (int tj = 0; tj < D::TJ; ++tj)
         *reinterpret_cast<f4*>(gs + (16 * tj + c) * Q::LDXP + 16 * ta + 4 * g) = dxt[ta][tj];
     __syncthreads();
-    // dX of the step's rows: add the R rank partials of each row in rank order
-    if (want_dx) {
+    // dX of the step's rows: add the R rank partials of each row in rank order (the mask
+    // reads x from the row's LDS copy)
+    if constexpr (DXM != 0) {
       constexpr int PER_ROW = D::IN / 4;
-      for (int f = tid; f < Q::RPI * PER_ROW; f += kThreads) {
+      constexpr int TOT = Q::RPI * PER_ROW;
+#pragma unroll
+      for (int t = 0; t < (TOT + kThreads - 1) / kThreads; ++t) {
+        const int f = tid + t * kThreads;
+        if (TOT % kThreads != 0 && f >= TOT) continue;
         const int s = f / PER_ROW, o = 4 * (f % PER_ROW);
         const int64_t row = grp * Q::RPI + s;
-        if (row >= N) continue;
+        if (kTail && row >= N) continue;
         const int j = o / D::M, a = o % D::M;
         f4 acc = *reinterpret_cast<const f4*>(wreg + (s * Q::R) * Q::WREG + j * Q::LDXP + a);
 #pragma unroll
         for (int i = 1; i < Q::R; ++i)
           acc += *reinterpret_cast<const f4*>(wreg + (s * Q::R + i) * Q::WREG + j * Q::LDXP + a);
-        if (mask) {
-          const f4 xv = *reinterpret_cast<const f4*>(x + row * D::IN + o);
+        if constexpr (DXM == 2) {
+          const f4 xv = *reinterpret_cast<const f4*>(rowbuf + s * Q::SLOT + j * Q::LX + a);
 #pragma unroll
           for (int v = 0; v < 4; ++v) acc[v] = xv[v] > 0.f ? acc[v] : 0.f;
         }
         *reinterpret_cast<f4*>(dx + row * D::IN + o) = acc;
       }
     }
-  }
+  };
+  // groups whose rows are all valid, then the one partial group (if N % RPI != 0)
+  const int64_t nfull = N / Q::RPI;
+  int64_t grp = blockIdx.x;
+  for (; grp < nfull; grp += gridDim.x) step(grp, std::false_type{});
+  if (grp < ngrp) step(grp, std::true_type{});
 
   // Partial row of this workgroup: [dB (R*M*N) | dA (R*P*Q) | dS (P*Q) | dbias (Q*N)].
   __syncthreads();
@@ -1016,13 +1042,25 @@ template <class D>
 void run_bwd(const LayerArgs& a, int grid, hipStream_t s) {
   if constexpr (RP<D>::OK) {
     static const bool attr = [] {
-      (void)hipFuncSetAttribute((const void*)bwd_rp_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      (void)hipFuncSetAttribute((const void*)bwd_rp_kernel<D, 0>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)RP<D>::LDS);
+      (void)hipFuncSetAttribute((const void*)bwd_rp_kernel<D, 1>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)RP<D>::LDS);
+      (void)hipFuncSetAttribute((const void*)bwd_rp_kernel<D, 2>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)RP<D>::LDS);
       return true;
     }();
     (void)attr;
-    hipLaunchKernelGGL(bwd_rp_kernel<D>, dim3(grid), dim3(kThreads), RP<D>::LDS, s, a.N, a.flags, a.x, a.S,
-                       a.A, a.B, a.dy, a.dx, a.part);
+    const int dxm = a.dx == nullptr ? 0 : ((a.flags & KRON_DX_RELU_MASK) ? 2 : 1);
+    if (dxm == 0)
+      hipLaunchKernelGGL((bwd_rp_kernel<D, 0>), dim3(grid), dim3(kThreads), RP<D>::LDS, s, a.N, a.flags, a.x,
+                         a.S, a.A, a.B, a.dy, a.dx, a.part);
+    else if (dxm == 1)
+      hipLaunchKernelGGL((bwd_rp_kernel<D, 1>), dim3(grid), dim3(kThreads), RP<D>::LDS, s, a.N, a.flags, a.x,
+                         a.S, a.A, a.B, a.dy, a.dx, a.part);
+    else
+      hipLaunchKernelGGL((bwd_rp_kernel<D, 2>), dim3(grid), dim3(kThreads), RP<D>::LDS, s, a.N, a.flags, a.x,
+                         a.S, a.A, a.B, a.dy, a.dx, a.part);
   } else if constexpr (D::BWD_OK) {
     static const bool attr = [] {
       (void)hipFuncSetAttribute((const void*)bwd_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
