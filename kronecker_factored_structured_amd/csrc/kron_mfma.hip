@@ -95,11 +95,16 @@ __device__ __forceinline__ void table_read(float (&dst)[L], const float* blk, in
 
 // Lay out table[i][tile][chunk][lane][w] (i < R, tile < T, L values per lane) from
 // val(i, tile, g, c, s) with s = chunk * W + w.
+// (fully unrolled, so that a thread's reads of the source values are all in flight at once)
 template <int R, int T, int L, class F>
 __device__ __forceinline__ void build_table(float* tab, F val) {
   constexpr int W = chunk_width<L>();
   constexpr int total = R * T * 64 * L;
-  for (int e = threadIdx.x; e < total; e += kThreads) {
+  constexpr int iters = (total + kThreads - 1) / kThreads;
+#pragma unroll
+  for (int it = 0; it < iters; ++it) {
+    const int e = threadIdx.x + it * kThreads;
+    if (total % kThreads != 0 && e >= total) break;
     int r = e;
     const int w = r % W; r /= W;
     const int l = r % 64; r /= 64;
