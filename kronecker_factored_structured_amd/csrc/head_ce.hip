@@ -107,7 +107,8 @@ __global__ __launch_bounds__(kThreads) void head_dw_kernel(int64_t N, int K, int
   const int64_t r0 = (int64_t)blockIdx.y * R;
   const int64_t r1 = (r0 + R) < N ? (r0 + R) : N;
   const int64_t PW = (int64_t)K * C + C + 1;
-  float* out = part + (int64_t)blockIdx.y * PW;
+  const PartRow out{part, (int64_t)gridDim.y, (int64_t)blockIdx.y, 0};
+  (void)PW;
   float acc[CMAX];
 #pragma unroll
   for (int c = 0; c < CMAX; ++c) acc[c] = 0.f;

@@ -111,7 +111,7 @@ BwdPlan bwd_plan(const kron_shape_t* s, bool want_dx) {
     pl.G = kron::generic_bwd_groups(s->N, T);
   }
   const int64_t PW = kron::partial_width(s->p, s->q, s->m, s->n, s->r);
-  pl.ws_bytes = (size_t)pl.G * (size_t)PW * sizeof(float);
+  pl.ws_bytes = (size_t)kron::part_floats(pl.G, PW) * sizeof(float);
   return pl;
 }
 
@@ -302,7 +302,7 @@ int32_t kron_adam_l1_step(int32_t ntensors, float* const* params, const float* c
 size_t kron_head_ce_workspace_bytes(int64_t N, int32_t K, int32_t C) {
   if (N < 0 || K < 1 || C < 1) return 0;
   const int G = kron::head_groups(N);
-  const size_t floats = (size_t)N * C + (size_t)N + (size_t)G * ((size_t)K * C + C + 1);
+  const size_t floats = (size_t)N * C + (size_t)N + (size_t)kron::part_floats(G, (int64_t)K * C + C + 1);
   return ((floats * 4 + 255) & ~size_t(255)) + 256;
 }
 

@@ -100,10 +100,10 @@ __global__ __launch_bounds__(kThreads) void bwd_generic_kernel(
   float* dXs = Ss + pq;          // T x in (only with dx)
   const int tid = threadIdx.x;
   const int PW = (int)partial_width(p, q, m, n, r);
-  float* pdB = part + (int64_t)blockIdx.x * PW;
-  float* pdC = pdB + r * mn;     // dC_i during the loop, dA_i at the end
-  float* pdS = pdC + r * pq;
-  float* pdb = pdS + pq;
+  const PartRow pdB{part, (int64_t)gridDim.x, (int64_t)blockIdx.x, 0};
+  const PartRow pdC = pdB + r * mn;   // dC_i during the loop, dA_i at the end
+  const PartRow pdS = pdC + r * pq;
+  const PartRow pdb = pdS + pq;
   for (int e = tid; e < PW; e += kThreads) pdB[e] = 0.f;
   if (S)
     for (int e = tid; e < pq; e += kThreads) Ss[e] = S[e];
@@ -196,25 +196,25 @@ __global__ __launch_bounds__(kThreads) void bwd_generic_kernel(
   }
 }
 
-// part is G x PW.  A workgroup of CX * RY threads reduces CX * VEC consecutive columns
-// (one 128-byte line of each partial row): thread (tx, ty) reads VEC columns as one
-// vector from rows g = ty (mod RY), eight loads in flight, and sums them in fp64 in row
-// order; the RY per-thread sums are then combined in a fixed tree, so the result does
-// not depend on timing.
+// A workgroup of CX * RY threads reduces one block of CX * VEC = kRedCols columns: thread
+// (tx, ty) reads VEC columns as one vector from partial rows g = ty (mod RY), eight
+// loads in flight, and sums them in fp64 in row order; the RY per-thread sums are then
+// combined in a fixed tree, so the result does not depend on timing.
 template <int VEC, int CX, int RY>
 __global__ __launch_bounds__(CX * RY) void column_reduce_kernel(const float* __restrict__ part, int G, int PW,
                                                                 RedPlan plan) {
+  static_assert(CX * VEC == kRedCols, "one workgroup per column block");
   typedef float fv __attribute__((ext_vector_type(VEC)));
   constexpr int U = 8;
   __shared__ double red[RY][CX * VEC];
   const int tx = threadIdx.x % CX, ty = threadIdx.x / CX;
-  const int col0 = (blockIdx.x * CX + tx) * VEC;
+  const int col0 = blockIdx.x * kRedCols + tx * VEC;
   double s[VEC];
 #pragma unroll
   for (int v = 0; v < VEC; ++v) s[v] = 0.0;
-  if (col0 < PW) {
-    const float* p = part + col0;
-    auto ld = [&](int g) { return *reinterpret_cast<const fv*>(p + (int64_t)g * PW); };
+  {
+    const float* p = part + (int64_t)blockIdx.x * G * kRedCols + tx * VEC;
+    auto ld = [&](int g) { return *reinterpret_cast<const fv*>(p + (int64_t)g * kRedCols); };
     int g = ty;
     for (; g + (U - 1) * RY < G; g += U * RY) {
       fv a[U];
@@ -310,13 +310,12 @@ hipError_t launch_bwd_generic(const LayerArgs& a, int G, hipStream_t s) {
 hipError_t launch_column_reduce(const float* part, int32_t G, int32_t PW, const RedPlan& plan,
                                 hipStream_t stream) {
   if (PW == 0) return hipSuccess;
-  // vector loads need every row of the partial block 16-byte aligned
-  if (PW % 4 == 0 && ((uintptr_t)part & 15) == 0)
-    hipLaunchKernelGGL((column_reduce_kernel<4, 8, 64>), dim3((PW + 31) / 32), dim3(512), 0, stream, part, G,
-                       PW, plan);
+  // 16-byte vector loads need the partial sums 16-byte aligned (workspaces are 256-byte aligned)
+  const unsigned blocks = (unsigned)((PW + kRedCols - 1) / kRedCols);
+  if (((uintptr_t)part & 15) == 0)
+    hipLaunchKernelGGL((column_reduce_kernel<4, 8, 64>), dim3(blocks), dim3(512), 0, stream, part, G, PW, plan);
   else
-    hipLaunchKernelGGL((column_reduce_kernel<1, 32, 16>), dim3((PW + 31) / 32), dim3(512), 0, stream, part, G,
-                       PW, plan);
+    hipLaunchKernelGGL((column_reduce_kernel<1, 32, 16>), dim3(blocks), dim3(512), 0, stream, part, G, PW, plan);
   return hipGetLastError();
 }
 

@@ -11,10 +11,28 @@
 namespace kron {
 
 // ---------------------------------------------------------------------------------
-// Column reduction of per-workgroup partial sums: part is G x PW fp32 (row g holds
-// workgroup g's partial sums); column c is summed over g in a fixed order in fp64 and
-// written, scaled, to the segment that covers c.
+// Column reduction of per-workgroup partial sums: G partial rows of PW fp32 columns
+// (row g holds workgroup g's partial sums); column c is summed over g in a fixed order
+// in fp64 and written, scaled, to the segment that covers c.
+//
+// Storage is blocked by columns: the G values of a block of kRedCols columns are
+// contiguous (G x kRedCols floats, block after block), so a producer writes its row as
+// whole 128-byte lines and the reduction of a block reads one contiguous range.
 // ---------------------------------------------------------------------------------
+constexpr int kRedCols = 32;
+__host__ __device__ inline int64_t part_floats(int64_t G, int64_t PW) {
+  return G * ((PW + kRedCols - 1) / kRedCols) * kRedCols;
+}
+__host__ __device__ inline int64_t part_index(int64_t G, int64_t g, int64_t col) {
+  return (col / kRedCols) * G * kRedCols + g * kRedCols + col % kRedCols;
+}
+// Row g of the partial sums, from column `off` on.
+struct PartRow {
+  float* part;
+  int64_t G, g, off;
+  __device__ float& operator[](int64_t col) const { return part[part_index(G, g, off + col)]; }
+  __device__ PartRow operator+(int64_t d) const { return PartRow{part, G, g, off + d}; }
+};
 struct RedSeg {
   float* dst;     // NULL: skip this segment
   int32_t count;  // columns in this segment
@@ -47,7 +65,7 @@ struct LayerArgs {
   float* dA;
   float* dB;
   float* dbias;
-  float* part;   // workspace: G x PW partial sums
+  float* part;   // workspace: G partial rows of PW columns (column-blocked)
 };
 
 // Partial sums of one backward workgroup, in this order:
@@ -133,7 +151,7 @@ struct HeadArgs {
   float* dW;
   float* db;
   float* dz;     // workspace: N x C
-  float* part;   // workspace: G x (K*C + C + 1)
+  float* part;   // workspace: G partial rows of K*C + C + 1 columns (column-blocked)
 };
 int head_groups(int64_t N);
 int64_t head_rows_per_group(int64_t N);

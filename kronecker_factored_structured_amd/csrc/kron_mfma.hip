@@ -631,7 +631,7 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
         if (k < D::Q && b < D::N) red[D::R * (MN + PQ) + k * D::N + b] = db[tk][tb][v];
       }
   __syncthreads();
-  float* out = part + (int64_t)blockIdx.x * D::PW;
+  const PartRow out{part, (int64_t)gridDim.x, (int64_t)blockIdx.x, 0};
   auto wsum = [&](int e) {
     float t = lds[e];
 #pragma unroll
@@ -976,7 +976,7 @@ void bwd_rp_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, const
         }
   }
   __syncthreads();
-  float* out = part + (int64_t)blockIdx.x * D::PW;
+  const PartRow out{part, (int64_t)gridDim.x, (int64_t)blockIdx.x, 0};
   auto ssum = [&](int e) {
     float t = lds[e];
 #pragma unroll
