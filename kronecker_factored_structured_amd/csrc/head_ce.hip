@@ -176,9 +176,9 @@ hipError_t launch_head(const HeadArgs& a, int G, hipStream_t s) {
   }
   RedPlan plan{};
   plan.nseg = 3;
-  plan.seg[0] = RedSeg{a.dW, a.K * a.C, 1.f};
-  plan.seg[1] = RedSeg{a.db, a.C, 1.f};
-  plan.seg[2] = RedSeg{a.loss, 1, a.N > 0 ? (float)(1.0 / (double)a.N) : 0.f};
+  plan.seg[0] = RedSeg{a.dW, a.K * a.C, 1.f, 0};
+  plan.seg[1] = RedSeg{a.db, a.C, 1.f, 0};
+  plan.seg[2] = RedSeg{a.loss, 1, a.N > 0 ? (float)(1.0 / (double)a.N) : 0.f, 0};
   return launch_column_reduce(a.part, G, a.K * a.C + a.C + 1, plan, s);
 }
 

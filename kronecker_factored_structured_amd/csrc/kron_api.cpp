@@ -94,17 +94,25 @@ int32_t check_shape(const kron_shape_t* s) {
 }
 
 // Which backward kernel runs for a shape, with how many workgroups (= partial rows).
+// chunk > 0: the ranks run in passes of `chunk` ranks each (partial rows per pass).
 struct BwdPlan {
   bool mfma;
+  int chunk;
   int G;
   size_t ws_bytes;
 };
 
 BwdPlan bwd_plan(const kron_shape_t* s, bool want_dx) {
-  BwdPlan pl{false, 0, 0};
+  BwdPlan pl{false, 0, 0, 0};
   if (kron::mfma_bwd_supported(s->p, s->q, s->m, s->n, s->r)) {
     pl.mfma = true;
     pl.G = kron::mfma_bwd_groups(s->N, s->p, s->q, s->m, s->n, s->r);
+  } else if ((pl.chunk = kron::mfma_bwd_chunk(s->p, s->q, s->m, s->n, s->r)) > 0) {
+    pl.mfma = true;
+    pl.G = kron::mfma_bwd_groups(s->N, s->p, s->q, s->m, s->n, pl.chunk);
+    const int64_t PWc = kron::partial_width(s->p, s->q, s->m, s->n, pl.chunk);
+    pl.ws_bytes = (size_t)kron::part_floats(pl.G, PWc) * sizeof(float);
+    return pl;
   } else {
     const int T = kron::generic_bwd_rows_per_tile(s->p, s->q, s->m, s->n, want_dx);
     if (T == 0) return pl;
@@ -219,14 +227,41 @@ int32_t kron_linear_bwd(const kron_shape_t* s, const float* x, const float* S, c
   a.dS = dS; a.dA = dA; a.dB = dB; a.dbias = dbias;
   a.part = (float*)workspace;
   const BwdPlan pl = bwd_plan(s, a.dx != nullptr);
+  const int32_t pq32 = s->p * s->q, mn32 = s->m * s->n;
+  if (pl.chunk > 0) {
+    // ranks in passes of pl.chunk: pass c handles ranks [c*chunk, (c+1)*chunk); dX is
+    // written by the first pass and added to by the others (the ReLU mask, if any, is
+    // applied by the last pass), dS sums over the passes and dbias comes from the first
+    const int passes = s->r / pl.chunk;
+    const int32_t PWc = (int32_t)kron::partial_width(s->p, s->q, s->m, s->n, pl.chunk);
+    for (int c = 0; c < passes; ++c) {
+      kron::LayerArgs ac = a;
+      ac.r = pl.chunk;
+      ac.A = A + (size_t)c * pl.chunk * pq32;
+      ac.B = B + (size_t)c * pl.chunk * mn32;
+      ac.flags = (c == passes - 1) ? s->flags : (s->flags & ~KRON_DX_RELU_MASK);
+      ac.dx_accumulate = c > 0;
+      hipError_t e = kron::launch_bwd_mfma(ac, pl.G, stream);
+      if (e != hipSuccess) return hip_fail(e, "kron_linear_bwd launch");
+      kron::RedPlan rp{};
+      rp.nseg = 4;
+      rp.seg[0] = kron::RedSeg{dB + (size_t)c * pl.chunk * mn32, pl.chunk * mn32, 1.f, 0};
+      rp.seg[1] = kron::RedSeg{dA + (size_t)c * pl.chunk * pq32, pl.chunk * pq32, 1.f, 0};
+      rp.seg[2] = kron::RedSeg{dS, pq32, 1.f, c > 0};
+      rp.seg[3] = kron::RedSeg{c == 0 ? dbias : nullptr, s->q * s->n, 1.f, 0};
+      e = kron::launch_column_reduce(a.part, pl.G, PWc, rp, stream);
+      if (e != hipSuccess) return hip_fail(e, "kron_linear_bwd reduce launch");
+    }
+    return ok();
+  }
   hipError_t e = pl.mfma ? kron::launch_bwd_mfma(a, pl.G, stream) : kron::launch_bwd_generic(a, pl.G, stream);
   if (e != hipSuccess) return hip_fail(e, "kron_linear_bwd launch");
   kron::RedPlan rp{};
   rp.nseg = 4;
-  rp.seg[0] = kron::RedSeg{dB, s->r * s->m * s->n, 1.f};
-  rp.seg[1] = kron::RedSeg{dA, s->r * s->p * s->q, 1.f};
-  rp.seg[2] = kron::RedSeg{dS, s->p * s->q, 1.f};
-  rp.seg[3] = kron::RedSeg{dbias, s->q * s->n, 1.f};
+  rp.seg[0] = kron::RedSeg{dB, s->r * mn32, 1.f, 0};
+  rp.seg[1] = kron::RedSeg{dA, s->r * pq32, 1.f, 0};
+  rp.seg[2] = kron::RedSeg{dS, pq32, 1.f, 0};
+  rp.seg[3] = kron::RedSeg{dbias, s->q * s->n, 1.f, 0};
   const int32_t PW = (int32_t)kron::partial_width(s->p, s->q, s->m, s->n, s->r);
   e = kron::launch_column_reduce(a.part, pl.G, PW, rp, stream);
   if (e != hipSuccess) return hip_fail(e, "kron_linear_bwd reduce launch");

@@ -249,7 +249,11 @@ __global__ __launch_bounds__(CX * RY) void column_reduce_kernel(const float* __r
       const double tot = red[0][tx * VEC + v];
       for (int k = 0; k < plan.nseg; ++k) {
         if (c < plan.seg[k].count) {
-          if (plan.seg[k].dst) plan.seg[k].dst[c] = (float)(tot * (double)plan.seg[k].scale);
+          if (plan.seg[k].dst) {
+            double v = tot * (double)plan.seg[k].scale;
+            if (plan.seg[k].accumulate) v += (double)plan.seg[k].dst[c];
+            plan.seg[k].dst[c] = (float)v;
+          }
           break;
         }
         c -= plan.seg[k].count;

@@ -34,9 +34,10 @@ struct PartRow {
   __device__ PartRow operator+(int64_t d) const { return PartRow{part, G, g, off + d}; }
 };
 struct RedSeg {
-  float* dst;     // NULL: skip this segment
-  int32_t count;  // columns in this segment
+  float* dst;          // NULL: skip this segment
+  int32_t count;       // columns in this segment
   float scale;
+  int32_t accumulate;  // 0: dst = scale * sum;  1: dst += scale * sum
 };
 constexpr int kMaxRedSeg = 4;
 struct RedPlan {
@@ -66,6 +67,7 @@ struct LayerArgs {
   float* dB;
   float* dbias;
   float* part;   // workspace: G partial rows of PW columns (column-blocked)
+  int32_t dx_accumulate;   // backward: dx += this call's dX (before the optional mask)
 };
 
 // Partial sums of one backward workgroup, in this order:
@@ -89,6 +91,9 @@ hipError_t launch_bwd_generic(const LayerArgs& a, int G, hipStream_t s);
 bool mfma_fwd_supported(int p, int q, int m, int n, int r);
 bool mfma_bwd_supported(int p, int q, int m, int n, int r);
 int mfma_bwd_groups(int64_t N, int p, int q, int m, int n, int r);
+// Ranks per chunk when a backward with r ranks runs as r / chunk passes of the
+// chunk-rank MFMA kernel (dX accumulated over the passes), else 0.
+int mfma_bwd_chunk(int p, int q, int m, int n, int r);
 hipError_t launch_fwd_mfma(const LayerArgs& a, hipStream_t s);
 hipError_t launch_bwd_mfma(const LayerArgs& a, int G, hipStream_t s);
 

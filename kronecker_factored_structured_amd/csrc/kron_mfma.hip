@@ -688,17 +688,21 @@ struct RP {
   static constexpr size_t LDS = (size_t)(MAIN > COMBINE ? MAIN : COMBINE) * 4;
   static constexpr int NF4 = ROWBUF / SLOT * (D::IN + D::OUT) / 4;   // float4s staged per step
   static constexpr int NPF = (NF4 + kThreads - 1) / kThreads;
-  static constexpr bool OK = (R == 1 || R == 2 || R == 4) && LDS * 2 <= kMaxLds && D::IN % 4 == 0 &&
+  // workgroups per compute unit: two when their LDS fits twice (two wavefronts per SIMD),
+  // else one (one wavefront per SIMD, with the whole register file)
+  static constexpr int WPC = LDS * 2 <= kMaxLds ? 2 : 1;
+  static constexpr bool OK = (R == 1 || R == 2 || R == 4) && LDS <= kMaxLds && D::IN % 4 == 0 &&
                              D::OUT % 4 == 0;
 };
 
 __device__ __forceinline__ int kidx(int s, int g) { return 16 * (s >> 2) + 4 * g + (s & 3); }
 
-// DXM: 0 = no dX, 1 = dX, 2 = dX masked by [x > 0].  With the mode fixed at compile time
+// DXM: 0 = no dX, 1 = dX, 2 = dX masked by [x > 0], 3 = dX added to dx, 4 = dX added to
+// dx and the sum masked by [x > 0] (modes 3 and 4 serve rank chunks after the first).  With the mode fixed at compile time
 // and the one partial row group peeled off the loop, every step issues the same stores,
 // so the wait for the next step's prefetched rows does not also wait for them.
 template <class D, int DXM>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RP<D>::WPC, RP<D>::WPC)))
 void bwd_rp_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, const float* __restrict__ Sm,
                    const float* __restrict__ A, const float* __restrict__ B, const float* __restrict__ dy,
                    float* __restrict__ dx, float* __restrict__ part) {
@@ -927,7 +931,8 @@ void bwd_rp_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, const
 #pragma unroll
         for (int i = 1; i < Q::R; ++i)
           acc += *reinterpret_cast<const f4*>(wreg + (s * Q::R + i) * Q::WREG + j * Q::LDXP + a);
-        if constexpr (DXM == 2) {
+        if constexpr (DXM >= 3) acc += *reinterpret_cast<const f4*>(dx + row * D::IN + o);
+        if constexpr (DXM == 2 || DXM == 4) {
           const f4 xv = *reinterpret_cast<const f4*>(rowbuf + s * Q::SLOT + j * Q::LX + a);
 #pragma unroll
           for (int v = 0; v < 4; ++v) acc[v] = xv[v] > 0.f ? acc[v] : 0.f;
@@ -1005,6 +1010,7 @@ struct Entry {
   int p, q, m, n, r;
   bool fwd_ok, bwd_ok, bwd_rp;
   int rows_per_step;   // of the rank-parallel backward
+  int rp_per_cu;       // its workgroups per compute unit
   void (*fwd)(const LayerArgs&, int, hipStream_t);
   void (*bwd)(const LayerArgs&, int, hipStream_t);
 };
@@ -1043,9 +1049,11 @@ void run_fwd(const LayerArgs& a, int max_grid, hipStream_t s) {
   }
 }
 
-template <class D>
+// RPF: prefer the rank-parallel kernel when both backward kernels fit (measured per shape).
+template <class D, bool RPF>
 void run_bwd(const LayerArgs& a, int grid, hipStream_t s) {
-  if constexpr (RP<D>::OK) {
+  constexpr bool use_rp = RP<D>::OK && (RPF || !D::BWD_OK);
+  if constexpr (use_rp) {
     static const bool attr = [] {
       (void)hipFuncSetAttribute((const void*)bwd_rp_kernel<D, 0>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)RP<D>::LDS);
@@ -1053,19 +1061,26 @@ void run_bwd(const LayerArgs& a, int grid, hipStream_t s) {
                                 (int)RP<D>::LDS);
       (void)hipFuncSetAttribute((const void*)bwd_rp_kernel<D, 2>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)RP<D>::LDS);
+      (void)hipFuncSetAttribute((const void*)bwd_rp_kernel<D, 3>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)RP<D>::LDS);
+      (void)hipFuncSetAttribute((const void*)bwd_rp_kernel<D, 4>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)RP<D>::LDS);
       return true;
     }();
     (void)attr;
-    const int dxm = a.dx == nullptr ? 0 : ((a.flags & KRON_DX_RELU_MASK) ? 2 : 1);
-    if (dxm == 0)
-      hipLaunchKernelGGL((bwd_rp_kernel<D, 0>), dim3(grid), dim3(kThreads), RP<D>::LDS, s, a.N, a.flags, a.x,
-                         a.S, a.A, a.B, a.dy, a.dx, a.part);
-    else if (dxm == 1)
-      hipLaunchKernelGGL((bwd_rp_kernel<D, 1>), dim3(grid), dim3(kThreads), RP<D>::LDS, s, a.N, a.flags, a.x,
-                         a.S, a.A, a.B, a.dy, a.dx, a.part);
-    else
-      hipLaunchKernelGGL((bwd_rp_kernel<D, 2>), dim3(grid), dim3(kThreads), RP<D>::LDS, s, a.N, a.flags, a.x,
-                         a.S, a.A, a.B, a.dy, a.dx, a.part);
+    const bool mask = a.flags & KRON_DX_RELU_MASK;
+    const int dxm = a.dx == nullptr ? 0 : (a.dx_accumulate ? (mask ? 4 : 3) : (mask ? 2 : 1));
+#define KRON_RP_LAUNCH(M)                                                                                \
+  hipLaunchKernelGGL((bwd_rp_kernel<D, M>), dim3(grid), dim3(kThreads), RP<D>::LDS, s, a.N, a.flags, a.x, \
+                     a.S, a.A, a.B, a.dy, a.dx, a.part)
+    switch (dxm) {
+      case 0: KRON_RP_LAUNCH(0); break;
+      case 1: KRON_RP_LAUNCH(1); break;
+      case 2: KRON_RP_LAUNCH(2); break;
+      case 3: KRON_RP_LAUNCH(3); break;
+      default: KRON_RP_LAUNCH(4); break;
+    }
+#undef KRON_RP_LAUNCH
   } else if constexpr (D::BWD_OK) {
     static const bool attr = [] {
       (void)hipFuncSetAttribute((const void*)bwd_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1078,19 +1093,24 @@ void run_bwd(const LayerArgs& a, int grid, hipStream_t s) {
   }
 }
 
-#define KRON_ENTRY(P, Q, M, N, R)                                                                      \
+#define KRON_ENTRY(P, Q, M, N, R, RPF)                                                                 \
   Entry{P, Q, M, N, R, Dims<P, Q, M, N, R>::FWD_OK,                                                    \
-        Dims<P, Q, M, N, R>::BWD_OK || RP<Dims<P, Q, M, N, R>>::OK, RP<Dims<P, Q, M, N, R>>::OK,         \
-        RP<Dims<P, Q, M, N, R>>::RPI, &run_fwd<Dims<P, Q, M, N, R>>, &run_bwd<Dims<P, Q, M, N, R>>}
+        Dims<P, Q, M, N, R>::BWD_OK || RP<Dims<P, Q, M, N, R>>::OK,                                     \
+        RP<Dims<P, Q, M, N, R>>::OK && (RPF || !Dims<P, Q, M, N, R>::BWD_OK),                           \
+        RP<Dims<P, Q, M, N, R>>::RPI, RP<Dims<P, Q, M, N, R>>::WPC, &run_fwd<Dims<P, Q, M, N, R>>,        \
+        &run_bwd<Dims<P, Q, M, N, R>, RPF>}
 
 // The shapes of the workloads: the 64x64 tiny layer (m = 8), the 1024x1024 layers with
 // m = 32 and m = 64, and the GPT-2 FFN pair 768 <-> 3072.
 const Entry kTable[] = {
-    KRON_ENTRY(8, 8, 8, 8, 1),      KRON_ENTRY(8, 8, 8, 8, 2),      KRON_ENTRY(32, 32, 32, 32, 1),
-    KRON_ENTRY(32, 32, 32, 32, 2),  KRON_ENTRY(32, 32, 32, 32, 4),  KRON_ENTRY(16, 16, 64, 64, 1),
-    KRON_ENTRY(16, 16, 64, 64, 2),  KRON_ENTRY(32, 64, 24, 48, 1),  KRON_ENTRY(32, 64, 24, 48, 2),
-    KRON_ENTRY(32, 64, 24, 48, 4),  KRON_ENTRY(32, 64, 24, 48, 8),  KRON_ENTRY(64, 32, 48, 24, 1),
-    KRON_ENTRY(64, 32, 48, 24, 2),  KRON_ENTRY(64, 32, 48, 24, 4),  KRON_ENTRY(64, 32, 48, 24, 8),
+    KRON_ENTRY(8, 8, 8, 8, 1, true),       KRON_ENTRY(8, 8, 8, 8, 2, true),
+    KRON_ENTRY(32, 32, 32, 32, 1, true),   KRON_ENTRY(32, 32, 32, 32, 2, true),
+    KRON_ENTRY(32, 32, 32, 32, 4, true),   KRON_ENTRY(16, 16, 64, 64, 1, false),
+    KRON_ENTRY(16, 16, 64, 64, 2, false),  KRON_ENTRY(32, 64, 24, 48, 1, true),
+    KRON_ENTRY(32, 64, 24, 48, 2, false),  KRON_ENTRY(32, 64, 24, 48, 4, true),
+    KRON_ENTRY(32, 64, 24, 48, 8, true),   KRON_ENTRY(64, 32, 48, 24, 1, false),
+    KRON_ENTRY(64, 32, 48, 24, 2, true),   KRON_ENTRY(64, 32, 48, 24, 4, true),
+    KRON_ENTRY(64, 32, 48, 24, 8, true),
 };
 
 const Entry* find(int p, int q, int m, int n, int r) {
@@ -1111,12 +1131,19 @@ bool mfma_bwd_supported(int p, int q, int m, int n, int r) {
   return e && e->bwd_ok;
 }
 
+int mfma_bwd_chunk(int p, int q, int m, int n, int r) {
+  if (r <= 4 || r % 4 != 0 || mfma_bwd_supported(p, q, m, n, r)) return 0;
+  const Entry* e = find(p, q, m, n, 4);
+  return (e && e->bwd_rp) ? 4 : 0;
+}
+
 int mfma_bwd_groups(int64_t N, int p, int q, int m, int n, int r) {
   const Entry* e = find(p, q, m, n, r);
   if (e && e->bwd_rp) {
-    // two workgroups per compute unit, each stepping over rows_per_step rows at a time
+    // rp_per_cu workgroups per compute unit, each stepping over rows_per_step rows at a time
     const int64_t g = (N + e->rows_per_step - 1) / e->rows_per_step;
-    return (int)(g < 2 * kBwdGroups ? g : 2 * kBwdGroups);
+    const int64_t gmax = (int64_t)e->rp_per_cu * kBwdGroups;
+    return (int)(g < gmax ? g : gmax);
   }
   const int64_t g = (N + kWaves - 1) / kWaves;
   return (int)(g < kBwdGroups ? g : kBwdGroups);

@@ -111,6 +111,28 @@ def test_relu_flags():
     assert np.all(g["dx"][xr <= 0] == 0)
 
 
+@pytest.mark.parametrize("shape", [(32, 64, 24, 48), (64, 32, 48, 24)])
+def test_rank8_in_chunks_with_S_and_bias(shape):
+    """r = 8 runs as two passes of four ranks: dX written then added to, dS summed over
+    the passes, dbias from the first pass."""
+    p, q, m, n = shape
+    compare_layer(kron_inputs(37, 1031, p, q, m, n, 8, s_mode="uniform_zeroed", bias_mode="normal"))
+
+
+def test_rank8_in_chunks_relu_mask():
+    """The ReLU mask of dX is applied once, to the sum over the rank passes."""
+    inp = kron_inputs(38, 515, 32, 64, 24, 48, 8, s_mode="uniform", bias_mode="normal")
+    xr = np.maximum(inp.x, 0).astype(np.float32)
+    inp.x = xr
+    y, g = run_layer(inp, relu_mask=True)
+    W = OK.weight(inp.S, inp.A, inp.B)
+    go = OK.backward(xr, inp.S, inp.A, inp.B, inp.dy, W=W)
+    assert rel_err(g["dx"], go["dx"] * (xr > 0)) <= TOL_F32
+    assert np.all(g["dx"][xr <= 0] == 0)
+    for k in ("dS", "dA", "dB", "dbias"):
+        assert rel_err(g[k], go[k]) <= TOL_F32, k
+
+
 def test_one_hot_rows_bit_exact_rank1():
     """fwd(I_in) with zero bias reproduces W; for r = 1 and S absent every entry of W is a
     single fp32 product A[j,k]*B[a,b], so the GPU result must equal it bit for bit."""
