@@ -70,9 +70,21 @@ def work_per_row(p, q, m, n, r, nnz):
     return ff, fb, bf, bb
 
 
+SETTLE_SECONDS = [1.0]
+
+
 def timed(fn, steps, warmup):
-    """Mean ms per call of fn (events on the current stream) and the host wall clock."""
+    """Mean ms per call of fn (events on the current stream) and the host wall clock.
+
+    Before the `warmup` untimed calls, fn runs untimed for SETTLE_SECONDS so that the
+    GPU clock has left its idle state (the first ~0.1 s of work after idle runs about 10%
+    slower); neither phase is part of the timed region."""
     import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_SECONDS[0]:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -190,6 +202,7 @@ def run_headline(args, dev):
         "t_fwd_us": round(t_fwd * 1e6, 2), "t_bwd_us": round(t_bwd * 1e6, 2),
         "wall_ms_per_step": round(wall_ms, 5),
         "kernel_source_sha": kernel_source_sha(),
+        "settle_seconds": args.settle_seconds,
     }
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (oracle) for ~{args.cpu_seconds} s")
@@ -321,7 +334,10 @@ def main():
     ap.add_argument("--workload", default="headline",
                     choices=("headline", "tiny", "mlp_step", "gpt2_ffn", "ks"))
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--settle-seconds", type=float, default=1.0,
+                    help="untimed running before the warmup steps, for the GPU clock to ramp up")
     args = ap.parse_args()
+    SETTLE_SECONDS[0] = args.settle_seconds
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the Kronecker layer's hot path runs on one GPU's share "
               f"of rows); --gpus {args.gpus} is not supported", file=sys.stderr)
