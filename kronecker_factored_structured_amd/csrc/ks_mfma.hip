@@ -12,8 +12,10 @@
 // (a bf16 x bf16 product is exact in fp32, so only the accumulation order differs from a
 // bf16 matrix instruction).
 //
-// Workgroups (8 wavefronts) are specialised by alpha and keep V[alpha] in LDS as
-// chunk-interleaved operand tables: table[de][gamma tile][chunk][lane][4] holds
+// Two kernels.  For d = 4 (ks_vreg_kernel, below) each wavefront keeps its slice of V in
+// registers and only rows pass through LDS.  For the other shapes of the table
+// (ks_mfma_kernel) workgroups (8 wavefronts) are specialised by alpha and keep V[alpha]
+// in LDS as chunk-interleaved operand tables: table[de][gamma tile][chunk][lane][4] holds
 // V[al][de][be = g*SB + s][ga = 16*tile + c] for K step s, so that one ds_read_b128 per
 // chunk is contiguous across the wavefront.  Tasks are dealt round-robin to the
 // workgroup's wavefronts; the GQ gamma groups of a row tile go to neighbouring
@@ -193,6 +195,132 @@ __global__ __launch_bounds__(kThreads) void ks_mfma_kernel(int64_t N, int a_coun
   }
 }
 
+// ---------------------------------------------------------------------------------
+// d = 4: V held in registers.  One workgroup per compute unit, alpha fixed per
+// workgroup, one wavefront per 16-wide gamma tile (c / 16 wavefronts).  Wavefront w
+// keeps v[de][s] = V[al][de][be = g*SB + s][ga = 16*w + c] for all four delta in
+// registers for the whole kernel, so the LDS holds only rows: 16-row tiles of the
+// alpha slab of X (16 x 4b floats, row stride 4b + 4 so that the sixteen lanes of a
+// lane group read disjoint banks), double-buffered with one barrier per tile.  A lane's
+// 16-byte LDS read of X[row c][be = g*SB + s][0..3] gives its A operand for all four
+// delta, and its four accumulators give one 16-byte store of Y per output row.  Full
+// tiles run in the loop (stores unconditional, so waiting for the next tile's rows does
+// not wait for the stores); the partial tile, if any, is peeled off.
+// ---------------------------------------------------------------------------------
+template <int B_, int C_, int GS_ = 1>
+struct KV {
+  static constexpr int GS = GS_;                 // workgroups sharing one row tile (gamma split)
+  static constexpr int NW = C_ / 16 / GS_, NT = 64 * NW;
+  static constexpr int SB = B_ / 4;
+  static constexpr int ROWF = 4 * B_;            // floats of one row's alpha slab
+  static constexpr int LXS = ROWF + 4;
+  static constexpr int TILE = 16 * LXS;
+  static constexpr int NF4 = 16 * ROWF / 4;      // float4s per row tile
+  static constexpr int NPF = (NF4 + NT - 1) / NT;
+  static constexpr size_t LDS = (size_t)2 * TILE * 4;
+  static constexpr bool OK = B_ % 4 == 0 && C_ % (16 * GS_) == 0 && NW >= 1 && NW <= 16 && LDS <= kMaxLds;
+};
+
+// Four consecutive inputs as loaded (raw), widened to fp32 only when staged in LDS, so
+// that a prefetch does not wait for its own data.
+template <class TIn> struct Raw4;
+template <> struct Raw4<float> { typedef f4 type; };
+template <> struct Raw4<uint16_t> { typedef uint2 type; };
+__device__ __forceinline__ f4 load_raw4(const float* p) { return *reinterpret_cast<const f4*>(p); }
+__device__ __forceinline__ uint2 load_raw4(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ f4 widen4(f4 v) { return v; }
+__device__ __forceinline__ f4 widen4(uint2 v) {
+  return f4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
+            __uint_as_float(v.y & 0xffff0000u)};
+}
+
+template <int B_, int C_, int GS_, class TIn>
+__global__ __launch_bounds__((KV<B_, C_, GS_>::NT)) void ks_vreg_kernel(int64_t N, int a_count,
+                                                                    const TIn* __restrict__ x,
+                                                                    const TIn* __restrict__ vals,
+                                                                    float* __restrict__ y) {
+  using K = KV<B_, C_, GS_>;
+  extern __shared__ float lds[];   // 2 x TILE
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int al = blockIdx.x % a_count;
+  const int h = (blockIdx.x / a_count) % GS_;    // which gamma share
+  const int w = h * K::NW + (tid >> 6);          // this wavefront's gamma tile
+  const int64_t step = gridDim.x / (a_count * GS_);   // workgroups per (alpha, share); grid is a multiple
+  const int64_t ntile = (N + 15) / 16, nfull = N / 16;
+  const int64_t in_w = (int64_t)a_count * K::ROWF, out_w = (int64_t)a_count * C_ * 4;
+  const TIn* xa = x + (int64_t)al * K::ROWF;
+  float* ya = y + ((int64_t)al * C_ + 16 * w + c) * 4;
+
+  typedef typename Raw4<TIn>::type R4;
+  R4 pf[K::NPF];
+  auto fetch = [&](int64_t tile) {
+#pragma unroll
+    for (int t = 0; t < K::NPF; ++t) {
+      const int f = tid + t * K::NT;
+      R4 v = {};
+      if (K::NF4 % K::NT == 0 || f < K::NF4) {
+        const int r = f / (K::ROWF / 4), o = 4 * (f % (K::ROWF / 4));
+        const int64_t row = tile * 16 + r;
+        if (tile < ntile && row < N) v = load_raw4(xa + row * in_w + o);
+      }
+      pf[t] = v;
+    }
+  };
+  auto stash = [&](float* buf) {
+#pragma unroll
+    for (int t = 0; t < K::NPF; ++t) {
+      const int f = tid + t * K::NT;
+      if (K::NF4 % K::NT == 0 || f < K::NF4) {
+        const int r = f / (K::ROWF / 4), o = 4 * (f % (K::ROWF / 4));
+        *reinterpret_cast<f4*>(buf + r * K::LXS + o) = widen4(pf[t]);
+      }
+    }
+  };
+
+  int64_t tile = blockIdx.x / (a_count * GS_);
+  fetch(tile);
+  float v[4][K::SB];
+  const TIn* V = vals + (int64_t)al * 4 * B_ * C_;
+#pragma unroll
+  for (int de = 0; de < 4; ++de)
+#pragma unroll
+    for (int s = 0; s < K::SB; ++s) v[de][s] = widen(V[((int64_t)de * B_ + g * K::SB + s) * C_ + 16 * w + c]);
+  stash(lds);
+  fetch(tile + step);
+  __syncthreads();
+
+  auto compute = [&](const float* xs, f4 (&acc)[4]) {
+#pragma unroll
+    for (int de = 0; de < 4; ++de) acc[de] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < K::SB; ++s) {
+      const f4 xv = *reinterpret_cast<const f4*>(xs + c * K::LXS + (g * K::SB + s) * 4);
+#pragma unroll
+      for (int de = 0; de < 4; ++de) acc[de] = mfma(xv[de], v[de][s], acc[de]);
+    }
+  };
+  int it = 0;
+  for (; tile < nfull; tile += step, ++it) {
+    f4 acc[4];
+    compute(lds + (it & 1) * K::TILE, acc);
+#pragma unroll
+    for (int vv = 0; vv < 4; ++vv)
+      *reinterpret_cast<f4*>(ya + (tile * 16 + 4 * g + vv) * out_w) = f4{acc[0][vv], acc[1][vv], acc[2][vv], acc[3][vv]};
+    stash(lds + ((it + 1) & 1) * K::TILE);
+    fetch(tile + 2 * step);
+    __syncthreads();
+  }
+  if (tile < ntile) {   // the partial tile
+    f4 acc[4];
+    compute(lds + (it & 1) * K::TILE, acc);
+#pragma unroll
+    for (int vv = 0; vv < 4; ++vv) {
+      const int64_t row = tile * 16 + 4 * g + vv;
+      if (row < N) *reinterpret_cast<f4*>(ya + row * out_w) = f4{acc[0][vv], acc[1][vv], acc[2][vv], acc[3][vv]};
+    }
+  }
+}
+
 struct KsEntry {
   int b, c, d;
   bool ok;
@@ -224,14 +352,54 @@ int device_cus_ks() {
   return v;
 }
 
+struct KvEntry {
+  int b, c, gs;
+  size_t lds;
+  int nt;
+  const void* kf32;
+  const void* kbf16;
+};
+#define KV_ENTRY(B, C, GS)                                                                               \
+  KvEntry{B, C, GS, KV<B, C, GS>::LDS, KV<B, C, GS>::NT, (const void*)&ks_vreg_kernel<B, C, GS, float>, \
+          (const void*)&ks_vreg_kernel<B, C, GS, uint16_t>}
+// d = 4 shapes with V in registers: the ViT-S/16 MLP pattern (b, c) = (48, 192), one
+// workgroup per row tile (splitting the gamma tiles over two or three workgroups was
+// measured no faster).
+const KvEntry kKvTable[] = {KV_ENTRY(48, 192, 1)};
+
+const KvEntry* kv_find(int b, int c, int d) {
+  if (d != 4) return nullptr;
+  for (const KvEntry& e : kKvTable)
+    if (e.b == b && e.c == c) return &e;
+  return nullptr;
+}
+
+hipError_t launch_ks_vreg(const KvEntry* e, const KSArgs& k, hipStream_t s) {
+  const void* fn = k.dtype == KRON_F32 ? e->kf32 : e->kbf16;
+  (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)e->lds);
+  int per_cu = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, e->nt, e->lds) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  // workgroups per (alpha, gamma share): as many as fit, and no more than the row tiles
+  int64_t per_share = (int64_t)per_cu * device_cus_ks() / (k.a * e->gs);
+  if (per_share < 1) per_share = 1;
+  const int64_t tiles = (k.N + 15) / 16;
+  if (per_share > tiles) per_share = tiles;
+  const int grid = (int)(per_share * k.a * e->gs);
+  void* args[] = {(void*)&k.N, (void*)&k.a, (void*)&k.x, (void*)&k.vals, (void*)&k.y};
+  return hipLaunchKernel(fn, dim3(grid), dim3(e->nt), args, e->lds, s);
+}
+
 }  // namespace
 
 bool ks_mfma_supported(int a, int b, int c, int d) {
   (void)a;
-  return ks_find(b, c, d) != nullptr;
+  return kv_find(b, c, d) != nullptr || ks_find(b, c, d) != nullptr;
 }
 
 hipError_t launch_ks_mfma(const KSArgs& k, hipStream_t s) {
+  if (k.N == 0) return hipSuccess;
+  if (const KvEntry* ev = kv_find(k.b, k.c, k.d)) return launch_ks_vreg(ev, k, s);
   const KsEntry* e = ks_find(k.b, k.c, k.d);
   if (!e) return hipErrorInvalidValue;
   if (k.N == 0) return hipSuccess;
