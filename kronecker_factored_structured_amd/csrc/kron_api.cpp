@@ -336,8 +336,11 @@ int32_t kron_adam_l1_step(int32_t ntensors, float* const* params, const float* c
 
 size_t kron_head_ce_workspace_bytes(int64_t N, int32_t K, int32_t C) {
   if (N < 0 || K < 1 || C < 1) return 0;
-  const int G = kron::head_groups(N);
-  const size_t floats = (size_t)N * C + (size_t)N + (size_t)kron::part_floats(G, (int64_t)K * C + C + 1);
+  // the larger of the two paths' partial sums (the matrix-core path uses more groups)
+  const int64_t PW = (int64_t)K * C + C + 1;
+  const int64_t p1 = kron::part_floats(kron::head_groups(N), PW);
+  const int64_t p2 = kron::head_mfma_ok(K, C) ? kron::part_floats(kron::head_mfma_groups(N), PW) : 0;
+  const size_t floats = (size_t)N * C + (size_t)N + (size_t)(p1 > p2 ? p1 : p2);
   return ((floats * 4 + 255) & ~size_t(255)) + 256;
 }
 

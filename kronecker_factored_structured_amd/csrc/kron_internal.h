@@ -159,6 +159,8 @@ struct HeadArgs {
   float* part;   // workspace: G partial rows of K*C + C + 1 columns (column-blocked)
 };
 int head_groups(int64_t N);
+int head_mfma_groups(int64_t N);
+bool head_mfma_ok(int K, int C);
 int64_t head_rows_per_group(int64_t N);
 hipError_t launch_head(const HeadArgs& a, int G, hipStream_t s);
 

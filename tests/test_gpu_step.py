@@ -56,26 +56,40 @@ def test_adam_l1_multi_tensor(numels):
         ref = [(host(P[i]), host(M[i]), host(V[i])) for i in range(len(numels))]
 
 
-@pytest.mark.parametrize("N,Kf,C", [(20000, 1024, 10), (77, 130, 3), (1, 64, 10), (513, 200, 40)])
-def test_head_ce(N, Kf, C):
-    print(f"[head] N={N} K={Kf} C={C}", flush=True)
+# K = 1024 with C <= 16 takes the matrix-core head; the other shapes the generic kernels.
+@pytest.mark.parametrize("N,Kf,C,want_dh,relu", [(20000, 1024, 10, True, True), (1031, 1024, 16, True, True),
+                                                 (37, 1024, 1, True, False), (515, 1024, 10, False, False),
+                                                 (77, 130, 3, True, True), (1, 64, 10, True, True),
+                                                 (513, 200, 40, True, True)])
+def test_head_ce(N, Kf, C, want_dh, relu):
+    print(f"[head] N={N} K={Kf} C={C} dh={want_dh} relu={relu}", flush=True)
     rng = np.random.default_rng(8)
-    h = np.maximum(rng.standard_normal((N, Kf)), 0).astype(np.float32)
+    h = rng.standard_normal((N, Kf))
+    if relu:
+        h = np.maximum(h, 0)
+    h = h.astype(np.float32)
     W = (rng.standard_normal((Kf, C)) / np.sqrt(Kf)).astype(np.float32)
     b = rng.standard_normal(C).astype(np.float32)
     lab = rng.integers(0, C, N)
-    out = K().kron_head_ce(dev(h), dev(W), dev(b), dev(lab), want_dh=True, relu_mask=True)
+    out = K().kron_head_ce(dev(h), dev(W), dev(b), dev(lab), want_dh=want_dh, relu_mask=relu)
     z = h.astype(np.float64) @ W + b
     loss, dz = OM.softmax_ce(z, lab)
     assert abs(host(out["loss"])[0] - loss) <= TOL_F32 * abs(loss)
     assert rel_err(host(out["dW"]), h.T.astype(np.float64) @ dz) <= TOL_F32
     assert rel_err(host(out["db"]), dz.sum(0)) <= TOL_F32
-    assert rel_err(host(out["dh"]), (dz @ W.T.astype(np.float64)) * (h > 0)) <= TOL_F32
+    if want_dh:
+        want = dz @ W.T.astype(np.float64)
+        if relu:
+            want = want * (h > 0)
+        assert rel_err(host(out["dh"]), want) <= TOL_F32
+    else:
+        assert out["dh"] is None
 
 
-def test_head_ce_bad_label_gives_nan_loss():
-    h = dev(np.ones((4, 64), np.float32))
-    W = dev(np.ones((64, 10), np.float32) * 0.01)
+@pytest.mark.parametrize("Kf", [64, 1024])
+def test_head_ce_bad_label_gives_nan_loss(Kf):
+    h = dev(np.ones((4, Kf), np.float32))
+    W = dev(np.ones((Kf, 10), np.float32) * 0.01)
     b = dev(np.zeros(10, np.float32))
     lab = dev(np.array([1, 2, 10, -1], np.int64))
     out = K().kron_head_ce(h, W, b, lab)
