@@ -35,7 +35,29 @@
 
 #include "kron_internal.h"
 
+// The file is compiled twice: pass 1 holds the forward kernels (built with the
+// instruction-level-parallelism scheduler, measured faster for them), pass 2 everything
+// else.  KRON_MFMA_PASS 0 compiles the whole file at once.
+#ifndef KRON_MFMA_PASS
+#define KRON_MFMA_PASS 0
+#endif
+
+// The shapes with matrix-core kernels, (p, q, m, n, r, prefer the rank-parallel backward):
+// the 64x64 tiny layer (m = 8), the 1024x1024 layers with m = 32 and m = 64, and the
+// GPT-2 FFN pair 768 <-> 3072.
+#define KRON_MFMA_SHAPES(X)                                                                             \
+  X(8, 8, 8, 8, 1, true) X(8, 8, 8, 8, 2, true) X(32, 32, 32, 32, 1, true) X(32, 32, 32, 32, 2, true)   \
+  X(32, 32, 32, 32, 4, true) X(16, 16, 64, 64, 1, false) X(16, 16, 64, 64, 2, false)                    \
+  X(32, 64, 24, 48, 1, true) X(32, 64, 24, 48, 2, false) X(32, 64, 24, 48, 4, true)                     \
+  X(32, 64, 24, 48, 8, true) X(64, 32, 48, 24, 1, false) X(64, 32, 48, 24, 2, true)                     \
+  X(64, 32, 48, 24, 4, true) X(64, 32, 48, 24, 8, true)
+
 namespace kron {
+
+// The forward of one shape (defined with the forward kernels).
+template <int P, int Q, int M, int N, int R>
+void run_fwd_shape(const LayerArgs& a, int max_grid, hipStream_t s);
+
 namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -43,7 +65,7 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;   // four wavefronts
 constexpr int kWaves = kThreads / 64;
-constexpr int kBwdGroups = 256; // workgroups of the backward per 256 CUs (fixed: the workspace depends on it)
+[[maybe_unused]] constexpr int kBwdGroups = 256; // backward workgroups per 256 CUs (fixed: the workspace depends on it)
 constexpr size_t kMaxLds = 160 * 1024;
 
 __device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
@@ -239,6 +261,7 @@ __device__ __forceinline__ void load_xa(float (&xa)[D::TJ][D::SA], const float* 
   }
 }
 
+#if KRON_MFMA_PASS != 2
 template <class D>
 __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t flags,
                                                             const float* __restrict__ x,
@@ -361,6 +384,9 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
   }
 }
 
+#endif  // forward kernels
+
+#if KRON_MFMA_PASS != 1
 // The backward's per-row operands.
 template <class D>
 struct BwdRow {
@@ -1003,6 +1029,8 @@ void bwd_rp_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, const
   for (int e = tid; e < QN; e += kThreads) out[D::R * (MN + PQ) + PQ + e] = ssum(D::R * (MN + PQ) + e);
 }
 
+#endif  // backward kernels
+
 // ---------------------------------------------------------------------------------
 // Shape table.
 // ---------------------------------------------------------------------------------
@@ -1028,6 +1056,7 @@ int device_cus() {
   return v;
 }
 
+#if KRON_MFMA_PASS != 2
 // The forward is persistent: as many workgroups as fit on the device at once (and no
 // more than one row per wavefront), each wavefront striding over rows.
 template <class D>
@@ -1049,6 +1078,9 @@ void run_fwd(const LayerArgs& a, int max_grid, hipStream_t s) {
   }
 }
 
+#endif
+
+#if KRON_MFMA_PASS != 1
 // RPF: prefer the rank-parallel kernel when both backward kernels fit (measured per shape).
 template <class D, bool RPF>
 void run_bwd(const LayerArgs& a, int grid, hipStream_t s) {
@@ -1097,29 +1129,31 @@ void run_bwd(const LayerArgs& a, int grid, hipStream_t s) {
   Entry{P, Q, M, N, R, Dims<P, Q, M, N, R>::FWD_OK,                                                    \
         Dims<P, Q, M, N, R>::BWD_OK || RP<Dims<P, Q, M, N, R>>::OK,                                     \
         RP<Dims<P, Q, M, N, R>>::OK && (RPF || !Dims<P, Q, M, N, R>::BWD_OK),                           \
-        RP<Dims<P, Q, M, N, R>>::RPI, RP<Dims<P, Q, M, N, R>>::WPC, &run_fwd<Dims<P, Q, M, N, R>>,        \
-        &run_bwd<Dims<P, Q, M, N, R>, RPF>}
+        RP<Dims<P, Q, M, N, R>>::RPI, RP<Dims<P, Q, M, N, R>>::WPC, &run_fwd_shape<P, Q, M, N, R>,       \
+        &run_bwd<Dims<P, Q, M, N, R>, RPF>},
 
-// The shapes of the workloads: the 64x64 tiny layer (m = 8), the 1024x1024 layers with
-// m = 32 and m = 64, and the GPT-2 FFN pair 768 <-> 3072.
-const Entry kTable[] = {
-    KRON_ENTRY(8, 8, 8, 8, 1, true),       KRON_ENTRY(8, 8, 8, 8, 2, true),
-    KRON_ENTRY(32, 32, 32, 32, 1, true),   KRON_ENTRY(32, 32, 32, 32, 2, true),
-    KRON_ENTRY(32, 32, 32, 32, 4, true),   KRON_ENTRY(16, 16, 64, 64, 1, false),
-    KRON_ENTRY(16, 16, 64, 64, 2, false),  KRON_ENTRY(32, 64, 24, 48, 1, true),
-    KRON_ENTRY(32, 64, 24, 48, 2, false),  KRON_ENTRY(32, 64, 24, 48, 4, true),
-    KRON_ENTRY(32, 64, 24, 48, 8, true),   KRON_ENTRY(64, 32, 48, 24, 1, false),
-    KRON_ENTRY(64, 32, 48, 24, 2, true),   KRON_ENTRY(64, 32, 48, 24, 4, true),
-    KRON_ENTRY(64, 32, 48, 24, 8, true),
-};
+const Entry kTable[] = {KRON_MFMA_SHAPES(KRON_ENTRY)};
 
 const Entry* find(int p, int q, int m, int n, int r) {
   for (const Entry& e : kTable)
     if (e.p == p && e.q == q && e.m == m && e.n == n && e.r == r) return &e;
   return nullptr;
 }
+#endif  // KRON_MFMA_PASS != 1
 
 }  // namespace
+
+#if KRON_MFMA_PASS != 2
+template <int P, int Q, int M, int N, int R>
+void run_fwd_shape(const LayerArgs& a, int max_grid, hipStream_t s) {
+  run_fwd<Dims<P, Q, M, N, R>>(a, max_grid, s);
+}
+#define KRON_FWD_INST(P, Q, M, N, R, RPF) template void run_fwd_shape<P, Q, M, N, R>(const LayerArgs&, int, hipStream_t);
+KRON_MFMA_SHAPES(KRON_FWD_INST)
+#undef KRON_FWD_INST
+#endif
+
+#if KRON_MFMA_PASS != 1
 
 bool mfma_fwd_supported(int p, int q, int m, int n, int r) {
   const Entry* e = find(p, q, m, n, r);
@@ -1166,5 +1200,6 @@ hipError_t launch_bwd_mfma(const LayerArgs& a, int G, hipStream_t s) {
   e->bwd(a, G, s);
   return hipGetLastError();
 }
+#endif  // KRON_MFMA_PASS != 1
 
 }  // namespace kron
