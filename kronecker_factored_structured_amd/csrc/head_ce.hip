@@ -7,6 +7,8 @@
 // 64 lanes, the softmax, dz, the row's loss and dh.  Pass 2: each thread owns one row
 // k of dW (all C classes in registers) over a chunk of rows; the chunks' partial sums
 // go through the shared fixed-order column reduction.
+#include <type_traits>
+
 #include "kron_internal.h"
 
 namespace kron {
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void head_dw_kernel(int64_t N, int K, int
 // W is held in registers in the two operand layouts.  dW, db and the loss sum stay in
 // registers over the workgroup's tiles and are written once as its partial row.
 // ---------------------------------------------------------------------------------
-template <int KK, int NWH>
+template <int KK, int NWH, bool DH>
 __global__ __launch_bounds__(64 * NWH) void head_mfma_kernel(int64_t N, int C, uint32_t flags,
                                                         const float* __restrict__ h, const float* __restrict__ W,
                                                         const float* __restrict__ b,
@@ -187,16 +189,41 @@ __global__ __launch_bounds__(64 * NWH) void head_mfma_kernel(int64_t N, int C, u
   for (int t = 0; t < TQ; ++t) dwacc[t] = f4{0.f, 0.f, 0.f, 0.f};
   float dbacc = 0.f, lossacc = 0.f;
 
-  for (int64_t tile = blockIdx.x; tile < ntile; tile += gridDim.x) {
-    const int64_t r0 = tile * 16;
-    __syncthreads();   // the previous tile's reads of hs and dzs are done
-#pragma unroll 4
-    for (int f = tid; f < 16 * KK / 4; f += NT) {
+  // A tile's rows (and labels) are loaded during the previous tile and staged in LDS at
+  // its start; full tiles run in the loop and the partial tile, if any, after it, so every
+  // loop iteration issues the same stores and waiting for the prefetch never waits for them.
+  constexpr int NPF = (16 * KK / 4 + NT - 1) / NT;
+  f4 pf[NPF];
+  int64_t lab_pf = 0;
+  auto fetch = [&](int64_t tile) {
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) {
+      const int f = tid + i * NT;
       const int r = f / (KK / 4), o = 4 * (f % (KK / 4));
       f4 v = f4{0.f, 0.f, 0.f, 0.f};
-      if (r0 + r < N) v = *reinterpret_cast<const f4*>(h + (r0 + r) * KK + o);
-      *reinterpret_cast<f4*>(hs + r * LH + o) = v;
+      if ((16 * KK / 4) % NT == 0 || f < 16 * KK / 4)
+        if (tile < ntile && tile * 16 + r < N) v = *reinterpret_cast<const f4*>(h + (tile * 16 + r) * KK + o);
+      pf[i] = v;
     }
+    lab_pf = (tid < 256 && tile < ntile && tile * 16 + row_t < N) ? labels[tile * 16 + row_t] : 0;
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) {
+      const int f = tid + i * NT;
+      const int r = f / (KK / 4), o = 4 * (f % (KK / 4));
+      if ((16 * KK / 4) % NT == 0 || f < 16 * KK / 4) *reinterpret_cast<f4*>(hs + r * LH + o) = pf[i];
+    }
+  };
+  fetch(blockIdx.x);
+  auto process = [&](int64_t tile, auto tail_c) {
+    constexpr bool kTail = decltype(tail_c)::value;
+    const int64_t r0 = tile * 16;
+    __syncthreads();   // the previous tile's reads of hs and dzs are done
+    stash();
+    const int64_t lab = lab_pf;
+    fetch(tile + gridDim.x);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     // z partial over this wavefront's quarter (two accumulator chains)
     {
@@ -236,8 +263,7 @@ __global__ __launch_bounds__(64 * NWH) void head_mfma_kernel(int64_t N, int C, u
 #pragma unroll
       for (int off = 8; off >= 1; off /= 2) ssum += __shfl_xor(ssum, off, 16);
       float d = 0.f;
-      if (row < N) {
-        const int64_t lab = labels[row];
+      if (!kTail || row < N) {
         const bool ok = lab >= 0 && lab < C;
         if (valid) d = (ex / ssum - ((ok && cls_t == lab) ? 1.f : 0.f)) * invN;
         // z[label] - max, from the label's lane
@@ -257,7 +283,7 @@ __global__ __launch_bounds__(64 * NWH) void head_mfma_kernel(int64_t N, int C, u
 #pragma unroll
       for (int t = 0; t < TQ; ++t) {
         const int col = w * KQ + 16 * t + c;
-        if (dh) {
+        if constexpr (DH) {
           f4 o = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < 4; ++s) o = __builtin_amdgcn_mfma_f32_16x16x4f32(dza[s], wh[t][s], o, 0, 0, 0);
@@ -266,7 +292,7 @@ __global__ __launch_bounds__(64 * NWH) void head_mfma_kernel(int64_t N, int C, u
             const int r = 4 * g + v;
             float val = o[v];
             if (mask && !(hs[r * LH + col] > 0.f)) val = 0.f;
-            if (r0 + r < N) dh[(r0 + r) * KK + col] = val;
+            if (!kTail || r0 + r < N) dh[(r0 + r) * KK + col] = val;
           }
         }
 #pragma unroll
@@ -274,7 +300,11 @@ __global__ __launch_bounds__(64 * NWH) void head_mfma_kernel(int64_t N, int C, u
           dwacc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(hs[(4 * g + s) * LH + col], dzb[s], dwacc[t], 0, 0, 0);
       }
     }
-  }
+  };
+  const int64_t nfull = N / 16;
+  int64_t tile = blockIdx.x;
+  for (; tile < nfull; tile += gridDim.x) process(tile, std::false_type{});
+  if (tile < ntile) process(tile, std::true_type{});
 
   // partial row: [dW (K*C) | db (C) | loss (1)]
   __syncthreads();
@@ -331,10 +361,12 @@ hipError_t launch_head(const HeadArgs& a, int G, hipStream_t s) {
     // as many workgroups as are resident at once (at most head_mfma_groups(N), which the
     // workspace is sized for)
     static const int per_cu = [] {
-      (void)hipFuncSetAttribute((const void*)head_mfma_kernel<kHeadMfmaK, kHeadMfmaWaves>,
+      (void)hipFuncSetAttribute((const void*)head_mfma_kernel<kHeadMfmaK, kHeadMfmaWaves, true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kHeadMfmaLds);
+      (void)hipFuncSetAttribute((const void*)head_mfma_kernel<kHeadMfmaK, kHeadMfmaWaves, false>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)kHeadMfmaLds);
       int nb = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, head_mfma_kernel<kHeadMfmaK, kHeadMfmaWaves>,
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, head_mfma_kernel<kHeadMfmaK, kHeadMfmaWaves, true>,
                                                        64 * kHeadMfmaWaves, kHeadMfmaLds) != hipSuccess || nb < 1)
         nb = 1;
       return nb;
@@ -346,9 +378,12 @@ hipError_t launch_head(const HeadArgs& a, int G, hipStream_t s) {
     int Gm = head_mfma_groups(a.N);
     if (Gm > per_cu * cus) Gm = per_cu * cus;
     if (Gm > 0) {
-      hipLaunchKernelGGL((head_mfma_kernel<kHeadMfmaK, kHeadMfmaWaves>), dim3(Gm), dim3(64 * kHeadMfmaWaves),
-                         kHeadMfmaLds, s, a.N, a.C, a.flags,
-                         a.h, a.W, a.b, a.labels, a.dh, a.part);
+      if (a.dh)
+        hipLaunchKernelGGL((head_mfma_kernel<kHeadMfmaK, kHeadMfmaWaves, true>), dim3(Gm), dim3(64 * kHeadMfmaWaves),
+                           kHeadMfmaLds, s, a.N, a.C, a.flags, a.h, a.W, a.b, a.labels, a.dh, a.part);
+      else
+        hipLaunchKernelGGL((head_mfma_kernel<kHeadMfmaK, kHeadMfmaWaves, false>), dim3(Gm), dim3(64 * kHeadMfmaWaves),
+                           kHeadMfmaLds, s, a.N, a.C, a.flags, a.h, a.W, a.b, a.labels, a.dh, a.part);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
