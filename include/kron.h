@@ -113,6 +113,27 @@ int32_t kron_linear_bwd(const kron_shape_t* shape, const float* x, const float* 
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * bf16 layer (mixed precision; the tutorial's "Takeaways" name a mixed-precision rerun as
+ * the next step).  Same operation as kron_linear_fwd / kron_linear_bwd with bf16 storage
+ * (bfloat16 bit patterns) for x, S, A, B, bias, dy and the outputs y and dx; products
+ * run on bf16 matrix instructions with fp32 accumulation.  C_i = S o A_i is formed in
+ * fp32 and rounded to bf16, and X_n B_i and G_{n,i} are rounded to bf16 before their
+ * second product (round to nearest even); y and dx are rounded once at the end.  The
+ * parameter gradients dS, dA, dB and dbias are fp32.
+ * Shapes: (p, q, m, n, r) in {(32,32,32,32,1), (32,32,32,32,2), (32,32,32,32,4),
+ * (16,16,64,64,2)}; other shapes return KRON_E_UNSUPPORTED.  Pointers as for the fp32
+ * calls (16-byte aligned); workspace from kron_linear_bwd_bf16_workspace_bytes.
+ */
+size_t kron_linear_bwd_bf16_workspace_bytes(const kron_shape_t* shape);
+int32_t kron_linear_fwd_bf16(const kron_shape_t* shape, const void* x, const void* S,
+                             const void* A, const void* B, const void* bias, void* y,
+                             hipStream_t stream);
+int32_t kron_linear_bwd_bf16(const kron_shape_t* shape, const void* x, const void* S,
+                             const void* A, const void* B, const void* dy, void* dx,
+                             float* dS, float* dA, float* dB, float* dbias,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Kronecker-sparse matmul ("Fast Inference with Kronecker-Sparse Matrices", abstract):
  * Y = X K with K of support I_a (x) 1_{b x c} (x) I_d, (a*b*d) x (a*c*d):
  *   Y[n, (al*c + ga)*d + de] = sum_be X[n, (al*b + be)*d + de] * vals[al][de][be][ga]

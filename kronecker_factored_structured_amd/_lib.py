@@ -32,6 +32,7 @@ EXPORTS = (
     "kron_abi_version", "kron_status_str", "kron_last_error", "kron_linear_check",
     "kron_linear_bwd_workspace_bytes", "kron_linear_fwd", "kron_linear_bwd", "ks_matmul",
     "kron_adam_l1_step", "kron_head_ce_workspace_bytes", "kron_head_ce",
+    "kron_linear_bwd_bf16_workspace_bytes", "kron_linear_fwd_bf16", "kron_linear_bwd_bf16",
 )
 
 
@@ -76,6 +77,9 @@ def lib() -> ctypes.CDLL:
                                         ctypes.c_double, ctypes.c_double, ctypes.c_double, vp]),
             "kron_head_ce_workspace_bytes": (sz, [i64, i32, i32]),
             "kron_head_ce": (i32, [i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, u32, vp, sz, vp]),
+            "kron_linear_bwd_bf16_workspace_bytes": (sz, [shp]),
+            "kron_linear_fwd_bf16": (i32, [shp, vp, vp, vp, vp, vp, vp, vp]),
+            "kron_linear_bwd_bf16": (i32, [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)

@@ -88,6 +88,56 @@ def kron_linear_bwd(x: torch.Tensor, S: Optional[torch.Tensor], A: torch.Tensor,
     return dict(dx=dx, dS=dS, dA=dA, dB=dB, dbias=dbias)
 
 
+def kron_linear_bwd_bf16_workspace_bytes(shape: KronShape) -> int:
+    return int(_lib.lib().kron_linear_bwd_bf16_workspace_bytes(ctypes.byref(shape)))
+
+
+def kron_linear_fwd_bf16(x: torch.Tensor, S: Optional[torch.Tensor], A: torch.Tensor, B: torch.Tensor,
+                         bias: Optional[torch.Tensor] = None, relu: bool = False,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 layer: y = x W + bias (bf16 tensors, fp32 accumulation, bf16 y)."""
+    bf = torch.bfloat16
+    for t, nm in ((x, "x"), (S, "S"), (A, "A"), (B, "B"), (bias, "bias"), (out, "out")):
+        _dev(t, nm, bf)
+    shape = layer_shape(x.shape[0], S, A, B, KRON_RELU_OUT if relu else 0)
+    if x.dim() != 2 or x.shape[1] != shape.p * shape.m:
+        raise ValueError(f"x must be N x {shape.p * shape.m}")
+    y = out if out is not None else torch.empty(x.shape[0], shape.q * shape.n, device=x.device, dtype=bf)
+    check("kron_linear_fwd_bf16", _lib.lib().kron_linear_fwd_bf16(
+        ctypes.byref(shape), _ptr(x), _ptr(S), _ptr(A), _ptr(B), _ptr(bias), _ptr(y), _stream(x.device)))
+    return y
+
+
+def kron_linear_bwd_bf16(x: torch.Tensor, S: Optional[torch.Tensor], A: torch.Tensor, B: torch.Tensor,
+                         dy: torch.Tensor, want_dx: bool = True, want_dbias: bool = True,
+                         relu_mask: bool = False, workspace: Optional[torch.Tensor] = None,
+                         outs: Optional[dict] = None) -> dict:
+    """bf16 layer backward: dx bf16; dS, dA, dB, dbias fp32 (None where not asked)."""
+    bf = torch.bfloat16
+    for t, nm in ((x, "x"), (S, "S"), (A, "A"), (B, "B"), (dy, "dy")):
+        _dev(t, nm, bf)
+    shape = layer_shape(x.shape[0], S, A, B, KRON_DX_RELU_MASK if relu_mask else 0)
+    dev = x.device
+    f32 = torch.float32
+    o = dict(outs or {})
+    dx = o.get("dx") if "dx" in o else (torch.empty_like(x) if want_dx else None)
+    dS = o.get("dS") if "dS" in o else (torch.empty(S.shape, device=dev, dtype=f32) if S is not None else None)
+    dA = o.get("dA") if "dA" in o else torch.empty(A.shape, device=dev, dtype=f32)
+    dB = o.get("dB") if "dB" in o else torch.empty(B.shape, device=dev, dtype=f32)
+    dbias = o.get("dbias") if "dbias" in o else (
+        torch.empty(shape.q * shape.n, device=dev, dtype=f32) if want_dbias else None)
+    _dev(dx, "dx", bf)
+    for t, nm in ((dS, "dS"), (dA, "dA"), (dB, "dB"), (dbias, "dbias")):
+        _dev(t, nm)
+    need = kron_linear_bwd_bf16_workspace_bytes(shape)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    check("kron_linear_bwd_bf16", _lib.lib().kron_linear_bwd_bf16(
+        ctypes.byref(shape), _ptr(x), _ptr(S), _ptr(A), _ptr(B), _ptr(dy), _ptr(dx), _ptr(dS), _ptr(dA),
+        _ptr(dB), _ptr(dbias), _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(dev)))
+    return dict(dx=dx, dS=dS, dA=dA, dB=dB, dbias=dbias)
+
+
 def ks_matmul(x: torch.Tensor, vals: torch.Tensor, a: int, b: int, c: int, d: int,
               out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y = X K for the Kronecker-sparse K with support I_a (x) 1_{b x c} (x) I_d; vals is

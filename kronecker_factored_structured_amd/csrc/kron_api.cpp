@@ -268,6 +268,89 @@ int32_t kron_linear_bwd(const kron_shape_t* s, const float* x, const float* S, c
   return ok();
 }
 
+size_t kron_linear_bwd_bf16_workspace_bytes(const kron_shape_t* s) {
+  if (kron_linear_check(s) != KRON_OK || !kron::bf16_supported(s->p, s->q, s->m, s->n, s->r)) return 0;
+  const int G = kron::bf16_bwd_groups(s->N, s->p, s->q, s->m, s->n, s->r);
+  const int64_t PW = kron::partial_width(s->p, s->q, s->m, s->n, s->r);
+  const size_t w = (size_t)kron::part_floats(G, PW) * sizeof(float);
+  return w == 0 ? 256 : (w + 255) & ~size_t(255);
+}
+
+int32_t kron_linear_fwd_bf16(const kron_shape_t* s, const void* x, const void* S, const void* A, const void* B,
+                             const void* bias, void* y, hipStream_t stream) {
+  int32_t st = kron_linear_check(s);
+  if (st != KRON_OK) return st;
+  if (s->flags & KRON_DX_RELU_MASK) return fail(KRON_E_ARG, "KRON_DX_RELU_MASK is a backward flag");
+  if (!kron::bf16_supported(s->p, s->q, s->m, s->n, s->r))
+    return fail(KRON_E_UNSUPPORTED, "no bf16 kernel for (p, q, m, n, r) = (%d, %d, %d, %d, %d)", s->p, s->q, s->m,
+                s->n, s->r);
+  if (!A || !B) return fail(KRON_E_NULL, "A and B are required");
+  if (s->N > 0 && (!x || !y)) return fail(KRON_E_NULL, "x and y are required when N > 0");
+  const size_t in = (size_t)s->p * s->m, out = (size_t)s->q * s->n;
+  const Range ins[5] = {{x, (size_t)s->N * in * 2, "x"},
+                        {S, (size_t)s->p * s->q * 2, "S"},
+                        {A, (size_t)s->r * s->p * s->q * 2, "A"},
+                        {B, (size_t)s->r * s->m * s->n * 2, "B"},
+                        {bias, out * 2, "bias"}};
+  const Range outs[1] = {{y, (size_t)s->N * out * 2, "y"}};
+  if ((st = check_align(ins, 5)) != KRON_OK || (st = check_align(outs, 1)) != KRON_OK) return st;
+  if ((st = check_alias(outs, 1, ins, 5)) != KRON_OK) return st;
+  if (s->N == 0) return ok();
+  kron::LayerArgsBf16 a{};
+  a.N = s->N; a.p = s->p; a.q = s->q; a.m = s->m; a.n = s->n; a.r = s->r; a.flags = s->flags;
+  a.x = (const uint16_t*)x; a.S = (const uint16_t*)S; a.A = (const uint16_t*)A; a.B = (const uint16_t*)B;
+  a.bias = (const uint16_t*)bias; a.y = (uint16_t*)y;
+  hipError_t e = kron::launch_fwd_bf16(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "kron_linear_fwd_bf16 launch");
+  return ok();
+}
+
+int32_t kron_linear_bwd_bf16(const kron_shape_t* s, const void* x, const void* S, const void* A, const void* B,
+                             const void* dy, void* dx, float* dS, float* dA, float* dB, float* dbias, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  int32_t st = kron_linear_check(s);
+  if (st != KRON_OK) return st;
+  if (s->flags & KRON_RELU_OUT) return fail(KRON_E_ARG, "KRON_RELU_OUT is a forward flag");
+  if (!kron::bf16_supported(s->p, s->q, s->m, s->n, s->r))
+    return fail(KRON_E_UNSUPPORTED, "no bf16 kernel for (p, q, m, n, r) = (%d, %d, %d, %d, %d)", s->p, s->q, s->m,
+                s->n, s->r);
+  if (!A || !B || !dA || !dB) return fail(KRON_E_NULL, "A, B, dA and dB are required");
+  if ((S == nullptr) != (dS == nullptr)) return fail(KRON_E_NULL, "dS must be given exactly when S is");
+  if (s->N > 0 && (!x || !dy)) return fail(KRON_E_NULL, "x and dy are required when N > 0");
+  if ((s->flags & KRON_DX_RELU_MASK) && !dx) return fail(KRON_E_ARG, "KRON_DX_RELU_MASK needs dx");
+  const size_t need = kron_linear_bwd_bf16_workspace_bytes(s);
+  if (!workspace || workspace_bytes < need)
+    return fail(KRON_E_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if (((uintptr_t)workspace & 255u) != 0) return fail(KRON_E_ALIGN, "workspace is not 256-byte aligned");
+  const size_t in = (size_t)s->p * s->m, out = (size_t)s->q * s->n;
+  const size_t pq = (size_t)s->p * s->q, mn = (size_t)s->m * s->n;
+  const Range ins[6] = {{x, (size_t)s->N * in * 2, "x"},     {S, pq * 2, "S"},
+                        {A, s->r * pq * 2, "A"},             {B, s->r * mn * 2, "B"},
+                        {dy, (size_t)s->N * out * 2, "dy"},  {workspace, need, "workspace"}};
+  const Range outs[5] = {{dx, (size_t)s->N * in * 2, "dx"}, {dS, pq * 4, "dS"}, {dA, s->r * pq * 4, "dA"},
+                         {dB, s->r * mn * 4, "dB"},         {dbias, out * 4, "dbias"}};
+  if ((st = check_align(ins, 6)) != KRON_OK || (st = check_align(outs, 5)) != KRON_OK) return st;
+  if ((st = check_alias(outs, 5, ins, 6)) != KRON_OK) return st;
+  kron::LayerArgsBf16 a{};
+  a.N = s->N; a.p = s->p; a.q = s->q; a.m = s->m; a.n = s->n; a.r = s->r; a.flags = s->flags;
+  a.x = (const uint16_t*)x; a.S = (const uint16_t*)S; a.A = (const uint16_t*)A; a.B = (const uint16_t*)B;
+  a.dy = (const uint16_t*)dy; a.dx = s->N > 0 ? (uint16_t*)dx : nullptr;
+  a.part = (float*)workspace;
+  const int G = kron::bf16_bwd_groups(s->N, s->p, s->q, s->m, s->n, s->r);
+  hipError_t e = kron::launch_bwd_bf16(a, G, stream);
+  if (e != hipSuccess) return hip_fail(e, "kron_linear_bwd_bf16 launch");
+  kron::RedPlan rp{};
+  rp.nseg = 4;
+  rp.seg[0] = kron::RedSeg{dB, (int32_t)(s->r * mn), 1.f, 0};
+  rp.seg[1] = kron::RedSeg{dA, (int32_t)(s->r * pq), 1.f, 0};
+  rp.seg[2] = kron::RedSeg{dS, (int32_t)pq, 1.f, 0};
+  rp.seg[3] = kron::RedSeg{dbias, s->q * s->n, 1.f, 0};
+  const int32_t PW = (int32_t)kron::partial_width(s->p, s->q, s->m, s->n, s->r);
+  e = kron::launch_column_reduce(a.part, G, PW, rp, stream);
+  if (e != hipSuccess) return hip_fail(e, "kron_linear_bwd_bf16 reduce launch");
+  return ok();
+}
+
 int32_t ks_matmul(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype, const void* x,
                   const void* vals, float* y, hipStream_t stream) {
   if (N < 0 || N > kMaxRows) return fail(KRON_E_SHAPE, "N = %lld out of range", (long long)N);

@@ -1,0 +1,576 @@
+// bf16 Kronecker-factored layer on bf16 matrix instructions (mixed precision: bf16
+// operands, fp32 accumulation).  Same products as the fp32 kernels (Kronecker layer
+// tutorial, "The vec trick" and "The vec trick without the loop"; the backward by
+// calculus from them); every product is v_mfma_f32_16x16x16_bf16:
+//   lane l = 16*g + c supplies A[c][4g..4g+3] and B[4g..4g+3][c] (four consecutive K
+//   values, 8 bytes) and receives D[4g+v][c], v = 0..3.
+// A D tile therefore holds, per lane, four consecutive values of its row index -- exactly
+// the four K values the lane supplies when the next product contracts over that index --
+// so an fp32 accumulator tile, rounded to bf16 (round-to-nearest-even), is the operand of
+// the next product without leaving the registers (Z into Y^T = Z^T C in the forward; Z^T
+// into dC and G^T into dX^T in the backward).
+//
+// Storage: x, S, A, B, bias, dy, y and dx are bf16 (bit patterns); dS, dA, dB and dbias
+// are fp32.  C_i = S o A_i is formed in fp32 (exact for bf16 factors) and rounded to
+// bf16; X B_i and G_i are rounded to bf16 before they enter their second product.
+// Dimensions p, q, m, n must be multiples of 16.
+#include <type_traits>
+
+#include "kron_internal.h"
+
+namespace kron {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+__device__ __forceinline__ f4 mfma16(s4 a, s4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+// fp32 -> bf16, round to nearest even (NaN stays NaN)
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ s4 pack4(f4 v) {
+  return s4{(short)f2bf(v[0]), (short)f2bf(v[1]), (short)f2bf(v[2]), (short)f2bf(v[3])};
+}
+__device__ __forceinline__ s4 load_s4(const uint16_t* p) { return *reinterpret_cast<const s4*>(p); }
+__device__ __forceinline__ s4 gather4(const uint16_t* p, int stride) {
+  return s4{(short)p[0], (short)p[stride], (short)p[2 * stride], (short)p[3 * stride]};
+}
+
+template <int P_, int Q_, int M_, int N_, int R_>
+struct BD {
+  static constexpr int P = P_, Q = Q_, M = M_, N = N_, R = R_;
+  static constexpr int TJ = P / 16, TK = Q / 16, TA = M / 16, TB = N / 16;
+  static constexpr int IN = P * M, OUT = Q * N;
+  static constexpr int MN = M * N, PQ = P * Q;
+  static constexpr int PW = R * MN + R * PQ + PQ + Q * N;   // partial row (partial_width())
+  static constexpr int PWW = R * MN + R * PQ + Q * N;       // one row slot's sums
+  static constexpr bool SHAPE_OK = P % 16 == 0 && Q % 16 == 0 && M % 16 == 0 && N % 16 == 0;
+};
+
+// ---------------------------------------------------------------------------------
+// Forward.  Persistent; one row per wavefront at a time.  Per rank i:
+//   Z_i   = X B_i      (TJ x TB tiles, TA products each)     A = X[j][a..], B = B_i[a..][b]
+//   Y^T  += Z_i^T C_i  (TB x TK tiles, TJ products each)     A = bf16(Z tile), B = C_i[j..][k]
+// The B_i and C_i operands of every lane live in registers for the whole kernel.
+// ---------------------------------------------------------------------------------
+template <class D>
+__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(int64_t N, uint32_t flags, const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ Sm,
+                                                            const uint16_t* __restrict__ A,
+                                                            const uint16_t* __restrict__ B,
+                                                            const uint16_t* __restrict__ bias,
+                                                            uint16_t* __restrict__ y) {
+  __shared__ uint16_t rB[D::R * D::MN];   // B as given
+  __shared__ uint16_t rC[D::R * D::PQ];   // C_i = S o A_i, rounded to bf16
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15, wave = tid >> 6;
+  const int64_t stride = (int64_t)gridDim.x * kWaves;
+  int64_t row = (int64_t)blockIdx.x * kWaves + wave;
+
+  // the first row's X operands: X[j = 16tj + c][a = 16t + 4g ..]
+  s4 xn[D::TJ][D::TA];
+  auto load_x = [&](s4 (&dst)[D::TJ][D::TA], int64_t r) {
+    const uint16_t* xr = x + r * D::IN;
+#pragma unroll
+    for (int tj = 0; tj < D::TJ; ++tj)
+#pragma unroll
+      for (int t = 0; t < D::TA; ++t) dst[tj][t] = load_s4(xr + (16 * tj + c) * D::M + 16 * t + 4 * g);
+  };
+  if (row < N) load_x(xn, row);
+
+  for (int e = tid; e < D::R * D::MN; e += kThreads) rB[e] = B[e];
+  for (int e = tid; e < D::R * D::PQ; e += kThreads) {
+    const float a = bf2f(A[e]);
+    rC[e] = f2bf(Sm ? bf2f(Sm[e % D::PQ]) * a : a);
+  }
+  __syncthreads();
+  s4 bop[D::R][D::TB][D::TA];   // B_i[a = 16t + 4g + v][b = 16tb + c]
+  s4 cop[D::R][D::TK][D::TJ];   // C_i[j = 16t + 4g + v][k = 16tk + c]
+#pragma unroll
+  for (int i = 0; i < D::R; ++i) {
+#pragma unroll
+    for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+      for (int t = 0; t < D::TA; ++t) bop[i][tb][t] = gather4(rB + i * D::MN + (16 * t + 4 * g) * D::N + 16 * tb + c, D::N);
+#pragma unroll
+    for (int tk = 0; tk < D::TK; ++tk)
+#pragma unroll
+      for (int t = 0; t < D::TJ; ++t) cop[i][tk][t] = gather4(rC + i * D::PQ + (16 * t + 4 * g) * D::Q + 16 * tk + c, D::Q);
+  }
+  const bool relu = flags & KRON_RELU_OUT;
+
+  for (; row < N; row += stride) {
+    s4 xa[D::TJ][D::TA];
+#pragma unroll
+    for (int tj = 0; tj < D::TJ; ++tj)
+#pragma unroll
+      for (int t = 0; t < D::TA; ++t) xa[tj][t] = xn[tj][t];
+    load_x(xn, row + stride < N ? row + stride : row);   // the next row (the last row reloads itself)
+    __builtin_amdgcn_sched_barrier(0);
+    f4 acc[D::TB][D::TK];
+#pragma unroll
+    for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+      for (int tk = 0; tk < D::TK; ++tk) acc[tb][tk] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < D::R; ++i) {
+      s4 zb[D::TJ][D::TB];   // bf16(Z_i)[j = 16tj + 4g + v][b = 16tb + c]
+#pragma unroll
+      for (int tj = 0; tj < D::TJ; ++tj)
+#pragma unroll
+        for (int tb = 0; tb < D::TB; ++tb) {
+          f4 z = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < D::TA; ++t) z = mfma16(xa[tj][t], bop[i][tb][t], z);
+          zb[tj][tb] = pack4(z);
+        }
+#pragma unroll
+      for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+        for (int tk = 0; tk < D::TK; ++tk)
+#pragma unroll
+          for (int tj = 0; tj < D::TJ; ++tj) acc[tb][tk] = mfma16(zb[tj][tb], cop[i][tk][tj], acc[tb][tk]);
+    }
+    // acc[tb][tk] register v = Y^T[b = 16tb + 4g + v][k = 16tk + c] -> y[k*N + b]
+    uint16_t* yr = y + row * D::OUT;
+#pragma unroll
+    for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+      for (int tk = 0; tk < D::TK; ++tk) {
+        const int off = (16 * tk + c) * D::N + 16 * tb + 4 * g;
+        f4 o = acc[tb][tk];
+        if (bias) {
+          const s4 bv = load_s4(bias + off);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) o[v] += bf2f((uint16_t)bv[v]);
+        }
+        if (relu) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) o[v] = o[v] > 0.f ? o[v] : 0.f;
+        }
+        *reinterpret_cast<s4*>(yr + off) = pack4(o);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Backward, rank-parallel: a workgroup of four wavefronts owns RPI = 4 / R rows per step,
+// wavefront w computes rank w % R of row slot w / R.  The rows are staged in LDS in both
+// index orders (X[j][a], X^T[a][j], dY[k][b], dY^T[b][k]) so that every operand is one
+// 8-byte read.  Per rank and row:
+//   Z^T[b][j]  = sum_a B_i[a][b] X[j][a]        A = B_i^T[b][a..] (registers), B = X[j][a..]
+//   dC[j][k]  += sum_b Z^T[b][j] dY[k][b]       A = bf16(Z^T tile),             B = dY[k][b..]
+//   G^T[b][j]  = sum_k dY[k][b] C_i[j][k]       A = dY^T[b][k..],               B = C_i[j][k..] (registers)
+//   dX^T[a][j] = sum_b B_i[a][b] G^T[b][j]      A = B_i[a][b..] (registers),    B = bf16(G^T tile)
+//   dB[a][b]  += sum_j X[j][a] G[j][b]          A = X^T[a][j..],                B = G (G^T tile through LDS)
+// dX^T partials of the R ranks of a row meet in LDS and are added in rank order; the
+// partial row [dB | dA | dS | dbias] and the fixed-order column reduction are those of the
+// fp32 layer.
+// ---------------------------------------------------------------------------------
+template <class D>
+struct RB {
+  static constexpr int R = D::R;
+  static constexpr int RPI = 4 / R;
+  // row strides (bf16 elements), padded by 8 so that rows stay 16-byte aligned and the
+  // sixteen rows of a lane group start on different banks
+  static constexpr int LXA = D::M + 8;   // X[j][a]
+  static constexpr int LXJ = D::P + 8;   // X^T[a][j]
+  static constexpr int LYB = D::N + 8;   // dY[k][b]
+  static constexpr int LYK = D::Q + 8;   // dY^T[b][k]
+  static constexpr int OX = 0, OXT = D::P * LXA, OY = OXT + D::M * LXJ, OYT = OY + D::Q * LYB;
+  static constexpr int SLOT = OYT + D::N * LYK;   // bf16 elements per row slot
+  static constexpr int ROWBUF = RPI * SLOT;
+  static constexpr int LG = D::P + 8;             // G^T tile gs[b][j] (bf16)
+  static constexpr int LDX = D::M + 4;            // dX^T partial dxp[j][a] (fp32)
+  static constexpr int WREG_BYTES = (D::N * LG * 2 > D::P * LDX * 4 ? D::N * LG * 2 : D::P * LDX * 4);
+  static constexpr int WREG = (WREG_BYTES + 15) / 16 * 16;   // bytes per wavefront
+  static constexpr size_t MAIN = (size_t)ROWBUF * 2 + (size_t)kWaves * WREG;
+  static constexpr size_t COMBINE = (size_t)RPI * D::PWW * 4;
+  static constexpr size_t LDS = (MAIN > COMBINE ? MAIN : COMBINE);
+  static constexpr int CHUNKS = (D::IN + D::OUT) / 8;   // 16-byte pieces of one row's x and dy
+  static constexpr int NPF = (RPI * CHUNKS + kThreads - 1) / kThreads;
+  static constexpr bool OK = D::SHAPE_OK && (R == 1 || R == 2 || R == 4) && LDS <= 80 * 1024;
+};
+
+template <class D, int DXM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_bf16_kernel(int64_t N, const uint16_t* __restrict__ x, const uint16_t* __restrict__ Sm,
+                     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+                     const uint16_t* __restrict__ dy, uint16_t* __restrict__ dx, float* __restrict__ part) {
+  using Q = RB<D>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint16_t* rowbuf = reinterpret_cast<uint16_t*>(smem);
+  unsigned char* wbase = smem + (size_t)Q::ROWBUF * 2;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15, wave = tid >> 6;
+  const int slot = wave / Q::R, rank = wave % Q::R;
+  const int64_t ngrp = (N + Q::RPI - 1) / Q::RPI;
+
+  // prefetch: 16-byte pieces of the step's rows (x then dy of each row slot)
+  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  u4 pf[Q::NPF];
+  auto fetch = [&](int64_t grp) {
+#pragma unroll
+    for (int t = 0; t < Q::NPF; ++t) {
+      const int f = tid + t * kThreads;
+      u4 v = u4{0u, 0u, 0u, 0u};
+      if (f < Q::RPI * Q::CHUNKS) {
+        const int s = f / Q::CHUNKS, o = 8 * (f % Q::CHUNKS);
+        const int64_t row = grp * Q::RPI + s;
+        if (grp < ngrp && row < N)
+          v = o < D::IN ? *reinterpret_cast<const u4*>(x + row * D::IN + o)
+                        : *reinterpret_cast<const u4*>(dy + row * D::OUT + (o - D::IN));
+      }
+      pf[t] = v;
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int t = 0; t < Q::NPF; ++t) {
+      const int f = tid + t * kThreads;
+      if (f < Q::RPI * Q::CHUNKS) {
+        const int s = f / Q::CHUNKS, o = 8 * (f % Q::CHUNKS);
+        uint16_t* sb = rowbuf + s * Q::SLOT;
+        const u4 v = pf[t];
+        const uint16_t e[8] = {(uint16_t)(v[0] & 0xffffu), (uint16_t)(v[0] >> 16), (uint16_t)(v[1] & 0xffffu),
+                               (uint16_t)(v[1] >> 16), (uint16_t)(v[2] & 0xffffu), (uint16_t)(v[2] >> 16),
+                               (uint16_t)(v[3] & 0xffffu), (uint16_t)(v[3] >> 16)};
+        if (o < D::IN) {   // X[j][a .. a+7] and X^T[a .. a+7][j]
+          const int j = o / D::M, a = o % D::M;
+          *reinterpret_cast<u4*>(sb + Q::OX + j * Q::LXA + a) = v;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) sb[Q::OXT + (a + u) * Q::LXJ + j] = e[u];
+        } else {           // dY[k][b .. b+7] and dY^T[b .. b+7][k]
+          const int o2 = o - D::IN, k = o2 / D::N, b = o2 % D::N;
+          *reinterpret_cast<u4*>(sb + Q::OY + k * Q::LYB + b) = v;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) sb[Q::OYT + (b + u) * Q::LYK + k] = e[u];
+        }
+      }
+    }
+  };
+  fetch(blockIdx.x);
+
+  // this wavefront's rank operands (bf16), straight from global memory
+  const uint16_t* Bi = B + rank * D::MN;
+  const uint16_t* Ai = A + rank * D::PQ;
+  s4 bt[D::TB][D::TA];   // B_i^T[b = 16tb + c][a = 16t + 4g ..]   (A operand of Z^T)
+  s4 ct[D::TJ][D::TK];   // C_i[j = 16tj + c][k = 16t + 4g ..]     (B operand of G^T)
+  s4 bx[D::TA][D::TB];   // B_i[a = 16ta + c][b = 16t + 4g ..]     (A operand of dX^T)
+#pragma unroll
+  for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+    for (int t = 0; t < D::TA; ++t) bt[tb][t] = gather4(Bi + (16 * t + 4 * g) * D::N + 16 * tb + c, D::N);
+#pragma unroll
+  for (int tj = 0; tj < D::TJ; ++tj)
+#pragma unroll
+    for (int t = 0; t < D::TK; ++t) {
+      const int j = 16 * tj + c, k0 = 16 * t + 4 * g;
+      s4 v;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float a = bf2f(Ai[j * D::Q + k0 + u]);
+        v[u] = (short)f2bf(Sm ? bf2f(Sm[j * D::Q + k0 + u]) * a : a);
+      }
+      ct[tj][t] = v;
+    }
+#pragma unroll
+  for (int ta = 0; ta < D::TA; ++ta)
+#pragma unroll
+    for (int t = 0; t < D::TB; ++t) bx[ta][t] = load_s4(Bi + (16 * ta + c) * D::N + 16 * t + 4 * g);
+
+  for (int e = tid; e < Q::ROWBUF; e += kThreads) rowbuf[e] = 0;   // padding stays zero
+  __syncthreads();
+
+  const uint16_t* Xs = rowbuf + slot * Q::SLOT;
+  uint16_t* gs = reinterpret_cast<uint16_t*>(wbase + wave * Q::WREG);   // G^T tile [b][j] (bf16)
+  float* dxp = reinterpret_cast<float*>(wbase + wave * Q::WREG);        // then the dX^T partial [j][a]
+
+  f4 dC[D::TJ][D::TK];   // dC_rank[j = 16tj + 4g + v][k = 16tk + c]
+  f4 dB[D::TA][D::TB];   // dB_rank[a = 16ta + 4g + v][b = 16tb + c]
+  f4 db[D::TK][D::TB];   // dbias[k = 16tk + c][b = 16tb + 4g + v]   (rank 0)
+#pragma unroll
+  for (int tj = 0; tj < D::TJ; ++tj)
+#pragma unroll
+    for (int tk = 0; tk < D::TK; ++tk) dC[tj][tk] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ta = 0; ta < D::TA; ++ta)
+#pragma unroll
+    for (int tb = 0; tb < D::TB; ++tb) dB[ta][tb] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int tk = 0; tk < D::TK; ++tk)
+#pragma unroll
+    for (int tb = 0; tb < D::TB; ++tb) db[tk][tb] = f4{0.f, 0.f, 0.f, 0.f};
+
+  auto step = [&](int64_t grp, auto tail_c) {
+    constexpr bool kTail = decltype(tail_c)::value;
+    stash();
+    __syncthreads();
+    fetch(grp + gridDim.x);
+    const uint16_t* X = Xs + Q::OX;
+    const uint16_t* XT = Xs + Q::OXT;
+    const uint16_t* Y = Xs + Q::OY;
+    const uint16_t* YT = Xs + Q::OYT;
+    // Z^T[b][j]
+    f4 zt[D::TB][D::TJ];
+#pragma unroll
+    for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+      for (int tj = 0; tj < D::TJ; ++tj) {
+        f4 t4 = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < D::TA; ++t) t4 = mfma16(bt[tb][t], load_s4(X + (16 * tj + c) * Q::LXA + 16 * t + 4 * g), t4);
+        zt[tb][tj] = t4;
+      }
+    // dC[j][k] += sum_b Z^T[b][j] dY[k][b];  dbias += dY (rank 0)
+#pragma unroll
+    for (int tk = 0; tk < D::TK; ++tk)
+#pragma unroll
+      for (int tb = 0; tb < D::TB; ++tb) {
+        const s4 yk = load_s4(Y + (16 * tk + c) * Q::LYB + 16 * tb + 4 * g);   // dY[k = 16tk + c][b = 16tb + 4g ..]
+        if (rank == 0) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) db[tk][tb][v] += bf2f((uint16_t)yk[v]);
+        }
+#pragma unroll
+        for (int tj = 0; tj < D::TJ; ++tj) dC[tj][tk] = mfma16(pack4(zt[tb][tj]), yk, dC[tj][tk]);
+      }
+    // G^T[b][j]
+    f4 gt[D::TB][D::TJ];
+#pragma unroll
+    for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+      for (int tj = 0; tj < D::TJ; ++tj) {
+        f4 t4 = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < D::TK; ++t) t4 = mfma16(load_s4(YT + (16 * tb + c) * Q::LYK + 16 * t + 4 * g), ct[tj][t], t4);
+        gt[tb][tj] = t4;
+      }
+    // G^T tile -> LDS as gs[b][j] (bf16)
+    s4 gb[D::TB][D::TJ];
+#pragma unroll
+    for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+      for (int tj = 0; tj < D::TJ; ++tj) {
+        gb[tb][tj] = pack4(gt[tb][tj]);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) gs[(16 * tb + 4 * g + v) * Q::LG + 16 * tj + c] = (uint16_t)gb[tb][tj][v];
+      }
+    __builtin_amdgcn_wave_barrier();
+    // dX^T[a][j] = sum_b B_i[a][b] G^T[b][j]
+    f4 dxt[D::TA][D::TJ];
+#pragma unroll
+    for (int ta = 0; ta < D::TA; ++ta)
+#pragma unroll
+      for (int tj = 0; tj < D::TJ; ++tj) {
+        f4 t4 = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tb = 0; tb < D::TB; ++tb) t4 = mfma16(bx[ta][tb], gb[tb][tj], t4);
+        dxt[ta][tj] = t4;
+      }
+    // dB[a][b] += sum_j X^T[a][j] G[j][b]
+#pragma unroll
+    for (int ta = 0; ta < D::TA; ++ta)
+#pragma unroll
+      for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+        for (int t = 0; t < D::TJ; ++t)
+          dB[ta][tb] = mfma16(load_s4(XT + (16 * ta + c) * Q::LXJ + 16 * t + 4 * g),
+                              load_s4(gs + (16 * tb + c) * Q::LG + 16 * t + 4 * g), dB[ta][tb]);
+    __builtin_amdgcn_wave_barrier();
+    // this rank's dX^T partial -> LDS as dxp[j][a] (fp32)
+#pragma unroll
+    for (int ta = 0; ta < D::TA; ++ta)
+#pragma unroll
+      for (int tj = 0; tj < D::TJ; ++tj)
+        *reinterpret_cast<f4*>(dxp + (16 * tj + c) * Q::LDX + 16 * ta + 4 * g) = dxt[ta][tj];
+    __syncthreads();
+    // dX of the step's rows: the R rank partials added in rank order, rounded to bf16
+    if constexpr (DXM != 0) {
+      constexpr int PER_ROW = D::IN / 4;
+      constexpr int TOT = Q::RPI * PER_ROW;
+#pragma unroll
+      for (int t = 0; t < (TOT + kThreads - 1) / kThreads; ++t) {
+        const int f = tid + t * kThreads;
+        if (TOT % kThreads != 0 && f >= TOT) continue;
+        const int s = f / PER_ROW, o = 4 * (f % PER_ROW);
+        const int64_t row = grp * Q::RPI + s;
+        if (kTail && row >= N) continue;
+        const int j = o / D::M, a = o % D::M;
+        const float* w0 = reinterpret_cast<const float*>(wbase + (s * Q::R) * Q::WREG);
+        f4 acc = *reinterpret_cast<const f4*>(w0 + j * Q::LDX + a);
+#pragma unroll
+        for (int i = 1; i < Q::R; ++i)
+          acc += *reinterpret_cast<const f4*>(reinterpret_cast<const float*>(wbase + (s * Q::R + i) * Q::WREG) +
+                                              j * Q::LDX + a);
+        if constexpr (DXM == 2) {
+          const uint16_t* xr = rowbuf + s * Q::SLOT + Q::OX + j * Q::LXA + a;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[v] = bf2f(xr[v]) > 0.f ? acc[v] : 0.f;
+        }
+        *reinterpret_cast<s4*>(dx + row * D::IN + o) = pack4(acc);
+      }
+    }
+    __syncthreads();   // the next step's stash overwrites the rows and this step's partials
+  };
+  const int64_t nfull = N / Q::RPI;
+  int64_t grp = blockIdx.x;
+  for (; grp < nfull; grp += gridDim.x) step(grp, std::false_type{});
+  if (grp < ngrp) step(grp, std::true_type{});
+
+  // Partial row of this workgroup: [dB (R*M*N) | dA (R*P*Q) | dS (P*Q) | dbias (Q*N)], fp32.
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem) + slot * D::PWW;
+#pragma unroll
+  for (int ta = 0; ta < D::TA; ++ta)
+#pragma unroll
+    for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[rank * D::MN + (16 * ta + 4 * g + v) * D::N + 16 * tb + c] = dB[ta][tb][v];
+#pragma unroll
+  for (int tj = 0; tj < D::TJ; ++tj)
+#pragma unroll
+    for (int tk = 0; tk < D::TK; ++tk)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        red[D::R * D::MN + rank * D::PQ + (16 * tj + 4 * g + v) * D::Q + 16 * tk + c] = dC[tj][tk][v];
+  if (rank == 0) {
+#pragma unroll
+    for (int tk = 0; tk < D::TK; ++tk)
+#pragma unroll
+      for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          red[D::R * (D::MN + D::PQ) + (16 * tk + c) * D::N + 16 * tb + 4 * g + v] = db[tk][tb][v];
+  }
+  __syncthreads();
+  const PartRow out{part, (int64_t)gridDim.x, (int64_t)blockIdx.x, 0};
+  const float* L = reinterpret_cast<const float*>(smem);
+  auto ssum = [&](int e) {
+    float t = L[e];
+#pragma unroll
+    for (int s = 1; s < Q::RPI; ++s) t += L[s * D::PWW + e];
+    return t;
+  };
+  for (int e = tid; e < D::R * D::MN; e += kThreads) out[e] = ssum(e);
+  for (int e = tid; e < D::PQ; e += kThreads) {
+    const float sv = Sm ? bf2f(Sm[e]) : 1.f;
+    float ds = 0.f;
+#pragma unroll
+    for (int i = 0; i < D::R; ++i) {
+      const float dcv = ssum(D::R * D::MN + i * D::PQ + e);
+      ds = fmaf(bf2f(A[i * D::PQ + e]), dcv, ds);
+      out[D::R * D::MN + i * D::PQ + e] = sv * dcv;
+    }
+    out[D::R * (D::MN + D::PQ) + e] = Sm ? ds : 0.f;
+  }
+  for (int e = tid; e < D::Q * D::N; e += kThreads) out[D::R * (D::MN + D::PQ) + D::PQ + e] = ssum(D::R * (D::MN + D::PQ) + e);
+}
+
+int device_cus_bf16() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) return 256;
+  return v;
+}
+
+template <class D>
+void run_fwd_bf16(const LayerArgsBf16& a, hipStream_t s) {
+  static const int per_cu = [] {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fwd_bf16_kernel<D>, kThreads, 0) != hipSuccess || nb < 1)
+      nb = 1;
+    return nb;
+  }();
+  int64_t grid = (int64_t)per_cu * device_cus_bf16();
+  const int64_t need = (a.N + kWaves - 1) / kWaves;
+  if (grid > need) grid = need;
+  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3((unsigned)grid), dim3(kThreads), 0, s, a.N, a.flags, a.x, a.S, a.A,
+                     a.B, a.bias, a.y);
+}
+
+template <class D>
+void run_bwd_bf16(const LayerArgsBf16& a, int grid, hipStream_t s) {
+  using Q = RB<D>;
+  static const bool attr = [] {
+    (void)hipFuncSetAttribute((const void*)bwd_bf16_kernel<D, 0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Q::LDS);
+    (void)hipFuncSetAttribute((const void*)bwd_bf16_kernel<D, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Q::LDS);
+    (void)hipFuncSetAttribute((const void*)bwd_bf16_kernel<D, 2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Q::LDS);
+    return true;
+  }();
+  (void)attr;
+  const int dxm = a.dx == nullptr ? 0 : ((a.flags & KRON_DX_RELU_MASK) ? 2 : 1);
+  if (dxm == 0)
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, 0>), dim3(grid), dim3(kThreads), Q::LDS, s, a.N, a.x, a.S, a.A, a.B,
+                       a.dy, a.dx, a.part);
+  else if (dxm == 1)
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, 1>), dim3(grid), dim3(kThreads), Q::LDS, s, a.N, a.x, a.S, a.A, a.B,
+                       a.dy, a.dx, a.part);
+  else
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, 2>), dim3(grid), dim3(kThreads), Q::LDS, s, a.N, a.x, a.S, a.A, a.B,
+                       a.dy, a.dx, a.part);
+}
+
+struct EntryBf16 {
+  int p, q, m, n, r;
+  int rows_per_step;
+  void (*fwd)(const LayerArgsBf16&, hipStream_t);
+  void (*bwd)(const LayerArgsBf16&, int, hipStream_t);
+};
+
+#define KRON_BF16_ENTRY(P, Q, M, N, R)                                                             \
+  EntryBf16{P, Q, M, N, R, RB<BD<P, Q, M, N, R>>::RPI, &run_fwd_bf16<BD<P, Q, M, N, R>>,            \
+            &run_bwd_bf16<BD<P, Q, M, N, R>>}
+
+// The 1024x1024 layers with m = 32 (r = 1, 2, 4) and m = 64 (r = 2).
+const EntryBf16 kBf16Table[] = {
+    KRON_BF16_ENTRY(32, 32, 32, 32, 1), KRON_BF16_ENTRY(32, 32, 32, 32, 2), KRON_BF16_ENTRY(32, 32, 32, 32, 4),
+    KRON_BF16_ENTRY(16, 16, 64, 64, 2),
+};
+static_assert(RB<BD<32, 32, 32, 32, 4>>::OK && RB<BD<32, 32, 32, 32, 2>>::OK && RB<BD<32, 32, 32, 32, 1>>::OK &&
+                  RB<BD<16, 16, 64, 64, 2>>::OK,
+              "every bf16 table shape fits its LDS budget");
+
+const EntryBf16* find_bf16(int p, int q, int m, int n, int r) {
+  for (const EntryBf16& e : kBf16Table)
+    if (e.p == p && e.q == q && e.m == m && e.n == n && e.r == r) return &e;
+  return nullptr;
+}
+
+}  // namespace
+
+bool bf16_supported(int p, int q, int m, int n, int r) { return find_bf16(p, q, m, n, r) != nullptr; }
+
+int bf16_bwd_groups(int64_t N, int p, int q, int m, int n, int r) {
+  const EntryBf16* e = find_bf16(p, q, m, n, r);
+  if (!e) return 0;
+  const int64_t g = (N + e->rows_per_step - 1) / e->rows_per_step;
+  const int64_t gmax = 2 * 256;   // two workgroups per compute unit (fixed: the workspace depends on it)
+  return (int)(g < gmax ? g : gmax);
+}
+
+hipError_t launch_fwd_bf16(const LayerArgsBf16& a, hipStream_t s) {
+  const EntryBf16* e = find_bf16(a.p, a.q, a.m, a.n, a.r);
+  if (!e) return hipErrorInvalidValue;
+  if (a.N == 0) return hipSuccess;
+  e->fwd(a, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_bf16(const LayerArgsBf16& a, int G, hipStream_t s) {
+  const EntryBf16* e = find_bf16(a.p, a.q, a.m, a.n, a.r);
+  if (!e) return hipErrorInvalidValue;
+  if (G == 0) return hipSuccess;
+  e->bwd(a, G, s);
+  return hipGetLastError();
+}
+
+}  // namespace kron

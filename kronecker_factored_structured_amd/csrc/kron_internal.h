@@ -91,6 +91,26 @@ hipError_t launch_bwd_generic(const LayerArgs& a, int G, hipStream_t s);
 bool mfma_fwd_supported(int p, int q, int m, int n, int r);
 bool mfma_bwd_supported(int p, int q, int m, int n, int r);
 int mfma_bwd_groups(int64_t N, int p, int q, int m, int n, int r);
+// bf16 layer (kron_bf16.hip): bf16 tensors as 16-bit patterns, fp32 parameter gradients.
+struct LayerArgsBf16 {
+  int64_t N;
+  int32_t p, q, m, n, r;
+  uint32_t flags;
+  const uint16_t* x;
+  const uint16_t* S;
+  const uint16_t* A;
+  const uint16_t* B;
+  const uint16_t* bias;
+  const uint16_t* dy;
+  uint16_t* y;
+  uint16_t* dx;
+  float* part;   // workspace: G partial rows of PW columns (column-blocked)
+};
+bool bf16_supported(int p, int q, int m, int n, int r);
+int bf16_bwd_groups(int64_t N, int p, int q, int m, int n, int r);
+hipError_t launch_fwd_bf16(const LayerArgsBf16& a, hipStream_t s);
+hipError_t launch_bwd_bf16(const LayerArgsBf16& a, int G, hipStream_t s);
+
 // Ranks per chunk when a backward with r ranks runs as r / chunk passes of the
 // chunk-rank MFMA kernel (dX accumulated over the passes), else 0.
 int mfma_bwd_chunk(int p, int q, int m, int n, int r);

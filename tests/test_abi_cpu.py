@@ -118,6 +118,29 @@ def test_bwd_argument_errors():
     assert bwd(sm, **a) == _lib.KRON_E_ARG
 
 
+def test_bf16_argument_errors():
+    """bf16 layer: unsupported shapes and bad arguments are refused on the host, before any
+    HIP call (fake device addresses are never dereferenced)."""
+    L = _lib.lib()
+    MB = 1 << 20
+    bad = KronShape(8, 32, 64, 24, 48, 1, 0)   # m = 24: no bf16 kernel
+    assert L.kron_linear_fwd_bf16(ctypes.byref(bad), P(0), None, P(MB), P(2 * MB), None, P(3 * MB), None) == \
+        _lib.KRON_E_UNSUPPORTED
+    assert L.kron_linear_bwd_bf16_workspace_bytes(ctypes.byref(bad)) == 0
+    s = KronShape(8, 32, 32, 32, 32, 4, 0)
+    need = L.kron_linear_bwd_bf16_workspace_bytes(ctypes.byref(s))
+    assert need > 0 and need % 256 == 0
+    assert L.kron_linear_fwd_bf16(ctypes.byref(s), P(4), None, P(MB), P(2 * MB), None, P(3 * MB), None) == \
+        _lib.KRON_E_ALIGN
+    assert L.kron_linear_fwd_bf16(ctypes.byref(s), P(0), None, P(MB), P(2 * MB), None, P(16), None) == \
+        _lib.KRON_E_ALIAS
+    args = [P(0), None, P(MB), P(2 * MB), P(3 * MB), P(4 * MB), None, P(5 * MB), P(6 * MB), P(7 * MB), P(8 * MB)]
+    assert L.kron_linear_bwd_bf16(ctypes.byref(s), *args, ctypes.c_size_t(need - 1), None) == _lib.KRON_E_WORKSPACE
+    args_ds = list(args)
+    args_ds[6] = P(9 * MB)   # dS without S
+    assert L.kron_linear_bwd_bf16(ctypes.byref(s), *args_ds, ctypes.c_size_t(need), None) == _lib.KRON_E_NULL
+
+
 def test_ks_argument_errors():
     L = _lib.lib()
     MB = 1 << 20
