@@ -1,7 +1,7 @@
 """Benchmark of the Kronecker-factored layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--cpu-seconds 10]
-    python bench.py --workload {headline,tiny,mlp_step,gpt2_ffn,ks}
+    python bench.py --workload {headline,headline_bf16,tiny,mlp_step,gpt2_ffn,ks}
     python bench.py --calibrate-copy      (plain device copy of known size, for HBM counters)
 
 Default workload (one JSON line): one step is one kron_linear_fwd + one kron_linear_bwd
@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP32_TFLOPS = 157.3     # MI355X dense fp32 matrix, published
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 matrix, published
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 METRIC = "kron_linear fwd+bwd rows/s and % of HBM/fp32 roofline, 1024² m=32 r=4"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_kron_linear_bwd_headline.json")
@@ -149,6 +150,42 @@ class Layer:
         self.K.kron_linear_bwd(self.x, self.S, self.A, self.B, self.dy, workspace=self.ws, outs=self.outs)
 
 
+class LayerBf16:
+    """bf16 tensors of one Kronecker layer workload (inputs rounded to bf16 once, on the host);
+    y and dx bf16, factor gradients fp32."""
+
+    def __init__(self, inp, dev):
+        import torch
+        import kronecker_factored_structured_amd as K
+        from workloads import bf16_bits
+        self.K = K
+
+        def t(a):
+            if a is None:
+                return None
+            bits = bf16_bits(np.ascontiguousarray(a, dtype=np.float32))
+            return torch.from_numpy(bits.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+
+        self.x, self.S, self.A, self.B, self.bias, self.dy = (t(a) for a in (inp.x, inp.S, inp.A, inp.B,
+                                                                           inp.bias, inp.dy))
+        sh = inp.shape
+        f32 = torch.float32
+        self.y = torch.empty(sh.N, sh.q * sh.n, device=dev, dtype=torch.bfloat16)
+        self.outs = dict(dx=torch.empty_like(self.x),
+                         dS=None if self.S is None else torch.empty(self.S.shape, device=dev, dtype=f32),
+                         dA=torch.empty(self.A.shape, device=dev, dtype=f32),
+                         dB=torch.empty(self.B.shape, device=dev, dtype=f32),
+                         dbias=None if self.bias is None else torch.empty(self.bias.shape, device=dev, dtype=f32))
+        shape = K.layer_shape(sh.N, self.S, self.A, self.B)
+        self.ws = torch.empty(K.kron_linear_bwd_bf16_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+
+    def fwd(self):
+        self.K.kron_linear_fwd_bf16(self.x, self.S, self.A, self.B, self.bias, out=self.y)
+
+    def bwd(self):
+        self.K.kron_linear_bwd_bf16(self.x, self.S, self.A, self.B, self.dy, workspace=self.ws, outs=self.outs)
+
+
 def split_times(layer, steps):
     """Mean seconds of the forward and of the backward call, from events around each call."""
     import torch
@@ -231,6 +268,35 @@ def layer_record(name, inp, L, args, extra=None):
     if extra:
         rec.update(extra)
     print(json.dumps(rec), flush=True)
+
+
+def run_headline_bf16(args, dev):
+    """The same layer and rows in bf16 (inputs, y, dx), fp32 accumulation and fp32 factor
+    gradients.  Algorithmic bytes halve with the element size while the flops stay, so at
+    this shape the pass is bound by HBM, not by the bf16 matrix rate."""
+    from workloads import headline_layer
+    inp = headline_layer()
+    sh = inp.shape
+    N, p, q, m, n, r = sh.N, sh.p, sh.q, sh.m, sh.n, sh.r
+    nnz = int(np.count_nonzero(inp.S))
+    L = LayerBf16(inp, dev)
+    ms, _ = timed(lambda: (L.fwd(), L.bwd()), args.steps, args.warmup)
+    t_fwd, t_bwd = split_times(L, args.steps)
+    ff, fb, _, _ = work_per_row(p, q, m, n, r, nnz)
+    bf, bb = 2 * (p * m + q * n), 2 * (2 * p * m + q * n)
+    t_flop = N * (ff + fb) / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = N * (bf + bb) / (PEAK_HBM_GBS * 1e9)
+    t_roof = max(t_flop, t_hbm)
+    print(json.dumps({"workload": "headline_bf16: kron_linear fwd+bwd, 1024x1024, m=n=32, r=4, half of S "
+                                  "zeroed, 20000 rows, bf16 x/S/A/B/bias/dy/y/dx, fp32 dS/dA/dB/dbias",
+                      "rows_per_s": round(N / (ms * 1e-3), 1), "us_per_fwd_bwd": round(ms * 1e3, 2),
+                      "t_fwd_us": round(t_fwd * 1e6, 2), "t_bwd_us": round(t_bwd * 1e6, 2),
+                      "achieved_gbs": round(N * (bf + bb) / (ms * 1e-3) / 1e9, 1),
+                      "effective_tflops": round(N * (ff + fb) / (ms * 1e-3) / 1e12, 3),
+                      "t_roof_us": round(t_roof * 1e6, 2), "roofline_frac": round(t_roof / (ms * 1e-3), 4),
+                      "bound": "hbm" if t_hbm >= t_flop else "bf16",
+                      "t_bf16_flops_us": round(t_flop * 1e6, 2), "t_hbm_us": round(t_hbm * 1e6, 2),
+                      "shape": {"N": N, "p": p, "q": q, "m": m, "n": n, "r": r}}), flush=True)
 
 
 def run_tiny(args, dev):
@@ -332,7 +398,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="headline",
-                    choices=("headline", "tiny", "mlp_step", "gpt2_ffn", "ks"))
+                    choices=("headline", "headline_bf16", "tiny", "mlp_step", "gpt2_ffn", "ks"))
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed running before the warmup steps, for the GPU clock to ramp up")
@@ -349,7 +415,7 @@ def main():
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         return run_copy(args, dev)
-    {"headline": run_headline, "tiny": run_tiny, "mlp_step": run_mlp_step, "gpt2_ffn": run_gpt2,
+    {"headline": run_headline, "headline_bf16": run_headline_bf16, "tiny": run_tiny, "mlp_step": run_mlp_step, "gpt2_ffn": run_gpt2,
      "ks": run_ks}[args.workload](args, dev)
 
 

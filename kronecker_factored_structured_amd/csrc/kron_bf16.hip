@@ -31,15 +31,17 @@ __device__ __forceinline__ f4 mfma16(s4 a, s4 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
-// fp32 -> bf16, round to nearest even (NaN stays NaN)
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// fp32 -> bf16 by the hardware conversion (v_cvt_pk_bf16_f32, two values per instruction),
+// round to nearest even under the default rounding mode
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), b2));
 }
 __device__ __forceinline__ s4 pack4(f4 v) {
-  return s4{(short)f2bf(v[0]), (short)f2bf(v[1]), (short)f2bf(v[2]), (short)f2bf(v[3])};
+  typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(s4, (u2{pack2(v[0], v[1]), pack2(v[2], v[3])}));
 }
 __device__ __forceinline__ s4 load_s4(const uint16_t* p) { return *reinterpret_cast<const s4*>(p); }
 __device__ __forceinline__ s4 gather4(const uint16_t* p, int stride) {

@@ -89,3 +89,27 @@ def test_mlp_layer_shape_with_relu_flags():
 
 def test_without_S_and_without_dx():
     compare_bf16(kron_inputs(62, 777, 32, 32, 32, 32, 4, s_mode="none", bias_mode="normal"), want_dx=False)
+
+
+def test_output_rounding_is_nearest_even():
+    """y = bf16(x + bias) with identity factors (r = 1, no S, A = B = I, so every product is
+    exact): fp32 sums that sit exactly halfway between two bf16 values round to the one with
+    an even last mantissa bit (1 + 2^-8 -> 1, 1 + 3*2^-8 -> 1 + 2^-6)."""
+    N, d = 4, 32
+    x = np.zeros((N, d * d), np.float32)
+    x[0] = 1.0
+    x[1] = 1.0 + 2.0 ** -7
+    x[2] = -(1.0 + 2.0 ** -7)
+    x[3] = 3.0
+    bias = np.full(d * d, 2.0 ** -8, np.float32)
+    eye = np.eye(d, dtype=np.float32)[None]
+    _, xt = bf16_round(x)
+    _, At = bf16_round(eye)
+    _, Bt = bf16_round(eye)
+    _, bt = bf16_round(bias)
+    y = to_f64(K().kron_linear_fwd_bf16(xt, None, At, Bt, bt))
+    # row 2: -(1 + 2^-7) + 2^-8 = -(1 + 2^-8), a tie between -1 and -(1 + 2^-7) -> -1;
+    # row 3: 3 + 2^-8 is a quarter of a bf16 step above 3 -> 3
+    want = {0: 1.0, 1: 1.0 + 2.0 ** -6, 2: -1.0, 3: 3.0}
+    for i, v in want.items():
+        assert np.all(y[i] == v), (i, np.unique(y[i]), v)
