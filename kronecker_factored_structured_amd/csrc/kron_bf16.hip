@@ -60,69 +60,154 @@ struct BD {
 };
 
 // ---------------------------------------------------------------------------------
+// Operands of 16 x 16 x (4W) products.  W = 4: v_mfma_f32_16x16x16_bf16; W = 8:
+// v_mfma_f32_16x16x32_bf16 (lane l = 16g + c supplies A[c][8g..8g+7] and B[8g..8g+7][c]).
+// A contraction does not depend on the order of its K values as long as both operands use
+// the same order, so each product fixes, per lane group g and element u, which K index the
+// element carries:
+//   k_row: W consecutive K values (an operand read from a row in memory),
+//   k_acc: four consecutive K values from each of W/4 accumulator tiles 16 apart (an
+//          operand assembled from D tiles of the previous product: a D tile gives lane
+//          group g the rows 4g..4g+3 of its 16).
+// The factor operand of the same product (a register table) is built in the matching order.
+// ---------------------------------------------------------------------------------
+typedef short s8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+
+template <int W>
+struct OpT;
+template <>
+struct OpT<4> {
+  typedef s4 T;
+};
+template <>
+struct OpT<8> {
+  typedef s8 T;
+};
+__device__ __forceinline__ f4 mfma(s4 a, s4 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0); }
+__device__ __forceinline__ f4 mfma(s8 a, s8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c, 0, 0, 0);
+}
+template <int W>
+__device__ __forceinline__ int k_row(int s, int g, int u) { return 4 * W * s + W * g + u; }
+template <int W>
+__device__ __forceinline__ int k_acc(int s, int g, int u) { return 4 * W * s + 16 * (u / 4) + 4 * g + (u % 4); }
+// operand of chunk s from accumulator tiles packed to bf16: tiles W/4*s .. W/4*s + W/4 - 1
+__device__ __forceinline__ s4 join(s4 a) { return a; }
+__device__ __forceinline__ s8 join(s4 a, s4 b) { return s8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}; }
+
+// ---------------------------------------------------------------------------------
 // Forward.  Persistent; one row per wavefront at a time.  Per rank i:
-//   Z_i   = X B_i      (TJ x TB tiles, TA products each)     A = X[j][a..], B = B_i[a..][b]
-//   Y^T  += Z_i^T C_i  (TB x TK tiles, TJ products each)     A = bf16(Z tile), B = C_i[j..][k]
-// The B_i and C_i operands of every lane live in registers for the whole kernel.
+//   Z_i   = X B_i      (TJ x TB tiles, KC1 products each)   A = X[j][k_row], B = B_i[k_row][b]
+//   Y^T  += Z_i^T C_i  (TB x TK tiles, KC2 products each)   A = bf16(Z tiles), B = C_i[k_acc][k]
+// B_i and C_i = S o A_i (rounded to bf16) are staged once per workgroup in LDS in lane
+// order (each lane's operand is one contiguous 8- or 16-byte piece) and then held in
+// registers; the bias values of the lane's outputs are held in registers too, so that the
+// only global loads in the row loop are the next row's x.
 // ---------------------------------------------------------------------------------
 template <class D>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(int64_t N, uint32_t flags, const uint16_t* __restrict__ x,
-                                                            const uint16_t* __restrict__ Sm,
-                                                            const uint16_t* __restrict__ A,
-                                                            const uint16_t* __restrict__ B,
-                                                            const uint16_t* __restrict__ bias,
-                                                            uint16_t* __restrict__ y) {
-  __shared__ uint16_t rB[D::R * D::MN];   // B as given
-  __shared__ uint16_t rC[D::R * D::PQ];   // C_i = S o A_i, rounded to bf16
-  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15, wave = tid >> 6;
-  const int64_t stride = (int64_t)gridDim.x * kWaves;
-  int64_t row = (int64_t)blockIdx.x * kWaves + wave;
+struct FB {
+  static constexpr int W1 = D::M % 32 == 0 ? 8 : 4, KC1 = D::M / (4 * W1);   // Z = X B_i over a
+  static constexpr int W2 = D::P % 32 == 0 ? 8 : 4, KC2 = D::P / (4 * W2);   // Y^T over j
+  static constexpr int TAB_B = D::R * D::TB * KC1 * 64;   // lane entries of W1 values
+  static constexpr int TAB_C = D::R * D::TK * KC2 * 64;   // lane entries of W2 values
+  // registers per lane: factor tables, x (current and next row), accumulators, Z tiles, bias
+  static constexpr int REGS = D::R * D::TB * KC1 * W1 / 2 + D::R * D::TK * KC2 * W2 / 2 + D::TJ * KC1 * W1 +
+                              D::TB * D::TK * 6 + D::TJ * D::TB * 2 + 16;
+  static constexpr int NT = REGS <= 128 ? 1024 : 512;
+  static constexpr int NW = NT / 64;
+};
 
-  // the first row's X operands: X[j = 16tj + c][a = 16t + 4g ..]
-  s4 xn[D::TJ][D::TA];
-  auto load_x = [&](s4 (&dst)[D::TJ][D::TA], int64_t r) {
+template <class D>
+__global__ __launch_bounds__((FB<D>::NT)) void fwd_bf16_kernel(int64_t N, uint32_t flags,
+                                                               const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ Sm,
+                                                               const uint16_t* __restrict__ A,
+                                                               const uint16_t* __restrict__ B,
+                                                               const uint16_t* __restrict__ bias,
+                                                               uint16_t* __restrict__ y) {
+  using F = FB<D>;
+  constexpr int W1 = F::W1, KC1 = F::KC1, W2 = F::W2, KC2 = F::KC2;
+  typedef typename OpT<W1>::T O1;
+  typedef typename OpT<W2>::T O2;
+  __shared__ __attribute__((aligned(16))) uint16_t tabB[F::TAB_B * W1];
+  __shared__ __attribute__((aligned(16))) uint16_t tabC[F::TAB_C * W2];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15, wave = tid >> 6;
+  const int64_t stride = (int64_t)gridDim.x * F::NW;
+  int64_t row = (int64_t)blockIdx.x * F::NW + wave;
+
+  // X operands of a row: X[j = 16tj + c][k_row(s, g, 0 .. W1-1)], one contiguous piece each
+  O1 xn[D::TJ][KC1];
+  auto load_x = [&](O1 (&dst)[D::TJ][KC1], int64_t r) {
     const uint16_t* xr = x + r * D::IN;
 #pragma unroll
     for (int tj = 0; tj < D::TJ; ++tj)
 #pragma unroll
-      for (int t = 0; t < D::TA; ++t) dst[tj][t] = load_s4(xr + (16 * tj + c) * D::M + 16 * t + 4 * g);
+      for (int s = 0; s < KC1; ++s)
+        dst[tj][s] = *reinterpret_cast<const O1*>(xr + (16 * tj + c) * D::M + k_row<W1>(s, g, 0));
   };
   if (row < N) load_x(xn, row);
 
-  for (int e = tid; e < D::R * D::MN; e += kThreads) rB[e] = B[e];
-  for (int e = tid; e < D::R * D::PQ; e += kThreads) {
-    const float a = bf2f(A[e]);
-    rC[e] = f2bf(Sm ? bf2f(Sm[e % D::PQ]) * a : a);
+  for (int e = tid; e < F::TAB_B; e += F::NT) {   // e = ((i*TB + tb)*KC1 + s)*64 + lane
+    const int ln = e & 63, rest = e >> 6, s = rest % KC1, tb = (rest / KC1) % D::TB, i = rest / (KC1 * D::TB);
+    const uint16_t* Bi = B + i * D::MN + 16 * tb + (ln & 15);
+    O1 v;
+#pragma unroll
+    for (int u = 0; u < W1; ++u) v[u] = (short)Bi[k_row<W1>(s, ln >> 4, u) * D::N];
+    *reinterpret_cast<O1*>(tabB + e * W1) = v;
   }
+  for (int e = tid; e < F::TAB_C; e += F::NT) {   // e = ((i*TK + tk)*KC2 + s)*64 + lane
+    const int ln = e & 63, rest = e >> 6, s = rest % KC2, tk = (rest / KC2) % D::TK, i = rest / (KC2 * D::TK);
+    const int k = 16 * tk + (ln & 15);
+    O2 v;
+#pragma unroll
+    for (int u = 0; u < W2; ++u) {
+      const int jk = k_acc<W2>(s, ln >> 4, u) * D::Q + k;
+      const float av = bf2f(A[i * D::PQ + jk]);
+      v[u] = (short)f2bf(Sm ? bf2f(Sm[jk]) * av : av);
+    }
+    *reinterpret_cast<O2*>(tabC + e * W2) = v;
+  }
+  // bias of the lane's outputs: Y^T[b = 16tb + 4g + v][k = 16tk + c] -> bias[k*N + b]
+  s4 bv[D::TB][D::TK];
+#pragma unroll
+  for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+    for (int tk = 0; tk < D::TK; ++tk)
+      bv[tb][tk] = bias ? load_s4(bias + (16 * tk + c) * D::N + 16 * tb + 4 * g) : s4{0, 0, 0, 0};
   __syncthreads();
-  s4 bop[D::R][D::TB][D::TA];   // B_i[a = 16t + 4g + v][b = 16tb + c]
-  s4 cop[D::R][D::TK][D::TJ];   // C_i[j = 16t + 4g + v][k = 16tk + c]
+  O1 bop[D::R][D::TB][KC1];
+  O2 cop[D::R][D::TK][KC2];
 #pragma unroll
   for (int i = 0; i < D::R; ++i) {
 #pragma unroll
     for (int tb = 0; tb < D::TB; ++tb)
 #pragma unroll
-      for (int t = 0; t < D::TA; ++t) bop[i][tb][t] = gather4(rB + i * D::MN + (16 * t + 4 * g) * D::N + 16 * tb + c, D::N);
+      for (int s = 0; s < KC1; ++s)
+        bop[i][tb][s] = *reinterpret_cast<const O1*>(tabB + (((i * D::TB + tb) * KC1 + s) * 64 + lane) * W1);
 #pragma unroll
     for (int tk = 0; tk < D::TK; ++tk)
 #pragma unroll
-      for (int t = 0; t < D::TJ; ++t) cop[i][tk][t] = gather4(rC + i * D::PQ + (16 * t + 4 * g) * D::Q + 16 * tk + c, D::Q);
+      for (int s = 0; s < KC2; ++s)
+        cop[i][tk][s] = *reinterpret_cast<const O2*>(tabC + (((i * D::TK + tk) * KC2 + s) * 64 + lane) * W2);
   }
   const bool relu = flags & KRON_RELU_OUT;
 
   for (; row < N; row += stride) {
-    s4 xa[D::TJ][D::TA];
+    O1 xa[D::TJ][KC1];
 #pragma unroll
     for (int tj = 0; tj < D::TJ; ++tj)
 #pragma unroll
-      for (int t = 0; t < D::TA; ++t) xa[tj][t] = xn[tj][t];
+      for (int s = 0; s < KC1; ++s) xa[tj][s] = xn[tj][s];
     load_x(xn, row + stride < N ? row + stride : row);   // the next row (the last row reloads itself)
     __builtin_amdgcn_sched_barrier(0);
     f4 acc[D::TB][D::TK];
 #pragma unroll
     for (int tb = 0; tb < D::TB; ++tb)
 #pragma unroll
-      for (int tk = 0; tk < D::TK; ++tk) acc[tb][tk] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int tk = 0; tk < D::TK; ++tk)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[tb][tk][v] = bf2f((uint16_t)bv[tb][tk][v]);
 #pragma unroll
     for (int i = 0; i < D::R; ++i) {
       s4 zb[D::TJ][D::TB];   // bf16(Z_i)[j = 16tj + 4g + v][b = 16tb + c]
@@ -132,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(int64_t N, uint32_t 
         for (int tb = 0; tb < D::TB; ++tb) {
           f4 z = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int t = 0; t < D::TA; ++t) z = mfma16(xa[tj][t], bop[i][tb][t], z);
+          for (int s = 0; s < KC1; ++s) z = mfma(xa[tj][s], bop[i][tb][s], z);
           zb[tj][tb] = pack4(z);
         }
 #pragma unroll
@@ -140,7 +225,14 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(int64_t N, uint32_t 
 #pragma unroll
         for (int tk = 0; tk < D::TK; ++tk)
 #pragma unroll
-          for (int tj = 0; tj < D::TJ; ++tj) acc[tb][tk] = mfma16(zb[tj][tb], cop[i][tk][tj], acc[tb][tk]);
+          for (int s = 0; s < KC2; ++s) {
+            O2 zo;
+            if constexpr (W2 == 8)
+              zo = join(zb[2 * s][tb], zb[2 * s + 1][tb]);
+            else
+              zo = join(zb[s][tb]);
+            acc[tb][tk] = mfma(zo, cop[i][tk][s], acc[tb][tk]);
+          }
     }
     // acc[tb][tk] register v = Y^T[b = 16tb + 4g + v][k = 16tk + c] -> y[k*N + b]
     uint16_t* yr = y + row * D::OUT;
@@ -148,18 +240,12 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(int64_t N, uint32_t 
     for (int tb = 0; tb < D::TB; ++tb)
 #pragma unroll
       for (int tk = 0; tk < D::TK; ++tk) {
-        const int off = (16 * tk + c) * D::N + 16 * tb + 4 * g;
         f4 o = acc[tb][tk];
-        if (bias) {
-          const s4 bv = load_s4(bias + off);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) o[v] += bf2f((uint16_t)bv[v]);
-        }
         if (relu) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) o[v] = o[v] > 0.f ? o[v] : 0.f;
         }
-        *reinterpret_cast<s4*>(yr + off) = pack4(o);
+        *reinterpret_cast<s4*>(yr + (16 * tk + c) * D::N + 16 * tb + 4 * g) = pack4(o);
       }
   }
 }
@@ -486,16 +572,17 @@ int device_cus_bf16() {
 
 template <class D>
 void run_fwd_bf16(const LayerArgsBf16& a, hipStream_t s) {
+  using F = FB<D>;
   static const int per_cu = [] {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fwd_bf16_kernel<D>, kThreads, 0) != hipSuccess || nb < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fwd_bf16_kernel<D>, F::NT, 0) != hipSuccess || nb < 1)
       nb = 1;
     return nb;
   }();
   int64_t grid = (int64_t)per_cu * device_cus_bf16();
-  const int64_t need = (a.N + kWaves - 1) / kWaves;
+  const int64_t need = (a.N + F::NW - 1) / F::NW;
   if (grid > need) grid = need;
-  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3((unsigned)grid), dim3(kThreads), 0, s, a.N, a.flags, a.x, a.S, a.A,
+  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3((unsigned)grid), dim3(F::NT), 0, s, a.N, a.flags, a.x, a.S, a.A,
                      a.B, a.bias, a.y);
 }
 
