@@ -24,12 +24,7 @@ namespace {
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef short s4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 
-__device__ __forceinline__ f4 mfma16(s4 a, s4 b, f4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 // fp32 -> bf16 by the hardware conversion (v_cvt_pk_bf16_f32, two values per instruction),
 // round to nearest even under the default rounding mode
@@ -44,9 +39,6 @@ __device__ __forceinline__ s4 pack4(f4 v) {
   return __builtin_bit_cast(s4, (u2{pack2(v[0], v[1]), pack2(v[2], v[3])}));
 }
 __device__ __forceinline__ s4 load_s4(const uint16_t* p) { return *reinterpret_cast<const s4*>(p); }
-__device__ __forceinline__ s4 gather4(const uint16_t* p, int stride) {
-  return s4{(short)p[0], (short)p[stride], (short)p[2 * stride], (short)p[3 * stride]};
-}
 
 template <int P_, int Q_, int M_, int N_, int R_>
 struct BD {
@@ -251,64 +243,104 @@ __global__ __launch_bounds__((FB<D>::NT)) void fwd_bf16_kernel(int64_t N, uint32
 }
 
 // ---------------------------------------------------------------------------------
-// Backward, rank-parallel: a workgroup of four wavefronts owns RPI = 4 / R rows per step,
-// wavefront w computes rank w % R of row slot w / R.  The rows are staged in LDS in both
-// index orders (X[j][a], X^T[a][j], dY[k][b], dY^T[b][k]) so that every operand is one
-// 8-byte read.  Per rank and row:
-//   Z^T[b][j]  = sum_a B_i[a][b] X[j][a]        A = B_i^T[b][a..] (registers), B = X[j][a..]
-//   dC[j][k]  += sum_b Z^T[b][j] dY[k][b]       A = bf16(Z^T tile),             B = dY[k][b..]
-//   G^T[b][j]  = sum_k dY[k][b] C_i[j][k]       A = dY^T[b][k..],               B = C_i[j][k..] (registers)
-//   dX^T[a][j] = sum_b B_i[a][b] G^T[b][j]      A = B_i[a][b..] (registers),    B = bf16(G^T tile)
-//   dB[a][b]  += sum_j X[j][a] G[j][b]          A = X^T[a][j..],                B = G (G^T tile through LDS)
-// dX^T partials of the R ranks of a row meet in LDS and are added in rank order; the
-// partial row [dB | dA | dS | dbias] and the fixed-order column reduction are those of the
-// fp32 layer.
+// Backward, rank-parallel: a workgroup of R * RPI wavefronts owns RPI rows per step;
+// wavefront w works on row slot w / R and rank i = w % R.  Per rank and row, with the K
+// order of each product's operands in brackets:
+//   Z^T[b][j]  = sum_a B_i^T[b][a] X[j][a]      A: table          B: X row pieces      [k_row]
+//   dC[j][k]  += sum_b Z[j][b] dY[k][b]         A: Z^T tiles      B: dY row pieces     [k_acc]
+//   G^T[b][j]  = sum_k dY[k][b] C_i[j][k]       A: dY columns     B: table             [k_acc]
+//   dB[a][b]  += sum_j X[j][a] G_i[j][b]        A: X columns      B: G_i columns       [k_acc]
+// and per row, all ranks in one contraction over (i, b), split by output tile over the
+// row's R wavefronts:
+//   dX^T[a][j] = sum_(i,b) B_i[a][b] G_i[j][b]  A: table          B: G_i row pieces    [k_row]
+// Rows and G_i tiles live in LDS in row-major order (16-byte row writes, 8-byte G_i writes);
+// column operands come from the LDS transpose read ds_read_b64_tr_b16, which hands each
+// lane four consecutive rows of one column.  Rows are triple-buffered and G tiles
+// double-buffered, so one barrier per step suffices: the rows of step t+1 are written
+// during step t into the buffer last read in step t-2, and every wavefront has left step
+// t-2 once all have reached the barrier of step t-1.
+// The partial row [dB | dA | dS | dbias] and the fixed-order column reduction are those of
+// the fp32 layer.
 // ---------------------------------------------------------------------------------
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+
+// lane (g, c) receives m[r0 + v][cb + c], v = 0..3, where r0 is the lane group's first row
+__device__ __forceinline__ s4 tr16(const uint16_t* m, int ld, int r0, int cb, int lane) {
+  const int l = lane & 15;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s4*)(m + (r0 + (l >> 2)) * ld + cb + 4 * (l & 3)));
+}
+// W values of one column (cb + c) over the K rows of chunk s in k_acc order
+template <int W>
+__device__ __forceinline__ typename OpT<W>::T col_op(const uint16_t* m, int ld, int s, int g, int cb, int lane) {
+  if constexpr (W == 8)
+    return join(tr16(m, ld, 32 * s + 4 * g, cb, lane), tr16(m, ld, 32 * s + 16 + 4 * g, cb, lane));
+  else
+    return tr16(m, ld, 16 * s + 4 * g, cb, lane);
+}
+// W values of one row in k_acc order (two 8-byte pieces for W = 8)
+template <int W>
+__device__ __forceinline__ typename OpT<W>::T row_acc(const uint16_t* r, int s, int g) {
+  if constexpr (W == 8)
+    return join(load_s4(r + 32 * s + 4 * g), load_s4(r + 32 * s + 16 + 4 * g));
+  else
+    return load_s4(r + 16 * s + 4 * g);
+}
+
 template <class D>
-struct RB {
+struct BB {
   static constexpr int R = D::R;
-  static constexpr int RPI = 4 / R;
-  // row strides (bf16 elements), padded by 8 so that rows stay 16-byte aligned and the
-  // sixteen rows of a lane group start on different banks
-  static constexpr int LXA = D::M + 8;   // X[j][a]
-  static constexpr int LXJ = D::P + 8;   // X^T[a][j]
-  static constexpr int LYB = D::N + 8;   // dY[k][b]
-  static constexpr int LYK = D::Q + 8;   // dY^T[b][k]
-  static constexpr int OX = 0, OXT = D::P * LXA, OY = OXT + D::M * LXJ, OYT = OY + D::Q * LYB;
-  static constexpr int SLOT = OYT + D::N * LYK;   // bf16 elements per row slot
-  static constexpr int ROWBUF = RPI * SLOT;
-  static constexpr int LG = D::P + 8;             // G^T tile gs[b][j] (bf16)
-  static constexpr int LDX = D::M + 4;            // dX^T partial dxp[j][a] (fp32)
-  static constexpr int WREG_BYTES = (D::N * LG * 2 > D::P * LDX * 4 ? D::N * LG * 2 : D::P * LDX * 4);
-  static constexpr int WREG = (WREG_BYTES + 15) / 16 * 16;   // bytes per wavefront
-  static constexpr size_t MAIN = (size_t)ROWBUF * 2 + (size_t)kWaves * WREG;
+  static constexpr int RPI = R == 4 ? 1 : 2;   // rows per step
+  static constexpr int NW = R * RPI, NT = 64 * NW;
+  static constexpr int WA = D::M % 32 == 0 ? 8 : 4, KA = D::M / (4 * WA);   // over a
+  static constexpr int WB = D::N % 32 == 0 ? 8 : 4, KB = D::N / (4 * WB);   // over b
+  static constexpr int WK = D::Q % 32 == 0 ? 8 : 4, KK = D::Q / (4 * WK);   // over k
+  static constexpr int WJ = D::P % 32 == 0 ? 8 : 4, KJ = D::P / (4 * WJ);   // over j
+  static constexpr int DXT = D::TA * D::TJ / R;                             // dX^T tiles per wavefront
+  // LDS (bf16 elements): row strides padded by 16 so that the rows a transpose read touches
+  // start on different banks; a step's rows: x [P][LX], dy [Q][LY]; its G tiles [R][P][LG]
+  static constexpr int LX = D::M + 16, LY = D::N + 16, LG = D::N + 16;
+  static constexpr int XS = D::P * LX, YS = D::Q * LY, GR = D::P * LG;
+  static constexpr int ROWS = RPI * (XS + YS), GBUF = RPI * R * GR;
+  static constexpr int NRB = 3, NGB = 2;
+  static constexpr size_t MAIN = (size_t)(NRB * ROWS + NGB * GBUF) * 2;
+  // prologue staging: B_i [a][b] and C_i [j][k] row-major with odd-word row strides
+  static constexpr int SB = D::N + 2, SC = D::Q + 2;
+  static constexpr size_t STAGE = (size_t)(R * D::M * SB + R * D::P * SC) * 2;
   static constexpr size_t COMBINE = (size_t)RPI * D::PWW * 4;
-  static constexpr size_t LDS = (MAIN > COMBINE ? MAIN : COMBINE);
+  static constexpr size_t LDS = MAIN > COMBINE ? (MAIN > STAGE ? MAIN : STAGE) : (COMBINE > STAGE ? COMBINE : STAGE);
   static constexpr int CHUNKS = (D::IN + D::OUT) / 8;   // 16-byte pieces of one row's x and dy
-  static constexpr int NPF = (RPI * CHUNKS + kThreads - 1) / kThreads;
-  static constexpr bool OK = D::SHAPE_OK && (R == 1 || R == 2 || R == 4) && LDS <= 80 * 1024;
+  static constexpr int NPF = (RPI * CHUNKS + NT - 1) / NT;
+  static constexpr bool OK = D::SHAPE_OK && (R == 1 || R == 2 || R == 4) && (D::TA * D::TJ) % R == 0 &&
+                             LDS <= 80 * 1024;
 };
 
 template <class D, int DXM>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_bf16_kernel(int64_t N, const uint16_t* __restrict__ x, const uint16_t* __restrict__ Sm,
-                     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
-                     const uint16_t* __restrict__ dy, uint16_t* __restrict__ dx, float* __restrict__ part) {
-  using Q = RB<D>;
+__global__ __launch_bounds__((BB<D>::NT)) void bwd_bf16_kernel(int64_t N, const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ Sm,
+                                                               const uint16_t* __restrict__ A,
+                                                               const uint16_t* __restrict__ B,
+                                                               const uint16_t* __restrict__ dy,
+                                                               uint16_t* __restrict__ dx, float* __restrict__ part) {
+  using Q = BB<D>;
+  constexpr int R = D::R, NT = Q::NT;
+  constexpr int WA = Q::WA, KA = Q::KA, WB = Q::WB, KB = Q::KB, WK = Q::WK, KK = Q::KK, WJ = Q::WJ, KJ = Q::KJ;
+  typedef typename OpT<WA>::T OA;
+  typedef typename OpT<WB>::T OB;
+  typedef typename OpT<WK>::T OQ;
+  typedef typename OpT<WJ>::T OJ;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint16_t* rowbuf = reinterpret_cast<uint16_t*>(smem);
-  unsigned char* wbase = smem + (size_t)Q::ROWBUF * 2;
+  uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15, wave = tid >> 6;
-  const int slot = wave / Q::R, rank = wave % Q::R;
+  const int slot = wave / R, rank = wave % R;
   const int64_t ngrp = (N + Q::RPI - 1) / Q::RPI;
 
-  // prefetch: 16-byte pieces of the step's rows (x then dy of each row slot)
-  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  // one step's rows as 16-byte pieces: x then dy of each row slot (zero past the last row)
   u4 pf[Q::NPF];
   auto fetch = [&](int64_t grp) {
 #pragma unroll
     for (int t = 0; t < Q::NPF; ++t) {
-      const int f = tid + t * kThreads;
+      const int f = tid + t * NT;
       u4 v = u4{0u, 0u, 0u, 0u};
       if (f < Q::RPI * Q::CHUNKS) {
         const int s = f / Q::CHUNKS, o = 8 * (f % Q::CHUNKS);
@@ -320,71 +352,80 @@ void bwd_bf16_kernel(int64_t N, const uint16_t* __restrict__ x, const uint16_t* 
       pf[t] = v;
     }
   };
-  auto stash = [&]() {
+  auto stash = [&](int buf) {
 #pragma unroll
     for (int t = 0; t < Q::NPF; ++t) {
-      const int f = tid + t * kThreads;
+      const int f = tid + t * NT;
       if (f < Q::RPI * Q::CHUNKS) {
         const int s = f / Q::CHUNKS, o = 8 * (f % Q::CHUNKS);
-        uint16_t* sb = rowbuf + s * Q::SLOT;
-        const u4 v = pf[t];
-        const uint16_t e[8] = {(uint16_t)(v[0] & 0xffffu), (uint16_t)(v[0] >> 16), (uint16_t)(v[1] & 0xffffu),
-                               (uint16_t)(v[1] >> 16), (uint16_t)(v[2] & 0xffffu), (uint16_t)(v[2] >> 16),
-                               (uint16_t)(v[3] & 0xffffu), (uint16_t)(v[3] >> 16)};
-        if (o < D::IN) {   // X[j][a .. a+7] and X^T[a .. a+7][j]
-          const int j = o / D::M, a = o % D::M;
-          *reinterpret_cast<u4*>(sb + Q::OX + j * Q::LXA + a) = v;
-#pragma unroll
-          for (int u = 0; u < 8; ++u) sb[Q::OXT + (a + u) * Q::LXJ + j] = e[u];
-        } else {           // dY[k][b .. b+7] and dY^T[b .. b+7][k]
-          const int o2 = o - D::IN, k = o2 / D::N, b = o2 % D::N;
-          *reinterpret_cast<u4*>(sb + Q::OY + k * Q::LYB + b) = v;
-#pragma unroll
-          for (int u = 0; u < 8; ++u) sb[Q::OYT + (b + u) * Q::LYK + k] = e[u];
-        }
+        uint16_t* rb = lds + buf * Q::ROWS + s * (Q::XS + Q::YS);
+        if (o < D::IN)
+          *reinterpret_cast<u4*>(rb + (o / D::M) * Q::LX + o % D::M) = pf[t];
+        else
+          *reinterpret_cast<u4*>(rb + Q::XS + ((o - D::IN) / D::N) * Q::LY + (o - D::IN) % D::N) = pf[t];
       }
     }
   };
   fetch(blockIdx.x);
 
-  // this wavefront's rank operands (bf16), straight from global memory
-  const uint16_t* Bi = B + rank * D::MN;
-  const uint16_t* Ai = A + rank * D::PQ;
-  s4 bt[D::TB][D::TA];   // B_i^T[b = 16tb + c][a = 16t + 4g ..]   (A operand of Z^T)
-  s4 ct[D::TJ][D::TK];   // C_i[j = 16tj + c][k = 16t + 4g ..]     (B operand of G^T)
-  s4 bx[D::TA][D::TB];   // B_i[a = 16ta + c][b = 16t + 4g ..]     (A operand of dX^T)
-#pragma unroll
-  for (int tb = 0; tb < D::TB; ++tb)
-#pragma unroll
-    for (int t = 0; t < D::TA; ++t) bt[tb][t] = gather4(Bi + (16 * t + 4 * g) * D::N + 16 * tb + c, D::N);
-#pragma unroll
-  for (int tj = 0; tj < D::TJ; ++tj)
-#pragma unroll
-    for (int t = 0; t < D::TK; ++t) {
-      const int j = 16 * tj + c, k0 = 16 * t + 4 * g;
-      s4 v;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float a = bf2f(Ai[j * D::Q + k0 + u]);
-        v[u] = (short)f2bf(Sm ? bf2f(Sm[j * D::Q + k0 + u]) * a : a);
-      }
-      ct[tj][t] = v;
+  // ---- prologue: B_i and C_i = S o A_i staged row-major, then this wavefront's operands
+  uint16_t* sB = lds;                               // [i][a][SB]
+  uint16_t* sC = lds + R * D::M * Q::SB;            // [i][j][SC]
+  for (int e = tid; e < R * D::MN / 2; e += NT) {   // pairs of B values
+    const int i = e / (D::MN / 2), r = 2 * (e % (D::MN / 2)), a = r / D::N, b = r % D::N;
+    *reinterpret_cast<uint32_t*>(sB + (i * D::M + a) * Q::SB + b) =
+        *reinterpret_cast<const uint32_t*>(B + i * D::MN + r);
+  }
+  for (int e = tid; e < R * D::PQ / 2; e += NT) {
+    const int i = e / (D::PQ / 2), r = 2 * (e % (D::PQ / 2)), j = r / D::Q, k = r % D::Q;
+    const uint32_t av = *reinterpret_cast<const uint32_t*>(A + i * D::PQ + r);
+    float a0 = bf2f((uint16_t)(av & 0xffffu)), a1 = bf2f((uint16_t)(av >> 16));
+    if (Sm) {
+      const uint32_t sv = *reinterpret_cast<const uint32_t*>(Sm + r);
+      a0 *= bf2f((uint16_t)(sv & 0xffffu));
+      a1 *= bf2f((uint16_t)(sv >> 16));
     }
+    *reinterpret_cast<uint32_t*>(sC + (i * D::P + j) * Q::SC + k) = pack2(a0, a1);
+  }
+  __syncthreads();
+  OA t1[D::TB][KA];         // B_i^T[b = 16tb + c][a = k_row(s, g, u)]
+  OQ t3[D::TJ][KK];         // C_i^T[k = k_acc(s, g, u)][j = 16tj + c]
+  OB t4[Q::DXT][R][KB];     // B_i'[a = 16ta + c][b = k_row(s, g, u)] for this wavefront's dX^T tiles
+  {
+    const uint16_t* Bi = sB + rank * D::M * Q::SB;
+    const uint16_t* Ci = sC + rank * D::P * Q::SC;
 #pragma unroll
-  for (int ta = 0; ta < D::TA; ++ta)
+    for (int tb = 0; tb < D::TB; ++tb)
 #pragma unroll
-    for (int t = 0; t < D::TB; ++t) bx[ta][t] = load_s4(Bi + (16 * ta + c) * D::N + 16 * t + 4 * g);
-
-  for (int e = tid; e < Q::ROWBUF; e += kThreads) rowbuf[e] = 0;   // padding stays zero
+      for (int s = 0; s < KA; ++s)
+#pragma unroll
+        for (int u = 0; u < WA; ++u) t1[tb][s][u] = (short)Bi[k_row<WA>(s, g, u) * Q::SB + 16 * tb + c];
+#pragma unroll
+    for (int tj = 0; tj < D::TJ; ++tj)
+#pragma unroll
+      for (int s = 0; s < KK; ++s)
+#pragma unroll
+        for (int u = 0; u < WK; ++u) t3[tj][s][u] = (short)Ci[(16 * tj + c) * Q::SC + k_acc<WK>(s, g, u)];
+#pragma unroll
+    for (int d = 0; d < Q::DXT; ++d) {
+      const int ta = (rank * Q::DXT + d) / D::TJ;
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int s = 0; s < KB; ++s)
+#pragma unroll
+          for (int u = 0; u < WB; ++u)
+            t4[d][i][s][u] = (short)sB[(i * D::M + 16 * ta + c) * Q::SB + k_row<WB>(s, g, u)];
+    }
+  }
+  __syncthreads();   // the staging area becomes row buffers
+  stash(0);
+  fetch(blockIdx.x + gridDim.x);
   __syncthreads();
 
-  const uint16_t* Xs = rowbuf + slot * Q::SLOT;
-  uint16_t* gs = reinterpret_cast<uint16_t*>(wbase + wave * Q::WREG);   // G^T tile [b][j] (bf16)
-  float* dxp = reinterpret_cast<float*>(wbase + wave * Q::WREG);        // then the dX^T partial [j][a]
-
-  f4 dC[D::TJ][D::TK];   // dC_rank[j = 16tj + 4g + v][k = 16tk + c]
-  f4 dB[D::TA][D::TB];   // dB_rank[a = 16ta + 4g + v][b = 16tb + c]
-  f4 db[D::TK][D::TB];   // dbias[k = 16tk + c][b = 16tb + 4g + v]   (rank 0)
+  f4 dC[D::TJ][D::TK];    // dC_i[j = 16tj + 4g + v][k = 16tk + c]
+  f4 dB[D::TA][D::TB];    // dB_i[a = 16ta + 4g + v][b = 16tb + c]
+  float db[D::TK][KB][WB];  // dbias[k = 16tk + c][b = k_acc(s, g, u)]   (rank 0)
 #pragma unroll
   for (int tj = 0; tj < D::TJ; ++tj)
 #pragma unroll
@@ -396,123 +437,119 @@ void bwd_bf16_kernel(int64_t N, const uint16_t* __restrict__ x, const uint16_t* 
 #pragma unroll
   for (int tk = 0; tk < D::TK; ++tk)
 #pragma unroll
-    for (int tb = 0; tb < D::TB; ++tb) db[tk][tb] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < KB; ++s)
+#pragma unroll
+      for (int u = 0; u < WB; ++u) db[tk][s][u] = 0.f;
 
-  auto step = [&](int64_t grp, auto tail_c) {
+  auto step = [&](int64_t grp, int rbuf, int gbuf, auto tail_c) {
     constexpr bool kTail = decltype(tail_c)::value;
-    stash();
-    __syncthreads();
-    fetch(grp + gridDim.x);
-    const uint16_t* X = Xs + Q::OX;
-    const uint16_t* XT = Xs + Q::OXT;
-    const uint16_t* Y = Xs + Q::OY;
-    const uint16_t* YT = Xs + Q::OYT;
-    // Z^T[b][j]
-    f4 zt[D::TB][D::TJ];
+    const uint16_t* X = lds + rbuf * Q::ROWS + slot * (Q::XS + Q::YS);
+    const uint16_t* Y = X + Q::XS;
+    uint16_t* Gs = lds + Q::NRB * Q::ROWS + gbuf * Q::GBUF + slot * R * Q::GR;   // G_i: Gs + i * GR
+    uint16_t* Gi = Gs + rank * Q::GR;
+    // Z^T[b][j] = sum_a B_i^T[b][a] X[j][a]
+    s4 zb[D::TB][D::TJ];
 #pragma unroll
-    for (int tb = 0; tb < D::TB; ++tb)
+    for (int tj = 0; tj < D::TJ; ++tj) {
+      OA xo[KA];
 #pragma unroll
-      for (int tj = 0; tj < D::TJ; ++tj) {
-        f4 t4 = f4{0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < KA; ++s) xo[s] = *reinterpret_cast<const OA*>(X + (16 * tj + c) * Q::LX + k_row<WA>(s, g, 0));
 #pragma unroll
-        for (int t = 0; t < D::TA; ++t) t4 = mfma16(bt[tb][t], load_s4(X + (16 * tj + c) * Q::LXA + 16 * t + 4 * g), t4);
-        zt[tb][tj] = t4;
+      for (int tb = 0; tb < D::TB; ++tb) {
+        f4 z = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KA; ++s) z = mfma(t1[tb][s], xo[s], z);
+        zb[tb][tj] = pack4(z);
       }
-    // dC[j][k] += sum_b Z^T[b][j] dY[k][b];  dbias += dY (rank 0)
+    }
+    // dC[j][k] += sum_b Z[j][b] dY[k][b];  dbias += dY (rank 0)
 #pragma unroll
     for (int tk = 0; tk < D::TK; ++tk)
 #pragma unroll
-      for (int tb = 0; tb < D::TB; ++tb) {
-        const s4 yk = load_s4(Y + (16 * tk + c) * Q::LYB + 16 * tb + 4 * g);   // dY[k = 16tk + c][b = 16tb + 4g ..]
+      for (int s = 0; s < KB; ++s) {
+        const OB yo = row_acc<WB>(Y + (16 * tk + c) * Q::LY, s, g);
         if (rank == 0) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) db[tk][tb][v] += bf2f((uint16_t)yk[v]);
+          for (int u = 0; u < WB; ++u) db[tk][s][u] += bf2f((uint16_t)yo[u]);
         }
 #pragma unroll
-        for (int tj = 0; tj < D::TJ; ++tj) dC[tj][tk] = mfma16(pack4(zt[tb][tj]), yk, dC[tj][tk]);
+        for (int tj = 0; tj < D::TJ; ++tj) {
+          OB zo;
+          if constexpr (WB == 8)
+            zo = join(zb[2 * s][tj], zb[2 * s + 1][tj]);
+          else
+            zo = join(zb[s][tj]);
+          dC[tj][tk] = mfma(zo, yo, dC[tj][tk]);
+        }
       }
-    // G^T[b][j]
-    f4 gt[D::TB][D::TJ];
+    // G^T[b][j] = sum_k dY[k][b] C_i[j][k]  ->  G_i[j][b] in LDS (bf16)
+#pragma unroll
+    for (int tb = 0; tb < D::TB; ++tb) {
+      OQ yc[KK];
+#pragma unroll
+      for (int s = 0; s < KK; ++s) yc[s] = col_op<WK>(Y, Q::LY, s, g, 16 * tb, lane);
+#pragma unroll
+      for (int tj = 0; tj < D::TJ; ++tj) {
+        f4 t4v = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KK; ++s) t4v = mfma(yc[s], t3[tj][s], t4v);
+        *reinterpret_cast<s4*>(Gi + (16 * tj + c) * Q::LG + 16 * tb + 4 * g) = pack4(t4v);
+      }
+    }
+    // the next step's rows into the next row buffer; the rows of the step after that in flight
+    stash(rbuf == Q::NRB - 1 ? 0 : rbuf + 1);
+    fetch(grp + 2 * (int64_t)gridDim.x);
+    __syncthreads();
+    // dX^T[a][j] = sum_(i,b) B_i[a][b] G_i[j][b]: this wavefront's tiles
+    const int64_t row = grp * Q::RPI + slot;
+#pragma unroll
+    for (int d = 0; d < Q::DXT; ++d) {
+      const int t = rank * Q::DXT + d, ta = t / D::TJ, tj = t % D::TJ;
+      f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int s = 0; s < KB; ++s)
+          acc = mfma(t4[d][i][s],
+                     *reinterpret_cast<const OB*>(Gs + i * Q::GR + (16 * tj + c) * Q::LG + k_row<WB>(s, g, 0)), acc);
+      if constexpr (DXM != 0) {
+        if (!kTail || row < N) {
+          const int off = (16 * tj + c) * D::M + 16 * ta + 4 * g;   // dX[j][a .. a+3]
+          if constexpr (DXM == 2) {
+            const s4 xm = load_s4(X + (16 * tj + c) * Q::LX + 16 * ta + 4 * g);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] = bf2f((uint16_t)xm[v]) > 0.f ? acc[v] : 0.f;
+          }
+          *reinterpret_cast<s4*>(dx + row * D::IN + off) = pack4(acc);
+        }
+      }
+    }
+    // dB_i[a][b] += sum_j X[j][a] G_i[j][b]
+    OJ gc[D::TB][KJ];
 #pragma unroll
     for (int tb = 0; tb < D::TB; ++tb)
 #pragma unroll
-      for (int tj = 0; tj < D::TJ; ++tj) {
-        f4 t4 = f4{0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < KJ; ++s) gc[tb][s] = col_op<WJ>(Gi, Q::LG, s, g, 16 * tb, lane);
 #pragma unroll
-        for (int t = 0; t < D::TK; ++t) t4 = mfma16(load_s4(YT + (16 * tb + c) * Q::LYK + 16 * t + 4 * g), ct[tj][t], t4);
-        gt[tb][tj] = t4;
-      }
-    // G^T tile -> LDS as gs[b][j] (bf16)
-    s4 gb[D::TB][D::TJ];
+    for (int ta = 0; ta < D::TA; ++ta) {
+      OJ xc[KJ];
 #pragma unroll
-    for (int tb = 0; tb < D::TB; ++tb)
-#pragma unroll
-      for (int tj = 0; tj < D::TJ; ++tj) {
-        gb[tb][tj] = pack4(gt[tb][tj]);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) gs[(16 * tb + 4 * g + v) * Q::LG + 16 * tj + c] = (uint16_t)gb[tb][tj][v];
-      }
-    __builtin_amdgcn_wave_barrier();
-    // dX^T[a][j] = sum_b B_i[a][b] G^T[b][j]
-    f4 dxt[D::TA][D::TJ];
-#pragma unroll
-    for (int ta = 0; ta < D::TA; ++ta)
-#pragma unroll
-      for (int tj = 0; tj < D::TJ; ++tj) {
-        f4 t4 = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int tb = 0; tb < D::TB; ++tb) t4 = mfma16(bx[ta][tb], gb[tb][tj], t4);
-        dxt[ta][tj] = t4;
-      }
-    // dB[a][b] += sum_j X^T[a][j] G[j][b]
-#pragma unroll
-    for (int ta = 0; ta < D::TA; ++ta)
+      for (int s = 0; s < KJ; ++s) xc[s] = col_op<WJ>(X, Q::LX, s, g, 16 * ta, lane);
 #pragma unroll
       for (int tb = 0; tb < D::TB; ++tb)
 #pragma unroll
-        for (int t = 0; t < D::TJ; ++t)
-          dB[ta][tb] = mfma16(load_s4(XT + (16 * ta + c) * Q::LXJ + 16 * t + 4 * g),
-                              load_s4(gs + (16 * tb + c) * Q::LG + 16 * t + 4 * g), dB[ta][tb]);
-    __builtin_amdgcn_wave_barrier();
-    // this rank's dX^T partial -> LDS as dxp[j][a] (fp32)
-#pragma unroll
-    for (int ta = 0; ta < D::TA; ++ta)
-#pragma unroll
-      for (int tj = 0; tj < D::TJ; ++tj)
-        *reinterpret_cast<f4*>(dxp + (16 * tj + c) * Q::LDX + 16 * ta + 4 * g) = dxt[ta][tj];
-    __syncthreads();
-    // dX of the step's rows: the R rank partials added in rank order, rounded to bf16
-    if constexpr (DXM != 0) {
-      constexpr int PER_ROW = D::IN / 4;
-      constexpr int TOT = Q::RPI * PER_ROW;
-#pragma unroll
-      for (int t = 0; t < (TOT + kThreads - 1) / kThreads; ++t) {
-        const int f = tid + t * kThreads;
-        if (TOT % kThreads != 0 && f >= TOT) continue;
-        const int s = f / PER_ROW, o = 4 * (f % PER_ROW);
-        const int64_t row = grp * Q::RPI + s;
-        if (kTail && row >= N) continue;
-        const int j = o / D::M, a = o % D::M;
-        const float* w0 = reinterpret_cast<const float*>(wbase + (s * Q::R) * Q::WREG);
-        f4 acc = *reinterpret_cast<const f4*>(w0 + j * Q::LDX + a);
-#pragma unroll
-        for (int i = 1; i < Q::R; ++i)
-          acc += *reinterpret_cast<const f4*>(reinterpret_cast<const float*>(wbase + (s * Q::R + i) * Q::WREG) +
-                                              j * Q::LDX + a);
-        if constexpr (DXM == 2) {
-          const uint16_t* xr = rowbuf + s * Q::SLOT + Q::OX + j * Q::LXA + a;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[v] = bf2f(xr[v]) > 0.f ? acc[v] : 0.f;
-        }
-        *reinterpret_cast<s4*>(dx + row * D::IN + o) = pack4(acc);
-      }
+        for (int s = 0; s < KJ; ++s) dB[ta][tb] = mfma(xc[s], gc[tb][s], dB[ta][tb]);
     }
-    __syncthreads();   // the next step's stash overwrites the rows and this step's partials
   };
   const int64_t nfull = N / Q::RPI;
   int64_t grp = blockIdx.x;
-  for (; grp < nfull; grp += gridDim.x) step(grp, std::false_type{});
-  if (grp < ngrp) step(grp, std::true_type{});
+  int rbuf = 0, gbuf = 0;
+  for (; grp < nfull; grp += gridDim.x) {
+    step(grp, rbuf, gbuf, std::false_type{});
+    rbuf = rbuf == Q::NRB - 1 ? 0 : rbuf + 1;
+    gbuf ^= 1;
+  }
+  if (grp < ngrp) step(grp, rbuf, gbuf, std::true_type{});
 
   // Partial row of this workgroup: [dB (R*M*N) | dA (R*P*Q) | dS (P*Q) | dbias (Q*N)], fp32.
   __syncthreads();
@@ -534,10 +571,10 @@ void bwd_bf16_kernel(int64_t N, const uint16_t* __restrict__ x, const uint16_t* 
 #pragma unroll
     for (int tk = 0; tk < D::TK; ++tk)
 #pragma unroll
-      for (int tb = 0; tb < D::TB; ++tb)
+      for (int s = 0; s < KB; ++s)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          red[D::R * (D::MN + D::PQ) + (16 * tk + c) * D::N + 16 * tb + 4 * g + v] = db[tk][tb][v];
+        for (int u = 0; u < WB; ++u)
+          red[D::R * (D::MN + D::PQ) + (16 * tk + c) * D::N + k_acc<WB>(s, g, u)] = db[tk][s][u];
   }
   __syncthreads();
   const PartRow out{part, (int64_t)gridDim.x, (int64_t)blockIdx.x, 0};
@@ -548,8 +585,8 @@ void bwd_bf16_kernel(int64_t N, const uint16_t* __restrict__ x, const uint16_t* 
     for (int s = 1; s < Q::RPI; ++s) t += L[s * D::PWW + e];
     return t;
   };
-  for (int e = tid; e < D::R * D::MN; e += kThreads) out[e] = ssum(e);
-  for (int e = tid; e < D::PQ; e += kThreads) {
+  for (int e = tid; e < D::R * D::MN; e += NT) out[e] = ssum(e);
+  for (int e = tid; e < D::PQ; e += NT) {
     const float sv = Sm ? bf2f(Sm[e]) : 1.f;
     float ds = 0.f;
 #pragma unroll
@@ -560,7 +597,7 @@ void bwd_bf16_kernel(int64_t N, const uint16_t* __restrict__ x, const uint16_t* 
     }
     out[D::R * (D::MN + D::PQ) + e] = Sm ? ds : 0.f;
   }
-  for (int e = tid; e < D::Q * D::N; e += kThreads) out[D::R * (D::MN + D::PQ) + D::PQ + e] = ssum(D::R * (D::MN + D::PQ) + e);
+  for (int e = tid; e < D::Q * D::N; e += NT) out[D::R * (D::MN + D::PQ) + D::PQ + e] = ssum(D::R * (D::MN + D::PQ) + e);
 }
 
 int device_cus_bf16() {
@@ -588,7 +625,7 @@ void run_fwd_bf16(const LayerArgsBf16& a, hipStream_t s) {
 
 template <class D>
 void run_bwd_bf16(const LayerArgsBf16& a, int grid, hipStream_t s) {
-  using Q = RB<D>;
+  using Q = BB<D>;
   static const bool attr = [] {
     (void)hipFuncSetAttribute((const void*)bwd_bf16_kernel<D, 0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Q::LDS);
     (void)hipFuncSetAttribute((const void*)bwd_bf16_kernel<D, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Q::LDS);
@@ -598,13 +635,13 @@ void run_bwd_bf16(const LayerArgsBf16& a, int grid, hipStream_t s) {
   (void)attr;
   const int dxm = a.dx == nullptr ? 0 : ((a.flags & KRON_DX_RELU_MASK) ? 2 : 1);
   if (dxm == 0)
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, 0>), dim3(grid), dim3(kThreads), Q::LDS, s, a.N, a.x, a.S, a.A, a.B,
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, 0>), dim3(grid), dim3(Q::NT), Q::LDS, s, a.N, a.x, a.S, a.A, a.B,
                        a.dy, a.dx, a.part);
   else if (dxm == 1)
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, 1>), dim3(grid), dim3(kThreads), Q::LDS, s, a.N, a.x, a.S, a.A, a.B,
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, 1>), dim3(grid), dim3(Q::NT), Q::LDS, s, a.N, a.x, a.S, a.A, a.B,
                        a.dy, a.dx, a.part);
   else
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, 2>), dim3(grid), dim3(kThreads), Q::LDS, s, a.N, a.x, a.S, a.A, a.B,
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, 2>), dim3(grid), dim3(Q::NT), Q::LDS, s, a.N, a.x, a.S, a.A, a.B,
                        a.dy, a.dx, a.part);
 }
 
@@ -616,7 +653,7 @@ struct EntryBf16 {
 };
 
 #define KRON_BF16_ENTRY(P, Q, M, N, R)                                                             \
-  EntryBf16{P, Q, M, N, R, RB<BD<P, Q, M, N, R>>::RPI, &run_fwd_bf16<BD<P, Q, M, N, R>>,            \
+  EntryBf16{P, Q, M, N, R, BB<BD<P, Q, M, N, R>>::RPI, &run_fwd_bf16<BD<P, Q, M, N, R>>,            \
             &run_bwd_bf16<BD<P, Q, M, N, R>>}
 
 // The 1024x1024 layers with m = 32 (r = 1, 2, 4) and m = 64 (r = 2).
@@ -624,8 +661,8 @@ const EntryBf16 kBf16Table[] = {
     KRON_BF16_ENTRY(32, 32, 32, 32, 1), KRON_BF16_ENTRY(32, 32, 32, 32, 2), KRON_BF16_ENTRY(32, 32, 32, 32, 4),
     KRON_BF16_ENTRY(16, 16, 64, 64, 2),
 };
-static_assert(RB<BD<32, 32, 32, 32, 4>>::OK && RB<BD<32, 32, 32, 32, 2>>::OK && RB<BD<32, 32, 32, 32, 1>>::OK &&
-                  RB<BD<16, 16, 64, 64, 2>>::OK,
+static_assert(BB<BD<32, 32, 32, 32, 4>>::OK && BB<BD<32, 32, 32, 32, 2>>::OK && BB<BD<32, 32, 32, 32, 1>>::OK &&
+                  BB<BD<16, 16, 64, 64, 2>>::OK,
               "every bf16 table shape fits its LDS budget");
 
 const EntryBf16* find_bf16(int p, int q, int m, int n, int r) {
