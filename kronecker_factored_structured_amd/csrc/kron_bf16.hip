@@ -287,10 +287,10 @@ __device__ __forceinline__ typename OpT<W>::T row_acc(const uint16_t* r, int s, 
     return load_s4(r + 16 * s + 4 * g);
 }
 
-template <class D>
+template <class D, int RPI_>
 struct BB {
   static constexpr int R = D::R;
-  static constexpr int RPI = R == 4 ? 1 : 2;   // rows per step
+  static constexpr int RPI = RPI_;   // rows per step
   static constexpr int NW = R * RPI, NT = 64 * NW;
   static constexpr int WA = D::M % 32 == 0 ? 8 : 4, KA = D::M / (4 * WA);   // over a
   static constexpr int WB = D::N % 32 == 0 ? 8 : 4, KB = D::N / (4 * WB);   // over b
@@ -312,17 +312,17 @@ struct BB {
   static constexpr int CHUNKS = (D::IN + D::OUT) / 8;   // 16-byte pieces of one row's x and dy
   static constexpr int NPF = (RPI * CHUNKS + NT - 1) / NT;
   static constexpr bool OK = D::SHAPE_OK && (R == 1 || R == 2 || R == 4) && (D::TA * D::TJ) % R == 0 &&
-                             LDS <= 80 * 1024;
+                             LDS <= 160 * 1024;
 };
 
-template <class D, int DXM>
-__global__ __launch_bounds__((BB<D>::NT)) void bwd_bf16_kernel(int64_t N, const uint16_t* __restrict__ x,
+template <class D, int RPI, int DXM>
+__global__ __launch_bounds__((BB<D, RPI>::NT)) void bwd_bf16_kernel(int64_t N, const uint16_t* __restrict__ x,
                                                                const uint16_t* __restrict__ Sm,
                                                                const uint16_t* __restrict__ A,
                                                                const uint16_t* __restrict__ B,
                                                                const uint16_t* __restrict__ dy,
                                                                uint16_t* __restrict__ dx, float* __restrict__ part) {
-  using Q = BB<D>;
+  using Q = BB<D, RPI>;
   constexpr int R = D::R, NT = Q::NT;
   constexpr int WA = Q::WA, KA = Q::KA, WB = Q::WB, KB = Q::KB, WK = Q::WK, KK = Q::KK, WJ = Q::WJ, KJ = Q::KJ;
   typedef typename OpT<WA>::T OA;
@@ -335,9 +335,10 @@ __global__ __launch_bounds__((BB<D>::NT)) void bwd_bf16_kernel(int64_t N, const 
   const int slot = wave / R, rank = wave % R;
   const int64_t ngrp = (N + Q::RPI - 1) / Q::RPI;
 
-  // one step's rows as 16-byte pieces: x then dy of each row slot (zero past the last row)
-  u4 pf[Q::NPF];
-  auto fetch = [&](int64_t grp) {
+  // one step's rows as 16-byte pieces: x then dy of each row slot (zero past the last row);
+  // two register sets alternate so that each step's rows are requested three steps ahead
+  u4 pfA[Q::NPF], pfB[Q::NPF];
+  auto fetch = [&](u4 (&pf)[Q::NPF], int64_t grp) {
 #pragma unroll
     for (int t = 0; t < Q::NPF; ++t) {
       const int f = tid + t * NT;
@@ -352,7 +353,7 @@ __global__ __launch_bounds__((BB<D>::NT)) void bwd_bf16_kernel(int64_t N, const 
       pf[t] = v;
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](const u4 (&pf)[Q::NPF], int buf) {
 #pragma unroll
     for (int t = 0; t < Q::NPF; ++t) {
       const int f = tid + t * NT;
@@ -366,7 +367,7 @@ __global__ __launch_bounds__((BB<D>::NT)) void bwd_bf16_kernel(int64_t N, const 
       }
     }
   };
-  fetch(blockIdx.x);
+  fetch(pfA, blockIdx.x);
 
   // ---- prologue: B_i and C_i = S o A_i staged row-major, then this wavefront's operands
   uint16_t* sB = lds;                               // [i][a][SB]
@@ -419,8 +420,9 @@ __global__ __launch_bounds__((BB<D>::NT)) void bwd_bf16_kernel(int64_t N, const 
     }
   }
   __syncthreads();   // the staging area becomes row buffers
-  stash(0);
-  fetch(blockIdx.x + gridDim.x);
+  stash(pfA, 0);
+  fetch(pfA, blockIdx.x + (int64_t)gridDim.x);
+  fetch(pfB, blockIdx.x + 2 * (int64_t)gridDim.x);
   __syncthreads();
 
   f4 dC[D::TJ][D::TK];    // dC_i[j = 16tj + 4g + v][k = 16tk + c]
@@ -441,7 +443,7 @@ __global__ __launch_bounds__((BB<D>::NT)) void bwd_bf16_kernel(int64_t N, const 
 #pragma unroll
       for (int u = 0; u < WB; ++u) db[tk][s][u] = 0.f;
 
-  auto step = [&](int64_t grp, int rbuf, int gbuf, auto tail_c) {
+  auto step = [&](int64_t grp, int rbuf, int gbuf, u4 (&pf)[Q::NPF], auto tail_c) {
     constexpr bool kTail = decltype(tail_c)::value;
     const uint16_t* X = lds + rbuf * Q::ROWS + slot * (Q::XS + Q::YS);
     const uint16_t* Y = X + Q::XS;
@@ -496,9 +498,9 @@ __global__ __launch_bounds__((BB<D>::NT)) void bwd_bf16_kernel(int64_t N, const 
         *reinterpret_cast<s4*>(Gi + (16 * tj + c) * Q::LG + 16 * tb + 4 * g) = pack4(t4v);
       }
     }
-    // the next step's rows into the next row buffer; the rows of the step after that in flight
-    stash(rbuf == Q::NRB - 1 ? 0 : rbuf + 1);
-    fetch(grp + 2 * (int64_t)gridDim.x);
+    // the next step's rows into the next row buffer; this register set fetches three steps ahead
+    stash(pf, rbuf == Q::NRB - 1 ? 0 : rbuf + 1);
+    fetch(pf, grp + 3 * (int64_t)gridDim.x);
     __syncthreads();
     // dX^T[a][j] = sum_(i,b) B_i[a][b] G_i[j][b]: this wavefront's tiles
     const int64_t row = grp * Q::RPI + slot;
@@ -541,15 +543,27 @@ __global__ __launch_bounds__((BB<D>::NT)) void bwd_bf16_kernel(int64_t N, const 
         for (int s = 0; s < KJ; ++s) dB[ta][tb] = mfma(xc[s], gc[tb][s], dB[ta][tb]);
     }
   };
-  const int64_t nfull = N / Q::RPI;
+  const int64_t nfull = N / Q::RPI, G = gridDim.x;
   int64_t grp = blockIdx.x;
   int rbuf = 0, gbuf = 0;
-  for (; grp < nfull; grp += gridDim.x) {
-    step(grp, rbuf, gbuf, std::false_type{});
+  auto advance = [&]() {
     rbuf = rbuf == Q::NRB - 1 ? 0 : rbuf + 1;
     gbuf ^= 1;
+    grp += G;
+  };
+  while (grp + G < nfull) {   // local steps in pairs: register set A, then B
+    step(grp, rbuf, gbuf, pfA, std::false_type{});
+    advance();
+    step(grp, rbuf, gbuf, pfB, std::false_type{});
+    advance();
   }
-  if (grp < ngrp) step(grp, rbuf, gbuf, std::true_type{});
+  if (grp < nfull) {
+    step(grp, rbuf, gbuf, pfA, std::false_type{});
+    advance();
+    if (grp < ngrp) step(grp, rbuf, gbuf, pfB, std::true_type{});
+  } else if (grp < ngrp) {
+    step(grp, rbuf, gbuf, pfA, std::true_type{});
+  }
 
   // Partial row of this workgroup: [dB (R*M*N) | dA (R*P*Q) | dS (P*Q) | dbias (Q*N)], fp32.
   __syncthreads();
@@ -623,46 +637,50 @@ void run_fwd_bf16(const LayerArgsBf16& a, hipStream_t s) {
                      a.B, a.bias, a.y);
 }
 
-template <class D>
+template <class D, int RPI>
 void run_bwd_bf16(const LayerArgsBf16& a, int grid, hipStream_t s) {
-  using Q = BB<D>;
+  using Q = BB<D, RPI>;
   static const bool attr = [] {
-    (void)hipFuncSetAttribute((const void*)bwd_bf16_kernel<D, 0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Q::LDS);
-    (void)hipFuncSetAttribute((const void*)bwd_bf16_kernel<D, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Q::LDS);
-    (void)hipFuncSetAttribute((const void*)bwd_bf16_kernel<D, 2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Q::LDS);
+    (void)hipFuncSetAttribute((const void*)bwd_bf16_kernel<D, RPI, 0>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)Q::LDS);
+    (void)hipFuncSetAttribute((const void*)bwd_bf16_kernel<D, RPI, 1>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)Q::LDS);
+    (void)hipFuncSetAttribute((const void*)bwd_bf16_kernel<D, RPI, 2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)Q::LDS);
     return true;
   }();
   (void)attr;
   const int dxm = a.dx == nullptr ? 0 : ((a.flags & KRON_DX_RELU_MASK) ? 2 : 1);
   if (dxm == 0)
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, 0>), dim3(grid), dim3(Q::NT), Q::LDS, s, a.N, a.x, a.S, a.A, a.B,
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, RPI, 0>), dim3(grid), dim3(Q::NT), Q::LDS, s, a.N, a.x, a.S, a.A, a.B,
                        a.dy, a.dx, a.part);
   else if (dxm == 1)
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, 1>), dim3(grid), dim3(Q::NT), Q::LDS, s, a.N, a.x, a.S, a.A, a.B,
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, RPI, 1>), dim3(grid), dim3(Q::NT), Q::LDS, s, a.N, a.x, a.S, a.A, a.B,
                        a.dy, a.dx, a.part);
   else
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, 2>), dim3(grid), dim3(Q::NT), Q::LDS, s, a.N, a.x, a.S, a.A, a.B,
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, RPI, 2>), dim3(grid), dim3(Q::NT), Q::LDS, s, a.N, a.x, a.S, a.A, a.B,
                        a.dy, a.dx, a.part);
 }
 
 struct EntryBf16 {
   int p, q, m, n, r;
-  int rows_per_step;
+  int rows_per_step, groups_per_cu;
   void (*fwd)(const LayerArgsBf16&, hipStream_t);
   void (*bwd)(const LayerArgsBf16&, int, hipStream_t);
 };
 
-#define KRON_BF16_ENTRY(P, Q, M, N, R)                                                             \
-  EntryBf16{P, Q, M, N, R, BB<BD<P, Q, M, N, R>>::RPI, &run_fwd_bf16<BD<P, Q, M, N, R>>,            \
-            &run_bwd_bf16<BD<P, Q, M, N, R>>}
+// Rows per backward step and backward workgroups per compute unit, chosen per shape so
+// that the resident workgroups' rows, G tiles (LDS) and registers fill a compute unit.
+#define KRON_BF16_ENTRY(P, Q, M, N, R, RPI, WPC)                                               \
+  EntryBf16{P, Q, M, N, R, RPI, WPC, &run_fwd_bf16<BD<P, Q, M, N, R>>, &run_bwd_bf16<BD<P, Q, M, N, R>, RPI>}
 
 // The 1024x1024 layers with m = 32 (r = 1, 2, 4) and m = 64 (r = 2).
 const EntryBf16 kBf16Table[] = {
-    KRON_BF16_ENTRY(32, 32, 32, 32, 1), KRON_BF16_ENTRY(32, 32, 32, 32, 2), KRON_BF16_ENTRY(32, 32, 32, 32, 4),
-    KRON_BF16_ENTRY(16, 16, 64, 64, 2),
+    KRON_BF16_ENTRY(32, 32, 32, 32, 1, 6, 1), KRON_BF16_ENTRY(32, 32, 32, 32, 2, 4, 1),
+    KRON_BF16_ENTRY(32, 32, 32, 32, 4, 3, 1), KRON_BF16_ENTRY(16, 16, 64, 64, 2, 2, 1),
 };
-static_assert(BB<BD<32, 32, 32, 32, 4>>::OK && BB<BD<32, 32, 32, 32, 2>>::OK && BB<BD<32, 32, 32, 32, 1>>::OK &&
-                  BB<BD<16, 16, 64, 64, 2>>::OK,
+static_assert(BB<BD<32, 32, 32, 32, 4>, 3>::OK && BB<BD<32, 32, 32, 32, 2>, 4>::OK &&
+                  BB<BD<32, 32, 32, 32, 1>, 6>::OK && BB<BD<16, 16, 64, 64, 2>, 2>::OK,
               "every bf16 table shape fits its LDS budget");
 
 const EntryBf16* find_bf16(int p, int q, int m, int n, int r) {
@@ -679,7 +697,7 @@ int bf16_bwd_groups(int64_t N, int p, int q, int m, int n, int r) {
   const EntryBf16* e = find_bf16(p, q, m, n, r);
   if (!e) return 0;
   const int64_t g = (N + e->rows_per_step - 1) / e->rows_per_step;
-  const int64_t gmax = 2 * 256;   // two workgroups per compute unit (fixed: the workspace depends on it)
+  const int64_t gmax = (int64_t)e->groups_per_cu * 256;   // fixed per shape: the workspace depends on it
   return (int)(g < gmax ? g : gmax);
 }
 
