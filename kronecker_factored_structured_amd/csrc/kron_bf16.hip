@@ -249,7 +249,8 @@ __global__ __launch_bounds__((FB<D>::NT)) void fwd_bf16_kernel(int64_t N, uint32
 //   Z^T[b][j]  = sum_a B_i^T[b][a] X[j][a]      A: table          B: X row pieces      [k_row]
 //   dC[j][k]  += sum_b Z[j][b] dY[k][b]         A: Z^T tiles      B: dY row pieces     [k_acc]
 //   G^T[b][j]  = sum_k dY[k][b] C_i[j][k]       A: dY columns     B: table             [k_acc]
-//   dB[a][b]  += sum_j X[j][a] G_i[j][b]        A: X columns      B: G_i columns       [k_acc]
+//   G[j][b]    = sum_k C_i[j][k] dY[k][b]       A: table          B: dY columns        [k_acc]
+//   dB[a][b]  += sum_j X[j][a] G_i[j][b]        A: X columns      B: G tiles           [k_acc]
 // and per row, all ranks in one contraction over (i, b), split by output tile over the
 // row's R wavefronts:
 //   dX^T[a][j] = sum_(i,b) B_i[a][b] G_i[j][b]  A: table          B: G_i row pieces    [k_row]
@@ -484,7 +485,10 @@ __global__ __launch_bounds__((BB<D, RPI>::NT)) void bwd_bf16_kernel(int64_t N, c
           dC[tj][tk] = mfma(zo, yo, dC[tj][tk]);
         }
       }
-    // G^T[b][j] = sum_k dY[k][b] C_i[j][k]  ->  G_i[j][b] in LDS (bf16)
+    // G_i in both orientations from the same two operands (the dY columns and the C_i
+    // table, which are each other's transpose roles): G^T[b][j] goes to LDS as G_i[j][b] for
+    // the dX contraction of all ranks; G[j][b] stays in registers as the B operand of dB.
+    s4 gj[D::TJ][D::TB];   // bf16 G[j = 16tj + 4g + v][b = 16tb + c]
 #pragma unroll
     for (int tb = 0; tb < D::TB; ++tb) {
       OQ yc[KK];
@@ -492,10 +496,14 @@ __global__ __launch_bounds__((BB<D, RPI>::NT)) void bwd_bf16_kernel(int64_t N, c
       for (int s = 0; s < KK; ++s) yc[s] = col_op<WK>(Y, Q::LY, s, g, 16 * tb, lane);
 #pragma unroll
       for (int tj = 0; tj < D::TJ; ++tj) {
-        f4 t4v = f4{0.f, 0.f, 0.f, 0.f};
+        f4 gtv = f4{0.f, 0.f, 0.f, 0.f}, gv = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KK; ++s) t4v = mfma(yc[s], t3[tj][s], t4v);
-        *reinterpret_cast<s4*>(Gi + (16 * tj + c) * Q::LG + 16 * tb + 4 * g) = pack4(t4v);
+        for (int s = 0; s < KK; ++s) {
+          gtv = mfma(yc[s], t3[tj][s], gtv);
+          gv = mfma(t3[tj][s], yc[s], gv);
+        }
+        *reinterpret_cast<s4*>(Gi + (16 * tj + c) * Q::LG + 16 * tb + 4 * g) = pack4(gtv);
+        gj[tj][tb] = pack4(gv);
       }
     }
     // the next step's rows into the next row buffer; this register set fetches three steps ahead
@@ -526,12 +534,18 @@ __global__ __launch_bounds__((BB<D, RPI>::NT)) void bwd_bf16_kernel(int64_t N, c
         }
       }
     }
-    // dB_i[a][b] += sum_j X[j][a] G_i[j][b]
+    // dB_i[a][b] += sum_j X[j][a] G_i[j][b]; the G operand (K = j in k_acc order) is the
+    // pair of G tiles 2s, 2s + 1 (or tile s) held since the first phase
     OJ gc[D::TB][KJ];
 #pragma unroll
     for (int tb = 0; tb < D::TB; ++tb)
 #pragma unroll
-      for (int s = 0; s < KJ; ++s) gc[tb][s] = col_op<WJ>(Gi, Q::LG, s, g, 16 * tb, lane);
+      for (int s = 0; s < KJ; ++s) {
+        if constexpr (WJ == 8)
+          gc[tb][s] = join(gj[2 * s][tb], gj[2 * s + 1][tb]);
+        else
+          gc[tb][s] = join(gj[s][tb]);
+      }
 #pragma unroll
     for (int ta = 0; ta < D::TA; ++ta) {
       OJ xc[KJ];
@@ -676,11 +690,11 @@ struct EntryBf16 {
 
 // The 1024x1024 layers with m = 32 (r = 1, 2, 4) and m = 64 (r = 2).
 const EntryBf16 kBf16Table[] = {
-    KRON_BF16_ENTRY(32, 32, 32, 32, 1, 6, 1), KRON_BF16_ENTRY(32, 32, 32, 32, 2, 4, 1),
+    KRON_BF16_ENTRY(32, 32, 32, 32, 1, 4, 1), KRON_BF16_ENTRY(32, 32, 32, 32, 2, 4, 1),
     KRON_BF16_ENTRY(32, 32, 32, 32, 4, 3, 1), KRON_BF16_ENTRY(16, 16, 64, 64, 2, 2, 1),
 };
 static_assert(BB<BD<32, 32, 32, 32, 4>, 3>::OK && BB<BD<32, 32, 32, 32, 2>, 4>::OK &&
-                  BB<BD<32, 32, 32, 32, 1>, 6>::OK && BB<BD<16, 16, 64, 64, 2>, 2>::OK,
+                  BB<BD<32, 32, 32, 32, 1>, 4>::OK && BB<BD<16, 16, 64, 64, 2>, 2>::OK,
               "every bf16 table shape fits its LDS budget");
 
 const EntryBf16* find_bf16(int p, int q, int m, int n, int r) {
