@@ -1,19 +1,16 @@
 // bf16 Kronecker-factored layer on bf16 matrix instructions (mixed precision: bf16
 // operands, fp32 accumulation).  Same products as the fp32 kernels (Kronecker layer
 // tutorial, "The vec trick" and "The vec trick without the loop"; the backward by
-// calculus from them); every product is v_mfma_f32_16x16x16_bf16:
-//   lane l = 16*g + c supplies A[c][4g..4g+3] and B[4g..4g+3][c] (four consecutive K
-//   values, 8 bytes) and receives D[4g+v][c], v = 0..3.
-// A D tile therefore holds, per lane, four consecutive values of its row index -- exactly
-// the four K values the lane supplies when the next product contracts over that index --
-// so an fp32 accumulator tile, rounded to bf16 (round-to-nearest-even), is the operand of
-// the next product without leaving the registers (Z into Y^T = Z^T C in the forward; Z^T
-// into dC and G^T into dX^T in the backward).
+// calculus from them), on v_mfma_f32_16x16x32_bf16 where the contracted dimension is a
+// multiple of 32 and v_mfma_f32_16x16x16_bf16 otherwise.  Lane l = 16g + c receives
+// D[4g+v][c], v = 0..3, so an fp32 accumulator tile, rounded to bf16, supplies four
+// consecutive values of its row index: two tiles 16 rows apart are the eight K values of a
+// 16x16x32 operand when the next product contracts over that index (see k_acc below).
 //
 // Storage: x, S, A, B, bias, dy, y and dx are bf16 (bit patterns); dS, dA, dB and dbias
 // are fp32.  C_i = S o A_i is formed in fp32 (exact for bf16 factors) and rounded to
-// bf16; X B_i and G_i are rounded to bf16 before they enter their second product.
-// Dimensions p, q, m, n must be multiples of 16.
+// bf16; X B_i and G_i are rounded to bf16 (round to nearest even) before they enter their
+// second product.  Dimensions p, q, m, n must be multiples of 16.
 #include <type_traits>
 
 #include "kron_internal.h"
@@ -298,9 +295,11 @@ struct BB {
   static constexpr int WK = D::Q % 32 == 0 ? 8 : 4, KK = D::Q / (4 * WK);   // over k
   static constexpr int WJ = D::P % 32 == 0 ? 8 : 4, KJ = D::P / (4 * WJ);   // over j
   static constexpr int DXT = D::TA * D::TJ / R;                             // dX^T tiles per wavefront
-  // LDS (bf16 elements): row strides padded by 16 so that the rows a transpose read touches
-  // start on different banks; a step's rows: x [P][LX], dy [Q][LY]; its G tiles [R][P][LG]
-  static constexpr int LX = D::M + 16, LY = D::N + 16, LG = D::N + 16;
+  // LDS (bf16 elements), row strides chosen by measured bank behaviour: x rows (16-byte row
+  // reads and transpose reads) at 16 mod 32 elements, dy rows (pairs of 8-byte row reads and
+  // transpose reads) and G rows (8-byte writes, 16-byte reads) at 8 mod 16 elements.
+  // A step's rows: x [P][LX], dy [Q][LY]; its G tiles [R][P][LG].
+  static constexpr int LX = D::M + 16, LY = D::N + 24, LG = D::N + 24;
   static constexpr int XS = D::P * LX, YS = D::Q * LY, GR = D::P * LG;
   static constexpr int ROWS = RPI * (XS + YS), GBUF = RPI * R * GR;
   static constexpr int NRB = 3, NGB = 2;
