@@ -342,7 +342,7 @@ def run_ks(args, dev):
     import torch
     import kronecker_factored_structured_amd as K
     from workloads import vit_ks
-    for dtype in ("f32", "bf16"):
+    for dtype, out_dtype in (("f32", "f32"), ("bf16", "f32"), ("bf16", "bf16")):
         sets = []
         for s in range(3):   # rotate buffer sets so the working set exceeds the last-level cache
             inp = vit_ks(dtype, seed=5 + 10 * s)
@@ -352,7 +352,8 @@ def run_ks(args, dev):
             else:
                 x = torch.from_numpy(inp.x).to(dev)
                 v = torch.from_numpy(inp.vals).to(dev)
-            y = torch.empty(x.shape[0], inp.a * inp.c * inp.d, device=dev)
+            y = torch.empty(x.shape[0], inp.a * inp.c * inp.d, device=dev,
+                            dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16)
             sets.append((x, v, y))
         a, b, c, d = inp.a, inp.b, inp.c, inp.d
         it = [0]
@@ -360,20 +361,28 @@ def run_ks(args, dev):
         def call():
             x, v, y = sets[it[0] % len(sets)]
             it[0] += 1
-            K.ks_matmul(x, v, a, b, c, d, out=y)
+            if out_dtype == "f32":
+                K.ks_matmul(x, v, a, b, c, d, out=y)
+            else:
+                K.ks_matmul_out(x, v, a, b, c, d, out_dtype=torch.bfloat16, out=y)
 
         ms, _ = timed(call, args.steps, args.warmup)
         N = sets[0][0].shape[0]
         s_in = 4 if dtype == "f32" else 2
+        s_out = 4 if out_dtype == "f32" else 2
         flops = N * 2 * a * b * c * d
-        byts = N * (s_in * a * b * d + 4 * a * c * d) + s_in * a * b * c * d
-        t_roof = max(flops / (PEAK_FP32_TFLOPS * 1e12), byts / (PEAK_HBM_GBS * 1e9))
-        print(json.dumps({"workload": f"ks_matmul (a,b,c,d)=(2,48,192,4), 25216 rows, {dtype} inputs",
+        byts = N * (s_in * a * b * d + s_out * a * c * d) + s_in * a * b * c * d
+        peak = PEAK_FP32_TFLOPS if dtype == "f32" else PEAK_BF16_TFLOPS   # the contraction's input dtype
+        t_flop, t_hbm = flops / (peak * 1e12), byts / (PEAK_HBM_GBS * 1e9)
+        t_roof = max(t_flop, t_hbm)
+        print(json.dumps({"workload": f"ks_matmul (a,b,c,d)=(2,48,192,4), 25216 rows, {dtype} inputs, "
+                                      f"{out_dtype} output",
                           "us_per_call": round(ms * 1e3, 2), "rows_per_s": round(N / (ms * 1e-3), 1),
                           "achieved_gbs": round(byts / (ms * 1e-3) / 1e9, 1),
                           "effective_tflops": round(flops / (ms * 1e-3) / 1e12, 3),
                           "t_roof_us": round(t_roof * 1e6, 2), "roofline_frac": round(t_roof / (ms * 1e-3), 4),
-                          "bound": "hbm"}), flush=True)
+                          "bound": "hbm" if t_hbm >= t_flop else ("fp32" if dtype == "f32" else "bf16")}),
+              flush=True)
 
 
 def run_copy(args, dev):

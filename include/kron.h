@@ -146,6 +146,17 @@ int32_t ks_matmul(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t
                   const void* x, const void* vals, float* y, hipStream_t stream);
 
 /*
+ * ks_matmul with the output dtype chosen (the same product; "Fast Inference with
+ * Kronecker-Sparse Matrices", abstract): out_dtype KRON_F32 gives ks_matmul exactly;
+ * KRON_BF16 stores each fp32-accumulated value of y rounded once to bf16 (nearest even),
+ * y being [N, a*c*d] bf16 (2-byte elements).  Same limits, alignment and errors as
+ * ks_matmul, plus KRON_E_DTYPE for an out_dtype other than KRON_F32 / KRON_BF16.
+ */
+int32_t ks_matmul_out(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype,
+                      int32_t out_dtype, const void* x, const void* vals, void* y,
+                      hipStream_t stream);
+
+/*
  * Fused multi-tensor Adam with an l1 penalty (tutorial, "Setup": Adam update of the
  * training step; intro: l1 penalty on S).  For tensor t and element e:
  *   g  = grads[t][e] + l1[t] * sign(params[t][e])       (sign(0) = 0)

@@ -138,10 +138,7 @@ def kron_linear_bwd_bf16(x: torch.Tensor, S: Optional[torch.Tensor], A: torch.Te
     return dict(dx=dx, dS=dS, dA=dA, dB=dB, dbias=dbias)
 
 
-def ks_matmul(x: torch.Tensor, vals: torch.Tensor, a: int, b: int, c: int, d: int,
-              out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y = X K for the Kronecker-sparse K with support I_a (x) 1_{b x c} (x) I_d; vals is
-    a x d x b x c.  x and vals are float32 or bfloat16 (same dtype); y is float32."""
+def _ks_checks(x, vals, a, b, c, d):
     if x.dtype == torch.float32:
         dt = KRON_F32
     elif x.dtype == torch.bfloat16:
@@ -150,14 +147,40 @@ def ks_matmul(x: torch.Tensor, vals: torch.Tensor, a: int, b: int, c: int, d: in
         raise ValueError(f"unsupported dtype {x.dtype}")
     _dev(x, "x", x.dtype)
     _dev(vals, "vals", x.dtype)
-    _dev(out, "out")
     if x.dim() != 2 or x.shape[1] != a * b * d:
         raise ValueError(f"x must be N x {a * b * d}")
     if vals.numel() != a * b * c * d:
         raise ValueError(f"vals must hold a*b*c*d = {a * b * c * d} values")
+    return dt
+
+
+def ks_matmul(x: torch.Tensor, vals: torch.Tensor, a: int, b: int, c: int, d: int,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X K for the Kronecker-sparse K with support I_a (x) 1_{b x c} (x) I_d; vals is
+    a x d x b x c.  x and vals are float32 or bfloat16 (same dtype); y is float32."""
+    dt = _ks_checks(x, vals, a, b, c, d)
+    _dev(out, "out")
     y = out if out is not None else torch.empty(x.shape[0], a * c * d, device=x.device)
     check("ks_matmul", _lib.lib().ks_matmul(x.shape[0], a, b, c, d, dt, _ptr(x), _ptr(vals), _ptr(y),
                                             _stream(x.device)))
+    return y
+
+
+def ks_matmul_out(x: torch.Tensor, vals: torch.Tensor, a: int, b: int, c: int, d: int,
+                  out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """ks_matmul with y stored as out_dtype (float32, or bfloat16 rounded to nearest even
+    from the fp32 accumulation)."""
+    dt = _ks_checks(x, vals, a, b, c, d)
+    if out_dtype == torch.float32:
+        odt = KRON_F32
+    elif out_dtype == torch.bfloat16:
+        odt = KRON_BF16
+    else:
+        raise ValueError(f"unsupported output dtype {out_dtype}")
+    _dev(out, "out", out_dtype)
+    y = out if out is not None else torch.empty(x.shape[0], a * c * d, device=x.device, dtype=out_dtype)
+    check("ks_matmul_out", _lib.lib().ks_matmul_out(x.shape[0], a, b, c, d, dt, odt, _ptr(x), _ptr(vals),
+                                                    _ptr(y), _stream(x.device)))
     return y
 
 

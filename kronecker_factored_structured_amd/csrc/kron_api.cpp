@@ -351,29 +351,35 @@ int32_t kron_linear_bwd_bf16(const kron_shape_t* s, const void* x, const void* S
   return ok();
 }
 
-int32_t ks_matmul(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype, const void* x,
-                  const void* vals, float* y, hipStream_t stream) {
+int32_t ks_matmul_out(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype, int32_t out_dtype,
+                      const void* x, const void* vals, void* y, hipStream_t stream) {
   if (N < 0 || N > kMaxRows) return fail(KRON_E_SHAPE, "N = %lld out of range", (long long)N);
   if (a < 1 || b < 1 || c < 1 || d < 1) return fail(KRON_E_SHAPE, "a, b, c, d must be >= 1");
   const int64_t in = (int64_t)a * b * d, out = (int64_t)a * c * d;
   if (in > kMaxFeatures || out > kMaxFeatures)
     return fail(KRON_E_UNSUPPORTED, "a*b*d = %lld or a*c*d = %lld exceeds %lld", (long long)in,
                 (long long)out, (long long)kMaxFeatures);
-  if (in_dtype != KRON_F32 && in_dtype != KRON_BF16) return fail(KRON_E_DTYPE, "dtype %d", in_dtype);
+  if (in_dtype != KRON_F32 && in_dtype != KRON_BF16) return fail(KRON_E_DTYPE, "input dtype %d", in_dtype);
+  if (out_dtype != KRON_F32 && out_dtype != KRON_BF16) return fail(KRON_E_DTYPE, "output dtype %d", out_dtype);
   if (!kron::ks_supported(a, b, c, d)) return fail(KRON_E_UNSUPPORTED, "b*d = %lld too large", (long long)b * d);
   if (!vals) return fail(KRON_E_NULL, "vals is required");
   if (N > 0 && (!x || !y)) return fail(KRON_E_NULL, "x and y are required when N > 0");
-  const size_t es = in_dtype == KRON_F32 ? 4 : 2;
+  const size_t es = in_dtype == KRON_F32 ? 4 : 2, os = out_dtype == KRON_F32 ? 4 : 2;
   const Range ins[2] = {{x, (size_t)N * in * es, "x"}, {vals, (size_t)a * b * c * d * es, "vals"}};
-  const Range outs[1] = {{y, (size_t)N * out * 4, "y"}};
+  const Range outs[1] = {{y, (size_t)N * out * os, "y"}};
   int32_t st;
   if ((st = check_align(ins, 2)) != KRON_OK || (st = check_align(outs, 1)) != KRON_OK) return st;
   if ((st = check_alias(outs, 1, ins, 2)) != KRON_OK) return st;
   if (N == 0) return ok();
-  kron::KSArgs k{N, a, b, c, d, in_dtype, x, vals, y};
+  kron::KSArgs k{N, a, b, c, d, in_dtype, out_dtype, x, vals, y};
   hipError_t e = kron::launch_ks(k, stream);
   if (e != hipSuccess) return hip_fail(e, "ks_matmul launch");
   return ok();
+}
+
+int32_t ks_matmul(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype, const void* x,
+                  const void* vals, float* y, hipStream_t stream) {
+  return ks_matmul_out(N, a, b, c, d, in_dtype, KRON_F32, x, vals, y, stream);
 }
 
 int32_t kron_adam_l1_step(int32_t ntensors, float* const* params, const float* const* grads, float* const* m,

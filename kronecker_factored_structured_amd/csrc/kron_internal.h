@@ -125,10 +125,11 @@ hipError_t launch_bwd_mfma(const LayerArgs& a, int G, hipStream_t s);
 struct KSArgs {
   int64_t N;
   int32_t a, b, c, d;
-  int32_t dtype;   // KRON_F32 / KRON_BF16
+  int32_t dtype;       // of x and vals: KRON_F32 / KRON_BF16
+  int32_t out_dtype;   // of y: KRON_F32 / KRON_BF16 (rounded to nearest even)
   const void* x;
   const void* vals;
-  float* y;
+  void* y;
 };
 bool ks_supported(int a, int b, int c, int d);
 hipError_t launch_ks(const KSArgs& k, hipStream_t s);

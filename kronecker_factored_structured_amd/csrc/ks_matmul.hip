@@ -20,12 +20,14 @@ __device__ __forceinline__ float load_in(const float* p, int64_t i) { return p[i
 __device__ __forceinline__ float load_in(const uint16_t* p, int64_t i) {
   return __uint_as_float(((uint32_t)p[i]) << 16);
 }
+__device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_out(uint16_t* p, float v) { *p = __builtin_bit_cast(uint16_t, (__bf16)v); }
 
-template <typename TIn>
+template <typename TIn, typename TOut>
 __global__ __launch_bounds__(kThreads) void ks_generic_kernel(int64_t N, int a, int b, int c, int d,
                                                               int T, const TIn* __restrict__ x,
                                                               const TIn* __restrict__ vals,
-                                                              float* __restrict__ y) {
+                                                              TOut* __restrict__ y) {
   extern __shared__ float Xs[];   // T x (b*d)
   const int al = blockIdx.y;
   const int bd = b * d, cd = c * d;
@@ -44,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void ks_generic_kernel(int64_t N, int a, 
     const float* xr = Xs + t * bd + de;
     float acc = 0.f;
     for (int be = 0; be < b; ++be) acc = fmaf(xr[be * d], load_in(v, (int64_t)be * c), acc);
-    y[(row0 + t) * outw + (int64_t)al * cd + rem] = acc;
+    store_out(y + (row0 + t) * outw + (int64_t)al * cd + rem, acc);
   }
 }
 
@@ -71,13 +73,19 @@ hipError_t launch_ks(const KSArgs& k, hipStream_t s) {
   if (gx == 0) return hipSuccess;
   const size_t lds = (size_t)T * k.b * k.d * sizeof(float);
   dim3 grid((unsigned)gx, (unsigned)k.a);
-  if (k.dtype == KRON_F32) {
-    hipLaunchKernelGGL(ks_generic_kernel<float>, grid, dim3(kThreads), lds, s, k.N, k.a, k.b, k.c, k.d,
-                       T, (const float*)k.x, (const float*)k.vals, k.y);
-  } else {
-    hipLaunchKernelGGL(ks_generic_kernel<uint16_t>, grid, dim3(kThreads), lds, s, k.N, k.a, k.b, k.c,
-                       k.d, T, (const uint16_t*)k.x, (const uint16_t*)k.vals, k.y);
-  }
+  const bool fin = k.dtype == KRON_F32, fout = k.out_dtype == KRON_F32;
+  if (fin && fout)
+    hipLaunchKernelGGL((ks_generic_kernel<float, float>), grid, dim3(kThreads), lds, s, k.N, k.a, k.b, k.c, k.d, T,
+                       (const float*)k.x, (const float*)k.vals, (float*)k.y);
+  else if (fin)
+    hipLaunchKernelGGL((ks_generic_kernel<float, uint16_t>), grid, dim3(kThreads), lds, s, k.N, k.a, k.b, k.c, k.d,
+                       T, (const float*)k.x, (const float*)k.vals, (uint16_t*)k.y);
+  else if (fout)
+    hipLaunchKernelGGL((ks_generic_kernel<uint16_t, float>), grid, dim3(kThreads), lds, s, k.N, k.a, k.b, k.c, k.d,
+                       T, (const uint16_t*)k.x, (const uint16_t*)k.vals, (float*)k.y);
+  else
+    hipLaunchKernelGGL((ks_generic_kernel<uint16_t, uint16_t>), grid, dim3(kThreads), lds, s, k.N, k.a, k.b, k.c,
+                       k.d, T, (const uint16_t*)k.x, (const uint16_t*)k.vals, (uint16_t*)k.y);
   return hipGetLastError();
 }
 

@@ -28,6 +28,20 @@ namespace {
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 
+// y stores: fp32 as is, or bf16 rounded to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), b2));
+}
+__device__ __forceinline__ void store4(float* p, f4 v) { *reinterpret_cast<f4*>(p) = v; }
+__device__ __forceinline__ void store4(uint16_t* p, f4 v) {
+  *reinterpret_cast<uint2*>(p) = uint2{bf16x2(v[0], v[1]), bf16x2(v[2], v[3])};
+}
+__device__ __forceinline__ void store2(float* p, f2 v) { *reinterpret_cast<f2*>(p) = v; }
+__device__ __forceinline__ void store2(uint16_t* p, f2 v) { *reinterpret_cast<uint32_t*>(p) = bf16x2(v[0], v[1]); }
+__device__ __forceinline__ void store1(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store1(uint16_t* p, float v) { *p = __builtin_bit_cast(uint16_t, (__bf16)v); }
+
 constexpr int kThreads = 512;   // eight wavefronts
 constexpr int kWaves = kThreads / 64;
 constexpr size_t kMaxLds = 160 * 1024;
@@ -86,10 +100,10 @@ __device__ __forceinline__ void load_d(float (&dst)[DV], const uint16_t* p) {
 __device__ __forceinline__ float widen(float v) { return v; }
 __device__ __forceinline__ float widen(uint16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
 
-template <class K, class TIn>
+template <class K, class TIn, class TOut>
 __global__ __launch_bounds__(kThreads) void ks_mfma_kernel(int64_t N, int a_count, const TIn* __restrict__ x,
                                                            const TIn* __restrict__ vals,
-                                                           float* __restrict__ y) {
+                                                           TOut* __restrict__ y) {
   constexpr int b = K::Bv, c_ = K::Cv, d = K::Dv, SB = K::SB;
   extern __shared__ float tab[];
   const int groups_per_alpha = gridDim.x / a_count;
@@ -179,16 +193,16 @@ __global__ __launch_bounds__(kThreads) void ks_mfma_kernel(int64_t N, int a_coun
     for (int v = 0; v < 4; ++v) {
       const int64_t orow = rt * 16 + 4 * g + v;
       if (orow >= N) continue;
-      float* yr = y + orow * out_w + (int64_t)al * c_ * d;
+      TOut* yr = y + orow * out_w + (int64_t)al * c_ * d;
 #pragma unroll
       for (int t = 0; t < K::TPQ; ++t) {
         const int ga = 16 * (q * K::TPQ + t) + c;
         if constexpr (d == 4) {
-          *reinterpret_cast<f4*>(yr + ga * 4) = f4{acc[t][0][v], acc[t][1][v], acc[t][2][v], acc[t][3][v]};
+          store4(yr + ga * 4, f4{acc[t][0][v], acc[t][1][v], acc[t][2][v], acc[t][3][v]});
         } else if constexpr (d == 2) {
-          *reinterpret_cast<f2*>(yr + ga * 2) = f2{acc[t][0][v], acc[t][1][v]};
+          store2(yr + ga * 2, f2{acc[t][0][v], acc[t][1][v]});
         } else {
-          yr[ga] = acc[t][0][v];
+          store1(yr + ga, acc[t][0][v]);
         }
       }
     }
@@ -234,11 +248,11 @@ __device__ __forceinline__ f4 widen4(uint2 v) {
             __uint_as_float(v.y & 0xffff0000u)};
 }
 
-template <int B_, int C_, int GS_, class TIn>
+template <int B_, int C_, int GS_, class TIn, class TOut>
 __global__ __launch_bounds__((KV<B_, C_, GS_>::NT)) void ks_vreg_kernel(int64_t N, int a_count,
                                                                     const TIn* __restrict__ x,
                                                                     const TIn* __restrict__ vals,
-                                                                    float* __restrict__ y) {
+                                                                    TOut* __restrict__ y) {
   using K = KV<B_, C_, GS_>;
   extern __shared__ float lds[];   // 2 x TILE
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
@@ -249,7 +263,7 @@ __global__ __launch_bounds__((KV<B_, C_, GS_>::NT)) void ks_vreg_kernel(int64_t 
   const int64_t ntile = (N + 15) / 16, nfull = N / 16;
   const int64_t in_w = (int64_t)a_count * K::ROWF, out_w = (int64_t)a_count * C_ * 4;
   const TIn* xa = x + (int64_t)al * K::ROWF;
-  float* ya = y + ((int64_t)al * C_ + 16 * w + c) * 4;
+  TOut* ya = y + ((int64_t)al * C_ + 16 * w + c) * 4;
 
   typedef typename Raw4<TIn>::type R4;
   R4 pf[K::NPF];
@@ -305,7 +319,7 @@ __global__ __launch_bounds__((KV<B_, C_, GS_>::NT)) void ks_vreg_kernel(int64_t 
     compute(lds + (it & 1) * K::TILE, acc);
 #pragma unroll
     for (int vv = 0; vv < 4; ++vv)
-      *reinterpret_cast<f4*>(ya + (tile * 16 + 4 * g + vv) * out_w) = f4{acc[0][vv], acc[1][vv], acc[2][vv], acc[3][vv]};
+      store4(ya + (tile * 16 + 4 * g + vv) * out_w, f4{acc[0][vv], acc[1][vv], acc[2][vv], acc[3][vv]});
     stash(lds + ((it + 1) & 1) * K::TILE);
     fetch(tile + 2 * step);
     __syncthreads();
@@ -316,7 +330,7 @@ __global__ __launch_bounds__((KV<B_, C_, GS_>::NT)) void ks_vreg_kernel(int64_t 
 #pragma unroll
     for (int vv = 0; vv < 4; ++vv) {
       const int64_t row = tile * 16 + 4 * g + vv;
-      if (row < N) *reinterpret_cast<f4*>(ya + row * out_w) = f4{acc[0][vv], acc[1][vv], acc[2][vv], acc[3][vv]};
+      if (row < N) store4(ya + row * out_w, f4{acc[0][vv], acc[1][vv], acc[2][vv], acc[3][vv]});
     }
   }
 }
@@ -325,13 +339,15 @@ struct KsEntry {
   int b, c, d;
   bool ok;
   size_t lds;
-  const void* kf32;
-  const void* kbf16;
+  const void* fn[2][2];   // [x and vals bf16][y bf16]
 };
 
-#define KS_ENTRY(B, C, D)                                                                                 \
-  KsEntry{B, C, D, KS<B, C, D>::OK, KS<B, C, D>::LDS, (const void*)&ks_mfma_kernel<KS<B, C, D>, float>,   \
-          (const void*)&ks_mfma_kernel<KS<B, C, D>, uint16_t>}
+#define KS_ENTRY(B, C, D)                                                                                      \
+  KsEntry{B, C, D, KS<B, C, D>::OK, KS<B, C, D>::LDS,                                                          \
+          {{(const void*)&ks_mfma_kernel<KS<B, C, D>, float, float>,                                          \
+            (const void*)&ks_mfma_kernel<KS<B, C, D>, float, uint16_t>},                                      \
+           {(const void*)&ks_mfma_kernel<KS<B, C, D>, uint16_t, float>,                                       \
+            (const void*)&ks_mfma_kernel<KS<B, C, D>, uint16_t, uint16_t>}}}
 
 // The ViT-S/16 MLP pattern (b, c, d) = (48, 192, 4), plus
 // the Kronecker-layer factors written as KS matrices with d = 1.
@@ -356,12 +372,13 @@ struct KvEntry {
   int b, c, gs;
   size_t lds;
   int nt;
-  const void* kf32;
-  const void* kbf16;
+  const void* fn[2][2];   // [x and vals bf16][y bf16]
 };
-#define KV_ENTRY(B, C, GS)                                                                               \
-  KvEntry{B, C, GS, KV<B, C, GS>::LDS, KV<B, C, GS>::NT, (const void*)&ks_vreg_kernel<B, C, GS, float>, \
-          (const void*)&ks_vreg_kernel<B, C, GS, uint16_t>}
+#define KV_ENTRY(B, C, GS)                                                                                        \
+  KvEntry{B, C, GS, KV<B, C, GS>::LDS, KV<B, C, GS>::NT,                                                          \
+          {{(const void*)&ks_vreg_kernel<B, C, GS, float, float>, (const void*)&ks_vreg_kernel<B, C, GS, float, uint16_t>}, \
+           {(const void*)&ks_vreg_kernel<B, C, GS, uint16_t, float>,                                             \
+            (const void*)&ks_vreg_kernel<B, C, GS, uint16_t, uint16_t>}}}
 // d = 4 shapes with V in registers: the ViT-S/16 MLP pattern (b, c) = (48, 192), one
 // workgroup per row tile (splitting the gamma tiles over two or three workgroups was
 // measured no faster).
@@ -375,7 +392,7 @@ const KvEntry* kv_find(int b, int c, int d) {
 }
 
 hipError_t launch_ks_vreg(const KvEntry* e, const KSArgs& k, hipStream_t s) {
-  const void* fn = k.dtype == KRON_F32 ? e->kf32 : e->kbf16;
+  const void* fn = e->fn[k.dtype == KRON_BF16][k.out_dtype == KRON_BF16];
   (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)e->lds);
   int per_cu = 1;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, e->nt, e->lds) != hipSuccess || per_cu < 1)
@@ -403,7 +420,7 @@ hipError_t launch_ks_mfma(const KSArgs& k, hipStream_t s) {
   const KsEntry* e = ks_find(k.b, k.c, k.d);
   if (!e) return hipErrorInvalidValue;
   if (k.N == 0) return hipSuccess;
-  const void* fn = k.dtype == KRON_F32 ? e->kf32 : e->kbf16;
+  const void* fn = e->fn[k.dtype == KRON_BF16][k.out_dtype == KRON_BF16];
   (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)e->lds);
   // one workgroup per compute unit, split evenly between the alphas
   int per_alpha = device_cus_ks() / k.a;

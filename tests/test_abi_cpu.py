@@ -154,6 +154,18 @@ def test_ks_argument_errors():
     assert L.ks_matmul(0, 2, 48, 192, 4, 1, None, P(MB), None, None) == 0
 
 
+def test_ks_out_argument_errors():
+    L = _lib.lib()
+    MB = 1 << 20
+    assert L.ks_matmul_out(8, 2, 48, 192, 4, 0, 7, P(0), P(MB), P(2 * MB), None) == _lib.KRON_E_DTYPE
+    assert L.ks_matmul_out(8, 2, 48, 192, 4, 7, 1, P(0), P(MB), P(2 * MB), None) == _lib.KRON_E_DTYPE
+    assert L.ks_matmul_out(8, 2, 48, 192, 4, 1, 1, P(0), None, P(2 * MB), None) == _lib.KRON_E_NULL
+    assert L.ks_matmul_out(8, 2, 48, 192, 4, 1, 1, P(0), P(MB), P(2 * MB + 8), None) == _lib.KRON_E_ALIGN
+    # bf16 x of 8 x 384 occupies [0, 6 KiB); a bf16 y (8 x 1536, 24 KiB) from 4 KiB overlaps it
+    assert L.ks_matmul_out(8, 2, 48, 192, 4, 1, 1, P(0), P(MB), P(4096), None) == _lib.KRON_E_ALIAS
+    assert L.ks_matmul_out(0, 2, 48, 192, 4, 1, 1, None, P(MB), None, None) == 0
+
+
 def test_adam_argument_errors():
     L = _lib.lib()
     arr = ctypes.c_void_p * 1

@@ -95,3 +95,68 @@ def test_kron_layer_equals_chain_of_ks_on_gpu():
     y2 = K().ks_matmul(z, dev(V2), 1, r * p, q, n)
     y1 = K().kron_linear_fwd(dev(inp.x), dev(inp.S), dev(inp.A), dev(inp.B), None)
     assert rel_err(host(y2), host(y1)) <= TOL_F32
+
+
+def _ks_dev_inputs(inp):
+    if inp.dtype == "bf16":
+        return (dev(inp.x_bits.view(np.int16)).view(torch.bfloat16),
+                dev(inp.vals_bits.view(np.int16)).view(torch.bfloat16))
+    return dev(inp.x), dev(inp.vals)
+
+
+def _bf16_host(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bf16_output_vit_shape(dtype):
+    """ks_matmul_out with a bf16 y (ViT shape, 25,216 rows).  Against the fp64 oracle each
+    value is within a bf16 rounding (2^-9 relative for nearest even; truncation would
+    reach 2^-7) plus the fp32 accumulation error; and it is exactly the nearest-even
+    rounding of the same kernel's fp32 result (same products, same order)."""
+    from workloads import bf16_bits, bf16_to_f32
+    inp = vit_ks(dtype)
+    x, v = _ks_dev_inputs(inp)
+    print(f"[ks bf16 out] N={x.shape[0]} dtype={dtype}", flush=True)
+    y16 = K().ks_matmul_out(x, v, inp.a, inp.b, inp.c, inp.d, out_dtype=torch.bfloat16)
+    y32 = K().ks_matmul(x, v, inp.a, inp.b, inp.c, inp.d)
+    torch.cuda.synchronize()
+    assert y16.dtype == torch.bfloat16 and y16.shape == y32.shape
+    bits = _bf16_host(y16)
+    got = bf16_to_f32(bits).astype(np.float64)
+    want = OKS.matmul(inp.x, inp.vals, inp.a, inp.b, inp.c, inp.d)
+    scale = np.abs(want).max()
+    assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + TOL_F32 * scale)
+    assert rel_err(got, want) <= TOL_BF16
+    assert np.array_equal(bits, bf16_bits(y32.cpu().numpy()))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("abcd", [(2, 48, 192, 4), (1, 5, 7, 1), (1, 64, 64, 1), (3, 4, 2, 5)])
+def test_bf16_output_support_bit_exact(dtype, abcd):
+    """Identity input, bf16 y: the nearest-even bf16 of K on the support, +0 off it."""
+    from workloads import bf16_bits
+    a, b, c, d = abcd
+    inp = ks_inputs(44, a * b * d, a, b, c, d, dtype)
+    eye = np.eye(a * b * d, dtype=np.float32)
+    if dtype == "bf16":
+        inp.x_bits = bf16_bits(eye)
+    inp.x = eye
+    x, v = _ks_dev_inputs(inp)
+    y = K().ks_matmul_out(x, v, a, b, c, d, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    dense = OKS.dense(inp.vals, a, b, c, d).astype(np.float32)
+    assert np.array_equal(_bf16_host(y), bf16_bits(dense))
+
+
+@pytest.mark.parametrize("N", [0, 1, 1001])
+def test_bf16_output_ragged_rows(N):
+    inp = ks_inputs(45, N, 2, 48, 192, 4, "bf16")
+    x, v = _ks_dev_inputs(inp)
+    y = K().ks_matmul_out(x, v, 2, 48, 192, 4, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert y.shape == (N, 1536)
+    if N:
+        from workloads import bf16_to_f32
+        got = bf16_to_f32(_bf16_host(y)).astype(np.float64)
+        assert rel_err(got, OKS.matmul(inp.x, inp.vals, 2, 48, 192, 4)) <= TOL_BF16
