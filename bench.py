@@ -1,7 +1,7 @@
 """Benchmark of the Kronecker-factored layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--cpu-seconds 10]
-    python bench.py --workload {headline,headline_bf16,tiny,mlp_step,gpt2_ffn,ks}
+    python bench.py --workload {headline,headline_bf16,tiny,mlp_step,gpt2_ffn,ks,sweep}
     python bench.py --calibrate-copy      (plain device copy of known size, for HBM counters)
 
 Default workload (one JSON line): one step is one kron_linear_fwd + one kron_linear_bwd
@@ -385,6 +385,56 @@ def run_ks(args, dev):
               flush=True)
 
 
+def run_sweep(args, dev):
+    """Batch-size sweep of the 1024 x 1024 layer (the tutorial's comparison): the Kronecker
+    layer's fwd+bwd against a dense layer and a dense layer with the group-LASSO penalty
+    on its m x n blocks (tutorial, "The baselines": the sum of the blocks' Frobenius norms,
+    each norm sqrt(sum of squares + 1e-12)).  The dense sides are PyTorch matrix products
+    (rocBLAS / hipBLASLt), timed as comparators only; nothing is dispatched to them."""
+    import torch
+    from workloads import kron_inputs
+    steps = max(5, min(args.steps, 20))
+    configs = [(32, 32, 32, 32, 4), (32, 32, 32, 32, 1), (16, 16, 64, 64, 2), (128, 128, 8, 8, 1)]
+    lam = 1e-4
+    for N in (256, 1024, 4096, 20000, 65536):
+        rec = {"workload": f"sweep: 1024x1024 layer fwd+bwd, {N} rows", "N": N}
+        for (p, q, m, n, r) in configs:
+            inp = kron_inputs(70 + r, N, p, q, m, n, r, s_mode="uniform_zeroed", bias_mode="zeros")
+            L = Layer(inp, dev)
+            ms, _ = timed(lambda: (L.fwd(), L.bwd()), steps, 3)
+            rec[f"kron p{p} m{m} r{r} us"] = round(ms * 1e3, 2)
+            del L
+        g = torch.Generator(device=dev).manual_seed(N)
+        x = torch.randn(N, 1024, device=dev, generator=g)
+        dy = torch.randn(N, 1024, device=dev, generator=g)
+        W = torch.randn(1024, 1024, device=dev, generator=g) / 32.0
+        bias = torch.zeros(1024, device=dev)
+        y = torch.empty(N, 1024, device=dev)
+        dx = torch.empty_like(x)
+        dW = torch.empty_like(W)
+
+        def dense():
+            torch.addmm(bias, x, W, out=y)
+            torch.mm(dy, W.t(), out=dx)
+            torch.mm(x.t(), dy, out=dW)
+            return dy.sum(0)
+
+        def dense_lasso():
+            db = dense()
+            blocks = W.view(32, 32, 32, 32)   # in x out = (p, m) x (q, n) blocks of 32 x 32
+            norms = (blocks.pow(2).sum(dim=(1, 3)) + 1e-12).sqrt()
+            pen = lam * norms.sum()
+            dW.view(32, 32, 32, 32).add_(blocks / norms[:, None, :, None], alpha=lam)
+            return db, pen
+
+        ms_d, _ = timed(dense, steps, 3)
+        ms_l, _ = timed(dense_lasso, steps, 3)
+        rec["dense us"] = round(ms_d * 1e3, 2)
+        rec["dense+group-lasso us"] = round(ms_l * 1e3, 2)
+        rec["kron r4 m32 speedup vs dense"] = round(ms_d / (rec["kron p32 m32 r4 us"] * 1e-3), 3)
+        print(json.dumps(rec), flush=True)
+
+
 def run_copy(args, dev):
     """Plain device-to-device copy of a known size (reference for the HBM counters)."""
     import torch
@@ -407,7 +457,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="headline",
-                    choices=("headline", "headline_bf16", "tiny", "mlp_step", "gpt2_ffn", "ks"))
+                    choices=("headline", "headline_bf16", "tiny", "mlp_step", "gpt2_ffn", "ks", "sweep"))
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed running before the warmup steps, for the GPU clock to ramp up")
@@ -424,7 +474,7 @@ def main():
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         return run_copy(args, dev)
-    {"headline": run_headline, "headline_bf16": run_headline_bf16, "tiny": run_tiny, "mlp_step": run_mlp_step, "gpt2_ffn": run_gpt2,
+    {"headline": run_headline, "headline_bf16": run_headline_bf16, "tiny": run_tiny, "sweep": run_sweep, "mlp_step": run_mlp_step, "gpt2_ffn": run_gpt2,
      "ks": run_ks}[args.workload](args, dev)
 
 

@@ -19,7 +19,7 @@ namespace kron {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr size_t kGenericLds = 64 * 1024;   // bytes of LDS the generic kernels may use
+constexpr size_t kGenericLds = 160 * 1024;   // bytes of LDS the generic kernels may use (a CU's LDS)
 constexpr int kMaxTileRows = 32;
 
 __global__ __launch_bounds__(kThreads) void fwd_generic_kernel(
@@ -295,6 +295,10 @@ hipError_t launch_fwd_generic(const LayerArgs& a, hipStream_t s) {
   const int64_t grid = (a.N + T - 1) / T;
   if (grid == 0) return hipSuccess;
   const size_t lds = fwd_lds_floats(T, a.p, a.q, a.m, a.n) * sizeof(float);
+  static const bool attr =
+      hipFuncSetAttribute((const void*)fwd_generic_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)kGenericLds) == hipSuccess;
+  (void)attr;
   hipLaunchKernelGGL(fwd_generic_kernel, dim3((unsigned)grid), dim3(kThreads), lds, s, a.N, a.p, a.q,
                      a.m, a.n, a.r, T, a.flags, a.x, a.S, a.A, a.B, a.bias, a.y);
   return hipGetLastError();
@@ -306,6 +310,10 @@ hipError_t launch_bwd_generic(const LayerArgs& a, int G, hipStream_t s) {
   if (T == 0) return hipErrorInvalidValue;
   if (G == 0) return hipSuccess;
   const size_t lds = bwd_lds_floats(T, a.p, a.q, a.m, a.n, want_dx) * sizeof(float);
+  static const bool attr =
+      hipFuncSetAttribute((const void*)bwd_generic_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)kGenericLds) == hipSuccess;
+  (void)attr;
   hipLaunchKernelGGL(bwd_generic_kernel, dim3(G), dim3(kThreads), lds, s, a.N, a.p, a.q, a.m, a.n,
                      a.r, T, a.flags, a.x, a.S, a.A, a.B, a.dy, a.dx, a.part);
   return hipGetLastError();

@@ -14,7 +14,7 @@ namespace kron {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr size_t kKsLds = 64 * 1024;
+constexpr size_t kKsLds = 160 * 1024;   // a CU's LDS
 
 __device__ __forceinline__ float load_in(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float load_in(const uint16_t* p, int64_t i) {
@@ -73,6 +73,16 @@ hipError_t launch_ks(const KSArgs& k, hipStream_t s) {
   if (gx == 0) return hipSuccess;
   const size_t lds = (size_t)T * k.b * k.d * sizeof(float);
   dim3 grid((unsigned)gx, (unsigned)k.a);
+  static const bool attr = [] {
+    const void* fns[4] = {(const void*)ks_generic_kernel<float, float>, (const void*)ks_generic_kernel<float, uint16_t>,
+                          (const void*)ks_generic_kernel<uint16_t, float>,
+                          (const void*)ks_generic_kernel<uint16_t, uint16_t>};
+    bool ok = true;
+    for (const void* f : fns)
+      ok = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kKsLds) == hipSuccess && ok;
+    return ok;
+  }();
+  (void)attr;
   const bool fin = k.dtype == KRON_F32, fout = k.out_dtype == KRON_F32;
   if (fin && fout)
     hipLaunchKernelGGL((ks_generic_kernel<float, float>), grid, dim3(kThreads), lds, s, k.N, k.a, k.b, k.c, k.d, T,

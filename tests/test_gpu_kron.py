@@ -93,6 +93,14 @@ def test_odd_shapes_with_bias_and_S(case):
     compare_layer(kron_inputs(32, 203, p, q, m, n, r, s_mode="uniform_zeroed", bias_mode="normal"))
 
 
+@pytest.mark.parametrize("case", [(128, 128, 8, 8, 1), (64, 64, 16, 16, 2)])
+def test_tutorial_small_block_layers(case):
+    """The tutorial's 1024 x 1024 layer with 8 x 8 and 16 x 16 blocks (generic kernels,
+    S and C_i staged in up to 148 KB of LDS)."""
+    p, q, m, n, r = case
+    compare_layer(kron_inputs(34, 37, p, q, m, n, r, s_mode="uniform_zeroed", bias_mode="normal"))
+
+
 def test_without_S_and_without_dx():
     compare_layer(kron_inputs(33, 500, 32, 32, 32, 32, 4, s_mode="none", bias_mode="normal"), want_dx=False)
 
