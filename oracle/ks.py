@@ -37,3 +37,19 @@ def dense(vals, a: int, b: int, c: int, d: int) -> np.ndarray:
 def matmul(x, vals, a: int, b: int, c: int, d: int) -> np.ndarray:
     """Y = X K with K the dense KS matrix."""
     return as64(x) @ dense(vals, a, b, c, d)
+
+
+def backward(x, vals, dy, a: int, b: int, c: int, d: int) -> dict:
+    """Gradients of the scalar <dY, X K> (by calculus from Y = X K with K the dense KS
+    matrix): dX = dY K^T, and dK = X^T dY, of which only the support entries are free
+    parameters; they are gathered back into the vals[alpha][delta][beta][gamma] layout."""
+    K = dense(vals, a, b, c, d)
+    dx = as64(dy) @ K.T
+    dK = as64(x).T @ as64(dy)
+    dv = np.empty((a, d, b, c))
+    for al in range(a):
+        for de in range(d):
+            rows = (al * b + np.arange(b)) * d + de
+            cols = (al * c + np.arange(c)) * d + de
+            dv[al, de] = dK[np.ix_(rows, cols)]
+    return {"dx": dx, "dvals": dv}

@@ -266,6 +266,44 @@ def test_ks_d_interleave_matches_permutation_form():
     assert np.array_equal(OKS.dense(v, 1, b, c, d), np.kron(M, np.eye(d)))
 
 
+@pytest.mark.parametrize("abcd", [(2, 3, 4, 2), (1, 5, 2, 1), (3, 1, 2, 3)])
+def test_ks_backward_exact_finite_differences(abcd):
+    """L(x, vals) = <dY, X K> is linear in x and in vals, so the central difference with
+    h = 1 is exact: on integer inputs every entry of dX and dvals equals its difference
+    quotient bit for bit."""
+    a, b, c, d = abcd
+    rng = np.random.default_rng(7)
+    N = 3
+    x = rng.integers(-3, 4, (N, a * b * d)).astype(float)
+    v = rng.integers(-3, 4, (a, d, b, c)).astype(float)
+    dy = rng.integers(-3, 4, (N, a * c * d)).astype(float)
+    L = lambda xx, vv: float(np.sum(dy * OKS.matmul(xx, vv, a, b, c, d)))
+    g = OKS.backward(x, v, dy, a, b, c, d)
+    for idx in np.ndindex(*x.shape):
+        e = np.zeros_like(x); e[idx] = 1.0
+        assert (L(x + e, v) - L(x - e, v)) / 2 == g["dx"][idx]
+    for idx in np.ndindex(*v.shape):
+        e = np.zeros_like(v); e[idx] = 1.0
+        assert (L(x, v + e) - L(x, v - e)) / 2 == g["dvals"][idx]
+
+
+def test_ks_backward_transpose_pattern_and_adjoint():
+    """dX is the forward product with the transposed pattern I_a (x) 1_{c x b} (x) I_d and
+    values vals[alpha][delta][gamma][beta] (K^T of a KS matrix is KS); and the adjoint
+    identities <dX, X> = <dvals, vals> = <dY, X K> hold (the form is bilinear)."""
+    a, b, c, d = 2, 5, 3, 4
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((6, a * b * d))
+    v = rng.standard_normal((a, d, b, c))
+    dy = rng.standard_normal((6, a * c * d))
+    g = OKS.backward(x, v, dy, a, b, c, d)
+    np.testing.assert_allclose(g["dx"], OKS.matmul(dy, v.transpose(0, 1, 3, 2), a, c, b, d), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(OKS.dense(v.transpose(0, 1, 3, 2), a, c, b, d), OKS.dense(v, a, b, c, d).T)
+    form = np.sum(dy * OKS.matmul(x, v, a, b, c, d))
+    assert np.isclose(np.sum(g["dx"] * x), form, rtol=1e-12)
+    assert np.isclose(np.sum(g["dvals"] * v), form, rtol=1e-12)
+
+
 @pytest.mark.parametrize("case", [(3, 2, 2, 3, 2), (2, 3, 3, 2, 1), (4, 4, 2, 2, 3)])
 def test_kron_layer_equals_chain_of_two_ks_factors(case):
     """The layer factors as (I_p (x) B_all) followed by a KS factor carrying the C_i:
