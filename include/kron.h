@@ -157,6 +157,28 @@ int32_t ks_matmul_out(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int
                       hipStream_t stream);
 
 /*
+ * Backward of ks_matmul (by calculus from Y = X K with the KS matrix K of "Fast Inference
+ * with Kronecker-Sparse Matrices", abstract):
+ *   dx    [N, a*b*d]     fp32:  dx = dy K^T, itself a KS product with the pattern
+ *                               (a, c, b, d) and each (alpha, delta) block transposed
+ *   dvals [a, d, b, c]   fp32:  dvals[al][de][be][ga] =
+ *                               sum_n x[n, (al*b + be)*d + de] * dy[n, (al*c + ga)*d + de]
+ * x, vals and dy are in in_dtype (KRON_F32 or KRON_BF16); accumulation is fp32.  dx or
+ * dvals may be NULL (not computed); with N = 0, dvals is written as zeros.  Outputs are
+ * overwritten.  dvals is summed over rows in a fixed order (bitwise repeatable).
+ * workspace: device memory of ks_matmul_bwd_workspace_bytes(...) bytes, 256-byte aligned,
+ * owned by the caller; its contents need no initialisation.  Limits: those of ks_matmul for
+ * both (a,b,c,d) and (a,c,b,d), and a*b*c*d <= 2^28.  Errors: KRON_E_SHAPE, KRON_E_DTYPE,
+ * KRON_E_UNSUPPORTED, KRON_E_NULL, KRON_E_ALIGN, KRON_E_ALIAS, KRON_E_WORKSPACE,
+ * KRON_E_HIP.  ks_matmul_bwd_workspace_bytes returns 0 for arguments ks_matmul_bwd rejects.
+ */
+size_t ks_matmul_bwd_workspace_bytes(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d,
+                                     int32_t in_dtype);
+int32_t ks_matmul_bwd(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype,
+                      const void* x, const void* vals, const void* dy, float* dx, float* dvals,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Fused multi-tensor Adam with an l1 penalty (tutorial, "Setup": Adam update of the
  * training step; intro: l1 penalty on S).  For tensor t and element e:
  *   g  = grads[t][e] + l1[t] * sign(params[t][e])       (sign(0) = 0)

@@ -184,6 +184,34 @@ def ks_matmul_out(x: torch.Tensor, vals: torch.Tensor, a: int, b: int, c: int, d
     return y
 
 
+def ks_matmul_bwd_workspace_bytes(N: int, a: int, b: int, c: int, d: int, dtype: torch.dtype = torch.float32) -> int:
+    dt = KRON_F32 if dtype == torch.float32 else KRON_BF16
+    return int(_lib.lib().ks_matmul_bwd_workspace_bytes(N, a, b, c, d, dt))
+
+
+def ks_matmul_bwd(x: torch.Tensor, vals: torch.Tensor, dy: torch.Tensor, a: int, b: int, c: int, d: int,
+                  want_dx: bool = True, want_dvals: bool = True, workspace: Optional[torch.Tensor] = None,
+                  outs: Optional[dict] = None) -> dict:
+    """Gradients of ks_matmul: dx = dy K^T and dvals (fp32), from x, vals, dy of one dtype."""
+    dt = _ks_checks(x, vals, a, b, c, d)
+    _dev(dy, "dy", x.dtype)
+    if dy.dim() != 2 or dy.shape != (x.shape[0], a * c * d):
+        raise ValueError(f"dy must be N x {a * c * d}")
+    o = dict(outs or {})
+    dev = x.device
+    dx = o.get("dx") if "dx" in o else (torch.empty(x.shape, device=dev) if want_dx else None)
+    dv = o.get("dvals") if "dvals" in o else (torch.empty(a, d, b, c, device=dev) if want_dvals else None)
+    _dev(dx, "dx")
+    _dev(dv, "dvals")
+    need = ks_matmul_bwd_workspace_bytes(x.shape[0], a, b, c, d, x.dtype)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    check("ks_matmul_bwd", _lib.lib().ks_matmul_bwd(
+        x.shape[0], a, b, c, d, dt, _ptr(x), _ptr(vals), _ptr(dy), _ptr(dx), _ptr(dv), _ptr(workspace),
+        ctypes.c_size_t(workspace.numel()), _stream(dev)))
+    return dict(dx=dx, dvals=dv)
+
+
 def kron_adam_l1_step(params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
                       m: Sequence[torch.Tensor], v: Sequence[torch.Tensor], step: int, lr: float,
                       beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,

@@ -32,6 +32,7 @@ OBJECTS = [
     ("kron_bf16.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"], "kron_bf16"),
     ("ks_matmul.hip", [], "ks_matmul"),
     ("ks_mfma.hip", [], "ks_mfma"),
+    ("ks_bwd.hip", [], "ks_bwd"),
     ("adam_l1.hip", [], "adam_l1"),
     ("head_ce.hip", [], "head_ce"),
 ]

@@ -382,6 +382,59 @@ int32_t ks_matmul(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t
   return ks_matmul_out(N, a, b, c, d, in_dtype, KRON_F32, x, vals, y, stream);
 }
 
+namespace {
+constexpr int64_t kMaxKsValues = int64_t{1} << 28;   // dvals columns of the reduction (int32)
+
+int32_t ks_shape_check(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype) {
+  if (N < 0 || N > kMaxRows) return fail(KRON_E_SHAPE, "N = %lld out of range", (long long)N);
+  if (a < 1 || b < 1 || c < 1 || d < 1) return fail(KRON_E_SHAPE, "a, b, c, d must be >= 1");
+  const int64_t in = (int64_t)a * b * d, out = (int64_t)a * c * d;
+  if (in > kMaxFeatures || out > kMaxFeatures)
+    return fail(KRON_E_UNSUPPORTED, "a*b*d = %lld or a*c*d = %lld exceeds %lld", (long long)in,
+                (long long)out, (long long)kMaxFeatures);
+  if ((int64_t)a * b * c * d > kMaxKsValues)
+    return fail(KRON_E_UNSUPPORTED, "a*b*c*d = %lld values exceed %lld", (long long)a * b * c * d,
+                (long long)kMaxKsValues);
+  if (in_dtype != KRON_F32 && in_dtype != KRON_BF16) return fail(KRON_E_DTYPE, "input dtype %d", in_dtype);
+  if (!kron::ks_supported(a, b, c, d) || !kron::ks_bwd_supported(a, b, c, d))
+    return fail(KRON_E_UNSUPPORTED, "b*d = %lld or c*d = %lld too large", (long long)b * d, (long long)c * d);
+  return KRON_OK;
+}
+}  // namespace
+
+size_t ks_matmul_bwd_workspace_bytes(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype) {
+  if (ks_shape_check(N, a, b, c, d, in_dtype) != KRON_OK) return 0;
+  return kron::ks_bwd_workspace_bytes(N, a, b, c, d, in_dtype);
+}
+
+int32_t ks_matmul_bwd(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype, const void* x,
+                      const void* vals, const void* dy, float* dx, float* dvals, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  int32_t st = ks_shape_check(N, a, b, c, d, in_dtype);
+  if (st != KRON_OK) return st;
+  if (!dx && !dvals) return ok();
+  if (dx && !vals) return fail(KRON_E_NULL, "vals is required for dx");
+  if (N > 0 && !dy) return fail(KRON_E_NULL, "dy is required when N > 0");
+  if (N > 0 && dvals && !x) return fail(KRON_E_NULL, "x is required for dvals when N > 0");
+  const size_t need = kron::ks_bwd_workspace_bytes(N, a, b, c, d, in_dtype);
+  if (!workspace || workspace_bytes < need)
+    return fail(KRON_E_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if (((uintptr_t)workspace & 255u) != 0) return fail(KRON_E_ALIGN, "workspace is not 256-byte aligned");
+  const size_t es = in_dtype == KRON_F32 ? 4 : 2;
+  const int64_t in = (int64_t)a * b * d, out = (int64_t)a * c * d, nv = (int64_t)a * b * c * d;
+  const Range ins[4] = {{x, (size_t)N * in * es, "x"},
+                        {vals, (size_t)nv * es, "vals"},
+                        {dy, (size_t)N * out * es, "dy"},
+                        {workspace, need, "workspace"}};
+  const Range outs[2] = {{dx, (size_t)N * in * 4, "dx"}, {dvals, (size_t)nv * 4, "dvals"}};
+  if ((st = check_align(ins, 4)) != KRON_OK || (st = check_align(outs, 2)) != KRON_OK) return st;
+  if ((st = check_alias(outs, 2, ins, 4)) != KRON_OK) return st;
+  kron::KSBwdArgs k{N, a, b, c, d, in_dtype, x, vals, dy, N > 0 ? dx : nullptr, dvals};
+  hipError_t e = kron::launch_ks_bwd(k, workspace, stream);
+  if (e != hipSuccess) return hip_fail(e, "ks_matmul_bwd launch");
+  return ok();
+}
+
 int32_t kron_adam_l1_step(int32_t ntensors, float* const* params, const float* const* grads, float* const* m,
                           float* const* v, const int64_t* numel, const float* l1, int64_t step, double lr,
                           double beta1, double beta2, double eps, hipStream_t stream) {

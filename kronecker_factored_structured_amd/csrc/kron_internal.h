@@ -136,6 +136,20 @@ hipError_t launch_ks(const KSArgs& k, hipStream_t s);
 // Matrix-core path for the (b, c, d) in its table (see ks_mfma.hip).
 bool ks_mfma_supported(int a, int b, int c, int d);
 hipError_t launch_ks_mfma(const KSArgs& k, hipStream_t s);
+// Backward of the KS matmul (ks_bwd.hip): dx = dy K^T (NULL: skipped), dvals (NULL: skipped).
+struct KSBwdArgs {
+  int64_t N;
+  int32_t a, b, c, d;
+  int32_t dtype;   // of x, vals and dy
+  const void* x;
+  const void* vals;
+  const void* dy;
+  float* dx;
+  float* dvals;
+};
+bool ks_bwd_supported(int a, int b, int c, int d);
+size_t ks_bwd_workspace_bytes(int64_t N, int a, int b, int c, int d, int dtype);
+hipError_t launch_ks_bwd(const KSBwdArgs& k, void* workspace, hipStream_t s);
 
 // ---------------------------------------------------------------------------------
 // Adam + l1.

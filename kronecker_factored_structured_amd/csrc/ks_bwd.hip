@@ -1,0 +1,179 @@
+// Backward of the Kronecker-sparse matmul Y = X K, K with support I_a (x) 1_{b x c} (x) I_d
+// ("Fast Inference with Kronecker-Sparse Matrices", abstract), by calculus from the forward:
+//   dX = dY K^T.  K^T is again Kronecker-sparse, with the pattern (a, c, b, d) and the
+//        values of each (alpha, delta) block transposed, so dX is the forward product on dY
+//        with those values (transposed once per call into the workspace).
+//   dvals[al][de][be][ga] = sum_n X[n, (al*b + be)*d + de] * dY[n, (al*c + ga)*d + de],
+//        a reduction over the rows: each workgroup sums its chunk of rows for one
+//        (alpha, delta) block (and one beta x gamma block of it) into a partial row, and the
+//        fixed-order column reduction adds the partial rows (deterministic, no atomics).
+#include "kron_internal.h"
+
+namespace kron {
+namespace {
+
+constexpr int kDvThreads = 256;
+constexpr int kDvOpt = 48;        // beta values per thread
+constexpr int kDvMaxRows = 32;    // rows per LDS tile
+constexpr size_t kDvLds = 160 * 1024;
+constexpr int kDvTargetGroups = 256;
+
+__device__ __forceinline__ float load_in(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_in(const uint16_t* p, int64_t i) {
+  return __uint_as_float(((uint32_t)p[i]) << 16);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void ks_vals_transpose_kernel(int64_t total, int b, int c, const T* __restrict__ v,
+                                                                T* __restrict__ vt) {
+  // vt[blk][ga][be] = v[blk][be][ga], blk = al*d + de
+  const int64_t bc = (int64_t)b * c;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int64_t blk = e / bc, r = e - blk * bc;
+    const int64_t ga = r / b, be = r - ga * b;
+    vt[e] = v[blk * bc + be * c + ga];
+  }
+}
+
+// Work split of the dvals reduction.  Threads: CW gamma columns x G beta groups; thread
+// (gi, gl) owns gamma g0 + gl and the betas b0 + gi + G*j, j < kDvOpt.
+struct DvPlan {
+  int CW, G, BH, ngb, nbb, T;
+  int64_t Gr;   // row chunks = partial rows
+};
+
+DvPlan dv_plan(int64_t N, int a, int b, int c, int d) {
+  DvPlan p{};
+  p.CW = c < kDvThreads ? c : kDvThreads;
+  p.G = kDvThreads / p.CW;
+  p.BH = p.G * kDvOpt;
+  p.ngb = (c + p.CW - 1) / p.CW;
+  p.nbb = (b + p.BH - 1) / p.BH;
+  const int64_t bhm = b < p.BH ? b : p.BH, gwm = p.CW;
+  int64_t T = (int64_t)(kDvLds / ((bhm + gwm) * sizeof(float)));
+  p.T = (int)(T > kDvMaxRows ? kDvMaxRows : (T < 1 ? 1 : T));
+  const int64_t blocks = (int64_t)a * d * p.ngb * p.nbb;
+  int64_t gr = (kDvTargetGroups + blocks - 1) / blocks;
+  const int64_t tiles = (N + p.T - 1) / p.T;
+  if (gr > tiles) gr = tiles;
+  p.Gr = gr < 1 ? 1 : gr;
+  return p;
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(kDvThreads) void ks_dv_kernel(int64_t N, int a, int b, int c, int d, DvPlan P,
+                                                           const TIn* __restrict__ x, const TIn* __restrict__ dy,
+                                                           float* __restrict__ part) {
+  extern __shared__ float s[];
+  const int n_oc = P.ngb * P.nbb;
+  const int oc = blockIdx.x % n_oc;
+  const int ad = (blockIdx.x / n_oc) % (a * d);
+  const int64_t chunk = blockIdx.x / ((int64_t)n_oc * a * d);
+  const int gb = oc % P.ngb, bb = oc / P.ngb;
+  const int al = ad / d, de = ad % d;
+  const int g0 = gb * P.CW, gw = c - g0 < P.CW ? c - g0 : P.CW;   // gamma block
+  const int b0 = bb * P.BH, bh = b - b0 < P.BH ? b - b0 : P.BH;   // beta block
+  float* Xs = s;                // T x bh
+  float* Ys = s + P.T * bh;     // T x gw
+  const int tid = threadIdx.x, gi = tid / P.CW, gl = tid % P.CW;
+  const bool active = gi < P.G && gl < gw;
+  float acc[kDvOpt];
+#pragma unroll
+  for (int j = 0; j < kDvOpt; ++j) acc[j] = 0.f;
+  const int64_t in_w = (int64_t)a * b * d, out_w = (int64_t)a * c * d;
+  const int64_t per = (N + P.Gr - 1) / P.Gr, r0 = chunk * per;
+  const int64_t r1 = r0 + per < N ? r0 + per : N;
+  for (int64_t t0 = r0; t0 < r1; t0 += P.T) {
+    const int rows = (int)(r1 - t0 < P.T ? r1 - t0 : P.T);
+    __syncthreads();
+    for (int i = tid; i < rows * bh; i += kDvThreads) {
+      const int t = i / bh, be = i - t * bh;
+      Xs[i] = load_in(x, (t0 + t) * in_w + ((int64_t)al * b + b0 + be) * d + de);
+    }
+    for (int i = tid; i < rows * gw; i += kDvThreads) {
+      const int t = i / gw, ga = i - t * gw;
+      Ys[i] = load_in(dy, (t0 + t) * out_w + ((int64_t)al * c + g0 + ga) * d + de);
+    }
+    __syncthreads();
+    if (active) {
+      for (int t = 0; t < rows; ++t) {
+        const float yv = Ys[t * gw + gl];
+        const float* xr = Xs + t * bh + gi;
+#pragma unroll
+        for (int j = 0; j < kDvOpt; ++j)
+          if (gi + P.G * j < bh) acc[j] = fmaf(xr[P.G * j], yv, acc[j]);
+      }
+    }
+  }
+  if (active) {
+    const PartRow out{part, P.Gr, chunk, (int64_t)ad * b * c};
+#pragma unroll
+    for (int j = 0; j < kDvOpt; ++j) {
+      const int be = gi + P.G * j;
+      if (be < bh) out[(int64_t)(b0 + be) * c + g0 + gl] = acc[j];
+    }
+  }
+}
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+}  // namespace
+
+bool ks_bwd_supported(int a, int b, int c, int d) { return ks_supported(a, c, b, d); }
+
+size_t ks_bwd_workspace_bytes(int64_t N, int a, int b, int c, int d, int dtype) {
+  const size_t es = dtype == KRON_F32 ? 4 : 2;
+  const DvPlan P = dv_plan(N, a, b, c, d);
+  return align256((size_t)a * b * c * d * es) + align256((size_t)part_floats(P.Gr, (int64_t)a * b * c * d) * 4);
+}
+
+hipError_t launch_ks_bwd(const KSBwdArgs& k, void* ws, hipStream_t s) {
+  const size_t es = k.dtype == KRON_F32 ? 4 : 2;
+  const int64_t total = (int64_t)k.a * k.b * k.c * k.d;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  void* vt = w;
+  float* part = reinterpret_cast<float*>(w + align256((size_t)total * es));
+  if (k.dx && k.N > 0) {
+    const int64_t blocks64 = (total + 255) / 256;
+    const unsigned blocks = (unsigned)(blocks64 < 4096 ? blocks64 : 4096);
+    if (k.dtype == KRON_F32)
+      hipLaunchKernelGGL(ks_vals_transpose_kernel<float>, dim3(blocks), dim3(256), 0, s, total, k.b, k.c,
+                         (const float*)k.vals, (float*)vt);
+    else
+      hipLaunchKernelGGL(ks_vals_transpose_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, total, k.b, k.c,
+                         (const uint16_t*)k.vals, (uint16_t*)vt);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const KSArgs f{k.N, k.a, k.c, k.b, k.d, k.dtype, KRON_F32, k.dy, vt, k.dx};
+    if ((e = launch_ks(f, s)) != hipSuccess) return e;
+  }
+  if (k.dvals) {
+    const DvPlan P = dv_plan(k.N, k.a, k.b, k.c, k.d);
+    const int bhm = k.b < P.BH ? k.b : P.BH;
+    const size_t lds = (size_t)P.T * (bhm + P.CW) * sizeof(float);
+    const int64_t grid = P.Gr * k.a * k.d * P.ngb * P.nbb;
+    static const bool attr = [] {
+      const bool a1 = hipFuncSetAttribute((const void*)ks_dv_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                          (int)kDvLds) == hipSuccess;
+      const bool a2 = hipFuncSetAttribute((const void*)ks_dv_kernel<uint16_t>,
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDvLds) == hipSuccess;
+      return a1 && a2;
+    }();
+    (void)attr;
+    if (k.dtype == KRON_F32)
+      hipLaunchKernelGGL(ks_dv_kernel<float>, dim3((unsigned)grid), dim3(kDvThreads), lds, s, k.N, k.a, k.b, k.c,
+                         k.d, P, (const float*)k.x, (const float*)k.dy, part);
+    else
+      hipLaunchKernelGGL(ks_dv_kernel<uint16_t>, dim3((unsigned)grid), dim3(kDvThreads), lds, s, k.N, k.a, k.b,
+                         k.c, k.d, P, (const uint16_t*)k.x, (const uint16_t*)k.dy, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    RedPlan plan{};
+    plan.seg[0] = RedSeg{k.dvals, (int32_t)total, 1.f, 0};
+    plan.nseg = 1;
+    if ((e = launch_column_reduce(part, (int32_t)P.Gr, (int32_t)total, plan, s)) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace kron

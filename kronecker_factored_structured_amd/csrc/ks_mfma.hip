@@ -349,10 +349,11 @@ struct KsEntry {
            {(const void*)&ks_mfma_kernel<KS<B, C, D>, uint16_t, float>,                                       \
             (const void*)&ks_mfma_kernel<KS<B, C, D>, uint16_t, uint16_t>}}}
 
-// The ViT-S/16 MLP pattern (b, c, d) = (48, 192, 4), plus
-// the Kronecker-layer factors written as KS matrices with d = 1.
+// The ViT-S/16 MLP pattern (b, c, d) = (48, 192, 4) and its transpose (192, 48, 4) (the
+// input gradient of the first), plus the Kronecker-layer factors written as KS matrices
+// with d = 1.
 const KsEntry kKsTable[] = {
-    KS_ENTRY(48, 192, 4), KS_ENTRY(32, 128, 1), KS_ENTRY(128, 32, 1), KS_ENTRY(64, 64, 1),
+    KS_ENTRY(48, 192, 4), KS_ENTRY(192, 48, 4), KS_ENTRY(32, 128, 1), KS_ENTRY(128, 32, 1), KS_ENTRY(64, 64, 1),
 };
 
 const KsEntry* ks_find(int b, int c, int d) {

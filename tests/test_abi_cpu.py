@@ -171,6 +171,29 @@ def test_ks_out_argument_errors():
     assert L.ks_matmul_out(0, 2, 48, 192, 4, 1, 1, None, P(MB), None, None) == 0
 
 
+def test_ks_bwd_argument_errors():
+    L = _lib.lib()
+    MB = 1 << 20
+    need = L.ks_matmul_bwd_workspace_bytes(8, 2, 48, 192, 4, 0)
+    assert need > 0
+    assert L.ks_matmul_bwd_workspace_bytes(8, 2, 48, 192, 4, 7) == 0
+    assert L.ks_matmul_bwd_workspace_bytes(-1, 2, 48, 192, 4, 0) == 0
+    args = lambda **kw: [kw.get("x", P(0)), kw.get("vals", P(MB)), kw.get("dy", P(2 * MB)), kw.get("dx", P(3 * MB)),
+                         kw.get("dv", P(4 * MB)), kw.get("ws", P(8 * MB)), ctypes.c_size_t(kw.get("bytes", need)), None]
+    assert L.ks_matmul_bwd(8, 2, 48, 192, 4, 7, *args()) == _lib.KRON_E_DTYPE
+    assert L.ks_matmul_bwd(-1, 2, 48, 192, 4, 0, *args()) == _lib.KRON_E_SHAPE
+    assert L.ks_matmul_bwd(8, 2, 48, 192, 4, 0, *args(vals=None)) == _lib.KRON_E_NULL
+    assert L.ks_matmul_bwd(8, 2, 48, 192, 4, 0, *args(dy=None)) == _lib.KRON_E_NULL
+    assert L.ks_matmul_bwd(8, 2, 48, 192, 4, 0, *args(x=None)) == _lib.KRON_E_NULL
+    assert L.ks_matmul_bwd(8, 2, 48, 192, 4, 0, *args(bytes=need - 1)) == _lib.KRON_E_WORKSPACE
+    assert L.ks_matmul_bwd(8, 2, 48, 192, 4, 0, *args(ws=P(8 * MB + 16))) == _lib.KRON_E_ALIGN
+    assert L.ks_matmul_bwd(8, 2, 48, 192, 4, 0, *args(dx=P(3 * MB + 4))) == _lib.KRON_E_ALIGN
+    assert L.ks_matmul_bwd(8, 2, 48, 192, 4, 0, *args(dv=P(2 * MB))) == _lib.KRON_E_ALIAS   # dvals over dy
+    assert L.ks_matmul_bwd(8, 2, 48, 192, 4, 0, *args(dx=P(8 * MB))) == _lib.KRON_E_ALIAS   # dx over workspace
+    assert L.ks_matmul_bwd(8, 2, 48, 192, 4, 0, *args(dx=None, dv=None)) == 0              # nothing asked
+    assert L.ks_matmul_bwd(8, 1, 65536, 65536, 1, 0, *args()) == _lib.KRON_E_UNSUPPORTED    # a*b*c*d > 2^28
+
+
 def test_adam_argument_errors():
     L = _lib.lib()
     arr = ctypes.c_void_p * 1

@@ -160,3 +160,60 @@ def test_bf16_output_ragged_rows(N):
         from workloads import bf16_to_f32
         got = bf16_to_f32(_bf16_host(y)).astype(np.float64)
         assert rel_err(got, OKS.matmul(inp.x, inp.vals, 2, 48, 192, 4)) <= TOL_BF16
+
+
+def _ks_bwd_case(inp, dy64, want_dx=True, want_dvals=True):
+    x, v = _ks_dev_inputs(inp)
+    if inp.dtype == "bf16":
+        from workloads import bf16_bits, bf16_to_f32
+        bits = bf16_bits(dy64.astype(np.float32))
+        dy_host = bf16_to_f32(bits).reshape(dy64.shape)
+        dy = dev(bits.view(np.int16)).view(torch.bfloat16)
+    else:
+        dy_host = dy64.astype(np.float32)
+        dy = dev(dy_host)
+    g = K().ks_matmul_bwd(x, v, dy, inp.a, inp.b, inp.c, inp.d, want_dx=want_dx, want_dvals=want_dvals)
+    torch.cuda.synchronize()
+    want = OKS.backward(inp.x, inp.vals, dy_host, inp.a, inp.b, inp.c, inp.d)
+    return g, want
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ks_backward_vit_shape_full_size(dtype):
+    """dx = dy K^T and dvals at (a,b,c,d) = (2,48,192,4), 25,216 rows, against the oracle
+    on the same (bf16-rounded) inputs; both sides see identical values, so fp32
+    accumulation is the only error."""
+    inp = vit_ks(dtype)
+    dy64 = np.random.default_rng(50).standard_normal((inp.x.shape[0], inp.a * inp.c * inp.d))
+    print(f"[ks bwd] N={inp.x.shape[0]} dtype={dtype}", flush=True)
+    g, want = _ks_bwd_case(inp, dy64)
+    ex, ev = rel_err(host(g["dx"]), want["dx"]), rel_err(host(g["dvals"]), want["dvals"])
+    print(f"   rel errors dx {ex:.2e} dvals {ev:.2e}", flush=True)
+    assert ex <= TOL_F32 and ev <= TOL_F32
+
+
+@pytest.mark.parametrize("N", [0, 1, 37, 300])
+@pytest.mark.parametrize("abcd", [(1, 5, 7, 1), (3, 4, 2, 5), (2, 3, 130, 2), (4, 1, 1, 3), (1, 64, 64, 1),
+                                  (2, 300, 3, 1)])
+def test_ks_backward_shapes_and_ragged_rows(abcd, N):
+    a, b, c, d = abcd
+    inp = ks_inputs(46, N, a, b, c, d, "f32")
+    dy64 = np.random.default_rng(51).standard_normal((N, a * c * d))
+    g, want = _ks_bwd_case(inp, dy64)
+    assert g["dx"].shape == (N, a * b * d) and g["dvals"].shape == (a, d, b, c)
+    if N:
+        assert rel_err(host(g["dx"]), want["dx"]) <= TOL_F32
+        assert rel_err(host(g["dvals"]), want["dvals"]) <= TOL_F32
+    else:
+        assert np.all(host(g["dvals"]) == 0)
+
+
+def test_ks_backward_single_outputs_and_determinism():
+    inp = ks_inputs(47, 1000, 2, 48, 192, 4, "f32")
+    dy64 = np.random.default_rng(52).standard_normal((1000, 1536))
+    g1, want = _ks_bwd_case(inp, dy64, want_dx=False)
+    assert g1["dx"] is None and rel_err(host(g1["dvals"]), want["dvals"]) <= TOL_F32
+    g2, _ = _ks_bwd_case(inp, dy64, want_dvals=False)
+    assert g2["dvals"] is None and rel_err(host(g2["dx"]), want["dx"]) <= TOL_F32
+    g3, _ = _ks_bwd_case(inp, dy64)
+    assert torch.equal(g3["dvals"], g1["dvals"]) and torch.equal(g3["dx"], g2["dx"])
