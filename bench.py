@@ -1,7 +1,7 @@
 """Benchmark of the Kronecker-factored layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--cpu-seconds 10]
-    python bench.py --workload {headline,headline_bf16,tiny,mlp_step,gpt2_ffn,ks,sweep}
+    python bench.py --workload {headline,headline_bf16,tiny,mlp_step,gpt2_ffn,ks,ks_bwd,sweep}
     python bench.py --calibrate-copy      (plain device copy of known size, for HBM counters)
 
 Default workload (one JSON line): one step is one kron_linear_fwd + one kron_linear_bwd
@@ -385,6 +385,44 @@ def run_ks(args, dev):
               flush=True)
 
 
+def run_ks_bwd(args, dev):
+    """ks_matmul_bwd at the ViT shape: dx = dy K^T and dvals in one call, fp32 and bf16
+    inputs (fp32 outputs).  Algorithmic work: 2 products of 2*a*b*c*d flop per row; bytes
+    read x and dy once and write dx once (s_in * (in + out) + 4 * in per row)."""
+    import torch
+    import kronecker_factored_structured_amd as K
+    from workloads import vit_ks
+    for dtype in ("f32", "bf16"):
+        inp = vit_ks(dtype, seed=5)
+        a, b, c, d = inp.a, inp.b, inp.c, inp.d
+        N = inp.x.shape[0]
+        g = torch.Generator(device=dev).manual_seed(3)
+        dy = torch.randn(N, a * c * d, device=dev, generator=g)
+        if dtype == "bf16":
+            x = torch.from_numpy(inp.x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+            v = torch.from_numpy(inp.vals_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+            dy = dy.to(torch.bfloat16)
+        else:
+            x = torch.from_numpy(inp.x).to(dev)
+            v = torch.from_numpy(inp.vals).to(dev)
+        ws = torch.empty(K.ks_matmul_bwd_workspace_bytes(N, a, b, c, d, x.dtype), dtype=torch.uint8, device=dev)
+        outs = dict(dx=torch.empty(N, a * b * d, device=dev), dvals=torch.empty(a, d, b, c, device=dev))
+        ms, _ = timed(lambda: K.ks_matmul_bwd(x, v, dy, a, b, c, d, workspace=ws, outs=outs), args.steps, args.warmup)
+        s_in = 4 if dtype == "f32" else 2
+        flops = 2 * N * 2 * a * b * c * d
+        byts = N * (s_in * (a * b * d + a * c * d) + 4 * a * b * d) + (s_in + 4) * a * b * c * d
+        peak = PEAK_FP32_TFLOPS if dtype == "f32" else PEAK_BF16_TFLOPS
+        t_flop, t_hbm = flops / (peak * 1e12), byts / (PEAK_HBM_GBS * 1e9)
+        t_roof = max(t_flop, t_hbm)
+        print(json.dumps({"workload": f"ks_matmul_bwd (a,b,c,d)=(2,48,192,4), 25216 rows, {dtype} inputs, dx and dvals",
+                          "us_per_call": round(ms * 1e3, 2), "rows_per_s": round(N / (ms * 1e-3), 1),
+                          "achieved_gbs": round(byts / (ms * 1e-3) / 1e9, 1),
+                          "effective_tflops": round(flops / (ms * 1e-3) / 1e12, 3),
+                          "t_roof_us": round(t_roof * 1e6, 2), "roofline_frac": round(t_roof / (ms * 1e-3), 4),
+                          "bound": "hbm" if t_hbm >= t_flop else ("fp32" if dtype == "f32" else "bf16")}),
+              flush=True)
+
+
 def run_sweep(args, dev):
     """Batch-size sweep of the 1024 x 1024 layer (the tutorial's comparison): the Kronecker
     layer's fwd+bwd against a dense layer and a dense layer with the group-LASSO penalty
@@ -457,7 +495,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="headline",
-                    choices=("headline", "headline_bf16", "tiny", "mlp_step", "gpt2_ffn", "ks", "sweep"))
+                    choices=("headline", "headline_bf16", "tiny", "mlp_step", "gpt2_ffn", "ks", "ks_bwd", "sweep"))
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed running before the warmup steps, for the GPU clock to ramp up")
@@ -474,7 +512,7 @@ def main():
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         return run_copy(args, dev)
-    {"headline": run_headline, "headline_bf16": run_headline_bf16, "tiny": run_tiny, "sweep": run_sweep, "mlp_step": run_mlp_step, "gpt2_ffn": run_gpt2,
+    {"headline": run_headline, "headline_bf16": run_headline_bf16, "tiny": run_tiny, "sweep": run_sweep, "ks_bwd": run_ks_bwd, "mlp_step": run_mlp_step, "gpt2_ffn": run_gpt2,
      "ks": run_ks}[args.workload](args, dev)
 
 

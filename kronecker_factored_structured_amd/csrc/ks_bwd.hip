@@ -115,6 +115,97 @@ __global__ __launch_bounds__(kDvThreads) void ks_dv_kernel(int64_t N, int a, int
   }
 }
 
+// ---------------------------------------------------------------------------------
+// dvals on the matrix cores, for d = 4 and b = 16*TB (TB <= 4), c = 16*NW (NW <= 16).
+// A workgroup owns one alpha and a chunk of rows; wavefront w owns the gamma tile
+// 16w .. 16w+15 and accumulates dvals[al][de][be][ga] for all TB beta tiles and all four
+// delta in registers.  One v_mfma_f32_16x16x4_f32 step contracts four rows:
+//   lane (g, c) supplies A[be = 16t + c][K = row g] = X[row g, (al*b + 16t + c)*4 + de]
+//   and B[K = row g][ga = 16w + c] = dY[row g, (al*c + 16w + c)*4 + de],
+// both read as one 16-byte load per lane covering the four delta.  Rows past the chunk
+// read as zeros.  The next step's operands are loaded while the current step runs.
+// ---------------------------------------------------------------------------------
+typedef float f4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f4 mfma4(float a, float b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0); }
+__device__ __forceinline__ f4 load4(const float* p) { return *reinterpret_cast<const f4*>(p); }
+__device__ __forceinline__ f4 load4(const uint16_t* p) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  return f4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
+            __uint_as_float(v.y & 0xffff0000u)};
+}
+constexpr int kDvmChunks = 128;   // row chunks per alpha
+
+template <int TB, typename TIn>
+__global__ __launch_bounds__(1024) void ks_dv_mfma_kernel(int64_t N, int a, int c, int64_t Gr,
+                                                          const TIn* __restrict__ x, const TIn* __restrict__ dy,
+                                                          float* __restrict__ part) {
+  constexpr int B = 16 * TB;
+  const int lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15, w = threadIdx.x >> 6;
+  const int al = blockIdx.x % a;
+  const int64_t chunk = blockIdx.x / a;
+  const int64_t in_w = (int64_t)a * B * 4, out_w = (int64_t)a * c * 4;
+  const int64_t per = ((N + Gr - 1) / Gr + 3) / 4 * 4, r0 = chunk * per;
+  const int64_t r1 = r0 + per < N ? r0 + per : N;
+  const TIn* xb = x + ((int64_t)al * B + cl) * 4;
+  const TIn* yb = dy + ((int64_t)al * c + 16 * w + cl) * 4;
+  f4 acc[TB][4];
+#pragma unroll
+  for (int t = 0; t < TB; ++t)
+#pragma unroll
+    for (int de = 0; de < 4; ++de) acc[t][de] = f4{0.f, 0.f, 0.f, 0.f};
+  f4 xn[TB], yn;
+  auto load = [&](f4 (&xv)[TB], f4& yv, int64_t row) {
+    const bool ok = row < r1;
+    const int64_t rr = ok ? row : 0;
+#pragma unroll
+    for (int t = 0; t < TB; ++t) xv[t] = load4(xb + rr * in_w + 64 * t);
+    yv = load4(yb + rr * out_w);
+    if (!ok) {
+#pragma unroll
+      for (int t = 0; t < TB; ++t) xv[t] = f4{0.f, 0.f, 0.f, 0.f};
+      yv = f4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  if (r0 < r1) load(xn, yn, r0 + g);
+  for (int64_t row = r0; row < r1; row += 4) {
+    f4 xv[TB], yv = yn;
+#pragma unroll
+    for (int t = 0; t < TB; ++t) xv[t] = xn[t];
+    load(xn, yn, row + 4 + g);
+#pragma unroll
+    for (int de = 0; de < 4; ++de)
+#pragma unroll
+      for (int t = 0; t < TB; ++t) acc[t][de] = mfma4(xv[t][de], yv[de], acc[t][de]);
+  }
+  // acc[t][de] register v = dvals[al][de][be = 16t + 4g + v][ga = 16w + cl]
+  const PartRow out{part, Gr, chunk, (int64_t)al * 4 * B * c};
+#pragma unroll
+  for (int de = 0; de < 4; ++de)
+#pragma unroll
+    for (int t = 0; t < TB; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) out[((int64_t)de * B + 16 * t + 4 * g + v) * c + 16 * w + cl] = acc[t][de][v];
+}
+
+bool dv_mfma_ok(int a, int b, int c, int d) {
+  (void)a;
+  return d == 4 && b % 16 == 0 && b / 16 >= 1 && b / 16 <= 4 && c % 16 == 0 && c / 16 >= 1 && c / 16 <= 16;
+}
+int64_t dv_mfma_chunks(int64_t N) {
+  const int64_t steps = (N + 3) / 4;
+  return steps < kDvmChunks ? (steps < 1 ? 1 : steps) : kDvmChunks;
+}
+
+template <int TB>
+void launch_dv_mfma(const KSBwdArgs& k, int64_t Gr, dim3 grid, dim3 block, float* part, hipStream_t s) {
+  if (k.dtype == KRON_F32)
+    hipLaunchKernelGGL((ks_dv_mfma_kernel<TB, float>), grid, block, 0, s, k.N, k.a, k.c, Gr, (const float*)k.x,
+                       (const float*)k.dy, part);
+  else
+    hipLaunchKernelGGL((ks_dv_mfma_kernel<TB, uint16_t>), grid, block, 0, s, k.N, k.a, k.c, Gr,
+                       (const uint16_t*)k.x, (const uint16_t*)k.dy, part);
+}
+
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 }  // namespace
@@ -123,8 +214,8 @@ bool ks_bwd_supported(int a, int b, int c, int d) { return ks_supported(a, c, b,
 
 size_t ks_bwd_workspace_bytes(int64_t N, int a, int b, int c, int d, int dtype) {
   const size_t es = dtype == KRON_F32 ? 4 : 2;
-  const DvPlan P = dv_plan(N, a, b, c, d);
-  return align256((size_t)a * b * c * d * es) + align256((size_t)part_floats(P.Gr, (int64_t)a * b * c * d) * 4);
+  const int64_t Gr = dv_mfma_ok(a, b, c, d) ? dv_mfma_chunks(N) : dv_plan(N, a, b, c, d).Gr;
+  return align256((size_t)a * b * c * d * es) + align256((size_t)part_floats(Gr, (int64_t)a * b * c * d) * 4);
 }
 
 hipError_t launch_ks_bwd(const KSBwdArgs& k, void* ws, hipStream_t s) {
@@ -147,7 +238,22 @@ hipError_t launch_ks_bwd(const KSBwdArgs& k, void* ws, hipStream_t s) {
     const KSArgs f{k.N, k.a, k.c, k.b, k.d, k.dtype, KRON_F32, k.dy, vt, k.dx};
     if ((e = launch_ks(f, s)) != hipSuccess) return e;
   }
-  if (k.dvals) {
+  if (k.dvals && dv_mfma_ok(k.a, k.b, k.c, k.d)) {
+    const int64_t Gr = dv_mfma_chunks(k.N);
+    const dim3 grid((unsigned)(Gr * k.a)), block((unsigned)(64 * (k.c / 16)));
+    switch (k.b / 16) {
+      case 1: launch_dv_mfma<1>(k, Gr, grid, block, part, s); break;
+      case 2: launch_dv_mfma<2>(k, Gr, grid, block, part, s); break;
+      case 3: launch_dv_mfma<3>(k, Gr, grid, block, part, s); break;
+      default: launch_dv_mfma<4>(k, Gr, grid, block, part, s); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    RedPlan plan{};
+    plan.seg[0] = RedSeg{k.dvals, (int32_t)total, 1.f, 0};
+    plan.nseg = 1;
+    if ((e = launch_column_reduce(part, (int32_t)Gr, (int32_t)total, plan, s)) != hipSuccess) return e;
+  } else if (k.dvals) {
     const DvPlan P = dv_plan(k.N, k.a, k.b, k.c, k.d);
     const int bhm = k.b < P.BH ? k.b : P.BH;
     const size_t lds = (size_t)P.T * (bhm + P.CW) * sizeof(float);

@@ -335,6 +335,136 @@ __global__ __launch_bounds__((KV<B_, C_, GS_>::NT)) void ks_vreg_kernel(int64_t 
   }
 }
 
+// ---------------------------------------------------------------------------------
+// d = 4 with a long contraction (b large, c small; e.g. the transposed ViT pattern
+// (192, 48) of the input gradient): V in registers as above, but each gamma tile's
+// contraction over beta is split over four wavefronts (a quarter of the K steps each, so
+// 48 registers of V per lane at b = 192).  After a row tile's products the four partial
+// 16 x 16 x 4-delta tiles meet in LDS; wavefront quarter q adds the four partials in
+// quarter order (fixed, deterministic) for output row 4g + q and stores it.
+// ---------------------------------------------------------------------------------
+template <int B_, int C_>
+struct KVK {
+  static constexpr int KSP = 4;                    // contraction split (one output row each)
+  static constexpr int NWG = C_ / 16;              // gamma tiles
+  static constexpr int NW = NWG * KSP, NT = 64 * NW;
+  static constexpr int SB = B_ / 4, SBK = SB / KSP;
+  static constexpr int ROWF = 4 * B_;
+  static constexpr int LXS = ROWF + 4;
+  static constexpr int TILE = 16 * LXS;
+  static constexpr int NF4 = 16 * ROWF / 4;
+  static constexpr int NPF = (NF4 + NT - 1) / NT;
+  static constexpr int RED = NW * 64 * 16;         // floats: every wavefront's 16 accumulators per lane
+  static constexpr size_t LDS = ((size_t)2 * TILE + RED) * 4;
+  static constexpr bool OK = B_ % (4 * KSP) == 0 && C_ % 16 == 0 && NW <= 16 && LDS <= kMaxLds;
+};
+
+template <int B_, int C_, class TIn, class TOut>
+__global__ __launch_bounds__((KVK<B_, C_>::NT)) void ks_vregk_kernel(int64_t N, int a_count, const TIn* __restrict__ x,
+                                                                 const TIn* __restrict__ vals,
+                                                                 TOut* __restrict__ y) {
+  using K = KVK<B_, C_>;
+  extern __shared__ float lds[];   // 2 x TILE rows, then RED
+  f4* red = reinterpret_cast<f4*>(lds + 2 * K::TILE);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15, wv = tid >> 6;
+  const int gt = wv % K::NWG, kq = wv / K::NWG;   // gamma tile, contraction quarter
+  const int al = blockIdx.x % a_count;
+  const int64_t step = gridDim.x / a_count;
+  const int64_t ntile = (N + 15) / 16, nfull = N / 16;
+  const int64_t in_w = (int64_t)a_count * K::ROWF, out_w = (int64_t)a_count * C_ * 4;
+  const TIn* xa = x + (int64_t)al * K::ROWF;
+  TOut* ya = y + ((int64_t)al * C_ + 16 * gt + c) * 4;
+
+  typedef typename Raw4<TIn>::type R4;
+  R4 pf[K::NPF];
+  auto fetch = [&](int64_t tile) {
+#pragma unroll
+    for (int t = 0; t < K::NPF; ++t) {
+      const int f = tid + t * K::NT;
+      R4 v = {};
+      if (K::NF4 % K::NT == 0 || f < K::NF4) {
+        const int r = f / (K::ROWF / 4), o = 4 * (f % (K::ROWF / 4));
+        const int64_t row = tile * 16 + r;
+        if (tile < ntile && row < N) v = load_raw4(xa + row * in_w + o);
+      }
+      pf[t] = v;
+    }
+  };
+  auto stash = [&](float* buf) {
+#pragma unroll
+    for (int t = 0; t < K::NPF; ++t) {
+      const int f = tid + t * K::NT;
+      if (K::NF4 % K::NT == 0 || f < K::NF4) {
+        const int r = f / (K::ROWF / 4), o = 4 * (f % (K::ROWF / 4));
+        *reinterpret_cast<f4*>(buf + r * K::LXS + o) = widen4(pf[t]);
+      }
+    }
+  };
+
+  int64_t tile = blockIdx.x / a_count;
+  fetch(tile);
+  // v[de][s] = V[al][de][be = g*SB + kq*SBK + s][ga = 16*gt + c]
+  float v[4][K::SBK];
+  const TIn* V = vals + (int64_t)al * 4 * B_ * C_;
+#pragma unroll
+  for (int de = 0; de < 4; ++de)
+#pragma unroll
+    for (int s = 0; s < K::SBK; ++s)
+      v[de][s] = widen(V[((int64_t)de * B_ + g * K::SB + kq * K::SBK + s) * C_ + 16 * gt + c]);
+  stash(lds);
+  fetch(tile + step);
+  __syncthreads();
+
+  // the quarter's partial tile -> LDS as red[wave][lane][vv] = f4 over delta; then this
+  // wavefront's output row vv = kq, summed over the quarters of its gamma tile
+  auto compute_and_reduce = [&](const float* xs) {
+    f4 acc[4];
+#pragma unroll
+    for (int de = 0; de < 4; ++de) acc[de] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < K::SBK; ++s) {
+      const f4 xv = *reinterpret_cast<const f4*>(xs + c * K::LXS + (g * K::SB + kq * K::SBK + s) * 4);
+#pragma unroll
+      for (int de = 0; de < 4; ++de) acc[de] = mfma(xv[de], v[de][s], acc[de]);
+    }
+#pragma unroll
+    for (int vv = 0; vv < 4; ++vv) red[(wv * 64 + lane) * 4 + vv] = f4{acc[0][vv], acc[1][vv], acc[2][vv], acc[3][vv]};
+    __syncthreads();
+    f4 sum = red[((0 * K::NWG + gt) * 64 + lane) * 4 + kq];
+#pragma unroll
+    for (int q = 1; q < K::KSP; ++q) sum += red[((q * K::NWG + gt) * 64 + lane) * 4 + kq];
+    return sum;   // Y[row 4g + kq][ga = 16*gt + c][0..3]
+  };
+  int it = 0;
+  for (; tile < nfull; tile += step, ++it) {
+    const f4 o = compute_and_reduce(lds + (it & 1) * K::TILE);
+    store4(ya + (tile * 16 + 4 * g + kq) * out_w, o);
+    stash(lds + ((it + 1) & 1) * K::TILE);
+    fetch(tile + 2 * step);
+    __syncthreads();
+  }
+  if (tile < ntile) {   // the partial tile
+    const f4 o = compute_and_reduce(lds + (it & 1) * K::TILE);
+    const int64_t row = tile * 16 + 4 * g + kq;
+    if (row < N) store4(ya + row * out_w, o);
+  }
+}
+
+struct KvkEntry {
+  int b, c;
+  size_t lds;
+  int nt;
+  const void* fn[2][2];   // [x and vals bf16][y bf16]
+};
+#define KVK_ENTRY(B, C)                                                                                   \
+  KvkEntry{B, C, KVK<B, C>::LDS, KVK<B, C>::NT,                                                           \
+           {{(const void*)&ks_vregk_kernel<B, C, float, float>, (const void*)&ks_vregk_kernel<B, C, float, uint16_t>}, \
+            {(const void*)&ks_vregk_kernel<B, C, uint16_t, float>,                                        \
+             (const void*)&ks_vregk_kernel<B, C, uint16_t, uint16_t>}}}
+// d = 4 shapes with the contraction split: the transposed ViT-S/16 MLP pattern (192, 48).
+const KvkEntry kKvkTable[] = {KVK_ENTRY(192, 48)};
+static_assert(KVK<192, 48>::OK, "the split-contraction KS shape fits the LDS");
+
 struct KsEntry {
   int b, c, d;
   bool ok;
@@ -349,11 +479,10 @@ struct KsEntry {
            {(const void*)&ks_mfma_kernel<KS<B, C, D>, uint16_t, float>,                                       \
             (const void*)&ks_mfma_kernel<KS<B, C, D>, uint16_t, uint16_t>}}}
 
-// The ViT-S/16 MLP pattern (b, c, d) = (48, 192, 4) and its transpose (192, 48, 4) (the
-// input gradient of the first), plus the Kronecker-layer factors written as KS matrices
-// with d = 1.
+// The ViT-S/16 MLP pattern (b, c, d) = (48, 192, 4), plus the Kronecker-layer factors
+// written as KS matrices with d = 1.
 const KsEntry kKsTable[] = {
-    KS_ENTRY(48, 192, 4), KS_ENTRY(192, 48, 4), KS_ENTRY(32, 128, 1), KS_ENTRY(128, 32, 1), KS_ENTRY(64, 64, 1),
+    KS_ENTRY(48, 192, 4), KS_ENTRY(32, 128, 1), KS_ENTRY(128, 32, 1), KS_ENTRY(64, 64, 1),
 };
 
 const KsEntry* ks_find(int b, int c, int d) {
@@ -392,6 +521,28 @@ const KvEntry* kv_find(int b, int c, int d) {
   return nullptr;
 }
 
+const KvkEntry* kvk_find(int b, int c, int d) {
+  if (d != 4) return nullptr;
+  for (const KvkEntry& e : kKvkTable)
+    if (e.b == b && e.c == c) return &e;
+  return nullptr;
+}
+
+hipError_t launch_ks_vregk(const KvkEntry* e, const KSArgs& k, hipStream_t s) {
+  const void* fn = e->fn[k.dtype == KRON_BF16][k.out_dtype == KRON_BF16];
+  (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)e->lds);
+  int per_cu = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, e->nt, e->lds) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  int64_t per_alpha = (int64_t)per_cu * device_cus_ks() / k.a;
+  if (per_alpha < 1) per_alpha = 1;
+  const int64_t tiles = (k.N + 15) / 16;
+  if (per_alpha > tiles) per_alpha = tiles;
+  const int grid = (int)(per_alpha * k.a);
+  void* args[] = {(void*)&k.N, (void*)&k.a, (void*)&k.x, (void*)&k.vals, (void*)&k.y};
+  return hipLaunchKernel(fn, dim3(grid), dim3(e->nt), args, e->lds, s);
+}
+
 hipError_t launch_ks_vreg(const KvEntry* e, const KSArgs& k, hipStream_t s) {
   const void* fn = e->fn[k.dtype == KRON_BF16][k.out_dtype == KRON_BF16];
   (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)e->lds);
@@ -412,12 +563,13 @@ hipError_t launch_ks_vreg(const KvEntry* e, const KSArgs& k, hipStream_t s) {
 
 bool ks_mfma_supported(int a, int b, int c, int d) {
   (void)a;
-  return kv_find(b, c, d) != nullptr || ks_find(b, c, d) != nullptr;
+  return kv_find(b, c, d) != nullptr || kvk_find(b, c, d) != nullptr || ks_find(b, c, d) != nullptr;
 }
 
 hipError_t launch_ks_mfma(const KSArgs& k, hipStream_t s) {
   if (k.N == 0) return hipSuccess;
   if (const KvEntry* ev = kv_find(k.b, k.c, k.d)) return launch_ks_vreg(ev, k, s);
+  if (const KvkEntry* ek = kvk_find(k.b, k.c, k.d)) return launch_ks_vregk(ek, k, s);
   const KsEntry* e = ks_find(k.b, k.c, k.d);
   if (!e) return hipErrorInvalidValue;
   if (k.N == 0) return hipSuccess;

@@ -48,8 +48,8 @@ def test_vit_shape_full_size(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("abcd", [(2, 48, 192, 4), (1, 5, 7, 1), (3, 4, 2, 5), (4, 1, 1, 3), (1, 64, 64, 1),
-                                  (2, 3, 130, 2)])
+@pytest.mark.parametrize("abcd", [(2, 48, 192, 4), (2, 192, 48, 4), (1, 5, 7, 1), (3, 4, 2, 5), (4, 1, 1, 3),
+                                  (1, 64, 64, 1), (2, 3, 130, 2)])
 def test_support_bit_exact(dtype, abcd):
     """Identity input: Y = K exactly, values on the support and +0.0 off it."""
     a, b, c, d = abcd
