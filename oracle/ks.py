@@ -53,3 +53,25 @@ def backward(x, vals, dy, a: int, b: int, c: int, d: int) -> dict:
             cols = (al * c + np.arange(c)) * d + de
             dv[al, de] = dK[np.ix_(rows, cols)]
     return {"dx": dx, "dvals": dv}
+
+
+def chain(x, factors) -> np.ndarray:
+    """Y = X K_1 K_2 ... K_F for Kronecker-sparse factors given as (a, b, c, d, vals): the
+    product of the dense KS matrices, applied left to right (each factor's input width
+    a*b*d equals the previous factor's output width a*c*d)."""
+    y = as64(x)
+    for (a, b, c, d, vals) in factors:
+        y = y @ dense(vals, a, b, c, d)
+    return y
+
+
+def kron3_factors(A, B, C):
+    """A (x) B (x) C as three KS factors (mixed-product rule):
+    (A (x) I_{p2 p3}) (I_{q1} (x) B (x) I_{p3}) (I_{q1 q2} (x) C), with every block of a
+    factor holding the same small matrix."""
+    A, B, C = as64(A), as64(B), as64(C)
+    (p1, q1), (p2, q2), (p3, q3) = A.shape, B.shape, C.shape
+    f1 = (1, p1, q1, p2 * p3, np.broadcast_to(A, (1, p2 * p3, p1, q1)).copy())
+    f2 = (q1, p2, q2, p3, np.broadcast_to(B, (q1, p3, p2, q2)).copy())
+    f3 = (q1 * q2, p3, q3, 1, np.broadcast_to(C, (q1 * q2, 1, p3, q3)).copy())
+    return [f1, f2, f3]

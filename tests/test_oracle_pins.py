@@ -304,6 +304,29 @@ def test_ks_backward_transpose_pattern_and_adjoint():
     assert np.isclose(np.sum(g["dvals"] * v), form, rtol=1e-12)
 
 
+@pytest.mark.parametrize("dims", [((2, 3), (3, 2), (2, 4)), ((1, 4), (5, 1), (3, 3)), ((4, 2), (2, 2), (1, 3))])
+def test_ks_chain_triple_kronecker_matches_numpy(dims):
+    """A (x) B (x) C as a chain of three KS factors equals numpy.kron(numpy.kron(A, B), C)
+    bit for bit on integer values (mixed-product rule)."""
+    rng = np.random.default_rng(9)
+    A, B, C = (rng.integers(-3, 4, dm).astype(float) for dm in dims)
+    x = rng.integers(-3, 4, (5, dims[0][0] * dims[1][0] * dims[2][0])).astype(float)
+    want = x @ np.kron(np.kron(A, B), C)
+    assert np.array_equal(OKS.chain(x, OKS.kron3_factors(A, B, C)), want)
+
+
+def test_ks_chain_single_factor_and_associativity():
+    """A one-factor chain is the KS matmul; a chain equals the product of its dense factors
+    in any grouping."""
+    rng = np.random.default_rng(10)
+    f1 = (2, 3, 4, 2, rng.standard_normal((2, 2, 3, 4)))   # 12 -> 16
+    f2 = (4, 2, 3, 2, rng.standard_normal((4, 2, 2, 3)))   # 16 -> 24
+    x = rng.standard_normal((3, 12))
+    assert np.array_equal(OKS.chain(x, [f1]), OKS.matmul(x, f1[4], *f1[:4]))
+    K1, K2 = OKS.dense(f1[4], *f1[:4]), OKS.dense(f2[4], *f2[:4])
+    np.testing.assert_allclose(OKS.chain(x, [f1, f2]), x @ (K1 @ K2), rtol=1e-12, atol=1e-12)
+
+
 @pytest.mark.parametrize("case", [(3, 2, 2, 3, 2), (2, 3, 3, 2, 1), (4, 4, 2, 2, 3)])
 def test_kron_layer_equals_chain_of_two_ks_factors(case):
     """The layer factors as (I_p (x) B_all) followed by a KS factor carrying the C_i:
