@@ -172,6 +172,32 @@ int32_t ks_matmul_out(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int
  * KRON_E_UNSUPPORTED, KRON_E_NULL, KRON_E_ALIGN, KRON_E_ALIAS, KRON_E_WORKSPACE,
  * KRON_E_HIP.  ks_matmul_bwd_workspace_bytes returns 0 for arguments ks_matmul_bwd rejects.
  */
+/*
+ * One Kronecker-sparse factor of a chain: support I_a (x) 1_{b x c} (x) I_d, values
+ * vals[a][d][b][c] (device pointer, dtype of the chain's input).
+ */
+typedef struct {
+  int32_t a, b, c, d;
+  const void* vals;
+} ks_factor_t;
+
+/*
+ * Fused chain y = x K_1 K_2 ... K_n of Kronecker-sparse factors ("Fast Inference with
+ * Kronecker-Sparse Matrices", abstract: products of KS factors such as butterfly and
+ * Monarch factors; the triple Kronecker product A (x) B (x) C is a three-factor chain by the
+ * mixed-product rule).  Each factor maps a*b*d values per row to a*c*d with the index map
+ * of ks_matmul; factor f+1 takes what factor f gives.  Intermediate rows stay on chip
+ * (fp32); only y is written.
+ *   factors  HOST array of nfactors (1..8) ks_factor_t
+ *   x        [N, a1*b1*d1]  fp32 or bf16 (in_dtype; every factor's vals in the same dtype)
+ *   y        [N, an*cn*dn]  fp32
+ * Limits: every row width <= 16384.  Errors: KRON_E_SHAPE (widths that do not chain),
+ * KRON_E_ARG (nfactors), KRON_E_NULL, KRON_E_DTYPE, KRON_E_UNSUPPORTED, KRON_E_ALIGN,
+ * KRON_E_ALIAS (y over x or any vals), KRON_E_HIP.
+ */
+int32_t ks_chain(int64_t N, int32_t nfactors, const ks_factor_t* factors, int32_t in_dtype,
+                 const void* x, float* y, hipStream_t stream);
+
 size_t ks_matmul_bwd_workspace_bytes(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d,
                                      int32_t in_dtype);
 int32_t ks_matmul_bwd(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype,

@@ -33,8 +33,13 @@ EXPORTS = (
     "kron_linear_bwd_workspace_bytes", "kron_linear_fwd", "kron_linear_bwd", "ks_matmul",
     "kron_adam_l1_step", "kron_head_ce_workspace_bytes", "kron_head_ce",
     "kron_linear_bwd_bf16_workspace_bytes", "kron_linear_fwd_bf16", "kron_linear_bwd_bf16",
-    "ks_matmul_out", "ks_matmul_bwd_workspace_bytes", "ks_matmul_bwd",
+    "ks_matmul_out", "ks_matmul_bwd_workspace_bytes", "ks_matmul_bwd", "ks_chain",
 )
+
+
+class KsFactor(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_int32), ("b", ctypes.c_int32), ("c", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("vals", ctypes.c_void_p)]
 
 
 class KronShape(ctypes.Structure):
@@ -76,6 +81,7 @@ def lib() -> ctypes.CDLL:
             "ks_matmul_out": (i32, [i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]),
             "ks_matmul_bwd_workspace_bytes": (ctypes.c_size_t, [i64, i32, i32, i32, i32, i32]),
             "ks_matmul_bwd": (i32, [i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
+            "ks_chain": (i32, [i64, i32, ctypes.POINTER(KsFactor), i32, vp, vp, vp]),
             "kron_adam_l1_step": (i32, [i32, pp, pp, pp, pp, ctypes.POINTER(ctypes.c_int64),
                                         ctypes.POINTER(ctypes.c_float), i64, ctypes.c_double,
                                         ctypes.c_double, ctypes.c_double, ctypes.c_double, vp]),

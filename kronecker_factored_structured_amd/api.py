@@ -212,6 +212,35 @@ def ks_matmul_bwd(x: torch.Tensor, vals: torch.Tensor, dy: torch.Tensor, a: int,
     return dict(dx=dx, dvals=dv)
 
 
+def ks_chain(x: torch.Tensor, factors: Sequence, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Fused y = x K_1 ... K_n; factors is a sequence of (vals, a, b, c, d) with vals
+    a x d x b x c in x's dtype (float32 or bfloat16); y is float32."""
+    if x.dtype == torch.float32:
+        dt = KRON_F32
+    elif x.dtype == torch.bfloat16:
+        dt = KRON_BF16
+    else:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    _dev(x, "x", x.dtype)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    arr = (_lib.KsFactor * max(len(factors), 1))()
+    for i, (v, a, b, c, d) in enumerate(factors):
+        _dev(v, "vals", x.dtype)
+        if v.numel() != a * b * c * d:
+            raise ValueError(f"factor {i}: vals must hold a*b*c*d = {a * b * c * d} values")
+        arr[i] = _lib.KsFactor(a, b, c, d, _ptr(v))
+    if factors:
+        v, a, b, c, d = factors[-1]
+        width = a * c * d
+    else:
+        width = 0
+    _dev(out, "out")
+    y = out if out is not None else torch.empty(x.shape[0], width, device=x.device)
+    check("ks_chain", _lib.lib().ks_chain(x.shape[0], len(factors), arr, dt, _ptr(x), _ptr(y), _stream(x.device)))
+    return y
+
+
 def kron_adam_l1_step(params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
                       m: Sequence[torch.Tensor], v: Sequence[torch.Tensor], step: int, lr: float,
                       beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,

@@ -33,6 +33,7 @@ OBJECTS = [
     ("ks_matmul.hip", [], "ks_matmul"),
     ("ks_mfma.hip", [], "ks_mfma"),
     ("ks_bwd.hip", [], "ks_bwd"),
+    ("ks_chain.hip", [], "ks_chain"),
     ("adam_l1.hip", [], "adam_l1"),
     ("head_ce.hip", [], "head_ce"),
 ]

@@ -435,6 +435,53 @@ int32_t ks_matmul_bwd(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int
   return ok();
 }
 
+int32_t ks_chain(int64_t N, int32_t nfactors, const ks_factor_t* factors, int32_t in_dtype, const void* x, float* y,
+                 hipStream_t stream) {
+  if (N < 0 || N > kMaxRows) return fail(KRON_E_SHAPE, "N = %lld out of range", (long long)N);
+  if (nfactors < 1 || nfactors > kron::kChainMaxFactors)
+    return fail(KRON_E_ARG, "nfactors = %d outside 1..%d", nfactors, kron::kChainMaxFactors);
+  if (!factors) return fail(KRON_E_NULL, "factors is required");
+  if (in_dtype != KRON_F32 && in_dtype != KRON_BF16) return fail(KRON_E_DTYPE, "input dtype %d", in_dtype);
+  const size_t es = in_dtype == KRON_F32 ? 4 : 2;
+  kron::ChainArgs A{};
+  A.N = N;
+  A.nf = nfactors;
+  A.dtype = in_dtype;
+  int64_t width = 0, maxw = 0;
+  Range ins[kron::kChainMaxFactors + 1];
+  for (int32_t f = 0; f < nfactors; ++f) {
+    const ks_factor_t& F = factors[f];
+    if (F.a < 1 || F.b < 1 || F.c < 1 || F.d < 1) return fail(KRON_E_SHAPE, "factor %d: a, b, c, d must be >= 1", f);
+    const int64_t win = (int64_t)F.a * F.b * F.d, wout = (int64_t)F.a * F.c * F.d;
+    if (win > kron::kChainMaxWidth || wout > kron::kChainMaxWidth)
+      return fail(KRON_E_UNSUPPORTED, "factor %d: width %lld -> %lld exceeds %d", f, (long long)win, (long long)wout,
+                  kron::kChainMaxWidth);
+    if (f > 0 && win != width)
+      return fail(KRON_E_SHAPE, "factor %d takes %lld values per row, factor %d gives %lld", f, (long long)win, f - 1,
+                  (long long)width);
+    if (!F.vals) return fail(KRON_E_NULL, "factor %d: vals is required", f);
+    ins[f + 1] = Range{F.vals, (size_t)F.a * F.b * F.c * F.d * es, "vals"};
+    A.f[f] = kron::ChainFactor{F.a, F.b, F.c, F.d, F.vals};
+    maxw = win > maxw ? win : maxw;
+    maxw = wout > maxw ? wout : maxw;
+    width = wout;
+  }
+  const int64_t w0 = (int64_t)factors[0].a * factors[0].b * factors[0].d;
+  if (N > 0 && (!x || !y)) return fail(KRON_E_NULL, "x and y are required when N > 0");
+  ins[0] = Range{x, (size_t)N * w0 * es, "x"};
+  const Range outs[1] = {{y, (size_t)N * width * 4, "y"}};
+  int32_t st;
+  if ((st = check_align(ins, nfactors + 1)) != KRON_OK || (st = check_align(outs, 1)) != KRON_OK) return st;
+  if ((st = check_alias(outs, 1, ins, nfactors + 1)) != KRON_OK) return st;
+  if (N == 0) return ok();
+  A.maxw = (int32_t)maxw;
+  A.x = x;
+  A.y = y;
+  hipError_t e = kron::launch_ks_chain(A, stream);
+  if (e != hipSuccess) return hip_fail(e, "ks_chain launch");
+  return ok();
+}
+
 int32_t kron_adam_l1_step(int32_t ntensors, float* const* params, const float* const* grads, float* const* m,
                           float* const* v, const int64_t* numel, const float* l1, int64_t step, double lr,
                           double beta1, double beta2, double eps, hipStream_t stream) {

@@ -147,6 +147,22 @@ struct KSBwdArgs {
   float* dx;
   float* dvals;
 };
+// Fused chain of KS factors (ks_chain.hip): y = x K_1 ... K_nf, rows of at most maxw values.
+constexpr int kChainMaxFactors = 8;
+constexpr int kChainMaxWidth = 16384;
+struct ChainFactor {
+  int32_t a, b, c, d;
+  const void* vals;
+};
+struct ChainArgs {
+  int64_t N;
+  int32_t nf, dtype, maxw;
+  ChainFactor f[kChainMaxFactors];
+  const void* x;
+  float* y;
+};
+int chain_rows_per_tile(int maxw);
+hipError_t launch_ks_chain(const ChainArgs& a, hipStream_t s);
 bool ks_bwd_supported(int a, int b, int c, int d);
 size_t ks_bwd_workspace_bytes(int64_t N, int a, int b, int c, int d, int dtype);
 hipError_t launch_ks_bwd(const KSBwdArgs& k, void* workspace, hipStream_t s);

@@ -194,6 +194,26 @@ def test_ks_bwd_argument_errors():
     assert L.ks_matmul_bwd(8, 1, 65536, 65536, 1, 0, *args()) == _lib.KRON_E_UNSUPPORTED    # a*b*c*d > 2^28
 
 
+def test_ks_chain_argument_errors():
+    L = _lib.lib()
+    MB = 1 << 20
+    F = _lib.KsFactor
+    two = (F * 2)(F(2, 3, 4, 2, P(MB)), F(4, 2, 3, 2, P(2 * MB)))   # 12 -> 16 -> 24
+    assert L.ks_chain(8, 0, two, 0, P(0), P(4 * MB), None) == _lib.KRON_E_ARG
+    assert L.ks_chain(8, 9, two, 0, P(0), P(4 * MB), None) == _lib.KRON_E_ARG
+    assert L.ks_chain(8, 2, None, 0, P(0), P(4 * MB), None) == _lib.KRON_E_NULL
+    assert L.ks_chain(8, 2, two, 7, P(0), P(4 * MB), None) == _lib.KRON_E_DTYPE
+    bad = (F * 2)(F(2, 3, 4, 2, P(MB)), F(4, 3, 3, 2, P(2 * MB)))   # 16 given, 24 taken
+    assert L.ks_chain(8, 2, bad, 0, P(0), P(4 * MB), None) == _lib.KRON_E_SHAPE
+    nul = (F * 2)(F(2, 3, 4, 2, P(MB)), F(4, 2, 3, 2, None))
+    assert L.ks_chain(8, 2, nul, 0, P(0), P(4 * MB), None) == _lib.KRON_E_NULL
+    wide = (F * 1)(F(1, 1, 20000, 1, P(MB)))
+    assert L.ks_chain(8, 1, wide, 0, P(0), P(4 * MB), None) == _lib.KRON_E_UNSUPPORTED
+    assert L.ks_chain(8, 2, two, 0, P(0), P(2 * MB), None) == _lib.KRON_E_ALIAS        # y over vals
+    assert L.ks_chain(8, 2, two, 0, P(8), P(4 * MB), None) == _lib.KRON_E_ALIGN
+    assert L.ks_chain(0, 2, two, 0, None, None, None) == 0
+
+
 def test_adam_argument_errors():
     L = _lib.lib()
     arr = ctypes.c_void_p * 1

@@ -217,3 +217,70 @@ def test_ks_backward_single_outputs_and_determinism():
     assert g2["dvals"] is None and rel_err(host(g2["dx"]), want["dx"]) <= TOL_F32
     g3, _ = _ks_bwd_case(inp, dy64)
     assert torch.equal(g3["dvals"], g1["dvals"]) and torch.equal(g3["dx"], g2["dx"])
+
+
+def _chain_dev(factors, dtype):
+    out = []
+    for (a, b, c, d, v) in factors:
+        v32 = np.ascontiguousarray(v, dtype=np.float32)
+        if dtype == "bf16":
+            from workloads import bf16_bits, bf16_to_f32
+            bits = bf16_bits(v32)
+            out.append(((a, b, c, d, bf16_to_f32(bits).reshape(v32.shape)),
+                        dev(bits.view(np.int16)).view(torch.bfloat16)))
+        else:
+            out.append(((a, b, c, d, v32), dev(v32)))
+    return out
+
+
+def _run_chain(x32, factors, dtype="f32"):
+    fs = _chain_dev(factors, dtype)
+    if dtype == "bf16":
+        from workloads import bf16_bits, bf16_to_f32
+        bits = bf16_bits(x32)
+        x_host = bf16_to_f32(bits).reshape(x32.shape)
+        x = dev(bits.view(np.int16)).view(torch.bfloat16)
+    else:
+        x_host, x = x32, dev(x32)
+    print(f"[ks chain] N={x32.shape[0]} factors={[f[0][:4] for f in fs]} dtype={dtype}", flush=True)
+    y = K().ks_chain(x, [(t, *f[:4]) for f, t in fs])
+    torch.cuda.synchronize()
+    return host(y), OKS.chain(x_host, [f for f, _ in fs])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ks_chain_triple_kronecker(dtype):
+    """x (A (x) B (x) C) for a 1024 x 1024 triple Kronecker product (8x8, 16x16, 8x8) as a
+    fused three-factor chain, against the oracle's product of dense factors."""
+    rng = np.random.default_rng(60)
+    A, B, C = (rng.standard_normal(s) / np.sqrt(s[0]) for s in ((8, 8), (16, 16), (8, 8)))
+    factors = OKS.kron3_factors(A, B, C)
+    x = rng.standard_normal((2053, 1024)).astype(np.float32)
+    y, want = _run_chain(x, factors, dtype)
+    e = rel_err(y, want)
+    print(f"   rel error {e:.2e}", flush=True)
+    assert e <= TOL_F32
+
+
+def test_ks_chain_monarch_two_factors():
+    """A Monarch-style product: block-diagonal (a=32 blocks of 32x32), then the same
+    pattern across the interleaved index (a=1, d=32), each block with its own values."""
+    rng = np.random.default_rng(61)
+    f1 = (32, 32, 32, 1, rng.standard_normal((32, 1, 32, 32)) / np.sqrt(32))
+    f2 = (1, 32, 32, 32, rng.standard_normal((1, 32, 32, 32)) / np.sqrt(32))
+    x = rng.standard_normal((1000, 1024)).astype(np.float32)
+    y, want = _run_chain(x, [f1, f2])
+    assert rel_err(y, want) <= TOL_F32
+
+
+@pytest.mark.parametrize("N", [0, 1, 17])
+def test_ks_chain_ragged_and_rectangular(N):
+    rng = np.random.default_rng(62)
+    f1 = (2, 3, 5, 4, rng.standard_normal((2, 4, 3, 5)))    # 24 -> 40
+    f2 = (5, 8, 3, 1, rng.standard_normal((5, 1, 8, 3)))    # 40 -> 15
+    f3 = (1, 15, 7, 1, rng.standard_normal((1, 1, 15, 7)))  # 15 -> 7
+    x = rng.standard_normal((N, 24)).astype(np.float32)
+    y, want = _run_chain(x, [f1, f2, f3])
+    assert y.shape == (N, 7)
+    if N:
+        assert rel_err(y, want) <= TOL_F32
