@@ -1,7 +1,7 @@
 """Benchmark of the Kronecker-factored layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--cpu-seconds 10]
-    python bench.py --workload {headline,headline_bf16,tiny,mlp_step,gpt2_ffn,ks,ks_bwd,sweep}
+    python bench.py --workload {headline,headline_bf16,tiny,mlp_step,gpt2_ffn,ks,ks_bwd,chain,sweep}
     python bench.py --calibrate-copy      (plain device copy of known size, for HBM counters)
 
 Default workload (one JSON line): one step is one kron_linear_fwd + one kron_linear_bwd
@@ -423,6 +423,42 @@ def run_ks_bwd(args, dev):
               flush=True)
 
 
+def run_chain(args, dev):
+    """Fused KS chains at 20,000 rows of 1024 values: the triple Kronecker product
+    (8x8) (x) (16x16) (x) (8x8) as three factors, and a Monarch-style pair of 32x32-block
+    factors.  Algorithmic work: sum over factors of 2*a*b*c*d flop per row; bytes: x read
+    and y written once (4 * (in + out) per row)."""
+    import torch
+    import kronecker_factored_structured_amd as K
+    rng = np.random.default_rng(70)
+    A, B, C = (rng.standard_normal(s) / np.sqrt(s[0]) for s in ((8, 8), (16, 16), (8, 8)))
+    # A (x) B (x) C = (A (x) I_128)(I_8 (x) B (x) I_8)(I_128 (x) C): each factor repeats its block
+    kron3 = [(1, 8, 8, 128, np.broadcast_to(A, (1, 128, 8, 8))),
+             (8, 16, 16, 8, np.broadcast_to(B, (8, 8, 16, 16))),
+             (128, 8, 8, 1, np.broadcast_to(C, (128, 1, 8, 8)))]
+    cases = {
+        "triple Kronecker (8x8)(x)(16x16)(x)(8x8)": kron3,
+        "Monarch pair, 32 blocks of 32x32 twice": [
+            (32, 32, 32, 1, rng.standard_normal((32, 1, 32, 32)) / np.sqrt(32)),
+            (1, 32, 32, 32, rng.standard_normal((1, 32, 32, 32)) / np.sqrt(32))],
+    }
+    N = 20000
+    x = torch.randn(N, 1024, device=dev)
+    y = torch.empty(N, 1024, device=dev)
+    for name, fs in cases.items():
+        tf = [(torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(dev), a, b, c, d) for (a, b, c, d, v) in fs]
+        ms, _ = timed(lambda: K.ks_chain(x, tf, out=y), args.steps, args.warmup)
+        flops = N * sum(2 * a * b * c * d for (a, b, c, d, _) in fs)
+        byts = N * 4 * (1024 + 1024)
+        t_flop, t_hbm = flops / (PEAK_FP32_TFLOPS * 1e12), byts / (PEAK_HBM_GBS * 1e9)
+        t_roof = max(t_flop, t_hbm)
+        print(json.dumps({"workload": f"ks_chain {name}, {N} rows, fp32", "us_per_call": round(ms * 1e3, 2),
+                          "rows_per_s": round(N / (ms * 1e-3), 1), "achieved_gbs": round(byts / (ms * 1e-3) / 1e9, 1),
+                          "effective_tflops": round(flops / (ms * 1e-3) / 1e12, 3), "t_roof_us": round(t_roof * 1e6, 2),
+                          "roofline_frac": round(t_roof / (ms * 1e-3), 4),
+                          "bound": "hbm" if t_hbm >= t_flop else "fp32"}), flush=True)
+
+
 def run_sweep(args, dev):
     """Batch-size sweep of the 1024 x 1024 layer (the tutorial's comparison): the Kronecker
     layer's fwd+bwd against a dense layer and a dense layer with the group-LASSO penalty
@@ -495,7 +531,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="headline",
-                    choices=("headline", "headline_bf16", "tiny", "mlp_step", "gpt2_ffn", "ks", "ks_bwd", "sweep"))
+                    choices=("headline", "headline_bf16", "tiny", "mlp_step", "gpt2_ffn", "ks", "ks_bwd", "chain", "sweep"))
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed running before the warmup steps, for the GPU clock to ramp up")
@@ -512,7 +548,7 @@ def main():
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         return run_copy(args, dev)
-    {"headline": run_headline, "headline_bf16": run_headline_bf16, "tiny": run_tiny, "sweep": run_sweep, "ks_bwd": run_ks_bwd, "mlp_step": run_mlp_step, "gpt2_ffn": run_gpt2,
+    {"headline": run_headline, "headline_bf16": run_headline_bf16, "tiny": run_tiny, "sweep": run_sweep, "ks_bwd": run_ks_bwd, "chain": run_chain, "mlp_step": run_mlp_step, "gpt2_ffn": run_gpt2,
      "ks": run_ks}[args.workload](args, dev)
 
 

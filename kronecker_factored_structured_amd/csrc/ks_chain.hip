@@ -9,7 +9,7 @@
 namespace kron {
 namespace {
 
-constexpr int kChainThreads = 256;
+constexpr int kChainThreads = 1024;
 constexpr int kChainMaxRows = 16;
 constexpr size_t kChainLds = 160 * 1024;
 
@@ -38,17 +38,32 @@ __global__ __launch_bounds__(kChainThreads) void ks_chain_kernel(ChainArgs A, in
     const int wout = a * c * d;
     const TIn* V = static_cast<const TIn*>(A.f[fi].vals);
     const bool last = fi == A.nf - 1;
-    for (int o = tid; o < rows * wout; o += kChainThreads) {
-      const int t = o / wout, col = o - t * wout;
+    // a thread owns output columns; each value is loaded once per tile and applied to
+    // every row of the tile from LDS
+    for (int col = tid; col < wout; col += kChainThreads) {
       const int de = col % d, rest = col / d, ga = rest % c, al = rest / c;
-      const float* ir = in + t * A.maxw + (al * b) * d + de;
+      const float* ir = in + (al * b) * d + de;
       const TIn* v = V + ((int64_t)(al * d + de) * b) * c + ga;
-      float acc = 0.f;
-      for (int be = 0; be < b; ++be) acc = fmaf(ir[be * d], load_in(v, (int64_t)be * c), acc);
-      if (last)
-        A.y[(row0 + t) * wout + col] = acc;
-      else
-        out[t * A.maxw + col] = acc;
+      float acc[kChainMaxRows];
+#pragma unroll
+      for (int t = 0; t < kChainMaxRows; ++t) acc[t] = 0.f;
+#pragma unroll 8
+      for (int be = 0; be < b; ++be) {
+        const float vv = load_in(v, (int64_t)be * c);
+        const float* ib = ir + be * d;
+#pragma unroll
+        for (int t = 0; t < kChainMaxRows; ++t)
+          if (t < rows) acc[t] = fmaf(ib[t * A.maxw], vv, acc[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < kChainMaxRows; ++t) {
+        if (t < rows) {
+          if (last)
+            A.y[(row0 + t) * wout + col] = acc[t];
+          else
+            out[t * A.maxw + col] = acc[t];
+        }
+      }
     }
     __syncthreads();
     float* tmp = in;
