@@ -15,6 +15,7 @@ import scipy.linalg
 import oracle
 from oracle import kron as OK
 from oracle import ks as OKS
+from oracle import vanloan as OVL
 from workloads import integer_kron_inputs, kron_inputs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -126,6 +127,39 @@ def test_van_loan_rearrangement_rank(r):
     sv = np.linalg.svd(R, compute_uv=False)
     assert np.all(sv[r:] <= 1e-12 * sv[0])
     assert sv[r - 1] > 1e-6 * sv[0]
+
+
+def test_van_loan_recovers_an_exact_kronecker_sum():
+    """W = sum of three Kronecker products (numpy.kron): the rank-3 projection rebuilds W,
+    and a rank-4 projection adds nothing (its fourth singular value is zero)."""
+    rng = np.random.default_rng(11)
+    p, q, m, n = 4, 3, 5, 2
+    W = sum(np.kron(rng.standard_normal((p, q)), rng.standard_normal((m, n))) for _ in range(3))
+    C, B, s = OVL.project(W, p, q, m, n, 3)
+    np.testing.assert_allclose(OVL.reconstruct(C, B), W, rtol=0, atol=1e-12 * np.abs(W).max())
+    _, _, s4 = OVL.project(W, p, q, m, n, 4)
+    assert s4[3] <= 1e-12 * s4[0]
+
+
+def test_van_loan_eckart_young_closed_form():
+    """Orthonormal vec(C_i) and vec(B_i) (QR) with weights w: R has singular values w, each
+    term is w_i C_i (x) B_i, and the rank-2 error is the sqrt of the dropped weights squared."""
+    rng = np.random.default_rng(12)
+    p, q, m, n = 4, 5, 3, 6
+    w = np.array([5.0, 3.0, 2.0, 1.0, 0.5])
+    Qc, _ = np.linalg.qr(rng.standard_normal((p * q, 5)))
+    Qb, _ = np.linalg.qr(rng.standard_normal((m * n, 5)))
+    W = sum(w[i] * np.kron(Qc[:, i].reshape(p, q), Qb[:, i].reshape(m, n)) for i in range(5))
+    C, B, s = OVL.project(W, p, q, m, n, 2)
+    np.testing.assert_allclose(s, w[:2], rtol=1e-12)
+    for i in range(2):
+        np.testing.assert_allclose(np.kron(C[i], B[i]),
+                                   w[i] * np.kron(Qc[:, i].reshape(p, q), Qb[:, i].reshape(m, n)), atol=1e-12)
+    err = np.linalg.norm(W - OVL.reconstruct(C, B))
+    assert np.isclose(err, np.sqrt(np.sum(w[2:] ** 2)), rtol=1e-12)
+    # sign convention: the largest entry of each C_i is positive
+    for i in range(2):
+        assert C[i].reshape(-1)[np.argmax(np.abs(C[i]))] > 0
 
 
 @pytest.mark.parametrize("p,q,m,n,r", [(1, 5, 1, 1, 1)])
