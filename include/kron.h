@@ -173,6 +173,29 @@ int32_t ks_matmul_out(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int
  * KRON_E_HIP.  ks_matmul_bwd_workspace_bytes returns 0 for arguments ks_matmul_bwd rejects.
  */
 /*
+ * Van Loan rank-r Kronecker projection of a dense W ("Replicating & Extending Krony-PT on
+ * GPT-2 Small", section "Core Algorithm - Van Loan Kronecker Decomposition"): factors with
+ * sum_i kron(C_i, B_i) the best rank-r Kronecker sum to W in the Frobenius norm, from the
+ * leading singular triplets of the rearrangement R[(j*q + k), (a*n + b)] = W[j*m + a, k*n + b]:
+ * C_i = sqrt(sigma_i) reshape(u_i, p x q), B_i = sqrt(sigma_i) reshape(v_i, m x n).  The
+ * triplets come from block subspace iteration of width s (r <= s <= 32) started from the
+ * caller's random block omega and run for iters power iterations; accuracy grows with
+ * s - r and iters (the error factor is (sigma_{s+1} / sigma_r)^(2 iters + 1)).  Sign of each
+ * pair: the entry of C_i largest in magnitude (first in row-major order) is positive.
+ *   W      [p*m, q*n]  fp32 (the layer's in x out orientation)
+ *   omega  [m*n, s]    fp32 starting block (e.g. standard normal draws)
+ *   C [r, p, q], B [r, m, n], sigma [r]: fp32 outputs (sigma decreasing)
+ * workspace: kron_van_loan_workspace_bytes(p, q, m, n, s) bytes, 256-byte aligned, caller
+ * owned.  Limits: p*q and m*n <= 8192, p*m and q*n <= 65536, 0 <= iters <= 100.  Errors:
+ * KRON_E_SHAPE, KRON_E_ARG, KRON_E_UNSUPPORTED, KRON_E_NULL, KRON_E_ALIGN, KRON_E_ALIAS,
+ * KRON_E_WORKSPACE, KRON_E_HIP.  The workspace query returns 0 for rejected shapes.
+ */
+size_t kron_van_loan_workspace_bytes(int32_t p, int32_t q, int32_t m, int32_t n, int32_t s);
+int32_t kron_van_loan(int32_t p, int32_t q, int32_t m, int32_t n, int32_t r, int32_t s,
+                      int32_t iters, const float* W, const float* omega, float* C, float* B,
+                      float* sigma, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * One Kronecker-sparse factor of a chain: support I_a (x) 1_{b x c} (x) I_d, values
  * vals[a][d][b][c] (device pointer, dtype of the chain's input).
  */

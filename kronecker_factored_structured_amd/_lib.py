@@ -34,6 +34,7 @@ EXPORTS = (
     "kron_adam_l1_step", "kron_head_ce_workspace_bytes", "kron_head_ce",
     "kron_linear_bwd_bf16_workspace_bytes", "kron_linear_fwd_bf16", "kron_linear_bwd_bf16",
     "ks_matmul_out", "ks_matmul_bwd_workspace_bytes", "ks_matmul_bwd", "ks_chain",
+    "kron_van_loan_workspace_bytes", "kron_van_loan",
 )
 
 
@@ -82,6 +83,8 @@ def lib() -> ctypes.CDLL:
             "ks_matmul_bwd_workspace_bytes": (ctypes.c_size_t, [i64, i32, i32, i32, i32, i32]),
             "ks_matmul_bwd": (i32, [i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
             "ks_chain": (i32, [i64, i32, ctypes.POINTER(KsFactor), i32, vp, vp, vp]),
+            "kron_van_loan_workspace_bytes": (ctypes.c_size_t, [i32, i32, i32, i32, i32]),
+            "kron_van_loan": (i32, [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
             "kron_adam_l1_step": (i32, [i32, pp, pp, pp, pp, ctypes.POINTER(ctypes.c_int64),
                                         ctypes.POINTER(ctypes.c_float), i64, ctypes.c_double,
                                         ctypes.c_double, ctypes.c_double, ctypes.c_double, vp]),

@@ -241,6 +241,30 @@ def ks_chain(x: torch.Tensor, factors: Sequence, out: Optional[torch.Tensor] = N
     return y
 
 
+def kron_van_loan(W: torch.Tensor, p: int, q: int, m: int, n: int, r: int, omega: torch.Tensor,
+                  iters: int = 8, workspace: Optional[torch.Tensor] = None) -> tuple:
+    """Rank-r Van Loan factors (C [r,p,q], B [r,m,n], sigma [r]) of a dense W [p*m, q*n];
+    omega [m*n, s] is the random starting block (its width s sets the subspace)."""
+    _dev(W, "W")
+    _dev(omega, "omega")
+    if W.shape != (p * m, q * n):
+        raise ValueError(f"W must be {p * m} x {q * n}")
+    if omega.dim() != 2 or omega.shape[0] != m * n:
+        raise ValueError(f"omega must be {m * n} x s")
+    s = omega.shape[1]
+    dev = W.device
+    C = torch.empty(r, p, q, device=dev)
+    B = torch.empty(r, m, n, device=dev)
+    sigma = torch.empty(r, device=dev)
+    need = int(_lib.lib().kron_van_loan_workspace_bytes(p, q, m, n, s))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    check("kron_van_loan", _lib.lib().kron_van_loan(p, q, m, n, r, s, iters, _ptr(W), _ptr(omega), _ptr(C), _ptr(B),
+                                                    _ptr(sigma), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                                                    _stream(dev)))
+    return C, B, sigma
+
+
 def kron_adam_l1_step(params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
                       m: Sequence[torch.Tensor], v: Sequence[torch.Tensor], step: int, lr: float,
                       beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,

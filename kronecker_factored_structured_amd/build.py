@@ -34,6 +34,7 @@ OBJECTS = [
     ("ks_mfma.hip", [], "ks_mfma"),
     ("ks_bwd.hip", [], "ks_bwd"),
     ("ks_chain.hip", [], "ks_chain"),
+    ("vanloan.hip", [], "vanloan"),
     ("adam_l1.hip", [], "adam_l1"),
     ("head_ce.hip", [], "head_ce"),
 ]

@@ -482,6 +482,50 @@ int32_t ks_chain(int64_t N, int32_t nfactors, const ks_factor_t* factors, int32_
   return ok();
 }
 
+namespace {
+constexpr int kVlMaxSide = 8192;   // p*q and m*n (one workgroup orthonormalises a p*q or m*n column)
+
+int32_t van_loan_check(int32_t p, int32_t q, int32_t m, int32_t n, int32_t r, int32_t s, int32_t iters) {
+  if (p < 1 || q < 1 || m < 1 || n < 1) return fail(KRON_E_SHAPE, "p, q, m, n must be >= 1");
+  const int64_t M = (int64_t)p * q, K = (int64_t)m * n;
+  if (M > kVlMaxSide || K > kVlMaxSide)
+    return fail(KRON_E_UNSUPPORTED, "p*q = %lld or m*n = %lld exceeds %d", (long long)M, (long long)K, kVlMaxSide);
+  if ((int64_t)p * m > kMaxFeatures || (int64_t)q * n > kMaxFeatures)
+    return fail(KRON_E_UNSUPPORTED, "W of %lld x %lld exceeds %lld per side", (long long)p * m, (long long)q * n,
+                (long long)kMaxFeatures);
+  if (s < 1 || s > 32 || s > M || s > K) return fail(KRON_E_ARG, "s = %d outside 1..min(32, p*q, m*n)", s);
+  if (r < 1 || r > s) return fail(KRON_E_ARG, "r = %d outside 1..s", r);
+  if (iters < 0 || iters > 100) return fail(KRON_E_ARG, "iters = %d outside 0..100", iters);
+  return KRON_OK;
+}
+}  // namespace
+
+size_t kron_van_loan_workspace_bytes(int32_t p, int32_t q, int32_t m, int32_t n, int32_t s) {
+  if (van_loan_check(p, q, m, n, 1, s, 0) != KRON_OK) return 0;
+  return kron::van_loan_workspace_bytes(p, q, m, n, s);
+}
+
+int32_t kron_van_loan(int32_t p, int32_t q, int32_t m, int32_t n, int32_t r, int32_t s, int32_t iters, const float* W,
+                      const float* omega, float* C, float* B, float* sigma, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  int32_t st = van_loan_check(p, q, m, n, r, s, iters);
+  if (st != KRON_OK) return st;
+  if (!W || !omega || !C || !B || !sigma) return fail(KRON_E_NULL, "W, omega, C, B and sigma are required");
+  const size_t need = kron::van_loan_workspace_bytes(p, q, m, n, s);
+  if (!workspace || workspace_bytes < need)
+    return fail(KRON_E_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if (((uintptr_t)workspace & 255u) != 0) return fail(KRON_E_ALIGN, "workspace is not 256-byte aligned");
+  const size_t M = (size_t)p * q, K = (size_t)m * n;
+  const Range ins[3] = {{W, (size_t)p * m * q * n * 4, "W"}, {omega, K * s * 4, "omega"}, {workspace, need, "workspace"}};
+  const Range outs[3] = {{C, r * M * 4, "C"}, {B, r * K * 4, "B"}, {sigma, (size_t)r * 4, "sigma"}};
+  if ((st = check_align(ins, 3)) != KRON_OK || (st = check_align(outs, 3)) != KRON_OK) return st;
+  if ((st = check_alias(outs, 3, ins, 3)) != KRON_OK) return st;
+  kron::VanLoanArgs A{p, q, m, n, r, s, iters, W, omega, C, B, sigma};
+  hipError_t e = kron::launch_van_loan(A, workspace, stream);
+  if (e != hipSuccess) return hip_fail(e, "kron_van_loan launch");
+  return ok();
+}
+
 int32_t kron_adam_l1_step(int32_t ntensors, float* const* params, const float* const* grads, float* const* m,
                           float* const* v, const int64_t* numel, const float* l1, int64_t step, double lr,
                           double beta1, double beta2, double eps, hipStream_t stream) {

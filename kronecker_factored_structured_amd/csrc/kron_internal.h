@@ -163,6 +163,17 @@ struct ChainArgs {
 };
 int chain_rows_per_tile(int maxw);
 hipError_t launch_ks_chain(const ChainArgs& a, hipStream_t s);
+// Van Loan rank-r projection (vanloan.hip).
+struct VanLoanArgs {
+  int32_t p, q, m, n, r, s, iters;
+  const float* W;       // [p*m, q*n]
+  const float* omega;   // [m*n, s] starting block
+  float* C;             // [r, p, q]
+  float* B;             // [r, m, n]
+  float* sigma;         // [r]
+};
+size_t van_loan_workspace_bytes(int p, int q, int m, int n, int s);
+hipError_t launch_van_loan(const VanLoanArgs& a, void* workspace, hipStream_t s);
 bool ks_bwd_supported(int a, int b, int c, int d);
 size_t ks_bwd_workspace_bytes(int64_t N, int a, int b, int c, int d, int dtype);
 hipError_t launch_ks_bwd(const KSBwdArgs& k, void* workspace, hipStream_t s);

@@ -214,6 +214,26 @@ def test_ks_chain_argument_errors():
     assert L.ks_chain(0, 2, two, 0, None, None, None) == 0
 
 
+def test_van_loan_argument_errors():
+    L = _lib.lib()
+    MB = 1 << 20
+    need = L.kron_van_loan_workspace_bytes(32, 32, 32, 32, 12)
+    assert need > 0
+    assert L.kron_van_loan_workspace_bytes(32, 32, 32, 32, 33) == 0          # s > 32
+    assert L.kron_van_loan_workspace_bytes(128, 128, 4, 4, 12) == 0          # p*q > 8192
+    ok = lambda **kw: [kw.get("W", P(0)), kw.get("om", P(8 * MB)), kw.get("C", P(9 * MB)), kw.get("B", P(10 * MB)),
+                       kw.get("sig", P(11 * MB)), kw.get("ws", P(12 * MB)), ctypes.c_size_t(kw.get("bytes", need)), None]
+    assert L.kron_van_loan(32, 32, 32, 32, 4, 12, 8, *ok(W=None)) == _lib.KRON_E_NULL
+    assert L.kron_van_loan(0, 32, 32, 32, 4, 12, 8, *ok()) == _lib.KRON_E_SHAPE
+    assert L.kron_van_loan(32, 32, 32, 32, 13, 12, 8, *ok()) == _lib.KRON_E_ARG      # r > s
+    assert L.kron_van_loan(32, 32, 32, 32, 4, 12, 101, *ok()) == _lib.KRON_E_ARG     # iters
+    assert L.kron_van_loan(2, 2, 32, 32, 2, 5, 8, *ok()) == _lib.KRON_E_ARG          # s > p*q
+    assert L.kron_van_loan(32, 32, 32, 32, 4, 12, 8, *ok(bytes=need - 1)) == _lib.KRON_E_WORKSPACE
+    assert L.kron_van_loan(32, 32, 32, 32, 4, 12, 8, *ok(ws=P(12 * MB + 64))) == _lib.KRON_E_ALIGN
+    assert L.kron_van_loan(32, 32, 32, 32, 4, 12, 8, *ok(C=P(8))) == _lib.KRON_E_ALIGN
+    assert L.kron_van_loan(32, 32, 32, 32, 4, 12, 8, *ok(C=P(MB))) == _lib.KRON_E_ALIAS   # C over W
+
+
 def test_adam_argument_errors():
     L = _lib.lib()
     arr = ctypes.c_void_p * 1
