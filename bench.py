@@ -1,7 +1,7 @@
 """Benchmark of the Kronecker-factored layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--cpu-seconds 10]
-    python bench.py --workload {headline,headline_bf16,tiny,mlp_step,gpt2_ffn,ks,ks_bwd,chain,sweep}
+    python bench.py --workload {headline,headline_bf16,tiny,mlp_step,gpt2_ffn,ks,ks_bwd,chain,van_loan,sweep}
     python bench.py --calibrate-copy      (plain device copy of known size, for HBM counters)
 
 Default workload (one JSON line): one step is one kron_linear_fwd + one kron_linear_bwd
@@ -459,6 +459,29 @@ def run_chain(args, dev):
                           "bound": "hbm" if t_hbm >= t_flop else "fp32"}), flush=True)
 
 
+def run_van_loan(args, dev):
+    """Van Loan rank-4 projection of a 1024 x 1024 W onto 32x32 (x) 32x32 factors: block
+    subspace iteration of width 12, 8 power iterations.  Each iteration reads W twice
+    (R Q and R^T Z); 2 * (iters + 1) reads of W's 4 MB are the algorithmic bytes."""
+    import torch
+    import kronecker_factored_structured_amd as K
+    rng = np.random.default_rng(81)
+    W = torch.from_numpy(rng.standard_normal((1024, 1024)).astype(np.float32)).to(dev)
+    omega = torch.from_numpy(rng.standard_normal((1024, 12)).astype(np.float32)).to(dev)
+    ws = torch.empty(int(K._lib.lib().kron_van_loan_workspace_bytes(32, 32, 32, 32, 12)), dtype=torch.uint8, device=dev)
+    iters = 8
+    ms, _ = timed(lambda: K.kron_van_loan(W, 32, 32, 32, 32, 4, omega, iters=iters, workspace=ws),
+                  max(5, args.steps // 5), 2)
+    byts = 2 * (iters + 1) * 4 * 1024 * 1024
+    print(json.dumps({"workload": "van_loan: rank-4 projection of a 1024x1024 W, p=q=m=n=32, subspace 12, 8 iterations",
+                      "us_per_call": round(ms * 1e3, 2), "achieved_gbs": round(byts / (ms * 1e-3) / 1e9, 1),
+                      "t_roof_us": round(byts / (PEAK_HBM_GBS * 1e9) * 1e6, 2),
+                      "roofline_frac": round(byts / (PEAK_HBM_GBS * 1e9) / (ms * 1e-3), 4), "bound": "hbm",
+                      "limited_by": "latency: a dependent chain of 30 launches, the orthonormalisations and the "
+                                    "Jacobi eigensolve on one compute unit each"}),
+          flush=True)
+
+
 def run_sweep(args, dev):
     """Batch-size sweep of the 1024 x 1024 layer (the tutorial's comparison): the Kronecker
     layer's fwd+bwd against a dense layer and a dense layer with the group-LASSO penalty
@@ -531,7 +554,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="headline",
-                    choices=("headline", "headline_bf16", "tiny", "mlp_step", "gpt2_ffn", "ks", "ks_bwd", "chain", "sweep"))
+                    choices=("headline", "headline_bf16", "tiny", "mlp_step", "gpt2_ffn", "ks", "ks_bwd", "chain", "van_loan", "sweep"))
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed running before the warmup steps, for the GPU clock to ramp up")
@@ -548,7 +571,7 @@ def main():
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         return run_copy(args, dev)
-    {"headline": run_headline, "headline_bf16": run_headline_bf16, "tiny": run_tiny, "sweep": run_sweep, "ks_bwd": run_ks_bwd, "chain": run_chain, "mlp_step": run_mlp_step, "gpt2_ffn": run_gpt2,
+    {"headline": run_headline, "headline_bf16": run_headline_bf16, "tiny": run_tiny, "sweep": run_sweep, "ks_bwd": run_ks_bwd, "chain": run_chain, "van_loan": run_van_loan, "mlp_step": run_mlp_step, "gpt2_ffn": run_gpt2,
      "ks": run_ks}[args.workload](args, dev)
 
 

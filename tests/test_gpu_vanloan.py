@@ -82,3 +82,19 @@ def test_deterministic():
     b = run(W, 32, 32, 32, 32, 3, 8, 6)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_odd_sizes():
+    """Sides that are not multiples of 4 (scalar staging of the panels) and output tiles
+    that run past the end of the rows."""
+    rng = np.random.default_rng(84)
+    W = kron_sum(rng, 3, 5, 7, 3, [3.0, 1.5, 0.6, 0.2], noise=1e-3)
+    check(W, 3, 5, 7, 3, 2, 6, 12)
+
+
+def test_tall_panel():
+    """p*q = 4096 rows in the R side, above the 1024 that one workgroup holds in registers:
+    the panel is orthonormalised in memory."""
+    rng = np.random.default_rng(85)
+    W = kron_sum(rng, 64, 64, 8, 8, [4.0, 2.0, 1.0, 0.5, 0.25, 0.12], noise=1e-3)
+    check(W, 64, 64, 8, 8, 3, 10, 8)
