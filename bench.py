@@ -443,7 +443,7 @@ def run_chain(args, dev):
             (1, 32, 32, 32, rng.standard_normal((1, 32, 32, 32)) / np.sqrt(32))],
     }
     N = 20000
-    x = torch.randn(N, 1024, device=dev)
+    x = torch.from_numpy(rng.standard_normal((N, 1024)).astype(np.float32)).to(dev)
     y = torch.empty(N, 1024, device=dev)
     for name, fs in cases.items():
         tf = [(torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(dev), a, b, c, d) for (a, b, c, d, v) in fs]
