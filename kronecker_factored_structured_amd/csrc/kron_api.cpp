@@ -475,6 +475,7 @@ int32_t ks_chain(int64_t N, int32_t nfactors, const ks_factor_t* factors, int32_
   if ((st = check_alias(outs, 1, ins, nfactors + 1)) != KRON_OK) return st;
   if (N == 0) return ok();
   A.maxw = (int32_t)maxw;
+  A.wl = (int32_t)width;
   A.x = x;
   A.y = y;
   hipError_t e = kron::launch_ks_chain(A, stream);

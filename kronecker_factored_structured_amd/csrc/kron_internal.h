@@ -156,7 +156,7 @@ struct ChainFactor {
 };
 struct ChainArgs {
   int64_t N;
-  int32_t nf, dtype, maxw;
+  int32_t nf, dtype, maxw, wl;   // wl: width of the output rows
   ChainFactor f[kChainMaxFactors];
   const void* x;
   float* y;

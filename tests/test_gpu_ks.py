@@ -284,3 +284,40 @@ def test_ks_chain_ragged_and_rectangular(N):
     assert y.shape == (N, 7)
     if N:
         assert rel_err(y, want) <= TOL_F32
+
+
+@pytest.mark.parametrize("N", [1, 16, 37, 600])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ks_chain_matrix_core_ragged_blocks(N, dtype):
+    """Row widths that are multiples of 4 (the matrix-core chain) with b and c that are not
+    multiples of 4 or 16 (3, 5, 6, 60, 28: zero padding of the 16x16x4 tiles), b longer than
+    one chunk of beta steps (60), and a last row tile that is partly past N."""
+    rng = np.random.default_rng(63)
+    f1 = (4, 3, 5, 4, rng.standard_normal((4, 4, 3, 5)))      # 48 -> 80
+    f2 = (5, 8, 6, 2, rng.standard_normal((5, 2, 8, 6)))      # 80 -> 60
+    f3 = (1, 60, 28, 1, rng.standard_normal((1, 1, 60, 28)))  # 60 -> 28
+    x = rng.standard_normal((N, 48)).astype(np.float32)
+    y, want = _run_chain(x, [f1, f2, f3], dtype)
+    assert y.shape == (N, 28)
+    assert rel_err(y, want) <= TOL_F32   # bf16 inputs are exact in fp32; accumulation is fp32
+
+
+@pytest.mark.parametrize("N", [5, 77])
+@pytest.mark.parametrize("case", ["three", "two"])
+def test_ks_chain_register_layouts_partly_used(N, case):
+    """Chains that the register-resident kernels take with slots to spare: fewer tasks per
+    wavefront and fewer beta steps than the layout holds, and c = 4 (one quarter of a
+    16-column tile live)."""
+    rng = np.random.default_rng(64)
+    if case == "three":
+        fs = [(1, 4, 8, 64, rng.standard_normal((1, 64, 4, 8))),     # 256 -> 512
+              (8, 16, 8, 4, rng.standard_normal((8, 4, 16, 8))),     # 512 -> 256
+              (64, 4, 4, 1, rng.standard_normal((64, 1, 4, 4)))]     # 256 -> 256
+        w0 = 256
+    else:
+        fs = [(16, 32, 16, 1, rng.standard_normal((16, 1, 32, 16))),  # 512 -> 256
+              (1, 16, 32, 16, rng.standard_normal((1, 16, 16, 32)))]  # 256 -> 512
+        w0 = 512
+    x = rng.standard_normal((N, w0)).astype(np.float32)
+    y, want = _run_chain(x, fs)
+    assert rel_err(y, want) <= TOL_F32
