@@ -187,6 +187,83 @@ __global__ __launch_bounds__(1024) void ks_dv_mfma_kernel(int64_t N, int a, int 
       for (int v = 0; v < 4; ++v) out[((int64_t)de * B + 16 * t + 4 * g + v) * c + 16 * w + cl] = acc[t][de][v];
 }
 
+// bf16 inputs on bf16 matrix instructions (v_mfma_f32_16x16x16_bf16): the contraction is
+// over rows, 16 per instruction; lane group g takes rows 16s + 4g + u (u < 4).  A lane loads,
+// for each of its four rows, the four delta values of its beta (and of its gamma) as one
+// 8-byte piece, and regroups the 4 rows x 4 deltas into one operand per delta with byte
+// permutes.  Same partial rows as the fp32 kernel.
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+
+// 4 rows x 4 deltas (row-major pieces) -> op[de] = {rows 0..3 of delta de}
+__device__ __forceinline__ void split_rows(const uint2 (&r)[4], s4 (&op)[4]) {
+  const unsigned LO = 0x05040100u, HI = 0x07060302u;
+  op[0] = __builtin_bit_cast(s4, (u2v{__builtin_amdgcn_perm(r[1].x, r[0].x, LO), __builtin_amdgcn_perm(r[3].x, r[2].x, LO)}));
+  op[1] = __builtin_bit_cast(s4, (u2v{__builtin_amdgcn_perm(r[1].x, r[0].x, HI), __builtin_amdgcn_perm(r[3].x, r[2].x, HI)}));
+  op[2] = __builtin_bit_cast(s4, (u2v{__builtin_amdgcn_perm(r[1].y, r[0].y, LO), __builtin_amdgcn_perm(r[3].y, r[2].y, LO)}));
+  op[3] = __builtin_bit_cast(s4, (u2v{__builtin_amdgcn_perm(r[1].y, r[0].y, HI), __builtin_amdgcn_perm(r[3].y, r[2].y, HI)}));
+}
+
+constexpr int kDv16MaxWaves = 12;   // gamma tiles (c <= 192): 768 threads leave 168 VGPRs a lane
+
+template <int TB>
+__global__ __launch_bounds__(64 * kDv16MaxWaves) void ks_dv_mfma16_kernel(int64_t N, int a, int c, int64_t Gr,
+                                                            const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ dy, float* __restrict__ part) {
+  constexpr int B = 16 * TB;
+  const int lane = threadIdx.x & 63, g = lane >> 4, cl = lane & 15, w = threadIdx.x >> 6;
+  const int al = blockIdx.x % a;
+  const int64_t chunk = blockIdx.x / a;
+  const int64_t in_w = (int64_t)a * B * 4, out_w = (int64_t)a * c * 4;
+  const int64_t per = ((N + Gr - 1) / Gr + 15) / 16 * 16, r0 = chunk * per;
+  const int64_t r1 = r0 + per < N ? r0 + per : N;
+  const uint16_t* xb = x + ((int64_t)al * B + cl) * 4;
+  const uint16_t* yb = dy + ((int64_t)al * c + 16 * w + cl) * 4;
+  f4 acc[TB][4];
+#pragma unroll
+  for (int t = 0; t < TB; ++t)
+#pragma unroll
+    for (int de = 0; de < 4; ++de) acc[t][de] = f4{0.f, 0.f, 0.f, 0.f};
+  uint2 xn[TB][4], yn[4];
+  auto load = [&](int64_t row0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t row = row0 + 4 * g + u;
+      const bool ok = row < r1;
+      const int64_t rr = ok ? row : 0;
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        const uint2 v = *reinterpret_cast<const uint2*>(xb + rr * in_w + 64 * t);
+        xn[t][u] = ok ? v : uint2{0u, 0u};
+      }
+      const uint2 v = *reinterpret_cast<const uint2*>(yb + rr * out_w);
+      yn[u] = ok ? v : uint2{0u, 0u};
+    }
+  };
+  if (r0 < r1) load(r0);
+  for (int64_t row = r0; row < r1; row += 16) {
+    s4 yo[4], xo[TB][4];   // this step's operands, formed before the next step's loads reuse xn, yn
+    split_rows(yn, yo);
+#pragma unroll
+    for (int t = 0; t < TB; ++t) split_rows(xn[t], xo[t]);
+    load(row + 16);
+#pragma unroll
+    for (int t = 0; t < TB; ++t)
+#pragma unroll
+      for (int de = 0; de < 4; ++de)
+        acc[t][de] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xo[t][de], yo[de], acc[t][de], 0, 0, 0);
+  }
+  // acc[t][de] register v = dvals[al][de][be = 16t + 4g + v][ga = 16w + cl]
+  const PartRow out{part, Gr, chunk, (int64_t)al * 4 * B * c};
+#pragma unroll
+  for (int de = 0; de < 4; ++de)
+#pragma unroll
+    for (int t = 0; t < TB; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) out[((int64_t)de * B + 16 * t + 4 * g + v) * c + 16 * w + cl] = acc[t][de][v];
+}
+
 bool dv_mfma_ok(int a, int b, int c, int d) {
   (void)a;
   return d == 4 && b % 16 == 0 && b / 16 >= 1 && b / 16 <= 4 && c % 16 == 0 && c / 16 >= 1 && c / 16 <= 16;
@@ -201,6 +278,9 @@ void launch_dv_mfma(const KSBwdArgs& k, int64_t Gr, dim3 grid, dim3 block, float
   if (k.dtype == KRON_F32)
     hipLaunchKernelGGL((ks_dv_mfma_kernel<TB, float>), grid, block, 0, s, k.N, k.a, k.c, Gr, (const float*)k.x,
                        (const float*)k.dy, part);
+  else if (k.c / 16 <= kDv16MaxWaves)
+    hipLaunchKernelGGL((ks_dv_mfma16_kernel<TB>), grid, block, 0, s, k.N, k.a, k.c, Gr, (const uint16_t*)k.x,
+                       (const uint16_t*)k.dy, part);
   else
     hipLaunchKernelGGL((ks_dv_mfma_kernel<TB, uint16_t>), grid, block, 0, s, k.N, k.a, k.c, Gr,
                        (const uint16_t*)k.x, (const uint16_t*)k.dy, part);

@@ -450,20 +450,263 @@ __global__ __launch_bounds__((KVK<B_, C_>::NT)) void ks_vregk_kernel(int64_t N, 
   }
 }
 
+// ---------------------------------------------------------------------------------
+// bf16 inputs, d = 4: the same two kernels on bf16 matrix instructions
+// (v_mfma_f32_16x16x16_bf16, fp32 accumulation).  Rows stay bf16 in LDS.  A K step covers
+// 16 beta values; lane group g takes beta = 16s + 4g + u (u < 4) in both operands.  A lane
+// reads its 4 beta x 4 delta values of a row as 32 contiguous bytes and regroups them into
+// one 4-value operand per delta with byte permutes; its V operands (4 beta of one gamma, per
+// delta and step) sit in registers as packed bf16.
+// ---------------------------------------------------------------------------------
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f4 mfma16(s4 a, s4 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0); }
+
+// 4 beta x 4 delta bf16 (beta-major, as in a row) -> op[de] = {beta 0..3 of delta de}
+__device__ __forceinline__ void split_deltas(u4v lo, u4v hi, s4 (&op)[4]) {
+  // words: lo = beta0 (d0d1, d2d3), beta1 (d0d1, d2d3); hi = beta2, beta3
+  const unsigned LO = 0x05040100u, HI = 0x07060302u;   // low / high halves of (S1, S0)
+  op[0] = __builtin_bit_cast(s4, (u2v{__builtin_amdgcn_perm(lo[2], lo[0], LO), __builtin_amdgcn_perm(hi[2], hi[0], LO)}));
+  op[1] = __builtin_bit_cast(s4, (u2v{__builtin_amdgcn_perm(lo[2], lo[0], HI), __builtin_amdgcn_perm(hi[2], hi[0], HI)}));
+  op[2] = __builtin_bit_cast(s4, (u2v{__builtin_amdgcn_perm(lo[3], lo[1], LO), __builtin_amdgcn_perm(hi[3], hi[1], LO)}));
+  op[3] = __builtin_bit_cast(s4, (u2v{__builtin_amdgcn_perm(lo[3], lo[1], HI), __builtin_amdgcn_perm(hi[3], hi[1], HI)}));
+}
+
+__device__ __forceinline__ s4 vals4(const uint16_t* p, int stride) {   // 4 bf16 at p, p + stride, ...
+  return s4{(short)p[0], (short)p[stride], (short)p[2 * stride], (short)p[3 * stride]};
+}
+
+template <int B_>
+struct Row16 {
+  static constexpr int ROWE = 4 * B_;                        // bf16 of one row's alpha slab
+  static constexpr int LXB = (ROWE * 2 + 127) / 128 * 128 + 64;   // row pitch in bytes: /4 = 16 mod 32
+  static constexpr int TILEB = 16 * LXB;
+  static constexpr int NU2 = ROWE / 4;                        // 8-byte pieces per row
+};
+
+template <int B_, int C_>
+struct KV16 {
+  static constexpr int NW = C_ / 16, NT = 64 * NW;
+  static constexpr int SK = B_ / 16;                          // K steps
+  using R = Row16<B_>;
+  static constexpr int NP = 16 * R::NU2;                      // pieces per row tile
+  static constexpr int NPF = (NP + NT - 1) / NT;
+  static constexpr size_t LDS = (size_t)2 * R::TILEB;
+  static constexpr bool OK = B_ % 16 == 0 && C_ % 16 == 0 && NW >= 1 && NW <= 16 && LDS <= kMaxLds;
+};
+
+template <int B_, int C_, class TOut>
+__global__ __launch_bounds__((KV16<B_, C_>::NT)) void ks_vreg16_kernel(int64_t N, int a_count,
+                                                                     const uint16_t* __restrict__ x,
+                                                                     const uint16_t* __restrict__ vals,
+                                                                     TOut* __restrict__ y) {
+  using K = KV16<B_, C_>;
+  using R = typename K::R;
+  extern __shared__ float lds[];
+  unsigned char* lb = reinterpret_cast<unsigned char*>(lds);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15, w = tid >> 6;
+  const int al = blockIdx.x % a_count;
+  const int64_t step = gridDim.x / a_count;
+  const int64_t ntile = (N + 15) / 16, nfull = N / 16;
+  const int64_t in_w = (int64_t)a_count * R::ROWE, out_w = (int64_t)a_count * C_ * 4;
+  const uint16_t* xa = x + (int64_t)al * R::ROWE;
+  TOut* ya = y + ((int64_t)al * C_ + 16 * w + c) * 4;
+
+  uint2 pf[K::NPF];
+  auto fetch = [&](int64_t tile) {
+#pragma unroll
+    for (int t = 0; t < K::NPF; ++t) {
+      const int f = tid + t * K::NT;
+      uint2 v = {0u, 0u};
+      if (K::NP % K::NT == 0 || f < K::NP) {
+        const int r = f / R::NU2, o = 4 * (f % R::NU2);
+        const int64_t row = tile * 16 + r;
+        if (tile < ntile && row < N) v = *reinterpret_cast<const uint2*>(xa + row * in_w + o);
+      }
+      pf[t] = v;
+    }
+  };
+  auto stash = [&](unsigned char* buf) {
+#pragma unroll
+    for (int t = 0; t < K::NPF; ++t) {
+      const int f = tid + t * K::NT;
+      if (K::NP % K::NT == 0 || f < K::NP) {
+        const int r = f / R::NU2, o = 4 * (f % R::NU2);
+        *reinterpret_cast<uint2*>(buf + r * R::LXB + 2 * o) = pf[t];
+      }
+    }
+  };
+
+  int64_t tile = blockIdx.x / a_count;
+  fetch(tile);
+  s4 v[4][K::SK];   // V[al][de][16s + 4g + u][16w + c], u = 0..3
+  const uint16_t* V = vals + (int64_t)al * 4 * B_ * C_;
+#pragma unroll
+  for (int de = 0; de < 4; ++de)
+#pragma unroll
+    for (int s = 0; s < K::SK; ++s) v[de][s] = vals4(V + ((int64_t)de * B_ + 16 * s + 4 * g) * C_ + 16 * w + c, C_);
+  stash(lb);
+  fetch(tile + step);
+  __syncthreads();
+
+  auto compute = [&](const unsigned char* xs, f4 (&acc)[4]) {
+#pragma unroll
+    for (int de = 0; de < 4; ++de) acc[de] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < K::SK; ++s) {
+      const unsigned char* p = xs + c * R::LXB + (16 * s + 4 * g) * 8;
+      s4 op[4];
+      split_deltas(*reinterpret_cast<const u4v*>(p), *reinterpret_cast<const u4v*>(p + 16), op);
+#pragma unroll
+      for (int de = 0; de < 4; ++de) acc[de] = mfma16(op[de], v[de][s], acc[de]);
+    }
+  };
+  int it = 0;
+  for (; tile < nfull; tile += step, ++it) {
+    f4 acc[4];
+    compute(lb + (it & 1) * R::TILEB, acc);
+#pragma unroll
+    for (int vv = 0; vv < 4; ++vv)
+      store4(ya + (tile * 16 + 4 * g + vv) * out_w, f4{acc[0][vv], acc[1][vv], acc[2][vv], acc[3][vv]});
+    stash(lb + ((it + 1) & 1) * R::TILEB);
+    fetch(tile + 2 * step);
+    __syncthreads();
+  }
+  if (tile < ntile) {
+    f4 acc[4];
+    compute(lb + (it & 1) * R::TILEB, acc);
+#pragma unroll
+    for (int vv = 0; vv < 4; ++vv) {
+      const int64_t row = tile * 16 + 4 * g + vv;
+      if (row < N) store4(ya + row * out_w, f4{acc[0][vv], acc[1][vv], acc[2][vv], acc[3][vv]});
+    }
+  }
+}
+
+// The split-contraction kernel on bf16: quarter kq of a gamma tile takes beta in
+// [kq*B/4, (kq+1)*B/4), K steps of 16 inside it.
+template <int B_, int C_>
+struct KVK16 {
+  static constexpr int KSP = 4;
+  static constexpr int NWG = C_ / 16;
+  static constexpr int NW = NWG * KSP, NT = 64 * NW;
+  static constexpr int QB = B_ / KSP, SKQ = QB / 16;         // beta per quarter, K steps per quarter
+  using R = Row16<B_>;
+  static constexpr int NP = 16 * R::NU2;
+  static constexpr int NPF = (NP + NT - 1) / NT;
+  static constexpr int RED = NW * 64 * 16;                    // floats
+  static constexpr size_t LDS = (size_t)2 * R::TILEB + (size_t)RED * 4;
+  static constexpr bool OK = B_ % (16 * KSP) == 0 && C_ % 16 == 0 && NW <= 16 && LDS <= kMaxLds;
+};
+
+template <int B_, int C_, class TOut>
+__global__ __launch_bounds__((KVK16<B_, C_>::NT)) void ks_vregk16_kernel(int64_t N, int a_count,
+                                                                       const uint16_t* __restrict__ x,
+                                                                       const uint16_t* __restrict__ vals,
+                                                                       TOut* __restrict__ y) {
+  using K = KVK16<B_, C_>;
+  using R = typename K::R;
+  extern __shared__ float lds[];
+  unsigned char* lb = reinterpret_cast<unsigned char*>(lds);
+  f4* red = reinterpret_cast<f4*>(lb + 2 * R::TILEB);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15, wv = tid >> 6;
+  const int gt = wv % K::NWG, kq = wv / K::NWG;
+  const int al = blockIdx.x % a_count;
+  const int64_t step = gridDim.x / a_count;
+  const int64_t ntile = (N + 15) / 16, nfull = N / 16;
+  const int64_t in_w = (int64_t)a_count * R::ROWE, out_w = (int64_t)a_count * C_ * 4;
+  const uint16_t* xa = x + (int64_t)al * R::ROWE;
+  TOut* ya = y + ((int64_t)al * C_ + 16 * gt + c) * 4;
+
+  uint2 pf[K::NPF];
+  auto fetch = [&](int64_t tile) {
+#pragma unroll
+    for (int t = 0; t < K::NPF; ++t) {
+      const int f = tid + t * K::NT;
+      uint2 v = {0u, 0u};
+      if (K::NP % K::NT == 0 || f < K::NP) {
+        const int r = f / R::NU2, o = 4 * (f % R::NU2);
+        const int64_t row = tile * 16 + r;
+        if (tile < ntile && row < N) v = *reinterpret_cast<const uint2*>(xa + row * in_w + o);
+      }
+      pf[t] = v;
+    }
+  };
+  auto stash = [&](unsigned char* buf) {
+#pragma unroll
+    for (int t = 0; t < K::NPF; ++t) {
+      const int f = tid + t * K::NT;
+      if (K::NP % K::NT == 0 || f < K::NP) {
+        const int r = f / R::NU2, o = 4 * (f % R::NU2);
+        *reinterpret_cast<uint2*>(buf + r * R::LXB + 2 * o) = pf[t];
+      }
+    }
+  };
+
+  int64_t tile = blockIdx.x / a_count;
+  fetch(tile);
+  s4 v[4][K::SKQ];   // V[al][de][kq*QB + 16s + 4g + u][16gt + c]
+  const uint16_t* V = vals + (int64_t)al * 4 * B_ * C_;
+#pragma unroll
+  for (int de = 0; de < 4; ++de)
+#pragma unroll
+    for (int s = 0; s < K::SKQ; ++s)
+      v[de][s] = vals4(V + ((int64_t)de * B_ + kq * K::QB + 16 * s + 4 * g) * C_ + 16 * gt + c, C_);
+  stash(lb);
+  fetch(tile + step);
+  __syncthreads();
+
+  auto compute_and_reduce = [&](const unsigned char* xs) {
+    f4 acc[4];
+#pragma unroll
+    for (int de = 0; de < 4; ++de) acc[de] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < K::SKQ; ++s) {
+      const unsigned char* p = xs + c * R::LXB + (kq * K::QB + 16 * s + 4 * g) * 8;
+      s4 op[4];
+      split_deltas(*reinterpret_cast<const u4v*>(p), *reinterpret_cast<const u4v*>(p + 16), op);
+#pragma unroll
+      for (int de = 0; de < 4; ++de) acc[de] = mfma16(op[de], v[de][s], acc[de]);
+    }
+#pragma unroll
+    for (int vv = 0; vv < 4; ++vv) red[(wv * 64 + lane) * 4 + vv] = f4{acc[0][vv], acc[1][vv], acc[2][vv], acc[3][vv]};
+    __syncthreads();
+    f4 sum = red[((0 * K::NWG + gt) * 64 + lane) * 4 + kq];
+#pragma unroll
+    for (int q = 1; q < K::KSP; ++q) sum += red[((q * K::NWG + gt) * 64 + lane) * 4 + kq];
+    return sum;
+  };
+  int it = 0;
+  for (; tile < nfull; tile += step, ++it) {
+    const f4 o = compute_and_reduce(lb + (it & 1) * R::TILEB);
+    store4(ya + (tile * 16 + 4 * g + kq) * out_w, o);
+    stash(lb + ((it + 1) & 1) * R::TILEB);
+    fetch(tile + 2 * step);
+    __syncthreads();
+  }
+  if (tile < ntile) {
+    const f4 o = compute_and_reduce(lb + (it & 1) * R::TILEB);
+    const int64_t row = tile * 16 + 4 * g + kq;
+    if (row < N) store4(ya + row * out_w, o);
+  }
+}
+
 struct KvkEntry {
   int b, c;
-  size_t lds;
+  size_t lds[2];          // [x and vals bf16]
   int nt;
   const void* fn[2][2];   // [x and vals bf16][y bf16]
 };
 #define KVK_ENTRY(B, C)                                                                                   \
-  KvkEntry{B, C, KVK<B, C>::LDS, KVK<B, C>::NT,                                                           \
+  KvkEntry{B, C, {KVK<B, C>::LDS, KVK16<B, C>::LDS}, KVK<B, C>::NT,                                        \
            {{(const void*)&ks_vregk_kernel<B, C, float, float>, (const void*)&ks_vregk_kernel<B, C, float, uint16_t>}, \
-            {(const void*)&ks_vregk_kernel<B, C, uint16_t, float>,                                        \
-             (const void*)&ks_vregk_kernel<B, C, uint16_t, uint16_t>}}}
+            {(const void*)&ks_vregk16_kernel<B, C, float>, (const void*)&ks_vregk16_kernel<B, C, uint16_t>}}}
 // d = 4 shapes with the contraction split: the transposed ViT-S/16 MLP pattern (192, 48).
 const KvkEntry kKvkTable[] = {KVK_ENTRY(192, 48)};
-static_assert(KVK<192, 48>::OK, "the split-contraction KS shape fits the LDS");
+static_assert(KVK<192, 48>::OK && KVK16<192, 48>::OK && KVK16<192, 48>::NT == KVK<192, 48>::NT,
+              "the split-contraction KS shape fits the LDS");
 
 struct KsEntry {
   int b, c, d;
@@ -500,19 +743,20 @@ int device_cus_ks() {
 
 struct KvEntry {
   int b, c, gs;
-  size_t lds;
+  size_t lds[2];          // [x and vals bf16]
   int nt;
   const void* fn[2][2];   // [x and vals bf16][y bf16]
 };
-#define KV_ENTRY(B, C, GS)                                                                                        \
-  KvEntry{B, C, GS, KV<B, C, GS>::LDS, KV<B, C, GS>::NT,                                                          \
-          {{(const void*)&ks_vreg_kernel<B, C, GS, float, float>, (const void*)&ks_vreg_kernel<B, C, GS, float, uint16_t>}, \
-           {(const void*)&ks_vreg_kernel<B, C, GS, uint16_t, float>,                                             \
-            (const void*)&ks_vreg_kernel<B, C, GS, uint16_t, uint16_t>}}}
+// bf16 inputs run on bf16 matrix instructions (one workgroup per row tile, GS = 1)
+#define KV_ENTRY(B, C)                                                                                            \
+  KvEntry{B, C, 1, {KV<B, C, 1>::LDS, KV16<B, C>::LDS}, KV<B, C, 1>::NT,                                          \
+          {{(const void*)&ks_vreg_kernel<B, C, 1, float, float>, (const void*)&ks_vreg_kernel<B, C, 1, float, uint16_t>}, \
+           {(const void*)&ks_vreg16_kernel<B, C, float>, (const void*)&ks_vreg16_kernel<B, C, uint16_t>}}}
 // d = 4 shapes with V in registers: the ViT-S/16 MLP pattern (b, c) = (48, 192), one
 // workgroup per row tile (splitting the gamma tiles over two or three workgroups was
 // measured no faster).
-const KvEntry kKvTable[] = {KV_ENTRY(48, 192, 1)};
+const KvEntry kKvTable[] = {KV_ENTRY(48, 192)};
+static_assert(KV16<48, 192>::OK && KV16<48, 192>::NT == KV<48, 192, 1>::NT, "the bf16 register KS shape fits");
 
 const KvEntry* kv_find(int b, int c, int d) {
   if (d != 4) return nullptr;
@@ -530,9 +774,10 @@ const KvkEntry* kvk_find(int b, int c, int d) {
 
 hipError_t launch_ks_vregk(const KvkEntry* e, const KSArgs& k, hipStream_t s) {
   const void* fn = e->fn[k.dtype == KRON_BF16][k.out_dtype == KRON_BF16];
-  (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)e->lds);
+  const size_t lds = e->lds[k.dtype == KRON_BF16];
+  (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   int per_cu = 1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, e->nt, e->lds) != hipSuccess || per_cu < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, e->nt, lds) != hipSuccess || per_cu < 1)
     per_cu = 1;
   int64_t per_alpha = (int64_t)per_cu * device_cus_ks() / k.a;
   if (per_alpha < 1) per_alpha = 1;
@@ -540,14 +785,15 @@ hipError_t launch_ks_vregk(const KvkEntry* e, const KSArgs& k, hipStream_t s) {
   if (per_alpha > tiles) per_alpha = tiles;
   const int grid = (int)(per_alpha * k.a);
   void* args[] = {(void*)&k.N, (void*)&k.a, (void*)&k.x, (void*)&k.vals, (void*)&k.y};
-  return hipLaunchKernel(fn, dim3(grid), dim3(e->nt), args, e->lds, s);
+  return hipLaunchKernel(fn, dim3(grid), dim3(e->nt), args, lds, s);
 }
 
 hipError_t launch_ks_vreg(const KvEntry* e, const KSArgs& k, hipStream_t s) {
   const void* fn = e->fn[k.dtype == KRON_BF16][k.out_dtype == KRON_BF16];
-  (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)e->lds);
+  const size_t lds = e->lds[k.dtype == KRON_BF16];
+  (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   int per_cu = 1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, e->nt, e->lds) != hipSuccess || per_cu < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, e->nt, lds) != hipSuccess || per_cu < 1)
     per_cu = 1;
   // workgroups per (alpha, gamma share): as many as fit, and no more than the row tiles
   int64_t per_share = (int64_t)per_cu * device_cus_ks() / (k.a * e->gs);
@@ -556,7 +802,7 @@ hipError_t launch_ks_vreg(const KvEntry* e, const KSArgs& k, hipStream_t s) {
   if (per_share > tiles) per_share = tiles;
   const int grid = (int)(per_share * k.a * e->gs);
   void* args[] = {(void*)&k.N, (void*)&k.a, (void*)&k.x, (void*)&k.vals, (void*)&k.y};
-  return hipLaunchKernel(fn, dim3(grid), dim3(e->nt), args, e->lds, s);
+  return hipLaunchKernel(fn, dim3(grid), dim3(e->nt), args, lds, s);
 }
 
 }  // namespace

@@ -321,3 +321,36 @@ def test_ks_chain_register_layouts_partly_used(N, case):
     x = rng.standard_normal((N, w0)).astype(np.float32)
     y, want = _run_chain(x, fs)
     assert rel_err(y, want) <= TOL_F32
+
+
+@pytest.mark.parametrize("N", [1, 17, 1000])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_bf16_vit_shape_ragged_rows(N, out_dtype):
+    """bf16 inputs at the ViT shape (bf16 matrix instructions) with row counts that leave a
+    partial 16-row tile, fp32 and bf16 outputs."""
+    inp = ks_inputs(48, N, 2, 48, 192, 4, "bf16")
+    x, v = _ks_dev_inputs(inp)
+    od = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    y = K().ks_matmul_out(x, v, 2, 48, 192, 4, out_dtype=od)
+    torch.cuda.synchronize()
+    want = OKS.matmul(inp.x, inp.vals, 2, 48, 192, 4)
+    if out_dtype == "f32":
+        assert rel_err(host(y), want) <= TOL_F32
+    else:
+        from workloads import bf16_to_f32
+        assert rel_err(bf16_to_f32(_bf16_host(y)).astype(np.float64), want) <= TOL_BF16
+
+
+@pytest.mark.parametrize("N", [1, 37, 300])
+@pytest.mark.parametrize("abcd", [(2, 48, 192, 4), (1, 16, 32, 4), (2, 32, 48, 4), (1, 64, 16, 4), (1, 16, 256, 4)])
+def test_ks_backward_bf16_shapes_and_ragged_rows(abcd, N):
+    """bf16 inputs: dvals on bf16 matrix instructions for each number of 16-wide beta tiles
+    (b = 16 .. 64), the fp32-instruction kernel for c = 256 (more gamma tiles than the bf16
+    kernel's workgroup holds), dx through the bf16 split-contraction kernel at the ViT shape;
+    row counts that end inside a 16-row step."""
+    a, b, c, d = abcd
+    inp = ks_inputs(49, N, a, b, c, d, "bf16")
+    dy64 = np.random.default_rng(53).standard_normal((N, a * c * d))
+    g, want = _ks_bwd_case(inp, dy64)
+    assert rel_err(host(g["dx"]), want["dx"]) <= TOL_F32
+    assert rel_err(host(g["dvals"]), want["dvals"]) <= TOL_F32
