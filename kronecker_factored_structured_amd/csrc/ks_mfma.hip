@@ -10,7 +10,8 @@
 // No permutation pass exists: the interleave is absorbed by which accumulator a product
 // goes to.  Products are 16x16x4 fp32 MFMAs; bf16 inputs are widened to fp32 on load
 // (a bf16 x bf16 product is exact in fp32, so only the accumulation order differs from a
-// bf16 matrix instruction).
+// bf16 matrix instruction), except in the d = 4 register kernels, whose bf16 twins run
+// 16x16x16 bf16 MFMAs.
 //
 // Two kernels.  For d = 4 (ks_vreg_kernel, below) each wavefront keeps its slice of V in
 // registers and only rows pass through LDS.  For the other shapes of the table
