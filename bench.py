@@ -121,6 +121,7 @@ def cpu_baseline(inp, seconds: float):
             break
     dt = time.perf_counter() - t0
     return {"value": rows / dt, "unit": "rows/s", "cores": int(cpu_threads()), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{calls} x (fwd+bwd over all {N} rows of the same workload), fp64 numpy/OpenBLAS, "
                       f"{dt:.1f} s"}
 
@@ -186,8 +187,62 @@ class LayerBf16:
         self.K.kron_linear_bwd_bf16(self.x, self.S, self.A, self.B, self.dy, workspace=self.ws, outs=self.outs)
 
 
-def split_times(layer, steps):
-    """Mean seconds of the forward and of the backward call, from events around each call."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def measured_ceilings(dev):
+    """Context for the roofline fractions, measured on this GPU outside the timed region:
+    a 1 GiB device copy (read + write bytes per second) and a large fp32 GEMM through the
+    vendor library (matrix-core throughput without the layer's structure)."""
+    import torch
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    nb = 1 << 30
+    a = torch.empty(nb // 4, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = ev(), ev()
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * nb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    n = 8192
+    allow = torch.backends.cuda.matmul.allow_tf32
+    torch.backends.cuda.matmul.allow_tf32 = False
+    A = torch.randn(n, n, device=dev)
+    B = torch.randn(n, n, device=dev)
+    C = torch.empty(n, n, device=dev)
+    for _ in range(2):
+        torch.mm(A, B, out=C)
+    e0, e1 = ev(), ev()
+    e0.record()
+    for _ in range(5):
+        torch.mm(A, B, out=C)
+    e1.record()
+    torch.cuda.synchronize()
+    torch.backends.cuda.matmul.allow_tf32 = allow
+    gemm_tflops = 2 * n ** 3 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del A, B, C
+    torch.cuda.empty_cache()
+    return {"copy_gbs": round(copy_gbs, 1), "fp32_gemm_tflops": round(gemm_tflops, 2),
+            "how": "1 GiB torch device copy x10 (read+write bytes); torch.mm fp32 8192^3 x5, TF32 off"}
+
+
+def split_times(layer, steps, medians=False):
+    """Mean seconds of the forward and of the backward call, from events around each call
+    (and their medians, and the median of their sum, when asked)."""
     import torch
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -199,8 +254,11 @@ def split_times(layer, steps):
         layer.bwd()
         c.record()
     torch.cuda.synchronize()
-    t_fwd = float(np.mean([a.elapsed_time(b) for a, b, _ in ev])) * 1e-3
-    t_bwd = float(np.mean([b.elapsed_time(c) for _, b, c in ev])) * 1e-3
+    f = np.array([a.elapsed_time(b) for a, b, _ in ev]) * 1e-3
+    g = np.array([b.elapsed_time(c) for _, b, c in ev]) * 1e-3
+    t_fwd, t_bwd = float(np.mean(f)), float(np.mean(g))
+    if medians:
+        return t_fwd, t_bwd, float(np.median(f)), float(np.median(g)), float(np.median(f + g))
     return t_fwd, t_bwd
 
 
@@ -213,7 +271,7 @@ def run_headline(args, dev):
     L = Layer(inp, dev)
     log(f"[bench] headline: warmup {args.warmup}, timing {args.steps} steps")
     ms_step, wall_ms = timed(lambda: (L.fwd(), L.bwd()), args.steps, args.warmup)
-    t_fwd, t_bwd = split_times(L, args.steps)
+    t_fwd, t_bwd, med_fwd, med_bwd, med_step = split_times(L, args.steps, medians=True)
     ff, fb, bf, bb = work_per_row(p, q, m, n, r, nnz)
     t_roof = max(N * (ff + fb) / (PEAK_FP32_TFLOPS * 1e12), N * (bf + bb) / (PEAK_HBM_GBS * 1e9))
     achieved = N * fb / t_bwd / 1e12
@@ -237,10 +295,18 @@ def run_headline(args, dev):
                           "t_us": round(ms_step * 1e3, 2), "frac": round(t_roof / (ms_step * 1e-3), 4),
                           "effective_tflops": round(N * (ff + fb) / (ms_step * 1e-3) / 1e12, 3)},
         "t_fwd_us": round(t_fwd * 1e6, 2), "t_bwd_us": round(t_bwd * 1e6, 2),
+        "median_us": {"fwd": round(med_fwd * 1e6, 2), "bwd": round(med_bwd * 1e6, 2),
+                      "fwd_bwd": round(med_step * 1e6, 2)},
         "wall_ms_per_step": round(wall_ms, 5),
         "kernel_source_sha": kernel_source_sha(),
         "settle_seconds": args.settle_seconds,
     }
+    if not args.no_ceilings:
+        log("[bench] measured ceilings (copy, fp32 GEMM)")
+        ceil = measured_ceilings(dev)
+        ceil["bwd_frac_of_gemm"] = round(achieved / ceil["fp32_gemm_tflops"], 4)
+        ceil["pass_frac_of_gemm"] = round(N * (ff + fb) / (ms_step * 1e-3) / 1e12 / ceil["fp32_gemm_tflops"], 4)
+        rec["measured_ceilings"] = ceil
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (oracle) for ~{args.cpu_seconds} s")
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
@@ -252,7 +318,7 @@ def layer_record(name, inp, L, args, extra=None):
     N, p, q, m, n, r = sh.N, sh.p, sh.q, sh.m, sh.n, sh.r
     nnz = p * q if inp.S is None else int(np.count_nonzero(inp.S))
     ms, _ = timed(lambda: (L.fwd(), L.bwd()), args.steps, args.warmup)
-    t_fwd, t_bwd = split_times(L, args.steps)
+    t_fwd, t_bwd, med_fwd, med_bwd, med_step = split_times(L, args.steps, medians=True)
     ff, fb, bf, bb = work_per_row(p, q, m, n, r, nnz)
     if inp.S is None:   # dense factors: the cheaper association of each product counts
         ff = 2 * r * min(p * n * (m + q), q * m * (p + n))
@@ -553,6 +619,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the copy and GEMM ceiling measurements")
     ap.add_argument("--workload", default="headline",
                     choices=("headline", "headline_bf16", "tiny", "mlp_step", "gpt2_ffn", "ks", "ks_bwd", "chain", "van_loan", "sweep"))
     ap.add_argument("--calibrate-copy", action="store_true")
