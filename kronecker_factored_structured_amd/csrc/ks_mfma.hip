@@ -249,6 +249,27 @@ __device__ __forceinline__ f4 widen4(uint2 v) {
             __uint_as_float(v.y & 0xffff0000u)};
 }
 
+// Wait, before a row-tile loop, for the registers loaded ahead of it (V and the first
+// prefetch).  The loop issues each prefetch before its tile's stores, so on the back edge a
+// prefetch can be waited for while the stores stay in flight; without this wait the loop
+// head would merge that state with the preheader's (loads outstanding) and wait for every
+// store of the previous tile.
+__device__ __forceinline__ void settle1(float v) { asm volatile("" ::"v"(v)); }
+__device__ __forceinline__ void settle1(f4 v) { asm volatile("" ::"v"(v)); }
+__device__ __forceinline__ void settle1(uint2 v) { asm volatile("" ::"v"(v.x), "v"(v.y)); }
+typedef short s4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void settle1(s4 v) { asm volatile("" ::"v"(v)); }
+template <class T, int A>
+__device__ __forceinline__ void settle(const T (&v)[A]) {
+#pragma unroll
+  for (int i = 0; i < A; ++i) settle1(v[i]);
+}
+template <class T, int A, int B>
+__device__ __forceinline__ void settle(const T (&v)[A][B]) {
+#pragma unroll
+  for (int i = 0; i < A; ++i) settle(v[i]);
+}
+
 template <int B_, int C_, int GS_, class TIn, class TOut>
 __global__ __launch_bounds__((KV<B_, C_, GS_>::NT)) void ks_vreg_kernel(int64_t N, int a_count,
                                                                     const TIn* __restrict__ x,
@@ -302,6 +323,8 @@ __global__ __launch_bounds__((KV<B_, C_, GS_>::NT)) void ks_vreg_kernel(int64_t 
     for (int s = 0; s < K::SB; ++s) v[de][s] = widen(V[((int64_t)de * B_ + g * K::SB + s) * C_ + 16 * w + c]);
   stash(lds);
   fetch(tile + step);
+  settle(v);
+  settle(pf);
   __syncthreads();
 
   auto compute = [&](const float* xs, f4 (&acc)[4]) {
@@ -314,15 +337,19 @@ __global__ __launch_bounds__((KV<B_, C_, GS_>::NT)) void ks_vreg_kernel(int64_t 
       for (int de = 0; de < 4; ++de) acc[de] = mfma(xv[de], v[de][s], acc[de]);
     }
   };
+  // Per tile: products, the next tile's rows into LDS, the loads two tiles ahead, then
+  // this tile's stores.  The vector-memory counter retires in issue order, so loads issued
+  // before the stores can be waited for (next iteration's stash) without waiting for them.
   int it = 0;
   for (; tile < nfull; tile += step, ++it) {
     f4 acc[4];
     compute(lds + (it & 1) * K::TILE, acc);
+    stash(lds + ((it + 1) & 1) * K::TILE);
+    fetch(tile + 2 * step);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int vv = 0; vv < 4; ++vv)
       store4(ya + (tile * 16 + 4 * g + vv) * out_w, f4{acc[0][vv], acc[1][vv], acc[2][vv], acc[3][vv]});
-    stash(lds + ((it + 1) & 1) * K::TILE);
-    fetch(tile + 2 * step);
     __syncthreads();
   }
   if (tile < ntile) {   // the partial tile
@@ -414,6 +441,8 @@ __global__ __launch_bounds__((KVK<B_, C_>::NT)) void ks_vregk_kernel(int64_t N, 
       v[de][s] = widen(V[((int64_t)de * B_ + g * K::SB + kq * K::SBK + s) * C_ + 16 * gt + c]);
   stash(lds);
   fetch(tile + step);
+  settle(v);
+  settle(pf);
   __syncthreads();
 
   // the quarter's partial tile -> LDS as red[wave][lane][vv] = f4 over delta; then this
@@ -437,11 +466,12 @@ __global__ __launch_bounds__((KVK<B_, C_>::NT)) void ks_vregk_kernel(int64_t N, 
     return sum;   // Y[row 4g + kq][ga = 16*gt + c][0..3]
   };
   int it = 0;
-  for (; tile < nfull; tile += step, ++it) {
+  for (; tile < nfull; tile += step, ++it) {   // same order as ks_vreg_kernel
     const f4 o = compute_and_reduce(lds + (it & 1) * K::TILE);
-    store4(ya + (tile * 16 + 4 * g + kq) * out_w, o);
     stash(lds + ((it + 1) & 1) * K::TILE);
     fetch(tile + 2 * step);
+    __builtin_amdgcn_sched_barrier(0);
+    store4(ya + (tile * 16 + 4 * g + kq) * out_w, o);
     __syncthreads();
   }
   if (tile < ntile) {   // the partial tile
@@ -550,6 +580,8 @@ __global__ __launch_bounds__((KV16<B_, C_>::NT)) void ks_vreg16_kernel(int64_t N
     for (int s = 0; s < K::SK; ++s) v[de][s] = vals4(V + ((int64_t)de * B_ + 16 * s + 4 * g) * C_ + 16 * w + c, C_);
   stash(lb);
   fetch(tile + step);
+  settle(v);
+  settle(pf);
   __syncthreads();
 
   auto compute = [&](const unsigned char* xs, f4 (&acc)[4]) {
@@ -565,14 +597,15 @@ __global__ __launch_bounds__((KV16<B_, C_>::NT)) void ks_vreg16_kernel(int64_t N
     }
   };
   int it = 0;
-  for (; tile < nfull; tile += step, ++it) {
+  for (; tile < nfull; tile += step, ++it) {   // same order as ks_vreg_kernel
     f4 acc[4];
     compute(lb + (it & 1) * R::TILEB, acc);
+    stash(lb + ((it + 1) & 1) * R::TILEB);
+    fetch(tile + 2 * step);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int vv = 0; vv < 4; ++vv)
       store4(ya + (tile * 16 + 4 * g + vv) * out_w, f4{acc[0][vv], acc[1][vv], acc[2][vv], acc[3][vv]});
-    stash(lb + ((it + 1) & 1) * R::TILEB);
-    fetch(tile + 2 * step);
     __syncthreads();
   }
   if (tile < ntile) {
@@ -657,6 +690,8 @@ __global__ __launch_bounds__((KVK16<B_, C_>::NT)) void ks_vregk16_kernel(int64_t
       v[de][s] = vals4(V + ((int64_t)de * B_ + kq * K::QB + 16 * s + 4 * g) * C_ + 16 * gt + c, C_);
   stash(lb);
   fetch(tile + step);
+  settle(v);
+  settle(pf);
   __syncthreads();
 
   auto compute_and_reduce = [&](const unsigned char* xs) {
@@ -680,11 +715,12 @@ __global__ __launch_bounds__((KVK16<B_, C_>::NT)) void ks_vregk16_kernel(int64_t
     return sum;
   };
   int it = 0;
-  for (; tile < nfull; tile += step, ++it) {
+  for (; tile < nfull; tile += step, ++it) {   // same order as ks_vreg_kernel
     const f4 o = compute_and_reduce(lb + (it & 1) * R::TILEB);
-    store4(ya + (tile * 16 + 4 * g + kq) * out_w, o);
     stash(lb + ((it + 1) & 1) * R::TILEB);
     fetch(tile + 2 * step);
+    __builtin_amdgcn_sched_barrier(0);
+    store4(ya + (tile * 16 + 4 * g + kq) * out_w, o);
     __syncthreads();
   }
   if (tile < ntile) {
