@@ -100,6 +100,26 @@ __device__ __forceinline__ float4 load4_in(const uint16_t* p) {
                      __uint_as_float(v.y & 0xffff0000u));
 }
 
+// A tile's output rows from LDS to y: a fixed number of unconditional 16-byte stores per
+// thread (items past the tile's last row or column store that row's or column's own value
+// again).  A fixed count lets the wait for the next tile's prefetch, issued before these
+// stores, leave them in flight (the vector-memory counter retires in issue order).
+constexpr int kCmStores = (kCmRows * 1248 / 4 + kCmThreads - 1) / kCmThreads;
+
+__device__ __forceinline__ void store_tile(float* __restrict__ y, const float* ob, int LD, int64_t tile, int64_t N,
+                                           int wl, int ql) {
+  const int rmax = (int)(N - tile * kCmRows < kCmRows ? N - tile * kCmRows : kCmRows) - 1;
+#pragma unroll
+  for (int u = 0; u < kCmStores; ++u) {
+    const int e = threadIdx.x + u * kCmThreads;
+    int r = e & (kCmRows - 1), c4 = e / kCmRows;
+    r = r < rmax ? r : rmax;
+    c4 = c4 < ql - 1 ? c4 : ql - 1;
+    const float* p = ob + r * LD + 4 * c4;
+    *reinterpret_cast<float4*>(y + (tile * kCmRows + r) * wl + 4 * c4) = make_float4(p[0], p[1], p[2], p[3]);
+  }
+}
+
 // x = quo * dv + rem for 0 <= x < 2^24, dv >= 1: the float quotient is off by at most one,
 // which one correction step fixes.
 __device__ __forceinline__ void divmod(int x, int dv, float inv, int& quo, int& rem) {
@@ -270,15 +290,7 @@ __global__ __launch_bounds__(kCmThreads) void ks_chain_mfma_kernel(ChainArgs A, 
       __syncthreads();
       cur ^= 1;
     }
-    {   // the tile's output rows to y
-      const float* ob = smem + cur * kCmRows * LD;
-      for (int e = tid; e < kCmRows * ql; e += kCmThreads) {
-        const int r = e & (kCmRows - 1), c4 = e / kCmRows;
-        const int64_t row = tile * kCmRows + r;
-        const float* p = ob + r * LD + 4 * c4;
-        if (row < A.N) *reinterpret_cast<float4*>(A.y + row * wl + 4 * c4) = make_float4(p[0], p[1], p[2], p[3]);
-      }
-    }
+    store_tile(A.y, smem + cur * kCmRows * LD, LD, tile, A.N, wl, ql);
     __syncthreads();   // buffer 0 is free again
     if (tile + gridDim.x < ntiles) stage();
   }
@@ -417,6 +429,19 @@ __global__ __launch_bounds__(kCmThreads) void ks_chain_reg_kernel(ChainArgs A, i
   int64_t tile = blockIdx.x;
   fetch(tile);
   stage();
+  // the factor values must be in registers before the loop: otherwise the loop head merges
+  // the preheader's outstanding value loads with the tile's prefetch, and the first product
+  // of every tile waits for that prefetch
+#pragma unroll
+  for (int i = 0; i < T0 * S0; ++i) asm volatile("" ::"v"(v0[i]));
+  if constexpr (NF > 1) {
+#pragma unroll
+    for (int i = 0; i < T1 * S1; ++i) asm volatile("" ::"v"(v1[i]));
+  }
+  if constexpr (NF > 2) {
+#pragma unroll
+    for (int i = 0; i < T2 * S2; ++i) asm volatile("" ::"v"(v2[i]));
+  }
   for (; tile < ntiles; tile += gridDim.x) {
     if (tile + gridDim.x < ntiles) fetch(tile + gridDim.x);
     __syncthreads();
@@ -430,15 +455,7 @@ __global__ __launch_bounds__(kCmThreads) void ks_chain_reg_kernel(ChainArgs A, i
       run_slots<T2, S2>(v2, d2, nt[2], w, nk[2], cc[2], dd[2], LD, b0, b1, dummy);
       __syncthreads();
     }
-    {
-      const float* ob = (NF & 1) ? b1 : b0;
-      for (int e = tid; e < kCmRows * ql; e += kCmThreads) {
-        const int r = e & (kCmRows - 1), c4 = e / kCmRows;
-        const int64_t row = tile * kCmRows + r;
-        const float* p = ob + r * LD + 4 * c4;
-        if (row < A.N) *reinterpret_cast<float4*>(A.y + row * wl + 4 * c4) = make_float4(p[0], p[1], p[2], p[3]);
-      }
-    }
+    store_tile(A.y, (NF & 1) ? b1 : b0, LD, tile, A.N, wl, ql);
     __syncthreads();
     if (tile + gridDim.x < ntiles) stage();
   }
