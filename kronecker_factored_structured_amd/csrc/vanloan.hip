@@ -8,7 +8,8 @@
 // The singular triplets come from block subspace iteration (the standard randomized
 // range finder with power iterations) started from a caller-supplied random K x s block:
 //   Q <- orth(Omega); repeat iters times: Q <- orth(R^T (R Q)) (orthogonal iteration on
-//   R^T R; the span of R^T R Q does not depend on orthonormalising R Q first);
+//   R^T R; the span of R^T R Q does not depend on orthonormalising R Q first; inside the
+//   loop orth is a shifted Cholesky-QR re-basing, which keeps the span);
 //   Z <- orth(R Q); Bt <- R^T Z (= (Z^T R)^T); G = Bt^T Bt = E diag(lambda) E^T (Jacobi);
 //   u_i = Z E e_i, sigma_i = sqrt(lambda_i), v_i = Bt E e_i / sigma_i.
 // R is never materialised: the products read W through the index map above.  The s-column
@@ -241,16 +242,21 @@ __device__ __forceinline__ float dpp_mov(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-  v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
-  v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
-  v += dpp_mov<0x124>(v);   // row_ror 4
-  v += dpp_mov<0x128>(v);   // row_ror 8
+// the four 16-lane row totals (each row already holds its total in every lane), added in order
+__device__ __forceinline__ float row_total(float v) {
   const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
   const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
   const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
   const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
   return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_mov<0x124>(v);   // row_ror 4
+  v += dpp_mov<0x128>(v);   // row_ror 8
+  return row_total(v);
 }
 
 // Columns of an L x s panel (L <= 1024) made orthonormal: classical Gram-Schmidt with one
@@ -262,33 +268,47 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 constexpr int kVlOrthRegThreads = 256;
 constexpr int kVlOrthRegRows = 4;
 
-template <bool ROWIN>
+template <int SM, bool ROWIN>
 __global__ __launch_bounds__(kVlOrthRegThreads) void vl_orth_reg_kernel(int L, int s, const float* in, float* X) {
   constexpr int NW = kVlOrthRegThreads / 64;
   __shared__ float part[2][NW][kVlMaxS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float x[kVlOrthRegRows][kVlMaxS];
+  float x[kVlOrthRegRows][SM];
 #pragma unroll
   for (int i = 0; i < kVlOrthRegRows; ++i) {
     const int l = tid + i * kVlOrthRegThreads;
 #pragma unroll
-    for (int u = 0; u < kVlMaxS; ++u)
+    for (int u = 0; u < SM; ++u)
       x[i][u] = (l < L && u < s) ? (ROWIN ? in[(int64_t)l * s + u] : in[(int64_t)u * L + l]) : 0.f;
   }
   int buf = 0;
 #pragma unroll
-  for (int t = 0; t < kVlMaxS; ++t) {
+  for (int t = 0; t < SM; ++t) {
     if (t < s) {
 #pragma unroll
       for (int pass = 0; pass < 2; ++pass) {
         if (t > 0) {
+          // the t sums advance together, one DPP step for all of them at a time
+          float pd[SM];
 #pragma unroll
           for (int u = 0; u < t; ++u) {
-            float pd = 0.f;
+            pd[u] = 0.f;
 #pragma unroll
-            for (int i = 0; i < kVlOrthRegRows; ++i) pd = fmaf(x[i][t], x[i][u], pd);
-            const float w = wave_sum_dpp(pd);
-            if (lane == 0) part[buf][wave][u] = w;
+            for (int i = 0; i < kVlOrthRegRows; ++i) pd[u] = fmaf(x[i][t], x[i][u], pd[u]);
+          }
+#pragma unroll
+          for (int u = 0; u < t; ++u) pd[u] += dpp_mov<0xB1>(pd[u]);
+#pragma unroll
+          for (int u = 0; u < t; ++u) pd[u] += dpp_mov<0x4E>(pd[u]);
+#pragma unroll
+          for (int u = 0; u < t; ++u) pd[u] += dpp_mov<0x124>(pd[u]);
+#pragma unroll
+          for (int u = 0; u < t; ++u) pd[u] += dpp_mov<0x128>(pd[u]);
+#pragma unroll
+          for (int u = 0; u < t; ++u) pd[u] = row_total(pd[u]);
+          if (lane == 0) {
+#pragma unroll
+            for (int u = 0; u < t; ++u) part[buf][wave][u] = pd[u];
           }
           __syncthreads();
 #pragma unroll
@@ -319,7 +339,124 @@ __global__ __launch_bounds__(kVlOrthRegThreads) void vl_orth_reg_kernel(int L, i
     const int l = tid + i * kVlOrthRegThreads;
     if (l < L) {
 #pragma unroll
-      for (int u = 0; u < kVlMaxS; ++u)
+      for (int u = 0; u < SM; ++u)
+        if (u < s) X[(int64_t)u * L + l] = x[i][u];
+    }
+  }
+}
+
+// Inside the power iteration only the span of Q matters, so its L x s panel (L <= 1024) is
+// re-based with one round of shifted Cholesky-QR instead of Gram-Schmidt: the Gram matrix
+// G = X^T X (all s(s+1)/2 sums at once: per wavefront by DPP, then over wavefronts in fp64),
+// G + shift * I = R^T R by Cholesky in fp64 on one wavefront (the shift, 1e-6 of G's mean
+// diagonal, keeps a rank-deficient panel factorisable), then X <- X R^{-1} row by row by
+// forward substitution.  Columns that carry the dominant directions come out orthonormal to
+// about the shift; the last orthonormalisation (of Z) is the Gram-Schmidt kernel above.
+constexpr int kVlPairs = kVlMaxS * (kVlMaxS + 1) / 2;
+
+template <int SM, bool ROWIN>
+__global__ __launch_bounds__(kVlOrthRegThreads) void vl_cholqr_kernel(int L, int s, const float* in, float* X) {
+  constexpr int NW = kVlOrthRegThreads / 64;
+  __shared__ float part[NW][kVlPairs];
+  __shared__ double G[kVlMaxS][kVlMaxS + 1];
+  __shared__ float R[kVlMaxS][kVlMaxS + 1];   // upper triangle of R; R[t][t] holds 1 / R_tt
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float x[kVlOrthRegRows][SM];
+#pragma unroll
+  for (int i = 0; i < kVlOrthRegRows; ++i) {
+    const int l = tid + i * kVlOrthRegThreads;
+#pragma unroll
+    for (int u = 0; u < SM; ++u)
+      x[i][u] = (l < L && u < s) ? (ROWIN ? in[(int64_t)l * s + u] : in[(int64_t)u * L + l]) : 0.f;
+  }
+  // Gram row u: pairs (u, v), v >= u, at pair index u*s - u(u-1)/2 + (v - u)
+#pragma unroll
+  for (int u = 0; u < SM; ++u) {
+    if (u < s) {
+      float pd[SM];
+#pragma unroll
+      for (int v = u; v < SM; ++v) {
+        pd[v] = 0.f;
+#pragma unroll
+        for (int i = 0; i < kVlOrthRegRows; ++i) pd[v] = fmaf(x[i][u], x[i][v], pd[v]);
+      }
+#pragma unroll
+      for (int v = u; v < SM; ++v) pd[v] += dpp_mov<0xB1>(pd[v]);
+#pragma unroll
+      for (int v = u; v < SM; ++v) pd[v] += dpp_mov<0x4E>(pd[v]);
+#pragma unroll
+      for (int v = u; v < SM; ++v) pd[v] += dpp_mov<0x124>(pd[v]);
+#pragma unroll
+      for (int v = u; v < SM; ++v) pd[v] += dpp_mov<0x128>(pd[v]);
+#pragma unroll
+      for (int v = u; v < SM; ++v) pd[v] = row_total(pd[v]);
+      if (lane == 0) {
+        const int base = u * s - u * (u - 1) / 2 - u;
+#pragma unroll
+        for (int v = u; v < SM; ++v)
+          if (v < s) part[wave][base + v] = pd[v];
+      }
+    }
+  }
+  __syncthreads();
+  const int npairs = s * (s + 1) / 2;
+  for (int pi = tid; pi < npairs; pi += kVlOrthRegThreads) {
+    int u = 0, rem = pi;
+    while (rem >= s - u) {
+      rem -= s - u;
+      ++u;
+    }
+    const int v = u + rem;
+    double g = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) g += (double)part[w][pi];
+    G[u][v] = g;
+    G[v][u] = g;
+  }
+  __syncthreads();
+  if (tid < 64) {   // Cholesky of G + shift * I, right-looking, lanes over the trailing columns
+    const int l = tid;
+    double tr = 0.0;
+    if (l < s) tr = G[l][l];
+    tr = wave_sum(tr);
+    const double shift = 1e-6 * tr / s + 1e-300;
+    if (l < s) G[l][l] += shift;
+    wave_sync();
+    for (int t = 0; t < s; ++t) {
+      const double d = sqrt(G[t][t] > 0.0 ? G[t][t] : shift);
+      const double inv = 1.0 / d;
+      if (l >= t && l < s) R[t][l] = l == t ? (float)inv : (float)(G[t][l] * inv);
+      wave_sync();
+      for (int e = l; e < (s - t - 1) * (s - t - 1); e += 64) {   // trailing update
+        const int a = t + 1 + e / (s - t - 1), b = t + 1 + e % (s - t - 1);
+        G[a][b] -= (G[t][a] * inv) * (G[t][b] * inv);
+      }
+      wave_sync();
+    }
+  }
+  __syncthreads();
+  // X <- X R^{-1}: x_t = (x_t - sum_{u<t} R[u][t] x_u) / R_tt, row by row
+#pragma unroll
+  for (int t = 0; t < SM; ++t) {
+    if (t < s) {
+#pragma unroll
+      for (int u = 0; u < t; ++u) {
+        const float ru = R[u][t];
+#pragma unroll
+        for (int i = 0; i < kVlOrthRegRows; ++i) x[i][t] = fmaf(-ru, x[i][u], x[i][t]);
+      }
+      const float inv = R[t][t];
+#pragma unroll
+      for (int i = 0; i < kVlOrthRegRows; ++i) x[i][t] *= inv;
+    }
+  }
+  __syncthreads();   // an aliased input has been read by every thread before any write
+#pragma unroll
+  for (int i = 0; i < kVlOrthRegRows; ++i) {
+    const int l = tid + i * kVlOrthRegThreads;
+    if (l < L) {
+#pragma unroll
+      for (int u = 0; u < SM; ++u)
         if (u < s) X[(int64_t)u * L + l] = x[i][u];
     }
   }
@@ -665,10 +802,30 @@ void launch_apply(const VanLoanArgs& A, const float* Xt, float* Yt, hipStream_t 
                      st, A.p, A.q, A.m, A.n, A.s, CH, A.W, Xt, Yt);
 }
 
+// Re-basing inside the power iteration (the span is what matters): Cholesky-QR when the
+// panel fits the register kernels, else Gram-Schmidt in memory.
+template <bool ROWIN>
+void launch_rebase(int L, int s, const float* in, float* X, hipStream_t st) {
+  const dim3 g(1), b(kVlOrthRegThreads);
+  if (L <= kVlOrthRegThreads * kVlOrthRegRows && s <= 8)
+    hipLaunchKernelGGL((vl_cholqr_kernel<8, ROWIN>), g, b, 0, st, L, s, in, X);
+  else if (L <= kVlOrthRegThreads * kVlOrthRegRows && s <= 16)
+    hipLaunchKernelGGL((vl_cholqr_kernel<16, ROWIN>), g, b, 0, st, L, s, in, X);
+  else if (L <= kVlOrthRegThreads * kVlOrthRegRows)
+    hipLaunchKernelGGL((vl_cholqr_kernel<32, ROWIN>), g, b, 0, st, L, s, in, X);
+  else
+    hipLaunchKernelGGL((vl_orth_mem_kernel<ROWIN>), dim3(1), dim3(kVlOrthThreads), 0, st, L, s, in, X);
+}
+
 template <bool ROWIN>
 void launch_orth(int L, int s, const float* in, float* X, hipStream_t st) {
-  if (L <= kVlOrthRegThreads * kVlOrthRegRows)
-    hipLaunchKernelGGL((vl_orth_reg_kernel<ROWIN>), dim3(1), dim3(kVlOrthRegThreads), 0, st, L, s, in, X);
+  const dim3 g(1), b(kVlOrthRegThreads);
+  if (L <= kVlOrthRegThreads * kVlOrthRegRows && s <= 8)
+    hipLaunchKernelGGL((vl_orth_reg_kernel<8, ROWIN>), g, b, 0, st, L, s, in, X);
+  else if (L <= kVlOrthRegThreads * kVlOrthRegRows && s <= 16)
+    hipLaunchKernelGGL((vl_orth_reg_kernel<16, ROWIN>), g, b, 0, st, L, s, in, X);
+  else if (L <= kVlOrthRegThreads * kVlOrthRegRows)
+    hipLaunchKernelGGL((vl_orth_reg_kernel<32, ROWIN>), g, b, 0, st, L, s, in, X);
   else
     hipLaunchKernelGGL((vl_orth_mem_kernel<ROWIN>), dim3(1), dim3(kVlOrthThreads), 0, st, L, s, in, X);
 }
@@ -687,11 +844,11 @@ hipError_t launch_van_loan(const VanLoanArgs& A, void* ws, hipStream_t st) {
   float* Q = reinterpret_cast<float*>(w + align256v((size_t)M * s * 4));   // s x K panel
   float* E = reinterpret_cast<float*>(w + align256v((size_t)M * s * 4) + align256v((size_t)K * s * 4));
   float* lam = E + align256v((size_t)s * s * 4) / 4;
-  launch_orth<true>(K, s, A.omega, Q, st);
+  launch_rebase<true>(K, s, A.omega, Q, st);
   for (int it = 0; it < A.iters; ++it) {   // orthogonal iteration on R^T R
     launch_apply<0, kVlO0>(A, Q, Z, st);
     launch_apply<1, kVlO1>(A, Z, Q, st);
-    launch_orth<false>(K, s, Q, Q, st);
+    launch_rebase<false>(K, s, Q, Q, st);
   }
   launch_apply<0, kVlO0>(A, Q, Z, st);
   launch_orth<false>(M, s, Z, Z, st);

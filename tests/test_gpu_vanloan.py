@@ -98,3 +98,10 @@ def test_tall_panel():
     rng = np.random.default_rng(85)
     W = kron_sum(rng, 64, 64, 8, 8, [4.0, 2.0, 1.0, 0.5, 0.25, 0.12], noise=1e-3)
     check(W, 64, 64, 8, 8, 3, 10, 8)
+
+
+def test_wide_subspace():
+    """s = 20 (more than 16 panel columns): the register kernels' widest instantiation."""
+    rng = np.random.default_rng(86)
+    W = kron_sum(rng, 16, 16, 16, 16, 0.7 ** np.arange(24), noise=1e-4)
+    check(W, 16, 16, 16, 16, 3, 20, 6)
