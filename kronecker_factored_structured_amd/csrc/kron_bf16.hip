@@ -336,38 +336,47 @@ __global__ __launch_bounds__((BB<D, RPI>::NT)) void bwd_bf16_kernel(int64_t N, c
   const int64_t ngrp = (N + Q::RPI - 1) / Q::RPI;
 
   // one step's rows as 16-byte pieces: x then dy of each row slot (zero past the last row);
-  // two register sets alternate so that each step's rows are requested three steps ahead
+  // two register sets alternate so that each step's rows are requested three steps ahead.
+  // Every piece is loaded unconditionally (rows past the end read the last row, or the
+  // workspace when there are no rows) and a bit per piece says whether it is live; the
+  // zeroing waits for the stash.  With no branches around the loads the compiler can count
+  // them, so a stash waits only for its own loads, not for the dX stores issued after them.
   u4 pfA[Q::NPF], pfB[Q::NPF];
-  auto fetch = [&](u4 (&pf)[Q::NPF], int64_t grp) {
+  uint32_t okA = 0, okB = 0;
+  static_assert(Q::NPF <= 32, "one live bit per prefetched piece");
+  auto fetch = [&](u4 (&pf)[Q::NPF], uint32_t& ok, int64_t grp) {
+    ok = 0;
 #pragma unroll
     for (int t = 0; t < Q::NPF; ++t) {
       const int f = tid + t * NT;
-      u4 v = u4{0u, 0u, 0u, 0u};
-      if (f < Q::RPI * Q::CHUNKS) {
-        const int s = f / Q::CHUNKS, o = 8 * (f % Q::CHUNKS);
-        const int64_t row = grp * Q::RPI + s;
-        if (grp < ngrp && row < N)
-          v = o < D::IN ? *reinterpret_cast<const u4*>(x + row * D::IN + o)
-                        : *reinterpret_cast<const u4*>(dy + row * D::OUT + (o - D::IN));
-      }
-      pf[t] = v;
+      const bool fin = f < Q::RPI * Q::CHUNKS;
+      const int fc = fin ? f : Q::RPI * Q::CHUNKS - 1;
+      const int s = fc / Q::CHUNKS, o = 8 * (fc % Q::CHUNKS);
+      const int64_t row = grp * Q::RPI + s;
+      const bool live = fin && grp < ngrp && row < N;
+      const int64_t rc = row < N ? row : N - 1;
+      const uint16_t* src = o < D::IN ? x + rc * D::IN + o : dy + rc * D::OUT + (o - D::IN);
+      if (N == 0) src = reinterpret_cast<const uint16_t*>(part);
+      pf[t] = *reinterpret_cast<const u4*>(src);
+      ok |= (live ? 1u : 0u) << t;
     }
   };
-  auto stash = [&](const u4 (&pf)[Q::NPF], int buf) {
+  auto stash = [&](const u4 (&pf)[Q::NPF], uint32_t ok, int buf) {
 #pragma unroll
     for (int t = 0; t < Q::NPF; ++t) {
       const int f = tid + t * NT;
       if (f < Q::RPI * Q::CHUNKS) {
         const int s = f / Q::CHUNKS, o = 8 * (f % Q::CHUNKS);
         uint16_t* rb = lds + buf * Q::ROWS + s * (Q::XS + Q::YS);
+        const u4 v = (ok >> t) & 1u ? pf[t] : u4{0u, 0u, 0u, 0u};
         if (o < D::IN)
-          *reinterpret_cast<u4*>(rb + (o / D::M) * Q::LX + o % D::M) = pf[t];
+          *reinterpret_cast<u4*>(rb + (o / D::M) * Q::LX + o % D::M) = v;
         else
-          *reinterpret_cast<u4*>(rb + Q::XS + ((o - D::IN) / D::N) * Q::LY + (o - D::IN) % D::N) = pf[t];
+          *reinterpret_cast<u4*>(rb + Q::XS + ((o - D::IN) / D::N) * Q::LY + (o - D::IN) % D::N) = v;
       }
     }
   };
-  fetch(pfA, blockIdx.x);
+  fetch(pfA, okA, blockIdx.x);
 
   // ---- prologue: B_i and C_i = S o A_i staged row-major, then this wavefront's operands
   uint16_t* sB = lds;                               // [i][a][SB]
@@ -420,9 +429,9 @@ __global__ __launch_bounds__((BB<D, RPI>::NT)) void bwd_bf16_kernel(int64_t N, c
     }
   }
   __syncthreads();   // the staging area becomes row buffers
-  stash(pfA, 0);
-  fetch(pfA, blockIdx.x + (int64_t)gridDim.x);
-  fetch(pfB, blockIdx.x + 2 * (int64_t)gridDim.x);
+  stash(pfA, okA, 0);
+  fetch(pfA, okA, blockIdx.x + (int64_t)gridDim.x);
+  fetch(pfB, okB, blockIdx.x + 2 * (int64_t)gridDim.x);
   __syncthreads();
 
   f4 dC[D::TJ][D::TK];    // dC_i[j = 16tj + 4g + v][k = 16tk + c]
@@ -443,7 +452,7 @@ __global__ __launch_bounds__((BB<D, RPI>::NT)) void bwd_bf16_kernel(int64_t N, c
 #pragma unroll
       for (int u = 0; u < WB; ++u) db[tk][s][u] = 0.f;
 
-  auto step = [&](int64_t grp, int rbuf, int gbuf, u4 (&pf)[Q::NPF], auto tail_c) {
+  auto step = [&](int64_t grp, int rbuf, int gbuf, u4 (&pf)[Q::NPF], uint32_t& ok, auto tail_c) {
     constexpr bool kTail = decltype(tail_c)::value;
     const uint16_t* X = lds + rbuf * Q::ROWS + slot * (Q::XS + Q::YS);
     const uint16_t* Y = X + Q::XS;
@@ -506,8 +515,8 @@ __global__ __launch_bounds__((BB<D, RPI>::NT)) void bwd_bf16_kernel(int64_t N, c
       }
     }
     // the next step's rows into the next row buffer; this register set fetches three steps ahead
-    stash(pf, rbuf == Q::NRB - 1 ? 0 : rbuf + 1);
-    fetch(pf, grp + 3 * (int64_t)gridDim.x);
+    stash(pf, ok, rbuf == Q::NRB - 1 ? 0 : rbuf + 1);
+    fetch(pf, ok, grp + 3 * (int64_t)gridDim.x);
     __syncthreads();
     // dX^T[a][j] = sum_(i,b) B_i[a][b] G_i[j][b]: this wavefront's tiles
     const int64_t row = grp * Q::RPI + slot;
@@ -565,17 +574,17 @@ __global__ __launch_bounds__((BB<D, RPI>::NT)) void bwd_bf16_kernel(int64_t N, c
     grp += G;
   };
   while (grp + G < nfull) {   // local steps in pairs: register set A, then B
-    step(grp, rbuf, gbuf, pfA, std::false_type{});
+    step(grp, rbuf, gbuf, pfA, okA, std::false_type{});
     advance();
-    step(grp, rbuf, gbuf, pfB, std::false_type{});
+    step(grp, rbuf, gbuf, pfB, okB, std::false_type{});
     advance();
   }
   if (grp < nfull) {
-    step(grp, rbuf, gbuf, pfA, std::false_type{});
+    step(grp, rbuf, gbuf, pfA, okA, std::false_type{});
     advance();
-    if (grp < ngrp) step(grp, rbuf, gbuf, pfB, std::true_type{});
+    if (grp < ngrp) step(grp, rbuf, gbuf, pfB, okB, std::true_type{});
   } else if (grp < ngrp) {
-    step(grp, rbuf, gbuf, pfA, std::true_type{});
+    step(grp, rbuf, gbuf, pfA, okA, std::true_type{});
   }
 
   // Partial row of this workgroup: [dB (R*M*N) | dA (R*P*Q) | dS (P*Q) | dbias (Q*N)], fp32.
