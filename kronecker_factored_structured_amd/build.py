@@ -29,6 +29,7 @@ OBJECTS = [
     ("kron_generic.hip", [], "kron_generic"),
     ("kron_mfma.hip", ["-DKRON_MFMA_PASS=1", "-mllvm", "-amdgpu-sched-strategy=max-ilp"], "kron_mfma_fwd"),
     ("kron_mfma.hip", ["-DKRON_MFMA_PASS=2"], "kron_mfma_bwd"),
+    ("kron_small.hip", [], "kron_small"),
     ("kron_bf16.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"], "kron_bf16"),
     ("ks_matmul.hip", [], "ks_matmul"),
     ("ks_mfma.hip", [], "ks_mfma"),

@@ -97,13 +97,22 @@ int32_t check_shape(const kron_shape_t* s) {
 // chunk > 0: the ranks run in passes of `chunk` ranks each (partial rows per pass).
 struct BwdPlan {
   bool mfma;
+  bool small;
   int chunk;
   int G;
   size_t ws_bytes;
+  kron::SmallBwdPlan sp;
 };
 
 BwdPlan bwd_plan(const kron_shape_t* s, bool want_dx) {
-  BwdPlan pl{false, 0, 0, 0};
+  BwdPlan pl{false, false, 0, 0, 0, {}};
+  if (kron::small_supported(s->p, s->q, s->m, s->n, s->r) &&
+      !kron::mfma_bwd_supported(s->p, s->q, s->m, s->n, s->r)) {
+    pl.small = true;
+    pl.sp = kron::small_bwd_plan(s->N, s->p, s->q, s->m, s->n, s->r);
+    pl.ws_bytes = (size_t)pl.sp.ws_floats * sizeof(float);
+    return pl;
+  }
   if (kron::mfma_bwd_supported(s->p, s->q, s->m, s->n, s->r)) {
     pl.mfma = true;
     pl.G = kron::mfma_bwd_groups(s->N, s->p, s->q, s->m, s->n, s->r);
@@ -158,8 +167,9 @@ const char* kron_last_error(void) { return g_last_error.c_str(); }
 int32_t kron_linear_check(const kron_shape_t* s) {
   const int32_t st = check_shape(s);
   if (st != KRON_OK) return st;
-  if (kron::generic_fwd_rows_per_tile(s->p, s->q, s->m, s->n) == 0 ||
-      kron::generic_bwd_rows_per_tile(s->p, s->q, s->m, s->n, true) == 0)
+  if (!kron::small_supported(s->p, s->q, s->m, s->n, s->r) &&
+      (kron::generic_fwd_rows_per_tile(s->p, s->q, s->m, s->n) == 0 ||
+       kron::generic_bwd_rows_per_tile(s->p, s->q, s->m, s->n, true) == 0))
     return fail(KRON_E_UNSUPPORTED, "per-row working set of p=%d q=%d m=%d n=%d exceeds LDS", s->p, s->q,
                 s->m, s->n);
   return ok();
@@ -190,8 +200,9 @@ int32_t kron_linear_fwd(const kron_shape_t* s, const float* x, const float* S, c
   kron::LayerArgs a{};
   a.N = s->N; a.p = s->p; a.q = s->q; a.m = s->m; a.n = s->n; a.r = s->r; a.flags = s->flags;
   a.x = x; a.S = S; a.A = A; a.B = B; a.bias = bias; a.y = y;
-  hipError_t e = kron::mfma_fwd_supported(a.p, a.q, a.m, a.n, a.r) ? kron::launch_fwd_mfma(a, stream)
-                                                                    : kron::launch_fwd_generic(a, stream);
+  hipError_t e = kron::mfma_fwd_supported(a.p, a.q, a.m, a.n, a.r)    ? kron::launch_fwd_mfma(a, stream)
+                 : kron::small_supported(a.p, a.q, a.m, a.n, a.r) ? kron::launch_fwd_small(a, stream)
+                                                                  : kron::launch_fwd_generic(a, stream);
   if (e != hipSuccess) return hip_fail(e, "kron_linear_fwd launch");
   return ok();
 }
@@ -228,6 +239,11 @@ int32_t kron_linear_bwd(const kron_shape_t* s, const float* x, const float* S, c
   a.part = (float*)workspace;
   const BwdPlan pl = bwd_plan(s, a.dx != nullptr);
   const int32_t pq32 = s->p * s->q, mn32 = s->m * s->n;
+  if (pl.small) {
+    hipError_t e = kron::launch_bwd_small(a, pl.sp, stream);
+    if (e != hipSuccess) return hip_fail(e, "kron_linear_bwd launch");
+    return ok();
+  }
   if (pl.chunk > 0) {
     // ranks in passes of pl.chunk: pass c handles ranks [c*chunk, (c+1)*chunk); dX is
     // written by the first pass and added to by the others (the ReLU mask, if any, is

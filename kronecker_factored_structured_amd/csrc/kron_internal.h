@@ -111,6 +111,22 @@ int bf16_bwd_groups(int64_t N, int p, int q, int m, int n, int r);
 hipError_t launch_fwd_bf16(const LayerArgsBf16& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const LayerArgsBf16& a, int G, hipStream_t s);
 
+// Small-block matrix-core path (kron_small.hip): m = n in {2, 4, 8}, p and q multiples
+// of 16, r <= 16.  The backward writes two partial arrays into the workspace: dB rows
+// (G1 x r*m*n) at float offset 0 and [dC | dbias] rows (G2 x (r*p*q + q*n)) at off2.
+struct SmallBwdPlan {
+  int G1, G2;
+  int64_t rpg;          // rows per row group of the dC kernel
+  int64_t PW1, PW2;     // partial widths
+  int64_t off2;         // float offset of the second partial array
+  int64_t ws_floats;    // workspace floats
+};
+bool small_supported(int p, int q, int m, int n, int r);
+SmallBwdPlan small_bwd_plan(int64_t N, int p, int q, int m, int n, int r);
+hipError_t launch_fwd_small(const LayerArgs& a, hipStream_t s);
+// Runs the whole backward: kernels, both column reductions and the dA / dS epilogue.
+hipError_t launch_bwd_small(const LayerArgs& a, const SmallBwdPlan& pl, hipStream_t s);
+
 // Ranks per chunk when a backward with r ranks runs as r / chunk passes of the
 // chunk-rank MFMA kernel (dX accumulated over the passes), else 0.
 int mfma_bwd_chunk(int p, int q, int m, int n, int r);

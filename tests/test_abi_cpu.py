@@ -51,11 +51,17 @@ def test_shape_validation():
     assert check(KronShape(10, 32, 32, 32, 32, 0, 0)) == _lib.KRON_E_SHAPE
     assert check(KronShape(10, 32, 32, 32, 32, 65, 0)) == _lib.KRON_E_UNSUPPORTED
     assert check(KronShape(10, 4096, 32, 32, 32, 1, 0)) == _lib.KRON_E_UNSUPPORTED  # in > 65536
-    # the tutorial's 1024 x 1024 layer with 8 x 8 and 16 x 16 blocks fits the generic kernels'
-    # LDS (S and C_i of 128 x 128); 4 x 4 blocks (256 x 256) do not
+    # the tutorial's 1024 x 1024 layer: 16 x 16 blocks fit the generic kernels' LDS; 8 x 8,
+    # 4 x 4 and 2 x 2 blocks (p = q = 128, 256, 512) take the small-block matrix-core path
+    # up to rank 16, beyond which only 8 x 8 blocks (S and C_i of 128 x 128) still fit the
+    # generic kernels; blocks smaller than 16 x 16 need p and q multiples of 16
     assert check(KronShape(256, 128, 128, 8, 8, 1, 0)) == 0
     assert check(KronShape(256, 64, 64, 16, 16, 4, 0)) == 0
-    assert check(KronShape(256, 256, 256, 4, 4, 1, 0)) == _lib.KRON_E_UNSUPPORTED
+    assert check(KronShape(256, 256, 256, 4, 4, 1, 0)) == 0
+    assert check(KronShape(256, 512, 512, 2, 2, 16, 0)) == 0
+    assert check(KronShape(256, 128, 128, 8, 8, 17, 0)) == 0
+    assert check(KronShape(256, 256, 256, 4, 4, 17, 0)) == _lib.KRON_E_UNSUPPORTED
+    assert check(KronShape(256, 250, 256, 4, 4, 1, 0)) == _lib.KRON_E_UNSUPPORTED
     assert check(KronShape(10, 32, 32, 32, 32, 4, 8)) == _lib.KRON_E_ARG           # unknown flag
     assert "flag" in _lib.last_error()
     assert _lib.lib().kron_linear_check(None) == _lib.KRON_E_NULL

@@ -221,3 +221,89 @@ def test_kron_linear_module_autograd():
     assert rel_err(host(y), OK.forward(inp.x, inp.S, inp.A, inp.B, inp.bias)) <= TOL_F32
     for t, k in ((x, "dx"), (layer.S, "dS"), (layer.A, "dA"), (layer.B, "dB"), (layer.bias, "dbias")):
         assert rel_err(host(t.grad), go[k]) <= TOL_F32, k
+
+
+# ---------------------------------------------------------------------------------
+# Small blocks (m = n in {2, 4, 8}, p and q multiples of 16): the matrix-core GEMM path.
+# The tutorial's 1024 x 1024 layer with 8 x 8, 4 x 4 and 2 x 2 blocks is p = q = 128, 256, 512.
+# ---------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", [(128, 8, 1), (128, 8, 2), (128, 8, 4), (256, 4, 1), (256, 4, 2), (512, 2, 1),
+                                  (512, 2, 2)])
+def test_small_block_layers(case):
+    """1031 rows (a ragged 64-row tile), half of S zeroed, bias."""
+    p, m, r = case
+    compare_layer(kron_inputs(40, 1031, p, p, m, m, r, s_mode="uniform_zeroed", bias_mode="normal"))
+
+
+@pytest.mark.parametrize("case", [(48, 80, 4, 3), (160, 32, 8, 2), (528, 16, 2, 1), (16, 16, 8, 5)])
+def test_small_block_partial_tiles(case):
+    """p, q not multiples of the kernels' tile widths (16-multiples only)."""
+    p, q, m, r = case
+    compare_layer(kron_inputs(41, 333, p, q, m, m, r, s_mode="uniform_zeroed", bias_mode="normal"))
+
+
+@pytest.mark.parametrize("N", [0, 1, 63, 65])
+def test_small_block_ragged_rows(N):
+    inp = kron_inputs(42, N, 128, 128, 8, 8, 2, s_mode="uniform_zeroed", bias_mode="normal")
+    if N == 0:
+        y, g = run_layer(inp)
+        assert y.shape == (0, 1024)
+        for k in ("dS", "dA", "dB", "dbias"):
+            assert not np.any(g[k]), k
+        return
+    compare_layer(inp)
+
+
+@pytest.mark.parametrize("case", [(128, 8, 1), (256, 4, 2)])
+def test_small_block_full_size(case):
+    """20,000 rows of the 1024 x 1024 layer (the tutorial's batch) against the oracle."""
+    p, m, r = case
+    compare_layer(kron_inputs(43, 20000, p, p, m, m, r, s_mode="uniform_zeroed", bias_mode="normal"))
+
+
+def test_small_block_rank16_without_S_and_dx():
+    compare_layer(kron_inputs(44, 200, 128, 128, 8, 8, 16, s_mode="none", bias_mode="normal"), want_dx=False)
+    compare_layer(kron_inputs(45, 200, 256, 256, 4, 4, 16, s_mode="none", bias_mode="none"))
+
+
+@pytest.mark.parametrize("m", [8, 4, 2])
+def test_small_block_relu_flags(m):
+    """ReLU on the forward; the dX mask applies once, to the sum over the ranks."""
+    p = 1024 // m
+    inp = kron_inputs(46, 300, p, p, m, m, 3, s_mode="uniform", bias_mode="normal")
+    xr = np.maximum(inp.x, 0).astype(np.float32)
+    inp.x = xr
+    y, g = run_layer(inp, relu=True, relu_mask=True)
+    W = OK.weight(inp.S, inp.A, inp.B)
+    assert rel_err(y, np.maximum(xr.astype(np.float64) @ W + inp.bias, 0)) <= TOL_F32
+    go = OK.backward(xr, inp.S, inp.A, inp.B, inp.dy, W=W)
+    assert rel_err(g["dx"], go["dx"] * (xr > 0)) <= TOL_F32
+    assert np.all(g["dx"][xr <= 0] == 0)
+    for k in ("dS", "dA", "dB", "dbias"):
+        assert rel_err(g[k], go[k]) <= TOL_F32, k
+
+
+def test_small_block_integer_inputs_exact():
+    """Small-integer inputs keep every partial sum exact: the small-block path equals the
+    oracle bit for bit (this pins its indexing independently of rounding)."""
+    for p, m in ((128, 8), (256, 4)):
+        inp = integer_kron_inputs(47, 20, p, p, m, m, 2, lo=-1, hi=2)
+        y, g = run_layer(inp)
+        W = OK.weight(inp.S, inp.A, inp.B)
+        assert np.array_equal(y, inp.x.astype(np.float64) @ W + inp.bias)
+        go = OK.backward(inp.x, inp.S, inp.A, inp.B, inp.dy, W=W)
+        for k in ("dx", "dS", "dA", "dB", "dbias"):
+            assert np.array_equal(g[k], go[k]), (p, k)
+
+
+def test_small_block_deterministic():
+    inp = kron_inputs(48, 4099, 256, 256, 4, 4, 2, s_mode="uniform_zeroed", bias_mode="normal")
+    x, S, A, B, dy = (dev(a) for a in (inp.x, inp.S, inp.A, inp.B, inp.dy))
+    outs = []
+    for _ in range(2):
+        y = K().kron_linear_fwd(x, S, A, B, None)
+        g = K().kron_linear_bwd(x, S, A, B, dy)
+        outs.append([bits(y)] + [bits(g[k]) for k in ("dx", "dS", "dA", "dB", "dbias")])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
