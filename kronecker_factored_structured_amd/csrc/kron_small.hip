@@ -65,6 +65,37 @@ __device__ __forceinline__ void store_vec(float* p, const float (&v)[M]) {
   }
 }
 
+// Lane stride of an LDS factor table in which each lane's T tile values of one inner index
+// are contiguous (one or a few 8/16-byte reads): conflict-free for the 8 or 16 lanes a
+// read serves at a time.
+constexpr int lane_stride(int T) { return T == 2 ? 2 : T == 4 ? 4 : T + 4; }
+
+template <int T>
+__device__ __forceinline__ void read_tiles(float (&v)[T], const float* p) {
+  if constexpr (T == 2) {
+    const f2 a = *reinterpret_cast<const f2*>(p);
+    v[0] = a[0]; v[1] = a[1];
+  } else {
+    static_assert(T % 4 == 0, "2, 4, 8 or 16 tiles");
+#pragma unroll
+    for (int u = 0; u < T / 4; ++u) {
+      const f4 a = *reinterpret_cast<const f4*>(p + 4 * u);
+      v[4 * u] = a[0]; v[4 * u + 1] = a[1]; v[4 * u + 2] = a[2]; v[4 * u + 3] = a[3];
+    }
+  }
+}
+
+// An empty use of registers loaded before a loop: the wait for those loads is placed
+// here once, instead of inside the loop on every trip (the wait-count pass merges the
+// loop entry's pending loads into the loop header).
+template <int A, int B>
+__device__ __forceinline__ void settle(float (&v)[A][B]) {
+#pragma unroll
+  for (int a = 0; a < A; ++a)
+#pragma unroll
+    for (int b = 0; b < B; ++b) asm volatile("" ::"v"(v[a][b]));
+}
+
 template <int CTRL, int ROWMASK>
 __device__ __forceinline__ float dpp_add_src(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWMASK, 0xF, false));
@@ -100,7 +131,8 @@ template <int NB>
 struct SbF {
   static constexpr int KT = 32 / NB;        // 16-wide k tiles per workgroup: 4 KT NB = 128 accumulators
   static constexpr int TN = 16 * KT;
-  static constexpr int LD = TN + 16;        // chunk row stride: lanes 0-31 read two rows on disjoint banks
+  static constexpr int KS = lane_stride(KT);
+  static constexpr int LD = 16 * KS;        // one inner index: lane c16's KT values at c16 * KS
   static constexpr int NST = TN / 64;       // float4s of the chunk per thread
 };
 
@@ -113,7 +145,7 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_fwd_kernel(int64_t N, int p,
                                                              const float* __restrict__ bias,
                                                              float* __restrict__ y) {
   using F = SbF<NB>;
-  constexpr int KT = F::KT, TN = F::TN, LD = F::LD, NST = F::NST;
+  constexpr int KT = F::KT, TN = F::TN, KS = F::KS, LD = F::LD, NST = F::NST;
   __shared__ __align__(16) float cs[2][kSbKC * LD];
   const int nkb = (q + TN - 1) / TN;
   int kb;
@@ -128,7 +160,12 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_fwd_kernel(int64_t N, int p,
   const float* xr = x + (arow < N ? arow : N - 1) * in;
   const int nch = r * (p / kSbKC);
 
-  f4 st[NST];
+  // A_i and S pieces are loaded raw (S read from A's address when absent, so the loads are
+  // unconditional) and multiplied only when stored, so no wait for them precedes the
+  // chunk's products
+  const bool hs = S != nullptr;
+  const float* Sp = hs ? S : A;
+  f4 sta[NST], sts[NST];
   auto stage_load = [&](int ch) {
     const int kap0 = ch * kSbKC, i = kap0 / p, j0 = kap0 - i * p;
     const float* Ai = A + (int64_t)i * pq;
@@ -136,11 +173,9 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_fwd_kernel(int64_t N, int p,
     for (int u = 0; u < NST; ++u) {
       const int f = tid + u * kSbThreads;
       const int kk = f / (TN / 4), kc = 4 * (f % (TN / 4));
-      const bool ok = k0 + kc < q;
-      const int64_t e = (int64_t)(j0 + kk) * q + (ok ? k0 + kc : 0);
-      f4 a = *reinterpret_cast<const f4*>(Ai + e);
-      if (S) a *= *reinterpret_cast<const f4*>(S + e);
-      st[u] = ok ? a : f4{0.f, 0.f, 0.f, 0.f};
+      const int64_t e = (int64_t)(j0 + kk) * q + (k0 + kc < q ? k0 + kc : 0);
+      sta[u] = *reinterpret_cast<const f4*>(Ai + e);
+      sts[u] = *reinterpret_cast<const f4*>(Sp + e);
     }
   };
   auto stage_store = [&](int buf) {
@@ -148,7 +183,10 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_fwd_kernel(int64_t N, int p,
     for (int u = 0; u < NST; ++u) {
       const int f = tid + u * kSbThreads;
       const int kk = f / (TN / 4), kc = 4 * (f % (TN / 4));
-      *reinterpret_cast<f4*>(&cs[buf][kk * LD + kc]) = st[u];
+      const f4 a = k0 + kc < q ? (hs ? sta[u] * sts[u] : sta[u]) : f4{0.f, 0.f, 0.f, 0.f};
+      const int t = kc >> 4, cl = kc & 15;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) cs[buf][kk * LD + (cl + h) * KS + t] = a[h];
     }
   };
   float xv[4][MB], xn[4][MB];
@@ -167,6 +205,7 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_fwd_kernel(int64_t N, int p,
   stage_load(0);
   x_load(0, xv);
   stage_store(0);
+  settle(xv);
   __syncthreads();
   for (int ch = 0; ch < nch; ++ch) {
     const int buf = ch & 1;
@@ -175,6 +214,7 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_fwd_kernel(int64_t N, int p,
       stage_load(ch + 1);
       x_load(ch + 1, xn);
     }
+    __builtin_amdgcn_sched_barrier(0);
     const int i = (ch * kSbKC) / p;
     const float* Bi = B + (int64_t)i * MB * NB;
     float bm[MB][NB];
@@ -182,8 +222,11 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_fwd_kernel(int64_t N, int p,
     for (int b = 0; b < MB; ++b)
 #pragma unroll
       for (int c = 0; c < NB; ++c) bm[b][c] = Bi[b * NB + c];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    // the factor values of step s + 1 are read while step s's products run; the
+    // scheduling barrier keeps the compiler from hoisting further reads (registers)
+    float bo0[KT], bo1[KT];
+    auto kstep = [&](const int s, float (&cur)[KT], float (&nxt)[KT]) {
+      if (s < 3) read_tiles<KT>(nxt, &cs[buf][(4 * (s + 1) + g) * LD + c16 * KS]);
       float z[NB];
 #pragma unroll
       for (int c = 0; c < NB; ++c) {
@@ -191,14 +234,17 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_fwd_kernel(int64_t N, int p,
 #pragma unroll
         for (int b = 0; b < MB; ++b) z[c] = fmaf(xv[s][b], bm[b][c], z[c]);
       }
-      const float* crow = &cs[buf][(4 * s + g) * LD + c16];
 #pragma unroll
-      for (int t = 0; t < KT; ++t) {
-        const float bo = crow[16 * t];
+      for (int t = 0; t < KT; ++t)
 #pragma unroll
-        for (int c = 0; c < NB; ++c) acc[t][c] = mfma(z[c], bo, acc[t][c]);
-      }
-    }
+        for (int c = 0; c < NB; ++c) acc[t][c] = mfma(z[c], cur[t], acc[t][c]);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    read_tiles<KT>(bo0, &cs[buf][g * LD + c16 * KS]);
+    kstep(0, bo0, bo1);
+    kstep(1, bo1, bo0);
+    kstep(2, bo0, bo1);
+    kstep(3, bo1, bo0);
     if (more) {
       stage_store(buf ^ 1);
 #pragma unroll
@@ -212,7 +258,7 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_fwd_kernel(int64_t N, int p,
   // lane (g, c16) holds Y_c[row = 4g + v][k = k0 + 16t + c16] in acc[t][c][v]
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
-    if (t >= ktv) break;
+    if (t >= ktv) continue;
     const int k = k0 + 16 * t + c16;
     float bb[NB];
 #pragma unroll
@@ -245,7 +291,8 @@ template <int NB>
 struct SbG {
   static constexpr int JT = 16 / NB;        // 16-wide j tiles: 4 JT NB = 64 accumulators
   static constexpr int TN = 16 * JT;
-  static constexpr int LD = TN + 16;
+  static constexpr int KS = lane_stride(JT);
+  static constexpr int LD = 16 * KS;        // one k: lane c16's JT values at c16 * KS
   static constexpr int NST = (4 * TN + kSbThreads - 1) / kSbThreads;
 };
 
@@ -260,7 +307,7 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_bwd_g_kernel(int64_t N, int 
                                                                float* __restrict__ dx,
                                                                float* __restrict__ part) {
   using Gd = SbG<NB>;
-  constexpr int JT = Gd::JT, TN = Gd::TN, LD = Gd::LD, NST = Gd::NST, MN = MB * NB;
+  constexpr int JT = Gd::JT, TN = Gd::TN, KS = Gd::KS, LD = Gd::LD, NST = Gd::NST, MN = MB * NB;
   __shared__ __align__(16) float cs[2][kSbKC * LD];
   __shared__ float dbs[4][kSbMaxRank * MN];
   __shared__ float bms[kSbMaxRank * MN];
@@ -269,6 +316,8 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_bwd_g_kernel(int64_t N, int 
   const int njb = (p + TN - 1) / TN;
   const int nkc = q / kSbKC;
   const int nch = r * nkc;
+  const bool hs = S != nullptr;
+  const float* Sp = hs ? S : A;
   for (int e = tid; e < 4 * kSbMaxRank * MN; e += kSbThreads) (&dbs[0][0])[e] = 0.f;
   for (int e = tid; e < r * MN; e += kSbThreads) bms[e] = B[e];
   __syncthreads();
@@ -282,7 +331,8 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_bwd_g_kernel(int64_t N, int 
     const int64_t arow = rb * 64 + w * 16 + c16;
     const float* yr = dy + (arow < N ? arow : N - 1) * out;
 
-    f4 st[NST];
+    // raw A_i and S pieces (S read from A's address when absent), multiplied when stored
+    f4 sta[NST], sts[NST];
     auto stage_load = [&](int ch) {
       const int i = ch / nkc, kc0 = (ch - i * nkc) * kSbKC;
       const float* Ai = A + (int64_t)i * pq;
@@ -292,9 +342,8 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_bwd_g_kernel(int64_t N, int 
         const int jj = f >> 2, kq = f & 3;
         const bool ok = f < 4 * TN && j0 + jj < p;
         const int64_t e = (int64_t)(ok ? j0 + jj : 0) * q + kc0 + 4 * kq;
-        f4 a = *reinterpret_cast<const f4*>(Ai + e);
-        if (S) a *= *reinterpret_cast<const f4*>(S + e);
-        st[u] = ok ? a : f4{0.f, 0.f, 0.f, 0.f};
+        sta[u] = *reinterpret_cast<const f4*>(Ai + e);
+        sts[u] = *reinterpret_cast<const f4*>(Sp + e);
       }
     };
     auto stage_store = [&](int buf) {
@@ -303,8 +352,9 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_bwd_g_kernel(int64_t N, int 
         const int f = tid + u * kSbThreads;
         if (4 * TN % kSbThreads != 0 && f >= 4 * TN) continue;
         const int jj = f >> 2, kq = f & 3;
+        const f4 a = j0 + jj < p ? (hs ? sta[u] * sts[u] : sta[u]) : f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int h = 0; h < 4; ++h) cs[buf][(4 * kq + h) * LD + jj] = st[u][h];
+        for (int h = 0; h < 4; ++h) cs[buf][(4 * kq + h) * LD + (jj & 15) * KS + (jj >> 4)] = a[h];
       }
     };
     float yv[4][NB], yn[4][NB];
@@ -323,6 +373,7 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_bwd_g_kernel(int64_t N, int 
     stage_load(0);
     y_load(0, yv);
     stage_store(0);
+    settle(yv);
     __syncthreads();
     for (int ch = 0; ch < nch; ++ch) {
       const int buf = ch & 1;
@@ -332,15 +383,15 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_bwd_g_kernel(int64_t N, int 
         stage_load(ch + 1);
         y_load(ch + 1, yn);
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const float* crow = &cs[buf][(4 * s + g) * LD + c16];
+        float bo[JT];
+        read_tiles<JT>(bo, &cs[buf][(4 * s + g) * LD + c16 * KS]);
 #pragma unroll
-        for (int t = 0; t < JT; ++t) {
-          const float bo = crow[16 * t];
+        for (int t = 0; t < JT; ++t)
 #pragma unroll
-          for (int c = 0; c < NB; ++c) acc[t][c] = mfma(yv[s][c], bo, acc[t][c]);
-        }
+          for (int c = 0; c < NB; ++c) acc[t][c] = mfma(yv[s][c], bo[t], acc[t][c]);
       }
       if (rank_end) {
         // lane (g, c16) holds G_{i,c}[row = 4g + v][j = j0 + 16t + c16] in acc[t][c][v].
@@ -365,11 +416,15 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_bwd_g_kernel(int64_t N, int 
           for (int t = 0; t < JT; ++t) {
             const int j = j0 + 16 * t + lj;
             const int jc = j < p ? j : p - 1;
+            // x of dead rows is zeroed (their G, from a clamped dY row, is not); G of
+            // dead j is zero already (zero factor columns were staged)
             float xt[4][MB];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
               const int64_t row = rb * 64 + w * 16 + lrow + v;
               load_vec<MB>(xt[v], x + (row < N ? row : N - 1) * in + (int64_t)jc * MB);
+#pragma unroll
+              for (int b = 0; b < MB; ++b) xt[v][b] = row < N ? xt[v][b] : 0.f;
             }
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
@@ -404,17 +459,20 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_bwd_g_kernel(int64_t N, int 
               for (int b = 0; b < MB; ++b)
 #pragma unroll
                 for (int c = 0; c < CW; ++c)
-                  dbp[b][c] = fmaf(xt[v][b], live ? acc[t][cp * CW + c][v] : 0.f, dbp[b][c]);
+                  dbp[b][c] = fmaf(xt[v][b], acc[t][cp * CW + c][v], dbp[b][c]);
             }
             __builtin_amdgcn_sched_barrier(0);
           }
 #pragma unroll
           for (int b = 0; b < MB; ++b)
 #pragma unroll
-            for (int c = 0; c < CW; ++c) {
-              const float tot = wave_total_lane63(dbp[b][c]);
-              if (lane == 63) dbs[w][i * MN + b * NB + cp * CW + c] += tot;
-            }
+            for (int c = 0; c < CW; ++c) dbp[b][c] = wave_total_lane63(dbp[b][c]);
+          if (lane == 63) {
+#pragma unroll
+            for (int b = 0; b < MB; ++b)
+#pragma unroll
+              for (int c = 0; c < CW; ++c) dbs[w][i * MN + b * NB + cp * CW + c] += dbp[b][c];
+          }
         }
 #pragma unroll
         for (int t = 0; t < JT; ++t)
