@@ -1,7 +1,7 @@
 """Benchmark of the Kronecker-factored layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--cpu-seconds 10]
-    python bench.py --workload {headline,headline_bf16,tiny,mlp_step,gpt2_ffn,ks,ks_bwd,chain,van_loan,sweep}
+    python bench.py --workload {headline,headline_bf16,tiny,mlp_step,gpt2_ffn,ks,ks_bwd,chain,van_loan,sweep,small_blocks}
     python bench.py --calibrate-copy      (plain device copy of known size, for HBM counters)
 
 Default workload (one JSON line): one step is one kron_linear_fwd + one kron_linear_bwd
@@ -379,6 +379,16 @@ def run_gpt2(args, dev):
         layer_record(f"gpt2 ffn 3072->768 (A 64x32, B 48x24), r={r}, 8192 rows", down, Layer(down, dev), args)
 
 
+def run_small_blocks(args, dev):
+    """The tutorial's 1024 x 1024 layer with small blocks (8x8, 4x4, 2x2; the settings its
+    batch-20,000 results single out), half of S zeroed, 20,000 rows."""
+    from workloads import kron_inputs
+    for p, m, r in ((128, 8, 1), (128, 8, 2), (256, 4, 1), (256, 4, 2), (512, 2, 1)):
+        inp = kron_inputs(80 + r, 20000, p, p, m, m, r, s_mode="uniform_zeroed", bias_mode="zeros")
+        layer_record(f"small_blocks: 1024x1024 layer, {m}x{m} blocks (p=q={p}), r={r}, half of S zeroed, "
+                     f"20000 rows", inp, Layer(inp, dev), args)
+
+
 def run_mlp_step(args, dev):
     import torch
     import kronecker_factored_structured_amd as K
@@ -557,7 +567,8 @@ def run_sweep(args, dev):
     import torch
     from workloads import kron_inputs
     steps = max(5, min(args.steps, 20))
-    configs = [(32, 32, 32, 32, 4), (32, 32, 32, 32, 1), (16, 16, 64, 64, 2), (128, 128, 8, 8, 1)]
+    configs = [(32, 32, 32, 32, 4), (32, 32, 32, 32, 1), (16, 16, 64, 64, 2), (128, 128, 8, 8, 1),
+               (128, 128, 8, 8, 2), (256, 256, 4, 4, 1), (256, 256, 4, 4, 2), (512, 512, 2, 2, 1)]
     lam = 1e-4
     for N in (256, 1024, 4096, 20000, 65536):
         rec = {"workload": f"sweep: 1024x1024 layer fwd+bwd, {N} rows", "N": N}
@@ -595,6 +606,7 @@ def run_sweep(args, dev):
         rec["dense us"] = round(ms_d * 1e3, 2)
         rec["dense+group-lasso us"] = round(ms_l * 1e3, 2)
         rec["kron r4 m32 speedup vs dense"] = round(ms_d / (rec["kron p32 m32 r4 us"] * 1e-3), 3)
+        rec["kron r1 m8 speedup vs dense"] = round(ms_d / (rec["kron p128 m8 r1 us"] * 1e-3), 3)
         print(json.dumps(rec), flush=True)
 
 
@@ -621,7 +633,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the copy and GEMM ceiling measurements")
     ap.add_argument("--workload", default="headline",
-                    choices=("headline", "headline_bf16", "tiny", "mlp_step", "gpt2_ffn", "ks", "ks_bwd", "chain", "van_loan", "sweep"))
+                    choices=("headline", "headline_bf16", "tiny", "mlp_step", "gpt2_ffn", "ks", "ks_bwd", "chain", "van_loan", "sweep", "small_blocks"))
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed running before the warmup steps, for the GPU clock to ramp up")
@@ -638,7 +650,7 @@ def main():
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         return run_copy(args, dev)
-    {"headline": run_headline, "headline_bf16": run_headline_bf16, "tiny": run_tiny, "sweep": run_sweep, "ks_bwd": run_ks_bwd, "chain": run_chain, "van_loan": run_van_loan, "mlp_step": run_mlp_step, "gpt2_ffn": run_gpt2,
+    {"headline": run_headline, "headline_bf16": run_headline_bf16, "tiny": run_tiny, "sweep": run_sweep, "small_blocks": run_small_blocks, "ks_bwd": run_ks_bwd, "chain": run_chain, "van_loan": run_van_loan, "mlp_step": run_mlp_step, "gpt2_ffn": run_gpt2,
      "ks": run_ks}[args.workload](args, dev)
 
 

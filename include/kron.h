@@ -66,8 +66,9 @@ typedef struct {
 } kron_shape_t;
 
 /* Limits of this build: 1 <= p,q,m,n <= 4096, 1 <= r <= 64, p*m and q*n <= 65536,
- * N <= 2^31 - 1; r*p*q and r*m*n <= 2^24.  Shapes whose per-row working set does not
- * fit in one workgroup's LDS return KRON_E_UNSUPPORTED. */
+ * N <= 2^31 - 1; r*p*q and r*m*n <= 2^24.  Small square blocks (m = n in {2, 4, 8},
+ * p and q multiples of 16, r <= 16) always run; other shapes whose per-row working set
+ * does not fit in one workgroup's LDS return KRON_E_UNSUPPORTED. */
 
 int32_t kron_abi_version(void);
 const char* kron_status_str(int32_t status);
