@@ -687,14 +687,21 @@ __global__ __launch_bounds__(256) void sb_dcs_kernel(int64_t pq, int r, const fl
 
 int64_t round8(int64_t v) { return (v + 7) / 8 * 8; }
 
+// One launch per 2^24 rows at most, so the grid (a workgroup per 64 rows and k block)
+// stays far below the 2^31 limit for every valid shape.
 template <int MB>
 void fwd_small(const LayerArgs& a, hipStream_t s) {
   constexpr int NB = MB;
-  const int64_t nrb = (a.N + 63) / 64;
+  constexpr int64_t kRowsPerLaunch = int64_t(1) << 24;
   const int nkb = (a.q + SbF<NB>::TN - 1) / SbF<NB>::TN;
-  const int64_t grid = 8 * nkb * ((nrb + 7) / 8);
-  hipLaunchKernelGGL((sb_fwd_kernel<MB, NB>), dim3((unsigned)grid), dim3(kSbThreads), 0, s, a.N, a.p, a.q, a.r,
-                     a.flags, a.x, a.S, a.A, a.B, a.bias, a.y);
+  const int64_t in = (int64_t)a.p * MB, out = (int64_t)a.q * NB;
+  for (int64_t r0 = 0; r0 < a.N; r0 += kRowsPerLaunch) {
+    const int64_t rows = std::min(kRowsPerLaunch, a.N - r0);
+    const int64_t nrb = (rows + 63) / 64;
+    const int64_t grid = 8 * nkb * ((nrb + 7) / 8);
+    hipLaunchKernelGGL((sb_fwd_kernel<MB, NB>), dim3((unsigned)grid), dim3(kSbThreads), 0, s, rows, a.p, a.q, a.r,
+                       a.flags, a.x + r0 * in, a.S, a.A, a.B, a.bias, a.y + r0 * out);
+  }
 }
 
 template <int MB, int DXM>

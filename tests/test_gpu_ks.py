@@ -194,7 +194,7 @@ def test_ks_backward_vit_shape_full_size(dtype):
 
 @pytest.mark.parametrize("N", [0, 1, 37, 300])
 @pytest.mark.parametrize("abcd", [(1, 5, 7, 1), (3, 4, 2, 5), (2, 3, 130, 2), (4, 1, 1, 3), (1, 64, 64, 1),
-                                  (2, 300, 3, 1)])
+                                  (2, 300, 3, 1), (2, 48, 192, 4), (1, 48, 192, 4)])
 def test_ks_backward_shapes_and_ragged_rows(abcd, N):
     a, b, c, d = abcd
     inp = ks_inputs(46, N, a, b, c, d, "f32")
