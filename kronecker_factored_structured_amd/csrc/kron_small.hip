@@ -207,7 +207,16 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_fwd_kernel(int64_t N, int p,
   stage_store(0);
   settle(xv);
   __syncthreads();
-  for (int ch = 0; ch < nch; ++ch) {
+  // ranks outside, chunks of j inside: B_i goes to scalar registers once per rank
+  const int njc = p / kSbKC;
+  for (int i = 0, ch = 0; i < r; ++i) {
+  const float* Bi = B + (int64_t)i * MB * NB;
+  float bm[MB][NB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b)
+#pragma unroll
+    for (int c = 0; c < NB; ++c) bm[b][c] = Bi[b * NB + c];
+  for (int jc = 0; jc < njc; ++jc, ++ch) {
     const int buf = ch & 1;
     const bool more = ch + 1 < nch;
     if (more) {
@@ -215,36 +224,40 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_fwd_kernel(int64_t N, int p,
       x_load(ch + 1, xn);
     }
     __builtin_amdgcn_sched_barrier(0);
-    const int i = (ch * kSbKC) / p;
-    const float* Bi = B + (int64_t)i * MB * NB;
-    float bm[MB][NB];
-#pragma unroll
-    for (int b = 0; b < MB; ++b)
-#pragma unroll
-      for (int c = 0; c < NB; ++c) bm[b][c] = Bi[b * NB + c];
     // the factor values of step s + 1 are read while step s's products run; the
-    // scheduling barrier keeps the compiler from hoisting further reads (registers)
+    // scheduling barrier keeps the compiler from hoisting further reads (registers).
+    // The A operands of step s + 1 are mixed inside step s, so their VALU work runs
+    // while step s's products occupy the matrix core.
     float bo0[KT], bo1[KT];
-    auto kstep = [&](const int s, float (&cur)[KT], float (&nxt)[KT]) {
-      if (s < 3) read_tiles<KT>(nxt, &cs[buf][(4 * (s + 1) + g) * LD + c16 * KS]);
-      float z[NB];
+    float za[NB], zb[NB];
+    auto mix = [&](const int s, float (&z)[NB]) {
 #pragma unroll
       for (int c = 0; c < NB; ++c) {
         z[c] = 0.f;
 #pragma unroll
         for (int b = 0; b < MB; ++b) z[c] = fmaf(xv[s][b], bm[b][c], z[c]);
       }
+    };
+    auto kstep = [&](const int s, float (&cur)[KT], float (&nxt)[KT], float (&z)[NB], float (&zn)[NB]) {
+      if (s < 3) read_tiles<KT>(nxt, &cs[buf][(4 * (s + 1) + g) * LD + c16 * KS]);
 #pragma unroll
-      for (int t = 0; t < KT; ++t)
+      for (int c = 0; c < NB; ++c) {
 #pragma unroll
-        for (int c = 0; c < NB; ++c) acc[t][c] = mfma(z[c], cur[t], acc[t][c]);
+        for (int t = 0; t < KT; ++t) acc[t][c] = mfma(z[c], cur[t], acc[t][c]);
+        if (s < 3) {
+          zn[c] = 0.f;
+#pragma unroll
+          for (int b = 0; b < MB; ++b) zn[c] = fmaf(xv[s + 1][b], bm[b][c], zn[c]);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     };
     read_tiles<KT>(bo0, &cs[buf][g * LD + c16 * KS]);
-    kstep(0, bo0, bo1);
-    kstep(1, bo1, bo0);
-    kstep(2, bo0, bo1);
-    kstep(3, bo1, bo0);
+    mix(0, za);
+    kstep(0, bo0, bo1, za, zb);
+    kstep(1, bo1, bo0, zb, za);
+    kstep(2, bo0, bo1, za, zb);
+    kstep(3, bo1, bo0, zb, za);
     if (more) {
       stage_store(buf ^ 1);
 #pragma unroll
@@ -253,6 +266,7 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_fwd_kernel(int64_t N, int p,
         for (int b = 0; b < MB; ++b) xv[s][b] = xn[s][b];
     }
     __syncthreads();
+  }
   }
 
   // lane (g, c16) holds Y_c[row = 4g + v][k = k0 + 16t + c16] in acc[t][c][v]
