@@ -262,6 +262,12 @@ def test_small_block_full_size(case):
     compare_layer(kron_inputs(43, 20000, p, p, m, m, r, s_mode="uniform_zeroed", bias_mode="normal"))
 
 
+def test_small_blocks_beyond_rank16_take_the_generic_kernels():
+    """r = 17 at 8 x 8 blocks is past the small-block kernels' rank limit and runs on the
+    generic kernels (S and C_i of 128 x 128 fit their LDS)."""
+    compare_layer(kron_inputs(49, 37, 128, 128, 8, 8, 17, s_mode="uniform_zeroed", bias_mode="normal"))
+
+
 def test_small_block_rank16_without_S_and_dx():
     compare_layer(kron_inputs(44, 200, 128, 128, 8, 8, 16, s_mode="none", bias_mode="normal"), want_dx=False)
     compare_layer(kron_inputs(45, 200, 256, 256, 4, 4, 16, s_mode="none", bias_mode="none"))
