@@ -76,6 +76,22 @@ def test_workspace_size_depends_on_shape_only():
     assert L.kron_linear_bwd_workspace_bytes(ctypes.byref(KronShape(-1, 1, 1, 1, 1, 1, 0))) == 0
 
 
+def test_small_block_workspace():
+    """The small-block backward's workspace holds its two partial arrays (dB rows, then
+    dC and dbias rows of r*p*q + q*n floats); it grows with N only up to the row-group cap."""
+    L = _lib.lib()
+    ws = lambda N, p, m, r: L.kron_linear_bwd_workspace_bytes(ctypes.byref(KronShape(N, p, p, m, m, r, 0)))
+    for p, m in ((128, 8), (256, 4), (512, 2)):
+        w = ws(20000, p, m, 1)
+        assert w > 0 and w % 256 == 0
+        assert w >= 8 * (p * p + p * m) * 4            # at least 8 row groups of dC + dbias
+        assert ws(0, p, m, 1) > 0                        # an empty batch still writes zero partials
+        assert ws(10 ** 6, p, m, 1) == ws(2 * 10 ** 6, p, m, 1)
+    # more ranks mean more dC tiles per row group and so fewer row groups: the partial
+    # storage stays near 512 workgroups' worth
+    assert 0.5 < ws(20000, 128, 8, 2) / ws(20000, 128, 8, 1) < 2
+
+
 def fwd(shape, x, S, A, B, bias, y):
     return _lib.lib().kron_linear_fwd(ctypes.byref(shape), x, S, A, B, bias, y, None)
 
