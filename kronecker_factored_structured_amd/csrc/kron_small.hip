@@ -297,9 +297,9 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_fwd_kernel(int64_t N, int p,
 // rank the G_{i,c} tiles (rows x j, one per c) accumulate over k in chunks of 16, whose
 // C_i^T chunk (16 x TN) is staged in LDS; dY's n floats at (row, k) are the A operands of
 // the n products.  After the rank's last chunk its G is folded into dX (mixing by B_i^T,
-// summed over the ranks in registers) and into this lane's share of dB_i, which is summed
-// over the wavefront in a fixed order and added to the wavefront's LDS slot.  Workgroups
-// are persistent over tiles; each writes one partial row of dB (all ranks).
+// added in place to the rank-sum in dx) and into this lane's share of dB_i, which is
+// summed over the wavefront in a fixed order and added to the wavefront's LDS slot.
+// Workgroups are persistent over tiles; each writes one partial row of dB (all ranks).
 // ---------------------------------------------------------------------------------
 template <int NB>
 struct SbG {
