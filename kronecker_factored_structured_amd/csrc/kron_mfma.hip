@@ -42,15 +42,16 @@
 #define KRON_MFMA_PASS 0
 #endif
 
-// The shapes with matrix-core kernels, (p, q, m, n, r, prefer the rank-parallel backward):
-// the 64x64 tiny layer (m = 8), the 1024x1024 layers with m = 32 and m = 64, and the
-// GPT-2 FFN pair 768 <-> 3072.
+// The shapes with matrix-core kernels, (p, q, m, n, r, backward kernel): the 64x64 tiny
+// layer (m = 8), the 1024x1024 layers with m = 32 and m = 64, and the GPT-2 FFN pair
+// 768 <-> 3072.  Backward kernel (measured per shape): 0 = bwd_mfma_kernel, 1 = the
+// rank-parallel bwd_rp_kernel, 2 = the whole-row bwd_solo_kernel.
 #define KRON_MFMA_SHAPES(X)                                                                             \
-  X(8, 8, 8, 8, 1, true) X(8, 8, 8, 8, 2, true) X(32, 32, 32, 32, 1, true) X(32, 32, 32, 32, 2, true)   \
-  X(32, 32, 32, 32, 4, true) X(16, 16, 64, 64, 1, false) X(16, 16, 64, 64, 2, false)                    \
-  X(32, 64, 24, 48, 1, true) X(32, 64, 24, 48, 2, false) X(32, 64, 24, 48, 4, true)                     \
-  X(32, 64, 24, 48, 8, true) X(64, 32, 48, 24, 1, false) X(64, 32, 48, 24, 2, true)                     \
-  X(64, 32, 48, 24, 4, true) X(64, 32, 48, 24, 8, true)
+  X(8, 8, 8, 8, 1, 1) X(8, 8, 8, 8, 2, 1) X(32, 32, 32, 32, 1, 1) X(32, 32, 32, 32, 2, 1)               \
+  X(32, 32, 32, 32, 4, 2) X(16, 16, 64, 64, 1, 0) X(16, 16, 64, 64, 2, 0)                               \
+  X(32, 64, 24, 48, 1, 1) X(32, 64, 24, 48, 2, 0) X(32, 64, 24, 48, 4, 1)                               \
+  X(32, 64, 24, 48, 8, 1) X(64, 32, 48, 24, 1, 0) X(64, 32, 48, 24, 2, 1)                               \
+  X(64, 32, 48, 24, 4, 1) X(64, 32, 48, 24, 8, 1)
 
 namespace kron {
 
@@ -183,22 +184,43 @@ struct Dims {
   static constexpr bool BWD_PREFETCH = BWD_REGS + ROW_REGS <= 420;   // double-buffer the row operands
 };
 
-// Stage B (as is) and C = S o A in LDS with coalesced 16-byte loads.
+// Stage B (as is) and C = S o A in LDS with coalesced 16-byte loads.  Every global load
+// is issued before the first LDS store, so the staging costs one memory round trip.
 template <class D>
 __device__ __forceinline__ void stage_raw(float* rB, float* rC, const float* __restrict__ B,
                                           const float* __restrict__ S, const float* __restrict__ A) {
   constexpr int PQ = D::P * D::Q;
-#pragma unroll 4
-  for (int e = threadIdx.x; e < D::RAWB / 4; e += kThreads)
-    reinterpret_cast<f4*>(rB)[e] = reinterpret_cast<const f4*>(B)[e];
   if constexpr (PQ % 4 == 0) {
-#pragma unroll 4
-    for (int e = threadIdx.x; e < D::R * PQ / 4; e += kThreads) {
-      f4 a = reinterpret_cast<const f4*>(A)[e];
-      if (S) a *= reinterpret_cast<const f4*>(S)[e % (PQ / 4)];
-      reinterpret_cast<f4*>(rC)[e] = a;
+    constexpr int NB = D::RAWB / 4, NC = D::R * PQ / 4;
+    constexpr int KB = (NB + kThreads - 1) / kThreads, KC = (NC + kThreads - 1) / kThreads;
+    f4 b[KB], a[KC], m[KC];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int e = threadIdx.x + k * kThreads;
+      if (NB % kThreads == 0 || e < NB) b[k] = reinterpret_cast<const f4*>(B)[e];
+    }
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      const int e = threadIdx.x + k * kThreads;
+      if (NC % kThreads == 0 || e < NC) {
+        a[k] = reinterpret_cast<const f4*>(A)[e];
+        m[k] = S ? reinterpret_cast<const f4*>(S)[e % (PQ / 4)] : f4{1.f, 1.f, 1.f, 1.f};
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int e = threadIdx.x + k * kThreads;
+      if (NB % kThreads == 0 || e < NB) reinterpret_cast<f4*>(rB)[e] = b[k];
+    }
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      const int e = threadIdx.x + k * kThreads;
+      if (NC % kThreads == 0 || e < NC) reinterpret_cast<f4*>(rC)[e] = S ? a[k] * m[k] : a[k];
     }
   } else {
+#pragma unroll 4
+    for (int e = threadIdx.x; e < D::RAWB / 4; e += kThreads)
+      reinterpret_cast<f4*>(rB)[e] = reinterpret_cast<const f4*>(B)[e];
     for (int e = threadIdx.x; e < D::R * PQ; e += kThreads) rC[e] = S ? S[e % PQ] * A[e] : A[e];
   }
 }
@@ -280,6 +302,16 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
   // the first row's X is loaded while the tables are built
   float xa[D::TJ][D::SA];   // X[j = 16tj+c][a = g*SA+s]
   if (row < N) load_xa<D>(xa, x + row * D::IN, g, c);
+  // the bias is loaded with the first row, before the tables are built
+  f4 bb[D::TB][D::TK];
+#pragma unroll
+  for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+    for (int tk = 0; tk < D::TK; ++tk) {
+      const int k = 16 * tk + c, b0 = 16 * tb + 4 * g;
+      bb[tb][tk] = (bias && k < D::Q && b0 < D::N) ? *reinterpret_cast<const f4*>(bias + k * D::N + b0)
+                                                  : f4{0.f, 0.f, 0.f, 0.f};
+    }
   if constexpr (D::FWD_RAW) {
     float* rB = cop + D::COPF;
     float* rC = rB + D::RAWB;
@@ -305,15 +337,6 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
   }
   __syncthreads();
 
-  f4 bb[D::TB][D::TK];
-#pragma unroll
-  for (int tb = 0; tb < D::TB; ++tb)
-#pragma unroll
-    for (int tk = 0; tk < D::TK; ++tk) {
-      const int k = 16 * tk + c, b0 = 16 * tb + 4 * g;
-      bb[tb][tk] = (bias && k < D::Q && b0 < D::N) ? *reinterpret_cast<const f4*>(bias + k * D::N + b0)
-                                                  : f4{0.f, 0.f, 0.f, 0.f};
-    }
   const bool relu = flags & KRON_RELU_OUT;
 
   // The next row's X is loaded at the top of each row (the last row reloads itself), and
@@ -708,15 +731,27 @@ struct RP {
   static constexpr int DXP = 16 * D::TJ * LDXP;
   static constexpr int WREG = GS > DXP ? GS : DXP;  // per wavefront: G tile, then dX partial
   static constexpr int RAWMAX = D::RAWB > D::RAWC ? D::RAWB : D::RAWC;
-  static constexpr int WORK = (ROWBUF + 4 * WREG) > RAWMAX ? (ROWBUF + 4 * WREG) : RAWMAX;
-  static constexpr int MAIN = TABLES + WORK;
   static constexpr int COMBINE = RPI * D::PWW;
-  static constexpr size_t LDS = (size_t)(MAIN > COMBINE ? MAIN : COMBINE) * 4;
-  static constexpr int NF4 = ROWBUF / SLOT * (D::IN + D::OUT) / 4;   // float4s staged per step
-  static constexpr int NPF = (NF4 + kThreads - 1) / kThreads;
+  static constexpr int STEPW = ROWBUF + 4 * WREG;
+  // the work area stages B and then C (two passes), or both at once when that still
+  // leaves room for the same number of workgroups per compute unit
+  static constexpr int WORK2 = STEPW > RAWMAX ? STEPW : RAWMAX;
+  static constexpr int WORK1 = STEPW > D::RAWB + D::RAWC ? STEPW : D::RAWB + D::RAWC;
+  static constexpr size_t lds_of(int work) {
+    return (size_t)((TABLES + work) > COMBINE ? (TABLES + work) : COMBINE) * 4;
+  }
   // workgroups per compute unit: two when their LDS fits twice (two wavefronts per SIMD),
   // else one (one wavefront per SIMD, with the whole register file)
-  static constexpr int WPC = LDS * 2 <= kMaxLds ? 2 : 1;
+  static constexpr int WPC = lds_of(WORK2) * 2 <= kMaxLds ? 2 : 1;
+  static constexpr bool ONE_PASS = lds_of(WORK1) * WPC <= kMaxLds;
+  static constexpr int WORK = ONE_PASS ? WORK1 : WORK2;
+  static constexpr int MAIN = TABLES + WORK;
+  static constexpr size_t LDS = lds_of(WORK);
+  // padded row entries are read (and must stay zero) unless every dimension is a
+  // multiple of 16
+  static constexpr bool PADDED = D::P % 16 != 0 || D::Q % 16 != 0 || D::M % 16 != 0 || D::N % 16 != 0;
+  static constexpr int NF4 = ROWBUF / SLOT * (D::IN + D::OUT) / 4;   // float4s staged per step
+  static constexpr int NPF = (NF4 + kThreads - 1) / kThreads;
   static constexpr bool OK = (R == 1 || R == 2 || R == 4) && LDS <= kMaxLds && D::IN % 4 == 0 &&
                              D::OUT % 4 == 0;
 };
@@ -779,24 +814,44 @@ void bwd_rp_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, const
   };
   fetch(blockIdx.x);
 
-  // operand tables, B first and then C through the same staging area
-  stage_raw_b<D>(work, B);
-  __syncthreads();
-  build_table<D::R, D::TB, D::SA>(bop, [&](int i, int tb, int gg, int cc, int s) {
-    return rawB<D>(work, i, gg * D::SA + s, 16 * tb + cc);
-  });
-  build_table<D::R, D::TA, D::TB * 4>(bopx, [&](int i, int ta, int gg, int cc, int sv) {
-    return rawB<D>(work, i, 16 * ta + cc, 16 * (sv / 4) + 4 * gg + (sv % 4));
-  });
-  __syncthreads();
-  stage_raw_c<D>(work, Sm, A);
-  __syncthreads();
-  build_table<D::R, D::TJ, Q::SKP>(copg, [&](int i, int tj, int gg, int cc, int s) {
-    return rawC<D>(work, i, 16 * tj + cc, kidx(s, gg));
-  });
-  __syncthreads();
-  for (int e = tid; e < Q::ROWBUF; e += kThreads) rowbuf[e] = 0.f;   // padding stays zero
-  __syncthreads();
+  if constexpr (Q::ONE_PASS) {
+    // operand tables from B and C staged together (one memory round trip)
+    float* rB = work;
+    float* rC = work + D::RAWB;
+    stage_raw<D>(rB, rC, B, Sm, A);
+    __syncthreads();
+    build_table<D::R, D::TB, D::SA>(bop, [&](int i, int tb, int gg, int cc, int s) {
+      return rawB<D>(rB, i, gg * D::SA + s, 16 * tb + cc);
+    });
+    build_table<D::R, D::TA, D::TB * 4>(bopx, [&](int i, int ta, int gg, int cc, int sv) {
+      return rawB<D>(rB, i, 16 * ta + cc, 16 * (sv / 4) + 4 * gg + (sv % 4));
+    });
+    build_table<D::R, D::TJ, Q::SKP>(copg, [&](int i, int tj, int gg, int cc, int s) {
+      return rawC<D>(rC, i, 16 * tj + cc, kidx(s, gg));
+    });
+    __syncthreads();
+  } else {
+    // operand tables, B first and then C through the same staging area
+    stage_raw_b<D>(work, B);
+    __syncthreads();
+    build_table<D::R, D::TB, D::SA>(bop, [&](int i, int tb, int gg, int cc, int s) {
+      return rawB<D>(work, i, gg * D::SA + s, 16 * tb + cc);
+    });
+    build_table<D::R, D::TA, D::TB * 4>(bopx, [&](int i, int ta, int gg, int cc, int sv) {
+      return rawB<D>(work, i, 16 * ta + cc, 16 * (sv / 4) + 4 * gg + (sv % 4));
+    });
+    __syncthreads();
+    stage_raw_c<D>(work, Sm, A);
+    __syncthreads();
+    build_table<D::R, D::TJ, Q::SKP>(copg, [&](int i, int tj, int gg, int cc, int s) {
+      return rawC<D>(work, i, 16 * tj + cc, kidx(s, gg));
+    });
+    __syncthreads();
+  }
+  if constexpr (Q::PADDED || !Q::ONE_PASS) {
+    for (int e = tid; e < Q::ROWBUF; e += kThreads) rowbuf[e] = 0.f;   // padding stays zero
+    __syncthreads();
+  }
 
   const float* bop_i = bop + rank * D::TB * 64 * D::SA;
   const float* copg_i = copg + rank * D::TJ * 64 * Q::SKP;
@@ -1029,6 +1084,330 @@ void bwd_rp_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, const
   for (int e = tid; e < QN; e += kThreads) out[D::R * (MN + PQ) + PQ + e] = ssum(D::R * (MN + PQ) + e);
 }
 
+// ---------------------------------------------------------------------------------
+// Whole-row backward ("solo") for the 32 x 32 factor blocks (p = q = m = n = 32, r <= 4).
+// One wavefront per SIMD: a workgroup of four wavefronts per compute unit, each
+// wavefront owning whole rows and every rank of them, so the row loop has no barrier and
+// no exchange between wavefronts.  Per row and rank i:
+//   Z^T = B_i^T X^T,  G^T = dY^T C_i^T,  dC_i += Z dY^T,  dX^T += B_i G^T,  dB_i += X^T G,
+// with dX accumulated over the ranks in registers and stored once.  The ranks' operand
+// tables (B_i in two lane orders, C_i) are in LDS, read one rank ahead and cyclically
+// into the next row.  Each wavefront's LDS tiles stage its next row: the row's global
+// loads are issued at the top of the row, written to the tiles once the current row's
+// operands have been read from them, and the next row's operands (row- and column-order
+// reads of X and dY) are read back after the last rank.  G takes one trip through a
+// per-wavefront tile to swap its indices for dB.  Under this kernel the matrix cores run
+// about 90% busy and the engine clock settles near 2.1 GHz (power-bound).
+// ---------------------------------------------------------------------------------
+template <class D>
+struct Solo {
+  static constexpr int R = D::R;
+  static constexpr bool OK = D::P == 32 && D::Q == 32 && D::M == 32 && D::N == 32 && R <= 4;
+  static constexpr int L = 36;               // pitch of a 32-float row in the tiles
+  static constexpr int TILE = 32 * L;
+  static constexpr int TAB = R * 1024;       // one table: [rank][tile 2][chunk 2][lane][4]
+  static constexpr int WSP = 3 * TILE;       // per wavefront: X tile, dY tile, G tile
+  static constexpr int MAIN = 3 * TAB + kWaves * WSP;
+  static constexpr int RW = 2 * R * 1024 + 1024;   // per wavefront at the end: dB | dC | dbias
+  static constexpr int COMBINE = kWaves * RW;
+  static constexpr size_t LDS = (size_t)(MAIN > COMBINE ? MAIN : COMBINE) * 4;
+  static_assert(!OK || 2 * R * 1024 <= kWaves * WSP, "raw factors are staged in the tile area");
+};
+
+__device__ __forceinline__ int kxs(int s, int g) { return 16 * (s >> 2) + 4 * g + (s & 3); }
+
+// DXM as for bwd_rp_kernel: 0 = no dX, 1 = dX, 2 = dX masked by [x > 0], 3 = dX added to
+// dx, 4 = dX added to dx and the sum masked.
+template <class D, int DXM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_solo_kernel(int64_t N, const float* __restrict__ x, const float* __restrict__ Sm,
+                     const float* __restrict__ A, const float* __restrict__ B, const float* __restrict__ dy,
+                     float* __restrict__ dx, float* __restrict__ part) {
+  using SL = Solo<D>;
+  constexpr int R = D::R, L = SL::L, TILE = SL::TILE;
+  extern __shared__ float lds[];
+  float* tabB = lds;                 // B_i[8g+s][16t+c]                 (A operand of Z^T)
+  float* tabC = lds + SL::TAB;       // C_i[16t+c][kxs(s,g)]             (B operand of G^T)
+  float* tabX = lds + 2 * SL::TAB;   // B_i[16t+c][16(s>>2)+4g+(s&3)]    (A operand of dX^T)
+  float* wsp = lds + 3 * SL::TAB;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15, w = tid >> 6;
+  float* xt = wsp + w * SL::WSP;
+  float* yt = xt + TILE;
+  float* gs = yt + TILE;
+  const int64_t stride = (int64_t)gridDim.x * kWaves;
+  int64_t row = (int64_t)blockIdx.x * kWaves + w;
+
+  // this lane's pieces of a row (float4 index 64t + lane), placed so that each 16-lane
+  // group writes rows j and j + 8 of a tile (no bank conflicts)
+  int soff[4], goff[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int f = 64 * t + lane, q = f & 15, g16 = f >> 4;
+    const int pj = (g16 & 7) + 16 * (g16 >> 3) + 8 * (q >> 3), pa = 4 * (q & 7);
+    soff[t] = pj * L + pa;
+    goff[t] = pj * 32 + pa;
+  }
+  f4 sx[4], sy[4];
+  auto fetch = [&](int64_t r) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      sx[t] = *reinterpret_cast<const f4*>(x + r * D::IN + goff[t]);
+      sy[t] = *reinterpret_cast<const f4*>(dy + r * D::OUT + goff[t]);
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      *reinterpret_cast<f4*>(xt + soff[t]) = sx[t];
+      *reinterpret_cast<f4*>(yt + soff[t]) = sy[t];
+    }
+  };
+  if (row < N) fetch(row);
+  {
+    // tables: B and C = S o A staged raw in the tile area, then laid out per lane
+    float* rB = wsp;
+    float* rC = wsp + R * 1024;
+    f4 b[R], a[R], m[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      b[k] = reinterpret_cast<const f4*>(B)[tid + kThreads * k];
+      a[k] = reinterpret_cast<const f4*>(A)[tid + kThreads * k];
+      m[k] = Sm ? reinterpret_cast<const f4*>(Sm)[tid] : f4{1.f, 1.f, 1.f, 1.f};
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      reinterpret_cast<f4*>(rB)[tid + kThreads * k] = b[k];
+      reinterpret_cast<f4*>(rC)[tid + kThreads * k] = a[k] * m[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 4 * R; ++it) {
+      const int e = tid + kThreads * it;
+      const int v = e & 3, l = (e >> 2) & 63, ch = (e >> 8) & 1, tl = (e >> 9) & 1, i = e >> 10;
+      const int gg = l >> 4, cc = l & 15, s = 4 * ch + v;
+      tabB[e] = rB[(i * 32 + 8 * gg + s) * 32 + 16 * tl + cc];
+      tabC[e] = rC[(i * 32 + 16 * tl + cc) * 32 + kxs(s, gg)];
+      tabX[e] = rB[(i * 32 + 16 * tl + cc) * 32 + 16 * (s >> 2) + 4 * gg + (s & 3)];
+    }
+    __syncthreads();
+  }
+  auto rd_tab = [&](float (&d)[2][8], const float* t, int i) {
+#pragma unroll
+    for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        const f4 v = reinterpret_cast<const f4*>(t)[((i * 2 + tl) * 2 + ch) * 64 + lane];
+        d[tl][4 * ch] = v[0]; d[tl][4 * ch + 1] = v[1]; d[tl][4 * ch + 2] = v[2]; d[tl][4 * ch + 3] = v[3];
+      }
+  };
+  float xa[2][8], xaj[2][8], dyb[2][8];   // X[16t+c][8g+s], X[kxs][16t+c], dY[kxs][16t+c]
+  f4 dyk[2][2];                           // dY[16tk+c][16tb+4g..]
+  auto rd_ops = [&]() {
+#pragma unroll
+    for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const f4 v = *reinterpret_cast<const f4*>(xt + (16 * tj + c) * L + 8 * g + 4 * t);
+        xa[tj][4 * t] = v[0]; xa[tj][4 * t + 1] = v[1]; xa[tj][4 * t + 2] = v[2]; xa[tj][4 * t + 3] = v[3];
+      }
+#pragma unroll
+    for (int tk = 0; tk < 2; ++tk)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) dyk[tk][tb] = *reinterpret_cast<const f4*>(yt + (16 * tk + c) * L + 16 * tb + 4 * g);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        xaj[t][s] = xt[kxs(s, g) * L + 16 * t + c];
+        dyb[t][s] = yt[kxs(s, g) * L + 16 * t + c];
+      }
+  };
+  f4 dC[R][2][2], dB[R][2][2], db[2][2];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int v = 0; v < 2; ++v) { dC[i][u][v] = f4{0.f, 0.f, 0.f, 0.f}; dB[i][u][v] = f4{0.f, 0.f, 0.f, 0.f}; }
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 2; ++v) db[u][v] = f4{0.f, 0.f, 0.f, 0.f};
+  float bo[2][8], co[2][8], bx[2][8];
+  if (row < N) {
+    stage();
+    rd_ops();
+  }
+  rd_tab(bo, tabB, 0);
+  rd_tab(co, tabC, 0);
+  if constexpr (DXM != 0) rd_tab(bx, tabX, 0);
+  for (; row < N; row += stride) {
+    fetch(row + stride < N ? row + stride : row);
+    f4 xm[2][2], dold[2][2];   // x under this lane's dX entries (mask), dx already there
+    if constexpr (DXM == 2 || DXM == 4) {
+#pragma unroll
+      for (int ta = 0; ta < 2; ++ta)
+#pragma unroll
+        for (int tj = 0; tj < 2; ++tj) xm[ta][tj] = *reinterpret_cast<const f4*>(xt + (16 * tj + c) * L + 16 * ta + 4 * g);
+    }
+    if constexpr (DXM >= 3) {
+#pragma unroll
+      for (int ta = 0; ta < 2; ++ta)
+#pragma unroll
+        for (int tj = 0; tj < 2; ++tj)
+          dold[ta][tj] = *reinterpret_cast<const f4*>(dx + row * D::IN + (16 * tj + c) * 32 + 16 * ta + 4 * g);
+    }
+#pragma unroll
+    for (int tk = 0; tk < 2; ++tk)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) db[tk][tb] += dyk[tk][tb];
+    f4 dxt[2][2];   // dX^T[16ta+4g+v][16tj+c]
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int v = 0; v < 2; ++v) dxt[u][v] = f4{0.f, 0.f, 0.f, 0.f};
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      f4 zt[2][2];   // Z^T[16tb+4g+v][16tj+c]
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int tj = 0; tj < 2; ++tj) {
+          f4 t = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 8; ++s) t = mfma(bo[tb][s], xa[tj][s], t);
+          zt[tb][tj] = t;
+        }
+      f4 gt[2][2];   // G^T[16tb+4g+v][16tj+c]
+#pragma unroll
+      for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          f4 t = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 8; ++s) t = mfma(dyb[tb][s], co[tj][s], t);
+          gt[tb][tj] = t;
+        }
+      // the next rank's tables (the last rank reads rank 0 for the next row)
+      float bo2[2][8], co2[2][8];
+      rd_tab(bo2, tabB, (i + 1) % R);
+      rd_tab(co2, tabC, (i + 1) % R);
+      __builtin_amdgcn_sched_barrier(0);
+      // dC_i[16tj+4g+v][16tk+c] += sum_b Z[j][b] dY[k][b]
+#pragma unroll
+      for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+        for (int tk = 0; tk < 2; ++tk)
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) dC[i][tj][tk] = mfma(zt[tb][tj][v], dyk[tk][tb][v], dC[i][tj][tk]);
+      // G as gs[j][b], read back in column order for dB
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int tj = 0; tj < 2; ++tj) *reinterpret_cast<f4*>(gs + (16 * tj + c) * L + 16 * tb + 4 * g) = gt[tb][tj];
+      float gcol[2][8];   // G[kxs][16tb+c]
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int s = 0; s < 8; ++s) gcol[tb][s] = gs[kxs(s, g) * L + 16 * tb + c];
+      __builtin_amdgcn_sched_barrier(0);
+      float bx2[2][8];
+      if constexpr (DXM != 0) {
+        // dX^T[a][j] += sum_b B_i[a][b] G^T[b][j]
+#pragma unroll
+        for (int ta = 0; ta < 2; ++ta)
+#pragma unroll
+          for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+              for (int v = 0; v < 4; ++v) dxt[ta][tj] = mfma(bx[ta][tb * 4 + v], gt[tb][tj][v], dxt[ta][tj]);
+        rd_tab(bx2, tabX, (i + 1) % R);
+      }
+      if (i == 0) stage();   // the next row into the tiles: this row's reads of them are done
+      __builtin_amdgcn_sched_barrier(0);
+      // dB_i[16ta+4g+v][16tb+c] += sum_j X[j][a] G[j][b]
+#pragma unroll
+      for (int ta = 0; ta < 2; ++ta)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int s = 0; s < 8; ++s) dB[i][ta][tb] = mfma(xaj[ta][s], gcol[tb][s], dB[i][ta][tb]);
+      if (i == R - 1) rd_ops();   // the next row's operands from the tiles
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          bo[u][v] = bo2[u][v];
+          co[u][v] = co2[u][v];
+          if constexpr (DXM != 0) bx[u][v] = bx2[u][v];
+        }
+    }
+    if constexpr (DXM != 0) {
+      float* dxr = dx + row * D::IN;
+#pragma unroll
+      for (int ta = 0; ta < 2; ++ta)
+#pragma unroll
+        for (int tj = 0; tj < 2; ++tj) {
+          f4 o = dxt[ta][tj];
+          if constexpr (DXM >= 3) o += dold[ta][tj];
+          if constexpr (DXM == 2 || DXM == 4) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) o[v] = xm[ta][tj][v] > 0.f ? o[v] : 0.f;
+          }
+          *reinterpret_cast<f4*>(dxr + (16 * tj + c) * 32 + 16 * ta + 4 * g) = o;
+        }
+    }
+  }
+  // Partial row of this workgroup: [dB (R*M*N) | dA (R*P*Q) | dS (P*Q) | dbias (Q*N)],
+  // the four wavefronts added in wavefront order.
+  __syncthreads();
+  float* red = lds + w * SL::RW;   // [dB | dC | dbias] of this wavefront
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          red[i * 1024 + (16 * u + 4 * g + v) * 32 + 16 * t + c] = dB[i][u][t][v];
+          red[R * 1024 + i * 1024 + (16 * u + 4 * g + v) * 32 + 16 * t + c] = dC[i][u][t][v];
+        }
+#pragma unroll
+  for (int tk = 0; tk < 2; ++tk)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) *reinterpret_cast<f4*>(red + 2 * R * 1024 + (16 * tk + c) * 32 + 16 * tb + 4 * g) = db[tk][tb];
+  __syncthreads();
+  auto wsum = [&](int e) {
+    f4 t = *reinterpret_cast<const f4*>(lds + e);
+#pragma unroll
+    for (int v = 1; v < kWaves; ++v) t += *reinterpret_cast<const f4*>(lds + v * SL::RW + e);
+    return t;
+  };
+  const int64_t G = gridDim.x, gb = blockIdx.x;
+  auto store = [&](int col, f4 v) { *reinterpret_cast<f4*>(part + part_index(G, gb, col)) = v; };
+#pragma unroll
+  for (int k = 0; k < R; ++k) store(4 * (tid + kThreads * k), wsum(4 * (tid + kThreads * k)));
+  {
+    const int e = 4 * tid;
+    const f4 sv = Sm ? *reinterpret_cast<const f4*>(Sm + e) : f4{1.f, 1.f, 1.f, 1.f};
+    f4 ds = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const f4 d = wsum(R * 1024 + i * 1024 + e);
+      store(R * 1024 + i * 1024 + e, sv * d);
+      ds += *reinterpret_cast<const f4*>(A + i * 1024 + e) * d;
+    }
+    store(2 * R * 1024 + e, Sm ? ds : f4{0.f, 0.f, 0.f, 0.f});
+    store(2 * R * 1024 + 1024 + e, wsum(2 * R * 1024 + e));
+  }
+}
+
 #endif  // backward kernels
 
 // ---------------------------------------------------------------------------------
@@ -1036,9 +1415,10 @@ void bwd_rp_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, const
 // ---------------------------------------------------------------------------------
 struct Entry {
   int p, q, m, n, r;
-  bool fwd_ok, bwd_ok, bwd_rp;
-  int rows_per_step;   // of the rank-parallel backward
-  int rp_per_cu;       // its workgroups per compute unit
+  bool fwd_ok, bwd_ok;
+  int bwd_kind;        // backward kernel that runs: 0 bwd_mfma, 1 rank-parallel, 2 whole-row
+  int rows_per_step;   // rows a workgroup takes per step of its row loop
+  int per_cu;          // backward workgroups per compute unit
   void (*fwd)(const LayerArgs&, int, hipStream_t);
   void (*bwd)(const LayerArgs&, int, hipStream_t);
 };
@@ -1081,11 +1461,45 @@ void run_fwd(const LayerArgs& a, int max_grid, hipStream_t s) {
 #endif
 
 #if KRON_MFMA_PASS != 1
-// RPF: prefer the rank-parallel kernel when both backward kernels fit (measured per shape).
-template <class D, bool RPF>
+// The backward kernel of a shape: the preferred one (BK, measured per shape) when it
+// supports the shape, else the rank-parallel one, else bwd_mfma_kernel.
+template <class D, int BK>
+constexpr int bwd_kind() {
+  return (BK == 2 && Solo<D>::OK) ? 2 : (RP<D>::OK && (BK >= 1 || !D::BWD_OK)) ? 1 : 0;
+}
+
+template <class D, int BK>
 void run_bwd(const LayerArgs& a, int grid, hipStream_t s) {
-  constexpr bool use_rp = RP<D>::OK && (RPF || !D::BWD_OK);
-  if constexpr (use_rp) {
+  constexpr int kind = bwd_kind<D, BK>();
+  if constexpr (kind == 2) {
+    static const bool attr = [] {
+      (void)hipFuncSetAttribute((const void*)bwd_solo_kernel<D, 0>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)Solo<D>::LDS);
+      (void)hipFuncSetAttribute((const void*)bwd_solo_kernel<D, 1>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)Solo<D>::LDS);
+      (void)hipFuncSetAttribute((const void*)bwd_solo_kernel<D, 2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)Solo<D>::LDS);
+      (void)hipFuncSetAttribute((const void*)bwd_solo_kernel<D, 3>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)Solo<D>::LDS);
+      (void)hipFuncSetAttribute((const void*)bwd_solo_kernel<D, 4>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)Solo<D>::LDS);
+      return true;
+    }();
+    (void)attr;
+    const bool mask = a.flags & KRON_DX_RELU_MASK;
+    const int dxm = a.dx == nullptr ? 0 : (a.dx_accumulate ? (mask ? 4 : 3) : (mask ? 2 : 1));
+#define KRON_SOLO_LAUNCH(M)                                                                                 \
+  hipLaunchKernelGGL((bwd_solo_kernel<D, M>), dim3(grid), dim3(kThreads), Solo<D>::LDS, s, a.N, a.x, a.S, a.A, \
+                     a.B, a.dy, a.dx, a.part)
+    switch (dxm) {
+      case 0: KRON_SOLO_LAUNCH(0); break;
+      case 1: KRON_SOLO_LAUNCH(1); break;
+      case 2: KRON_SOLO_LAUNCH(2); break;
+      case 3: KRON_SOLO_LAUNCH(3); break;
+      default: KRON_SOLO_LAUNCH(4); break;
+    }
+#undef KRON_SOLO_LAUNCH
+  } else if constexpr (kind == 1) {
     static const bool attr = [] {
       (void)hipFuncSetAttribute((const void*)bwd_rp_kernel<D, 0>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)RP<D>::LDS);
@@ -1125,12 +1539,13 @@ void run_bwd(const LayerArgs& a, int grid, hipStream_t s) {
   }
 }
 
-#define KRON_ENTRY(P, Q, M, N, R, RPF)                                                                 \
+#define KRON_ENTRY(P, Q, M, N, R, BK)                                                                  \
   Entry{P, Q, M, N, R, Dims<P, Q, M, N, R>::FWD_OK,                                                    \
-        Dims<P, Q, M, N, R>::BWD_OK || RP<Dims<P, Q, M, N, R>>::OK,                                     \
-        RP<Dims<P, Q, M, N, R>>::OK && (RPF || !Dims<P, Q, M, N, R>::BWD_OK),                           \
-        RP<Dims<P, Q, M, N, R>>::RPI, RP<Dims<P, Q, M, N, R>>::WPC, &run_fwd_shape<P, Q, M, N, R>,       \
-        &run_bwd<Dims<P, Q, M, N, R>, RPF>},
+        Dims<P, Q, M, N, R>::BWD_OK || RP<Dims<P, Q, M, N, R>>::OK || Solo<Dims<P, Q, M, N, R>>::OK,    \
+        bwd_kind<Dims<P, Q, M, N, R>, BK>(),                                                           \
+        bwd_kind<Dims<P, Q, M, N, R>, BK>() == 1 ? RP<Dims<P, Q, M, N, R>>::RPI : kWaves,              \
+        bwd_kind<Dims<P, Q, M, N, R>, BK>() == 1 ? RP<Dims<P, Q, M, N, R>>::WPC : 1,                   \
+        &run_fwd_shape<P, Q, M, N, R>, &run_bwd<Dims<P, Q, M, N, R>, BK>},
 
 const Entry kTable[] = {KRON_MFMA_SHAPES(KRON_ENTRY)};
 
@@ -1148,7 +1563,7 @@ template <int P, int Q, int M, int N, int R>
 void run_fwd_shape(const LayerArgs& a, int max_grid, hipStream_t s) {
   run_fwd<Dims<P, Q, M, N, R>>(a, max_grid, s);
 }
-#define KRON_FWD_INST(P, Q, M, N, R, RPF) template void run_fwd_shape<P, Q, M, N, R>(const LayerArgs&, int, hipStream_t);
+#define KRON_FWD_INST(P, Q, M, N, R, BK) template void run_fwd_shape<P, Q, M, N, R>(const LayerArgs&, int, hipStream_t);
 KRON_MFMA_SHAPES(KRON_FWD_INST)
 #undef KRON_FWD_INST
 #endif
@@ -1168,15 +1583,15 @@ bool mfma_bwd_supported(int p, int q, int m, int n, int r) {
 int mfma_bwd_chunk(int p, int q, int m, int n, int r) {
   if (r <= 4 || r % 4 != 0 || mfma_bwd_supported(p, q, m, n, r)) return 0;
   const Entry* e = find(p, q, m, n, 4);
-  return (e && e->bwd_rp) ? 4 : 0;
+  return (e && e->bwd_kind >= 1) ? 4 : 0;
 }
 
 int mfma_bwd_groups(int64_t N, int p, int q, int m, int n, int r) {
   const Entry* e = find(p, q, m, n, r);
-  if (e && e->bwd_rp) {
-    // rp_per_cu workgroups per compute unit, each stepping over rows_per_step rows at a time
+  if (e && e->bwd_kind >= 1) {
+    // per_cu workgroups per compute unit, each stepping over rows_per_step rows at a time
     const int64_t g = (N + e->rows_per_step - 1) / e->rows_per_step;
-    const int64_t gmax = (int64_t)e->rp_per_cu * kBwdGroups;
+    const int64_t gmax = (int64_t)e->per_cu * kBwdGroups;
     return (int)(g < gmax ? g : gmax);
   }
   const int64_t g = (N + kWaves - 1) / kWaves;
