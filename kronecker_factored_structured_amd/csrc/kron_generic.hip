@@ -197,15 +197,15 @@ __global__ __launch_bounds__(kThreads) void bwd_generic_kernel(
 }
 
 // A workgroup of CX * RY threads reduces one block of CX * VEC = kRedCols columns: thread
-// (tx, ty) reads VEC columns as one vector from partial rows g = ty (mod RY), eight
-// loads in flight, and sums them in fp64 in row order; the RY per-thread sums are then
-// combined in a fixed tree, so the result does not depend on timing.
-template <int VEC, int CX, int RY>
+// (tx, ty) reads VEC columns as one vector from partial rows g = ty (mod RY), U loads in
+// flight at a time (all of them at once for G <= U * RY), and sums them in fp64 in row
+// order; the RY per-thread sums are then combined in a fixed tree, so the result does not
+// depend on timing.
+template <int VEC, int CX, int RY, int U>
 __global__ __launch_bounds__(CX * RY) void column_reduce_kernel(const float* __restrict__ part, int G, int PW,
                                                                 RedPlan plan) {
   static_assert(CX * VEC == kRedCols, "one workgroup per column block");
   typedef float fv __attribute__((ext_vector_type(VEC)));
-  constexpr int U = 8;
   __shared__ double red[RY][CX * VEC];
   const int tx = threadIdx.x % CX, ty = threadIdx.x / CX;
   const int col0 = blockIdx.x * kRedCols + tx * VEC;
@@ -214,21 +214,22 @@ __global__ __launch_bounds__(CX * RY) void column_reduce_kernel(const float* __r
   for (int v = 0; v < VEC; ++v) s[v] = 0.0;
   {
     const float* p = part + (int64_t)blockIdx.x * G * kRedCols + tx * VEC;
-    auto ld = [&](int g) { return *reinterpret_cast<const fv*>(p + (int64_t)g * kRedCols); };
-    int g = ty;
-    for (; g + (U - 1) * RY < G; g += U * RY) {
+    for (int g0 = ty; g0 < G; g0 += U * RY) {
       fv a[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) a[u] = ld(g + u * RY);
+      for (int u = 0; u < U; ++u) {
+        const int g = g0 + u * RY;
+        if (g < G) {
+          a[u] = *reinterpret_cast<const fv*>(p + (int64_t)g * kRedCols);
+        } else {
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) a[u][v] = 0.f;
+        }
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int v = 0; v < VEC; ++v) s[v] += (double)a[u][v];
-    }
-    for (; g < G; g += RY) {
-      const fv a = ld(g);
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) s[v] += (double)a[v];
     }
   }
 #pragma unroll
@@ -325,9 +326,9 @@ hipError_t launch_column_reduce(const float* part, int32_t G, int32_t PW, const 
   // 16-byte vector loads need the partial sums 16-byte aligned (workspaces are 256-byte aligned)
   const unsigned blocks = (unsigned)((PW + kRedCols - 1) / kRedCols);
   if (((uintptr_t)part & 15) == 0)
-    hipLaunchKernelGGL((column_reduce_kernel<4, 8, 64>), dim3(blocks), dim3(512), 0, stream, part, G, PW, plan);
+    hipLaunchKernelGGL((column_reduce_kernel<4, 8, 32, 8>), dim3(blocks), dim3(256), 0, stream, part, G, PW, plan);
   else
-    hipLaunchKernelGGL((column_reduce_kernel<1, 32, 16>), dim3(blocks), dim3(512), 0, stream, part, G, PW, plan);
+    hipLaunchKernelGGL((column_reduce_kernel<1, 32, 8, 16>), dim3(blocks), dim3(256), 0, stream, part, G, PW, plan);
   return hipGetLastError();
 }
 

@@ -61,7 +61,10 @@ def test_headline_layer_full_size():
     compare_layer(headline_layer())
 
 
-@pytest.mark.parametrize("N", [0, 1, 3, 257, 1031])
+# With one workgroup of four row-owning wavefronts per compute unit, 1 and 257 rows are
+# split by rank only, 1031 and 3500 leave a split tail after whole rounds, 2000 leaves a
+# tail too long to split and 2048 none.
+@pytest.mark.parametrize("N", [0, 1, 3, 257, 1031, 2000, 2048, 3500])
 def test_headline_shape_ragged_rows(N):
     inp = headline_layer(N=N)
     if N == 0:
@@ -117,6 +120,21 @@ def test_relu_flags():
     go = OK.backward(xr, inp.S, inp.A, inp.B, inp.dy, W=W)
     assert rel_err(g["dx"], go["dx"] * (xr > 0)) <= TOL_F32
     assert np.all(g["dx"][xr <= 0] == 0)
+
+
+@pytest.mark.parametrize("N", [1031, 1900])
+def test_relu_mask_headline_shape(N):
+    """dx o [x > 0] on the 32 x 32-block layer with r = 4, with and without rank-split rows."""
+    inp = kron_inputs(39, N, 32, 32, 32, 32, 4, s_mode="uniform_zeroed", bias_mode="normal")
+    xr = np.maximum(inp.x, 0).astype(np.float32)
+    inp.x = xr
+    y, g = run_layer(inp, relu_mask=True)
+    W = OK.weight(inp.S, inp.A, inp.B)
+    go = OK.backward(xr, inp.S, inp.A, inp.B, inp.dy, W=W)
+    assert rel_err(g["dx"], go["dx"] * (xr > 0)) <= TOL_F32
+    assert np.all(g["dx"][xr <= 0] == 0)
+    for k in ("dS", "dA", "dB", "dbias"):
+        assert rel_err(g[k], go[k]) <= TOL_F32, k
 
 
 @pytest.mark.parametrize("shape", [(32, 64, 24, 48), (64, 32, 48, 24)])

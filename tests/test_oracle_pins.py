@@ -300,6 +300,29 @@ def test_ks_d_interleave_matches_permutation_form():
     assert np.array_equal(OKS.dense(v, 1, b, c, d), np.kron(M, np.eye(d)))
 
 
+@pytest.mark.parametrize("abcd", [(2, 3, 4, 3), (2, 1, 2, 3), (3, 2, 1, 2)])
+def test_ks_value_layout_against_kron_sum(abcd):
+    """The value layout vals[alpha][delta][beta][gamma]: with E_kk the one-hot k-th
+    diagonal unit matrix, K = sum over (alpha, delta) of E_alpha,alpha (x) V[alpha][delta]
+    (x) E_delta,delta, built with numpy.kron.  Every (alpha, delta) block holds distinct
+    integers, so a swapped alpha/delta order or a transposed block changes K exactly."""
+    a, b, c, d = abcd
+    V = np.arange(1, a * d * b * c + 1, dtype=float).reshape(a, d, b, c)
+    V = V * np.where(np.arange(V.size).reshape(V.shape) % 2, 1.0, -1.0)
+    K = np.zeros((a * b * d, a * c * d))
+    for al in range(a):
+        Ea = np.zeros((a, a))
+        Ea[al, al] = 1.0
+        for de in range(d):
+            Ed = np.zeros((d, d))
+            Ed[de, de] = 1.0
+            K += np.kron(np.kron(Ea, V[al, de]), Ed)
+    assert np.array_equal(OKS.dense(V.reshape(-1), a, b, c, d), K)
+    # the same, as the product X K on an integer X (exact in fp64)
+    x = np.random.default_rng(7).integers(-3, 4, (5, a * b * d)).astype(float)
+    assert np.array_equal(OKS.matmul(x, V, a, b, c, d), x @ K)
+
+
 @pytest.mark.parametrize("abcd", [(2, 3, 4, 2), (1, 5, 2, 1), (3, 1, 2, 3)])
 def test_ks_backward_exact_finite_differences(abcd):
     """L(x, vals) = <dY, X K> is linear in x and in vals, so the central difference with
