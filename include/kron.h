@@ -71,13 +71,13 @@ typedef struct {
  * does not fit in one workgroup's LDS return KRON_E_UNSUPPORTED. */
 
 int32_t kron_abi_version(void);
-const char* kron_status_str(int32_t status);
+const char* kron_status_str(kron_status_t status);
 /* Detail string of the last failed call on this thread ("" if none).  Valid until the
  * next call on the same thread. */
 const char* kron_last_error(void);
 
 /* Host-only shape validation (no HIP call); returns KRON_OK or the error. */
-int32_t kron_linear_check(const kron_shape_t* shape);
+kron_status_t kron_linear_check(const kron_shape_t* shape);
 
 /* Bytes of workspace kron_linear_bwd needs for this shape (0 on an invalid shape).
  * Depends only on the shape. */
@@ -90,9 +90,9 @@ size_t kron_linear_bwd_workspace_bytes(const kron_shape_t* shape);
  *   x    [N, p*m]   S [p, q] or NULL   A [r, p, q]   B [r, m, n]
  *   bias [q*n] or NULL                  y [N, q*n]  (must not overlap any input)
  */
-int32_t kron_linear_fwd(const kron_shape_t* shape, const float* x, const float* S,
-                        const float* A, const float* B, const float* bias, float* y,
-                        hipStream_t stream);
+kron_status_t kron_linear_fwd(const kron_shape_t* shape, const float* x, const float* S,
+                              const float* A, const float* B, const float* bias, float* y,
+                              hipStream_t stream);
 
 /*
  * Backward of y = x W + bias for the upstream gradient dy [N, q*n]:
@@ -108,10 +108,10 @@ int32_t kron_linear_fwd(const kron_shape_t* shape, const float* x, const float* 
  * 256-byte aligned; its contents on entry are ignored.  Outputs must not overlap each
  * other, the inputs or the workspace.
  */
-int32_t kron_linear_bwd(const kron_shape_t* shape, const float* x, const float* S,
-                        const float* A, const float* B, const float* dy,
-                        float* dx, float* dS, float* dA, float* dB, float* dbias,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+kron_status_t kron_linear_bwd(const kron_shape_t* shape, const float* x, const float* S,
+                              const float* A, const float* B, const float* dy,
+                              float* dx, float* dS, float* dA, float* dB, float* dbias,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * bf16 layer (mixed precision; the tutorial's "Takeaways" name a mixed-precision rerun as
@@ -126,13 +126,13 @@ int32_t kron_linear_bwd(const kron_shape_t* shape, const float* x, const float* 
  * calls (16-byte aligned); workspace from kron_linear_bwd_bf16_workspace_bytes.
  */
 size_t kron_linear_bwd_bf16_workspace_bytes(const kron_shape_t* shape);
-int32_t kron_linear_fwd_bf16(const kron_shape_t* shape, const void* x, const void* S,
-                             const void* A, const void* B, const void* bias, void* y,
-                             hipStream_t stream);
-int32_t kron_linear_bwd_bf16(const kron_shape_t* shape, const void* x, const void* S,
-                             const void* A, const void* B, const void* dy, void* dx,
-                             float* dS, float* dA, float* dB, float* dbias,
-                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+kron_status_t kron_linear_fwd_bf16(const kron_shape_t* shape, const void* x, const void* S,
+                                   const void* A, const void* B, const void* bias, void* y,
+                                   hipStream_t stream);
+kron_status_t kron_linear_bwd_bf16(const kron_shape_t* shape, const void* x, const void* S,
+                                   const void* A, const void* B, const void* dy, void* dx,
+                                   float* dS, float* dA, float* dB, float* dbias,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Kronecker-sparse matmul ("Fast Inference with Kronecker-Sparse Matrices", abstract):
@@ -143,8 +143,8 @@ int32_t kron_linear_bwd_bf16(const kron_shape_t* shape, const void* x, const voi
  *   y    [N, a*c*d]  fp32, accumulated in fp32
  * Limits: a*b*d and a*c*d <= 65536.
  */
-int32_t ks_matmul(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype,
-                  const void* x, const void* vals, float* y, hipStream_t stream);
+kron_status_t ks_matmul(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype,
+                        const void* x, const void* vals, float* y, hipStream_t stream);
 
 /*
  * ks_matmul with the output dtype chosen (the same product; "Fast Inference with
@@ -153,9 +153,9 @@ int32_t ks_matmul(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t
  * y being [N, a*c*d] bf16 (2-byte elements).  Same limits, alignment and errors as
  * ks_matmul, plus KRON_E_DTYPE for an out_dtype other than KRON_F32 / KRON_BF16.
  */
-int32_t ks_matmul_out(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype,
-                      int32_t out_dtype, const void* x, const void* vals, void* y,
-                      hipStream_t stream);
+kron_status_t ks_matmul_out(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype,
+                            int32_t out_dtype, const void* x, const void* vals, void* y,
+                            hipStream_t stream);
 
 /*
  * Backward of ks_matmul (by calculus from Y = X K with the KS matrix K of "Fast Inference
@@ -192,9 +192,9 @@ int32_t ks_matmul_out(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int
  * KRON_E_WORKSPACE, KRON_E_HIP.  The workspace query returns 0 for rejected shapes.
  */
 size_t kron_van_loan_workspace_bytes(int32_t p, int32_t q, int32_t m, int32_t n, int32_t s);
-int32_t kron_van_loan(int32_t p, int32_t q, int32_t m, int32_t n, int32_t r, int32_t s,
-                      int32_t iters, const float* W, const float* omega, float* C, float* B,
-                      float* sigma, void* workspace, size_t workspace_bytes, hipStream_t stream);
+kron_status_t kron_van_loan(int32_t p, int32_t q, int32_t m, int32_t n, int32_t r, int32_t s,
+                            int32_t iters, const float* W, const float* omega, float* C, float* B,
+                            float* sigma, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * One Kronecker-sparse factor of a chain: support I_a (x) 1_{b x c} (x) I_d, values
@@ -219,14 +219,14 @@ typedef struct {
  * KRON_E_ARG (nfactors), KRON_E_NULL, KRON_E_DTYPE, KRON_E_UNSUPPORTED, KRON_E_ALIGN,
  * KRON_E_ALIAS (y over x or any vals), KRON_E_HIP.
  */
-int32_t ks_chain(int64_t N, int32_t nfactors, const ks_factor_t* factors, int32_t in_dtype,
-                 const void* x, float* y, hipStream_t stream);
+kron_status_t ks_chain(int64_t N, int32_t nfactors, const ks_factor_t* factors, int32_t in_dtype,
+                       const void* x, float* y, hipStream_t stream);
 
 size_t ks_matmul_bwd_workspace_bytes(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d,
                                      int32_t in_dtype);
-int32_t ks_matmul_bwd(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype,
-                      const void* x, const void* vals, const void* dy, float* dx, float* dvals,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+kron_status_t ks_matmul_bwd(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype,
+                            const void* x, const void* vals, const void* dy, float* dx, float* dvals,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Fused multi-tensor Adam with an l1 penalty (tutorial, "Setup": Adam update of the
@@ -240,10 +240,10 @@ int32_t ks_matmul_bwd(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int
  * double: 1 - beta and the bias corrections are formed on the host in double and
  * rounded once to fp32 (1 - 0.999f in fp32 would be off by 1.3e-5 relative).
  */
-int32_t kron_adam_l1_step(int32_t ntensors, float* const* params, const float* const* grads,
-                          float* const* m, float* const* v, const int64_t* numel,
-                          const float* l1, int64_t step, double lr, double beta1, double beta2,
-                          double eps, hipStream_t stream);
+kron_status_t kron_adam_l1_step(int32_t ntensors, float* const* params, const float* const* grads,
+                                float* const* m, float* const* v, const int64_t* numel,
+                                const float* l1, int64_t step, double lr, double beta1, double beta2,
+                                double eps, hipStream_t stream);
 
 /*
  * Dense classification head with mean softmax cross-entropy, forward and backward in
@@ -259,10 +259,42 @@ int32_t kron_adam_l1_step(int32_t ntensors, float* const* params, const float* c
  * Limits: 1 <= C <= 64, 1 <= K <= 8192.  workspace as for kron_linear_bwd.
  */
 size_t kron_head_ce_workspace_bytes(int64_t N, int32_t K, int32_t C);
-int32_t kron_head_ce(int64_t N, int32_t K, int32_t C, const float* h, const float* Wh,
-                     const float* bh, const int64_t* labels, float* loss, float* dh,
-                     float* dWh, float* dbh, uint32_t flags, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream);
+kron_status_t kron_head_ce(int64_t N, int32_t K, int32_t C, const float* h, const float* Wh,
+                           const float* bh, const int64_t* labels, float* loss, float* dh,
+                           float* dWh, float* dbh, uint32_t flags, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The gradient through a ReLU output (tutorial, "Setup": the hidden layers end in a
+ * ReLU): out = dy o [y > 0] for y = max(z, 0), n elements.  out may be dy itself (in
+ * place); otherwise out must not overlap y or dy.  Used for a layer whose forward ran
+ * with KRON_RELU_OUT, before its kron_linear_bwd.
+ */
+kron_status_t kron_relu_bwd(int64_t n, const float* y, const float* dy, float* out, hipStream_t stream);
+
+/* kron_l1_penalty flags */
+#define KRON_ACCUMULATE 1u    /* add to *loss instead of overwriting it */
+
+/*
+ * The l1 penalty on S (tutorial, intro: S is l1-penalised; "Setup": the loss is the
+ * cross-entropy plus the model's penalty):
+ *   loss[0] = (flags & KRON_ACCUMULATE ? loss[0] : 0) + lam * sum_t sum_e |tensors[t][e]|
+ * tensors and numel are HOST arrays of length ntensors (<= 64); tensors holds device
+ * pointers.  loss is one device float and must not overlap a tensor.  The sum is taken in
+ * fp64 in a fixed order by a single workgroup (meant for S-sized tensors), then rounded
+ * once to fp32: bitwise reproducible.  ntensors = 0 sets (or keeps) loss[0].
+ */
+kron_status_t kron_l1_penalty(int32_t ntensors, const float* const* tensors, const int64_t* numel,
+                              float lam, float* loss, uint32_t flags, hipStream_t stream);
+
+/*
+ * Subgradient of lam * sum|S| scaled by an upstream scalar gradient g (one device float):
+ *   dS = lam * g[0] * sign(S),  sign(0) = 0,  n elements.
+ * dS must not overlap S or g.  (kron_adam_l1_step applies the same subgradient inside the
+ * update; this call serves autograd-style callers.)
+ */
+kron_status_t kron_l1_penalty_grad(int64_t n, const float* S, float lam, const float* g, float* dS,
+                                   hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -27,6 +27,8 @@ KRON_BF16 = 1
 KRON_RELU_OUT = 1
 KRON_DX_RELU_MASK = 2
 
+KRON_ACCUMULATE = 1
+
 # Every symbol include/kron.h declares.
 EXPORTS = (
     "kron_abi_version", "kron_status_str", "kron_last_error", "kron_linear_check",
@@ -34,7 +36,8 @@ EXPORTS = (
     "kron_adam_l1_step", "kron_head_ce_workspace_bytes", "kron_head_ce",
     "kron_linear_bwd_bf16_workspace_bytes", "kron_linear_fwd_bf16", "kron_linear_bwd_bf16",
     "ks_matmul_out", "ks_matmul_bwd_workspace_bytes", "ks_matmul_bwd", "ks_chain",
-    "kron_van_loan_workspace_bytes", "kron_van_loan",
+    "kron_van_loan_workspace_bytes", "kron_van_loan", "kron_relu_bwd", "kron_l1_penalty",
+    "kron_l1_penalty_grad",
 )
 
 
@@ -93,6 +96,9 @@ def lib() -> ctypes.CDLL:
             "kron_linear_bwd_bf16_workspace_bytes": (sz, [shp]),
             "kron_linear_fwd_bf16": (i32, [shp, vp, vp, vp, vp, vp, vp, vp]),
             "kron_linear_bwd_bf16": (i32, [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "kron_relu_bwd": (i32, [i64, vp, vp, vp, vp]),
+            "kron_l1_penalty": (i32, [i32, pp, ctypes.POINTER(ctypes.c_int64), ctypes.c_float, vp, u32, vp]),
+            "kron_l1_penalty_grad": (i32, [i64, vp, ctypes.c_float, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)

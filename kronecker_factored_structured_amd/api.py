@@ -12,7 +12,7 @@ from typing import Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import KRON_BF16, KRON_DX_RELU_MASK, KRON_F32, KRON_RELU_OUT, KronShape, check
+from ._lib import KRON_ACCUMULATE, KRON_BF16, KRON_DX_RELU_MASK, KRON_F32, KRON_RELU_OUT, KronShape, check
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -30,11 +30,27 @@ def _dev(t: Optional[torch.Tensor], name: str, dtype=torch.float32) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _need(t: Optional[torch.Tensor], name: str, shape: tuple, dtype=torch.float32,
+          device: Optional[torch.device] = None) -> None:
+    """t (if given) must be a contiguous GPU tensor of exactly this shape and dtype (on
+    `device` when one is given): libkron derives every extent from the sizes it is passed,
+    so a tensor of another shape would be read or written past its end."""
+    if t is None:
+        return
+    _dev(t, name, dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
 def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
 def layer_shape(x_rows: int, S, A: torch.Tensor, B: torch.Tensor, flags: int = 0) -> KronShape:
+    if A.dim() != 3 or B.dim() != 3:
+        raise ValueError("A must be r x p x q and B r x m x n")
     r, p, q = A.shape
     rb, m, n = B.shape
     if rb != r:
@@ -42,6 +58,38 @@ def layer_shape(x_rows: int, S, A: torch.Tensor, B: torch.Tensor, flags: int = 0
     if S is not None and tuple(S.shape) != (p, q):
         raise ValueError(f"S must be {p}x{q}, got {tuple(S.shape)}")
     return KronShape(int(x_rows), p, q, m, n, r, flags)
+
+
+def _layer_io_checks(x: torch.Tensor, shape: KronShape, S, A: torch.Tensor, B: torch.Tensor,
+                     dy: Optional[torch.Tensor] = None) -> None:
+    """x is N x p*m (and dy N x q*n), every tensor on x's device."""
+    if x.dim() != 2 or x.shape[1] != shape.p * shape.m:
+        raise ValueError(f"x must be N x {shape.p * shape.m}, got {tuple(x.shape)}")
+    for t, nm in ((S, "S"), (A, "A"), (B, "B"), (dy, "dy")):
+        if t is not None and t.device != x.device:
+            raise ValueError(f"{nm} is on {t.device}, expected {x.device}")
+    if dy is not None and tuple(dy.shape) != (x.shape[0], shape.q * shape.n):
+        raise ValueError(f"dy must have shape {(x.shape[0], shape.q * shape.n)}, got {tuple(dy.shape)}")
+
+
+def _grad_out_checks(o: dict, x: torch.Tensor, shape: KronShape, dx_dtype=torch.float32) -> None:
+    """Caller-supplied gradient buffers: exact shapes, dx in dx_dtype, the rest fp32."""
+    N, p, q, m, n, r = x.shape[0], shape.p, shape.q, shape.m, shape.n, shape.r
+    _need(o.get("dx"), "dx", (N, p * m), dx_dtype, x.device)
+    _need(o.get("dS"), "dS", (p, q), device=x.device)
+    _need(o.get("dA"), "dA", (r, p, q), device=x.device)
+    _need(o.get("dB"), "dB", (r, m, n), device=x.device)
+    _need(o.get("dbias"), "dbias", (q * n,), device=x.device)
+
+
+def _workspace(workspace: Optional[torch.Tensor], need: int, dev: torch.device) -> torch.Tensor:
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
+        if workspace.device != dev:
+            raise ValueError(f"workspace is on {workspace.device}, expected {dev}")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    return workspace
 
 
 def kron_linear_bwd_workspace_bytes(shape: KronShape) -> int:
@@ -52,11 +100,12 @@ def kron_linear_fwd(x: torch.Tensor, S: Optional[torch.Tensor], A: torch.Tensor,
                     bias: Optional[torch.Tensor] = None, relu: bool = False,
                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y = x W + bias with W = sum_i kron(S o A_i, B_i) (optionally ReLU-ed)."""
-    for t, nm in ((x, "x"), (S, "S"), (A, "A"), (B, "B"), (bias, "bias"), (out, "out")):
+    for t, nm in ((x, "x"), (S, "S"), (A, "A"), (B, "B")):
         _dev(t, nm)
     shape = layer_shape(x.shape[0], S, A, B, KRON_RELU_OUT if relu else 0)
-    if x.dim() != 2 or x.shape[1] != shape.p * shape.m:
-        raise ValueError(f"x must be N x {shape.p * shape.m}")
+    _layer_io_checks(x, shape, S, A, B)
+    _need(bias, "bias", (shape.q * shape.n,), device=x.device)
+    _need(out, "out", (x.shape[0], shape.q * shape.n), device=x.device)
     y = out if out is not None else torch.empty(x.shape[0], shape.q * shape.n, device=x.device)
     check("kron_linear_fwd", _lib.lib().kron_linear_fwd(
         ctypes.byref(shape), _ptr(x), _ptr(S), _ptr(A), _ptr(B), _ptr(bias), _ptr(y), _stream(x.device)))
@@ -71,17 +120,17 @@ def kron_linear_bwd(x: torch.Tensor, S: Optional[torch.Tensor], A: torch.Tensor,
     for t, nm in ((x, "x"), (S, "S"), (A, "A"), (B, "B"), (dy, "dy")):
         _dev(t, nm)
     shape = layer_shape(x.shape[0], S, A, B, KRON_DX_RELU_MASK if relu_mask else 0)
+    _layer_io_checks(x, shape, S, A, B, dy)
     dev = x.device
     o = dict(outs or {})
+    _grad_out_checks(o, x, shape)
     dx = o.get("dx") if "dx" in o else (torch.empty_like(x) if want_dx else None)
     dS = o.get("dS") if "dS" in o else (torch.empty_like(S) if S is not None else None)
     dA = o.get("dA") if "dA" in o else torch.empty_like(A)
     dB = o.get("dB") if "dB" in o else torch.empty_like(B)
     dbias = o.get("dbias") if "dbias" in o else (
         torch.empty(shape.q * shape.n, device=dev) if want_dbias else None)
-    need = kron_linear_bwd_workspace_bytes(shape)
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, kron_linear_bwd_workspace_bytes(shape), dev)
     check("kron_linear_bwd", _lib.lib().kron_linear_bwd(
         ctypes.byref(shape), _ptr(x), _ptr(S), _ptr(A), _ptr(B), _ptr(dy), _ptr(dx), _ptr(dS), _ptr(dA),
         _ptr(dB), _ptr(dbias), _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(dev)))
@@ -97,11 +146,12 @@ def kron_linear_fwd_bf16(x: torch.Tensor, S: Optional[torch.Tensor], A: torch.Te
                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """bf16 layer: y = x W + bias (bf16 tensors, fp32 accumulation, bf16 y)."""
     bf = torch.bfloat16
-    for t, nm in ((x, "x"), (S, "S"), (A, "A"), (B, "B"), (bias, "bias"), (out, "out")):
+    for t, nm in ((x, "x"), (S, "S"), (A, "A"), (B, "B")):
         _dev(t, nm, bf)
     shape = layer_shape(x.shape[0], S, A, B, KRON_RELU_OUT if relu else 0)
-    if x.dim() != 2 or x.shape[1] != shape.p * shape.m:
-        raise ValueError(f"x must be N x {shape.p * shape.m}")
+    _layer_io_checks(x, shape, S, A, B)
+    _need(bias, "bias", (shape.q * shape.n,), bf, x.device)
+    _need(out, "out", (x.shape[0], shape.q * shape.n), bf, x.device)
     y = out if out is not None else torch.empty(x.shape[0], shape.q * shape.n, device=x.device, dtype=bf)
     check("kron_linear_fwd_bf16", _lib.lib().kron_linear_fwd_bf16(
         ctypes.byref(shape), _ptr(x), _ptr(S), _ptr(A), _ptr(B), _ptr(bias), _ptr(y), _stream(x.device)))
@@ -117,21 +167,18 @@ def kron_linear_bwd_bf16(x: torch.Tensor, S: Optional[torch.Tensor], A: torch.Te
     for t, nm in ((x, "x"), (S, "S"), (A, "A"), (B, "B"), (dy, "dy")):
         _dev(t, nm, bf)
     shape = layer_shape(x.shape[0], S, A, B, KRON_DX_RELU_MASK if relu_mask else 0)
+    _layer_io_checks(x, shape, S, A, B, dy)
     dev = x.device
     f32 = torch.float32
     o = dict(outs or {})
+    _grad_out_checks(o, x, shape, bf)
     dx = o.get("dx") if "dx" in o else (torch.empty_like(x) if want_dx else None)
     dS = o.get("dS") if "dS" in o else (torch.empty(S.shape, device=dev, dtype=f32) if S is not None else None)
     dA = o.get("dA") if "dA" in o else torch.empty(A.shape, device=dev, dtype=f32)
     dB = o.get("dB") if "dB" in o else torch.empty(B.shape, device=dev, dtype=f32)
     dbias = o.get("dbias") if "dbias" in o else (
         torch.empty(shape.q * shape.n, device=dev, dtype=f32) if want_dbias else None)
-    _dev(dx, "dx", bf)
-    for t, nm in ((dS, "dS"), (dA, "dA"), (dB, "dB"), (dbias, "dbias")):
-        _dev(t, nm)
-    need = kron_linear_bwd_bf16_workspace_bytes(shape)
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, kron_linear_bwd_bf16_workspace_bytes(shape), dev)
     check("kron_linear_bwd_bf16", _lib.lib().kron_linear_bwd_bf16(
         ctypes.byref(shape), _ptr(x), _ptr(S), _ptr(A), _ptr(B), _ptr(dy), _ptr(dx), _ptr(dS), _ptr(dA),
         _ptr(dB), _ptr(dbias), _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(dev)))
@@ -151,6 +198,8 @@ def _ks_checks(x, vals, a, b, c, d):
         raise ValueError(f"x must be N x {a * b * d}")
     if vals.numel() != a * b * c * d:
         raise ValueError(f"vals must hold a*b*c*d = {a * b * c * d} values")
+    if vals.device != x.device:
+        raise ValueError(f"vals is on {vals.device}, expected {x.device}")
     return dt
 
 
@@ -159,7 +208,7 @@ def ks_matmul(x: torch.Tensor, vals: torch.Tensor, a: int, b: int, c: int, d: in
     """Y = X K for the Kronecker-sparse K with support I_a (x) 1_{b x c} (x) I_d; vals is
     a x d x b x c.  x and vals are float32 or bfloat16 (same dtype); y is float32."""
     dt = _ks_checks(x, vals, a, b, c, d)
-    _dev(out, "out")
+    _need(out, "out", (x.shape[0], a * c * d), device=x.device)
     y = out if out is not None else torch.empty(x.shape[0], a * c * d, device=x.device)
     check("ks_matmul", _lib.lib().ks_matmul(x.shape[0], a, b, c, d, dt, _ptr(x), _ptr(vals), _ptr(y),
                                             _stream(x.device)))
@@ -177,7 +226,7 @@ def ks_matmul_out(x: torch.Tensor, vals: torch.Tensor, a: int, b: int, c: int, d
         odt = KRON_BF16
     else:
         raise ValueError(f"unsupported output dtype {out_dtype}")
-    _dev(out, "out", out_dtype)
+    _need(out, "out", (x.shape[0], a * c * d), out_dtype, x.device)
     y = out if out is not None else torch.empty(x.shape[0], a * c * d, device=x.device, dtype=out_dtype)
     check("ks_matmul_out", _lib.lib().ks_matmul_out(x.shape[0], a, b, c, d, dt, odt, _ptr(x), _ptr(vals),
                                                     _ptr(y), _stream(x.device)))
@@ -194,18 +243,17 @@ def ks_matmul_bwd(x: torch.Tensor, vals: torch.Tensor, dy: torch.Tensor, a: int,
                   outs: Optional[dict] = None) -> dict:
     """Gradients of ks_matmul: dx = dy K^T and dvals (fp32), from x, vals, dy of one dtype."""
     dt = _ks_checks(x, vals, a, b, c, d)
-    _dev(dy, "dy", x.dtype)
-    if dy.dim() != 2 or dy.shape != (x.shape[0], a * c * d):
-        raise ValueError(f"dy must be N x {a * c * d}")
+    _need(dy, "dy", (x.shape[0], a * c * d), x.dtype, x.device)
     o = dict(outs or {})
     dev = x.device
+    _need(o.get("dx"), "dx", tuple(x.shape), device=dev)
+    if o.get("dvals") is not None:
+        _dev(o["dvals"], "dvals")
+        if o["dvals"].numel() != a * b * c * d or o["dvals"].device != dev:
+            raise ValueError(f"dvals must hold a*b*c*d = {a * b * c * d} values on {dev}")
     dx = o.get("dx") if "dx" in o else (torch.empty(x.shape, device=dev) if want_dx else None)
     dv = o.get("dvals") if "dvals" in o else (torch.empty(a, d, b, c, device=dev) if want_dvals else None)
-    _dev(dx, "dx")
-    _dev(dv, "dvals")
-    need = ks_matmul_bwd_workspace_bytes(x.shape[0], a, b, c, d, x.dtype)
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, ks_matmul_bwd_workspace_bytes(x.shape[0], a, b, c, d, x.dtype), dev)
     check("ks_matmul_bwd", _lib.lib().ks_matmul_bwd(
         x.shape[0], a, b, c, d, dt, _ptr(x), _ptr(vals), _ptr(dy), _ptr(dx), _ptr(dv), _ptr(workspace),
         ctypes.c_size_t(workspace.numel()), _stream(dev)))
@@ -225,17 +273,20 @@ def ks_chain(x: torch.Tensor, factors: Sequence, out: Optional[torch.Tensor] = N
     if x.dim() != 2:
         raise ValueError("x must be 2-D")
     arr = (_lib.KsFactor * max(len(factors), 1))()
+    width = x.shape[1]
     for i, (v, a, b, c, d) in enumerate(factors):
         _dev(v, "vals", x.dtype)
         if v.numel() != a * b * c * d:
             raise ValueError(f"factor {i}: vals must hold a*b*c*d = {a * b * c * d} values")
-        arr[i] = _lib.KsFactor(a, b, c, d, _ptr(v))
-    if factors:
-        v, a, b, c, d = factors[-1]
+        if v.device != x.device:
+            raise ValueError(f"factor {i}: vals is on {v.device}, expected {x.device}")
+        if a * b * d != width:
+            raise ValueError(f"factor {i}: input width a*b*d = {a * b * d} but the previous width is {width}")
         width = a * c * d
-    else:
+        arr[i] = _lib.KsFactor(a, b, c, d, _ptr(v))
+    if not factors:
         width = 0
-    _dev(out, "out")
+    _need(out, "out", (x.shape[0], width), device=x.device)
     y = out if out is not None else torch.empty(x.shape[0], width, device=x.device)
     check("ks_chain", _lib.lib().ks_chain(x.shape[0], len(factors), arr, dt, _ptr(x), _ptr(y), _stream(x.device)))
     return y
@@ -245,20 +296,16 @@ def kron_van_loan(W: torch.Tensor, p: int, q: int, m: int, n: int, r: int, omega
                   iters: int = 8, workspace: Optional[torch.Tensor] = None) -> tuple:
     """Rank-r Van Loan factors (C [r,p,q], B [r,m,n], sigma [r]) of a dense W [p*m, q*n];
     omega [m*n, s] is the random starting block (its width s sets the subspace)."""
-    _dev(W, "W")
+    _need(W, "W", (p * m, q * n))
     _dev(omega, "omega")
-    if W.shape != (p * m, q * n):
-        raise ValueError(f"W must be {p * m} x {q * n}")
-    if omega.dim() != 2 or omega.shape[0] != m * n:
-        raise ValueError(f"omega must be {m * n} x s")
+    if omega.dim() != 2 or omega.shape[0] != m * n or omega.device != W.device:
+        raise ValueError(f"omega must be {m * n} x s on {W.device}")
     s = omega.shape[1]
     dev = W.device
     C = torch.empty(r, p, q, device=dev)
     B = torch.empty(r, m, n, device=dev)
     sigma = torch.empty(r, device=dev)
-    need = int(_lib.lib().kron_van_loan_workspace_bytes(p, q, m, n, s))
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, int(_lib.lib().kron_van_loan_workspace_bytes(p, q, m, n, s)), dev)
     check("kron_van_loan", _lib.lib().kron_van_loan(p, q, m, n, r, s, iters, _ptr(W), _ptr(omega), _ptr(C), _ptr(B),
                                                     _ptr(sigma), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
                                                     _stream(dev)))
@@ -278,6 +325,8 @@ def kron_adam_l1_step(params: Sequence[torch.Tensor], grads: Sequence[torch.Tens
             _dev(t, f"{nm}[{i}]")
             if t.numel() != params[i].numel():
                 raise ValueError(f"tensor {i}: sizes differ")
+            if t.device != params[0].device:
+                raise ValueError(f"{nm}[{i}] is on {t.device}, expected {params[0].device}")
     if nt == 0:
         return
     arr = ctypes.c_void_p * nt
@@ -297,12 +346,14 @@ def kron_head_ce(h: torch.Tensor, W: torch.Tensor, b: torch.Tensor, labels: torc
     """Dense head + mean softmax cross-entropy, forward and backward in one call:
     dict(loss (1-element tensor), dh, dW, db)."""
     _dev(h, "h")
-    _dev(W, "W")
-    _dev(b, "b")
-    _dev(labels, "labels", torch.int64)
+    if h.dim() != 2 or W.dim() != 2:
+        raise ValueError("h must be N x K and W K x C")
     N, K = h.shape
     C = W.shape[1]
     dev = h.device
+    _need(W, "W", (K, C), device=dev)
+    _need(b, "b", (C,), device=dev)
+    _need(labels, "labels", (N,), torch.int64, dev)
     loss = torch.empty(1, device=dev)
     dh = torch.empty_like(h) if want_dh else None
     dW = torch.empty_like(W)
@@ -313,3 +364,53 @@ def kron_head_ce(h: torch.Tensor, W: torch.Tensor, b: torch.Tensor, labels: torc
         N, K, C, _ptr(h), _ptr(W), _ptr(b), _ptr(labels), _ptr(loss), _ptr(dh), _ptr(dW), _ptr(db),
         KRON_DX_RELU_MASK if relu_mask else 0, _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev)))
     return dict(loss=loss, dh=dh, dW=dW, db=db)
+
+
+def kron_relu_bwd(y: torch.Tensor, dy: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dy o [y > 0], the gradient through y = max(z, 0); out may be dy (in place)."""
+    _dev(y, "y")
+    _need(dy, "dy", tuple(y.shape), device=y.device)
+    _need(out, "out", tuple(y.shape), device=y.device)
+    o = out if out is not None else torch.empty_like(dy)
+    check("kron_relu_bwd", _lib.lib().kron_relu_bwd(y.numel(), _ptr(y), _ptr(dy), _ptr(o), _stream(y.device)))
+    return o
+
+
+def kron_l1_penalty(tensors: Sequence[torch.Tensor], lam: float, loss: Optional[torch.Tensor] = None,
+                    accumulate: bool = False) -> torch.Tensor:
+    """lam * sum_t sum|t| into a 1-element device tensor (added to `loss` with accumulate)."""
+    tensors = [t for t in tensors if t is not None]
+    dev = loss.device if loss is not None else (tensors[0].device if tensors else None)
+    if dev is None:
+        raise ValueError("kron_l1_penalty needs a tensor or a loss buffer to place its result")
+    for i, t in enumerate(tensors):
+        _dev(t, f"tensors[{i}]")
+        if t.device != dev:
+            raise ValueError(f"tensors[{i}] is on {t.device}, expected {dev}")
+    if loss is None:
+        if accumulate:
+            raise ValueError("accumulate needs a loss buffer")
+        loss = torch.empty(1, device=dev)
+    _need(loss, "loss", (1,), device=dev)
+    nt = len(tensors)
+    arr = (ctypes.c_void_p * max(nt, 1))(*[t.data_ptr() for t in tensors])
+    n = (ctypes.c_int64 * max(nt, 1))(*[t.numel() for t in tensors])
+    check("kron_l1_penalty", _lib.lib().kron_l1_penalty(nt, arr, n, float(lam), _ptr(loss),
+                                                        KRON_ACCUMULATE if accumulate else 0, _stream(dev)))
+    return loss
+
+
+def kron_l1_penalty_grad(S: torch.Tensor, lam: float, g: torch.Tensor,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """lam * g * sign(S) for a 1-element device tensor g (the upstream gradient)."""
+    _dev(S, "S")
+    if g.numel() != 1:
+        raise ValueError("g must hold one value")
+    _dev(g, "g")
+    if g.device != S.device:
+        raise ValueError(f"g is on {g.device}, expected {S.device}")
+    _need(out, "out", tuple(S.shape), device=S.device)
+    o = out if out is not None else torch.empty_like(S)
+    check("kron_l1_penalty_grad", _lib.lib().kron_l1_penalty_grad(S.numel(), _ptr(S), float(lam), _ptr(g), _ptr(o),
+                                                                  _stream(S.device)))
+    return o

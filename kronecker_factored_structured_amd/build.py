@@ -38,6 +38,7 @@ OBJECTS = [
     ("vanloan.hip", [], "vanloan"),
     ("adam_l1.hip", [], "adam_l1"),
     ("head_ce.hip", [], "head_ce"),
+    ("loss_terms.hip", [], "loss_terms"),
 ]
 SOURCES = sorted({src for src, _, _ in OBJECTS})
 

@@ -12,7 +12,7 @@ namespace {
 
 thread_local std::string g_last_error;
 
-int32_t fail(kron_status_t st, const char* fmt, ...) {
+kron_status_t fail(kron_status_t st, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -22,12 +22,12 @@ int32_t fail(kron_status_t st, const char* fmt, ...) {
   return st;
 }
 
-int32_t ok() {
+kron_status_t ok() {
   g_last_error.clear();
   return KRON_OK;
 }
 
-int32_t hip_fail(hipError_t e, const char* where) {
+kron_status_t hip_fail(hipError_t e, const char* where) {
   return fail(KRON_E_HIP, "%s: %s", where, hipGetErrorString(e));
 }
 
@@ -47,7 +47,7 @@ bool overlap(const Range& a, const Range& b) {
 }
 
 // Every output must be disjoint from every input and from every other output.
-int32_t check_alias(const Range* outs, int nout, const Range* ins, int nin) {
+kron_status_t check_alias(const Range* outs, int nout, const Range* ins, int nin) {
   for (int i = 0; i < nout; ++i) {
     for (int j = 0; j < nin; ++j)
       if (overlap(outs[i], ins[j]))
@@ -59,7 +59,7 @@ int32_t check_alias(const Range* outs, int nout, const Range* ins, int nin) {
   return KRON_OK;
 }
 
-int32_t check_align(const Range* rs, int n) {
+kron_status_t check_align(const Range* rs, int n) {
   for (int i = 0; i < n; ++i)
     if (rs[i].p && !aligned16(rs[i].p))
       return fail(KRON_E_ALIGN, "%s is not 16-byte aligned (%p)", rs[i].name, rs[i].p);
@@ -72,7 +72,7 @@ constexpr int64_t kMaxFeatures = 65536;
 constexpr int64_t kMaxParams = int64_t(1) << 24;
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
 
-int32_t check_shape(const kron_shape_t* s) {
+kron_status_t check_shape(const kron_shape_t* s) {
   if (!s) return fail(KRON_E_NULL, "shape is NULL");
   if (s->N < 0 || s->N > kMaxRows) return fail(KRON_E_SHAPE, "N = %lld out of range", (long long)s->N);
   const int32_t d[5] = {s->p, s->q, s->m, s->n, s->r};
@@ -146,7 +146,7 @@ extern "C" {
 
 int32_t kron_abi_version(void) { return KRON_ABI_VERSION; }
 
-const char* kron_status_str(int32_t st) {
+const char* kron_status_str(kron_status_t st) {
   switch (st) {
     case KRON_OK: return "ok";
     case KRON_E_NULL: return "null pointer";
@@ -164,8 +164,8 @@ const char* kron_status_str(int32_t st) {
 
 const char* kron_last_error(void) { return g_last_error.c_str(); }
 
-int32_t kron_linear_check(const kron_shape_t* s) {
-  const int32_t st = check_shape(s);
+kron_status_t kron_linear_check(const kron_shape_t* s) {
+  const kron_status_t st = check_shape(s);
   if (st != KRON_OK) return st;
   if (!kron::small_supported(s->p, s->q, s->m, s->n, s->r) &&
       (kron::generic_fwd_rows_per_tile(s->p, s->q, s->m, s->n) == 0 ||
@@ -180,9 +180,9 @@ size_t kron_linear_bwd_workspace_bytes(const kron_shape_t* s) {
   return bwd_workspace(s);
 }
 
-int32_t kron_linear_fwd(const kron_shape_t* s, const float* x, const float* S, const float* A,
+kron_status_t kron_linear_fwd(const kron_shape_t* s, const float* x, const float* S, const float* A,
                         const float* B, const float* bias, float* y, hipStream_t stream) {
-  int32_t st = kron_linear_check(s);
+  kron_status_t st = kron_linear_check(s);
   if (st != KRON_OK) return st;
   if (s->flags & KRON_DX_RELU_MASK) return fail(KRON_E_ARG, "KRON_DX_RELU_MASK is a backward flag");
   if (!A || !B) return fail(KRON_E_NULL, "A and B are required");
@@ -207,10 +207,10 @@ int32_t kron_linear_fwd(const kron_shape_t* s, const float* x, const float* S, c
   return ok();
 }
 
-int32_t kron_linear_bwd(const kron_shape_t* s, const float* x, const float* S, const float* A,
+kron_status_t kron_linear_bwd(const kron_shape_t* s, const float* x, const float* S, const float* A,
                         const float* B, const float* dy, float* dx, float* dS, float* dA, float* dB,
                         float* dbias, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  int32_t st = kron_linear_check(s);
+  kron_status_t st = kron_linear_check(s);
   if (st != KRON_OK) return st;
   if (s->flags & KRON_RELU_OUT) return fail(KRON_E_ARG, "KRON_RELU_OUT is a forward flag");
   if (!A || !B || !dA || !dB) return fail(KRON_E_NULL, "A, B, dA and dB are required");
@@ -292,9 +292,9 @@ size_t kron_linear_bwd_bf16_workspace_bytes(const kron_shape_t* s) {
   return w == 0 ? 256 : (w + 255) & ~size_t(255);
 }
 
-int32_t kron_linear_fwd_bf16(const kron_shape_t* s, const void* x, const void* S, const void* A, const void* B,
+kron_status_t kron_linear_fwd_bf16(const kron_shape_t* s, const void* x, const void* S, const void* A, const void* B,
                              const void* bias, void* y, hipStream_t stream) {
-  int32_t st = kron_linear_check(s);
+  kron_status_t st = kron_linear_check(s);
   if (st != KRON_OK) return st;
   if (s->flags & KRON_DX_RELU_MASK) return fail(KRON_E_ARG, "KRON_DX_RELU_MASK is a backward flag");
   if (!kron::bf16_supported(s->p, s->q, s->m, s->n, s->r))
@@ -321,10 +321,10 @@ int32_t kron_linear_fwd_bf16(const kron_shape_t* s, const void* x, const void* S
   return ok();
 }
 
-int32_t kron_linear_bwd_bf16(const kron_shape_t* s, const void* x, const void* S, const void* A, const void* B,
+kron_status_t kron_linear_bwd_bf16(const kron_shape_t* s, const void* x, const void* S, const void* A, const void* B,
                              const void* dy, void* dx, float* dS, float* dA, float* dB, float* dbias, void* workspace,
                              size_t workspace_bytes, hipStream_t stream) {
-  int32_t st = kron_linear_check(s);
+  kron_status_t st = kron_linear_check(s);
   if (st != KRON_OK) return st;
   if (s->flags & KRON_RELU_OUT) return fail(KRON_E_ARG, "KRON_RELU_OUT is a forward flag");
   if (!kron::bf16_supported(s->p, s->q, s->m, s->n, s->r))
@@ -367,7 +367,7 @@ int32_t kron_linear_bwd_bf16(const kron_shape_t* s, const void* x, const void* S
   return ok();
 }
 
-int32_t ks_matmul_out(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype, int32_t out_dtype,
+kron_status_t ks_matmul_out(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype, int32_t out_dtype,
                       const void* x, const void* vals, void* y, hipStream_t stream) {
   if (N < 0 || N > kMaxRows) return fail(KRON_E_SHAPE, "N = %lld out of range", (long long)N);
   if (a < 1 || b < 1 || c < 1 || d < 1) return fail(KRON_E_SHAPE, "a, b, c, d must be >= 1");
@@ -383,7 +383,7 @@ int32_t ks_matmul_out(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int
   const size_t es = in_dtype == KRON_F32 ? 4 : 2, os = out_dtype == KRON_F32 ? 4 : 2;
   const Range ins[2] = {{x, (size_t)N * in * es, "x"}, {vals, (size_t)a * b * c * d * es, "vals"}};
   const Range outs[1] = {{y, (size_t)N * out * os, "y"}};
-  int32_t st;
+  kron_status_t st;
   if ((st = check_align(ins, 2)) != KRON_OK || (st = check_align(outs, 1)) != KRON_OK) return st;
   if ((st = check_alias(outs, 1, ins, 2)) != KRON_OK) return st;
   if (N == 0) return ok();
@@ -393,7 +393,7 @@ int32_t ks_matmul_out(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int
   return ok();
 }
 
-int32_t ks_matmul(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype, const void* x,
+kron_status_t ks_matmul(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype, const void* x,
                   const void* vals, float* y, hipStream_t stream) {
   return ks_matmul_out(N, a, b, c, d, in_dtype, KRON_F32, x, vals, y, stream);
 }
@@ -401,7 +401,7 @@ int32_t ks_matmul(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t
 namespace {
 constexpr int64_t kMaxKsValues = int64_t{1} << 28;   // dvals columns of the reduction (int32)
 
-int32_t ks_shape_check(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype) {
+kron_status_t ks_shape_check(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype) {
   if (N < 0 || N > kMaxRows) return fail(KRON_E_SHAPE, "N = %lld out of range", (long long)N);
   if (a < 1 || b < 1 || c < 1 || d < 1) return fail(KRON_E_SHAPE, "a, b, c, d must be >= 1");
   const int64_t in = (int64_t)a * b * d, out = (int64_t)a * c * d;
@@ -423,10 +423,10 @@ size_t ks_matmul_bwd_workspace_bytes(int64_t N, int32_t a, int32_t b, int32_t c,
   return kron::ks_bwd_workspace_bytes(N, a, b, c, d, in_dtype);
 }
 
-int32_t ks_matmul_bwd(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype, const void* x,
+kron_status_t ks_matmul_bwd(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int32_t in_dtype, const void* x,
                       const void* vals, const void* dy, float* dx, float* dvals, void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
-  int32_t st = ks_shape_check(N, a, b, c, d, in_dtype);
+  kron_status_t st = ks_shape_check(N, a, b, c, d, in_dtype);
   if (st != KRON_OK) return st;
   if (!dx && !dvals) return ok();
   if (dx && !vals) return fail(KRON_E_NULL, "vals is required for dx");
@@ -451,7 +451,7 @@ int32_t ks_matmul_bwd(int64_t N, int32_t a, int32_t b, int32_t c, int32_t d, int
   return ok();
 }
 
-int32_t ks_chain(int64_t N, int32_t nfactors, const ks_factor_t* factors, int32_t in_dtype, const void* x, float* y,
+kron_status_t ks_chain(int64_t N, int32_t nfactors, const ks_factor_t* factors, int32_t in_dtype, const void* x, float* y,
                  hipStream_t stream) {
   if (N < 0 || N > kMaxRows) return fail(KRON_E_SHAPE, "N = %lld out of range", (long long)N);
   if (nfactors < 1 || nfactors > kron::kChainMaxFactors)
@@ -486,7 +486,7 @@ int32_t ks_chain(int64_t N, int32_t nfactors, const ks_factor_t* factors, int32_
   if (N > 0 && (!x || !y)) return fail(KRON_E_NULL, "x and y are required when N > 0");
   ins[0] = Range{x, (size_t)N * w0 * es, "x"};
   const Range outs[1] = {{y, (size_t)N * width * 4, "y"}};
-  int32_t st;
+  kron_status_t st;
   if ((st = check_align(ins, nfactors + 1)) != KRON_OK || (st = check_align(outs, 1)) != KRON_OK) return st;
   if ((st = check_alias(outs, 1, ins, nfactors + 1)) != KRON_OK) return st;
   if (N == 0) return ok();
@@ -502,7 +502,7 @@ int32_t ks_chain(int64_t N, int32_t nfactors, const ks_factor_t* factors, int32_
 namespace {
 constexpr int kVlMaxSide = 8192;   // p*q and m*n (one workgroup orthonormalises a p*q or m*n column)
 
-int32_t van_loan_check(int32_t p, int32_t q, int32_t m, int32_t n, int32_t r, int32_t s, int32_t iters) {
+kron_status_t van_loan_check(int32_t p, int32_t q, int32_t m, int32_t n, int32_t r, int32_t s, int32_t iters) {
   if (p < 1 || q < 1 || m < 1 || n < 1) return fail(KRON_E_SHAPE, "p, q, m, n must be >= 1");
   const int64_t M = (int64_t)p * q, K = (int64_t)m * n;
   if (M > kVlMaxSide || K > kVlMaxSide)
@@ -522,10 +522,10 @@ size_t kron_van_loan_workspace_bytes(int32_t p, int32_t q, int32_t m, int32_t n,
   return kron::van_loan_workspace_bytes(p, q, m, n, s);
 }
 
-int32_t kron_van_loan(int32_t p, int32_t q, int32_t m, int32_t n, int32_t r, int32_t s, int32_t iters, const float* W,
+kron_status_t kron_van_loan(int32_t p, int32_t q, int32_t m, int32_t n, int32_t r, int32_t s, int32_t iters, const float* W,
                       const float* omega, float* C, float* B, float* sigma, void* workspace, size_t workspace_bytes,
                       hipStream_t stream) {
-  int32_t st = van_loan_check(p, q, m, n, r, s, iters);
+  kron_status_t st = van_loan_check(p, q, m, n, r, s, iters);
   if (st != KRON_OK) return st;
   if (!W || !omega || !C || !B || !sigma) return fail(KRON_E_NULL, "W, omega, C, B and sigma are required");
   const size_t need = kron::van_loan_workspace_bytes(p, q, m, n, s);
@@ -543,7 +543,7 @@ int32_t kron_van_loan(int32_t p, int32_t q, int32_t m, int32_t n, int32_t r, int
   return ok();
 }
 
-int32_t kron_adam_l1_step(int32_t ntensors, float* const* params, const float* const* grads, float* const* m,
+kron_status_t kron_adam_l1_step(int32_t ntensors, float* const* params, const float* const* grads, float* const* m,
                           float* const* v, const int64_t* numel, const float* l1, int64_t step, double lr,
                           double beta1, double beta2, double eps, hipStream_t stream) {
   if (ntensors < 0 || ntensors > 4096) return fail(KRON_E_ARG, "ntensors = %d out of range", ntensors);
@@ -557,7 +557,7 @@ int32_t kron_adam_l1_step(int32_t ntensors, float* const* params, const float* c
     if (numel[t] == 0) continue;
     if (!params[t] || !grads[t] || !m[t] || !v[t]) return fail(KRON_E_NULL, "tensor %d has a NULL pointer", t);
     const Range rs[4] = {{params[t], 0, "param"}, {grads[t], 0, "grad"}, {m[t], 0, "m"}, {v[t], 0, "v"}};
-    int32_t st = check_align(rs, 4);
+    kron_status_t st = check_align(rs, 4);
     if (st != KRON_OK) return st;
     const size_t by = (size_t)numel[t] * 4;
     const Range outs[3] = {{params[t], by, "param"}, {m[t], by, "m"}, {v[t], by, "v"}};
@@ -584,6 +584,68 @@ int32_t kron_adam_l1_step(int32_t ntensors, float* const* params, const float* c
   return ok();
 }
 
+kron_status_t kron_relu_bwd(int64_t n, const float* y, const float* dy, float* out, hipStream_t stream) {
+  if (n < 0) return fail(KRON_E_SHAPE, "n = %lld must be >= 0", (long long)n);
+  if (n == 0) return ok();
+  if (!y || !dy || !out) return fail(KRON_E_NULL, "y, dy and out are required");
+  const Range rs[3] = {{y, 0, "y"}, {dy, 0, "dy"}, {out, 0, "out"}};
+  kron_status_t st = check_align(rs, 3);
+  if (st != KRON_OK) return st;
+  const size_t by = (size_t)n * 4;
+  const Range outs[1] = {{out, by, "out"}};
+  const Range ins[2] = {{y, by, "y"}, {dy, by, "dy"}};
+  // out may be dy itself (in place); any other overlap is refused
+  if ((st = check_alias(outs, 1, ins, out == dy ? 1 : 2)) != KRON_OK) return st;
+  hipError_t e = kron::launch_relu_bwd(n, y, dy, out, stream);
+  if (e != hipSuccess) return hip_fail(e, "kron_relu_bwd launch");
+  return ok();
+}
+
+kron_status_t kron_l1_penalty(int32_t ntensors, const float* const* tensors, const int64_t* numel, float lam,
+                              float* loss, uint32_t flags, hipStream_t stream) {
+  if (ntensors < 0 || ntensors > kron::kL1MaxTensors)
+    return fail(KRON_E_ARG, "ntensors = %d out of range [0, %d]", ntensors, kron::kL1MaxTensors);
+  if (!loss) return fail(KRON_E_NULL, "loss is required");
+  if (ntensors > 0 && (!tensors || !numel)) return fail(KRON_E_NULL, "tensors and numel are required");
+  if (flags & ~KRON_ACCUMULATE) return fail(KRON_E_ARG, "unknown flag bits 0x%x", flags);
+  if (!std::isfinite(lam)) return fail(KRON_E_ARG, "lam is not finite");
+  const Range lr[1] = {{loss, 4, "loss"}};
+  kron_status_t st = check_align(lr, 1);
+  if (st != KRON_OK) return st;
+  kron::L1Batch b{};
+  for (int32_t t = 0; t < ntensors; ++t) {
+    if (numel[t] < 0) return fail(KRON_E_ARG, "numel[%d] < 0", t);
+    if (numel[t] == 0) continue;
+    if (!tensors[t]) return fail(KRON_E_NULL, "tensor %d is NULL", t);
+    const Range in[1] = {{tensors[t], (size_t)numel[t] * 4, "tensor"}};
+    if ((st = check_align(in, 1)) != KRON_OK) return st;
+    if ((st = check_alias(lr, 1, in, 1)) != KRON_OK) return st;
+    b.t[b.count] = tensors[t];
+    b.numel[b.count] = numel[t];
+    ++b.count;
+  }
+  hipError_t e = kron::launch_l1_penalty(b, lam, loss, (flags & KRON_ACCUMULATE) != 0, stream);
+  if (e != hipSuccess) return hip_fail(e, "kron_l1_penalty launch");
+  return ok();
+}
+
+kron_status_t kron_l1_penalty_grad(int64_t n, const float* S, float lam, const float* g, float* dS,
+                                   hipStream_t stream) {
+  if (n < 0) return fail(KRON_E_SHAPE, "n = %lld must be >= 0", (long long)n);
+  if (n == 0) return ok();
+  if (!S || !g || !dS) return fail(KRON_E_NULL, "S, g and dS are required");
+  if (!std::isfinite(lam)) return fail(KRON_E_ARG, "lam is not finite");
+  const Range rs[3] = {{S, 0, "S"}, {g, 0, "g"}, {dS, 0, "dS"}};
+  kron_status_t st = check_align(rs, 3);
+  if (st != KRON_OK) return st;
+  const Range outs[1] = {{dS, (size_t)n * 4, "dS"}};
+  const Range ins[2] = {{S, (size_t)n * 4, "S"}, {g, 4, "g"}};
+  if ((st = check_alias(outs, 1, ins, 2)) != KRON_OK) return st;
+  hipError_t e = kron::launch_l1_grad(n, S, lam, g, dS, stream);
+  if (e != hipSuccess) return hip_fail(e, "kron_l1_penalty_grad launch");
+  return ok();
+}
+
 size_t kron_head_ce_workspace_bytes(int64_t N, int32_t K, int32_t C) {
   if (N < 0 || K < 1 || C < 1) return 0;
   // the larger of the two paths' partial sums (the matrix-core path uses more groups)
@@ -594,7 +656,7 @@ size_t kron_head_ce_workspace_bytes(int64_t N, int32_t K, int32_t C) {
   return ((floats * 4 + 255) & ~size_t(255)) + 256;
 }
 
-int32_t kron_head_ce(int64_t N, int32_t K, int32_t C, const float* h, const float* Wh, const float* bh,
+kron_status_t kron_head_ce(int64_t N, int32_t K, int32_t C, const float* h, const float* Wh, const float* bh,
                      const int64_t* labels, float* loss, float* dh, float* dWh, float* dbh, uint32_t flags,
                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (N < 0 || N > kMaxRows) return fail(KRON_E_SHAPE, "N = %lld out of range", (long long)N);
@@ -612,7 +674,7 @@ int32_t kron_head_ce(int64_t N, int32_t K, int32_t C, const float* h, const floa
                         {labels, (size_t)N * 8, "labels"}, {workspace, need, "workspace"}};
   const Range outs[4] = {{loss, 4, "loss"}, {dh, (size_t)N * K * 4, "dh"}, {dWh, (size_t)K * C * 4, "dWh"},
                          {dbh, (size_t)C * 4, "dbh"}};
-  int32_t st;
+  kron_status_t st;
   if ((st = check_align(ins, 5)) != KRON_OK || (st = check_align(outs, 4)) != KRON_OK) return st;
   if ((st = check_alias(outs, 4, ins, 5)) != KRON_OK) return st;
   kron::HeadArgs a{};

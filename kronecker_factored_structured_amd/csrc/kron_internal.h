@@ -219,6 +219,20 @@ struct AdamHyper {
 hipError_t launch_adam(const AdamBatch& b, int64_t max_numel, const AdamHyper& h, hipStream_t s);
 
 // ---------------------------------------------------------------------------------
+// ReLU gradient and the l1 penalty on S.
+// ---------------------------------------------------------------------------------
+constexpr int kL1MaxTensors = 64;
+struct L1Batch {
+  const float* t[kL1MaxTensors];
+  int64_t numel[kL1MaxTensors];
+  int32_t count;
+  int32_t pad_;
+};
+hipError_t launch_relu_bwd(int64_t n, const float* y, const float* dy, float* out, hipStream_t s);
+hipError_t launch_l1_penalty(const L1Batch& b, float lam, float* loss, bool accumulate, hipStream_t s);
+hipError_t launch_l1_grad(int64_t n, const float* S, float lam, const float* g, float* dS, hipStream_t s);
+
+// ---------------------------------------------------------------------------------
 // Dense head + softmax cross-entropy.
 // ---------------------------------------------------------------------------------
 struct HeadArgs {

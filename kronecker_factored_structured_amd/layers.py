@@ -28,7 +28,7 @@ class _KronLinearFn(torch.autograd.Function):
         x, S, A, B, y = ctx.saved_tensors
         dy = dy.contiguous()
         if ctx.relu:
-            dy = dy * (y > 0)
+            dy = api.kron_relu_bwd(y, dy)
         g = api.kron_linear_bwd(x, S, A, B, dy, want_dx=ctx.needs_input_grad[0],
                                 want_dbias=ctx.has_bias)
         return g["dx"], g["dS"], g["dA"], g["dB"], g["dbias"], None
@@ -57,7 +57,20 @@ class KronLinear(nn.Module):
         return _KronLinearFn.apply(x, self.S, self.A, self.B, self.bias, self.relu)
 
     def l1_penalty(self):
-        return self.S.abs().sum() if self.S is not None else 0.0
+        """sum|S| as a 0-dim tensor with autograd (sign(S) times the upstream gradient)."""
+        return _L1Fn.apply(self.S) if self.S is not None else 0.0
+
+
+class _L1Fn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, S):
+        ctx.save_for_backward(S)
+        return api.kron_l1_penalty([S.contiguous()], 1.0).view(())
+
+    @staticmethod
+    def backward(ctx, g):
+        (S,) = ctx.saved_tensors
+        return api.kron_l1_penalty_grad(S.contiguous(), 1.0, g.reshape(1).contiguous())
 
 
 class KSLinear(nn.Module):
@@ -82,7 +95,7 @@ class KronMLPStep:
 
     Parameters live in flat lists of device tensors in the order
     S1, A1, B1, bias1, S2, A2, B2, bias2, head_w (hidden x classes), head_b.
-    One step is 9 kernel launches plus the column reductions, independent of r.
+    One step is 10 kernel launches plus the column reductions, independent of r.
     """
 
     def __init__(self, layers, head_w, head_b, lam: float, lr: float, device,
@@ -110,12 +123,14 @@ class KronMLPStep:
         return w
 
     def grads(self, x: torch.Tensor, labels: torch.Tensor):
-        """Forward + backward; returns (loss tensor, gradient list, activations).  The l1
-        subgradient of the penalty is applied inside the Adam step."""
+        """Forward + backward; returns (loss tensor, gradient list, activations).  The loss is
+        the mean cross-entropy plus lam * (sum|S1| + sum|S2|); the l1 subgradient of the
+        penalty is applied inside the Adam step."""
         S1, A1, B1, b1, S2, A2, B2, b2, hw, hb = self.params
         h1 = api.kron_linear_fwd(x, S1, A1, B1, b1, relu=True)
         h2 = api.kron_linear_fwd(h1, S2, A2, B2, b2, relu=True)
         head = api.kron_head_ce(h2, hw, hb, labels, want_dh=True, relu_mask=True)
+        api.kron_l1_penalty([S1, S2], self.lam, loss=head["loss"], accumulate=True)
         shape2 = api.layer_shape(h1.shape[0], S2, A2, B2)
         g2 = api.kron_linear_bwd(h1, S2, A2, B2, head["dh"], want_dx=True, relu_mask=True,
                                  workspace=self._workspace("l2", api.kron_linear_bwd_workspace_bytes(shape2)))
@@ -127,7 +142,7 @@ class KronMLPStep:
         return head["loss"], grads, dict(h1=h1, h2=h2, dh2=head["dh"], dh1=g2["dx"])
 
     def step(self, x: torch.Tensor, labels: torch.Tensor):
-        """One full training step; returns the loss (cross-entropy part, device tensor)."""
+        """One full training step; returns the loss (cross-entropy + l1 penalty, device tensor)."""
         loss, grads, _ = self.grads(x, labels)
         self.step_count += 1
         api.kron_adam_l1_step(self.params, grads, self.m, self.v, self.step_count, self.lr,

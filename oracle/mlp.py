@@ -40,6 +40,11 @@ def softmax_ce(z, labels):
     return loss, dz
 
 
+def l1_penalty(tensors, lam):
+    """lam * sum over the tensors of sum|t| (the model's penalty; intro: S is l1-penalised)."""
+    return lam * sum(np.abs(as64(t)).sum() for t in tensors)
+
+
 def forward(x, layers, head_w, head_b):
     """Returns the activations (h1, h2) and the logits z."""
     h1 = kron.forward(x, layers[0]["S"], layers[0]["A"], layers[0]["B"], layers[0]["bias"], relu=True)
@@ -54,7 +59,7 @@ def step_grads(x, labels, layers, head_w, head_b, lam):
     Returns (loss, grads, acts) with grads = [layer1 dict, layer2 dict, head dict]."""
     h1, h2, z = forward(x, layers, head_w, head_b)
     ce, dz = softmax_ce(z, labels)
-    penalty = lam * sum(np.abs(as64(L["S"])).sum() for L in layers)
+    penalty = l1_penalty([L["S"] for L in layers], lam)
     head = dict(dW=h2.T @ dz, db=dz.sum(axis=0))
     dh2 = (dz @ as64(head_w).T) * (h2 > 0)
     g2 = kron.backward(h1, layers[1]["S"], layers[1]["A"], layers[1]["B"], dh2, want_dx=True)

@@ -290,6 +290,34 @@ def test_head_argument_errors():
     assert L.kron_head_ce(*bad) == _lib.KRON_E_ALIAS
 
 
+def test_relu_bwd_and_l1_argument_errors():
+    L = _lib.lib()
+    MB = 1 << 20
+    assert L.kron_relu_bwd(0, None, None, None, None) == 0                     # nothing to do
+    assert L.kron_relu_bwd(-1, P(0), P(MB), P(2 * MB), None) == _lib.KRON_E_SHAPE
+    assert L.kron_relu_bwd(10, None, P(MB), P(2 * MB), None) == _lib.KRON_E_NULL
+    assert L.kron_relu_bwd(10, P(4), P(MB), P(2 * MB), None) == _lib.KRON_E_ALIGN
+    assert L.kron_relu_bwd(10, P(0), P(MB), P(16), None) == _lib.KRON_E_ALIAS      # out over y
+    assert L.kron_relu_bwd(10, P(0), P(MB), P(MB + 16), None) == _lib.KRON_E_ALIAS  # out partly over dy
+    arr = ctypes.c_void_p * 2
+    n = (ctypes.c_int64 * 2)(100, 50)
+    T = arr(BASE, BASE + MB)
+    assert L.kron_l1_penalty(65, T, n, 1.0, P(2 * MB), 0, None) == _lib.KRON_E_ARG
+    assert L.kron_l1_penalty(2, T, n, 1.0, None, 0, None) == _lib.KRON_E_NULL
+    assert L.kron_l1_penalty(2, None, n, 1.0, P(2 * MB), 0, None) == _lib.KRON_E_NULL
+    assert L.kron_l1_penalty(2, T, n, 1.0, P(2 * MB), 2, None) == _lib.KRON_E_ARG          # unknown flag
+    assert L.kron_l1_penalty(2, T, n, float("nan"), P(2 * MB), 0, None) == _lib.KRON_E_ARG
+    assert L.kron_l1_penalty(2, T, (ctypes.c_int64 * 2)(100, -1), 1.0, P(2 * MB), 0, None) == _lib.KRON_E_ARG
+    assert L.kron_l1_penalty(2, T, n, 1.0, P(MB + 64), 0, None) == _lib.KRON_E_ALIAS        # loss in a tensor
+    assert L.kron_l1_penalty(2, arr(BASE, BASE + MB + 4), n, 1.0, P(2 * MB), 0, None) == _lib.KRON_E_ALIGN
+    assert L.kron_l1_penalty_grad(-1, P(0), 1.0, P(MB), P(2 * MB), None) == _lib.KRON_E_SHAPE
+    assert L.kron_l1_penalty_grad(0, None, 1.0, None, None, None) == 0
+    assert L.kron_l1_penalty_grad(10, P(0), 1.0, None, P(2 * MB), None) == _lib.KRON_E_NULL
+    assert L.kron_l1_penalty_grad(10, P(0), float("inf"), P(MB), P(2 * MB), None) == _lib.KRON_E_ARG
+    assert L.kron_l1_penalty_grad(10, P(0), 1.0, P(MB), P(16), None) == _lib.KRON_E_ALIAS   # dS over S
+    assert L.kron_l1_penalty_grad(10, P(0), 1.0, P(32), P(16), None) == _lib.KRON_E_ALIAS
+
+
 def test_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     import kronecker_factored_structured_amd as K

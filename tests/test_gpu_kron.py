@@ -241,6 +241,38 @@ def test_kron_linear_module_autograd():
         assert rel_err(host(t.grad), go[k]) <= TOL_F32, k
 
 
+def test_kron_linear_module_autograd_relu_and_penalty():
+    """KronLinear(relu=True): y = max(x W + bias, 0); the loss <R, y> + lam * sum|S| through
+    autograd gives the oracle's gradients with dY = R o [y > 0] (the mask taken from the
+    GPU's own y, so a sign decided differently at a rounding tie cannot flip a row), and
+    dS gains lam * sign(S)."""
+    mod = K()
+    lam = 3e-3
+    layer = mod.KronLinear(1024, 1024, m=32, r=4, with_S=True, relu=True, device="cuda")
+    inp = kron_inputs(43, 1031, 32, 32, 32, 32, 4, s_mode="uniform_zeroed", bias_mode="normal")
+    with torch.no_grad():
+        layer.S.copy_(dev(inp.S)); layer.A.copy_(dev(inp.A)); layer.B.copy_(dev(inp.B))
+        layer.bias.copy_(dev(inp.bias))
+        layer.S[0, :5] = -layer.S[0, :5]           # negative entries: sign(S) = -1 there
+    S_host = host(layer.S).astype(np.float32)
+    x = dev(inp.x).requires_grad_(True)
+    y = layer(x)
+    pen = layer.l1_penalty()
+    assert pen.dim() == 0
+    loss = (y * dev(inp.dy)).sum() + lam * pen
+    loss.backward()
+    torch.cuda.synchronize()
+    yh = host(y)
+    W = OK.weight(S_host, inp.A, inp.B)
+    assert rel_err(yh, np.maximum(inp.x.astype(np.float64) @ W + inp.bias, 0)) <= TOL_F32
+    assert abs(host(pen) - np.abs(S_host.astype(np.float64)).sum()) <= TOL_F32 * np.abs(S_host).sum()
+    dym = inp.dy * (yh > 0)
+    go = OK.backward(inp.x, S_host, inp.A, inp.B, dym, W=W)
+    go["dS"] = go["dS"] + lam * np.sign(S_host.astype(np.float64))
+    for t, k in ((x, "dx"), (layer.S, "dS"), (layer.A, "dA"), (layer.B, "dB"), (layer.bias, "dbias")):
+        assert rel_err(host(t.grad), go[k]) <= TOL_F32, k
+
+
 # ---------------------------------------------------------------------------------
 # Small blocks (m = n in {2, 4, 8}, p and q multiples of 16): the matrix-core GEMM path.
 # The tutorial's 1024 x 1024 layer with 8 x 8, 4 x 4 and 2 x 2 blocks is p = q = 128, 256, 512.
