@@ -114,6 +114,28 @@ kron_status_t kron_linear_bwd(const kron_shape_t* shape, const float* x, const f
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * kron_linear_bwd without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same operation, arguments, checks and results as kron_linear_bwd; the
+ * partial-row workspace is a fixed scratch array inside the library instead, one copy
+ * per GPU, KRON_NOALLOC_SCRATCH_BYTES long, held until the process ends.  The call
+ * itself allocates and frees nothing.
+ *   - A shape whose kron_linear_bwd_workspace_bytes exceeds KRON_NOALLOC_SCRATCH_BYTES
+ *     is refused with KRON_E_UNSUPPORTED before anything runs.
+ *   - The first call made with a device current looks up that device's scratch address
+ *     (hipGetSymbolAddress); a failure there returns KRON_E_HIP.
+ *   - Every call on one GPU uses that GPU's one scratch array: calls that may overlap on
+ *     one GPU (different streams, different host threads) race on it and must be
+ *     serialised by the caller.  Calls ordered on one stream are safe.  Nothing in the
+ *     scratch needs to start at zero: each call writes the part it reads.
+ */
+#define KRON_NOALLOC_SCRATCH_BYTES (32u << 20)
+kron_status_t kron_linear_bwd_noalloc(const kron_shape_t* shape, const float* x, const float* S,
+                                      const float* A, const float* B, const float* dy,
+                                      float* dx, float* dS, float* dA, float* dB, float* dbias,
+                                      hipStream_t stream);
+
+/*
  * bf16 layer (mixed precision; the tutorial's "Takeaways" name a mixed-precision rerun as
  * the next step).  Same operation as kron_linear_fwd / kron_linear_bwd with bf16 storage
  * (bfloat16 bit patterns) for x, S, A, B, bias, dy and the outputs y and dx; products

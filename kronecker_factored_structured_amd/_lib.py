@@ -37,8 +37,10 @@ EXPORTS = (
     "kron_linear_bwd_bf16_workspace_bytes", "kron_linear_fwd_bf16", "kron_linear_bwd_bf16",
     "ks_matmul_out", "ks_matmul_bwd_workspace_bytes", "ks_matmul_bwd", "ks_chain",
     "kron_van_loan_workspace_bytes", "kron_van_loan", "kron_relu_bwd", "kron_l1_penalty",
-    "kron_l1_penalty_grad",
+    "kron_l1_penalty_grad", "kron_linear_bwd_noalloc",
 )
+
+KRON_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class KsFactor(ctypes.Structure):
@@ -96,6 +98,7 @@ def lib() -> ctypes.CDLL:
             "kron_linear_bwd_bf16_workspace_bytes": (sz, [shp]),
             "kron_linear_fwd_bf16": (i32, [shp, vp, vp, vp, vp, vp, vp, vp]),
             "kron_linear_bwd_bf16": (i32, [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "kron_linear_bwd_noalloc": (i32, [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "kron_relu_bwd": (i32, [i64, vp, vp, vp, vp]),
             "kron_l1_penalty": (i32, [i32, pp, ctypes.POINTER(ctypes.c_int64), ctypes.c_float, vp, u32, vp]),
             "kron_l1_penalty_grad": (i32, [i64, vp, ctypes.c_float, vp, vp, vp]),

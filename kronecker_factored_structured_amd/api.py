@@ -137,6 +137,23 @@ def kron_linear_bwd(x: torch.Tensor, S: Optional[torch.Tensor], A: torch.Tensor,
     return dict(dx=dx, dS=dS, dA=dA, dB=dB, dbias=dbias)
 
 
+def kron_linear_bwd_noalloc(x: torch.Tensor, S: Optional[torch.Tensor], A: torch.Tensor, B: torch.Tensor,
+                            dy: torch.Tensor, outs: dict, relu_mask: bool = False) -> dict:
+    """kron_linear_bwd into caller-given buffers (outs: dx or None, dS, dA, dB, dbias or None)
+    with the library's fixed scratch as workspace: the call allocates nothing."""
+    for t, nm in ((x, "x"), (S, "S"), (A, "A"), (B, "B"), (dy, "dy")):
+        _dev(t, nm)
+    shape = layer_shape(x.shape[0], S, A, B, KRON_DX_RELU_MASK if relu_mask else 0)
+    _layer_io_checks(x, shape, S, A, B, dy)
+    o = dict(outs)
+    _grad_out_checks(o, x, shape)
+    dx, dS, dA, dB, dbias = (o.get(k) for k in ("dx", "dS", "dA", "dB", "dbias"))
+    check("kron_linear_bwd_noalloc", _lib.lib().kron_linear_bwd_noalloc(
+        ctypes.byref(shape), _ptr(x), _ptr(S), _ptr(A), _ptr(B), _ptr(dy), _ptr(dx), _ptr(dS), _ptr(dA),
+        _ptr(dB), _ptr(dbias), _stream(x.device)))
+    return dict(dx=dx, dS=dS, dA=dA, dB=dB, dbias=dbias)
+
+
 def kron_linear_bwd_bf16_workspace_bytes(shape: KronShape) -> int:
     return int(_lib.lib().kron_linear_bwd_bf16_workspace_bytes(ctypes.byref(shape)))
 

@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "kron_internal.h"
@@ -207,9 +208,13 @@ kron_status_t kron_linear_fwd(const kron_shape_t* s, const float* x, const float
   return ok();
 }
 
-kron_status_t kron_linear_bwd(const kron_shape_t* s, const float* x, const float* S, const float* A,
-                        const float* B, const float* dy, float* dx, float* dS, float* dA, float* dB,
-                        float* dbias, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// kron_linear_bwd's argument checks (host only), with the workspace size taken as given.
+kron_status_t bwd_checks(const kron_shape_t* s, const float* x, const float* S, const float* A, const float* B,
+                         const float* dy, float* dx, float* dS, float* dA, float* dB, float* dbias) {
   kron_status_t st = kron_linear_check(s);
   if (st != KRON_OK) return st;
   if (s->flags & KRON_RELU_OUT) return fail(KRON_E_ARG, "KRON_RELU_OUT is a forward flag");
@@ -217,6 +222,14 @@ kron_status_t kron_linear_bwd(const kron_shape_t* s, const float* x, const float
   if ((S == nullptr) != (dS == nullptr)) return fail(KRON_E_NULL, "dS must be given exactly when S is");
   if (s->N > 0 && (!x || !dy)) return fail(KRON_E_NULL, "x and dy are required when N > 0");
   if ((s->flags & KRON_DX_RELU_MASK) && !dx) return fail(KRON_E_ARG, "KRON_DX_RELU_MASK needs dx");
+  return KRON_OK;
+}
+
+kron_status_t bwd_run(const kron_shape_t* s, const float* x, const float* S, const float* A, const float* B,
+                      const float* dy, float* dx, float* dS, float* dA, float* dB, float* dbias, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  kron_status_t st = bwd_checks(s, x, S, A, B, dy, dx, dS, dA, dB, dbias);
+  if (st != KRON_OK) return st;
   const size_t need = bwd_workspace(s);
   if (!workspace || workspace_bytes < need)
     return fail(KRON_E_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
@@ -282,6 +295,67 @@ kron_status_t kron_linear_bwd(const kron_shape_t* s, const float* x, const float
   e = kron::launch_column_reduce(a.part, pl.G, PW, rp, stream);
   if (e != hipSuccess) return hip_fail(e, "kron_linear_bwd reduce launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kron_status_t kron_linear_bwd(const kron_shape_t* s, const float* x, const float* S, const float* A,
+                              const float* B, const float* dy, float* dx, float* dS, float* dA, float* dB,
+                              float* dbias, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_run(s, x, S, A, B, dy, dx, dS, dA, dB, dbias, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// The fixed scratch of kron_linear_bwd_noalloc: the backward's partial-row workspace for
+// callers that cannot allocate.  Each GPU the library runs on holds its own copy for the
+// life of the process.  In host code `scratch` only names the symbol; its device address
+// on the current GPU comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[KRON_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// The device address of `scratch` on the current device (looked up on the first call
+// made with that device current).
+kron_status_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(KRON_E_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || ((uintptr_t)p & 255u) != 0) return fail(KRON_E_HIP, "scratch has no 256-byte aligned address");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return KRON_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kron_status_t kron_linear_bwd_noalloc(const kron_shape_t* s, const float* x, const float* S, const float* A,
+                                      const float* B, const float* dy, float* dx, float* dS, float* dA,
+                                      float* dB, float* dbias, hipStream_t stream) {
+  kron_status_t st = bwd_checks(s, x, S, A, B, dy, dx, dS, dA, dB, dbias);
+  if (st != KRON_OK) return st;
+  const size_t need = bwd_workspace(s);
+  if (need > KRON_NOALLOC_SCRATCH_BYTES)
+    return fail(KRON_E_UNSUPPORTED, "this shape needs %zu bytes of scratch; the fixed scratch holds %zu", need,
+                (size_t)KRON_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != KRON_OK) return st;
+  return bwd_run(s, x, S, A, B, dy, dx, dS, dA, dB, dbias, ws, KRON_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t kron_linear_bwd_bf16_workspace_bytes(const kron_shape_t* s) {
