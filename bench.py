@@ -129,10 +129,11 @@ def cpu_baseline(inp, seconds: float):
 class Layer:
     """Device tensors and preallocated outputs of one Kronecker layer workload."""
 
-    def __init__(self, inp, dev):
+    def __init__(self, inp, dev, sparse_rows=False):
         import torch
         import kronecker_factored_structured_amd as K
         self.K = K
+        self.sparse_rows = sparse_rows
         t = lambda a: None if a is None else torch.from_numpy(a).to(dev).contiguous()
         self.x, self.S, self.A, self.B, self.bias, self.dy = (t(a) for a in (inp.x, inp.S, inp.A, inp.B,
                                                                            inp.bias, inp.dy))
@@ -145,7 +146,7 @@ class Layer:
         self.ws = torch.empty(K.kron_linear_bwd_workspace_bytes(shape), dtype=torch.uint8, device=dev)
 
     def fwd(self):
-        self.K.kron_linear_fwd(self.x, self.S, self.A, self.B, self.bias, out=self.y)
+        self.K.kron_linear_fwd(self.x, self.S, self.A, self.B, self.bias, out=self.y, sparse_rows=self.sparse_rows)
 
     def bwd(self):
         self.K.kron_linear_bwd(self.x, self.S, self.A, self.B, self.dy, workspace=self.ws, outs=self.outs)
@@ -387,6 +388,25 @@ def run_small_blocks(args, dev):
         inp = kron_inputs(80 + r, 20000, p, p, m, m, r, s_mode="uniform_zeroed", bias_mode="zeros")
         layer_record(f"small_blocks: 1024x1024 layer, {m}x{m} blocks (p=q={p}), r={r}, half of S zeroed, "
                      f"20000 rows", inp, Layer(inp, dev), args)
+
+
+def run_sparse_s(args, dev):
+    """The 1024 x 1024 layer (m = 32, r = 4, 20,000 rows) with whole rows of S zero (the
+    structure an l1-pruned mask can leave), against S with the same share of zero entries
+    at random positions, which leaves no row empty: the forward's row map runs only the
+    16-row tiles that hold nonzero rows of C = S o A_i."""
+    from workloads import kron_inputs
+    for mode, frac in (("uniform_zeroed", 0.5), ("rows_zeroed", 0.0), ("rows_zeroed", 0.25), ("rows_zeroed", 0.5),
+                       ("rows_zeroed", 0.75), ("rows_zeroed", 0.875)):
+        inp = kron_inputs(90, 20000, 32, 32, 32, 32, 4, s_mode=mode, zero_frac=frac, bias_mode="zeros")
+        rows_left = int(np.count_nonzero(inp.S.any(axis=1)))
+        what = (f"{frac:.0%} of S's entries zero at random" if mode == "uniform_zeroed"
+                else f"{frac:.1%} of S's rows zero ({rows_left} of 32 rows left)")
+        for hint in (False, True):
+            layer_record(f"sparse_s: 1024x1024 layer, m=32, r=4, 20000 rows, {what}, "
+                         f"{'KRON_SPARSE_ROWS' if hint else 'dense path'}", inp, Layer(inp, dev, sparse_rows=hint),
+                         args, extra={"s_rows_nonzero": rows_left, "sparse_rows": hint,
+                                      "fwd_tiles_run": max(1, -(-rows_left // 16)) if hint else 2})
 
 
 def run_mlp_step(args, dev):
@@ -633,7 +653,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the copy and GEMM ceiling measurements")
     ap.add_argument("--workload", default="headline",
-                    choices=("headline", "headline_bf16", "tiny", "mlp_step", "gpt2_ffn", "ks", "ks_bwd", "chain", "van_loan", "sweep", "small_blocks"))
+                    choices=("headline", "headline_bf16", "tiny", "mlp_step", "gpt2_ffn", "ks", "ks_bwd", "chain", "van_loan", "sweep", "small_blocks", "sparse_s"))
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed running before the warmup steps, for the GPU clock to ramp up")
@@ -650,7 +670,7 @@ def main():
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         return run_copy(args, dev)
-    {"headline": run_headline, "headline_bf16": run_headline_bf16, "tiny": run_tiny, "sweep": run_sweep, "small_blocks": run_small_blocks, "ks_bwd": run_ks_bwd, "chain": run_chain, "van_loan": run_van_loan, "mlp_step": run_mlp_step, "gpt2_ffn": run_gpt2,
+    {"headline": run_headline, "headline_bf16": run_headline_bf16, "sparse_s": run_sparse_s, "tiny": run_tiny, "sweep": run_sweep, "small_blocks": run_small_blocks, "ks_bwd": run_ks_bwd, "chain": run_chain, "van_loan": run_van_loan, "mlp_step": run_mlp_step, "gpt2_ffn": run_gpt2,
      "ks": run_ks}[args.workload](args, dev)
 
 

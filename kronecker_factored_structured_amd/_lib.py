@@ -26,6 +26,7 @@ KRON_BF16 = 1
 
 KRON_RELU_OUT = 1
 KRON_DX_RELU_MASK = 2
+KRON_SPARSE_ROWS = 4
 
 KRON_ACCUMULATE = 1
 

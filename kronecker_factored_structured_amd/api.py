@@ -12,7 +12,8 @@ from typing import Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import KRON_ACCUMULATE, KRON_BF16, KRON_DX_RELU_MASK, KRON_F32, KRON_RELU_OUT, KronShape, check
+from ._lib import (KRON_ACCUMULATE, KRON_BF16, KRON_DX_RELU_MASK, KRON_F32, KRON_RELU_OUT, KRON_SPARSE_ROWS, KronShape,
+                   check)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -98,11 +99,13 @@ def kron_linear_bwd_workspace_bytes(shape: KronShape) -> int:
 
 def kron_linear_fwd(x: torch.Tensor, S: Optional[torch.Tensor], A: torch.Tensor, B: torch.Tensor,
                     bias: Optional[torch.Tensor] = None, relu: bool = False,
-                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """y = x W + bias with W = sum_i kron(S o A_i, B_i) (optionally ReLU-ed)."""
+                    out: Optional[torch.Tensor] = None, sparse_rows: bool = False) -> torch.Tensor:
+    """y = x W + bias with W = sum_i kron(S o A_i, B_i) (optionally ReLU-ed).  sparse_rows:
+    S is expected to have whole rows zero; the forward then skips the 16-row tiles of C that
+    hold only such rows (KRON_SPARSE_ROWS)."""
     for t, nm in ((x, "x"), (S, "S"), (A, "A"), (B, "B")):
         _dev(t, nm)
-    shape = layer_shape(x.shape[0], S, A, B, KRON_RELU_OUT if relu else 0)
+    shape = layer_shape(x.shape[0], S, A, B, (KRON_RELU_OUT if relu else 0) | (KRON_SPARSE_ROWS if sparse_rows else 0))
     _layer_io_checks(x, shape, S, A, B)
     _need(bias, "bias", (shape.q * shape.n,), device=x.device)
     _need(out, "out", (x.shape[0], shape.q * shape.n), device=x.device)

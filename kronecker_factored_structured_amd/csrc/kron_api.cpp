@@ -89,7 +89,7 @@ kron_status_t check_shape(const kron_shape_t* s) {
                 (long long)kMaxFeatures);
   if ((int64_t)s->r * s->p * s->q > kMaxParams || (int64_t)s->r * s->m * s->n > kMaxParams)
     return fail(KRON_E_UNSUPPORTED, "factor tensors exceed %lld elements", (long long)kMaxParams);
-  if (s->flags & ~(KRON_RELU_OUT | KRON_DX_RELU_MASK))
+  if (s->flags & ~(KRON_RELU_OUT | KRON_DX_RELU_MASK | KRON_SPARSE_ROWS))
     return fail(KRON_E_ARG, "unknown flag bits 0x%x", s->flags);
   return KRON_OK;
 }

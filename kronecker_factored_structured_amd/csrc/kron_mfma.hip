@@ -167,7 +167,9 @@ struct Dims {
   // the forward stages the raw factors next to its tables when they fit, else builds the
   // tables straight from global memory
   static constexpr bool FWD_RAW = (size_t)(BOP + COPF + RAW) * 4 <= kMaxLds;
-  static constexpr int FWD_FLOATS = BOP + COPF + (FWD_RAW ? RAW : 0);
+  // the forward's row map (FwdMap): a 64-bit row mask per wavefront and the map (TJ*16 ints)
+  static constexpr int FWD_MAP = (2 * kWaves + TJ * 16 + 3) / 4 * 4;
+  static constexpr int FWD_FLOATS = BOP + COPF + (FWD_RAW ? RAW + FWD_MAP : 0);
   static constexpr int BWD_TABLES = BOP + COPG + BOPX;
   static constexpr int BWD_SCRATCH = (kWaves * GS > RAW) ? kWaves * GS : RAW;
   static constexpr int BWD_MAIN = BWD_TABLES + BWD_SCRATCH;
@@ -186,9 +188,12 @@ struct Dims {
 
 // Stage B (as is) and C = S o A in LDS with coalesced 16-byte loads.  Every global load
 // is issued before the first LDS store, so the staging costs one memory round trip.
+// With cbits, also set bit j of *cbits for every row j of C (any rank) that holds a
+// nonzero value among this thread's entries (Q % 4 == 0: a 4-float vector lies in one row).
 template <class D>
 __device__ __forceinline__ void stage_raw(float* rB, float* rC, const float* __restrict__ B,
-                                          const float* __restrict__ S, const float* __restrict__ A) {
+                                          const float* __restrict__ S, const float* __restrict__ A,
+                                          unsigned long long* cbits = nullptr) {
   constexpr int PQ = D::P * D::Q;
   if constexpr (PQ % 4 == 0) {
     constexpr int NB = D::RAWB / 4, NC = D::R * PQ / 4;
@@ -215,7 +220,14 @@ __device__ __forceinline__ void stage_raw(float* rB, float* rC, const float* __r
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
       const int e = threadIdx.x + k * kThreads;
-      if (NC % kThreads == 0 || e < NC) reinterpret_cast<f4*>(rC)[e] = S ? a[k] * m[k] : a[k];
+      if (NC % kThreads == 0 || e < NC) {
+        const f4 cv = S ? a[k] * m[k] : a[k];
+        reinterpret_cast<f4*>(rC)[e] = cv;
+        if constexpr (D::Q % 4 == 0 && D::P <= 64) {
+          if (cbits && (cv[0] != 0.f || cv[1] != 0.f || cv[2] != 0.f || cv[3] != 0.f))
+            *cbits |= 1ull << ((4 * e / D::Q) % D::P);
+        }
+      }
     }
   } else {
 #pragma unroll 4
@@ -284,69 +296,51 @@ __device__ __forceinline__ void load_xa(float (&xa)[D::TJ][D::SA], const float* 
 }
 
 #if KRON_MFMA_PASS != 2
-template <class D>
-__global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t flags,
-                                                            const float* __restrict__ x,
-                                                            const float* __restrict__ Sm,
-                                                            const float* __restrict__ A,
-                                                            const float* __restrict__ B,
-                                                            const float* __restrict__ bias,
-                                                            float* __restrict__ y) {
-  extern __shared__ float lds[];
-  float* bop = lds;              // B_i[g*SA+s][16tb+c]
-  float* cop = bop + D::BOP;     // C_i[16tj+4g+v][16tk+c]
-  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-  const int wave = threadIdx.x >> 6;
-  const int64_t stride = (int64_t)gridDim.x * kWaves;
-  int64_t row = (int64_t)blockIdx.x * kWaves + wave;
-  // the first row's X is loaded while the tables are built
-  float xa[D::TJ][D::SA];   // X[j = 16tj+c][a = g*SA+s]
-  if (row < N) load_xa<D>(xa, x + row * D::IN, g, c);
-  // the bias is loaded with the first row, before the tables are built
-  f4 bb[D::TB][D::TK];
+// The row map of the forward (the sparsity map of C = S o A_i, kept per row of C because
+// a matrix-core K step needs the same rows j for all 16 columns k of its tile): the rows
+// j of C with a nonzero entry in any rank, in order, then the all-zero rows.  Z rows and
+// stage-2 K steps are taken in map order over the first TJE 16-row tiles only, TJE =
+// ceil(nonzero rows / 16): the tiles beyond hold only zero rows of every C_i, whose
+// products add nothing.  With every row nonzero the map is the identity and TJE = TJ.
+template <class D, bool MAP>
+struct FwdMap {
+  static constexpr bool ON = MAP && D::FWD_RAW && D::TJ > 1 && D::P <= 64 && D::Q % 4 == 0 &&
+                             (D::P * D::Q) % 4 == 0;   // (one tile: nothing to skip)
+};
+
+// X[j = map(16tj+c)][a = g*SA+s] of one row for the first TJE tiles (jr < 0: padding).
+template <class D, int TJE>
+__device__ __forceinline__ void load_xa_map(float (&xa)[D::TJ][D::SA], const float* xr, const int (&jr)[D::TJ],
+                                            int g) {
 #pragma unroll
-  for (int tb = 0; tb < D::TB; ++tb)
+  for (int tj = 0; tj < TJE; ++tj) {
+    if (D::P % 16 == 0 || jr[tj] >= 0) {   // (a whole number of tiles has no padding rows)
+      vload<D::SA>(xa[tj], xr + jr[tj] * D::M + g * D::SA);
+    } else {
 #pragma unroll
-    for (int tk = 0; tk < D::TK; ++tk) {
-      const int k = 16 * tk + c, b0 = 16 * tb + 4 * g;
-      bb[tb][tk] = (bias && k < D::Q && b0 < D::N) ? *reinterpret_cast<const f4*>(bias + k * D::N + b0)
-                                                  : f4{0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < D::SA; ++s) xa[tj][s] = 0.f;
     }
-  if constexpr (D::FWD_RAW) {
-    float* rB = cop + D::COPF;
-    float* rC = rB + D::RAWB;
-    stage_raw<D>(rB, rC, B, Sm, A);
-    __syncthreads();
-    build_table<D::R, D::TB, D::SA>(bop, [&](int i, int tb, int g, int c, int s) {
-      return rawB<D>(rB, i, g * D::SA + s, 16 * tb + c);
-    });
-    build_table<D::R, D::TK, D::SJ>(cop, [&](int i, int tk, int g, int c, int sv) {
-      return rawC<D>(rC, i, 16 * (sv / 4) + 4 * g + (sv % 4), 16 * tk + c);
-    });
-  } else {
-    build_table<D::R, D::TB, D::SA>(bop, [&](int i, int tb, int g, int c, int s) {
-      const int a = g * D::SA + s, b = 16 * tb + c;
-      return (a < D::M && b < D::N) ? B[(i * D::M + a) * D::N + b] : 0.f;
-    });
-    build_table<D::R, D::TK, D::SJ>(cop, [&](int i, int tk, int g, int c, int sv) {
-      const int j = 16 * (sv / 4) + 4 * g + (sv % 4), k = 16 * tk + c;
-      if (j >= D::P || k >= D::Q) return 0.f;
-      const float a = A[(i * D::P + j) * D::Q + k];
-      return Sm ? Sm[j * D::Q + k] * a : a;
-    });
   }
-  __syncthreads();
+}
 
-  const bool relu = flags & KRON_RELU_OUT;
-
+// The row loop of the forward over the first TJE tiles of the row map.
+template <class D, int TJE>
+__device__ __forceinline__ void fwd_rows(int64_t row, int64_t N, bool relu, const float* __restrict__ x,
+                                         float* __restrict__ y, const float* bop, const float* cop,
+                                         float (&xa)[D::TJ][D::SA], const int (&jr)[D::TJ],
+                                         const f4 (&bb)[D::TB][D::TK], int lane, int g, int c) {
+  const int64_t stride = (int64_t)gridDim.x * kWaves;
   // The next row's X is loaded at the top of each row (the last row reloads itself), and
   // a scheduling barrier keeps the compiler from sinking those loads towards their use.
   float xn[D::TJ][D::SA];
-  settle(xa);
+#pragma unroll
+  for (int tj = 0; tj < TJE; ++tj)
+#pragma unroll
+    for (int s = 0; s < D::SA; ++s) asm volatile("" ::"v"(xa[tj][s]));
   for (; row < N; row += stride) {
     {
       const int64_t nr = row + stride < N ? row + stride : row;
-      load_xa<D>(xn, x + nr * D::IN, g, c);
+      load_xa_map<D, TJE>(xn, x + nr * D::IN, jr, g);
     }
     __builtin_amdgcn_sched_barrier(0);
     f4 acc[D::TB][D::TK];
@@ -359,17 +353,17 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
     // rank loop would not fit the register file)
 #pragma unroll(D::R <= 4 ? D::R : 2)
     for (int i = 0; i < D::R; ++i) {
-      f4 z[D::TJ][D::TB];
+      f4 z[TJE][D::TB];
 #pragma unroll
       for (int tb = 0; tb < D::TB; ++tb) {
         float bo[D::SA];
         table_read<D::SA>(bo, bop + (i * D::TB + tb) * 64 * D::SA, lane);
 #pragma unroll
-        for (int tj = 0; tj < D::TJ; ++tj) {
+        for (int tj = 0; tj < TJE; ++tj) {
           f4 t = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < D::SA; ++s) t = mfma(xa[tj][s], bo[s], t);
-          z[tj][tb] = t;   // Z[j = 16tj+4g+v][b = 16tb+c]
+          z[tj][tb] = t;   // Z[j = map(16tj+4g+v)][b = 16tb+c]
         }
       }
 #pragma unroll
@@ -379,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
 #pragma unroll
         for (int tb = 0; tb < D::TB; ++tb)
 #pragma unroll
-          for (int tj = 0; tj < D::TJ; ++tj)
+          for (int tj = 0; tj < TJE; ++tj)
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[tb][tk] = mfma(z[tj][tb][v], co[tj * 4 + v], acc[tb][tk]);
       }
@@ -401,10 +395,129 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
         }
       }
 #pragma unroll
-    for (int tj = 0; tj < D::TJ; ++tj)
+    for (int tj = 0; tj < TJE; ++tj)
 #pragma unroll
       for (int s = 0; s < D::SA; ++s) xa[tj][s] = xn[tj][s];
   }
+}
+
+template <class D, int T>
+__device__ __forceinline__ void fwd_rows_tje(int tje, int64_t row, int64_t N, bool relu, const float* __restrict__ x,
+                                             float* __restrict__ y, const float* bop, const float* cop,
+                                             float (&xa)[D::TJ][D::SA], const int (&jr)[D::TJ],
+                                             const f4 (&bb)[D::TB][D::TK], int lane, int g, int c) {
+  if constexpr (T >= 1) {
+    if (tje == T) {
+      fwd_rows<D, T>(row, N, relu, x, y, bop, cop, xa, jr, bb, lane, g, c);
+    } else {
+      fwd_rows_tje<D, T - 1>(tje, row, N, relu, x, y, bop, cop, xa, jr, bb, lane, g, c);
+    }
+  }
+}
+
+template <class D, bool MAP>
+__global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t flags,
+                                                            const float* __restrict__ x,
+                                                            const float* __restrict__ Sm,
+                                                            const float* __restrict__ A,
+                                                            const float* __restrict__ B,
+                                                            const float* __restrict__ bias,
+                                                            float* __restrict__ y) {
+  extern __shared__ float lds[];
+  float* bop = lds;              // B_i[g*SA+s][16tb+c]
+  float* cop = bop + D::BOP;     // C_i[map(16tj+4g+v)][16tk+c]
+  // the row map after the raw staging (kept in the dynamic block: a static LDS variable
+  // would shift the dynamic block off its 16-byte alignment)
+  unsigned long long* s_wmask = reinterpret_cast<unsigned long long*>(cop + D::COPF + D::RAW);  // per wavefront
+  int* s_map = reinterpret_cast<int*>(s_wmask + kWaves);                                    // position -> row
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  const int wave = threadIdx.x >> 6;
+  int64_t row = (int64_t)blockIdx.x * kWaves + wave;
+  // the first row's X (identity map) is loaded while the tables are built
+  int jr[D::TJ];
+#pragma unroll
+  for (int tj = 0; tj < D::TJ; ++tj) jr[tj] = 16 * tj + c < D::P ? 16 * tj + c : -1;
+  float xa[D::TJ][D::SA];   // X[j = map(16tj+c)][a = g*SA+s]
+  if (row < N) load_xa_map<D, D::TJ>(xa, x + row * D::IN, jr, g);
+  // the bias is loaded with the first row, before the tables are built
+  f4 bb[D::TB][D::TK];
+#pragma unroll
+  for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+    for (int tk = 0; tk < D::TK; ++tk) {
+      const int k = 16 * tk + c, b0 = 16 * tb + 4 * g;
+      bb[tb][tk] = (bias && k < D::Q && b0 < D::N) ? *reinterpret_cast<const f4*>(bias + k * D::N + b0)
+                                                  : f4{0.f, 0.f, 0.f, 0.f};
+    }
+  int tje = D::TJ;
+  bool remap = false;
+  if constexpr (D::FWD_RAW) {
+    float* rB = cop + D::COPF;
+    float* rC = rB + D::RAWB;
+    // the staged C also gives the sparsity map: the rows of C with a nonzero entry in
+    // any rank (a bit per row, ORed over each wavefront, then over the wavefronts)
+    unsigned long long bits = 0;
+    stage_raw<D>(rB, rC, B, Sm, A, FwdMap<D, MAP>::ON ? &bits : nullptr);
+    if constexpr (FwdMap<D, MAP>::ON) {
+      unsigned long long wbits = 0;   // the wavefront's OR, one ballot per row
+#pragma unroll
+      for (int j = 0; j < D::P; ++j)
+        if (__ballot((bits >> j) & 1)) wbits |= 1ull << j;
+      if (lane == 0) s_wmask[wave] = wbits;
+    }
+    __syncthreads();
+    build_table<D::R, D::TB, D::SA>(bop, [&](int i, int tb, int g, int c, int s) {
+      return rawB<D>(rB, i, g * D::SA + s, 16 * tb + c);
+    });
+    if constexpr (FwdMap<D, MAP>::ON) {
+      unsigned long long m64 = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) m64 |= s_wmask[w];
+      // the same in every lane: made scalar
+      const unsigned long long mask =
+          (unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)m64) |
+          ((unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(m64 >> 32)) << 32);
+      const int nnz = __popcll(mask);
+      tje = nnz == 0 ? 1 : (nnz + 15) / 16;
+      // nonzero rows not a prefix: compact them to the front
+      remap = mask != (nnz == 64 ? ~0ull : (1ull << nnz) - 1);
+      if (remap) {
+        if (threadIdx.x < D::P) {
+          const int jj = threadIdx.x;
+          const int before = __popcll(mask & ((1ull << jj) - 1));
+          s_map[(mask >> jj) & 1 ? before : nnz + (jj - before)] = jj;
+        }
+        __syncthreads();
+      }
+    }
+    if (FwdMap<D, MAP>::ON && remap) {
+      build_table<D::R, D::TK, D::SJ>(cop, [&](int i, int tk, int g, int c, int sv) {
+        const int jp = 16 * (sv / 4) + 4 * g + (sv % 4);
+        return jp < D::P ? rawC<D>(rC, i, s_map[jp], 16 * tk + c) : 0.f;
+      });
+#pragma unroll
+      for (int tj = 0; tj < D::TJ; ++tj) jr[tj] = 16 * tj + c < D::P ? s_map[16 * tj + c] : -1;
+      // the first row's X again, through the map
+      if (row < N) load_xa_map<D, D::TJ>(xa, x + row * D::IN, jr, g);
+    } else {
+      build_table<D::R, D::TK, D::SJ>(cop, [&](int i, int tk, int g, int c, int sv) {
+        return rawC<D>(rC, i, 16 * (sv / 4) + 4 * g + (sv % 4), 16 * tk + c);
+      });
+    }
+  } else {
+    build_table<D::R, D::TB, D::SA>(bop, [&](int i, int tb, int g, int c, int s) {
+      const int a = g * D::SA + s, b = 16 * tb + c;
+      return (a < D::M && b < D::N) ? B[(i * D::M + a) * D::N + b] : 0.f;
+    });
+    build_table<D::R, D::TK, D::SJ>(cop, [&](int i, int tk, int g, int c, int sv) {
+      const int j = 16 * (sv / 4) + 4 * g + (sv % 4), k = 16 * tk + c;
+      if (j >= D::P || k >= D::Q) return 0.f;
+      const float a = A[(i * D::P + j) * D::Q + k];
+      return Sm ? Sm[j * D::Q + k] * a : a;
+    });
+  }
+  __syncthreads();
+  fwd_rows_tje<D, D::TJ>(tje, row, N, (flags & KRON_RELU_OUT) != 0, x, y, bop, cop, xa, jr, bb, lane, g, c);
 }
 
 #endif  // forward kernels
@@ -1439,22 +1552,33 @@ int device_cus() {
 #if KRON_MFMA_PASS != 2
 // The forward is persistent: as many workgroups as fit on the device at once (and no
 // more than one row per wavefront), each wavefront striding over rows.
+template <class D, bool MAP>
+void run_fwd_map(const LayerArgs& a, int max_grid, hipStream_t s) {
+  static const int per_cu = [] {
+    (void)hipFuncSetAttribute((const void*)fwd_mfma_kernel<D, MAP>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)D::FWD_LDS);
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fwd_mfma_kernel<D, MAP>, kThreads, D::FWD_LDS) !=
+            hipSuccess || nb < 1)
+      nb = 1;
+    return nb;
+  }();
+  int64_t grid = (int64_t)per_cu * device_cus();
+  if (grid > max_grid) grid = max_grid;
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, MAP>), dim3((unsigned)grid), dim3(kThreads), D::FWD_LDS, s, a.N, a.flags,
+                     a.x, a.S, a.A, a.B, a.bias, a.y);
+}
+
 template <class D>
 void run_fwd(const LayerArgs& a, int max_grid, hipStream_t s) {
   if constexpr (D::FWD_OK) {
-    static const int per_cu = [] {
-      (void)hipFuncSetAttribute((const void*)fwd_mfma_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)D::FWD_LDS);
-      int nb = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fwd_mfma_kernel<D>, kThreads, D::FWD_LDS) !=
-              hipSuccess || nb < 1)
-        nb = 1;
-      return nb;
-    }();
-    int64_t grid = (int64_t)per_cu * device_cus();
-    if (grid > max_grid) grid = max_grid;
-    hipLaunchKernelGGL(fwd_mfma_kernel<D>, dim3((unsigned)grid), dim3(kThreads), D::FWD_LDS, s, a.N, a.flags,
-                       a.x, a.S, a.A, a.B, a.bias, a.y);
+    if constexpr (FwdMap<D, true>::ON) {
+      if (a.flags & KRON_SPARSE_ROWS) {
+        run_fwd_map<D, true>(a, max_grid, s);
+        return;
+      }
+    }
+    run_fwd_map<D, false>(a, max_grid, s);
   }
 }
 

@@ -14,9 +14,9 @@ from . import api
 
 class _KronLinearFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x, S, A, B, bias, relu: bool):
+    def forward(ctx, x, S, A, B, bias, relu: bool, sparse_rows: bool):
         x = x.contiguous()
-        y = api.kron_linear_fwd(x, S, A, B, bias, relu=relu)
+        y = api.kron_linear_fwd(x, S, A, B, bias, relu=relu, sparse_rows=sparse_rows)
         ctx.relu = relu
         ctx.save_for_backward(x, S, A, B, y if relu else None)
         ctx.has_S = S is not None
@@ -31,16 +31,17 @@ class _KronLinearFn(torch.autograd.Function):
             dy = api.kron_relu_bwd(y, dy)
         g = api.kron_linear_bwd(x, S, A, B, dy, want_dx=ctx.needs_input_grad[0],
                                 want_dbias=ctx.has_bias)
-        return g["dx"], g["dS"], g["dA"], g["dB"], g["dbias"], None
+        return g["dx"], g["dS"], g["dA"], g["dB"], g["dbias"], None, None
 
 
 class KronLinear(nn.Module):
     """y = x W + bias, W = sum_i kron(S o A_i, B_i) (Kronecker layer tutorial,
     "Build W, then multiply": S p x q initialised to ones, A_i ~ randn/sqrt(p),
-    B_i ~ randn/sqrt(m), bias zeros; p = in/m, q = out/n)."""
+    B_i ~ randn/sqrt(m), bias zeros; p = in/m, q = out/n).  sparse_rows: S is expected
+    to have whole rows zero (e.g. after l1 pruning) and the forward skips them."""
 
     def __init__(self, in_features: int, out_features: int, m: int, r: int, n: Optional[int] = None,
-                 with_S: bool = True, relu: bool = False, device=None):
+                 with_S: bool = True, relu: bool = False, device=None, sparse_rows: bool = False):
         super().__init__()
         n = m if n is None else n
         if in_features % m or out_features % n:
@@ -52,9 +53,10 @@ class KronLinear(nn.Module):
         self.B = nn.Parameter(torch.randn(r, m, n, device=dev) / math.sqrt(m))
         self.bias = nn.Parameter(torch.zeros(out_features, device=dev))
         self.relu = relu
+        self.sparse_rows = sparse_rows
 
     def forward(self, x):
-        return _KronLinearFn.apply(x, self.S, self.A, self.B, self.bias, self.relu)
+        return _KronLinearFn.apply(x, self.S, self.A, self.B, self.bias, self.relu, self.sparse_rows)
 
     def l1_penalty(self):
         """sum|S| as a 0-dim tensor with autograd (sign(S) times the upstream gradient)."""

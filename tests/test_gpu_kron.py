@@ -23,19 +23,20 @@ def K():
     return mod
 
 
-def run_layer(inp, want_dx=True, relu=False, relu_mask=False):
+def run_layer(inp, want_dx=True, relu=False, relu_mask=False, sparse_rows=False):
     """Forward and backward on the GPU; returns numpy fp64 results."""
     print(f"[kron] N={inp.shape.N} p={inp.shape.p} q={inp.shape.q} m={inp.shape.m} n={inp.shape.n} "
-          f"r={inp.shape.r} S={'yes' if inp.S is not None else 'no'} seed={inp.seed}", flush=True)
+          f"r={inp.shape.r} S={'yes' if inp.S is not None else 'no'} seed={inp.seed} sparse_rows={sparse_rows}",
+          flush=True)
     x, S, A, B, bias, dy = (dev(a) for a in (inp.x, inp.S, inp.A, inp.B, inp.bias, inp.dy))
-    y = K().kron_linear_fwd(x, S, A, B, bias, relu=relu)
+    y = K().kron_linear_fwd(x, S, A, B, bias, relu=relu, sparse_rows=sparse_rows)
     g = K().kron_linear_bwd(x, S, A, B, dy, want_dx=want_dx, want_dbias=bias is not None, relu_mask=relu_mask)
     torch.cuda.synchronize()
     return host(y), {k: host(v) for k, v in g.items()}
 
 
-def compare_layer(inp, tol=TOL_F32, want_dx=True):
-    y, g = run_layer(inp, want_dx=want_dx)
+def compare_layer(inp, tol=TOL_F32, want_dx=True, sparse_rows=False):
+    y, g = run_layer(inp, want_dx=want_dx, sparse_rows=sparse_rows)
     W = OK.weight(inp.S, inp.A, inp.B)
     yo = inp.x.astype(np.float64) @ W + (0.0 if inp.bias is None else inp.bias.astype(np.float64))
     go = OK.backward(inp.x, inp.S, inp.A, inp.B, inp.dy, want_dx=want_dx, W=W)
@@ -74,6 +75,53 @@ def test_headline_shape_ragged_rows(N):
             assert not np.any(g[k]), k          # empty batch: zero parameter gradients
         return
     compare_layer(inp)
+
+
+# Row-sparse S (whole rows of the mask zero): the forward's row map compacts the nonzero
+# rows of C = S o A_i to the front and runs only the 16-row tiles that hold them.
+@pytest.mark.parametrize("shape,frac", [((32, 32, 32, 32, 4), 0.75),     # 8 rows left: one tile
+                                        ((32, 32, 32, 32, 4), 0.5),      # 16 rows: one full tile
+                                        ((32, 32, 32, 32, 4), 15 / 32),  # 17 rows: two tiles, permuted
+                                        ((32, 32, 32, 32, 4), 1.0),      # S == 0: y = bias
+                                        ((32, 32, 32, 32, 1), 0.75),
+                                        ((32, 32, 32, 32, 2), 0.25),
+                                        ((64, 32, 48, 24, 4), 0.75),     # 16 of 64 rows: one tile
+                                        ((64, 32, 48, 24, 2), 0.6),      # 26 rows: two tiles
+                                        ((64, 32, 48, 24, 1), 0.3),      # 45 rows: three tiles
+                                        ((32, 64, 24, 48, 4), 0.75),
+                                        ((16, 16, 64, 64, 2), 0.5)])     # one tile: no map
+def test_row_sparse_S(shape, frac):
+    p, q, m, n, r = shape
+    inp = kron_inputs(44, 1031, p, q, m, n, r, s_mode="rows_zeroed", zero_frac=frac, bias_mode="normal")
+    compare_layer(inp, sparse_rows=True)
+    compare_layer(inp)                      # without the hint: the dense path, same results
+
+
+def test_row_sparse_S_full_size_and_relu():
+    """20,000 rows of the 1024 x 1024 layer with 24 of S's 32 rows zero, ReLU output."""
+    inp = kron_inputs(45, 20000, 32, 32, 32, 32, 4, s_mode="rows_zeroed", zero_frac=0.75, bias_mode="normal")
+    compare_layer(inp, sparse_rows=True)
+    x, S, A, B, bias = (dev(a) for a in (inp.x, inp.S, inp.A, inp.B, inp.bias))
+    y = K().kron_linear_fwd(x, S, A, B, bias, relu=True, sparse_rows=True)
+    W = OK.weight(inp.S, inp.A, inp.B)
+    rows = np.arange(0, 20000, 97)
+    want = np.maximum(inp.x[rows].astype(np.float64) @ W + inp.bias, 0)
+    assert rel_err(host(y)[rows], want) <= TOL_F32
+
+
+def test_zero_rows_of_A_without_S():
+    """S absent: rows of C = A_i that are zero in every rank are skipped the same way."""
+    inp = kron_inputs(46, 777, 32, 32, 32, 32, 4, s_mode="none", bias_mode="normal")
+    inp.A[:, [0, 3, 4, 9, 10, 11, 20, 21, 22, 23, 24, 25, 26, 27, 30, 31, 1, 2], :] = 0.0
+    compare_layer(inp, sparse_rows=True)
+
+
+def test_sparse_rows_hint_on_dense_S():
+    """The hint on an S with no empty row: identity map, every tile runs, same results."""
+    compare_layer(kron_inputs(47, 1031, 32, 32, 32, 32, 4, s_mode="uniform_zeroed", bias_mode="normal"),
+                  sparse_rows=True)
+    compare_layer(kron_inputs(48, 515, 64, 32, 48, 24, 4, s_mode="uniform_zeroed", bias_mode="normal"),
+                  sparse_rows=True)
 
 
 def test_mlp_hidden_layer_shape():

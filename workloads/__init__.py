@@ -101,8 +101,9 @@ def kron_inputs(seed: int, N: int, p: int, q: int, m: int, n: int, r: int, *,
 
     s_mode: "none" (S absent, S == 1), "ones" (S stored, all ones), "uniform"
     (U(0,1)), "uniform_zeroed" (U(0,1) with exactly round(zero_frac*p*q) entries set
-    to 0 at positions chosen by a seeded permutation), "integer" (small integers,
-    for exact-arithmetic tests).
+    to 0 at positions chosen by a seeded permutation), "rows_zeroed" (U(0,1) with
+    round(zero_frac*p) whole rows set to 0 at seeded positions: the structured sparsity
+    an l1-pruned mask can leave), "integer" (small integers, for exact-arithmetic tests).
     bias_mode: "none", "zeros", "normal".
     """
     nx, nS, nA, nB, nb, ndy = names
@@ -112,13 +113,16 @@ def kron_inputs(seed: int, N: int, p: int, q: int, m: int, n: int, r: int, *,
     S = None
     if s_mode == "ones":
         S = np.ones((p, q), np.float32)
-    elif s_mode in ("uniform", "uniform_zeroed"):
+    elif s_mode in ("uniform", "uniform_zeroed", "rows_zeroed"):
         g = _rng(seed, nS)
         S = f32(g.uniform(0.0, 1.0, (p, q)))
         if s_mode == "uniform_zeroed":
             nz = int(round(zero_frac * p * q))
             idx = g.permutation(p * q)[:nz]
             S.reshape(-1)[idx] = 0.0
+        elif s_mode == "rows_zeroed":
+            rows = g.permutation(p)[:int(round(zero_frac * p))]
+            S[rows, :] = 0.0
     elif s_mode != "none":
         raise ValueError(s_mode)
     bias = None
