@@ -636,6 +636,21 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
     const auto& xaj = cur.xaj;
     const auto& dyk = cur.dyk;
     const auto& dyb = cur.dyb;
+    // x under this lane's dX entries for the ReLU mask, requested now so that the row's
+    // products cover the load (read at the end, it leaves the load's latency exposed per
+    // row), where the registers allow
+    constexpr bool EARLY_MASK = D::BWD_REGS + 4 * D::TA * D::TJ <= 300;
+    f4 xm[D::TA][D::TJ];
+    if (EARLY_MASK && want_dx && mask) {
+#pragma unroll
+      for (int ta = 0; ta < D::TA; ++ta)
+#pragma unroll
+        for (int tj = 0; tj < D::TJ; ++tj) {
+          const int j = 16 * tj + c, a0 = 16 * ta + 4 * g;
+          xm[ta][tj] = (j < D::P && a0 < D::M) ? *reinterpret_cast<const f4*>(xr + j * D::M + a0)
+                                               : f4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
 #pragma unroll
     for (int tk = 0; tk < D::TK; ++tk)
 #pragma unroll
@@ -745,7 +760,7 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
           if (j < D::P && a0 < D::M) {
             f4 o = dxt[ta][tj];
             if (mask) {
-              const f4 xv = *reinterpret_cast<const f4*>(xr + j * D::M + a0);
+              const f4 xv = EARLY_MASK ? xm[ta][tj] : *reinterpret_cast<const f4*>(xr + j * D::M + a0);
 #pragma unroll
               for (int v = 0; v < 4; ++v) o[v] = xv[v] > 0.f ? o[v] : 0.f;
             }
