@@ -149,7 +149,8 @@ class Layer:
         self.K.kron_linear_fwd(self.x, self.S, self.A, self.B, self.bias, out=self.y, sparse_rows=self.sparse_rows)
 
     def bwd(self):
-        self.K.kron_linear_bwd(self.x, self.S, self.A, self.B, self.dy, workspace=self.ws, outs=self.outs)
+        self.K.kron_linear_bwd(self.x, self.S, self.A, self.B, self.dy, workspace=self.ws, outs=self.outs,
+                               sparse_rows=self.sparse_rows)
 
 
 class LayerBf16:

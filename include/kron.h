@@ -58,12 +58,13 @@ typedef enum { KRON_F32 = 0, KRON_BF16 = 1 } kron_dtype_t;
 /* kron_shape_t.flags */
 #define KRON_RELU_OUT     1u  /* fwd: y = max(x W + bias, 0)                              */
 #define KRON_DX_RELU_MASK 2u  /* bwd: dX = (dY W^T) o [x > 0]  (x is the output of a ReLU) */
-/* fwd hint, for S with whole rows zero (e.g. after l1 pruning): the 32- and 64-row block
- * layouts build the sparsity map of C = S o A_i (its rows with a nonzero entry in any
- * rank, compacted to the front) and run only the 16-row tiles that hold such rows
- * (tutorial, intro: zeros of S give zero blocks of W).  Results equal the dense path's up
- * to the order of the sums.  Costs about 2% on a dense S; other paths ignore it, and the
- * backward accepts and ignores it. */
+/* hint, for S with whole rows zero (e.g. after l1 pruning): the forward's 32- and 64-row
+ * block layouts and the 32x32-block, r = 4 backward build the sparsity map of C = S o A_i
+ * (its rows with a nonzero entry in any rank, compacted to the front) and run only the
+ * 16-row tiles that hold such rows (tutorial, intro: zeros of S give zero blocks of W): in
+ * the forward both products, in the backward G = C dY, dX and dB (Z and dC stay dense:
+ * dS needs dC everywhere).  Results equal the dense path's up to the order of the sums.
+ * Costs a little on an S with no empty tile; other kernels ignore it. */
 #define KRON_SPARSE_ROWS  4u
 
 typedef struct {

@@ -118,11 +118,13 @@ def kron_linear_fwd(x: torch.Tensor, S: Optional[torch.Tensor], A: torch.Tensor,
 def kron_linear_bwd(x: torch.Tensor, S: Optional[torch.Tensor], A: torch.Tensor, B: torch.Tensor,
                     dy: torch.Tensor, want_dx: bool = True, want_dbias: bool = True,
                     relu_mask: bool = False, workspace: Optional[torch.Tensor] = None,
-                    outs: Optional[dict] = None) -> dict:
-    """Gradients of sum(dy * (x W + bias)): dict(dx, dS, dA, dB, dbias) (None where not asked)."""
+                    outs: Optional[dict] = None, sparse_rows: bool = False) -> dict:
+    """Gradients of sum(dy * (x W + bias)): dict(dx, dS, dA, dB, dbias) (None where not asked).
+    sparse_rows: the KRON_SPARSE_ROWS hint (S expected to have whole rows zero)."""
     for t, nm in ((x, "x"), (S, "S"), (A, "A"), (B, "B"), (dy, "dy")):
         _dev(t, nm)
-    shape = layer_shape(x.shape[0], S, A, B, KRON_DX_RELU_MASK if relu_mask else 0)
+    shape = layer_shape(x.shape[0], S, A, B,
+                        (KRON_DX_RELU_MASK if relu_mask else 0) | (KRON_SPARSE_ROWS if sparse_rows else 0))
     _layer_io_checks(x, shape, S, A, B, dy)
     dev = x.device
     o = dict(outs or {})

@@ -1238,7 +1238,10 @@ struct Solo {
   static constexpr int MAIN = 3 * TAB + kWaves * WSP;
   static constexpr int RW = 2 * R * 1024 + 1024;   // per wavefront at the end: dB | dC | dbias
   static constexpr int COMBINE = kWaves * RW;
-  static constexpr size_t LDS = (size_t)(MAIN > COMBINE ? MAIN : COMBINE) * 4;
+  // the row map (KRON_SPARSE_ROWS): a word of row bits per wavefront, position -> row and
+  // row -> position, after the tables and tiles
+  static constexpr int MAPW = kWaves + 64;
+  static constexpr size_t LDS = (size_t)(MAIN + MAPW > COMBINE ? MAIN + MAPW : COMBINE) * 4;
   static_assert(!OK || 2 * R * 1024 <= kWaves * WSP, "raw factors are staged in the tile area");
 };
 
@@ -1246,7 +1249,12 @@ __device__ __forceinline__ int kxs(int s, int g) { return 16 * (s >> 2) + 4 * g 
 
 // DXM as for bwd_rp_kernel: 0 = no dX, 1 = dX, 2 = dX masked by [x > 0], 3 = dX added to
 // dx, 4 = dX added to dx and the sum masked.
-template <class D, int DXM>
+// MAP (KRON_SPARSE_ROWS): the rows j of C with a nonzero entry in any rank are compacted to
+// the front of the tiles (the X tile is staged in that order and the C table built in it),
+// and when they fit one 16-row tile the products that run over them -- G = C dY, dX and
+// dB -- take that tile only: G, dX and the dB terms of the other rows are zero.  Z and dC
+// stay dense (dS needs dC at every entry); dX and dC are written back in row order.
+template <class D, int DXM, bool MAP = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_solo_kernel(int64_t N, const float* __restrict__ x, const float* __restrict__ Sm,
                      const float* __restrict__ A, const float* __restrict__ B, const float* __restrict__ dy,
@@ -1262,18 +1270,22 @@ void bwd_solo_kernel(int64_t N, const float* __restrict__ x, const float* __rest
   float* xt = wsp + w * SL::WSP;
   float* yt = xt + TILE;
   float* gs = yt + TILE;
+  int* s_wrows = reinterpret_cast<int*>(lds + SL::MAIN);   // [wavefront] row bits
+  int* s_map = s_wrows + kWaves;                            // position -> row
+  int* s_inv = s_map + 32;                                  // row -> position
   const int64_t stride = (int64_t)gridDim.x * kWaves;
   int64_t row = (int64_t)blockIdx.x * kWaves + w;
 
   // this lane's pieces of a row (float4 index 64t + lane), placed so that each 16-lane
   // group writes rows j and j + 8 of a tile (no bank conflicts)
-  int soff[4], goff[4];
+  int soff[4], goff[4], soffx[4];   // (soffx: the X tile's, which follows the row map)
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int f = 64 * t + lane, q = f & 15, g16 = f >> 4;
     const int pj = (g16 & 7) + 16 * (g16 >> 3) + 8 * (q >> 3), pa = 4 * (q & 7);
     soff[t] = pj * L + pa;
     goff[t] = pj * 32 + pa;
+    soffx[t] = soff[t];
   }
   f4 sx[4], sy[4];
   auto fetch = [&](int64_t r) {
@@ -1286,10 +1298,15 @@ void bwd_solo_kernel(int64_t N, const float* __restrict__ x, const float* __rest
   auto stage = [&]() {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      *reinterpret_cast<f4*>(xt + soff[t]) = sx[t];
+      *reinterpret_cast<f4*>(xt + (MAP ? soffx[t] : soff[t])) = sx[t];
       *reinterpret_cast<f4*>(yt + soff[t]) = sy[t];
     }
   };
+  // the row map: tiles of rows run by G, dX and dB, whether rows moved, and where this
+  // lane's dX rows go
+  int tje = 2;
+  bool remap = false;
+  int dxrow[2] = {c, 16 + c};
   if (row < N) fetch(row);
   {
     // tables: B and C = S o A staged raw in the tile area, then laid out per lane
@@ -1302,19 +1319,57 @@ void bwd_solo_kernel(int64_t N, const float* __restrict__ x, const float* __rest
       a[k] = reinterpret_cast<const f4*>(A)[tid + kThreads * k];
       m[k] = Sm ? reinterpret_cast<const f4*>(Sm)[tid] : f4{1.f, 1.f, 1.f, 1.f};
     }
+    bool nz = false;   // this thread's C values all lie in row tid / 8 (every rank)
 #pragma unroll
     for (int k = 0; k < R; ++k) {
+      const f4 cv = a[k] * m[k];
       reinterpret_cast<f4*>(rB)[tid + kThreads * k] = b[k];
-      reinterpret_cast<f4*>(rC)[tid + kThreads * k] = a[k] * m[k];
+      reinterpret_cast<f4*>(rC)[tid + kThreads * k] = cv;
+      nz |= cv[0] != 0.f || cv[1] != 0.f || cv[2] != 0.f || cv[3] != 0.f;
+    }
+    if constexpr (MAP) {
+      // rows 8w .. 8w+7: one bit each, from the ballot of the wavefront's 8-lane groups
+      const unsigned long long bal = __ballot(nz);
+      int bits = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) bits |= ((bal >> (8 * q)) & 0xffull) ? 1 << q : 0;
+      if (lane == 0) s_wrows[w] = bits;
     }
     __syncthreads();
+    if constexpr (MAP) {
+      int m32 = 0;
+#pragma unroll
+      for (int q = 0; q < kWaves; ++q) m32 |= s_wrows[q] << (8 * q);
+      const uint32_t mask = (uint32_t)__builtin_amdgcn_readfirstlane(m32);
+      const int nnz = __popc(mask);
+      tje = nnz <= 16 ? 1 : 2;
+      remap = mask != (nnz == 32 ? 0xffffffffu : (1u << nnz) - 1);
+      if (remap) {   // nonzero rows not a prefix: compact them to the front (uniform branch)
+        if (tid < 32) {
+          const int before = __popc(mask & ((1u << tid) - 1));
+          const int pos = (mask >> tid) & 1 ? before : nnz + (tid - before);
+          s_map[pos] = tid;
+          s_inv[tid] = pos;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int f = 64 * t + lane, q = f & 15, g16 = f >> 4;
+          const int pj = (g16 & 7) + 16 * (g16 >> 3) + 8 * (q >> 3), pa = 4 * (q & 7);
+          soffx[t] = s_inv[pj] * L + pa;
+        }
+#pragma unroll
+        for (int tj = 0; tj < 2; ++tj) dxrow[tj] = s_map[16 * tj + c];
+      }
+    }
 #pragma unroll
     for (int it = 0; it < 4 * R; ++it) {
       const int e = tid + kThreads * it;
       const int v = e & 3, l = (e >> 2) & 63, ch = (e >> 8) & 1, tl = (e >> 9) & 1, i = e >> 10;
       const int gg = l >> 4, cc = l & 15, s = 4 * ch + v;
       tabB[e] = rB[(i * 32 + 8 * gg + s) * 32 + 16 * tl + cc];
-      tabC[e] = rC[(i * 32 + 16 * tl + cc) * 32 + kxs(s, gg)];
+      const int jc = (MAP && remap) ? s_map[16 * tl + cc] : 16 * tl + cc;
+      tabC[e] = rC[(i * 32 + jc) * 32 + kxs(s, gg)];
       tabX[e] = rB[(i * 32 + 16 * tl + cc) * 32 + 16 * (s >> 2) + 4 * gg + (s & 3)];
     }
     __syncthreads();
@@ -1369,130 +1424,149 @@ void bwd_solo_kernel(int64_t N, const float* __restrict__ x, const float* __rest
   rd_tab(bo, tabB, 0);
   rd_tab(co, tabC, 0);
   if constexpr (DXM != 0) rd_tab(bx, tabX, 0);
-  for (; row < N; row += stride) {
-    fetch(row + stride < N ? row + stride : row);
-    f4 xm[2][2], dold[2][2];   // x under this lane's dX entries (mask), dx already there
-    if constexpr (DXM == 2 || DXM == 4) {
-#pragma unroll
-      for (int ta = 0; ta < 2; ++ta)
-#pragma unroll
-        for (int tj = 0; tj < 2; ++tj) xm[ta][tj] = *reinterpret_cast<const f4*>(xt + (16 * tj + c) * L + 16 * ta + 4 * g);
-    }
-    if constexpr (DXM >= 3) {
-#pragma unroll
-      for (int ta = 0; ta < 2; ++ta)
-#pragma unroll
-        for (int tj = 0; tj < 2; ++tj)
-          dold[ta][tj] = *reinterpret_cast<const f4*>(dx + row * D::IN + (16 * tj + c) * 32 + 16 * ta + 4 * g);
-    }
-#pragma unroll
-    for (int tk = 0; tk < 2; ++tk)
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) db[tk][tb] += dyk[tk][tb];
-    f4 dxt[2][2];   // dX^T[16ta+4g+v][16tj+c]
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int v = 0; v < 2; ++v) dxt[u][v] = f4{0.f, 0.f, 0.f, 0.f};
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      f4 zt[2][2];   // Z^T[16tb+4g+v][16tj+c]
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int tj = 0; tj < 2; ++tj) {
-          f4 t = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < 8; ++s) t = mfma(bo[tb][s], xa[tj][s], t);
-          zt[tb][tj] = t;
-        }
-      f4 gt[2][2];   // G^T[16tb+4g+v][16tj+c]
-#pragma unroll
-      for (int tj = 0; tj < 2; ++tj)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          f4 t = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < 8; ++s) t = mfma(dyb[tb][s], co[tj][s], t);
-          gt[tb][tj] = t;
-        }
-      // the next rank's tables (the last rank reads rank 0 for the next row)
-      float bo2[2][8], co2[2][8];
-      rd_tab(bo2, tabB, (i + 1) % R);
-      rd_tab(co2, tabC, (i + 1) % R);
-      __builtin_amdgcn_sched_barrier(0);
-      // dC_i[16tj+4g+v][16tk+c] += sum_b Z[j][b] dY[k][b]
-#pragma unroll
-      for (int tj = 0; tj < 2; ++tj)
-#pragma unroll
-        for (int tk = 0; tk < 2; ++tk)
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) dC[i][tj][tk] = mfma(zt[tb][tj][v], dyk[tk][tb][v], dC[i][tj][tk]);
-      // G as gs[j][b], read back in column order for dB
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int tj = 0; tj < 2; ++tj) *reinterpret_cast<f4*>(gs + (16 * tj + c) * L + 16 * tb + 4 * g) = gt[tb][tj];
-      float gcol[2][8];   // G[kxs][16tb+c]
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int s = 0; s < 8; ++s) gcol[tb][s] = gs[kxs(s, g) * L + 16 * tb + c];
-      __builtin_amdgcn_sched_barrier(0);
-      float bx2[2][8];
-      if constexpr (DXM != 0) {
-        // dX^T[a][j] += sum_b B_i[a][b] G^T[b][j]
-#pragma unroll
+  // The row loop, instantiated per count of 16-row tiles that G, dX and dB run over (two
+  // without the row map).
+  auto rows = [&](auto tiles) {
+    constexpr int TJE_ = decltype(tiles)::value;
+    for (; row < N; row += stride) {
+      fetch(row + stride < N ? row + stride : row);
+      f4 xm[2][2], dold[2][2];   // x under this lane's dX entries (mask), dx already there
+      if constexpr (DXM == 2 || DXM == 4) {
+  #pragma unroll
         for (int ta = 0; ta < 2; ++ta)
-#pragma unroll
-          for (int tj = 0; tj < 2; ++tj)
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-              for (int v = 0; v < 4; ++v) dxt[ta][tj] = mfma(bx[ta][tb * 4 + v], gt[tb][tj][v], dxt[ta][tj]);
-        rd_tab(bx2, tabX, (i + 1) % R);
+  #pragma unroll
+          for (int tj = 0; tj < 2; ++tj) xm[ta][tj] = *reinterpret_cast<const f4*>(xt + (16 * tj + c) * L + 16 * ta + 4 * g);
       }
-      if (i == 0) stage();   // the next row into the tiles: this row's reads of them are done
-      __builtin_amdgcn_sched_barrier(0);
-      // dB_i[16ta+4g+v][16tb+c] += sum_j X[j][a] G[j][b]
-#pragma unroll
-      for (int ta = 0; ta < 2; ++ta)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int s = 0; s < 8; ++s) dB[i][ta][tb] = mfma(xaj[ta][s], gcol[tb][s], dB[i][ta][tb]);
-      if (i == R - 1) rd_ops();   // the next row's operands from the tiles
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
+      if constexpr (DXM >= 3) {
+  #pragma unroll
+        for (int ta = 0; ta < 2; ++ta)
+  #pragma unroll
+          for (int tj = 0; tj < 2; ++tj)
+            dold[ta][tj] = *reinterpret_cast<const f4*>(dx + row * D::IN + dxrow[tj] * 32 + 16 * ta + 4 * g);
+      }
+  #pragma unroll
+      for (int tk = 0; tk < 2; ++tk)
+  #pragma unroll
+        for (int tb = 0; tb < 2; ++tb) db[tk][tb] += dyk[tk][tb];
+      f4 dxt[2][2];   // dX^T[16ta+4g+v][16tj+c]
+  #pragma unroll
       for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          bo[u][v] = bo2[u][v];
-          co[u][v] = co2[u][v];
-          if constexpr (DXM != 0) bx[u][v] = bx2[u][v];
-        }
-    }
-    if constexpr (DXM != 0) {
-      float* dxr = dx + row * D::IN;
-#pragma unroll
-      for (int ta = 0; ta < 2; ++ta)
-#pragma unroll
-        for (int tj = 0; tj < 2; ++tj) {
-          f4 o = dxt[ta][tj];
-          if constexpr (DXM >= 3) o += dold[ta][tj];
-          if constexpr (DXM == 2 || DXM == 4) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) o[v] = xm[ta][tj][v] > 0.f ? o[v] : 0.f;
+  #pragma unroll
+        for (int v = 0; v < 2; ++v) dxt[u][v] = f4{0.f, 0.f, 0.f, 0.f};
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int i = 0; i < R; ++i) {
+        f4 zt[2][2];   // Z^T[16tb+4g+v][16tj+c]
+  #pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+  #pragma unroll
+          for (int tj = 0; tj < 2; ++tj) {
+            f4 t = f4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+            for (int s = 0; s < 8; ++s) t = mfma(bo[tb][s], xa[tj][s], t);
+            zt[tb][tj] = t;
           }
-          *reinterpret_cast<f4*>(dxr + (16 * tj + c) * 32 + 16 * ta + 4 * g) = o;
+        f4 gt[2][2];   // G^T[16tb+4g+v][16tj+c]
+  #pragma unroll
+        for (int tj = 0; tj < 2; ++tj)
+  #pragma unroll
+          for (int tb = 0; tb < 2; ++tb) {
+            f4 t = f4{0.f, 0.f, 0.f, 0.f};
+            if (TJE_ == 2 || tj < TJE_) {
+  #pragma unroll
+              for (int s = 0; s < 8; ++s) t = mfma(dyb[tb][s], co[tj][s], t);
+            }
+            gt[tb][tj] = t;
+          }
+        // the next rank's tables (the last rank reads rank 0 for the next row)
+        float bo2[2][8], co2[2][8];
+        rd_tab(bo2, tabB, (i + 1) % R);
+        rd_tab(co2, tabC, (i + 1) % R);
+        __builtin_amdgcn_sched_barrier(0);
+        // dC_i[16tj+4g+v][16tk+c] += sum_b Z[j][b] dY[k][b]
+  #pragma unroll
+        for (int tj = 0; tj < 2; ++tj)
+  #pragma unroll
+          for (int tk = 0; tk < 2; ++tk)
+  #pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+  #pragma unroll
+              for (int v = 0; v < 4; ++v) dC[i][tj][tk] = mfma(zt[tb][tj][v], dyk[tk][tb][v], dC[i][tj][tk]);
+        // G as gs[j][b], read back in column order for dB
+  #pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+  #pragma unroll
+          for (int tj = 0; tj < 2; ++tj)
+            if (TJE_ == 2 || tj < TJE_) *reinterpret_cast<f4*>(gs + (16 * tj + c) * L + 16 * tb + 4 * g) = gt[tb][tj];
+        float gcol[2][8];   // G[kxs][16tb+c]
+  #pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+  #pragma unroll
+          for (int s = 0; s < 8; ++s) gcol[tb][s] = (TJE_ == 2 || s < 4 * TJE_) ? gs[kxs(s, g) * L + 16 * tb + c] : 0.f;
+        __builtin_amdgcn_sched_barrier(0);
+        float bx2[2][8];
+        if constexpr (DXM != 0) {
+          // dX^T[a][j] += sum_b B_i[a][b] G^T[b][j]
+  #pragma unroll
+          for (int ta = 0; ta < 2; ++ta)
+  #pragma unroll
+            for (int tj = 0; tj < 2; ++tj)
+              if (TJE_ == 2 || tj < TJE_) {
+  #pragma unroll
+                for (int tb = 0; tb < 2; ++tb)
+  #pragma unroll
+                  for (int v = 0; v < 4; ++v) dxt[ta][tj] = mfma(bx[ta][tb * 4 + v], gt[tb][tj][v], dxt[ta][tj]);
+              }
+          rd_tab(bx2, tabX, (i + 1) % R);
         }
+        if (i == 0) stage();   // the next row into the tiles: this row's reads of them are done
+        __builtin_amdgcn_sched_barrier(0);
+        // dB_i[16ta+4g+v][16tb+c] += sum_j X[j][a] G[j][b]
+  #pragma unroll
+        for (int ta = 0; ta < 2; ++ta)
+  #pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+  #pragma unroll
+            for (int s = 0; s < 8; ++s)
+              if (TJE_ == 2 || s < 4 * TJE_) dB[i][ta][tb] = mfma(xaj[ta][s], gcol[tb][s], dB[i][ta][tb]);
+        if (i == R - 1) rd_ops();   // the next row's operands from the tiles
+        __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+        for (int u = 0; u < 2; ++u)
+  #pragma unroll
+          for (int v = 0; v < 8; ++v) {
+            bo[u][v] = bo2[u][v];
+            co[u][v] = co2[u][v];
+            if constexpr (DXM != 0) bx[u][v] = bx2[u][v];
+          }
+      }
+      if constexpr (DXM != 0) {
+        float* dxr = dx + row * D::IN;
+  #pragma unroll
+        for (int ta = 0; ta < 2; ++ta)
+  #pragma unroll
+          for (int tj = 0; tj < 2; ++tj) {
+            f4 o = dxt[ta][tj];
+            if constexpr (DXM >= 3) o += dold[ta][tj];
+            if constexpr (DXM == 2 || DXM == 4) {
+  #pragma unroll
+              for (int v = 0; v < 4; ++v) o[v] = xm[ta][tj][v] > 0.f ? o[v] : 0.f;
+            }
+            *reinterpret_cast<f4*>(dxr + dxrow[tj] * 32 + 16 * ta + 4 * g) = o;
+          }
+      }
     }
-  }
+  };
+  if (MAP && tje == 1) rows(std::integral_constant<int, 1>{});
+  else rows(std::integral_constant<int, 2>{});
   // Partial row of this workgroup: [dB (R*M*N) | dA (R*P*Q) | dS (P*Q) | dbias (Q*N)],
-  // the four wavefronts added in wavefront order.
+  // the four wavefronts added in wavefront order.  dC's rows go back to row order (the
+  // map is read before the combine area overwrites it).
+  int dcrow[2][4];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) dcrow[u][v] = (MAP && remap) ? s_map[16 * u + 4 * g + v] : 16 * u + 4 * g + v;
   __syncthreads();
   float* red = lds + w * SL::RW;   // [dB | dC | dbias] of this wavefront
 #pragma unroll
@@ -1504,7 +1578,7 @@ void bwd_solo_kernel(int64_t N, const float* __restrict__ x, const float* __rest
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           red[i * 1024 + (16 * u + 4 * g + v) * 32 + 16 * t + c] = dB[i][u][t][v];
-          red[R * 1024 + i * 1024 + (16 * u + 4 * g + v) * 32 + 16 * t + c] = dC[i][u][t][v];
+          red[R * 1024 + i * 1024 + dcrow[u][v] * 32 + 16 * t + c] = dC[i][u][t][v];
         }
 #pragma unroll
   for (int tk = 0; tk < 2; ++tk)
@@ -1625,17 +1699,36 @@ void run_bwd(const LayerArgs& a, int grid, hipStream_t s) {
       return true;
     }();
     (void)attr;
+    static const bool attr_map = [] {
+      (void)hipFuncSetAttribute((const void*)bwd_solo_kernel<D, 0, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)Solo<D>::LDS);
+      (void)hipFuncSetAttribute((const void*)bwd_solo_kernel<D, 1, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)Solo<D>::LDS);
+      (void)hipFuncSetAttribute((const void*)bwd_solo_kernel<D, 2, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)Solo<D>::LDS);
+      return true;
+    }();
+    (void)attr_map;
     const bool mask = a.flags & KRON_DX_RELU_MASK;
     const int dxm = a.dx == nullptr ? 0 : (a.dx_accumulate ? (mask ? 4 : 3) : (mask ? 2 : 1));
-#define KRON_SOLO_LAUNCH(M)                                                                                 \
-  hipLaunchKernelGGL((bwd_solo_kernel<D, M>), dim3(grid), dim3(kThreads), Solo<D>::LDS, s, a.N, a.x, a.S, a.A, \
+    const bool map = (a.flags & KRON_SPARSE_ROWS) && dxm <= 2;
+#define KRON_SOLO_LAUNCH(M, MP)                                                                                 \
+  hipLaunchKernelGGL((bwd_solo_kernel<D, M, MP>), dim3(grid), dim3(kThreads), Solo<D>::LDS, s, a.N, a.x, a.S, a.A, \
                      a.B, a.dy, a.dx, a.part)
-    switch (dxm) {
-      case 0: KRON_SOLO_LAUNCH(0); break;
-      case 1: KRON_SOLO_LAUNCH(1); break;
-      case 2: KRON_SOLO_LAUNCH(2); break;
-      case 3: KRON_SOLO_LAUNCH(3); break;
-      default: KRON_SOLO_LAUNCH(4); break;
+    if (map) {
+      switch (dxm) {
+        case 0: KRON_SOLO_LAUNCH(0, true); break;
+        case 1: KRON_SOLO_LAUNCH(1, true); break;
+        default: KRON_SOLO_LAUNCH(2, true); break;
+      }
+    } else {
+      switch (dxm) {
+        case 0: KRON_SOLO_LAUNCH(0, false); break;
+        case 1: KRON_SOLO_LAUNCH(1, false); break;
+        case 2: KRON_SOLO_LAUNCH(2, false); break;
+        case 3: KRON_SOLO_LAUNCH(3, false); break;
+        default: KRON_SOLO_LAUNCH(4, false); break;
+      }
     }
 #undef KRON_SOLO_LAUNCH
   } else if constexpr (kind == 1) {

@@ -18,6 +18,7 @@ class _KronLinearFn(torch.autograd.Function):
         x = x.contiguous()
         y = api.kron_linear_fwd(x, S, A, B, bias, relu=relu, sparse_rows=sparse_rows)
         ctx.relu = relu
+        ctx.sparse_rows = sparse_rows
         ctx.save_for_backward(x, S, A, B, y if relu else None)
         ctx.has_S = S is not None
         ctx.has_bias = bias is not None
@@ -30,7 +31,7 @@ class _KronLinearFn(torch.autograd.Function):
         if ctx.relu:
             dy = api.kron_relu_bwd(y, dy)
         g = api.kron_linear_bwd(x, S, A, B, dy, want_dx=ctx.needs_input_grad[0],
-                                want_dbias=ctx.has_bias)
+                                want_dbias=ctx.has_bias, sparse_rows=ctx.sparse_rows)
         return g["dx"], g["dS"], g["dA"], g["dB"], g["dbias"], None, None
 
 

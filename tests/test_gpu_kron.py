@@ -30,7 +30,8 @@ def run_layer(inp, want_dx=True, relu=False, relu_mask=False, sparse_rows=False)
           flush=True)
     x, S, A, B, bias, dy = (dev(a) for a in (inp.x, inp.S, inp.A, inp.B, inp.bias, inp.dy))
     y = K().kron_linear_fwd(x, S, A, B, bias, relu=relu, sparse_rows=sparse_rows)
-    g = K().kron_linear_bwd(x, S, A, B, dy, want_dx=want_dx, want_dbias=bias is not None, relu_mask=relu_mask)
+    g = K().kron_linear_bwd(x, S, A, B, dy, want_dx=want_dx, want_dbias=bias is not None, relu_mask=relu_mask,
+                            sparse_rows=sparse_rows)
     torch.cuda.synchronize()
     return host(y), {k: host(v) for k, v in g.items()}
 
@@ -114,6 +115,27 @@ def test_zero_rows_of_A_without_S():
     inp = kron_inputs(46, 777, 32, 32, 32, 32, 4, s_mode="none", bias_mode="normal")
     inp.A[:, [0, 3, 4, 9, 10, 11, 20, 21, 22, 23, 24, 25, 26, 27, 30, 31, 1, 2], :] = 0.0
     compare_layer(inp, sparse_rows=True)
+
+
+@pytest.mark.parametrize("frac,relu_mask,want_dx", [(0.75, False, True), (0.75, True, True), (0.5, False, False),
+                                                     (15 / 32, True, True), (1.0, False, True), (0.25, False, True)])
+def test_row_sparse_S_backward_variants(frac, relu_mask, want_dx):
+    """The whole-row backward with the row map: no dX, dX, dX o [x > 0]; 8, 16, 17, 0 and 24
+    nonzero rows (one tile, one tile, two permuted tiles, S == 0, two tiles)."""
+    inp = kron_inputs(49, 2000, 32, 32, 32, 32, 4, s_mode="rows_zeroed", zero_frac=frac, bias_mode="normal")
+    if relu_mask:
+        inp.x = np.maximum(inp.x, 0).astype(np.float32)
+    y, g = run_layer(inp, want_dx=want_dx, relu_mask=relu_mask, sparse_rows=True)
+    W = OK.weight(inp.S, inp.A, inp.B)
+    assert rel_err(y, inp.x.astype(np.float64) @ W + inp.bias) <= TOL_F32
+    go = OK.backward(inp.x, inp.S, inp.A, inp.B, inp.dy, want_dx=want_dx, W=W)
+    if want_dx:
+        want = go["dx"] * (inp.x > 0) if relu_mask else go["dx"]
+        assert rel_err(g["dx"], want) <= TOL_F32
+    else:
+        assert g["dx"] is None
+    for k in ("dS", "dA", "dB", "dbias"):
+        assert rel_err(g[k], go[k]) <= TOL_F32, k
 
 
 def test_sparse_rows_hint_on_dense_S():
