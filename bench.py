@@ -1,7 +1,7 @@
 """Benchmark of the Kronecker-factored layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--cpu-seconds 10]
-    python bench.py --workload {headline,headline_bf16,tiny,mlp_step,gpt2_ffn,ks,ks_bwd,chain,van_loan,sweep,small_blocks}
+    python bench.py --workload {headline,headline_bf16,tiny,mlp_step,gpt2_ffn,gpt2_ffn_bf16,ks,ks_bwd,chain,van_loan,sweep,small_blocks}
     python bench.py --calibrate-copy      (plain device copy of known size, for HBM counters)
 
 Default workload (one JSON line): one step is one kron_linear_fwd + one kron_linear_bwd
@@ -338,25 +338,24 @@ def layer_record(name, inp, L, args, extra=None):
     print(json.dumps(rec), flush=True)
 
 
-def run_headline_bf16(args, dev):
-    """The same layer and rows in bf16 (inputs, y, dx), fp32 accumulation and fp32 factor
-    gradients.  Algorithmic bytes halve with the element size while the flops stay, so at
-    this shape the pass is bound by HBM, not by the bf16 matrix rate."""
-    from workloads import headline_layer
-    inp = headline_layer()
+def bf16_layer_record(name, inp, L, args):
+    """One bf16 layer's fwd+bwd line.  Algorithmic bytes halve with the element size while
+    the flops stay, so these layers are bound by HBM or by the bf16 matrix rate, whichever
+    is slower."""
     sh = inp.shape
     N, p, q, m, n, r = sh.N, sh.p, sh.q, sh.m, sh.n, sh.r
-    nnz = int(np.count_nonzero(inp.S))
-    L = LayerBf16(inp, dev)
+    nnz = p * q if inp.S is None else int(np.count_nonzero(inp.S))
     ms, _ = timed(lambda: (L.fwd(), L.bwd()), args.steps, args.warmup)
     t_fwd, t_bwd = split_times(L, args.steps)
     ff, fb, _, _ = work_per_row(p, q, m, n, r, nnz)
+    if inp.S is None:   # dense factors: the cheaper association of each product counts
+        ff = 2 * r * min(p * n * (m + q), q * m * (p + n))
+        fb = 2 * ff
     bf, bb = 2 * (p * m + q * n), 2 * (2 * p * m + q * n)
     t_flop = N * (ff + fb) / (PEAK_BF16_TFLOPS * 1e12)
     t_hbm = N * (bf + bb) / (PEAK_HBM_GBS * 1e9)
     t_roof = max(t_flop, t_hbm)
-    print(json.dumps({"workload": "headline_bf16: kron_linear fwd+bwd, 1024x1024, m=n=32, r=4, half of S "
-                                  "zeroed, 20000 rows, bf16 x/S/A/B/bias/dy/y/dx, fp32 dS/dA/dB/dbias",
+    print(json.dumps({"workload": name,
                       "rows_per_s": round(N / (ms * 1e-3), 1), "us_per_fwd_bwd": round(ms * 1e3, 2),
                       "t_fwd_us": round(t_fwd * 1e6, 2), "t_bwd_us": round(t_bwd * 1e6, 2),
                       "achieved_gbs": round(N * (bf + bb) / (ms * 1e-3) / 1e9, 1),
@@ -365,6 +364,25 @@ def run_headline_bf16(args, dev):
                       "bound": "hbm" if t_hbm >= t_flop else "bf16",
                       "t_bf16_flops_us": round(t_flop * 1e6, 2), "t_hbm_us": round(t_hbm * 1e6, 2),
                       "shape": {"N": N, "p": p, "q": q, "m": m, "n": n, "r": r}}), flush=True)
+
+
+def run_headline_bf16(args, dev):
+    """The same layer and rows in bf16 (inputs, y, dx), fp32 accumulation and fp32 factor
+    gradients."""
+    from workloads import headline_layer
+    inp = headline_layer()
+    bf16_layer_record("headline_bf16: kron_linear fwd+bwd, 1024x1024, m=n=32, r=4, half of S zeroed, 20000 rows, "
+                      "bf16 x/S/A/B/bias/dy/y/dx, fp32 dS/dA/dB/dbias", inp, LayerBf16(inp, dev), args)
+
+
+def run_gpt2_bf16(args, dev):
+    """The GPT-2 small FFN pair in bf16 (the side of 24 padded to 32 inside the tiles)."""
+    from workloads import gpt2_ffn_layers
+    for r in (1, 2, 4, 8):
+        up, down = gpt2_ffn_layers(r)
+        bf16_layer_record(f"gpt2 ffn bf16 768->3072 (A 32x64, B 24x48), r={r}, 8192 rows", up, LayerBf16(up, dev), args)
+        bf16_layer_record(f"gpt2 ffn bf16 3072->768 (A 64x32, B 48x24), r={r}, 8192 rows", down,
+                          LayerBf16(down, dev), args)
 
 
 def run_tiny(args, dev):
@@ -654,7 +672,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the copy and GEMM ceiling measurements")
     ap.add_argument("--workload", default="headline",
-                    choices=("headline", "headline_bf16", "tiny", "mlp_step", "gpt2_ffn", "ks", "ks_bwd", "chain", "van_loan", "sweep", "small_blocks", "sparse_s"))
+                    choices=("headline", "headline_bf16", "tiny", "mlp_step", "gpt2_ffn", "gpt2_ffn_bf16", "ks", "ks_bwd", "chain", "van_loan", "sweep", "small_blocks", "sparse_s"))
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed running before the warmup steps, for the GPU clock to ramp up")
@@ -671,7 +689,7 @@ def main():
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         return run_copy(args, dev)
-    {"headline": run_headline, "headline_bf16": run_headline_bf16, "sparse_s": run_sparse_s, "tiny": run_tiny, "sweep": run_sweep, "small_blocks": run_small_blocks, "ks_bwd": run_ks_bwd, "chain": run_chain, "van_loan": run_van_loan, "mlp_step": run_mlp_step, "gpt2_ffn": run_gpt2,
+    {"headline": run_headline, "headline_bf16": run_headline_bf16, "sparse_s": run_sparse_s, "tiny": run_tiny, "sweep": run_sweep, "small_blocks": run_small_blocks, "ks_bwd": run_ks_bwd, "chain": run_chain, "van_loan": run_van_loan, "mlp_step": run_mlp_step, "gpt2_ffn": run_gpt2, "gpt2_ffn_bf16": run_gpt2_bf16,
      "ks": run_ks}[args.workload](args, dev)
 
 

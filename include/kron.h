@@ -152,8 +152,10 @@ kron_status_t kron_linear_bwd_noalloc(const kron_shape_t* shape, const float* x,
  * second product (round to nearest even); y and dx are rounded once at the end.  The
  * parameter gradients dS, dA, dB and dbias are fp32.
  * Shapes: (p, q, m, n, r) in {(32,32,32,32,1), (32,32,32,32,2), (32,32,32,32,4),
- * (16,16,64,64,2)}; other shapes return KRON_E_UNSUPPORTED.  Pointers as for the fp32
- * calls (16-byte aligned); workspace from kron_linear_bwd_bf16_workspace_bytes.
+ * (16,16,64,64,2)} and the GPT-2 small FFN pair (32,64,24,48,r) and (64,32,48,24,r) with
+ * r in {1, 2, 4, 8} (a side of 24 runs padded to 32 inside the kernels' tiles); other shapes
+ * return KRON_E_UNSUPPORTED.  Pointers as for the fp32 calls (16-byte aligned); workspace
+ * from kron_linear_bwd_bf16_workspace_bytes.
  */
 size_t kron_linear_bwd_bf16_workspace_bytes(const kron_shape_t* shape);
 kron_status_t kron_linear_fwd_bf16(const kron_shape_t* shape, const void* x, const void* S,

@@ -10,7 +10,8 @@
 // Storage: x, S, A, B, bias, dy, y and dx are bf16 (bit patterns); dS, dA, dB and dbias
 // are fp32.  C_i = S o A_i is formed in fp32 (exact for bf16 factors) and rounded to
 // bf16; X B_i and G_i are rounded to bf16 (round to nearest even) before they enter their
-// second product.  Dimensions p, q, m, n must be multiples of 16.
+// second product.  p and q are multiples of 16, m and n multiples of 8 (padded to 16 inside
+// the tiles).
 #include <type_traits>
 
 #include "kron_internal.h"
@@ -37,15 +38,21 @@ __device__ __forceinline__ s4 pack4(f4 v) {
 }
 __device__ __forceinline__ s4 load_s4(const uint16_t* p) { return *reinterpret_cast<const s4*>(p); }
 
+// P, Q, M, N are the layer's sizes; MP and NP round m and n up to a whole number of 16-wide
+// tiles.  The products run over the padded sizes: the factor operands beyond m or n are
+// zero (so is the padding of the row buffers), and nothing beyond m or n is stored.
 template <int P_, int Q_, int M_, int N_, int R_>
 struct BD {
   static constexpr int P = P_, Q = Q_, M = M_, N = N_, R = R_;
-  static constexpr int TJ = P / 16, TK = Q / 16, TA = M / 16, TB = N / 16;
+  static constexpr int MP = (M + 15) / 16 * 16, NP = (N + 15) / 16 * 16;
+  static constexpr int TJ = P / 16, TK = Q / 16, TA = MP / 16, TB = NP / 16;
   static constexpr int IN = P * M, OUT = Q * N;
   static constexpr int MN = M * N, PQ = P * Q;
   static constexpr int PW = R * MN + R * PQ + PQ + Q * N;   // partial row (partial_width())
   static constexpr int PWW = R * MN + R * PQ + Q * N;       // one row slot's sums
-  static constexpr bool SHAPE_OK = P % 16 == 0 && Q % 16 == 0 && M % 16 == 0 && N % 16 == 0;
+  // (m and n in 8-element pieces: a 16-byte piece of a row never straddles two rows and a
+  // padded K chunk starts on a piece boundary)
+  static constexpr bool SHAPE_OK = P % 16 == 0 && Q % 16 == 0 && M % 8 == 0 && N % 8 == 0;
 };
 
 // ---------------------------------------------------------------------------------
@@ -96,14 +103,14 @@ __device__ __forceinline__ s8 join(s4 a, s4 b) { return s8{a[0], a[1], a[2], a[3
 // ---------------------------------------------------------------------------------
 template <class D>
 struct FB {
-  static constexpr int W1 = D::M % 32 == 0 ? 8 : 4, KC1 = D::M / (4 * W1);   // Z = X B_i over a
+  static constexpr int W1 = D::MP % 32 == 0 ? 8 : 4, KC1 = D::MP / (4 * W1);  // Z = X B_i over a (padded)
   static constexpr int W2 = D::P % 32 == 0 ? 8 : 4, KC2 = D::P / (4 * W2);   // Y^T over j
   static constexpr int TAB_B = D::R * D::TB * KC1 * 64;   // lane entries of W1 values
   static constexpr int TAB_C = D::R * D::TK * KC2 * 64;   // lane entries of W2 values
   // registers per lane: factor tables, x (current and next row), accumulators, Z tiles, bias
   static constexpr int REGS = D::R * D::TB * KC1 * W1 / 2 + D::R * D::TK * KC2 * W2 / 2 + D::TJ * KC1 * W1 +
                               D::TB * D::TK * 6 + D::TJ * D::TB * 2 + 16;
-  static constexpr int NT = REGS <= 128 ? 1024 : 512;
+  static constexpr int NT = REGS <= 128 ? 1024 : (REGS <= 200 ? 512 : 256);
   static constexpr int NW = NT / 64;
 };
 
@@ -132,17 +139,27 @@ __global__ __launch_bounds__((FB<D>::NT)) void fwd_bf16_kernel(int64_t N, uint32
 #pragma unroll
     for (int tj = 0; tj < D::TJ; ++tj)
 #pragma unroll
-      for (int s = 0; s < KC1; ++s)
-        dst[tj][s] = *reinterpret_cast<const O1*>(xr + (16 * tj + c) * D::M + k_row<W1>(s, g, 0));
+      for (int s = 0; s < KC1; ++s) {
+        const int a0 = k_row<W1>(s, g, 0);   // (a piece lies wholly below or above m)
+        if (D::MP == D::M || a0 < D::M)
+          dst[tj][s] = *reinterpret_cast<const O1*>(xr + (16 * tj + c) * D::M + a0);
+        else
+          dst[tj][s] = O1{};
+      }
   };
+  static_assert(D::M % W1 == 0, "x pieces of W1 elements");
   if (row < N) load_x(xn, row);
 
   for (int e = tid; e < F::TAB_B; e += F::NT) {   // e = ((i*TB + tb)*KC1 + s)*64 + lane
     const int ln = e & 63, rest = e >> 6, s = rest % KC1, tb = (rest / KC1) % D::TB, i = rest / (KC1 * D::TB);
-    const uint16_t* Bi = B + i * D::MN + 16 * tb + (ln & 15);
+    const int b = 16 * tb + (ln & 15);
+    const uint16_t* Bi = B + i * D::MN + b;
     O1 v;
 #pragma unroll
-    for (int u = 0; u < W1; ++u) v[u] = (short)Bi[k_row<W1>(s, ln >> 4, u) * D::N];
+    for (int u = 0; u < W1; ++u) {
+      const int a = k_row<W1>(s, ln >> 4, u);
+      v[u] = (a < D::M && b < D::N) ? (short)Bi[a * D::N] : (short)0;
+    }
     *reinterpret_cast<O1*>(tabB + e * W1) = v;
   }
   for (int e = tid; e < F::TAB_C; e += F::NT) {   // e = ((i*TK + tk)*KC2 + s)*64 + lane
@@ -163,7 +180,8 @@ __global__ __launch_bounds__((FB<D>::NT)) void fwd_bf16_kernel(int64_t N, uint32
   for (int tb = 0; tb < D::TB; ++tb)
 #pragma unroll
     for (int tk = 0; tk < D::TK; ++tk)
-      bv[tb][tk] = bias ? load_s4(bias + (16 * tk + c) * D::N + 16 * tb + 4 * g) : s4{0, 0, 0, 0};
+      bv[tb][tk] = (bias && 16 * tb + 4 * g < D::N) ? load_s4(bias + (16 * tk + c) * D::N + 16 * tb + 4 * g)
+                                                     : s4{0, 0, 0, 0};
   __syncthreads();
   O1 bop[D::R][D::TB][KC1];
   O2 cop[D::R][D::TK][KC2];
@@ -234,7 +252,8 @@ __global__ __launch_bounds__((FB<D>::NT)) void fwd_bf16_kernel(int64_t N, uint32
 #pragma unroll
           for (int v = 0; v < 4; ++v) o[v] = o[v] > 0.f ? o[v] : 0.f;
         }
-        *reinterpret_cast<s4*>(yr + (16 * tk + c) * D::N + 16 * tb + 4 * g) = pack4(o);
+        if (D::NP == D::N || 16 * tb + 4 * g < D::N)
+          *reinterpret_cast<s4*>(yr + (16 * tk + c) * D::N + 16 * tb + 4 * g) = pack4(o);
       }
   }
 }
@@ -290,16 +309,18 @@ struct BB {
   static constexpr int R = D::R;
   static constexpr int RPI = RPI_;   // rows per step
   static constexpr int NW = R * RPI, NT = 64 * NW;
-  static constexpr int WA = D::M % 32 == 0 ? 8 : 4, KA = D::M / (4 * WA);   // over a
-  static constexpr int WB = D::N % 32 == 0 ? 8 : 4, KB = D::N / (4 * WB);   // over b
+  static constexpr int WA = D::MP % 32 == 0 ? 8 : 4, KA = D::MP / (4 * WA);   // over a (padded)
+  static constexpr int WB = D::NP % 32 == 0 ? 8 : 4, KB = D::NP / (4 * WB);   // over b (padded)
   static constexpr int WK = D::Q % 32 == 0 ? 8 : 4, KK = D::Q / (4 * WK);   // over k
   static constexpr int WJ = D::P % 32 == 0 ? 8 : 4, KJ = D::P / (4 * WJ);   // over j
-  static constexpr int DXT = D::TA * D::TJ / R;                             // dX^T tiles per wavefront
+  // dX^T tiles per wavefront (the last ranks' wavefronts get fewer when R does not divide
+  // the tile count)
+  static constexpr int DXT = (D::TA * D::TJ + R - 1) / R;
   // LDS (bf16 elements), row strides chosen by measured bank behaviour: x rows (16-byte row
   // reads and transpose reads) at 16 mod 32 elements, dy rows (pairs of 8-byte row reads and
   // transpose reads) and G rows (8-byte writes, 16-byte reads) at 8 mod 16 elements.
   // A step's rows: x [P][LX], dy [Q][LY]; its G tiles [R][P][LG].
-  static constexpr int LX = D::M + 16, LY = D::N + 24, LG = D::N + 24;
+  static constexpr int LX = D::MP + 16, LY = D::NP + 24, LG = D::NP + 24;
   static constexpr int XS = D::P * LX, YS = D::Q * LY, GR = D::P * LG;
   static constexpr int ROWS = RPI * (XS + YS), GBUF = RPI * R * GR;
   static constexpr int NRB = 3, NGB = 2;
@@ -311,7 +332,7 @@ struct BB {
   static constexpr size_t LDS = MAIN > COMBINE ? (MAIN > STAGE ? MAIN : STAGE) : (COMBINE > STAGE ? COMBINE : STAGE);
   static constexpr int CHUNKS = (D::IN + D::OUT) / 8;   // 16-byte pieces of one row's x and dy
   static constexpr int NPF = (RPI * CHUNKS + NT - 1) / NT;
-  static constexpr bool OK = D::SHAPE_OK && (R == 1 || R == 2 || R == 4) && (D::TA * D::TJ) % R == 0 &&
+  static constexpr bool OK = D::SHAPE_OK && (R == 1 || R == 2 || R == 4 || R == 8) && NW <= 16 &&
                              LDS <= 160 * 1024;
 };
 
@@ -409,7 +430,10 @@ __global__ __launch_bounds__((BB<D, RPI>::NT)) void bwd_bf16_kernel(int64_t N, c
 #pragma unroll
       for (int s = 0; s < KA; ++s)
 #pragma unroll
-        for (int u = 0; u < WA; ++u) t1[tb][s][u] = (short)Bi[k_row<WA>(s, g, u) * Q::SB + 16 * tb + c];
+        for (int u = 0; u < WA; ++u) {
+          const int a = k_row<WA>(s, g, u), b = 16 * tb + c;
+          t1[tb][s][u] = (a < D::M && b < D::N) ? (short)Bi[a * Q::SB + b] : (short)0;
+        }
 #pragma unroll
     for (int tj = 0; tj < D::TJ; ++tj)
 #pragma unroll
@@ -424,11 +448,28 @@ __global__ __launch_bounds__((BB<D, RPI>::NT)) void bwd_bf16_kernel(int64_t N, c
 #pragma unroll
         for (int s = 0; s < KB; ++s)
 #pragma unroll
-          for (int u = 0; u < WB; ++u)
-            t4[d][i][s][u] = (short)sB[(i * D::M + 16 * ta + c) * Q::SB + k_row<WB>(s, g, u)];
+          for (int u = 0; u < WB; ++u) {
+            const int a = 16 * ta + c, b = k_row<WB>(s, g, u);
+            t4[d][i][s][u] = (a < D::M && b < D::N) ? (short)sB[(i * D::M + a) * Q::SB + b] : (short)0;
+          }
     }
   }
   __syncthreads();   // the staging area becomes row buffers
+  if constexpr (D::MP != D::M || D::NP != D::N) {
+    // the padding columns of every row buffer (x: a in [m, MP), dy: b in [n, NP)) are read
+    // by the products and never written by the row stashes: zero them once
+    constexpr int XPAD = D::MP - D::M, YPAD = D::NP - D::N;
+    constexpr int XD = XPAD > 0 ? XPAD : 1, YD = YPAD > 0 ? YPAD : 1;
+    constexpr int PER = D::P * XPAD + D::Q * YPAD;   // padding elements of one row slot
+    for (int e = tid; e < Q::NRB * Q::RPI * PER; e += NT) {
+      const int slot_all = e / PER, r = e % PER;
+      uint16_t* rb = lds + (slot_all / Q::RPI) * Q::ROWS + (slot_all % Q::RPI) * (Q::XS + Q::YS);
+      if (r < D::P * XPAD)
+        rb[(r / XD) * Q::LX + D::M + r % XD] = 0;
+      else
+        rb[Q::XS + ((r - D::P * XPAD) / YD) * Q::LY + D::N + (r - D::P * XPAD) % YD] = 0;
+    }
+  }
   stash(pfA, okA, 0);
   fetch(pfA, okA, blockIdx.x + (int64_t)gridDim.x);
   fetch(pfB, okB, blockIdx.x + 2 * (int64_t)gridDim.x);
@@ -523,6 +564,7 @@ __global__ __launch_bounds__((BB<D, RPI>::NT)) void bwd_bf16_kernel(int64_t N, c
 #pragma unroll
     for (int d = 0; d < Q::DXT; ++d) {
       const int t = rank * Q::DXT + d, ta = t / D::TJ, tj = t % D::TJ;
+      if ((D::TA * D::TJ) % R != 0 && t >= D::TA * D::TJ) break;   // (uniform per wavefront)
       f4 acc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < R; ++i)
@@ -531,7 +573,7 @@ __global__ __launch_bounds__((BB<D, RPI>::NT)) void bwd_bf16_kernel(int64_t N, c
           acc = mfma(t4[d][i][s],
                      *reinterpret_cast<const OB*>(Gs + i * Q::GR + (16 * tj + c) * Q::LG + k_row<WB>(s, g, 0)), acc);
       if constexpr (DXM != 0) {
-        if (!kTail || row < N) {
+        if ((!kTail || row < N) && (D::MP == D::M || 16 * ta + 4 * g < D::M)) {
           const int off = (16 * tj + c) * D::M + 16 * ta + 4 * g;   // dX[j][a .. a+3]
           if constexpr (DXM == 2) {
             const s4 xm = load_s4(X + (16 * tj + c) * Q::LX + 16 * ta + 4 * g);
@@ -595,7 +637,10 @@ __global__ __launch_bounds__((BB<D, RPI>::NT)) void bwd_bf16_kernel(int64_t N, c
 #pragma unroll
     for (int tb = 0; tb < D::TB; ++tb)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) red[rank * D::MN + (16 * ta + 4 * g + v) * D::N + 16 * tb + c] = dB[ta][tb][v];
+      for (int v = 0; v < 4; ++v) {
+        const int a = 16 * ta + 4 * g + v, b = 16 * tb + c;
+        if (a < D::M && b < D::N) red[rank * D::MN + a * D::N + b] = dB[ta][tb][v];
+      }
 #pragma unroll
   for (int tj = 0; tj < D::TJ; ++tj)
 #pragma unroll
@@ -609,8 +654,10 @@ __global__ __launch_bounds__((BB<D, RPI>::NT)) void bwd_bf16_kernel(int64_t N, c
 #pragma unroll
       for (int s = 0; s < KB; ++s)
 #pragma unroll
-        for (int u = 0; u < WB; ++u)
-          red[D::R * (D::MN + D::PQ) + (16 * tk + c) * D::N + k_acc<WB>(s, g, u)] = db[tk][s][u];
+        for (int u = 0; u < WB; ++u) {
+          const int b = k_acc<WB>(s, g, u);
+          if (b < D::N) red[D::R * (D::MN + D::PQ) + (16 * tk + c) * D::N + b] = db[tk][s][u];
+        }
   }
   __syncthreads();
   const PartRow out{part, (int64_t)gridDim.x, (int64_t)blockIdx.x, 0};
@@ -696,14 +743,22 @@ struct EntryBf16 {
 #define KRON_BF16_ENTRY(P, Q, M, N, R, RPI, WPC)                                               \
   EntryBf16{P, Q, M, N, R, RPI, WPC, &run_fwd_bf16<BD<P, Q, M, N, R>>, &run_bwd_bf16<BD<P, Q, M, N, R>, RPI>}
 
-// The 1024x1024 layers with m = 32 (r = 1, 2, 4) and m = 64 (r = 2).
-const EntryBf16 kBf16Table[] = {
-    KRON_BF16_ENTRY(32, 32, 32, 32, 1, 4, 1), KRON_BF16_ENTRY(32, 32, 32, 32, 2, 4, 1),
-    KRON_BF16_ENTRY(32, 32, 32, 32, 4, 3, 1), KRON_BF16_ENTRY(16, 16, 64, 64, 2, 2, 1),
-};
-static_assert(BB<BD<32, 32, 32, 32, 4>, 3>::OK && BB<BD<32, 32, 32, 32, 2>, 4>::OK &&
-                  BB<BD<32, 32, 32, 32, 1>, 4>::OK && BB<BD<16, 16, 64, 64, 2>, 2>::OK,
-              "every bf16 table shape fits its LDS budget");
+// The 1024x1024 layers with m = 32 (r = 1, 2, 4) and m = 64 (r = 2), and the GPT-2 FFN
+// pair 768 <-> 3072 (A_i 32 x 64, B_i 24 x 48 and the transposed layer; r = 1, 2, 4, 8).
+#define KRON_BF16_SHAPES(X)                                                                       \
+  X(32, 32, 32, 32, 1, 4, 1) X(32, 32, 32, 32, 2, 4, 1) X(32, 32, 32, 32, 4, 3, 1)                \
+  X(16, 16, 64, 64, 2, 2, 1) X(32, 64, 24, 48, 1, 1, 3) X(32, 64, 24, 48, 2, 1, 2)                \
+  X(32, 64, 24, 48, 4, 1, 2) X(32, 64, 24, 48, 8, 1, 1) X(64, 32, 48, 24, 1, 1, 3)                \
+  X(64, 32, 48, 24, 2, 1, 2) X(64, 32, 48, 24, 4, 1, 1) X(64, 32, 48, 24, 8, 1, 1)
+#define KRON_BF16_ROW(P, Q, M, N, R, RPI, WPC) KRON_BF16_ENTRY(P, Q, M, N, R, RPI, WPC),
+const EntryBf16 kBf16Table[] = {KRON_BF16_SHAPES(KRON_BF16_ROW)};
+#undef KRON_BF16_ROW
+#define KRON_BF16_FITS(P, Q, M, N, R, RPI, WPC)                                                  \
+  static_assert(BD<P, Q, M, N, R>::SHAPE_OK && BB<BD<P, Q, M, N, R>, RPI>::OK &&                  \
+                    WPC * BB<BD<P, Q, M, N, R>, RPI>::LDS <= 160 * 1024,                            \
+                "bf16 table shape within its LDS budget");
+KRON_BF16_SHAPES(KRON_BF16_FITS)
+#undef KRON_BF16_FITS
 
 const EntryBf16* find_bf16(int p, int q, int m, int n, int r) {
   for (const EntryBf16& e : kBf16Table)

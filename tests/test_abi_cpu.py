@@ -150,7 +150,9 @@ def test_bf16_argument_errors():
     HIP call (fake device addresses are never dereferenced)."""
     L = _lib.lib()
     MB = 1 << 20
-    bad = KronShape(8, 32, 64, 24, 48, 1, 0)   # m = 24: no bf16 kernel
+    bad = KronShape(8, 32, 32, 20, 20, 1, 0)   # m = 20: no bf16 kernel
+    gpt2 = KronShape(8, 32, 64, 24, 48, 1, 0)  # m = 24 runs padded to 32
+    assert L.kron_linear_bwd_bf16_workspace_bytes(ctypes.byref(gpt2)) > 0
     assert L.kron_linear_fwd_bf16(ctypes.byref(bad), P(0), None, P(MB), P(2 * MB), None, P(3 * MB), None) == \
         _lib.KRON_E_UNSUPPORTED
     assert L.kron_linear_bwd_bf16_workspace_bytes(ctypes.byref(bad)) == 0

@@ -7,7 +7,7 @@ import pytest
 
 from _harness import TOL_BF16, dev, rel_err
 from oracle import kron as OK
-from workloads import bf16_bits, bf16_to_f32, headline_layer, kron_inputs
+from workloads import bf16_bits, bf16_to_f32, gpt2_ffn_layers, headline_layer, kron_inputs
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -80,6 +80,33 @@ def test_headline_shape_full_size():
 @pytest.mark.parametrize("N", [0, 1, 3, 1031])
 def test_ragged_rows(N, r):
     compare_bf16(kron_inputs(60 + r, N, 32, 32, 32, 32, r, s_mode="uniform_zeroed", bias_mode="normal"))
+
+
+@pytest.mark.parametrize("r", [1, 2, 4, 8])
+def test_gpt2_ffn_layers(r):
+    """768 -> 3072 (A_i 32x64, B_i 24x48: m = 24 runs padded to 32 inside the tiles) and
+    3072 -> 768 (A_i 64x32, B_i 48x24: n = 24 padded), 8192 rows."""
+    up, down = gpt2_ffn_layers(r)
+    compare_bf16(up)
+    compare_bf16(down)
+
+
+@pytest.mark.parametrize("shape", [(32, 64, 24, 48), (64, 32, 48, 24)])
+@pytest.mark.parametrize("N", [1, 3, 1031])
+def test_gpt2_ffn_ragged_rows_with_S_bias_and_relu(shape, N):
+    """The padded shapes with S, a bias, the ReLU output and the ReLU mask on dx, on ragged
+    row counts (r = 2)."""
+    p, q, m, n = shape
+    compare_bf16(kron_inputs(63 + N, N, p, q, m, n, 2, s_mode="uniform_zeroed", bias_mode="normal"), relu=True,
+                 relu_mask=True)
+
+
+@pytest.mark.parametrize("shape", [(32, 64, 24, 48), (64, 32, 48, 24)])
+def test_gpt2_ffn_rank8_with_S_and_mask(shape):
+    """r = 8 (eight wavefronts per row, the dX tiles shared unevenly) with S, a bias and the
+    ReLU mask, on a ragged row count."""
+    p, q, m, n = shape
+    compare_bf16(kron_inputs(71, 517, p, q, m, n, 8, s_mode="uniform_zeroed", bias_mode="normal"), relu_mask=True)
 
 
 def test_mlp_layer_shape_with_relu_flags():
