@@ -174,13 +174,13 @@ __global__ __launch_bounds__(64 * NWH) void head_mfma_kernel(int64_t N, int C, u
   const bool mask = flags & KRON_DX_RELU_MASK;
 
   float wz[SZ];                     // W[k = w*KQ + g*SZ + s][class c]
-  float wh[TQ][4];                  // W[k = w*KQ + 16t + c][class 4g + s]
+  float wh[TQ][4];                  // W[k = w*KQ + 16t + c][class 4s + g]
 #pragma unroll
   for (int s = 0; s < SZ; ++s) wz[s] = c < C ? W[(int64_t)(w * KQ + g * SZ + s) * C + c] : 0.f;
 #pragma unroll
   for (int t = 0; t < TQ; ++t)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) wh[t][s] = (4 * g + s) < C ? W[(int64_t)(w * KQ + 16 * t + c) * C + 4 * g + s] : 0.f;
+    for (int s = 0; s < 4; ++s) wh[t][s] = (4 * s + g) < C ? W[(int64_t)(w * KQ + 16 * t + c) * C + 4 * s + g] : 0.f;
   const int row_t = (tid >> 4) & 15, cls_t = tid & 15;   // the (row, class) of threads < 256 in the softmax
   const float bias_t = cls_t < C ? b[cls_t] : 0.f;
 
@@ -274,26 +274,31 @@ __global__ __launch_bounds__(64 * NWH) void head_mfma_kernel(int64_t N, int C, u
       dbacc += d;
     }
     __syncthreads();
-    // dh[:, quarter] = dz W[quarter, :]^T and dW[quarter, :] += h[:, quarter]^T dz
+    // dh[:, quarter] = dz W[quarter, :]^T and dW[quarter, :] += h[:, quarter]^T dz.  dh is
+    // formed transposed (dh^T[col][row] = sum_class W[col][class] dz[row][class]), so that a
+    // lane holds four consecutive columns of one row and writes them as one 16-byte store.
     {
-      const f4 dza = *reinterpret_cast<const f4*>(dzs + c * 16 + 4 * g);   // dz[row c][class 4g+s]
+      float dzr[4];                                                         // dz[row c][class 4s+g]
+#pragma unroll
+      for (int s = 0; s < 4; ++s) dzr[s] = dzs[c * 16 + 4 * s + g];
       float dzb[4];                                                         // dz[row 4g+s][class c]
 #pragma unroll
       for (int s = 0; s < 4; ++s) dzb[s] = dzs[(4 * g + s) * 16 + c];
+      const bool live = !kTail || r0 + c < N;
 #pragma unroll
       for (int t = 0; t < TQ; ++t) {
         const int col = w * KQ + 16 * t + c;
         if constexpr (DH) {
-          f4 o = f4{0.f, 0.f, 0.f, 0.f};
+          f4 o = f4{0.f, 0.f, 0.f, 0.f};   // dh[row c][cols w*KQ + 16t + 4g .. +3]
 #pragma unroll
-          for (int s = 0; s < 4; ++s) o = __builtin_amdgcn_mfma_f32_16x16x4f32(dza[s], wh[t][s], o, 0, 0, 0);
+          for (int s = 0; s < 4; ++s) o = __builtin_amdgcn_mfma_f32_16x16x4f32(wh[t][s], dzr[s], o, 0, 0, 0);
+          const int c0 = w * KQ + 16 * t + 4 * g;
+          if (mask) {
+            const f4 hv = *reinterpret_cast<const f4*>(hs + c * LH + c0);
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int r = 4 * g + v;
-            float val = o[v];
-            if (mask && !(hs[r * LH + col] > 0.f)) val = 0.f;
-            if (!kTail || r0 + r < N) __builtin_nontemporal_store(val, dh + (r0 + r) * KK + col);
+            for (int v = 0; v < 4; ++v) o[v] = hv[v] > 0.f ? o[v] : 0.f;
           }
+          if (live) __builtin_nontemporal_store(o, reinterpret_cast<f4*>(dh + (r0 + c) * KK + c0));
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s)
