@@ -323,7 +323,10 @@ struct BB {
   static constexpr int LX = D::MP + 16, LY = D::NP + 24, LG = D::NP + 24;
   static constexpr int XS = D::P * LX, YS = D::Q * LY, GR = D::P * LG;
   static constexpr int ROWS = RPI * (XS + YS), GBUF = RPI * R * GR;
-  static constexpr int NRB = 3, NGB = 2;
+  // Rows are triple-buffered and G tiles double-buffered so that one barrier per step
+  // orders the wavefronts; a workgroup of one wavefront needs neither (its LDS accesses
+  // complete in program order), so it keeps two row buffers and one G buffer.
+  static constexpr int NRB = NW == 1 ? 2 : 3, NGB = NW == 1 ? 1 : 2;
   static constexpr size_t MAIN = (size_t)(NRB * ROWS + NGB * GBUF) * 2;
   // prologue staging: B_i [a][b] and C_i [j][k] row-major with odd-word row strides
   static constexpr int SB = D::N + 2, SC = D::Q + 2;
@@ -612,7 +615,7 @@ __global__ __launch_bounds__((BB<D, RPI>::NT)) void bwd_bf16_kernel(int64_t N, c
   int rbuf = 0, gbuf = 0;
   auto advance = [&]() {
     rbuf = rbuf == Q::NRB - 1 ? 0 : rbuf + 1;
-    gbuf ^= 1;
+    gbuf = Q::NGB == 1 ? 0 : gbuf ^ 1;
     grp += G;
   };
   while (grp + G < nfull) {   // local steps in pairs: register set A, then B
@@ -747,8 +750,8 @@ struct EntryBf16 {
 // pair 768 <-> 3072 (A_i 32 x 64, B_i 24 x 48 and the transposed layer; r = 1, 2, 4, 8).
 #define KRON_BF16_SHAPES(X)                                                                       \
   X(32, 32, 32, 32, 1, 4, 1) X(32, 32, 32, 32, 2, 4, 1) X(32, 32, 32, 32, 4, 3, 1)                \
-  X(16, 16, 64, 64, 2, 2, 1) X(32, 64, 24, 48, 1, 1, 3) X(32, 64, 24, 48, 2, 1, 2)                \
-  X(32, 64, 24, 48, 4, 1, 2) X(32, 64, 24, 48, 8, 1, 1) X(64, 32, 48, 24, 1, 1, 3)                \
+  X(16, 16, 64, 64, 2, 2, 1) X(32, 64, 24, 48, 1, 1, 4) X(32, 64, 24, 48, 2, 1, 2)                \
+  X(32, 64, 24, 48, 4, 1, 2) X(32, 64, 24, 48, 8, 1, 1) X(64, 32, 48, 24, 1, 1, 4)                \
   X(64, 32, 48, 24, 2, 1, 2) X(64, 32, 48, 24, 4, 1, 1) X(64, 32, 48, 24, 8, 1, 1)
 #define KRON_BF16_ROW(P, Q, M, N, R, RPI, WPC) KRON_BF16_ENTRY(P, Q, M, N, R, RPI, WPC),
 const EntryBf16 kBf16Table[] = {KRON_BF16_SHAPES(KRON_BF16_ROW)};

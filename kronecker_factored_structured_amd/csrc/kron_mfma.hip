@@ -49,7 +49,7 @@
 #define KRON_MFMA_SHAPES(X)                                                                             \
   X(8, 8, 8, 8, 1, 1) X(8, 8, 8, 8, 2, 1) X(32, 32, 32, 32, 1, 1) X(32, 32, 32, 32, 2, 1)               \
   X(32, 32, 32, 32, 4, 2) X(16, 16, 64, 64, 1, 0) X(16, 16, 64, 64, 2, 0)                               \
-  X(32, 64, 24, 48, 1, 1) X(32, 64, 24, 48, 2, 0) X(32, 64, 24, 48, 4, 1)                               \
+  X(32, 64, 24, 48, 1, 0) X(32, 64, 24, 48, 2, 0) X(32, 64, 24, 48, 4, 1)                               \
   X(32, 64, 24, 48, 8, 1) X(64, 32, 48, 24, 1, 0) X(64, 32, 48, 24, 2, 1)                               \
   X(64, 32, 48, 24, 4, 1) X(64, 32, 48, 24, 8, 1)
 
@@ -174,12 +174,23 @@ struct Dims {
   static constexpr int BWD_SCRATCH = (kWaves * GS > RAW) ? kWaves * GS : RAW;
   static constexpr int BWD_MAIN = BWD_TABLES + BWD_SCRATCH;
   static constexpr size_t FWD_LDS = (size_t)FWD_FLOATS * 4;
-  static constexpr size_t BWD_LDS = (size_t)(BWD_MAIN > kWaves * PWW ? BWD_MAIN : kWaves * PWW) * 4;
   // registers held across a backward row (accumulators and per-row operands), in floats
   static constexpr int ROW_REGS = TJ * SA + TA * SJ + TK * TB * 4 + TB * SK;
   static constexpr int BWD_REGS =
       R * TJ * TK * 4 + R * TA * TB * 4 + TK * TB * 4 + ROW_REGS + TA * TJ * 4 + TB * TJ * 8;
   static_assert(M % 4 == 0 && N % 4 == 0, "rows are moved as 4-float vectors");
+  // bwd_mfma_kernel's row tiles: each wavefront stages its next row's x and dY in LDS
+  // (16-byte loads, 16-byte writes) and reads the row operands back from there.  Row
+  // pitches: x rows at m + 4 floats, dY rows at a pitch of 16 mod 32 words, so that the
+  // 4-byte column reads of one half-wavefront fall in distinct banks.
+  static constexpr int TLX = M + 4;
+  static constexpr int TLY = N + ((16 - N % 32) + 32) % 32;
+  static constexpr int TXT = P * TLX, TYT = Q * TLY;                    // one wavefront's tiles
+  static constexpr int NXF = (IN / 4 + 63) / 64, NYF = (OUT / 4 + 63) / 64;   // 16-byte loads per lane
+  static constexpr bool BWD_TILED = (size_t)(BWD_MAIN + kWaves * (TXT + TYT)) * 4 <= kMaxLds &&
+                                    BWD_REGS + 4 * (NXF + NYF) <= 420;
+  static constexpr int BWD_USED = BWD_MAIN + (BWD_TILED ? kWaves * (TXT + TYT) : 0);
+  static constexpr size_t BWD_LDS = (size_t)(BWD_USED > kWaves * PWW ? BWD_USED : kWaves * PWW) * 4;
   static constexpr bool FWD_OK = FWD_LDS <= kMaxLds;
   // thresholds measured against the compiler's allocation (no scratch below them)
   static constexpr bool BWD_OK = BWD_LDS <= kMaxLds && BWD_REGS <= 360;
@@ -573,7 +584,75 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
   float* rC = rB + D::RAWB;
   BwdRow<D> nx;   // the next row's operands, loaded while the current row computes; the
                   // first row's loads are issued before the tables are built
-  if constexpr (D::BWD_PREFETCH) {
+  // BWD_TILED: the next row's x and dY in registers as 16-byte pieces, staged in this
+  // wavefront's LDS tiles at the end of a row and read back as the row operands
+  float* xt = lds + D::BWD_MAIN + (threadIdx.x >> 6) * (D::TXT + D::TYT);
+  float* yt = xt + D::TXT;
+  f4 sx[D::NXF], sy[D::NYF];
+  auto fetch_t = [&](int64_t r) {
+    const int ln = threadIdx.x & 63;
+#pragma unroll
+    for (int t = 0; t < D::NXF; ++t) {
+      const int f = 64 * t + ln;
+      if (D::IN % 256 == 0 || f < D::IN / 4) sx[t] = *reinterpret_cast<const f4*>(x + r * D::IN + 4 * f);
+    }
+#pragma unroll
+    for (int t = 0; t < D::NYF; ++t) {
+      const int f = 64 * t + ln;
+      if (D::OUT % 256 == 0 || f < D::OUT / 4) sy[t] = *reinterpret_cast<const f4*>(dy + r * D::OUT + 4 * f);
+    }
+  };
+  auto stage_t = [&]() {
+    const int ln = threadIdx.x & 63;
+#pragma unroll
+    for (int t = 0; t < D::NXF; ++t) {
+      const int f = 64 * t + ln, e = 4 * f;
+      if (D::IN % 256 == 0 || f < D::IN / 4) *reinterpret_cast<f4*>(xt + (e / D::M) * D::TLX + e % D::M) = sx[t];
+    }
+#pragma unroll
+    for (int t = 0; t < D::NYF; ++t) {
+      const int f = 64 * t + ln, e = 4 * f;
+      if (D::OUT % 256 == 0 || f < D::OUT / 4) *reinterpret_cast<f4*>(yt + (e / D::N) * D::TLY + e % D::N) = sy[t];
+    }
+  };
+  auto rd_ops_t = [&](BwdRow<D>& o, int g, int c) {
+#pragma unroll
+    for (int tj = 0; tj < D::TJ; ++tj) {
+      const int j = 16 * tj + c;
+      if (j < D::P) {
+        vload<D::SA>(o.xa[tj], xt + j * D::TLX + g * D::SA);
+      } else {
+#pragma unroll
+        for (int s = 0; s < D::SA; ++s) o.xa[tj][s] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int ta = 0; ta < D::TA; ++ta)
+#pragma unroll
+      for (int s = 0; s < D::SJ; ++s) {
+        const int j = g * D::SJ + s, a = 16 * ta + c;
+        o.xaj[ta][s] = (j < D::P && a < D::M) ? xt[j * D::TLX + a] : 0.f;
+      }
+#pragma unroll
+    for (int tk = 0; tk < D::TK; ++tk)
+#pragma unroll
+      for (int tb = 0; tb < D::TB; ++tb) {
+        const int k = 16 * tk + c, b0 = 16 * tb + 4 * g;
+        o.dyk[tk][tb] = (k < D::Q && b0 < D::N) ? *reinterpret_cast<const f4*>(yt + k * D::TLY + b0)
+                                               : f4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int tb = 0; tb < D::TB; ++tb)
+#pragma unroll
+      for (int s = 0; s < D::SK; ++s) {
+        const int k = 4 * s + g, b = 16 * tb + c;
+        o.dyb[tb][s] = (k < D::Q && b < D::N) ? yt[k * D::TLY + b] : 0.f;
+      }
+  };
+  if constexpr (D::BWD_TILED) {
+    const int64_t row0 = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (row0 < N) fetch_t(row0);
+  } else if constexpr (D::BWD_PREFETCH) {
     const int64_t row0 = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
     if (row0 < N) load_bwd_row<D>(nx, x + row0 * D::IN, dy + row0 * D::OUT, (threadIdx.x & 63) >> 4, threadIdx.x & 15);
   }
@@ -617,7 +696,13 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
 
   const int64_t stride = (int64_t)gridDim.x * kWaves;
   int64_t row = (int64_t)blockIdx.x * kWaves + wave;
-  if constexpr (D::BWD_PREFETCH) {
+  BwdRow<D> cur;
+  if constexpr (D::BWD_TILED) {
+    if (row < N) {
+      stage_t();
+      rd_ops_t(cur, g, c);
+    }
+  } else if constexpr (D::BWD_PREFETCH) {
     settle(nx.xa);
     settle(nx.xaj);
     settle(nx.dyk);
@@ -625,8 +710,9 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
   }
   for (; row < N; row += stride) {
     const float* xr = x + row * D::IN;
-    BwdRow<D> cur;
-    if constexpr (D::BWD_PREFETCH) {
+    if constexpr (D::BWD_TILED) {
+      fetch_t(row + stride < N ? row + stride : row);
+    } else if constexpr (D::BWD_PREFETCH) {
       cur = nx;
       if (row + stride < N) load_bwd_row<D>(nx, x + (row + stride) * D::IN, dy + (row + stride) * D::OUT, g, c);
     } else {
@@ -647,8 +733,9 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
 #pragma unroll
         for (int tj = 0; tj < D::TJ; ++tj) {
           const int j = 16 * tj + c, a0 = 16 * ta + 4 * g;
-          xm[ta][tj] = (j < D::P && a0 < D::M) ? *reinterpret_cast<const f4*>(xr + j * D::M + a0)
-                                               : f4{0.f, 0.f, 0.f, 0.f};
+          xm[ta][tj] = (j < D::P && a0 < D::M)
+                           ? *reinterpret_cast<const f4*>(D::BWD_TILED ? xt + j * D::TLX + a0 : xr + j * D::M + a0)
+                           : f4{0.f, 0.f, 0.f, 0.f};
         }
     }
 #pragma unroll
@@ -760,13 +847,22 @@ void bwd_mfma_kernel(int64_t N, uint32_t flags, const float* __restrict__ x, con
           if (j < D::P && a0 < D::M) {
             f4 o = dxt[ta][tj];
             if (mask) {
-              const f4 xv = EARLY_MASK ? xm[ta][tj] : *reinterpret_cast<const f4*>(xr + j * D::M + a0);
+              const f4 xv = EARLY_MASK ? xm[ta][tj]
+                                       : *reinterpret_cast<const f4*>(D::BWD_TILED ? xt + j * D::TLX + a0
+                                                                                   : xr + j * D::M + a0);
 #pragma unroll
               for (int v = 0; v < 4; ++v) o[v] = xv[v] > 0.f ? o[v] : 0.f;
             }
             __builtin_nontemporal_store(o, reinterpret_cast<f4*>(dxr + j * D::M + a0));
           }
         }
+    }
+    if constexpr (D::BWD_TILED) {
+      // the next row into the tiles (this row's reads of them are done) and its operands
+      __builtin_amdgcn_wave_barrier();
+      stage_t();
+      __builtin_amdgcn_wave_barrier();
+      rd_ops_t(cur, g, c);
     }
   }
 
