@@ -148,3 +148,26 @@ def test_mlp_training_step(N):
     chained = [rel_err(g, o) for g, o in zip(ghost, ogl)]
     print(f"   chained: loss {host(loss)[0]:.7f} vs {oloss:.7f}; relu mask flips {flips1}+{flips2}; "
           f"max grad rel err {max(chained):.2e}", flush=True)
+
+
+def test_mlp_three_steps_loss_trajectory():
+    """Three consecutive training steps (fwd, CE + lam*sum|S|, bwd, fused Adam with its
+    state carried over) on 999 rows, against the oracle stepping its own parameters and
+    Adam state: the loss of every step within the fp32 bar.  (Parameters are not compared
+    entry by entry: Adam moves an entry by lr * sign(g) at the first step, so an entry whose
+    gradient is a rounding error away from zero may move either way.)"""
+    print("[step] three steps, N=999", flush=True)
+    inp = mlp_step_inputs(N=999)
+    step = K().KronMLPStep(inp.layers, inp.head_w, inp.head_b, inp.lam, inp.lr, "cuda")
+    x, lab = dev(inp.x), dev(inp.labels)
+    layers = [dict(L) for L in inp.layers]
+    hw, hb, state = inp.head_w, inp.head_b, None
+    for t in range(1, 4):
+        loss = host(step.step(x, lab))[0]
+        oloss, newp, state, _, _ = OM.full_step(inp.x, inp.labels, layers, hw, hb, inp.lam, inp.lr, step=t,
+                                                state=state)
+        print(f"   step {t}: loss {loss:.7f} vs oracle {oloss:.7f}", flush=True)
+        assert abs(loss - oloss) <= TOL_F32 * oloss, t
+        layers = [dict(S=newp[0], A=newp[1], B=newp[2], bias=newp[3]),
+                  dict(S=newp[4], A=newp[5], B=newp[6], bias=newp[7])]
+        hw, hb = newp[8], newp[9]
