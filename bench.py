@@ -295,7 +295,10 @@ def run_headline(args, dev):
         "roofline": roofline,
         "pass_roofline": {"bound": "fp32", "t_roof_us": round(t_roof * 1e6, 2),
                           "t_us": round(ms_step * 1e3, 2), "frac": round(t_roof / (ms_step * 1e-3), 4),
-                          "effective_tflops": round(N * (ff + fb) / (ms_step * 1e-3) / 1e12, 3)},
+                          "effective_tflops": round(N * (ff + fb) / (ms_step * 1e-3) / 1e12, 3),
+                          # context only: the flops the same pass would count with S dense
+                          "dense_equivalent_tflops": round(N * sum(work_per_row(p, q, m, n, r, p * q)[:2]) /
+                                                           (ms_step * 1e-3) / 1e12, 3)},
         "t_fwd_us": round(t_fwd * 1e6, 2), "t_bwd_us": round(t_bwd * 1e6, 2),
         "median_us": {"fwd": round(med_fwd * 1e6, 2), "bwd": round(med_bwd * 1e6, 2),
                       "fwd_bwd": round(med_step * 1e6, 2)},

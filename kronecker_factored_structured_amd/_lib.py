@@ -8,7 +8,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkron.so")
+# KRON_LIB_PATH selects another build of the library (e.g. the host-sanitized one)
+LIB_PATH = os.environ.get("KRON_LIB_PATH") or os.path.join(_HERE, "libkron.so")
 
 KRON_OK = 0
 KRON_E_NULL = 1

@@ -50,18 +50,36 @@ FLAGS = [
 ]
 
 
-def compile_commands(objdir: str) -> list:
+# Host-only AddressSanitizer and UndefinedBehaviorSanitizer (each flag behind -Xarch_host,
+# so no device code is instrumented): a build of the library for checking the host side,
+# the argument validation of the C ABI above all, on the CPU.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def compile_commands(objdir: str, host_sanitize: bool = False) -> list:
     cmds = []
     for src, extra, name in OBJECTS:
         path = os.path.join(CSRC, src)
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmds.append([HIPCC] + FLAGS + extra + ["-c"] + lang + [path, "-o", os.path.join(objdir, name + ".o")])
+        san = HOST_SANITIZE if host_sanitize else []
+        cmds.append([HIPCC] + FLAGS + extra + san + ["-c"] + lang + [path, "-o", os.path.join(objdir, name + ".o")])
     return cmds
 
 
-def link_command(objdir: str, out: str) -> list:
+def link_command(objdir: str, out: str, host_sanitize: bool = False) -> list:
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libsan"] \
+        if host_sanitize else []
     return [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}"] + \
-        [os.path.join(objdir, name + ".o") for _, _, name in OBJECTS] + ["-o", out]
+        [os.path.join(objdir, name + ".o") for _, _, name in OBJECTS] + san + ["-o", out]
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's AddressSanitizer runtime (to preload into a process that
+    loads the host-sanitized library), or '' when it is not installed."""
+    res = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    return path if res.returncode == 0 and os.path.isabs(path) and os.path.exists(path) else ""
 
 
 def _run(cmd, verbose):
@@ -75,20 +93,24 @@ def _run(cmd, verbose):
         sys.stderr.write(res.stderr)
 
 
-def build(verbose: bool = False) -> str:
-    """Compile libkron.so (always recompiles) and return its path."""
+def build(verbose: bool = False, host_sanitize: bool = False, out: str = LIB) -> str:
+    """Compile libkron.so (always recompiles) to `out` and return its path."""
     import tempfile
     from concurrent.futures import ThreadPoolExecutor
     with tempfile.TemporaryDirectory(prefix="kron_build_") as objdir:
-        cmds = compile_commands(objdir)
+        cmds = compile_commands(objdir, host_sanitize)
         workers = max(1, min(len(cmds), os.cpu_count() or 1, 8))
         with ThreadPoolExecutor(max_workers=workers) as ex:
             list(ex.map(lambda c: _run(c, verbose), cmds))
-        tmp = LIB + ".tmp"
-        _run(link_command(objdir, tmp), verbose)
-        os.replace(tmp, LIB)
-    return LIB
+        tmp = out + ".tmp"
+        _run(link_command(objdir, tmp, host_sanitize), verbose)
+        os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    # python -m kronecker_factored_structured_amd.build [--host-sanitize OUT.so]
+    if len(sys.argv) == 3 and sys.argv[1] == "--host-sanitize":
+        print(build(verbose=True, host_sanitize=True, out=os.path.abspath(sys.argv[2])))
+    else:
+        print(build(verbose=True))
