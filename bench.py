@@ -419,15 +419,18 @@ def run_sparse_s(args, dev):
     16-row tiles that hold nonzero rows of C = S o A_i."""
     from workloads import kron_inputs
     for mode, frac in (("uniform_zeroed", 0.5), ("rows_zeroed", 0.0), ("rows_zeroed", 0.25), ("rows_zeroed", 0.5),
-                       ("rows_zeroed", 0.75), ("rows_zeroed", 0.875)):
+                       ("rows_zeroed", 0.75), ("rows_zeroed", 0.875), ("blocks_zeroed", 0.5), ("blocks_zeroed", 0.75)):
         inp = kron_inputs(90, 20000, 32, 32, 32, 32, 4, s_mode=mode, zero_frac=frac, bias_mode="zeros")
         rows_left = int(np.count_nonzero(inp.S.any(axis=1)))
+        zero_blocks = [(tj, tk) for tj in range(2) for tk in range(2)
+                       if not inp.S[16 * tj:16 * tj + 16, 16 * tk:16 * tk + 16].any()]
         what = (f"{frac:.0%} of S's entries zero at random" if mode == "uniform_zeroed"
-                else f"{frac:.1%} of S's rows zero ({rows_left} of 32 rows left)")
+                else f"{frac:.1%} of S's rows zero ({rows_left} of 32 rows left)" if mode == "rows_zeroed"
+                else f"16x16 blocks {zero_blocks} of S zero")
         for hint in (False, True):
             layer_record(f"sparse_s: 1024x1024 layer, m=32, r=4, 20000 rows, {what}, "
                          f"{'KRON_SPARSE_ROWS' if hint else 'dense path'}", inp, Layer(inp, dev, sparse_rows=hint),
-                         args, extra={"s_rows_nonzero": rows_left, "sparse_rows": hint,
+                         args, extra={"s_rows_nonzero": rows_left, "s_zero_blocks": zero_blocks, "sparse_rows": hint,
                                       "fwd_tiles_run": max(1, -(-rows_left // 16)) if hint else 2})
 
 

@@ -63,8 +63,10 @@ typedef enum { KRON_F32 = 0, KRON_BF16 = 1 } kron_dtype_t;
  * (its rows with a nonzero entry in any rank, compacted to the front) and run only the
  * 16-row tiles that hold such rows (tutorial, intro: zeros of S give zero blocks of W): in
  * the forward both products, in the backward G = C dY, dX and dB (Z and dC stay dense:
- * dS needs dC everywhere).  Results equal the dense path's up to the order of the sums.
- * Costs a little on an S with no empty tile; other kernels ignore it. */
+ * dS needs dC everywhere).  The forward also skips the stage-2 steps over every 16 x 16
+ * block of S (rows in map order) that is entirely zero, e.g. a block-diagonal mask.
+ * Results equal the dense path's up to the order of the sums.  Costs a little on an S
+ * with no empty row tile or block; other kernels ignore it. */
 #define KRON_SPARSE_ROWS  4u
 
 typedef struct {

@@ -168,7 +168,7 @@ struct Dims {
   // tables straight from global memory
   static constexpr bool FWD_RAW = (size_t)(BOP + COPF + RAW) * 4 <= kMaxLds;
   // the forward's row map (FwdMap): a 64-bit row mask per wavefront and the map (TJ*16 ints)
-  static constexpr int FWD_MAP = (2 * kWaves + TJ * 16 + 3) / 4 * 4;
+  static constexpr int FWD_MAP = (2 * kWaves + TJ * 16 + 1 + 3) / 4 * 4;   // + the tile mask
   static constexpr int FWD_FLOATS = BOP + COPF + (FWD_RAW ? RAW + FWD_MAP : 0);
   static constexpr int BWD_TABLES = BOP + COPG + BOPX;
   static constexpr int BWD_SCRATCH = (kWaves * GS > RAW) ? kWaves * GS : RAW;
@@ -335,11 +335,13 @@ __device__ __forceinline__ void load_xa_map(float (&xa)[D::TJ][D::SA], const flo
 }
 
 // The row loop of the forward over the first TJE tiles of the row map.
-template <class D, int TJE>
+// With SKIP, bit tj*TK + tk of tmask says whether the 16 x 16 tile (tj, tk) of C (rows in
+// map order) holds a nonzero entry in any rank; stage 2 skips the K steps of the others.
+template <class D, int TJE, bool SKIP>
 __device__ __forceinline__ void fwd_rows(int64_t row, int64_t N, bool relu, const float* __restrict__ x,
                                          float* __restrict__ y, const float* bop, const float* cop,
                                          float (&xa)[D::TJ][D::SA], const int (&jr)[D::TJ],
-                                         const f4 (&bb)[D::TB][D::TK], int lane, int g, int c) {
+                                         const f4 (&bb)[D::TB][D::TK], int lane, int g, int c, unsigned tmask) {
   const int64_t stride = (int64_t)gridDim.x * kWaves;
   // The next row's X is loaded at the top of each row (the last row reloads itself), and
   // a scheduling barrier keeps the compiler from sinking those loads towards their use.
@@ -384,9 +386,11 @@ __device__ __forceinline__ void fwd_rows(int64_t row, int64_t N, bool relu, cons
 #pragma unroll
         for (int tb = 0; tb < D::TB; ++tb)
 #pragma unroll
-          for (int tj = 0; tj < TJE; ++tj)
+          for (int tj = 0; tj < TJE; ++tj) {
+            if (SKIP && !((tmask >> (tj * D::TK + tk)) & 1u)) continue;   // (uniform) all-zero tile of C
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[tb][tk] = mfma(z[tj][tb][v], co[tj * 4 + v], acc[tb][tk]);
+          }
       }
     }
     // acc[tb][tk] register v = Y^T[b = 16tb+4g+v][k = 16tk+c] -> y[k*N + b]
@@ -412,16 +416,21 @@ __device__ __forceinline__ void fwd_rows(int64_t row, int64_t N, bool relu, cons
   }
 }
 
-template <class D, int T>
+template <class D, int T, bool SKIP>
 __device__ __forceinline__ void fwd_rows_tje(int tje, int64_t row, int64_t N, bool relu, const float* __restrict__ x,
                                              float* __restrict__ y, const float* bop, const float* cop,
                                              float (&xa)[D::TJ][D::SA], const int (&jr)[D::TJ],
-                                             const f4 (&bb)[D::TB][D::TK], int lane, int g, int c) {
+                                             const f4 (&bb)[D::TB][D::TK], int lane, int g, int c, unsigned tmask) {
   if constexpr (T >= 1) {
     if (tje == T) {
-      fwd_rows<D, T>(row, N, relu, x, y, bop, cop, xa, jr, bb, lane, g, c);
+      // the tile branches only where a tile of the first T row tiles is empty (uniform)
+      constexpr unsigned kFull = (T * D::TK >= 32) ? ~0u : ((1u << (T * D::TK)) - 1u);
+      if (SKIP && (tmask & kFull) != kFull)
+        fwd_rows<D, T, SKIP>(row, N, relu, x, y, bop, cop, xa, jr, bb, lane, g, c, tmask);
+      else
+        fwd_rows<D, T, false>(row, N, relu, x, y, bop, cop, xa, jr, bb, lane, g, c, tmask);
     } else {
-      fwd_rows_tje<D, T - 1>(tje, row, N, relu, x, y, bop, cop, xa, jr, bb, lane, g, c);
+      fwd_rows_tje<D, T - 1, SKIP>(tje, row, N, relu, x, y, bop, cop, xa, jr, bb, lane, g, c, tmask);
     }
   }
 }
@@ -441,6 +450,8 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
   // would shift the dynamic block off its 16-byte alignment)
   unsigned long long* s_wmask = reinterpret_cast<unsigned long long*>(cop + D::COPF + D::RAW);  // per wavefront
   int* s_map = reinterpret_cast<int*>(s_wmask + kWaves);                                    // position -> row
+  int* s_tmask = s_map + D::TJ * 16;                                                         // nonzero tiles
+  if (FwdMap<D, MAP>::ON && threadIdx.x == 0) *s_tmask = 0;   // (read after the staging barrier)
   const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   const int wave = threadIdx.x >> 6;
   int64_t row = (int64_t)blockIdx.x * kWaves + wave;
@@ -462,6 +473,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
     }
   int tje = D::TJ;
   bool remap = false;
+  unsigned tmask = ~0u;
   if constexpr (D::FWD_RAW) {
     float* rB = cop + D::COPF;
     float* rC = rB + D::RAWB;
@@ -500,6 +512,22 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
         }
         __syncthreads();
       }
+      // the tile mask: which 16 x 16 tiles of S, rows in map order, hold a nonzero entry (a
+      // zero tile of S is a zero tile of every C_i; per output block-column tk, the row tiles
+      // its sum runs over).  Without S nothing is skipped.
+      static_assert(D::TJ * D::TK <= 32, "one bit per tile");
+      if (Sm) {
+        unsigned tm = 0;
+        constexpr int QV = D::Q / 4;   // 4-float pieces per row of S
+        for (int e = threadIdx.x; e < D::P * QV; e += kThreads) {
+          const int p = e / QV, k0 = 4 * (e % QV);
+          const f4 sv = *reinterpret_cast<const f4*>(Sm + (remap ? s_map[p] : p) * D::Q + k0);
+          if (sv[0] != 0.f || sv[1] != 0.f || sv[2] != 0.f || sv[3] != 0.f) tm |= 1u << ((p >> 4) * D::TK + (k0 >> 4));
+        }
+        if (tm) atomicOr(s_tmask, (int)tm);
+        __syncthreads();
+        tmask = (unsigned)__builtin_amdgcn_readfirstlane(*s_tmask);
+      }
     }
     if (FwdMap<D, MAP>::ON && remap) {
       build_table<D::R, D::TK, D::SJ>(cop, [&](int i, int tk, int g, int c, int sv) {
@@ -528,7 +556,8 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
     });
   }
   __syncthreads();
-  fwd_rows_tje<D, D::TJ>(tje, row, N, (flags & KRON_RELU_OUT) != 0, x, y, bop, cop, xa, jr, bb, lane, g, c);
+  fwd_rows_tje<D, D::TJ, FwdMap<D, MAP>::ON>(tje, row, N, (flags & KRON_RELU_OUT) != 0, x, y, bop, cop, xa, jr, bb,
+                                             lane, g, c, tmask);
 }
 
 #endif  // forward kernels

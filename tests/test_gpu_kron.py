@@ -117,6 +117,39 @@ def test_zero_rows_of_A_without_S():
     compare_layer(inp, sparse_rows=True)
 
 
+def _zero_blocks(S, blocks):
+    for tj, tk in blocks:
+        S[16 * tj:16 * tj + 16, 16 * tk:16 * tk + 16] = 0.0
+
+
+@pytest.mark.parametrize("case", ["diagonal", "one_block", "rows_and_block", "all_zero"])
+def test_block_sparse_S(case):
+    """S with whole 16 x 16 blocks zero (the forward's tile mask, taken in the row map's
+    order, skips the stage-2 steps over them): block-diagonal S, one zero block, zero rows
+    that are not block-aligned together with a zero block, and S = 0.  With and without the
+    hint, against the oracle."""
+    inp = kron_inputs(47, 1031, 32, 32, 32, 32, 4, s_mode="uniform", bias_mode="normal")
+    if case == "diagonal":
+        _zero_blocks(inp.S, [(0, 1), (1, 0)])
+    elif case == "one_block":
+        _zero_blocks(inp.S, [(0, 1)])
+    elif case == "rows_and_block":
+        inp.S[[2, 5, 7, 11, 13, 17, 19, 23, 29], :] = 0.0
+        _zero_blocks(inp.S, [(1, 1)])
+    else:
+        inp.S[:] = 0.0
+    compare_layer(inp, sparse_rows=True)
+    compare_layer(inp)
+
+
+@pytest.mark.parametrize("shape", [(32, 64, 24, 48, 2), (64, 32, 48, 24, 2)])
+def test_block_sparse_S_gpt2_shapes(shape):
+    """The tile mask on rectangular shapes (2 x 4 and 4 x 2 tiles of C), seeded zero blocks."""
+    p, q, m, n, r = shape
+    inp = kron_inputs(48, 517, p, q, m, n, r, s_mode="blocks_zeroed", zero_frac=0.5, bias_mode="normal")
+    compare_layer(inp, sparse_rows=True)
+
+
 @pytest.mark.parametrize("frac,relu_mask,want_dx", [(0.75, False, True), (0.75, True, True), (0.5, False, False),
                                                      (15 / 32, True, True), (1.0, False, True), (0.25, False, True)])
 def test_row_sparse_S_backward_variants(frac, relu_mask, want_dx):

@@ -103,7 +103,9 @@ def kron_inputs(seed: int, N: int, p: int, q: int, m: int, n: int, r: int, *,
     (U(0,1)), "uniform_zeroed" (U(0,1) with exactly round(zero_frac*p*q) entries set
     to 0 at positions chosen by a seeded permutation), "rows_zeroed" (U(0,1) with
     round(zero_frac*p) whole rows set to 0 at seeded positions: the structured sparsity
-    an l1-pruned mask can leave), "integer" (small integers, for exact-arithmetic tests).
+    an l1-pruned mask can leave), "blocks_zeroed" (U(0,1) with round(zero_frac * number of
+    16 x 16 blocks) whole blocks set to 0 at seeded positions; p and q multiples of 16),
+    "integer" (small integers, for exact-arithmetic tests).
     bias_mode: "none", "zeros", "normal".
     """
     nx, nS, nA, nB, nb, ndy = names
@@ -113,7 +115,7 @@ def kron_inputs(seed: int, N: int, p: int, q: int, m: int, n: int, r: int, *,
     S = None
     if s_mode == "ones":
         S = np.ones((p, q), np.float32)
-    elif s_mode in ("uniform", "uniform_zeroed", "rows_zeroed"):
+    elif s_mode in ("uniform", "uniform_zeroed", "rows_zeroed", "blocks_zeroed"):
         g = _rng(seed, nS)
         S = f32(g.uniform(0.0, 1.0, (p, q)))
         if s_mode == "uniform_zeroed":
@@ -123,6 +125,10 @@ def kron_inputs(seed: int, N: int, p: int, q: int, m: int, n: int, r: int, *,
         elif s_mode == "rows_zeroed":
             rows = g.permutation(p)[:int(round(zero_frac * p))]
             S[rows, :] = 0.0
+        elif s_mode == "blocks_zeroed":
+            bj, bk = p // 16, q // 16
+            for blk in g.permutation(bj * bk)[:int(round(zero_frac * bj * bk))]:
+                S[16 * (blk // bk):16 * (blk // bk) + 16, 16 * (blk % bk):16 * (blk % bk) + 16] = 0.0
     elif s_mode != "none":
         raise ValueError(s_mode)
     bias = None
