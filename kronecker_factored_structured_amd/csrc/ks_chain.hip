@@ -302,7 +302,8 @@ __global__ __launch_bounds__(kCmThreads) void ks_chain_mfma_kernel(ChainArgs A, 
 // with each slot's row and output offsets; a tile then costs only LDS reads, products and
 // LDS writes.  Same tiles, buffers, task split and operand roles as ks_chain_mfma_kernel.
 // Slot j of factor f for wavefront w: its values in registers (lane 16g + i: beta 4s + g,
-// gamma tile + i) and a descriptor {row offset, output offset, gamma tile, valid} in LDS,
+// gamma tile + i) and a descriptor {row offset, output offset, gamma values left (c - first
+// gamma of the tile; 0 for an unused slot), 0} in LDS,
 // the same for every lane of the wavefront.
 template <int TPW, int SK, typename TIn>
 __device__ __forceinline__ void load_slots(const ChainFactor& f, int w, float* vr, int4* desc) {
@@ -315,7 +316,7 @@ __device__ __forceinline__ void load_slots(const ChainFactor& f, int w, float* v
     const bool valid = task < ntask;
     const int ad = task / nct, ct = task - ad * nct, al = ad / d, de = ad - al * d;
     const int ga0 = 16 * ct;
-    if (lane == 0) desc[j] = valid ? make_int4(al * b * d + de, (al * c + ga0) * d + de, ga0, 1) : make_int4(0, 0, 0, 0);
+    if (lane == 0) desc[j] = valid ? make_int4(al * b * d + de, (al * c + ga0) * d + de, c - ga0, 0) : make_int4(0, 0, 0, 0);
 #pragma unroll
     for (int sk = 0; sk < SK; ++sk) {
       const int be = 4 * sk + g;
@@ -330,8 +331,8 @@ __device__ __forceinline__ void load_slots(const ChainFactor& f, int w, float* v
 constexpr int kCmBatch = 16;   // row values (slots x beta steps) read per batch
 
 template <int TPW, int SK>
-__device__ __forceinline__ void run_slots(const float* vr, const int4* __restrict__ desc, int ntask, int w, int nks,
-                                          int c, int d, int LD, const float* __restrict__ in,
+__device__ __forceinline__ void run_slots(const float* vr, const int4* __restrict__ desc, int nks,
+                                          int d, int LD, const float* __restrict__ in,
                                           float* __restrict__ out, float* __restrict__ dummy) {
   const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
   const int d4 = 4 * d, lx = li * LD + g * d, lo = li * LD + 4 * g * d;
@@ -346,8 +347,17 @@ __device__ __forceinline__ void run_slots(const float* vr, const int4* __restric
 #pragma unroll
     for (int jj = 0; jj < NB; ++jj) {
       const int j = j0 + jj;
-      const int4 ds = desc[j];
-      const bool live = w + kCmWaves * j < ntask && ds.z + 4 * g < c;
+      // The descriptor is the same for every lane.  With short beta loops it is moved to
+      // scalar registers, so that the selects below stay selects: a select fed by a load
+      // becomes a branch around the load, which splits the batch and makes each slot wait
+      // for its own descriptor.  With 8 or more beta steps per slot (one or two slots per
+      // batch) the extra scalar moves cost more than they save.
+      const int4 dv = desc[j];
+      int3 ds = make_int3(dv.x, dv.y, dv.z);
+      if constexpr (SK < 8)
+        ds = make_int3(__builtin_amdgcn_readfirstlane(dv.x), __builtin_amdgcn_readfirstlane(dv.y),
+                       __builtin_amdgcn_readfirstlane(dv.z));
+      const bool live = 4 * g < ds.z;
       op[jj] = live ? out + lo + ds.y : dummy + lane;
       st[jj] = live ? d : 64;
 #pragma unroll
@@ -392,13 +402,11 @@ __global__ __launch_bounds__(kCmThreads) void ks_chain_reg_kernel(ChainArgs A, i
   load_slots<T0, S0, TIn>(A.f[0], w, v0, d0);
   if constexpr (NF > 1) load_slots<T1, S1, TIn>(A.f[1], w, v1, d1);
   if constexpr (NF > 2) load_slots<T2, S2, TIn>(A.f[2], w, v2, d2);
-  int nt[3], nk[3], cc[3], dd[3];
+  int nk[3], dd[3];
 #pragma unroll
   for (int fi = 0; fi < 3; ++fi) {
     const int f = fi < NF ? fi : 0;
-    nt[fi] = A.f[f].a * A.f[f].d * ((A.f[f].c + 15) / 16);
     nk[fi] = (A.f[f].b + 3) / 4;
-    cc[fi] = A.f[f].c;
     dd[fi] = A.f[f].d;
   }
   float4 pre[kCmPre];
@@ -445,14 +453,14 @@ __global__ __launch_bounds__(kCmThreads) void ks_chain_reg_kernel(ChainArgs A, i
   for (; tile < ntiles; tile += gridDim.x) {
     if (tile + gridDim.x < ntiles) fetch(tile + gridDim.x);
     __syncthreads();
-    run_slots<T0, S0>(v0, d0, nt[0], w, nk[0], cc[0], dd[0], LD, b0, b1, dummy);
+    run_slots<T0, S0>(v0, d0, nk[0], dd[0], LD, b0, b1, dummy);
     __syncthreads();
     if constexpr (NF > 1) {
-      run_slots<T1, S1>(v1, d1, nt[1], w, nk[1], cc[1], dd[1], LD, b1, b0, dummy);
+      run_slots<T1, S1>(v1, d1, nk[1], dd[1], LD, b1, b0, dummy);
       __syncthreads();
     }
     if constexpr (NF > 2) {
-      run_slots<T2, S2>(v2, d2, nt[2], w, nk[2], cc[2], dd[2], LD, b0, b1, dummy);
+      run_slots<T2, S2>(v2, d2, nk[2], dd[2], LD, b0, b1, dummy);
       __syncthreads();
     }
     store_tile(A.y, (NF & 1) ? b1 : b0, LD, tile, A.N, wl, ql);
