@@ -165,13 +165,19 @@ __global__ __launch_bounds__((FB<D>::NT)) void fwd_bf16_kernel(int64_t N, uint32
   for (int e = tid; e < F::TAB_C; e += F::NT) {   // e = ((i*TK + tk)*KC2 + s)*64 + lane
     const int ln = e & 63, rest = e >> 6, s = rest % KC2, tk = (rest / KC2) % D::TK, i = rest / (KC2 * D::TK);
     const int k = 16 * tk + (ln & 15);
-    O2 v;
+    // every load unconditional (S absent: A stands in, and the factor is 1), so that the
+    // loads of all W2 values go out before the first wait
+    const uint16_t* Sp = Sm ? Sm : A;
+    uint16_t av[W2], sv[W2];
 #pragma unroll
     for (int u = 0; u < W2; ++u) {
       const int jk = k_acc<W2>(s, ln >> 4, u) * D::Q + k;
-      const float av = bf2f(A[i * D::PQ + jk]);
-      v[u] = (short)f2bf(Sm ? bf2f(Sm[jk]) * av : av);
+      av[u] = A[i * D::PQ + jk];
+      sv[u] = Sp[jk];
     }
+    O2 v;
+#pragma unroll
+    for (int u = 0; u < W2; ++u) v[u] = (short)f2bf((Sm ? bf2f(sv[u]) : 1.f) * bf2f(av[u]));
     *reinterpret_cast<O2*>(tabC + e * W2) = v;
   }
   // bias of the lane's outputs: Y^T[b = 16tb + 4g + v][k = 16tk + c] -> bias[k*N + b]
@@ -412,10 +418,11 @@ __global__ __launch_bounds__((BB<D, RPI>::NT)) void bwd_bf16_kernel(int64_t N, c
   }
   for (int e = tid; e < R * D::PQ / 2; e += NT) {
     const int i = e / (D::PQ / 2), r = 2 * (e % (D::PQ / 2)), j = r / D::Q, k = r % D::Q;
+    // (both loads unconditional: S absent, A stands in and the factor is 1)
     const uint32_t av = *reinterpret_cast<const uint32_t*>(A + i * D::PQ + r);
+    const uint32_t sv = *reinterpret_cast<const uint32_t*>((Sm ? Sm : A) + r);
     float a0 = bf2f((uint16_t)(av & 0xffffu)), a1 = bf2f((uint16_t)(av >> 16));
     if (Sm) {
-      const uint32_t sv = *reinterpret_cast<const uint32_t*>(Sm + r);
       a0 *= bf2f((uint16_t)(sv & 0xffffu));
       a1 *= bf2f((uint16_t)(sv >> 16));
     }

@@ -164,12 +164,14 @@ struct Dims {
   static constexpr int GS = 16 * TB * LDGT;
   static constexpr int PW = R * M * N + R * P * Q + P * Q + Q * N;   // see partial_width()
   static constexpr int PWW = R * M * N + R * P * Q + Q * N;           // one wavefront's sums
-  // the forward stages the raw factors next to its tables when they fit, else builds the
-  // tables straight from global memory
+  // the forward stages the raw factors next to its tables when they fit, else one rank's
+  // raw factors at a time (FWD_RAW1), else builds the tables straight from global memory
   static constexpr bool FWD_RAW = (size_t)(BOP + COPF + RAW) * 4 <= kMaxLds;
+  static constexpr int RAW1 = M * N + (P * Q + 3) / 4 * 4;
+  static constexpr bool FWD_RAW1 = !FWD_RAW && (P * Q) % 4 == 0 && (size_t)(BOP + COPF + RAW1) * 4 <= kMaxLds;
   // the forward's row map (FwdMap): a 64-bit row mask per wavefront and the map (TJ*16 ints)
   static constexpr int FWD_MAP = (2 * kWaves + TJ * 16 + 1 + 3) / 4 * 4;   // + the tile mask
-  static constexpr int FWD_FLOATS = BOP + COPF + (FWD_RAW ? RAW + FWD_MAP : 0);
+  static constexpr int FWD_FLOATS = BOP + COPF + (FWD_RAW ? RAW + FWD_MAP : (FWD_RAW1 ? RAW1 : 0));
   static constexpr int BWD_TABLES = BOP + COPG + BOPX;
   static constexpr int BWD_SCRATCH = (kWaves * GS > RAW) ? kWaves * GS : RAW;
   static constexpr int BWD_MAIN = BWD_TABLES + BWD_SCRATCH;
@@ -542,6 +544,50 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
       build_table<D::R, D::TK, D::SJ>(cop, [&](int i, int tk, int g, int c, int sv) {
         return rawC<D>(rC, i, 16 * (sv / 4) + 4 * g + (sv % 4), 16 * tk + c);
       });
+    }
+  } else if constexpr (D::FWD_RAW1) {
+    // One rank at a time: B_i and C_i = S o A_i staged with 16-byte loads, then that rank's
+    // slices of the tables built from LDS (the tables are rank-major).
+    float* rB = cop + D::COPF;
+    float* rC = rB + D::M * D::N;
+    constexpr int NB4 = D::M * D::N / 4, NC4 = D::P * D::Q / 4;
+    constexpr int KB = (NB4 + kThreads - 1) / kThreads, KC = (NC4 + kThreads - 1) / kThreads;
+    const f4* S4 = reinterpret_cast<const f4*>(Sm ? Sm : A);   // (A stands in without S)
+    for (int i = 0; i < D::R; ++i) {
+      const f4* B4 = reinterpret_cast<const f4*>(B + i * D::M * D::N);
+      const f4* A4 = reinterpret_cast<const f4*>(A + i * D::P * D::Q);
+      f4 b[KB], a[KC], m[KC];
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int e = threadIdx.x + k * kThreads;
+        if (NB4 % kThreads == 0 || e < NB4) b[k] = B4[e];
+      }
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        const int e = threadIdx.x + k * kThreads;
+        if (NC4 % kThreads == 0 || e < NC4) {
+          a[k] = A4[e];
+          m[k] = S4[e];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int e = threadIdx.x + k * kThreads;
+        if (NB4 % kThreads == 0 || e < NB4) reinterpret_cast<f4*>(rB)[e] = b[k];
+      }
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        const int e = threadIdx.x + k * kThreads;
+        if (NC4 % kThreads == 0 || e < NC4) reinterpret_cast<f4*>(rC)[e] = Sm ? a[k] * m[k] : a[k];
+      }
+      __syncthreads();
+      build_table<1, D::TB, D::SA>(bop + i * D::TB * 64 * D::SA, [&](int, int tb, int g, int c, int s) {
+        return rawB<D>(rB, 0, g * D::SA + s, 16 * tb + c);
+      });
+      build_table<1, D::TK, D::SJ>(cop + i * D::TK * 64 * D::SJ, [&](int, int tk, int g, int c, int sv) {
+        return rawC<D>(rC, 0, 16 * (sv / 4) + 4 * g + (sv % 4), 16 * tk + c);
+      });
+      __syncthreads();   // the staging area is reused by the next rank
     }
   } else {
     build_table<D::R, D::TB, D::SA>(bop, [&](int i, int tb, int g, int c, int s) {
