@@ -408,7 +408,14 @@ __device__ __forceinline__ void fwd_rows(int64_t row, int64_t N, bool relu, cons
 #pragma unroll
             for (int v = 0; v < 4; ++v) o[v] = o[v] > 0.f ? o[v] : 0.f;
           }
-          __builtin_nontemporal_store(o, reinterpret_cast<f4*>(yr + k * D::N + b0));   // y is not read back
+          // y is not read back: non-temporal stores, except at r = 1, where a row's few
+          // products leave the kernel closer to the memory bound and ordinary stores,
+          // combined in L2, were measured faster (GPT-2 pair at r = 1: 31.4 -> 28.5 and
+          // 29.1 -> 28.5 us; at r = 4 and at the headline shape they were 1% slower)
+          if constexpr (D::R == 1)
+            *reinterpret_cast<f4*>(yr + k * D::N + b0) = o;
+          else
+            __builtin_nontemporal_store(o, reinterpret_cast<f4*>(yr + k * D::N + b0));
         }
       }
 #pragma unroll

@@ -192,6 +192,14 @@ def test_gpt2_ffn_layers(r):
     compare_layer(down)
 
 
+@pytest.mark.parametrize("shape", [(32, 64, 24, 48), (64, 32, 48, 24)])
+def test_gpt2_rank8_without_S_ragged(shape):
+    """r = 8 at the GPT-2 pair, where the forward stages one rank's raw factors at a time;
+    no S (A alone forms C_i), a ragged row count, bias."""
+    p, q, m, n = shape
+    compare_layer(kron_inputs(35, 1001, p, q, m, n, 8, s_mode="none", bias_mode="normal"))
+
+
 @pytest.mark.parametrize("case", [(3, 5, 7, 2, 3), (1, 1, 4, 6, 2), (6, 4, 1, 1, 5), (5, 3, 2, 9, 16),
                                   (2, 7, 3, 3, 1), (33, 17, 5, 3, 2)])
 def test_odd_shapes_with_bias_and_S(case):
