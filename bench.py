@@ -129,7 +129,7 @@ def cpu_baseline(inp, seconds: float):
 class Layer:
     """Device tensors and preallocated outputs of one Kronecker layer workload."""
 
-    def __init__(self, inp, dev, sparse_rows=False):
+    def __init__(self, inp, dev, sparse_rows=False, save_z=False):
         import torch
         import kronecker_factored_structured_amd as K
         self.K = K
@@ -144,13 +144,16 @@ class Layer:
                          dbias=None if self.bias is None else torch.empty_like(self.bias))
         shape = K.layer_shape(sh.N, self.S, self.A, self.B)
         self.ws = torch.empty(K.kron_linear_bwd_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+        # save_z: the forward keeps Z_i = X B_i for the backward (None where the shape has no such path)
+        self.zc = K.new_zcache(self.x, self.S, self.A, self.B) if save_z else None
 
     def fwd(self):
-        self.K.kron_linear_fwd(self.x, self.S, self.A, self.B, self.bias, out=self.y, sparse_rows=self.sparse_rows)
+        self.K.kron_linear_fwd(self.x, self.S, self.A, self.B, self.bias, out=self.y, sparse_rows=self.sparse_rows,
+                               zcache=self.zc)
 
     def bwd(self):
         self.K.kron_linear_bwd(self.x, self.S, self.A, self.B, self.dy, workspace=self.ws, outs=self.outs,
-                               sparse_rows=self.sparse_rows)
+                               sparse_rows=self.sparse_rows, zcache=self.zc)
 
 
 class LayerBf16:
@@ -270,10 +273,22 @@ def run_headline(args, dev):
     sh = inp.shape
     N, p, q, m, n, r = sh.N, sh.p, sh.q, sh.m, sh.n, sh.r
     nnz = int(np.count_nonzero(inp.S))
-    L = Layer(inp, dev)
-    log(f"[bench] headline: warmup {args.warmup}, timing {args.steps} steps")
+    # the timed step saves Z_i = X B_i in the forward for the backward (kron_linear_fwd_save /
+    # kron_linear_bwd_saved); the recomputing pair (kron_linear_fwd / kron_linear_bwd) is
+    # timed beside it
+    L = Layer(inp, dev, save_z=not args.recompute_z)
+    log(f"[bench] headline ({'recomputed' if L.zc is None else 'saved'} Z): warmup {args.warmup}, "
+        f"timing {args.steps} steps")
     ms_step, wall_ms = timed(lambda: (L.fwd(), L.bwd()), args.steps, args.warmup)
     t_fwd, t_bwd, med_fwd, med_bwd, med_step = split_times(L, args.steps, medians=True)
+    other = None
+    if L.zc is not None:
+        L.zc = None
+        log(f"[bench] headline, recomputed Z: timing {args.steps} steps")
+        ms_r, _ = timed(lambda: (L.fwd(), L.bwd()), args.steps, args.warmup)
+        tf_r, tb_r = split_times(L, args.steps)
+        other = {"path": "kron_linear_fwd + kron_linear_bwd (Z recomputed in the backward)",
+                 "ms_per_step": round(ms_r, 5), "t_fwd_us": round(tf_r * 1e6, 2), "t_bwd_us": round(tb_r * 1e6, 2)}
     ff, fb, bf, bb = work_per_row(p, q, m, n, r, nnz)
     t_roof = max(N * (ff + fb) / (PEAK_FP32_TFLOPS * 1e12), N * (bf + bb) / (PEAK_HBM_GBS * 1e9))
     achieved = N * fb / t_bwd / 1e12
@@ -282,7 +297,10 @@ def run_headline(args, dev):
                 "traffic": measured_traffic(),
                 "kernel": "kron_linear_bwd (main kernel + fixed-order partial-sum reduction)",
                 "t_us": round(t_bwd * 1e6, 2), "flop_per_row": fb, "rows": N,
-                "algorithmic_bytes": N * bb}
+                "algorithmic_bytes": N * bb,
+                "z_saved": other is not None,
+                # the saved Z, written by the forward and read by the backward (not algorithmic)
+                "zcache_bytes": N * r * p * n * 4 if other is not None else 0}
     value = N / (ms_step * 1e-3)
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "rows/s", "n_gpus": 1,
@@ -303,6 +321,7 @@ def run_headline(args, dev):
         "median_us": {"fwd": round(med_fwd * 1e6, 2), "bwd": round(med_bwd * 1e6, 2),
                       "fwd_bwd": round(med_step * 1e6, 2)},
         "wall_ms_per_step": round(wall_ms, 5),
+        "recompute_path": other,
         "kernel_source_sha": kernel_source_sha(),
         "settle_seconds": args.settle_seconds,
     }
@@ -680,6 +699,8 @@ def main():
     ap.add_argument("--workload", default="headline",
                     choices=("headline", "headline_bf16", "tiny", "mlp_step", "gpt2_ffn", "gpt2_ffn_bf16", "ks", "ks_bwd", "chain", "van_loan", "sweep", "small_blocks", "sparse_s"))
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--recompute-z", action="store_true",
+                    help="headline: time the recomputing pair only (no saved Z)")
     ap.add_argument("--settle-seconds", type=float, default=1.0,
                     help="untimed running before the warmup steps, for the GPU clock to ramp up")
     args = ap.parse_args()

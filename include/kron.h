@@ -146,6 +146,43 @@ kron_status_t kron_linear_bwd_noalloc(const kron_shape_t* shape, const float* x,
                                       hipStream_t stream);
 
 /*
+ * Saved-intermediate variant of the layer: the forward also stores Z_{n,i} = X_n B_i (the
+ * first contraction of the tutorial's "The vec trick without the loop", which the
+ * tutorial's "Takeaways" recompute in the backward) for the first ranks, and the backward
+ * reads those back instead of recomputing them.  That trades HBM traffic (8 KB per row,
+ * written once and read once, for the 1024 x 1024 layer at m = 32, r = 4: Z of ranks 0
+ * and 1) for a tenth of the backward's products; saving more ranks makes the forward
+ * HBM-bound and the pair slower.
+ *
+ * kron_linear_zcache_bytes: bytes of the cache for shape->N rows; 0 when the shape has no
+ *   saved-intermediate path (then use kron_linear_fwd / kron_linear_bwd) or N == 0.
+ *   Available for p = q = m = n = 32 with r = 4.
+ *
+ * kron_linear_fwd_save: kron_linear_fwd (same arguments, checks and y, bit for bit) that
+ *   also fills zcache [zcache_bytes >= kron_linear_zcache_bytes(shape)], 16-byte aligned,
+ *   disjoint from every input and from y.  The cache's layout is private to the library.
+ *
+ * kron_linear_bwd_saved: kron_linear_bwd (same arguments, checks and results up to
+ *   rounding) that reads the saved Z from zcache.  zcache must hold what
+ *   kron_linear_fwd_save wrote for the same shape, x and B (A, S and bias may have changed
+ *   since: Z depends on x and B only); nothing checks this, and a stale cache gives wrong
+ *   dS and dA.
+ *
+ * Both return KRON_E_UNSUPPORTED for a shape without the path, KRON_E_ARG with
+ * KRON_SPARSE_ROWS, KRON_E_WORKSPACE for a short cache and KRON_E_NULL for a missing one
+ * (N > 0).
+ */
+size_t kron_linear_zcache_bytes(const kron_shape_t* shape);
+kron_status_t kron_linear_fwd_save(const kron_shape_t* shape, const float* x, const float* S,
+                                   const float* A, const float* B, const float* bias, float* y,
+                                   float* zcache, size_t zcache_bytes, hipStream_t stream);
+kron_status_t kron_linear_bwd_saved(const kron_shape_t* shape, const float* x, const float* S,
+                                    const float* A, const float* B, const float* dy,
+                                    const float* zcache, size_t zcache_bytes,
+                                    float* dx, float* dS, float* dA, float* dB, float* dbias,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * bf16 layer (mixed precision; the tutorial's "Takeaways" name a mixed-precision rerun as
  * the next step).  Same operation as kron_linear_fwd / kron_linear_bwd with bf16 storage
  * (bfloat16 bit patterns) for x, S, A, B, bias, dy and the outputs y and dx; products

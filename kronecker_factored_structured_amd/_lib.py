@@ -39,7 +39,8 @@ EXPORTS = (
     "kron_linear_bwd_bf16_workspace_bytes", "kron_linear_fwd_bf16", "kron_linear_bwd_bf16",
     "ks_matmul_out", "ks_matmul_bwd_workspace_bytes", "ks_matmul_bwd", "ks_chain",
     "kron_van_loan_workspace_bytes", "kron_van_loan", "kron_relu_bwd", "kron_l1_penalty",
-    "kron_l1_penalty_grad", "kron_linear_bwd_noalloc",
+    "kron_l1_penalty_grad", "kron_linear_bwd_noalloc", "kron_linear_zcache_bytes", "kron_linear_fwd_save",
+    "kron_linear_bwd_saved",
 )
 
 KRON_NOALLOC_SCRATCH_BYTES = 32 << 20
@@ -85,6 +86,9 @@ def lib() -> ctypes.CDLL:
             "kron_linear_bwd_workspace_bytes": (sz, [shp]),
             "kron_linear_fwd": (i32, [shp, vp, vp, vp, vp, vp, vp, vp]),
             "kron_linear_bwd": (i32, [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "kron_linear_zcache_bytes": (sz, [shp]),
+            "kron_linear_fwd_save": (i32, [shp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "kron_linear_bwd_saved": (i32, [shp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, sz, vp]),
             "ks_matmul": (i32, [i64, i32, i32, i32, i32, i32, vp, vp, vp, vp]),
             "ks_matmul_out": (i32, [i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]),
             "ks_matmul_bwd_workspace_bytes": (ctypes.c_size_t, [i64, i32, i32, i32, i32, i32]),

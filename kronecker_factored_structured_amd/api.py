@@ -97,12 +97,38 @@ def kron_linear_bwd_workspace_bytes(shape: KronShape) -> int:
     return int(_lib.lib().kron_linear_bwd_workspace_bytes(ctypes.byref(shape)))
 
 
+def kron_linear_zcache_bytes(shape: KronShape) -> int:
+    """Bytes of the saved Z_i = X B_i cache for shape.N rows (0: no saved path for the shape)."""
+    return int(_lib.lib().kron_linear_zcache_bytes(ctypes.byref(shape)))
+
+
+def new_zcache(x: torch.Tensor, S: Optional[torch.Tensor], A: torch.Tensor, B: torch.Tensor) -> Optional[torch.Tensor]:
+    """An uninitialised cache for kron_linear_fwd(..., zcache=) / kron_linear_bwd(..., zcache=)
+    over x's rows, or None when the layer's shape has no saved-intermediate path."""
+    nb = kron_linear_zcache_bytes(layer_shape(x.shape[0], S, A, B))
+    return torch.empty(nb // 4, dtype=torch.float32, device=x.device) if nb > 0 else None
+
+
+def _zcache_checks(zcache: torch.Tensor, shape: KronShape, device) -> int:
+    _dev(zcache, "zcache")
+    if zcache.device != device:
+        raise ValueError(f"zcache is on {zcache.device}, expected {device}")
+    need = kron_linear_zcache_bytes(shape)
+    if need == 0 and shape.N > 0:
+        raise ValueError("this layer shape has no saved-intermediate path (kron_linear_zcache_bytes is 0)")
+    if zcache.numel() * 4 < need:
+        raise ValueError(f"zcache holds {zcache.numel() * 4} bytes, {need} needed")
+    return zcache.numel() * 4
+
+
 def kron_linear_fwd(x: torch.Tensor, S: Optional[torch.Tensor], A: torch.Tensor, B: torch.Tensor,
                     bias: Optional[torch.Tensor] = None, relu: bool = False,
-                    out: Optional[torch.Tensor] = None, sparse_rows: bool = False) -> torch.Tensor:
+                    out: Optional[torch.Tensor] = None, sparse_rows: bool = False,
+                    zcache: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y = x W + bias with W = sum_i kron(S o A_i, B_i) (optionally ReLU-ed).  sparse_rows:
     S is expected to have whole rows zero; the forward then skips the 16-row tiles of C that
-    hold only such rows (KRON_SPARSE_ROWS)."""
+    hold only such rows (KRON_SPARSE_ROWS).  zcache (from new_zcache): also save Z_i = X B_i
+    there for kron_linear_bwd(..., zcache=)."""
     for t, nm in ((x, "x"), (S, "S"), (A, "A"), (B, "B")):
         _dev(t, nm)
     shape = layer_shape(x.shape[0], S, A, B, (KRON_RELU_OUT if relu else 0) | (KRON_SPARSE_ROWS if sparse_rows else 0))
@@ -110,6 +136,12 @@ def kron_linear_fwd(x: torch.Tensor, S: Optional[torch.Tensor], A: torch.Tensor,
     _need(bias, "bias", (shape.q * shape.n,), device=x.device)
     _need(out, "out", (x.shape[0], shape.q * shape.n), device=x.device)
     y = out if out is not None else torch.empty(x.shape[0], shape.q * shape.n, device=x.device)
+    if zcache is not None:
+        nb = _zcache_checks(zcache, shape, x.device)
+        check("kron_linear_fwd_save", _lib.lib().kron_linear_fwd_save(
+            ctypes.byref(shape), _ptr(x), _ptr(S), _ptr(A), _ptr(B), _ptr(bias), _ptr(y), _ptr(zcache),
+            ctypes.c_size_t(nb), _stream(x.device)))
+        return y
     check("kron_linear_fwd", _lib.lib().kron_linear_fwd(
         ctypes.byref(shape), _ptr(x), _ptr(S), _ptr(A), _ptr(B), _ptr(bias), _ptr(y), _stream(x.device)))
     return y
@@ -118,9 +150,12 @@ def kron_linear_fwd(x: torch.Tensor, S: Optional[torch.Tensor], A: torch.Tensor,
 def kron_linear_bwd(x: torch.Tensor, S: Optional[torch.Tensor], A: torch.Tensor, B: torch.Tensor,
                     dy: torch.Tensor, want_dx: bool = True, want_dbias: bool = True,
                     relu_mask: bool = False, workspace: Optional[torch.Tensor] = None,
-                    outs: Optional[dict] = None, sparse_rows: bool = False) -> dict:
+                    outs: Optional[dict] = None, sparse_rows: bool = False,
+                    zcache: Optional[torch.Tensor] = None) -> dict:
     """Gradients of sum(dy * (x W + bias)): dict(dx, dS, dA, dB, dbias) (None where not asked).
-    sparse_rows: the KRON_SPARSE_ROWS hint (S expected to have whole rows zero)."""
+    sparse_rows: the KRON_SPARSE_ROWS hint (S expected to have whole rows zero).  zcache: the
+    cache a kron_linear_fwd(..., zcache=) call filled for the same x and B; Z_i = X B_i is
+    then read from it instead of recomputed."""
     for t, nm in ((x, "x"), (S, "S"), (A, "A"), (B, "B"), (dy, "dy")):
         _dev(t, nm)
     shape = layer_shape(x.shape[0], S, A, B,
@@ -136,6 +171,13 @@ def kron_linear_bwd(x: torch.Tensor, S: Optional[torch.Tensor], A: torch.Tensor,
     dbias = o.get("dbias") if "dbias" in o else (
         torch.empty(shape.q * shape.n, device=dev) if want_dbias else None)
     workspace = _workspace(workspace, kron_linear_bwd_workspace_bytes(shape), dev)
+    if zcache is not None:
+        nb = _zcache_checks(zcache, shape, dev)
+        check("kron_linear_bwd_saved", _lib.lib().kron_linear_bwd_saved(
+            ctypes.byref(shape), _ptr(x), _ptr(S), _ptr(A), _ptr(B), _ptr(dy), _ptr(zcache), ctypes.c_size_t(nb),
+            _ptr(dx), _ptr(dS), _ptr(dA), _ptr(dB), _ptr(dbias), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+            _stream(dev)))
+        return dict(dx=dx, dS=dS, dA=dA, dB=dB, dbias=dbias)
     check("kron_linear_bwd", _lib.lib().kron_linear_bwd(
         ctypes.byref(shape), _ptr(x), _ptr(S), _ptr(A), _ptr(B), _ptr(dy), _ptr(dx), _ptr(dS), _ptr(dA),
         _ptr(dB), _ptr(dbias), _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(dev)))

@@ -143,6 +143,23 @@ size_t bwd_workspace(const kron_shape_t* s) {
 
 }  // namespace
 
+// Bytes of the Z cache for N rows (the saved ranks' Z_i = X B_i, p x n each, per row).
+size_t zcache_need(const kron_shape_t* s) {
+  return (size_t)s->N * kron::mfma_zcache_row_floats(s->p, s->q, s->m, s->n, s->r) * sizeof(float);
+}
+
+// The cache's own checks (the shape itself is checked by the caller first).
+kron_status_t zcache_checks(const kron_shape_t* s, const void* zc, size_t zc_bytes) {
+  if (kron::mfma_zcache_row_floats(s->p, s->q, s->m, s->n, s->r) == 0)
+    return fail(KRON_E_UNSUPPORTED, "no saved-intermediate path for p=%d q=%d m=%d n=%d r=%d", s->p, s->q, s->m,
+                s->n, s->r);
+  if (s->flags & KRON_SPARSE_ROWS) return fail(KRON_E_ARG, "the sparse-row hint has no saved-intermediate path");
+  if (zc_bytes < zcache_need(s))
+    return fail(KRON_E_WORKSPACE, "zcache of %zu bytes given, %zu needed", zc_bytes, zcache_need(s));
+  if (!aligned16(zc)) return fail(KRON_E_ALIGN, "zcache is not 16-byte aligned (%p)", zc);
+  return KRON_OK;
+}
+
 extern "C" {
 
 int32_t kron_abi_version(void) { return KRON_ABI_VERSION; }
@@ -181,31 +198,58 @@ size_t kron_linear_bwd_workspace_bytes(const kron_shape_t* s) {
   return bwd_workspace(s);
 }
 
-kron_status_t kron_linear_fwd(const kron_shape_t* s, const float* x, const float* S, const float* A,
-                        const float* B, const float* bias, float* y, hipStream_t stream) {
+size_t kron_linear_zcache_bytes(const kron_shape_t* s) {
+  if (kron_linear_check(s) != KRON_OK || kron::mfma_zcache_row_floats(s->p, s->q, s->m, s->n, s->r) == 0) return 0;
+  return zcache_need(s);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The forward, writing the Z cache as well when zc is given (zc_bytes checked here).
+kron_status_t fwd_run(const kron_shape_t* s, const float* x, const float* S, const float* A, const float* B,
+                      const float* bias, float* y, float* zc, size_t zc_bytes, hipStream_t stream) {
   kron_status_t st = kron_linear_check(s);
   if (st != KRON_OK) return st;
   if (s->flags & KRON_DX_RELU_MASK) return fail(KRON_E_ARG, "KRON_DX_RELU_MASK is a backward flag");
   if (!A || !B) return fail(KRON_E_NULL, "A and B are required");
   if (s->N > 0 && (!x || !y)) return fail(KRON_E_NULL, "x and y are required when N > 0");
+  if (zc && (st = zcache_checks(s, zc, zc_bytes)) != KRON_OK) return st;
   const size_t in = (size_t)s->p * s->m, out = (size_t)s->q * s->n;
   const Range ins[5] = {{x, (size_t)s->N * in * 4, "x"},
                         {S, (size_t)s->p * s->q * 4, "S"},
                         {A, (size_t)s->r * s->p * s->q * 4, "A"},
                         {B, (size_t)s->r * s->m * s->n * 4, "B"},
                         {bias, out * 4, "bias"}};
-  const Range outs[1] = {{y, (size_t)s->N * out * 4, "y"}};
-  if ((st = check_align(ins, 5)) != KRON_OK || (st = check_align(outs, 1)) != KRON_OK) return st;
-  if ((st = check_alias(outs, 1, ins, 5)) != KRON_OK) return st;
+  const Range outs[2] = {{y, (size_t)s->N * out * 4, "y"}, {zc, zc ? zcache_need(s) : 0, "zcache"}};
+  if ((st = check_align(ins, 5)) != KRON_OK || (st = check_align(outs, 2)) != KRON_OK) return st;
+  if ((st = check_alias(outs, 2, ins, 5)) != KRON_OK) return st;
   if (s->N == 0) return ok();
   kron::LayerArgs a{};
   a.N = s->N; a.p = s->p; a.q = s->q; a.m = s->m; a.n = s->n; a.r = s->r; a.flags = s->flags;
-  a.x = x; a.S = S; a.A = A; a.B = B; a.bias = bias; a.y = y;
+  a.x = x; a.S = S; a.A = A; a.B = B; a.bias = bias; a.y = y; a.zc = zc;
   hipError_t e = kron::mfma_fwd_supported(a.p, a.q, a.m, a.n, a.r)    ? kron::launch_fwd_mfma(a, stream)
                  : kron::small_supported(a.p, a.q, a.m, a.n, a.r) ? kron::launch_fwd_small(a, stream)
                                                                   : kron::launch_fwd_generic(a, stream);
   if (e != hipSuccess) return hip_fail(e, "kron_linear_fwd launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kron_status_t kron_linear_fwd(const kron_shape_t* s, const float* x, const float* S, const float* A,
+                              const float* B, const float* bias, float* y, hipStream_t stream) {
+  return fwd_run(s, x, S, A, B, bias, y, nullptr, 0, stream);
+}
+
+kron_status_t kron_linear_fwd_save(const kron_shape_t* s, const float* x, const float* S, const float* A,
+                                   const float* B, const float* bias, float* y, float* zcache, size_t zcache_bytes,
+                                   hipStream_t stream) {
+  if (!zcache && s && s->N > 0) return fail(KRON_E_NULL, "zcache is required when N > 0");
+  return fwd_run(s, x, S, A, B, bias, y, zcache, zcache_bytes, stream);
 }
 
 }  // extern "C"
@@ -227,22 +271,24 @@ kron_status_t bwd_checks(const kron_shape_t* s, const float* x, const float* S, 
 
 kron_status_t bwd_run(const kron_shape_t* s, const float* x, const float* S, const float* A, const float* B,
                       const float* dy, float* dx, float* dS, float* dA, float* dB, float* dbias, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
+                      size_t workspace_bytes, hipStream_t stream, const float* zc = nullptr, size_t zc_bytes = 0) {
   kron_status_t st = bwd_checks(s, x, S, A, B, dy, dx, dS, dA, dB, dbias);
   if (st != KRON_OK) return st;
+  if (zc && (st = zcache_checks(s, zc, zc_bytes)) != KRON_OK) return st;
   const size_t need = bwd_workspace(s);
   if (!workspace || workspace_bytes < need)
     return fail(KRON_E_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
   if (((uintptr_t)workspace & 255u) != 0) return fail(KRON_E_ALIGN, "workspace is not 256-byte aligned");
   const size_t in = (size_t)s->p * s->m, out = (size_t)s->q * s->n;
   const size_t pq = (size_t)s->p * s->q, mn = (size_t)s->m * s->n;
-  const Range ins[6] = {{x, (size_t)s->N * in * 4, "x"},     {S, pq * 4, "S"},
+  const Range ins[7] = {{x, (size_t)s->N * in * 4, "x"},     {S, pq * 4, "S"},
                         {A, s->r * pq * 4, "A"},             {B, s->r * mn * 4, "B"},
-                        {dy, (size_t)s->N * out * 4, "dy"},  {workspace, need, "workspace"}};
+                        {dy, (size_t)s->N * out * 4, "dy"},  {workspace, need, "workspace"},
+                        {zc, zc ? zcache_need(s) : 0, "zcache"}};
   const Range outs[5] = {{dx, (size_t)s->N * in * 4, "dx"}, {dS, pq * 4, "dS"}, {dA, s->r * pq * 4, "dA"},
                          {dB, s->r * mn * 4, "dB"},         {dbias, out * 4, "dbias"}};
-  if ((st = check_align(ins, 6)) != KRON_OK || (st = check_align(outs, 5)) != KRON_OK) return st;
-  if ((st = check_alias(outs, 5, ins, 6)) != KRON_OK) return st;
+  if ((st = check_align(ins, 7)) != KRON_OK || (st = check_align(outs, 5)) != KRON_OK) return st;
+  if ((st = check_alias(outs, 5, ins, 7)) != KRON_OK) return st;
 
   kron::LayerArgs a{};
   a.N = s->N; a.p = s->p; a.q = s->q; a.m = s->m; a.n = s->n; a.r = s->r; a.flags = s->flags;
@@ -250,7 +296,10 @@ kron_status_t bwd_run(const kron_shape_t* s, const float* x, const float* S, con
   a.dx = s->N > 0 ? dx : nullptr;
   a.dS = dS; a.dA = dA; a.dB = dB; a.dbias = dbias;
   a.part = (float*)workspace;
+  a.zc = const_cast<float*>(zc);   // (read only by the backward)
   const BwdPlan pl = bwd_plan(s, a.dx != nullptr);
+  if (zc && (!pl.mfma || pl.small || pl.chunk > 0))   // (a supported shape always takes the whole-row kernel)
+    return fail(KRON_E_UNSUPPORTED, "the saved-intermediate backward needs the whole-row kernel");
   const int32_t pq32 = s->p * s->q, mn32 = s->m * s->n;
   if (pl.small) {
     hipError_t e = kron::launch_bwd_small(a, pl.sp, stream);
@@ -305,6 +354,15 @@ kron_status_t kron_linear_bwd(const kron_shape_t* s, const float* x, const float
                               const float* B, const float* dy, float* dx, float* dS, float* dA, float* dB,
                               float* dbias, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return bwd_run(s, x, S, A, B, dy, dx, dS, dA, dB, dbias, workspace, workspace_bytes, stream);
+}
+
+kron_status_t kron_linear_bwd_saved(const kron_shape_t* s, const float* x, const float* S, const float* A,
+                                    const float* B, const float* dy, const float* zcache, size_t zcache_bytes,
+                                    float* dx, float* dS, float* dA, float* dB, float* dbias, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  if (!zcache && s && s->N > 0) return fail(KRON_E_NULL, "zcache is required when N > 0");
+  return bwd_run(s, x, S, A, B, dy, dx, dS, dA, dB, dbias, workspace, workspace_bytes, stream, zcache,
+                 zcache_bytes);
 }
 
 }  // extern "C"

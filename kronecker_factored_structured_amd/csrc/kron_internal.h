@@ -68,6 +68,7 @@ struct LayerArgs {
   float* dbias;
   float* part;   // workspace: G partial rows of PW columns (column-blocked)
   int32_t dx_accumulate;   // backward: dx += this call's dX (before the optional mask)
+  float* zc;     // saved Z_i = X B_i: written by the forward, read by the backward (NULL: none)
 };
 
 // Partial sums of one backward workgroup, in this order:
@@ -90,6 +91,9 @@ hipError_t launch_bwd_generic(const LayerArgs& a, int G, hipStream_t s);
 // Matrix-core path for the shapes in its table (see kron_mfma.hip).
 bool mfma_fwd_supported(int p, int q, int m, int n, int r);
 bool mfma_bwd_supported(int p, int q, int m, int n, int r);
+// Floats per row of the saved Z_i = X B_i that the forward writes and the backward reads
+// back (0: the shape has no saved path).
+int mfma_zcache_row_floats(int p, int q, int m, int n, int r);
 int mfma_bwd_groups(int64_t N, int p, int q, int m, int n, int r);
 // bf16 layer (kron_bf16.hip): bf16 tensors as 16-bit patterns, fp32 parameter gradients.
 struct LayerArgsBf16 {

@@ -199,6 +199,24 @@ struct Dims {
   static constexpr bool BWD_PREFETCH = BWD_REGS + ROW_REGS <= 420;   // double-buffer the row operands
 };
 
+// The saved intermediate Z_i = X B_i of the 32x32-block layers, for the ranks i < RANKS:
+// the forward writes it for every row, and the whole-row backward reads it for those ranks
+// instead of recomputing them.  RANKS = 2 of 4 was measured best at 20,000 rows: each
+// saved rank takes about 6 us off the backward, while the forward, whose HBM traffic
+// doubles with two saved ranks, slows by 3 and 7 us for one and two and by 18 us for
+// three, where it reaches the HBM rate a device copy gets.  Per row, rank-major; per
+// rank, the four 16x16 tiles (tb, tj) in the forward's lane order: lane 16g + c holds
+// Z[16tj + 4g + v][16tb + c] in slot v.  The forward stores a tile as one 16-byte piece
+// per lane (whole 128-byte lines); the backward, which needs the tile transposed, gathers
+// it with 4-byte loads whose lines L1 serves after the first.
+template <class D>
+struct ZCache {
+  static constexpr bool OK = D::P == 32 && D::Q == 32 && D::M == 32 && D::N == 32 && D::R == 4;
+  static constexpr int RANKS = 2;
+  static_assert(2 * RANKS <= D::R || !OK, "the next row's requests sit in recomputed ranks");
+  static constexpr int ROW = RANKS * 1024;   // floats per row
+};
+
 // Stage B (as is) and C = S o A in LDS with coalesced 16-byte loads.  Every global load
 // is issued before the first LDS store, so the staging costs one memory round trip.
 // With cbits, also set bit j of *cbits for every row j of C (any rank) that holds a
@@ -339,9 +357,10 @@ __device__ __forceinline__ void load_xa_map(float (&xa)[D::TJ][D::SA], const flo
 // The row loop of the forward over the first TJE tiles of the row map.
 // With SKIP, bit tj*TK + tk of tmask says whether the 16 x 16 tile (tj, tk) of C (rows in
 // map order) holds a nonzero entry in any rank; stage 2 skips the K steps of the others.
-template <class D, int TJE, bool SKIP>
+template <class D, int TJE, bool SKIP, bool ZS>
 __device__ __forceinline__ void fwd_rows(int64_t row, int64_t N, bool relu, const float* __restrict__ x,
-                                         float* __restrict__ y, const float* bop, const float* cop,
+                                         float* __restrict__ y, float* __restrict__ zc, const float* bop,
+                                         const float* cop,
                                          float (&xa)[D::TJ][D::SA], const int (&jr)[D::TJ],
                                          const f4 (&bb)[D::TB][D::TK], int lane, int g, int c, unsigned tmask) {
   const int64_t stride = (int64_t)gridDim.x * kWaves;
@@ -379,6 +398,11 @@ __device__ __forceinline__ void fwd_rows(int64_t row, int64_t N, bool relu, cons
 #pragma unroll
           for (int s = 0; s < D::SA; ++s) t = mfma(xa[tj][s], bo[s], t);
           z[tj][tb] = t;   // Z[j = map(16tj+4g+v)][b = 16tb+c]
+          // (read back by the backward only, much later: non-temporal stores, measured 4 us
+          // faster than ordinary ones at 20,000 rows)
+          if (ZS && TJE == D::TJ && i < ZCache<D>::RANKS)
+            __builtin_nontemporal_store(
+                t, reinterpret_cast<f4*>(zc + row * ZCache<D>::ROW + i * 1024 + (tb * 2 + tj) * 256) + lane);
         }
       }
 #pragma unroll
@@ -425,9 +449,10 @@ __device__ __forceinline__ void fwd_rows(int64_t row, int64_t N, bool relu, cons
   }
 }
 
-template <class D, int T, bool SKIP>
+template <class D, int T, bool SKIP, bool ZS>
 __device__ __forceinline__ void fwd_rows_tje(int tje, int64_t row, int64_t N, bool relu, const float* __restrict__ x,
-                                             float* __restrict__ y, const float* bop, const float* cop,
+                                             float* __restrict__ y, float* __restrict__ zc, const float* bop,
+                                             const float* cop,
                                              float (&xa)[D::TJ][D::SA], const int (&jr)[D::TJ],
                                              const f4 (&bb)[D::TB][D::TK], int lane, int g, int c, unsigned tmask) {
   if constexpr (T >= 1) {
@@ -435,23 +460,25 @@ __device__ __forceinline__ void fwd_rows_tje(int tje, int64_t row, int64_t N, bo
       // the tile branches only where a tile of the first T row tiles is empty (uniform)
       constexpr unsigned kFull = (T * D::TK >= 32) ? ~0u : ((1u << (T * D::TK)) - 1u);
       if (SKIP && (tmask & kFull) != kFull)
-        fwd_rows<D, T, SKIP>(row, N, relu, x, y, bop, cop, xa, jr, bb, lane, g, c, tmask);
+        fwd_rows<D, T, SKIP, ZS>(row, N, relu, x, y, zc, bop, cop, xa, jr, bb, lane, g, c, tmask);
       else
-        fwd_rows<D, T, false>(row, N, relu, x, y, bop, cop, xa, jr, bb, lane, g, c, tmask);
+        fwd_rows<D, T, false, ZS>(row, N, relu, x, y, zc, bop, cop, xa, jr, bb, lane, g, c, tmask);
     } else {
-      fwd_rows_tje<D, T - 1, SKIP>(tje, row, N, relu, x, y, bop, cop, xa, jr, bb, lane, g, c, tmask);
+      fwd_rows_tje<D, T - 1, SKIP, ZS>(tje, row, N, relu, x, y, zc, bop, cop, xa, jr, bb, lane, g, c, tmask);
     }
   }
 }
 
-template <class D, bool MAP>
+// ZS: also write Z_i = X B_i of every row into the cache zc (ZCache layout).
+template <class D, bool MAP, bool ZS = false>
 __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t flags,
                                                             const float* __restrict__ x,
                                                             const float* __restrict__ Sm,
                                                             const float* __restrict__ A,
                                                             const float* __restrict__ B,
                                                             const float* __restrict__ bias,
-                                                            float* __restrict__ y) {
+                                                            float* __restrict__ y, float* __restrict__ zc) {
+  static_assert(!ZS || (ZCache<D>::OK && !MAP), "the cache is written by the dense forward of its shapes");
   extern __shared__ float lds[];
   float* bop = lds;              // B_i[g*SA+s][16tb+c]
   float* cop = bop + D::BOP;     // C_i[map(16tj+4g+v)][16tk+c]
@@ -609,8 +636,8 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int64_t N, uint32_t 
     });
   }
   __syncthreads();
-  fwd_rows_tje<D, D::TJ, FwdMap<D, MAP>::ON>(tje, row, N, (flags & KRON_RELU_OUT) != 0, x, y, bop, cop, xa, jr, bb,
-                                             lane, g, c, tmask);
+  fwd_rows_tje<D, D::TJ, FwdMap<D, MAP>::ON, ZS>(tje, row, N, (flags & KRON_RELU_OUT) != 0, x, y, zc, bop, cop, xa,
+                                                 jr, bb, lane, g, c, tmask);
 }
 
 #endif  // forward kernels
@@ -1432,12 +1459,17 @@ __device__ __forceinline__ int kxs(int s, int g) { return 16 * (s >> 2) + 4 * g 
 // and when they fit one 16-row tile the products that run over them -- G = C dY, dX and
 // dB -- take that tile only: G, dX and the dB terms of the other rows are zero.  Z and dC
 // stay dense (dS needs dC at every entry); dX and dC are written back in row order.
-template <class D, int DXM, bool MAP = false>
+// ZC: Z_i = X B_i of the ranks i < ZR = ZCache<D>::RANKS is read from the forward's cache
+// zc instead of being recomputed.  Register slot k holds rank k of the current row; the
+// next row's rank k is requested at the top of rank k + R - ZR of this one (a recomputed
+// rank: ZR <= R / 2).
+template <class D, int DXM, bool MAP = false, bool ZC = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_solo_kernel(int64_t N, const float* __restrict__ x, const float* __restrict__ Sm,
                      const float* __restrict__ A, const float* __restrict__ B, const float* __restrict__ dy,
-                     float* __restrict__ dx, float* __restrict__ part) {
+                     float* __restrict__ dx, float* __restrict__ part, const float* __restrict__ zc) {
   using SL = Solo<D>;
+  static_assert(!ZC || (ZCache<D>::OK && !MAP && DXM <= 2), "the cached backward is dense, without dx accumulation");
   constexpr int R = D::R, L = SL::L, TILE = SL::TILE;
   extern __shared__ float lds[];
   float* tabB = lds;                 // B_i[8g+s][16t+c]                 (A operand of Z^T)
@@ -1564,13 +1596,15 @@ void bwd_solo_kernel(int64_t N, const float* __restrict__ x, const float* __rest
   float xa[2][8], xaj[2][8], dyb[2][8];   // X[16t+c][8g+s], X[kxs][16t+c], dY[kxs][16t+c]
   f4 dyk[2][2];                           // dY[16tk+c][16tb+4g..]
   auto rd_ops = [&]() {
+    if constexpr (!ZC || ZCache<D>::RANKS < R) {   // (X's row-order operand only feeds the recomputation of Z)
 #pragma unroll
-    for (int tj = 0; tj < 2; ++tj)
+      for (int tj = 0; tj < 2; ++tj)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const f4 v = *reinterpret_cast<const f4*>(xt + (16 * tj + c) * L + 8 * g + 4 * t);
-        xa[tj][4 * t] = v[0]; xa[tj][4 * t + 1] = v[1]; xa[tj][4 * t + 2] = v[2]; xa[tj][4 * t + 3] = v[3];
-      }
+        for (int t = 0; t < 2; ++t) {
+          const f4 v = *reinterpret_cast<const f4*>(xt + (16 * tj + c) * L + 8 * g + 4 * t);
+          xa[tj][4 * t] = v[0]; xa[tj][4 * t + 1] = v[1]; xa[tj][4 * t + 2] = v[2]; xa[tj][4 * t + 3] = v[3];
+        }
+    }
 #pragma unroll
     for (int tk = 0; tk < 2; ++tk)
 #pragma unroll
@@ -1599,15 +1633,37 @@ void bwd_solo_kernel(int64_t N, const float* __restrict__ x, const float* __rest
     stage();
     rd_ops();
   }
-  rd_tab(bo, tabB, 0);
+  if constexpr (!ZC) rd_tab(bo, tabB, 0);   // (the saved path reads it with its ranks)
   rd_tab(co, tabC, 0);
   if constexpr (DXM != 0) rd_tab(bx, tabX, 0);
+  f4 zs[R][2][2];   // the cached Z of the saved ranks
+  // Z^T[16tb+4g+v][16tj+c] = Z[16tj+c][16tb+4g+v] is slot c & 3 of the forward's lane
+  // 16(c >> 2) + 4g + v
+  auto zload = [&](f4 (&d)[2][2], int64_t r, int i) {
+    const float* zp = zc + r * ZCache<D>::ROW + i * 1024 + 64 * (c >> 2) + 16 * g + (c & 3);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) d[tb][tj][v] = zp[(tb * 2 + tj) * 256 + 4 * v];
+  };
   // The row loop, instantiated per count of 16-row tiles that G, dX and dB run over (two
   // without the row map).
-  auto rows = [&](auto tiles) {
+  auto rows = [&](auto tiles, auto zranks) {
     constexpr int TJE_ = decltype(tiles)::value;
+    constexpr int ZR = decltype(zranks)::value;
+    // the first row's saved ranks (a wavefront without rows reads the last row, unused),
+    // and rank 0's B table when rank 0 is recomputed
+    if constexpr (ZR > 0) {
+      const int64_t r0 = row < N ? row : N - 1;
+  #pragma unroll
+      for (int k = 0; k < ZR; ++k) zload(zs[k], r0, k);
+    }
+    if constexpr (ZC && ZR == 0) rd_tab(bo, tabB, 0);
     for (; row < N; row += stride) {
-      fetch(row + stride < N ? row + stride : row);
+      const int64_t nrow = row + stride < N ? row + stride : row;
+      fetch(nrow);
       f4 xm[2][2], dold[2][2];   // x under this lane's dX entries (mask), dx already there
       if constexpr (DXM == 2 || DXM == 4) {
   #pragma unroll
@@ -1635,15 +1691,25 @@ void bwd_solo_kernel(int64_t N, const float* __restrict__ x, const float* __rest
   #pragma unroll
       for (int i = 0; i < R; ++i) {
         f4 zt[2][2];   // Z^T[16tb+4g+v][16tj+c]
+        if (i < ZR) {
   #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
+          for (int tb = 0; tb < 2; ++tb)
   #pragma unroll
-          for (int tj = 0; tj < 2; ++tj) {
-            f4 t = f4{0.f, 0.f, 0.f, 0.f};
+            for (int tj = 0; tj < 2; ++tj) zt[tb][tj] = zs[i][tb][tj];
+        } else {
+          // the next row's saved rank i - (R - ZR), into the slot it takes there, requested
+          // before this rank's products (measured 0.6 us faster than after its dC products)
+          if (ZR > 0 && i >= R - ZR) zload(zs[i - (R - ZR)], nrow, i - (R - ZR));
   #pragma unroll
-            for (int s = 0; s < 8; ++s) t = mfma(bo[tb][s], xa[tj][s], t);
-            zt[tb][tj] = t;
-          }
+          for (int tb = 0; tb < 2; ++tb)
+  #pragma unroll
+            for (int tj = 0; tj < 2; ++tj) {
+              f4 t = f4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+              for (int s = 0; s < 8; ++s) t = mfma(bo[tb][s], xa[tj][s], t);
+              zt[tb][tj] = t;
+            }
+        }
         f4 gt[2][2];   // G^T[16tb+4g+v][16tj+c]
   #pragma unroll
         for (int tj = 0; tj < 2; ++tj)
@@ -1658,7 +1724,7 @@ void bwd_solo_kernel(int64_t N, const float* __restrict__ x, const float* __rest
           }
         // the next rank's tables (the last rank reads rank 0 for the next row)
         float bo2[2][8], co2[2][8];
-        rd_tab(bo2, tabB, (i + 1) % R);
+        if ((i + 1) % R >= ZR) rd_tab(bo2, tabB, (i + 1) % R);
         rd_tab(co2, tabC, (i + 1) % R);
         __builtin_amdgcn_sched_barrier(0);
         // dC_i[16tj+4g+v][16tk+c] += sum_b Z[j][b] dY[k][b]
@@ -1713,7 +1779,7 @@ void bwd_solo_kernel(int64_t N, const float* __restrict__ x, const float* __rest
         for (int u = 0; u < 2; ++u)
   #pragma unroll
           for (int v = 0; v < 8; ++v) {
-            bo[u][v] = bo2[u][v];
+            if ((i + 1) % R >= ZR) bo[u][v] = bo2[u][v];
             co[u][v] = co2[u][v];
             if constexpr (DXM != 0) bx[u][v] = bx2[u][v];
           }
@@ -1735,8 +1801,13 @@ void bwd_solo_kernel(int64_t N, const float* __restrict__ x, const float* __rest
       }
     }
   };
-  if (MAP && tje == 1) rows(std::integral_constant<int, 1>{});
-  else rows(std::integral_constant<int, 2>{});
+  if constexpr (ZC) {
+    rows(std::integral_constant<int, 2>{}, std::integral_constant<int, ZCache<D>::RANKS>{});
+  } else if (MAP && tje == 1) {
+    rows(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+  } else {
+    rows(std::integral_constant<int, 2>{}, std::integral_constant<int, 0>{});
+  }
   // Partial row of this workgroup: [dB (R*M*N) | dA (R*P*Q) | dS (P*Q) | dbias (Q*N)],
   // the four wavefronts added in wavefront order.  dC's rows go back to row order (the
   // map is read before the combine area overwrites it).
@@ -1799,6 +1870,7 @@ struct Entry {
   int bwd_kind;        // backward kernel that runs: 0 bwd_mfma, 1 rank-parallel, 2 whole-row
   int rows_per_step;   // rows a workgroup takes per step of its row loop
   int per_cu;          // backward workgroups per compute unit
+  int zc_row;          // floats per row of the saved Z (0: no saved path; whole-row kernel only)
   void (*fwd)(const LayerArgs&, int, hipStream_t);
   void (*bwd)(const LayerArgs&, int, hipStream_t);
 };
@@ -1819,26 +1891,32 @@ int device_cus() {
 #if KRON_MFMA_PASS != 2
 // The forward is persistent: as many workgroups as fit on the device at once (and no
 // more than one row per wavefront), each wavefront striding over rows.
-template <class D, bool MAP>
+template <class D, bool MAP, bool ZS = false>
 void run_fwd_map(const LayerArgs& a, int max_grid, hipStream_t s) {
   static const int per_cu = [] {
-    (void)hipFuncSetAttribute((const void*)fwd_mfma_kernel<D, MAP>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void*)fwd_mfma_kernel<D, MAP, ZS>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)D::FWD_LDS);
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fwd_mfma_kernel<D, MAP>, kThreads, D::FWD_LDS) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fwd_mfma_kernel<D, MAP, ZS>, kThreads, D::FWD_LDS) !=
             hipSuccess || nb < 1)
       nb = 1;
     return nb;
   }();
   int64_t grid = (int64_t)per_cu * device_cus();
   if (grid > max_grid) grid = max_grid;
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, MAP>), dim3((unsigned)grid), dim3(kThreads), D::FWD_LDS, s, a.N, a.flags,
-                     a.x, a.S, a.A, a.B, a.bias, a.y);
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, MAP, ZS>), dim3((unsigned)grid), dim3(kThreads), D::FWD_LDS, s, a.N,
+                     a.flags, a.x, a.S, a.A, a.B, a.bias, a.y, ZS ? a.zc : nullptr);
 }
 
 template <class D>
 void run_fwd(const LayerArgs& a, int max_grid, hipStream_t s) {
   if constexpr (D::FWD_OK) {
+    if constexpr (ZCache<D>::OK) {
+      if (a.zc) {   // (the host refuses the cache together with the sparse-row hint)
+        run_fwd_map<D, false, true>(a, max_grid, s);
+        return;
+      }
+    }
     if constexpr (FwdMap<D, true>::ON) {
       if (a.flags & KRON_SPARSE_ROWS) {
         run_fwd_map<D, true>(a, max_grid, s);
@@ -1892,7 +1970,30 @@ void run_bwd(const LayerArgs& a, int grid, hipStream_t s) {
     const bool map = (a.flags & KRON_SPARSE_ROWS) && dxm <= 2;
 #define KRON_SOLO_LAUNCH(M, MP)                                                                                 \
   hipLaunchKernelGGL((bwd_solo_kernel<D, M, MP>), dim3(grid), dim3(kThreads), Solo<D>::LDS, s, a.N, a.x, a.S, a.A, \
-                     a.B, a.dy, a.dx, a.part)
+                     a.B, a.dy, a.dx, a.part, (const float*)nullptr)
+#define KRON_SOLO_ZC_LAUNCH(M)                                                                                  \
+  hipLaunchKernelGGL((bwd_solo_kernel<D, M, false, true>), dim3(grid), dim3(kThreads), Solo<D>::LDS, s, a.N, a.x, \
+                     a.S, a.A, a.B, a.dy, a.dx, a.part, (const float*)a.zc)
+    if constexpr (ZCache<D>::OK) {
+      if (a.zc) {   // (the host refuses the cache with the sparse-row hint and with dx accumulation)
+        static const bool attr_zc = [] {
+          (void)hipFuncSetAttribute((const void*)bwd_solo_kernel<D, 0, false, true>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)Solo<D>::LDS);
+          (void)hipFuncSetAttribute((const void*)bwd_solo_kernel<D, 1, false, true>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)Solo<D>::LDS);
+          (void)hipFuncSetAttribute((const void*)bwd_solo_kernel<D, 2, false, true>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)Solo<D>::LDS);
+          return true;
+        }();
+        (void)attr_zc;
+        switch (dxm) {
+          case 0: KRON_SOLO_ZC_LAUNCH(0); break;
+          case 1: KRON_SOLO_ZC_LAUNCH(1); break;
+          default: KRON_SOLO_ZC_LAUNCH(2); break;
+        }
+        return;
+      }
+    }
     if (map) {
       switch (dxm) {
         case 0: KRON_SOLO_LAUNCH(0, true); break;
@@ -1909,6 +2010,7 @@ void run_bwd(const LayerArgs& a, int grid, hipStream_t s) {
       }
     }
 #undef KRON_SOLO_LAUNCH
+#undef KRON_SOLO_ZC_LAUNCH
   } else if constexpr (kind == 1) {
     static const bool attr = [] {
       (void)hipFuncSetAttribute((const void*)bwd_rp_kernel<D, 0>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1955,6 +2057,8 @@ void run_bwd(const LayerArgs& a, int grid, hipStream_t s) {
         bwd_kind<Dims<P, Q, M, N, R>, BK>(),                                                           \
         bwd_kind<Dims<P, Q, M, N, R>, BK>() == 1 ? RP<Dims<P, Q, M, N, R>>::RPI : kWaves,              \
         bwd_kind<Dims<P, Q, M, N, R>, BK>() == 1 ? RP<Dims<P, Q, M, N, R>>::WPC : 1,                   \
+        ZCache<Dims<P, Q, M, N, R>>::OK && bwd_kind<Dims<P, Q, M, N, R>, BK>() == 2                     \
+            ? ZCache<Dims<P, Q, M, N, R>>::ROW : 0,                                                     \
         &run_fwd_shape<P, Q, M, N, R>, &run_bwd<Dims<P, Q, M, N, R>, BK>},
 
 const Entry kTable[] = {KRON_MFMA_SHAPES(KRON_ENTRY)};
@@ -1988,6 +2092,11 @@ bool mfma_fwd_supported(int p, int q, int m, int n, int r) {
 bool mfma_bwd_supported(int p, int q, int m, int n, int r) {
   const Entry* e = find(p, q, m, n, r);
   return e && e->bwd_ok;
+}
+
+int mfma_zcache_row_floats(int p, int q, int m, int n, int r) {
+  const Entry* e = find(p, q, m, n, r);
+  return (e && e->fwd_ok && e->bwd_ok) ? e->zc_row : 0;
 }
 
 int mfma_bwd_chunk(int p, int q, int m, int n, int r) {

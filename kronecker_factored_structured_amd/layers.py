@@ -14,9 +14,12 @@ from . import api
 
 class _KronLinearFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x, S, A, B, bias, relu: bool, sparse_rows: bool):
+    def forward(ctx, x, S, A, B, bias, relu: bool, sparse_rows: bool, save_z: bool = False):
         x = x.contiguous()
-        y = api.kron_linear_fwd(x, S, A, B, bias, relu=relu, sparse_rows=sparse_rows)
+        # Z_i = X B_i saved for the backward where the shape has that path (else recomputed)
+        zc = api.new_zcache(x, S, A, B) if save_z and not sparse_rows else None
+        y = api.kron_linear_fwd(x, S, A, B, bias, relu=relu, sparse_rows=sparse_rows, zcache=zc)
+        ctx.zc = zc
         ctx.relu = relu
         ctx.sparse_rows = sparse_rows
         ctx.save_for_backward(x, S, A, B, y if relu else None)
@@ -31,18 +34,22 @@ class _KronLinearFn(torch.autograd.Function):
         if ctx.relu:
             dy = api.kron_relu_bwd(y, dy)
         g = api.kron_linear_bwd(x, S, A, B, dy, want_dx=ctx.needs_input_grad[0],
-                                want_dbias=ctx.has_bias, sparse_rows=ctx.sparse_rows)
-        return g["dx"], g["dS"], g["dA"], g["dB"], g["dbias"], None, None
+                                want_dbias=ctx.has_bias, sparse_rows=ctx.sparse_rows, zcache=ctx.zc)
+        ctx.zc = None
+        return g["dx"], g["dS"], g["dA"], g["dB"], g["dbias"], None, None, None
 
 
 class KronLinear(nn.Module):
     """y = x W + bias, W = sum_i kron(S o A_i, B_i) (Kronecker layer tutorial,
     "Build W, then multiply": S p x q initialised to ones, A_i ~ randn/sqrt(p),
     B_i ~ randn/sqrt(m), bias zeros; p = in/m, q = out/n).  sparse_rows: S is expected
-    to have whole rows zero (e.g. after l1 pruning) and the forward skips them."""
+    to have whole rows zero (e.g. after l1 pruning) and the forward skips them.  save_z: the
+    forward keeps Z_i = X B_i of the first ranks (kron_linear_zcache_bytes per batch) for the
+    backward instead of the backward recomputing it, where the shape has that path."""
 
     def __init__(self, in_features: int, out_features: int, m: int, r: int, n: Optional[int] = None,
-                 with_S: bool = True, relu: bool = False, device=None, sparse_rows: bool = False):
+                 with_S: bool = True, relu: bool = False, device=None, sparse_rows: bool = False,
+                 save_z: bool = False):
         super().__init__()
         n = m if n is None else n
         if in_features % m or out_features % n:
@@ -55,9 +62,10 @@ class KronLinear(nn.Module):
         self.bias = nn.Parameter(torch.zeros(out_features, device=dev))
         self.relu = relu
         self.sparse_rows = sparse_rows
+        self.save_z = save_z
 
     def forward(self, x):
-        return _KronLinearFn.apply(x, self.S, self.A, self.B, self.bias, self.relu, self.sparse_rows)
+        return _KronLinearFn.apply(x, self.S, self.A, self.B, self.bias, self.relu, self.sparse_rows, self.save_z)
 
     def l1_penalty(self):
         """sum|S| as a 0-dim tensor with autograd (sign(S) times the upstream gradient)."""

@@ -328,3 +328,46 @@ def test_binding_refuses_cpu_tensors():
     B = torch.zeros(1, 2, 2)
     with pytest.raises(ValueError, match="GPU tensor"):
         K.kron_linear_fwd(x, None, A, B)
+
+
+def test_saved_path_argument_errors():
+    """kron_linear_zcache_bytes / kron_linear_fwd_save / kron_linear_bwd_saved refuse what
+    they cannot run before any HIP call."""
+    L = _lib.lib()
+    MB = 1 << 20
+    s = KronShape(64, 32, 32, 32, 32, 4, 0)
+    zc_bytes = L.kron_linear_zcache_bytes(ctypes.byref(s))
+    per_rank = 64 * 32 * 32 * 4                               # N * p * n floats per saved rank
+    assert zc_bytes % per_rank == 0 and 1 <= zc_bytes // per_rank <= 4
+    for other in (KronShape(64, 32, 32, 32, 32, 2, 0), KronShape(64, 16, 16, 64, 64, 2, 0),
+                  KronShape(64, 8, 8, 8, 8, 1, 0), KronShape(-1, 32, 32, 32, 32, 4, 0)):
+        assert L.kron_linear_zcache_bytes(ctypes.byref(other)) == 0
+    assert L.kron_linear_zcache_bytes(ctypes.byref(KronShape(0, 32, 32, 32, 32, 4, 0))) == 0
+
+    def fs(shape, zc=P(80 * MB), zb=zc_bytes, x=P(0), y=P(16 * MB)):
+        return L.kron_linear_fwd_save(ctypes.byref(shape), x, None, P(32 * MB), P(48 * MB), None, y, zc,
+                                      ctypes.c_size_t(zb), None)
+
+    assert fs(s, zc=None) == _lib.KRON_E_NULL
+    assert fs(s, zb=zc_bytes - 4) == _lib.KRON_E_WORKSPACE
+    assert fs(s, zc=P(80 * MB + 4)) == _lib.KRON_E_ALIGN
+    assert fs(s, zc=P(128 * 1024)) == _lib.KRON_E_ALIAS          # the cache overlaps x
+    assert fs(s, zc=P(16 * MB + 64)) == _lib.KRON_E_ALIAS        # the cache overlaps y
+    assert fs(KronShape(64, 32, 32, 32, 32, 2, 0)) == _lib.KRON_E_UNSUPPORTED
+    assert fs(KronShape(64, 32, 32, 32, 32, 4, _lib.KRON_SPARSE_ROWS)) == _lib.KRON_E_ARG
+    assert fs(KronShape(0, 32, 32, 32, 32, 4, 0), zc=None, x=None, y=None) == 0   # N == 0: no-op
+
+    ws = L.kron_linear_bwd_workspace_bytes(ctypes.byref(s))
+
+    def bs(shape, zc=P(80 * MB), zb=zc_bytes, dx=P(96 * MB)):
+        return L.kron_linear_bwd_saved(ctypes.byref(shape), P(0), P(16 * MB), P(32 * MB), P(48 * MB), P(64 * MB),
+                                       zc, ctypes.c_size_t(zb), dx, P(112 * MB), P(128 * MB), P(144 * MB),
+                                       P(160 * MB), P(192 * MB), ctypes.c_size_t(ws), None)
+
+    assert bs(s, zc=None) == _lib.KRON_E_NULL
+    assert bs(s, zb=zc_bytes - 4) == _lib.KRON_E_WORKSPACE
+    assert bs(s, zc=P(80 * MB + 8)) == _lib.KRON_E_ALIGN
+    assert bs(s, dx=P(80 * MB + 256)) == _lib.KRON_E_ALIAS       # dx overlaps the cache
+    assert bs(KronShape(64, 32, 32, 32, 32, 1, 0)) == _lib.KRON_E_UNSUPPORTED
+    assert bs(KronShape(64, 32, 32, 32, 32, 4, _lib.KRON_SPARSE_ROWS)) == _lib.KRON_E_ARG
+    assert "sparse-row" in _lib.last_error()
