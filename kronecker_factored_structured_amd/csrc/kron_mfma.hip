@@ -1656,9 +1656,15 @@ void bwd_solo_kernel(int64_t N, const float* __restrict__ x, const float* __rest
     // the first row's saved ranks (a wavefront without rows reads the last row, unused),
     // and rank 0's B table when rank 0 is recomputed
     if constexpr (ZR > 0) {
+      // in rank order, as the row loop requests them: the compiler derives the loop's
+      // memory waits from both paths into it, and with rank 1 issued first it waited for
+      // rank 1 and the last row's dX stores before rank 0's first product
       const int64_t r0 = row < N ? row : N - 1;
   #pragma unroll
-      for (int k = 0; k < ZR; ++k) zload(zs[k], r0, k);
+      for (int k = 0; k < ZR; ++k) {
+        zload(zs[k], r0, k);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if constexpr (ZC && ZR == 0) rd_tab(bo, tabB, 0);
     for (; row < N; row += stride) {
