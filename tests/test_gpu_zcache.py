@@ -153,3 +153,21 @@ def test_binding_refuses_bad_caches():
     assert mod.new_zcache(xs, Ss, As, Bs) is None
     with pytest.raises(ValueError, match="no saved-intermediate path"):
         mod.kron_linear_fwd(xs, Ss, As, Bs, zcache=zc)
+
+
+def test_cache_depends_on_x_and_B_only():
+    """Z_i = X B_i holds no S, A or bias: a cache written with one S and A serves a backward
+    with another (the gradients are the oracle's for the new factors)."""
+    inp = headline_layer(seed=56, N=1031)
+    x, S, A, B, bias, dy = (dev(a) for a in (inp.x, inp.S, inp.A, inp.B, inp.bias, inp.dy))
+    zc = K().new_zcache(x, S, A, B)
+    K().kron_linear_fwd(x, S, A, B, bias, zcache=zc)
+    other = headline_layer(seed=57, N=1031)          # new S and A, the same x, B and dy
+    other.x, other.B, other.dy = inp.x, inp.B, inp.dy
+    S2, A2 = dev(other.S), dev(other.A)
+    print(f"[zcache] N=1031 reused cache, S and A from seed 57", flush=True)
+    g = K().kron_linear_bwd(x, S2, A2, B, dy, want_dbias=False, zcache=zc)
+    torch.cuda.synchronize()
+    _, go = oracle_pass(other)
+    for k in ("dx", "dS", "dA", "dB"):
+        assert rel_err(host(g[k]), go[k]) <= TOL_F32, k
