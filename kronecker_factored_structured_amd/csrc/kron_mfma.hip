@@ -421,6 +421,31 @@ __device__ __forceinline__ void fwd_rows(int64_t row, int64_t N, bool relu, cons
     }
     // acc[tb][tk] register v = Y^T[b = 16tb+4g+v][k = 16tk+c] -> y[k*N + b]
     float* yr = y + row * D::OUT;
+    if constexpr (D::N == 32 && D::Q % 16 == 0 && D::R != 1) {
+      // Rows of 32 floats: lanes c and c ^ 8 swap one 16-byte piece, so that each store
+      // covers eight whole 128-byte rows of y (lanes c < 8 the pieces 0-3 of row c, lanes
+      // c >= 8 the pieces 4-7) instead of half of sixteen.
+      const bool lo = c < 8;
+#pragma unroll
+      for (int tk = 0; tk < D::TK; ++tk) {
+        f4 o[2];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          o[tb] = acc[tb][tk] + bb[tb][tk];
+          if (relu) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) o[tb][v] = o[tb][v] > 0.f ? o[tb][v] : 0.f;
+          }
+        }
+        const f4 send = lo ? o[1] : o[0];
+        f4 recv;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) recv[v] = __shfl_xor(send[v], 8);
+        float* yk = yr + (16 * tk + (c & 7)) * 32 + (lo ? 0 : 16) + 4 * g;
+        __builtin_nontemporal_store(lo ? o[0] : recv, reinterpret_cast<f4*>(yk));
+        __builtin_nontemporal_store(lo ? recv : o[1], reinterpret_cast<f4*>(yk + 8 * 32));
+      }
+    } else {
 #pragma unroll
     for (int tb = 0; tb < D::TB; ++tb)
 #pragma unroll
@@ -442,6 +467,7 @@ __device__ __forceinline__ void fwd_rows(int64_t row, int64_t N, bool relu, cons
             __builtin_nontemporal_store(o, reinterpret_cast<f4*>(yr + k * D::N + b0));
         }
       }
+    }
 #pragma unroll
     for (int tj = 0; tj < TJE; ++tj)
 #pragma unroll
@@ -1792,18 +1818,23 @@ void bwd_solo_kernel(int64_t N, const float* __restrict__ x, const float* __rest
       }
       if constexpr (DXM != 0) {
         float* dxr = dx + row * D::IN;
+        f4 o[2][2];
   #pragma unroll
         for (int ta = 0; ta < 2; ++ta)
   #pragma unroll
           for (int tj = 0; tj < 2; ++tj) {
-            f4 o = dxt[ta][tj];
-            if constexpr (DXM >= 3) o += dold[ta][tj];
+            o[ta][tj] = dxt[ta][tj];
+            if constexpr (DXM >= 3) o[ta][tj] += dold[ta][tj];
             if constexpr (DXM == 2 || DXM == 4) {
   #pragma unroll
-              for (int v = 0; v < 4; ++v) o[v] = xm[ta][tj][v] > 0.f ? o[v] : 0.f;
+              for (int v = 0; v < 4; ++v) o[ta][tj][v] = xm[ta][tj][v] > 0.f ? o[ta][tj][v] : 0.f;
             }
-            __builtin_nontemporal_store(o, reinterpret_cast<f4*>(dxr + dxrow[tj] * 32 + 16 * ta + 4 * g));
           }
+  #pragma unroll
+          for (int ta = 0; ta < 2; ++ta)
+  #pragma unroll
+            for (int tj = 0; tj < 2; ++tj)
+              __builtin_nontemporal_store(o[ta][tj], reinterpret_cast<f4*>(dxr + dxrow[tj] * 32 + 16 * ta + 4 * g));
       }
     }
   };
